@@ -1,0 +1,421 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself: published
+generator values, library routines (torch float64 SDPA, rms_norm, bfloat16 casts),
+closed forms (RoPE as complex rotation), invariants and brute force.  No GPU."""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from synth import CONFIGS, make_weights, make_x0, rng
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------------------- generator
+
+def test_splitmix64_published_value():
+    # SplitMix64 (Steele-Lea-Flood 2014, Vigna's splitmix64.c): state 0 -> first output.
+    with open(os.path.join(GOLDEN, "splitmix64.txt")) as fh:
+        lines = [l.split("#")[0].strip() for l in fh if l.split("#")[0].strip()]
+    state, first = (int(v, 16) for v in lines[0].split())
+    assert rng.mix_int(state + rng.GAMMA) == first
+
+
+def test_rng_torch_matches_python_and_random_access():
+    n = torch.arange(1000, dtype=torch.int64)
+    raw = rng.raw_at(n, 5, 9)
+    base = rng.stream_base(5, 9)
+    for i in (0, 1, 17, 999):
+        assert (int(raw[i]) & rng.MASK64) == rng.mix_int(base + (i + 1) * rng.GAMMA)
+    full = rng.normal((40, 30), 3, 4)
+    part = rng.normal((10, 30), 3, 4, offset=25 * 30)
+    assert torch.equal(full[25:35], part)
+
+
+def test_rng_normal_moments():
+    x = rng.normal((1 << 20,), 11, 2).double()
+    assert abs(x.mean().item()) < 5e-3
+    assert abs(x.std().item() - 1.0) < 5e-3
+    u = rng.uniform((1 << 18,), 11, 3, -0.2, 0.2).double()
+    assert u.min() >= -0.2 and u.max() < 0.2 and abs(u.mean().item()) < 2e-3
+
+
+# ------------------------------------------------------------------------------ rounding
+
+def test_bf16_round_matches_torch_cast():
+    x = (torch.randn(200000, dtype=torch.float64) * 3).float()
+    ref = x.to(torch.bfloat16).double().numpy()
+    got = oracle.bf16_round(x.double().numpy())
+    assert np.array_equal(ref, got)
+    # ties to even: 1 + 2^-8 is halfway between 1 and 1 + 2^-7
+    assert oracle.bf16_round(1.0 + 2 ** -8) == 1.0
+    assert oracle.bf16_round(1.0 + 3 * 2 ** -8) == 1.0 + 2 ** -6
+
+
+# ---------------------------------------------------------------------------------- RoPE
+
+def _rope_complex(u, pos, base):
+    """RoPE written as complex multiplication of the pairs (u_i, u_{i+D/2})."""
+    D = u.shape[-1]
+    half = D // 2
+    z = u[..., :half] + 1j * u[..., half:]
+    theta = np.array([base ** (-(2.0 * i) / D) for i in range(half)])
+    z = z * np.exp(1j * np.asarray(pos, np.float64) * theta)
+    return np.concatenate([z.real, z.imag], axis=-1)
+
+
+def test_rope_is_complex_rotation():
+    r = np.random.default_rng(0)
+    u = r.standard_normal((5, 16))
+    pos = r.integers(0, 50, size=(5, 1)).astype(np.float64)
+    assert np.allclose(oracle.rope(u, pos, 10000.0), _rope_complex(u, pos, 10000.0),
+                       atol=1e-13)
+    # D = 2: theta_0 = 1, so the angle equals the position exactly
+    v = np.array([[1.0, 0.0]])
+    assert np.allclose(oracle.rope(v, 0.5, 10000.0), [[math.cos(0.5), math.sin(0.5)]])
+
+
+def test_rope_norm_and_relative_position():
+    r = np.random.default_rng(1)
+    q, k = r.standard_normal((2, 32))
+    for m, n in [(0, 3), (7, 2)]:
+        s1 = oracle.rope(q, m, 1e4) @ oracle.rope(k, n, 1e4)
+        s2 = oracle.rope(q, m + 11, 1e4) @ oracle.rope(k, n + 11, 1e4)
+        assert abs(s1 - s2) < 1e-12
+    assert abs(np.linalg.norm(oracle.rope(q, 9, 1e4)) - np.linalg.norm(q)) < 1e-12
+
+
+def _halves(u):
+    D = u.shape[-1]
+    q4 = D // 4
+    fwd = np.r_[0:q4, D // 2:D // 2 + q4]
+    rev = np.r_[q4:D // 2, D // 2 + q4:D]
+    return fwd, rev
+
+
+def test_depth_rope_forward_half_relative_reversed_half_distance_to_L():
+    r = np.random.default_rng(2)
+    D, L = 64, 16
+    q, k = r.standard_normal((2, D))
+    fwd, rev = _halves(q)
+    def parts(m, n, LL):
+        a = oracle.depth_rope(q, m, LL, 1e4)
+        b = oracle.depth_rope(k, n, LL, 1e4)
+        return a[fwd] @ b[fwd], a[rev] @ b[rev]
+    f1, r1 = parts(5, 2, L)
+    f2, r2 = parts(9, 6, L)      # same offset, shifted
+    assert abs(f1 - f2) < 1e-12 and abs(r1 - r2) < 1e-12
+    # reversed half at (m, n; L) == plain RoPE score of that half at (L-1-m, L-1-n)
+    m, n = 3, 11
+    a = oracle.depth_rope(q, m, L, 1e4)
+    b = oracle.depth_rope(k, n, L, 1e4)
+    pa = _rope_complex(q, L - 1 - m, 1e4)
+    pb = _rope_complex(k, L - 1 - n, 1e4)
+    assert abs(a[rev] @ b[rev] - pa[rev] @ pb[rev]) < 1e-12
+    assert abs(a[fwd] @ b[fwd] - _rope_complex(q, m, 1e4)[fwd] @ _rope_complex(k, n, 1e4)[fwd]) < 1e-12
+    # position-less key (router): the reversed half depends only on L-1-l
+    sa = oracle.depth_rope(q, 4, 10, 1e4)[rev] @ k[rev]
+    sb = oracle.depth_rope(q, 9, 15, 1e4)[rev] @ k[rev]
+    assert abs(sa - sb) < 1e-12
+    fa = oracle.depth_rope(q, 4, 10, 1e4)[fwd] @ k[fwd]
+    fb = oracle.depth_rope(q, 9, 15, 1e4)[fwd] @ k[fwd]
+    assert abs(fa - fb) > 1e-6
+    # the reversed half sees the depth offset with its sign flipped: its score at
+    # (m, n) is the plain-RoPE score of the same dims at (n, m)
+    a = oracle.depth_rope(q, 7, L, 1e4)
+    b = oracle.depth_rope(k, 4, L, 1e4)
+    pa = _rope_complex(q, 4, 1e4)
+    pb = _rope_complex(k, 7, 1e4)
+    assert abs(a[rev] @ b[rev] - pa[rev] @ pb[rev]) < 1e-12
+
+
+# ------------------------------------------------------------------------------ attention
+
+def _sdpa(q, k, v, causal=True):
+    """torch float64 SDPA with [B, n, H, d] layout."""
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(np.asarray(a, np.float64).transpose(0, 2, 1, 3)))
+    o = F.scaled_dot_product_attention(t(q), t(k), t(v), is_causal=causal)
+    return o.numpy().transpose(0, 2, 1, 3)
+
+
+def test_depth_attn_first_depth_returns_v_exactly():
+    r = np.random.default_rng(3)
+    R, H, d, L = 7, 4, 16, 5
+    q, k, v = r.standard_normal((3, R, H, d))
+    for bf16 in (False, True):
+        vv = oracle.bf16_round(v) if bf16 else v
+        kc, vc = np.full((R, L, H, d), np.nan), np.full((R, L, H, d), np.nan)
+        out = oracle.depth_attn(q, k, vv, kc, vc, 0, L, bf16=bf16)
+        assert np.array_equal(out, vv)
+
+
+def test_depth_attn_equals_causal_sdpa_over_depth():
+    r = np.random.default_rng(4)
+    R, H, d, L = 6, 2, 8, 7
+    q, k, v = r.standard_normal((3, R, L, H, d))
+    kc, vc = np.full((R, L, H, d), np.nan), np.full((R, L, H, d), np.nan)
+    outs = np.stack([oracle.depth_attn(q[:, l], k[:, l], v[:, l], kc, vc, l, L, use_rope=False)
+                     for l in range(L)], axis=1)
+    ref = _sdpa(q, k, v, causal=True)   # rows as batch, depth as the sequence axis
+    assert np.allclose(outs, ref, atol=1e-12)
+
+
+def test_depth_attn_ignores_future_slots_and_constant_values():
+    r = np.random.default_rng(5)
+    R, H, d, L, l = 4, 2, 8, 6, 3
+    kc = r.standard_normal((R, L, H, d))
+    vc = np.ones((R, L, H, d)) * 0.75
+    kc[:, l + 1:] = np.nan
+    vc[:, l + 1:] = np.nan
+    q, k = r.standard_normal((2, R, H, d))
+    out = oracle.depth_attn(q, k, np.full((R, H, d), 0.75), kc, vc, l, L)
+    assert np.allclose(out, 0.75, atol=1e-14)
+
+
+def test_seq_attn_equals_sdpa_and_causality():
+    r = np.random.default_rng(6)
+    B, n, H, d = 2, 9, 3, 8
+    q, k, v = r.standard_normal((3, B, n, H, d))
+    out, _, _ = oracle.seq_attn(q, k, v, sa_rope=False)
+    assert np.allclose(out, _sdpa(q, k, v), atol=1e-12)
+    # with RoPE: equals SDPA on q, k rotated by the complex formulation
+    pos = np.arange(n, dtype=np.float64)[None, :, None, None]
+    out2, krot, _ = oracle.seq_attn(q, k, v, sa_rope=True)
+    qr, kr = _rope_complex(q, pos, 1e4), _rope_complex(k, pos, 1e4)
+    assert np.allclose(out2, _sdpa(qr, kr, v), atol=1e-12)
+    assert np.allclose(krot, kr, atol=1e-12)
+    # causality: perturbing token p+1 leaves rows <= p unchanged
+    k2, v2 = k.copy(), v.copy()
+    k2[:, 5] += 1.0
+    v2[:, 5] -= 2.0
+    out3, _, _ = oracle.seq_attn(q, k2, v2)
+    assert np.array_equal(out3[:, :5], out2[:, :5])
+
+
+def test_seq_attn_decode_equals_prefill_last_row():
+    r = np.random.default_rng(7)
+    B, n, H, d = 2, 6, 2, 8
+    q, k, v = r.standard_normal((3, B, n, H, d))
+    full, krot, vv = oracle.seq_attn(q, k, v)
+    cap = n + 2
+    kc, vc = np.full((B, cap, H, d), np.nan), np.full((B, cap, H, d), np.nan)
+    kc[:, :n - 1], vc[:, :n - 1] = krot[:, :n - 1], vv[:, :n - 1]
+    dec, _, _ = oracle.seq_attn(q[:, n - 1:], k[:, n - 1:], v[:, n - 1:], pos0=n - 1,
+                                k_cache=kc, v_cache=vc)
+    assert np.allclose(dec[:, 0], full[:, n - 1], atol=1e-12)
+
+
+# -------------------------------------------------------------------------------- routing
+
+def _topk_bruteforce(key, k):
+    """Rank by counting the experts that beat e: higher key, or equal key and lower index."""
+    E = key.shape[0]
+    rank = [sum(1 for f in range(E) if key[f] > key[e] or (key[f] == key[e] and f < e))
+            for e in range(E)]
+    sel = sorted([e for e in range(E) if rank[e] < k], key=lambda e: rank[e])
+    return sel
+
+
+def test_topk_matches_bruteforce_with_ties():
+    r = np.random.default_rng(8)
+    for trial in range(300):
+        E = int(r.integers(1, 13))
+        k = int(r.integers(1, min(3, E) + 1))
+        key = np.round(r.standard_normal(E), 1)          # many exact ties
+        got = list(oracle.topk_select(key[None], k)[0])
+        assert got == _topk_bruteforce(key, k)
+        # the set is the best k-subset by key sum (among subsets, lexicographic ties aside)
+        best = max(itertools.combinations(range(E), k), key=lambda c: sum(key[list(c)]))
+        assert abs(sum(key[got]) - sum(key[list(best)])) < 1e-12
+
+
+def test_route_gate_properties():
+    r = np.random.default_rng(9)
+    T, h, rr, E = 11, 16, 8, 10
+    x = r.standard_normal((T, h))
+    w_r = r.standard_normal((rr, h)) * 0.3
+    keys = r.standard_normal((E, rr)) * 0.3
+    bias = r.uniform(-0.2, 0.2, E)
+    idx, gate, counts, z = oracle.expert_route(x, w_r, keys, bias, 3, 2, 6)
+    assert np.allclose(gate.sum(-1), 1.0, atol=1e-12)
+    assert counts.sum() == T * 3
+    idx1, g1, _, z1 = oracle.expert_route(x, w_r, keys, bias, 1, 2, 6, normalize=False)
+    assert np.allclose(g1[:, 0], 1 / (1 + np.exp(-z1[np.arange(T), idx1[:, 0]])))
+    idxE, _, cE, _ = oracle.expert_route(x, w_r, keys, bias, E, 2, 6)
+    assert (cE == T).all()
+    # relabelling the experts permutes the indices, leaves the gates unchanged
+    perm = r.permutation(E)
+    inv = np.argsort(perm)
+    idx_p, gate_p, _, _ = oracle.expert_route(x, w_r, keys[perm], bias[perm], 3, 2, 6)
+    assert np.array_equal(perm[idx_p], idx) and np.allclose(gate_p, gate)
+    assert np.array_equal(inv[idx], idx_p)
+
+
+def test_route_scores_closed_form_small_rank():
+    # r = 4: pairs (0,2) and (1,3); pair 0 at depth l with theta 1, pair 1 reversed at
+    # L-1-l with theta = base^-1/2.  Written as two complex rotations.
+    x = np.array([[1.0, 0.0, 0.0]])
+    w_r = np.array([[2.0, 0, 0], [0, 0, 0], [0, 0, 0], [1.0, 0, 0]])  # u = (2, 0, 0, 1)
+    keys = np.eye(4)
+    l, L, base = 2, 5, 100.0
+    _, _, _, z = oracle.expert_route(x, w_r, keys, np.zeros(4), 1, l, L, base=base)
+    c0 = 2.0 * np.exp(1j * l * 1.0)                          # (u0 + i u2) e^{i l}
+    c1 = (0.0 + 1j * 1.0) * np.exp(1j * (L - 1 - l) * base ** -0.5)
+    assert np.allclose(z[0], [c0.real, c1.real, c0.imag, c1.imag], atol=1e-14)
+
+
+def test_bias_update_zero_sum_sign():
+    N = np.array([5, 1, 9, 3, 4, 7, 2])   # distinct counts
+    b = oracle.bias_update(np.zeros(7), N, 0.1)
+    assert np.isclose(b.sum(), 0.0)  # odd E, distinct counts: as many above as below the median
+    assert np.allclose(b, 0.1 * np.sign(np.median(N) - N))
+
+
+# -------------------------------------------------------------------------------- experts
+
+def test_single_expert_is_dense_mlp():
+    r = np.random.default_rng(10)
+    T, h, f = 9, 12, 6
+    y = r.standard_normal((T, h))
+    w1, w3 = r.standard_normal((2, 1, f, h)) * 0.4
+    w2 = r.standard_normal((1, h, f)) * 0.4
+    w_r, keys = r.standard_normal((4, h)) * 0.3, r.standard_normal((1, 4))
+    idx, gate, _, z = oracle.expert_route(y, w_r, keys, np.zeros(1), 1, 0, 3, normalize=False)
+    yt = torch.from_numpy(y)
+    for kind in ("swiglu", "gelu"):
+        out = oracle.expert_ffn(kind, y, idx, gate, w1, w3, w2)
+        if kind == "swiglu":
+            hid = F.silu(F.linear(yt, torch.from_numpy(w1[0]))) * F.linear(yt, torch.from_numpy(w3[0]))
+        else:
+            hid = F.gelu(F.linear(yt, torch.from_numpy(w1[0])))
+        mlp = F.linear(hid, torch.from_numpy(w2[0])).numpy()
+        sig = 1.0 / (1.0 + np.exp(-z[:, 0]))
+        assert np.allclose(out, sig[:, None] * mlp, atol=1e-12)
+
+
+def test_grouped_experts_equal_per_token_loop():
+    r = np.random.default_rng(11)
+    T, h, f, E, k = 13, 8, 4, 5, 2
+    x = r.standard_normal((T, h))
+    w1, w3 = r.standard_normal((2, E, f, h))
+    w2 = r.standard_normal((E, h, f))
+    idx = np.stack([r.choice(E, k, replace=False) for _ in range(T)])
+    gate = r.uniform(0.1, 1, (T, k))
+    res = r.standard_normal((T, h))
+    out = oracle.expert_ffn("swiglu", x, idx, gate, w1, w3, w2, residual=res)
+    ref = res.copy()
+    for t in range(T):
+        for i in range(k):
+            e = idx[t, i]
+            a = w1[e] @ x[t]
+            u = w3[e] @ x[t]
+            ref[t] += gate[t, i] * (w2[e] @ (a / (1 + np.exp(-a)) * u))
+    assert np.allclose(out, ref, atol=1e-12)
+    wl = r.standard_normal((E, 3, h))
+    lin = oracle.expert_ffn("linear", x, idx[:, :1], gate[:, :1], wl)
+    ref_l = np.stack([gate[t, 0] * (wl[idx[t, 0]] @ x[t]) for t in range(T)])
+    assert np.allclose(lin, ref_l, atol=1e-12)
+
+
+def test_shared_expert_identity_top1():
+    """sigma x W_e + max(sigma_hat) x W_sh == sigma x (W_e + W_sh) for top-1 ([PN] key design 3)."""
+    cfg = CONFIGS["linear_moe"].replace(b=1, s=8, h=32, H=2, d=16, L=3, E=8, k=2, f=8, r=8,
+                                        proj_experts=4, dtype="f32")
+    W = oracle.prepare_weights(make_weights(cfg))
+    x0 = make_x0(cfg).numpy()
+    ref = oracle.layer_forward(cfg, W, x0)
+    Wa = dict(W)
+    for nm in ("qkv", "o"):
+        Wa["w_%s_e" % nm] = W["w_%s_e" % nm] + W["w_%s_sh" % nm][None]
+        Wa["w_%s_sh" % nm] = np.zeros_like(W["w_%s_sh" % nm])
+    got = oracle.layer_forward(cfg, Wa, x0)
+    assert np.array_equal(got["pidx"], ref["pidx"])
+    assert np.allclose(got["x_out"], ref["x_out"], atol=1e-12, rtol=0)
+
+
+# ---------------------------------------------------------------------------------- layer
+
+def test_layer_without_da_ea_is_plain_recurrent_attention_block():
+    cfg = CONFIGS["tiny"].replace(use_da=False, use_ea=False, sa_rope=False, b=2, s=10)
+    W = oracle.prepare_weights(make_weights(cfg))
+    x0 = make_x0(cfg).numpy()
+    got = oracle.layer_forward(cfg, W, x0)["x_out"]
+    x = torch.from_numpy(x0.reshape(cfg.T, cfg.h).astype(np.float64))
+    g = torch.from_numpy(W["g"])
+    wq, wk, wv = (torch.from_numpy(W["w_qkv"][j * cfg.h:(j + 1) * cfg.h]) for j in range(3))
+    wo = torch.from_numpy(W["w_o"][:, :cfg.h])
+    for _ in range(cfg.L):
+        xh = F.rms_norm(x, (cfg.h,), g, eps=cfg.rms_eps)
+        sh = lambda a: a.reshape(cfg.b, cfg.s, cfg.H, cfg.d).transpose(1, 2)
+        att = F.scaled_dot_product_attention(sh(F.linear(xh, wq)), sh(F.linear(xh, wk)),
+                                             sh(F.linear(xh, wv)), is_causal=True)
+        x = xh + F.linear(att.transpose(1, 2).reshape(cfg.T, cfg.h), wo)
+    assert np.allclose(got, x.numpy(), atol=1e-11)
+
+
+def test_layer_batch_independence():
+    cfg = CONFIGS["tiny"].replace(b=3, s=6)
+    W = oracle.prepare_weights(make_weights(cfg))
+    x0 = make_x0(cfg).numpy()
+    a = oracle.layer_forward(cfg, W, x0)["x_out"].reshape(3, 6, -1)
+    b = oracle.layer_forward(cfg, W, x0[[2, 0, 1]])["x_out"].reshape(3, 6, -1)
+    assert np.allclose(b, a[[2, 0, 1]], atol=1e-13)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_prefill_then_decode_equals_longer_prefill(bf16):
+    base_cfg = CONFIGS["decode"].replace(h=64, H=4, d=16, L=4, E=16, k=2, f=16, r=16,
+                                         dtype="bf16" if bf16 else "f32")
+    s = 7
+    pre = base_cfg.replace(decode=False, b=2, s=s + 1, sa_pos=0)
+    W = oracle.prepare_weights(make_weights(pre))
+    x0 = make_x0(pre).numpy()                     # [2, s+1, h]
+    full = oracle.layer_forward(pre, W, x0)["x_out"].reshape(2, s + 1, -1)
+    short = pre.replace(s=s)
+    cap = s + 1
+    sk = np.full((short.L, 2, cap, short.H, short.d), np.nan)
+    sv = np.full_like(sk, np.nan)
+    oracle.layer_forward(short, W, x0[:, :s], sa_k=sk, sa_v=sv)
+    dec = base_cfg.replace(b=2, s=1, decode=True, sa_pos=s)
+    out = oracle.layer_forward(dec, W, x0[:, s], sa_k=sk, sa_v=sv)["x_out"]
+    # float32 storage: identical up to float64 summation order; bf16 storage: one
+    # rounding flip can move a value by a bf16 ulp, so compare at bf16 resolution
+    assert np.allclose(out, full[:, s], atol=3e-2 if bf16 else 1e-11)
+
+
+def test_decode_da_cache_overwritten_before_read():
+    cfg = CONFIGS["decode"].replace(h=64, H=4, d=16, L=3, E=8, k=2, f=8, r=16, b=2, sa_pos=3,
+                                    dtype="f32")
+    W = oracle.prepare_weights(make_weights(cfg))
+    x0 = make_x0(cfg).numpy()
+    r = np.random.default_rng(12)
+    sk = r.standard_normal((cfg.L, 2, 4, cfg.H, cfg.d))
+    sv = r.standard_normal((cfg.L, 2, 4, cfg.H, cfg.d))
+    out = oracle.layer_forward(cfg, W, x0, sa_k=sk.copy(), sa_v=sv.copy())["x_out"]
+    assert np.isfinite(out).all()   # layer_forward starts from NaN DA caches
+
+
+def test_bf16_emulation_rounds_storage_points():
+    cfg = CONFIGS["small"].replace(b=1, s=8, L=2)
+    W = oracle.prepare_weights(make_weights(cfg))
+    x0 = make_x0(cfg).numpy()
+    out = oracle.layer_forward(cfg, W, x0, return_steps=True)
+    yb = out["steps"][1]["yb"]
+    assert np.array_equal(yb, oracle.bf16_round(yb))
+    assert not np.array_equal(out["steps"][1]["y"], yb)
+
+
+def test_golden_tiny_regression():
+    """Stored oracle output of the tiny workload (written by tests/golden/make_golden.py,
+    which calls only the oracle): guards the oracle against silent drift."""
+    data = np.load(os.path.join(GOLDEN, "tiny_oracle.npz"))
+    cfg = CONFIGS["tiny"]
+    W = oracle.prepare_weights(make_weights(cfg))
+    r = oracle.layer_forward(cfg, W, make_x0(cfg).numpy())
+    assert np.allclose(r["x_out"], data["x_out"], atol=1e-12, rtol=0)
+    assert np.array_equal(r["idx"], data["idx"])
