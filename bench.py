@@ -1,0 +1,180 @@
+"""Throughput of the Dreamer layer forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload small] [--no-cpu-baseline]
+
+One step = one dreamer_layer_forward over the whole workload (all L depth steps of
+RMSNorm, projections, SA, DA, routing, permutation, expert FFNs and combine) on inputs
+already resident in HBM.  Prints one JSON line.  Inputs are seeded synthetic tensors of
+the workload's shapes (weights N(0, 0.02), tokens N(0, 1)), drawn on the device.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3       # fp32 vector
+METRIC = "token-depth-steps/sec, Dreamer layer fwd; % of HBM BW / MFMA peak"
+CLASSES = ["gemm", "seq_attn", "depth_attn", "route", "permute", "expert_ffn", "combine"]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="small")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--kernel-class", default=None, help="time this class live (default: dominant)")
+    return p.parse_args()
+
+
+def algorithmic_work(cfg, counts_per_depth):
+    """Algorithmic bytes / flops per forward for each kernel class (what the method must
+    move or compute, not what the kernels happen to move)."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    T, h, L, k, f, r, E = cfg.T, cfg.h, cfg.L, cfg.k, cfg.f, cfg.r, cfg.E
+    nq = 6 if cfg.use_da else 3
+    w = {}
+    w["gemm"] = dict(bound="mfma", flops=L * (2 * T * h * nq * h + 2 * T * (nq // 3) * h * h
+                                                + 2 * T * h * r), launches=3 * L)
+    w["seq_attn"] = dict(bound="mfma", flops=L * 4 * cfg.b * h * (cfg.s * (cfg.s + 1) // 2),
+                         launches=L)
+    da_bytes = sum(T * h * es * (6 + 2 * l) for l in range(L))
+    w["depth_attn"] = dict(bound="hbm", bytes=da_bytes, launches=L)
+    touched = sum(int((c > 0).sum()) for c in counts_per_depth)
+    nw = 3 if cfg.ffn == "swiglu" else 2
+    w["expert_ffn"] = dict(bound="hbm", bytes=touched * nw * h * f * es + L * 2 * T * k * h * es,
+                           flops=L * 2 * T * k * nw * h * f, launches=L)
+    w["combine"] = dict(bound="hbm", bytes=L * T * h * (k * es + 4 + es), launches=L + 1)
+    w["route"] = dict(bound="alu", flops=L * 2 * T * r * E, launches=L)
+    w["permute"] = dict(bound="hbm", bytes=L * T * k * 12, launches=L)
+    return w
+
+
+def roofline_entry(work, avg_ms):
+    if work["bound"] == "hbm":
+        ach = work["bytes"] / work["launches"] / (avg_ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None}
+    if work["bound"] == "mfma":
+        ach = work["flops"] / work["launches"] / (avg_ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    ach = work["flops"] / work["launches"] / (avg_ms * 1e-3) / 1e12
+    return {"bound": "alu", "achieved": round(ach, 2), "peak": PEAK_FP32_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(ach / PEAK_FP32_TFLOPS, 4), "traffic": None}
+
+
+def cpu_baseline(cfg):
+    """The CPU oracle, as it stands, on the full workload (bounded: ~10 s here)."""
+    import oracle
+    from synth import make_weights, make_x0
+    from threadpoolctl import threadpool_info
+    W = oracle.prepare_weights(make_weights(cfg), big_as_f32=True)
+    x0 = make_x0(cfg).reshape(cfg.T, cfg.h).numpy()
+    t0 = time.perf_counter()
+    oracle.layer_forward(cfg, W, x0)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(cfg.T * cfg.L / dt, 2), "unit": "token-depth-steps/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"full {cfg.name} workload (b={cfg.b}, s={cfg.s}, L={cfg.L}), one forward, "
+                      f"{dt:.1f} s, float64 numpy with bf16 storage emulation"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from depth_recurrent_layer_amd import dreamer as D
+    from synth import CONFIGS, make_weights, make_x0
+
+    cfg = CONFIGS[args.workload]
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    W = make_weights(cfg, device=dev)
+    G = {k: v.contiguous() for k, v in W.items()}
+    if cfg.proj_experts:
+        G["w_qkv"] = D.dreamer_absorb_shared(G.pop("w_qkv_e"), G.pop("w_qkv_sh"))
+        G["w_o"] = D.dreamer_absorb_shared(G.pop("w_o_e"), G.pop("w_o_sh"))
+    x0 = make_x0(cfg, device=dev).reshape(cfg.T, cfg.h).contiguous()
+    lc = D.make_layer_cfg(dtype=cfg.dtype, b=cfg.b, s=cfg.s, h=cfg.h, H=cfg.H, d=cfg.d, L=cfg.L,
+                          E=cfg.E, k=cfg.k, f=cfg.f, r=cfg.r, ffn=cfg.ffn,
+                          normalize=cfg.normalize, proj_experts=cfg.proj_experts,
+                          rope_base=cfg.rope_base, rms_eps=cfg.rms_eps, rho=cfg.rho)
+    ws = torch.empty(D.layer_ws_bytes(lc), dtype=torch.uint8, device=dev)
+    x_out = torch.empty((cfg.T, cfg.h), dtype=torch.float32, device=dev)
+    route = (torch.empty((cfg.L, cfg.T, cfg.k), dtype=torch.int32, device=dev),
+             torch.empty((cfg.L, cfg.T, cfg.k), dtype=torch.float32, device=dev))
+
+    def step(with_route=False):
+        D.dreamer_layer_forward(lc, G, x0, x_out=x_out, ws=ws,
+                                route=route if with_route else None)
+
+    step(with_route=True)
+    torch.cuda.synchronize()
+    counts = [np.bincount(route[0][l].cpu().numpy().reshape(-1), minlength=cfg.E)
+              for l in range(cfg.L)]
+    work = algorithmic_work(cfg, counts)
+    for _ in range(args.warmup):
+        step()
+    # dominant kernel class: one instrumented forward per class (untimed)
+    per_class = {}
+    for kc in CLASSES:
+        D.timing_enable(kc, 4 * cfg.L + 8)
+        step()
+        n, ms = D.timing_read()
+        D.timing_disable()
+        per_class[kc] = (n, ms)
+    dom = args.kernel_class or max(per_class, key=lambda c: per_class[c][1])
+    if dom not in work or ("bytes" not in work[dom] and "flops" not in work[dom]):
+        dom = "expert_ffn"
+
+    # timed region: K forwards, the dominant class bracketed by HIP events on its stream
+    D.timing_enable(dom, args.steps * work[dom]["launches"] + 8)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    n_launch, dom_ms = D.timing_read()
+    D.timing_disable()
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = cfg.T * cfg.L * args.steps / elapsed
+    roof = roofline_entry(work[dom], dom_ms / max(n_launch, 1))
+    roof["kernel"] = dom
+    roof["launches_timed"] = n_launch
+    roof["avg_launch_us"] = round(dom_ms / max(n_launch, 1) * 1e3, 2)
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "token-depth-steps/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.dtype} Dreamer layer forward b={cfg.b} s={cfg.s} "
+                               f"h={cfg.h} heads={cfg.H}x{cfg.d} L={cfg.L} E={cfg.E} top-{cfg.k} "
+                               f"{cfg.ffn} f={cfg.f} r={cfg.r}",
+                   "tokens": cfg.T, "depths": cfg.L, "parallelism": "single GPU"},
+        "roofline": roof,
+        "kernel_ms_per_step": {c: round(per_class[c][1], 4) for c in CLASSES},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,683 @@
+// C ABI of libdreamer (declared in include/dreamer.h): argument validation, workspace
+// planning and the depth loop of the layer forward.  All device work is enqueued on the
+// caller's stream through the launchers in kernels.h.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/dreamer.h"
+#include "kernels.h"
+
+using namespace dreamer;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = 0;
+  return DREAMER_OK;
+}
+
+// Checks the launch queue after enqueuing kernels.
+int check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(DREAMER_E_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+size_t esize(int dtype) { return dtype == DREAMER_BF16 ? 2 : 4; }
+
+bool dtype_ok(int dtype) { return dtype == DREAMER_F32 || dtype == DREAMER_BF16; }
+
+// Bump allocator over the caller's workspace (base == nullptr: size planning only).
+struct Bump {
+  char* base;
+  size_t off = 0;
+  explicit Bump(void* b) : base((char*)b) {}
+  void* take(size_t bytes) {
+    off = (off + 255) & ~(size_t)255;
+    void* p = base ? base + off : nullptr;
+    off += bytes;
+    return p;
+  }
+  template <typename T>
+  T* take_n(size_t n) { return (T*)take(n * sizeof(T)); }
+};
+
+hipStream_t S(dreamer_stream_t s) { return (hipStream_t)s; }
+
+// ---------------------------------------------------------------------------- timing
+struct Timing {
+  int kclass = 0;
+  int max = 0;
+  int n = 0;
+  std::vector<hipEvent_t> ev0, ev1;
+} g_tm;
+
+}  // namespace
+
+namespace dreamer {
+void timing_begin(int kclass, hipStream_t st) {
+  if (g_tm.kclass == kclass && g_tm.n < g_tm.max) (void)hipEventRecord(g_tm.ev0[g_tm.n], st);
+}
+void timing_end(int kclass, hipStream_t st) {
+  if (g_tm.kclass == kclass && g_tm.n < g_tm.max) {
+    (void)hipEventRecord(g_tm.ev1[g_tm.n], st);
+    ++g_tm.n;
+  }
+}
+}  // namespace dreamer
+
+#define TB(kc) timing_begin(kc, st)
+#define TE(kc) timing_end(kc, st)
+
+extern "C" {
+
+const char* dreamer_last_error(void) { return g_err; }
+
+int dreamer_version(void) { return 100; }
+
+int dreamer_timing_enable(int kclass, int max_launches) {
+  dreamer_timing_disable();
+  if (kclass < DREAMER_KC_GEMM || kclass > DREAMER_KC_COMBINE || max_launches <= 0)
+    return fail(DREAMER_E_INVAL, "timing_enable: bad class or count");
+  g_tm.ev0.resize(max_launches);
+  g_tm.ev1.resize(max_launches);
+  for (int i = 0; i < max_launches; ++i) {
+    if (hipEventCreate(&g_tm.ev0[i]) != hipSuccess || hipEventCreate(&g_tm.ev1[i]) != hipSuccess)
+      return fail(DREAMER_E_HIP, "timing_enable: hipEventCreate failed");
+  }
+  g_tm.max = max_launches;
+  g_tm.n = 0;
+  g_tm.kclass = kclass;
+  return ok();
+}
+
+int dreamer_timing_read(int* n_launches, double* total_ms) {
+  double tot = 0.0;
+  for (int i = 0; i < g_tm.n; ++i) {
+    if (hipEventSynchronize(g_tm.ev1[i]) != hipSuccess)
+      return fail(DREAMER_E_HIP, "timing_read: event sync failed");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, g_tm.ev0[i], g_tm.ev1[i]) != hipSuccess)
+      return fail(DREAMER_E_HIP, "timing_read: elapsed time failed");
+    tot += ms;
+  }
+  if (n_launches) *n_launches = g_tm.n;
+  if (total_ms) *total_ms = tot;
+  return ok();
+}
+
+int dreamer_timing_disable(void) {
+  for (auto e : g_tm.ev0) (void)hipEventDestroy(e);
+  for (auto e : g_tm.ev1) (void)hipEventDestroy(e);
+  g_tm.ev0.clear();
+  g_tm.ev1.clear();
+  g_tm.kclass = 0;
+  g_tm.max = g_tm.n = 0;
+  return ok();
+}
+
+int dreamer_rope_tables(int D, int npos, double base, float* cos_out, float* sin_out,
+                        dreamer_stream_t stream) {
+  if (D <= 0 || D % 2 || npos < 0 || !(base > 0.0)) return fail(DREAMER_E_INVAL, "rope_tables: bad D/npos/base");
+  if (npos > 0 && (!cos_out || !sin_out)) return fail(DREAMER_E_INVAL, "rope_tables: null output");
+  launch_rope_tables(D, npos, base, cos_out, sin_out, S(stream));
+  return check_launch("rope_tables");
+}
+
+int dreamer_depth_attn(int dtype, int64_t rows, int H, int d, int l, int L, const void* q,
+                       const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                       void* out, const float* cos_d, const float* sin_d, float scale,
+                       dreamer_stream_t stream) {
+  if (!dtype_ok(dtype)) return fail(DREAMER_E_INVAL, "depth_attn: bad dtype");
+  if (rows < 0 || H <= 0 || d <= 0 || L <= 0 || l < 0 || l >= L)
+    return fail(DREAMER_E_INVAL, "depth_attn: bad sizes (rows=%lld H=%d d=%d l=%d L=%d)",
+                (long long)rows, H, d, l, L);
+  if (rows == 0) return ok();
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !out || !cos_d || !sin_d)
+    return fail(DREAMER_E_INVAL, "depth_attn: null pointer");
+  const int vec = dtype == DREAMER_BF16 ? 8 : 4;
+  if (d % (2 * vec) || (d / vec) > 64 || ((d / vec) & (d / vec - 1)))
+    return fail(DREAMER_E_UNSUPPORTED, "depth_attn: head dim %d unsupported", d);
+  const int64_t h = (int64_t)H * d;
+  hipStream_t st = S(stream);
+  TB(DREAMER_KC_DEPTH_ATTN);
+  int rc = launch_depth_attn(dtype, rows, H, d, l, L, q, h, k_new, h, v_new, h, k_cache,
+                             v_cache, out, h, cos_d, sin_d, scale, st);
+  TE(DREAMER_KC_DEPTH_ATTN);
+  if (rc) return fail(DREAMER_E_UNSUPPORTED, "depth_attn: head dim %d unsupported", d);
+  return check_launch("depth_attn");
+}
+
+size_t dreamer_seq_attn_ws_bytes(int dtype, int B, int q_len, int H, int d, int64_t pos0) {
+  return seq_attn_ws(dtype, B, q_len, H, d, pos0);
+}
+
+static int validate_seq(int dtype, int B, int q_len, int H, int d, int64_t pos0, int64_t cap,
+                        bool has_cache) {
+  if (!dtype_ok(dtype)) return fail(DREAMER_E_INVAL, "seq_attn: bad dtype");
+  if (B < 0 || q_len < 0 || H <= 0 || d <= 0 || pos0 < 0)
+    return fail(DREAMER_E_INVAL, "seq_attn: bad sizes");
+  const int vec = dtype == DREAMER_BF16 ? 8 : 4;
+  if (d % (2 * vec) || (d / vec) > 16 || ((d / vec) & (d / vec - 1)))
+    return fail(DREAMER_E_UNSUPPORTED, "seq_attn: head dim %d unsupported", d);
+  if ((int64_t)H * d / vec > 1024) return fail(DREAMER_E_UNSUPPORTED, "seq_attn: hidden too large");
+  if (pos0 > 0) {
+    if (q_len != 1) return fail(DREAMER_E_UNSUPPORTED, "seq_attn: decode needs q_len == 1");
+    if (!has_cache) return fail(DREAMER_E_INVAL, "seq_attn: decode needs k_cache/v_cache");
+    if (cap <= pos0) return fail(DREAMER_E_INVAL, "seq_attn: cap must exceed pos0");
+  } else if (has_cache && cap < q_len) {
+    return fail(DREAMER_E_INVAL, "seq_attn: cap < q_len");
+  }
+  return ok();
+}
+
+int dreamer_seq_attn(int dtype, int B, int q_len, int H, int d, int64_t pos0, const void* q,
+                     const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                     int64_t cap, void* out, const float* cos_s, const float* sin_s,
+                     float scale, int sa_rope, void* ws, size_t ws_bytes,
+                     dreamer_stream_t stream) {
+  int rc = validate_seq(dtype, B, q_len, H, d, pos0, cap, k_cache && v_cache);
+  if (rc) return rc;
+  if (B == 0 || q_len == 0) return ok();
+  if (!q || !k_new || !v_new || !out) return fail(DREAMER_E_INVAL, "seq_attn: null pointer");
+  if (sa_rope && (!cos_s || !sin_s)) return fail(DREAMER_E_INVAL, "seq_attn: null rope table");
+  const size_t need = seq_attn_ws(dtype, B, q_len, H, d, pos0);
+  if (ws_bytes < need || (need && !ws))
+    return fail(DREAMER_E_WORKSPACE, "seq_attn: workspace %zu < %zu", ws_bytes, need);
+  const int64_t h = (int64_t)H * d;
+  hipStream_t st = S(stream);
+  TB(DREAMER_KC_SEQ_ATTN);
+  rc = launch_seq_attn(dtype, B, q_len, H, d, pos0, q, h, k_new, h, v_new, h, k_cache,
+                       v_cache, cap, out, h, cos_s, sin_s, scale, sa_rope, ws, ws_bytes, st);
+  TE(DREAMER_KC_SEQ_ATTN);
+  if (rc) return fail(DREAMER_E_UNSUPPORTED, "seq_attn: unsupported shape (%d)", rc);
+  return check_launch("seq_attn");
+}
+
+static int validate_route(int dtype, int64_t T, int h, int r, int E, int k, int l, int L) {
+  if (!dtype_ok(dtype)) return fail(DREAMER_E_INVAL, "expert_route: bad dtype");
+  if (T < 0 || h <= 0 || r <= 0 || E <= 0 || k <= 0 || L <= 0 || l < 0 || l >= L)
+    return fail(DREAMER_E_INVAL, "expert_route: bad sizes");
+  if (k > E || k > 32) return fail(DREAMER_E_UNSUPPORTED, "expert_route: k=%d (E=%d) unsupported", k, E);
+  if (r % 8) return fail(DREAMER_E_UNSUPPORTED, "expert_route: r %% 8 != 0");
+  if (E > 16384) return fail(DREAMER_E_UNSUPPORTED, "expert_route: E > 16384");
+  if (dtype == DREAMER_BF16 && h % 64) return fail(DREAMER_E_UNSUPPORTED, "expert_route: h %% 64 != 0");
+  return ok();
+}
+
+size_t dreamer_expert_route_ws_bytes(int64_t T, int r, int E) {
+  (void)E;
+  return (size_t)(T > 0 ? T : 0) * (r > 0 ? r : 0) * 4 + 256;
+}
+
+// u = x W_r^T (f32), then the routing kernel.  counts must be zeroed by the caller of
+// this helper when accumulation from zero is wanted.
+static int route_impl(int dtype, int64_t T, int h, int r, int E, int k, int l, int L,
+                      const void* x, int64_t ldx, const void* w_r, const void* keys,
+                      const float* bias, float rho, int normalize, const float* cos_r,
+                      const float* sin_r, int32_t* idx, float* gate, int32_t* counts,
+                      float* u, hipStream_t st, const int32_t* idx_in = nullptr) {
+  GemmArgs ga;
+  ga.M = (int)T;
+  ga.N = r;
+  ga.K = h;
+  ga.A = x;
+  ga.lda = ldx;
+  ga.B = w_r;
+  ga.ldb = h;
+  ga.C = u;
+  ga.ldc = r;
+  TB(DREAMER_KC_GEMM);
+  int rc = launch_gemm(ga, dtype, 1, st);
+  TE(DREAMER_KC_GEMM);
+  if (rc) return fail(DREAMER_E_UNSUPPORTED, "router projection: unsupported shape");
+  TB(DREAMER_KC_ROUTE);
+  rc = launch_route(dtype, T, r, E, k, l, L, u, keys, bias, rho, normalize, cos_r, sin_r, idx,
+                    gate, counts, idx_in, st);
+  TE(DREAMER_KC_ROUTE);
+  if (rc) return fail(DREAMER_E_UNSUPPORTED, "expert_route: unsupported shape");
+  return ok();
+}
+
+int dreamer_expert_route(int dtype, int64_t T, int h, int r, int E, int k, int l, int L,
+                         const void* x, const void* w_r, const void* keys, const float* bias,
+                         float rho, int normalize, const float* cos_r, const float* sin_r,
+                         int32_t* idx, float* gate, int32_t* counts, void* ws,
+                         size_t ws_bytes, dreamer_stream_t stream) {
+  int rc = validate_route(dtype, T, h, r, E, k, l, L);
+  if (rc) return rc;
+  if (T == 0) return ok();
+  if (!x || !w_r || !keys || !bias || !cos_r || !sin_r || !idx || !gate)
+    return fail(DREAMER_E_INVAL, "expert_route: null pointer");
+  const size_t need = dreamer_expert_route_ws_bytes(T, r, E);
+  if (!ws || ws_bytes < need) return fail(DREAMER_E_WORKSPACE, "expert_route: workspace %zu < %zu", ws_bytes, need);
+  hipStream_t st = S(stream);
+  if (counts) launch_fill_i32(counts, E, 0, st);
+  rc = route_impl(dtype, T, h, r, E, k, l, L, x, h, w_r, keys, bias, rho, normalize, cos_r,
+                  sin_r, idx, gate, counts, (float*)ws, st);
+  if (rc) return rc;
+  return check_launch("expert_route");
+}
+
+// ------------------------------------------------------------------------ expert FFN
+struct FfnWs {
+  int32_t *counts, *goff, *toff, *cursor, *perm;
+  void* slots;
+};
+
+static FfnWs plan_ffn(Bump& b, int dtype, int64_t T, int h_out, int E, int k) {
+  FfnWs w;
+  w.counts = b.take_n<int32_t>(E);
+  w.goff = b.take_n<int32_t>(E + 1);
+  w.toff = b.take_n<int32_t>(E + 1);
+  w.cursor = b.take_n<int32_t>(E);
+  w.perm = b.take_n<int32_t>((size_t)T * k);
+  w.slots = b.take((size_t)T * k * h_out * esize(dtype));
+  return w;
+}
+
+size_t dreamer_expert_ffn_ws_bytes(int dtype, int kind, int64_t T, int h_in, int f,
+                                   int h_out, int E, int k) {
+  (void)kind; (void)h_in; (void)f;
+  if (T < 0 || E <= 0 || k <= 0 || h_out <= 0) return 0;
+  Bump b(nullptr);
+  plan_ffn(b, dtype, T, h_out, E, k);
+  return b.off + 256;
+}
+
+// Routed slots for (idx, gate): slots[t*k+i] = gate * FFN_idx(x[t]).  bf16 groups the
+// slots by expert first (histogram unless the counts are already there, scan, scatter).
+static int ffn_slots(int dtype, int kind, int64_t T, int h_in, int f, int h_out, int E, int k,
+                     const void* x, const int32_t* idx, const float* gate, const void* w1,
+                     const void* w3, const void* w2, const FfnWs& w, bool have_counts,
+                     hipStream_t st) {
+  const int64_t ns = T * k;
+  if (dtype == DREAMER_F32) {
+    TB(DREAMER_KC_EXPERT_FFN);
+    int rc = launch_expert_ffn_f32(kind, ns, k, h_in, f, h_out, (const float*)x, idx, gate,
+                                   (const float*)w1, (const float*)w3, (const float*)w2,
+                                   (float*)w.slots, st);
+    TE(DREAMER_KC_EXPERT_FFN);
+    return rc ? fail(DREAMER_E_UNSUPPORTED, "expert_ffn: f32 shape unsupported") : ok();
+  }
+  TB(DREAMER_KC_PERMUTE);
+  if (!have_counts) {
+    launch_fill_i32(w.counts, E, 0, st);
+    launch_moe_histogram(idx, ns, w.counts, st);
+  }
+  launch_moe_scan(w.counts, E, FFN_TILE_M, w.goff, w.toff, w.cursor, st);
+  launch_moe_scatter(idx, ns, w.goff, w.cursor, w.perm, st);
+  TE(DREAMER_KC_PERMUTE);
+  int rc;
+  if (kind == DREAMER_FFN_LINEAR) {
+    GemmArgs ga;
+    ga.M = (int)ns;
+    ga.N = h_out;
+    ga.K = h_in;
+    ga.A = x;
+    ga.lda = h_in;
+    ga.B = w1;
+    ga.ldb = h_in;
+    ga.b_gstride = (int64_t)h_out * h_in;
+    ga.rows = w.perm;
+    ga.row_div = k;
+    ga.row_scale = gate;
+    ga.goff = w.goff;
+    ga.toff = w.toff;
+    ga.G = E;
+    ga.tile_m = FFN_TILE_M;
+    ga.C = w.slots;
+    ga.ldc = h_out;
+    TB(DREAMER_KC_EXPERT_FFN);
+    rc = launch_gemm(ga, dtype, 0, st);
+    TE(DREAMER_KC_EXPERT_FFN);
+  } else {
+    TB(DREAMER_KC_EXPERT_FFN);
+    rc = launch_expert_ffn(dtype, kind, ns, k, h_in, f, h_out, E, x, gate, w1, w3, w2, w.perm,
+                           w.goff, w.toff, w.slots, st);
+    TE(DREAMER_KC_EXPERT_FFN);
+  }
+  return rc ? fail(DREAMER_E_UNSUPPORTED, "expert_ffn: shape unsupported (f=%d h_in=%d h_out=%d)",
+                   f, h_in, h_out)
+            : ok();
+}
+
+static int validate_ffn(int dtype, int kind, int64_t T, int h_in, int f, int h_out, int E,
+                        int k) {
+  if (!dtype_ok(dtype)) return fail(DREAMER_E_INVAL, "expert_ffn: bad dtype");
+  if (kind < DREAMER_FFN_GELU || kind > DREAMER_FFN_LINEAR) return fail(DREAMER_E_INVAL, "expert_ffn: bad kind");
+  if (T < 0 || h_in <= 0 || h_out <= 0 || E <= 0 || k <= 0 || (kind != DREAMER_FFN_LINEAR && f <= 0))
+    return fail(DREAMER_E_INVAL, "expert_ffn: bad sizes");
+  if (h_out > 4096) return fail(DREAMER_E_UNSUPPORTED, "expert_ffn: h_out > 4096");
+  if (T * k > INT32_MAX / 2) return fail(DREAMER_E_UNSUPPORTED, "expert_ffn: too many slots");
+  if (dtype == DREAMER_BF16) {
+    if (h_in % 64 || h_out % 64) return fail(DREAMER_E_UNSUPPORTED, "expert_ffn: bf16 needs h %% 64 == 0");
+    if (kind != DREAMER_FFN_LINEAR && f != 64 && f != 128)
+      return fail(DREAMER_E_UNSUPPORTED, "expert_ffn: bf16 needs f in {64, 128}");
+  } else if (kind != DREAMER_FFN_LINEAR && f > 16384) {
+    return fail(DREAMER_E_UNSUPPORTED, "expert_ffn: f too large");
+  }
+  return ok();
+}
+
+int dreamer_expert_ffn(int dtype, int kind, int64_t T, int h_in, int f, int h_out, int E,
+                       int k, const void* x, const int32_t* idx, const float* gate,
+                       const void* w1, const void* w3, const void* w2, const float* residual,
+                       float* out, void* ws, size_t ws_bytes, dreamer_stream_t stream) {
+  int rc = validate_ffn(dtype, kind, T, h_in, f, h_out, E, k);
+  if (rc) return rc;
+  if (T == 0) return ok();
+  if (!x || !idx || !gate || !w1 || !out || (kind == DREAMER_FFN_SWIGLU && !w3) ||
+      (kind != DREAMER_FFN_LINEAR && !w2))
+    return fail(DREAMER_E_INVAL, "expert_ffn: null pointer");
+  const size_t need = dreamer_expert_ffn_ws_bytes(dtype, kind, T, h_in, f, h_out, E, k);
+  if (!ws || ws_bytes < need) return fail(DREAMER_E_WORKSPACE, "expert_ffn: workspace %zu < %zu", ws_bytes, need);
+  hipStream_t st = S(stream);
+  Bump b(ws);
+  FfnWs w = plan_ffn(b, dtype, T, h_out, E, k);
+  rc = ffn_slots(dtype, kind, T, h_in, f, h_out, E, k, x, idx, gate, w1, w3, w2, w, false, st);
+  if (rc) return rc;
+  TB(DREAMER_KC_COMBINE);
+  launch_combine_norm(dtype, T, h_out, k, residual, w.slots, out, nullptr, nullptr, 0.f,
+                      nullptr, nullptr, st);
+  TE(DREAMER_KC_COMBINE);
+  return check_launch("expert_ffn");
+}
+
+int dreamer_absorb_shared(int dtype, int64_t n_experts, int64_t n, const void* w_e,
+                          const void* w_shared, void* out, dreamer_stream_t stream) {
+  if (!dtype_ok(dtype) || n_experts < 0 || n < 0) return fail(DREAMER_E_INVAL, "absorb_shared: bad args");
+  if (n_experts * n == 0) return ok();
+  if (!w_e || !w_shared || !out) return fail(DREAMER_E_INVAL, "absorb_shared: null pointer");
+  launch_absorb(dtype, n_experts, n, w_e, w_shared, out, S(stream));
+  return check_launch("absorb_shared");
+}
+
+// ------------------------------------------------------------------------------ layer
+struct LayerWs {
+  float *cos_s, *sin_s, *cos_d, *sin_d, *cos_r, *sin_r;
+  void *xh, *qkv, *att, *yb;
+  float* xh32;  // float32 copy of xhat for the residual (bf16 storage only)
+  float *y, *u, *rgate, *pgate, *zero_pbias;
+  int32_t *ridx, *pidx;
+  FfnWs ffn;
+  int32_t *pcounts, *pgoff, *ptoff, *pcursor, *pperm;
+  void *da_k, *da_v, *sa_ws;
+  size_t sa_ws_bytes;
+};
+
+static int64_t sa_npos(const dreamer_layer_cfg* c) { return c->decode ? c->sa_pos + 1 : c->s; }
+
+static LayerWs plan_layer(Bump& b, const dreamer_layer_cfg* c, bool need_yb, bool need_route,
+                          bool need_proj_route, bool need_da) {
+  LayerWs w{};
+  const int64_t T = (int64_t)c->b * c->s;
+  const size_t es = esize(c->dtype);
+  const int64_t h = c->h;
+  const int64_t npos = sa_npos(c);
+  w.cos_s = b.take_n<float>(npos * (c->d / 2));
+  w.sin_s = b.take_n<float>(npos * (c->d / 2));
+  w.cos_d = b.take_n<float>((size_t)c->L * (c->d / 2));
+  w.sin_d = b.take_n<float>((size_t)c->L * (c->d / 2));
+  w.cos_r = b.take_n<float>((size_t)c->L * (c->r / 2));
+  w.sin_r = b.take_n<float>((size_t)c->L * (c->r / 2));
+  w.xh = b.take(T * h * es);
+  w.xh32 = c->dtype == DREAMER_BF16 ? b.take_n<float>(T * h) : nullptr;
+  w.qkv = b.take(T * 6 * h * es);
+  w.att = b.take(T * 2 * h * es);
+  w.y = b.take_n<float>(T * h);
+  w.yb = need_yb ? b.take(T * h * es) : nullptr;
+  w.u = b.take_n<float>(T * c->r);
+  if (c->use_ea) {
+    if (need_route) {
+      w.ridx = b.take_n<int32_t>(T * c->k);
+      w.rgate = b.take_n<float>(T * c->k);
+    }
+    w.ffn = plan_ffn(b, c->dtype, T, c->h, c->E, c->k);
+  }
+  if (c->proj_experts) {
+    const int Ep = c->proj_experts;
+    if (need_proj_route) {
+      w.pidx = b.take_n<int32_t>(T);
+      w.pgate = b.take_n<float>(T);
+    }
+    w.zero_pbias = b.take_n<float>(Ep);
+    w.pcounts = b.take_n<int32_t>(Ep);
+    w.pgoff = b.take_n<int32_t>(Ep + 1);
+    w.ptoff = b.take_n<int32_t>(Ep + 1);
+    w.pcursor = b.take_n<int32_t>(Ep);
+    w.pperm = b.take_n<int32_t>(T);
+  }
+  if (need_da) {
+    w.da_k = b.take(T * c->L * h * es);
+    w.da_v = b.take(T * c->L * h * es);
+  }
+  w.sa_ws_bytes = seq_attn_ws(c->dtype, c->b, c->s, c->H, c->d, c->decode ? c->sa_pos : 0);
+  w.sa_ws = w.sa_ws_bytes ? b.take(w.sa_ws_bytes) : nullptr;
+  return w;
+}
+
+static int validate_layer(const dreamer_layer_cfg* c, const dreamer_layer_weights* w) {
+  if (!c || !w) return fail(DREAMER_E_INVAL, "layer: null cfg or weights");
+  if (!dtype_ok(c->dtype)) return fail(DREAMER_E_INVAL, "layer: bad dtype");
+  if (c->b <= 0 || c->s <= 0 || c->h <= 0 || c->H <= 0 || c->d <= 0 || c->L <= 0 || c->r <= 0)
+    return fail(DREAMER_E_INVAL, "layer: non-positive size");
+  if ((int64_t)c->H * c->d != c->h) return fail(DREAMER_E_INVAL, "layer: h != H * d");
+  if (c->mixture != DREAMER_MIX_PARTIAL) return fail(DREAMER_E_UNSUPPORTED, "layer: mixture %d", c->mixture);
+  if (c->decode && (c->s != 1 || c->sa_pos <= 0 || c->sa_cap <= c->sa_pos))
+    return fail(DREAMER_E_INVAL, "layer: decode needs s == 1, sa_pos > 0, sa_cap > sa_pos");
+  if (!c->decode && c->sa_cap < 0) return fail(DREAMER_E_INVAL, "layer: bad sa_cap");
+  if (c->h > 4096) return fail(DREAMER_E_UNSUPPORTED, "layer: h > 4096");
+  if ((int64_t)c->b * c->s * 6 * c->h > INT32_MAX) return fail(DREAMER_E_UNSUPPORTED, "layer: T * 6h too large");
+  if (c->r % 8) return fail(DREAMER_E_UNSUPPORTED, "layer: r %% 8 != 0");
+  int rc = validate_seq(c->dtype, c->b, c->s, c->H, c->d, c->decode ? c->sa_pos : 0,
+                        c->sa_cap, c->decode != 0);
+  if (rc) return rc;
+  if (c->use_ea) {
+    rc = validate_route(c->dtype, (int64_t)c->b * c->s, c->h, c->r, c->E, c->k, 0, c->L);
+    if (rc) return rc;
+    if (c->ffn_kind != DREAMER_FFN_GELU && c->ffn_kind != DREAMER_FFN_SWIGLU)
+      return fail(DREAMER_E_INVAL, "layer: ffn_kind must be GELU or SWIGLU");
+    rc = validate_ffn(c->dtype, c->ffn_kind, (int64_t)c->b * c->s, c->h, c->f, c->h, c->E, c->k);
+    if (rc) return rc;
+    if (!w->w_r || !w->keys || !w->bias || !w->w1 || !w->w2 ||
+        (c->ffn_kind == DREAMER_FFN_SWIGLU && !w->w3))
+      return fail(DREAMER_E_INVAL, "layer: null expert weights");
+  }
+  if (c->proj_experts) {
+    rc = validate_route(c->dtype, (int64_t)c->b * c->s, c->h, c->r, c->proj_experts, 1, 0, c->L);
+    if (rc) return rc;
+    if (!w->w_pr || !w->pkeys) return fail(DREAMER_E_INVAL, "layer: null projection router");
+  }
+  if (c->dtype == DREAMER_BF16 && c->h % 64) return fail(DREAMER_E_UNSUPPORTED, "layer: h %% 64 != 0");
+  if (!w->g || !w->w_qkv || !w->w_o) return fail(DREAMER_E_INVAL, "layer: null projection weights");
+  if (!(c->rope_base > 0.0)) return fail(DREAMER_E_INVAL, "layer: rope_base must be > 0");
+  return ok();
+}
+
+size_t dreamer_layer_ws_bytes(const dreamer_layer_cfg* cfg) {
+  if (!cfg || cfg->b <= 0 || cfg->s <= 0 || cfg->h <= 0 || cfg->d <= 0 || cfg->L <= 0) return 0;
+  Bump b(nullptr);
+  plan_layer(b, cfg, true, true, true, true);
+  return b.off + 256;
+}
+
+int dreamer_layer_forward(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* w,
+                          const float* x_in, float* x_out, int32_t* route_idx,
+                          float* route_gate, int32_t* proj_idx, float* proj_gate,
+                          float* x_steps, void* y_steps, void* da_k, void* da_v, void* sa_k,
+                          void* sa_v, const int32_t* route_in, const int32_t* proj_route_in,
+                          void* ws, size_t ws_bytes, dreamer_stream_t stream) {
+  int rc = validate_layer(cfg, w);
+  if (rc) return rc;
+  const dreamer_layer_cfg& c = *cfg;
+  if (!x_in || !x_out) return fail(DREAMER_E_INVAL, "layer: null x_in / x_out");
+  if (c.decode && (!sa_k || !sa_v)) return fail(DREAMER_E_INVAL, "layer: decode needs sa_k / sa_v");
+  if ((da_k == nullptr) != (da_v == nullptr)) return fail(DREAMER_E_INVAL, "layer: da_k / da_v must both be given");
+  if ((sa_k == nullptr) != (sa_v == nullptr)) return fail(DREAMER_E_INVAL, "layer: sa_k / sa_v must both be given");
+  if ((route_idx == nullptr) != (route_gate == nullptr) ||
+      (proj_idx == nullptr) != (proj_gate == nullptr))
+    return fail(DREAMER_E_INVAL, "layer: routing outputs must come in (idx, gate) pairs");
+  if (sa_k && !c.decode && c.sa_cap < c.s) return fail(DREAMER_E_INVAL, "layer: sa_cap < s");
+  const size_t need = dreamer_layer_ws_bytes(cfg);
+  if (!ws || ws_bytes < need) return fail(DREAMER_E_WORKSPACE, "layer: workspace %zu < %zu", ws_bytes, need);
+
+  hipStream_t st = S(stream);
+  Bump b(ws);
+  LayerWs lw = plan_layer(b, cfg, y_steps == nullptr, route_idx == nullptr,
+                          proj_idx == nullptr, da_k == nullptr);
+  const int dt = c.dtype;
+  const size_t es = esize(dt);
+  const int64_t T = (int64_t)c.b * c.s, h = c.h;
+  const int L = c.L, k = c.k;
+  const float scale = 1.0f / sqrtf((float)c.d);
+  void* DAk = da_k ? da_k : lw.da_k;
+  void* DAv = da_v ? da_v : lw.da_v;
+  const int64_t cap = sa_k ? c.sa_cap : 0;
+  const int64_t pos0 = c.decode ? c.sa_pos : 0;
+
+  launch_rope_tables(c.d, (int)sa_npos(cfg), c.rope_base, lw.cos_s, lw.sin_s, st);
+  launch_rope_tables(c.d, L, c.rope_base, lw.cos_d, lw.sin_d, st);
+  launch_rope_tables(c.r, L, c.rope_base, lw.cos_r, lw.sin_r, st);
+  if (c.proj_experts) launch_fill_i32((int32_t*)lw.zero_pbias, c.proj_experts, 0, st);
+  TB(DREAMER_KC_COMBINE);
+  launch_rmsnorm(dt, T, c.h, x_in, w->g, c.rms_eps, lw.xh, lw.xh32, st);
+  const float* resid = lw.xh32 ? lw.xh32 : (const float*)lw.xh;
+  TE(DREAMER_KC_COMBINE);
+
+  const int nqkv = c.use_da ? 6 : 3;
+  for (int l = 0; l < L; ++l) {
+    int32_t* pidx = nullptr;
+    float* pgate = nullptr;
+    // ---- Q/K/V projections (dense, or the top-1 linear MoE sharing one router score)
+    GemmArgs gq;
+    gq.M = (int)T;
+    gq.N = nqkv * (int)h;
+    gq.K = (int)h;
+    gq.A = lw.xh;
+    gq.lda = h;
+    gq.B = w->w_qkv;
+    gq.ldb = h;
+    gq.C = lw.qkv;
+    gq.ldc = 6 * h;
+    if (c.proj_experts) {
+      const int Ep = c.proj_experts;
+      pidx = proj_idx ? proj_idx + (int64_t)l * T : lw.pidx;
+      pgate = proj_gate ? proj_gate + (int64_t)l * T : lw.pgate;
+      launch_fill_i32(lw.pcounts, Ep, 0, st);
+      rc = route_impl(dt, T, c.h, c.r, Ep, 1, l, L, lw.xh, h, w->w_pr, w->pkeys,
+                      w->pbias ? w->pbias : lw.zero_pbias, c.rho, 0, lw.cos_r, lw.sin_r, pidx,
+                      pgate, lw.pcounts, lw.u, st,
+                      proj_route_in ? proj_route_in + (int64_t)l * T : nullptr);
+      if (rc) return rc;
+      TB(DREAMER_KC_PERMUTE);
+      launch_moe_scan(lw.pcounts, Ep, 64, lw.pgoff, lw.ptoff, lw.pcursor, st);
+      launch_moe_scatter(pidx, T, lw.pgoff, lw.pcursor, lw.pperm, st);
+      TE(DREAMER_KC_PERMUTE);
+      gq.b_gstride = 6 * h * h;
+      gq.rows = lw.pperm;
+      gq.row_scale = pgate;
+      gq.goff = lw.pgoff;
+      gq.toff = lw.ptoff;
+      gq.G = Ep;
+      gq.tile_m = 64;
+    }
+    TB(DREAMER_KC_GEMM);
+    rc = launch_gemm(gq, dt, 0, st);
+    TE(DREAMER_KC_GEMM);
+    if (rc) return fail(DREAMER_E_UNSUPPORTED, "layer: QKV projection shape");
+    char* qkv = (char*)lw.qkv;
+    char* att = (char*)lw.att;
+    // ---- SA at depth l
+    void* sk = sa_k ? (char*)sa_k + (size_t)l * c.b * cap * h * es : nullptr;
+    void* sv = sa_v ? (char*)sa_v + (size_t)l * c.b * cap * h * es : nullptr;
+    TB(DREAMER_KC_SEQ_ATTN);
+    rc = launch_seq_attn(dt, c.b, c.s, c.H, c.d, pos0, qkv, 6 * h, qkv + h * es, 6 * h,
+                         qkv + 2 * h * es, 6 * h, sk, sv, cap, att, 2 * h, lw.cos_s, lw.sin_s,
+                         scale, c.sa_rope, lw.sa_ws, lw.sa_ws_bytes, st);
+    TE(DREAMER_KC_SEQ_ATTN);
+    if (rc) return fail(DREAMER_E_UNSUPPORTED, "layer: sequence attention shape (%d)", rc);
+    // ---- DA over depths 0..l
+    if (c.use_da) {
+      TB(DREAMER_KC_DEPTH_ATTN);
+      rc = launch_depth_attn(dt, T, c.H, c.d, l, L, qkv + 3 * h * es, 6 * h, qkv + 4 * h * es,
+                             6 * h, qkv + 5 * h * es, 6 * h, DAk, DAv, att + h * es, 2 * h,
+                             lw.cos_d, lw.sin_d, scale, st);
+      TE(DREAMER_KC_DEPTH_ATTN);
+      if (rc) return fail(DREAMER_E_UNSUPPORTED, "layer: depth attention shape");
+    }
+    // ---- y = xh + [a_SA | a_DA] W_o^T  (f32, plus the storage copy read by EA)
+    void* yb = y_steps ? (char*)y_steps + (size_t)l * T * h * es : lw.yb;
+    GemmArgs go;
+    go.M = (int)T;
+    go.N = (int)h;
+    go.K = c.use_da ? 2 * (int)h : (int)h;
+    go.A = att;
+    go.lda = 2 * h;
+    go.B = w->w_o;
+    go.ldb = 2 * h;
+    go.C = lw.y;
+    go.ldc = h;
+    go.resid = resid;
+    go.ldr = h;
+    go.C2 = yb;
+    go.ldc2 = h;
+    if (c.proj_experts) {
+      go.b_gstride = 2 * h * h;
+      go.rows = lw.pperm;
+      go.row_scale = pgate;
+      go.goff = lw.pgoff;
+      go.toff = lw.ptoff;
+      go.G = c.proj_experts;
+      go.tile_m = 64;
+    }
+    TB(DREAMER_KC_GEMM);
+    rc = launch_gemm(go, dt, 1, st);
+    TE(DREAMER_KC_GEMM);
+    if (rc) return fail(DREAMER_E_UNSUPPORTED, "layer: output projection shape");
+    // ---- EA on y, residual, next step's RMSNorm
+    const bool last = l == L - 1;
+    float* xs = x_steps ? x_steps + (size_t)l * T * h : nullptr;
+    float* xo = last ? x_out : nullptr;
+    void* xh_next = last ? nullptr : lw.xh;
+    if (c.use_ea) {
+      int32_t* ridx = route_idx ? route_idx + (size_t)l * T * k : lw.ridx;
+      float* rgate = route_gate ? route_gate + (size_t)l * T * k : lw.rgate;
+      launch_fill_i32(lw.ffn.counts, c.E, 0, st);
+      rc = route_impl(dt, T, c.h, c.r, c.E, k, l, L, yb, h, w->w_r, w->keys, w->bias, c.rho,
+                      c.normalize_gates, lw.cos_r, lw.sin_r, ridx, rgate, lw.ffn.counts, lw.u,
+                      st, route_in ? route_in + (size_t)l * T * k : nullptr);
+      if (rc) return rc;
+      rc = ffn_slots(dt, c.ffn_kind, T, c.h, c.f, c.h, c.E, k, yb, ridx, rgate, w->w1, w->w3,
+                     w->w2, lw.ffn, true, st);
+      if (rc) return rc;
+      TB(DREAMER_KC_COMBINE);
+      launch_combine_norm(dt, T, c.h, k, lw.y, lw.ffn.slots, xo, xs, w->g, c.rms_eps, xh_next,
+                          last ? nullptr : lw.xh32, st);
+      TE(DREAMER_KC_COMBINE);
+    } else {
+      TB(DREAMER_KC_COMBINE);
+      launch_combine_norm(dt, T, c.h, 0, lw.y, nullptr, xo, xs, w->g, c.rms_eps, xh_next,
+                          last ? nullptr : lw.xh32, st);
+      TE(DREAMER_KC_COMBINE);
+    }
+  }
+  return check_launch("layer_forward");
+}
+
+}  // extern "C"

@@ -1,0 +1,105 @@
+// Internal launcher interface between the C-ABI layer (api.cpp) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dreamer {
+
+enum { DT_F32 = 0, DT_BF16 = 1 };
+enum { FFN_GELU = 0, FFN_SWIGLU = 1, FFN_LINEAR = 2 };
+
+struct GemmArgs {
+  int M = 0, N = 0, K = 0;           // positions, columns, reduction length
+  const void* A = nullptr;           // storage dtype, row stride lda
+  int64_t lda = 0;
+  const void* B = nullptr;           // [N, K] per group, row stride ldb
+  int64_t ldb = 0;
+  int64_t b_gstride = 0;             // elements between group matrices
+  const int* rows = nullptr;         // position -> output row (A row = rows[m] / row_div)
+  int row_div = 1;
+  const float* row_scale = nullptr;  // per output row
+  const int* goff = nullptr;         // [G+1] position offsets of groups (device)
+  const int* toff = nullptr;         // [G+1] m-tile offsets of groups (device, tile_m rows)
+  int G = 1;
+  int tile_m = 64;                   // rows per m-tile used to build toff
+  void* C = nullptr;                 // OutT, row stride ldc
+  int64_t ldc = 0;
+  const float* resid = nullptr;      // float32 residual, row stride ldr
+  int64_t ldr = 0;
+  void* C2 = nullptr;                // optional bf16 (f32 in f32 mode) copy, row stride ldc2
+  int64_t ldc2 = 0;
+};
+
+// out_f32: C is float32 (else storage dtype).  Returns -1 on an unsupported shape.
+int launch_gemm(const GemmArgs& a, int dtype, int out_f32, hipStream_t st);
+
+// RoPE tables in float64 math: cos/sin [npos, D/2].
+void launch_rope_tables(int D, int npos, double base, float* c, float* s, hipStream_t st);
+
+// Depth attention (row strides in elements for q/k/v/out; cache contiguous [rows,L,H,d]).
+int launch_depth_attn(int dtype, int64_t rows, int H, int d, int l, int L, const void* q,
+                      int64_t ldq, const void* kn, int64_t ldk, const void* vn, int64_t ldv,
+                      void* kc, void* vc, void* out, int64_t ldo, const float* cosd,
+                      const float* sind, float scale, hipStream_t st);
+
+// Sequence attention.  Workspace bytes needed for (B, q_len, H, d, pos0).
+size_t seq_attn_ws(int dtype, int B, int q_len, int H, int d, int64_t pos0);
+int launch_seq_attn(int dtype, int B, int q_len, int H, int d, int64_t pos0, const void* q,
+                    int64_t ldq, const void* kn, int64_t ldk, const void* vn, int64_t ldv,
+                    void* kc, void* vc, int64_t cap, void* out, int64_t ldo,
+                    const float* cos_s, const float* sin_s, float scale, int sa_rope,
+                    void* ws, size_t ws_bytes, hipStream_t st);
+
+// Router: u = x W_r^T must already be in `u` [T, r] f32.  Fills idx/gate, adds to counts.
+// idx_in (optional, [T, k]): adopt these experts instead of selecting (gates still from
+// the token's own scores).
+int launch_route(int dtype, int64_t T, int r, int E, int k, int l, int L, const float* u,
+                 const void* keys, const float* bias, float rho, int normalize,
+                 const float* cos_r, const float* sin_r, int32_t* idx, float* gate,
+                 int32_t* counts, const int32_t* idx_in, hipStream_t st);
+
+// Fill n ints with a value (graph-safe replacement of memset).
+void launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st);
+
+// counts [E] -> goff [E+1], toff [E+1] (tiles of tile_m rows), cursor [E] = 0.
+void launch_moe_scan(const int32_t* counts, int E, int tile_m, int32_t* goff, int32_t* toff,
+                     int32_t* cursor, hipStream_t st);
+// counts[idx[s]] += 1 for every slot s.
+void launch_moe_histogram(const int32_t* idx, int64_t nslots, int32_t* counts, hipStream_t st);
+// perm[goff[e] + j] = slot id (t*k + i) of the j-th pair routed to e (order unspecified).
+void launch_moe_scatter(const int32_t* idx, int64_t nslots, const int32_t* goff,
+                        int32_t* cursor, int32_t* perm, hipStream_t st);
+
+// Fused expert FFN (GELU / SWIGLU): slots[s] = gate[s] * FFN_e(x[s / k]) for every
+// routed slot s, written in storage dtype [T*k, h_out].
+int launch_expert_ffn(int dtype, int kind, int64_t nslots, int k, int h_in, int f, int h_out,
+                      int E, const void* x, const float* gate, const void* w1,
+                      const void* w3, const void* w2, const int32_t* perm,
+                      const int32_t* goff, const int32_t* toff, void* slots,
+                      hipStream_t st);
+constexpr int FFN_TILE_M = 64;
+// float32 per-slot expert FFN (any kind, any f): slots[s] = gate[s] * FFN_idx[s](x[s/k]).
+int launch_expert_ffn_f32(int kind, int64_t nslots, int k, int h_in, int f, int h_out,
+                          const float* x, const int32_t* idx, const float* gate,
+                          const float* w1, const float* w3, const float* w2, float* slots,
+                          hipStream_t st);
+
+// x_next[t] = y[t] + sum_i slots[t*k+i] (k may be 0, y may be null = 0); optional stores
+// of x_next (f32, up to two destinations) and of xhat = RMSNorm(x_next) * g in storage
+// dtype (xhat) and in float32 (xhat32, optional).
+void launch_combine_norm(int dtype, int64_t T, int h, int k, const float* y,
+                         const void* slots, float* x_out, float* x_out2, const void* g,
+                         float eps, void* xhat, float* xhat32, hipStream_t st);
+// xhat = RMSNorm(x) * g from an f32 stream.
+void launch_rmsnorm(int dtype, int64_t T, int h, const float* x, const void* g, float eps,
+                    void* xhat, float* xhat32, hipStream_t st);
+
+// out[e*n + i] = w_e[e*n + i] + w_sh[i]
+void launch_absorb(int dtype, int64_t ne, int64_t n, const void* we, const void* wsh,
+                   void* out, hipStream_t st);
+
+// Kernel-class timing hooks (api.cpp).
+void timing_begin(int kclass, hipStream_t st);
+void timing_end(int kclass, hipStream_t st);
+
+}  // namespace dreamer

@@ -23,8 +23,9 @@ Where the pages leave a step open, the reading taken is stated at the function
 
 Storage emulation: with ``bf16=True`` every value that the GPU path stores in bfloat16
 is rounded to bfloat16 (round-to-nearest-even) at the same named points:
-x_hat, the six projections, rotated q/k, attention outputs, the bf16 copy of y, the
-expert hidden state, the gated expert outputs.  Everything else stays float64.
+x_hat as projection input (the residual keeps it unrounded), the six projections,
+rotated q/k, attention outputs, the bf16 copy of y, the expert hidden state, the gated
+expert outputs.  Everything else stays float64.
 """
 from __future__ import annotations
 
@@ -257,13 +258,15 @@ def _f64(a):
     return None if a is None else np.asarray(a, np.float64)
 
 
-def prepare_weights(W: dict) -> dict:
-    """float64 copies of a synth weight dict (torch tensors or arrays)."""
+def prepare_weights(W: dict, big_as_f32: bool = False) -> dict:
+    """float64 copies of a synth weight dict (torch tensors or arrays).  With big_as_f32
+    the expert stacks stay float32 arrays (the same values; read per expert as float64)."""
     out = {}
     for k_, v in W.items():
         if hasattr(v, "detach"):
             v = v.detach().to("cpu").float().numpy()
-        out[k_] = np.asarray(v, np.float64)
+        keep32 = big_as_f32 and k_ in ("w1", "w3", "w2", "w_qkv_e", "w_o_e")
+        out[k_] = np.asarray(v, np.float32 if keep32 else np.float64)
     return out
 
 
@@ -300,22 +303,22 @@ def layer_step(cfg, W, x, l, da_k, da_v, sa_k=None, sa_v=None, force_idx=None,
     b, s = cfg.b, cfg.s
     base = cfg.rope_base
     # R2: one RMSNorm per step, on the stream itself, at the loop head; x_hat is both
-    # the attention input and the residual of the parallel-residual equation.
-    xh = st(rmsnorm(x, W["g"], cfg.rms_eps))
-    pidx = pgate = None
+    # the attention input and the residual of the parallel-residual equation.  R20: the
+    # residual keeps x_hat at full precision; the projections read its storage copy.
+    xh = rmsnorm(x, W["g"], cfg.rms_eps)
+    xhb = st(xh)
+    pidx = pgate = pz = None
     if cfg.proj_experts:
         # R12: one top-1 projection router per token and depth on x_hat, shared by all
         # Q/K/V/O projection MoEs; gate = raw sigmoid; bias 0.
-        pidx, pgate, _, _ = expert_route(xh, W["w_pr"], W["pkeys"],
-                                         np.zeros(cfg.proj_experts), 1, l, L, cfg.rho,
-                                         normalize=False, base=base)
+        pidx, pgate, _, pz = expert_route(xhb, W["w_pr"], W["pkeys"],
+                                          np.zeros(cfg.proj_experts), 1, l, L, cfg.rho,
+                                          normalize=False, base=base)
         if force_pidx is not None:
             pidx = np.asarray(force_pidx).reshape(T, 1)
-            _, _, _, zp = expert_route(xh, W["w_pr"], W["pkeys"], np.zeros(cfg.proj_experts),
-                                       1, l, L, cfg.rho, False, base)
-            pgate = sigmoid(np.take_along_axis(zp, pidx, axis=-1))
+            pgate = sigmoid(np.take_along_axis(pz, pidx, axis=-1))
         pidx, pgate = pidx[:, 0], pgate[:, 0]
-    qkv = st(_project(cfg, W, xh, "qkv", pidx, pgate, st))
+    qkv = st(_project(cfg, W, xhb, "qkv", pidx, pgate, st))
     q_sa, k_sa, v_sa, q_da, k_da, v_da = [qkv[:, j * h:(j + 1) * h].reshape(T, H, d)
                                           for j in range(6)]
     # SA at depth l only ([PN] equation: SA(x_l)).
@@ -343,7 +346,7 @@ def layer_step(cfg, W, x, l, da_k, da_v, sa_k=None, sa_v=None, force_idx=None,
     # output projections act on [a_SA | a_DA] (R6: separate SA and DA projections).
     y = xh + _project(cfg, W, att, "o", pidx, pgate, st)
     yb = st(y)
-    idx = gate = counts = None
+    idx = gate = counts = z = None
     x_next = y
     if cfg.use_ea:
         # R7: EA reads y (no second norm).
@@ -358,7 +361,7 @@ def layer_step(cfg, W, x, l, da_k, da_v, sa_k=None, sa_v=None, force_idx=None,
         x_next = expert_ffn(cfg.ffn, yb, idx, gate, W["w1"], W.get("w3"), W["w2"],
                             residual=y, bf16=bf16)
     return dict(x_next=x_next, y=y, yb=yb, idx=idx, gate=gate, pidx=pidx, pgate=pgate,
-                counts=counts)
+                counts=counts, z=z, pz=pz)
 
 
 def new_da_cache(cfg):

@@ -1,0 +1,280 @@
+"""GPU parity of each C-ABI entry point against the CPU oracle (same seeded inputs).
+
+Tolerances: float32 storage -> max|err| / max|ref| <= 1e-5.  bf16 storage -> the oracle
+rounds at the same storage points, so outputs must agree to 1-2 bf16 ulps, plus a term
+for the one internal rounding the oracle does not model (bf16 softmax weights inside the
+MFMA attention kernel: |dP| <= 2^-9 P, hence |dO| <= 2^-9 max|v|).  Routing: the selected
+sets must be identical except where the oracle's k-th and (k+1)-th biased scores are within
+1e-6; gates to 1e-5 relative."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import assert_close_ulps, rel_err, routing_mismatch
+from synth import rng
+
+pytestmark = pytest.mark.gpu
+
+
+def _t(shape, seed, tid, std=1.0, dtype=torch.bfloat16):
+    return rng.normal(shape, seed, tid, std, dtype).cuda()
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+TD = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+# ------------------------------------------------------------------------ depth attention
+
+@pytest.mark.parametrize("dt,H,d,rows,L", [("bf16", 8, 64, 300, 8), ("f32", 4, 16, 37, 4),
+                                           ("bf16", 32, 64, 70, 64), ("bf16", 4, 16, 50, 5),
+                                           ("f32", 2, 64, 9, 3)])
+def test_depth_attn(gpu_lib, dt, H, d, rows, L):
+    D = gpu_lib
+    tdt, bf = TD[dt], dt == "bf16"
+    print(f"depth_attn {dt} H={H} d={d} rows={rows} L={L}", flush=True)
+    cos, sin = D.dreamer_rope_tables(d, L)
+    kc = torch.full((rows, L, H, d), float("nan"), dtype=tdt, device="cuda")
+    vc = torch.full_like(kc, float("nan"))
+    rk = np.full((rows, L, H, d), np.nan)
+    rv = np.full_like(rk, np.nan)
+    for l in range(L):
+        q, k, v = (_t((rows, H, d), 7, 100 + 3 * l + j, dtype=tdt) for j in range(3))
+        out = D.dreamer_depth_attn(q, k, v, kc, vc, l, L, cos, sin)
+        ref = oracle.depth_attn(_np(q), _np(k), _np(v), rk, rv, l, L, bf16=bf)
+        torch.cuda.synchronize()
+        g = _np(out)
+        if l == 0:
+            assert torch.equal(out, v), "depth 0 must return v exactly"
+        assert np.isfinite(g).all()
+        if bf:
+            # rotated q and k are a bf16 storage point rounded independently on each side;
+            # a one-ulp flip moves a score by <= |q_i k_i| 2^-7 / sqrt(d), which moves the
+            # output by a small multiple of 2^-8 max|v|
+            vmax = np.abs(_np(v)).max()
+            assert_close_ulps(g, ref, ulps=2, atol=2.0 ** -8 * vmax, what=f"DA out l={l}")
+            # x cos - y sin in float32 is off by <= 2^-23 (|x| + |y|) before rounding, which
+            # matters where the two products cancel; inputs here are |x|, |y| < 8
+            assert_close_ulps(_np(kc[:, l]), rk[:, l], ulps=1, atol=2.0 ** -20,
+                              what="rotated key")
+        else:
+            assert rel_err(g, ref) <= 1e-5
+            assert rel_err(_np(kc[:, l]), rk[:, l]) <= 1e-6
+        assert torch.equal(vc[:, l], v)
+
+
+# ---------------------------------------------------------------------- sequence attention
+
+@pytest.mark.parametrize("dt,B,S,H,d,rope", [("bf16", 2, 200, 4, 64, True),
+                                             ("bf16", 1, 64, 2, 64, False),
+                                             ("bf16", 3, 1, 2, 64, True),
+                                             ("f32", 2, 37, 4, 16, True),
+                                             ("bf16", 2, 45, 2, 16, True)])
+def test_seq_attn_prefill(gpu_lib, dt, B, S, H, d, rope):
+    D = gpu_lib
+    tdt, bf = TD[dt], dt == "bf16"
+    print(f"seq_attn prefill {dt} B={B} S={S} H={H} d={d} rope={rope}", flush=True)
+    q, k, v = (_t((B, S, H, d), 11, j, dtype=tdt) for j in range(3))
+    cos, sin = D.dreamer_rope_tables(d, S)
+    cap = S + 3
+    kc = torch.full((B, cap, H, d), float("nan"), dtype=tdt, device="cuda")
+    vc = torch.full_like(kc, float("nan"))
+    out = D.dreamer_seq_attn(q, k, v, 0, kc, vc, cos, sin, sa_rope=rope)
+    ref, krot, _ = oracle.seq_attn(_np(q), _np(k), _np(v), 0, None, None, rope, 1e4, bf)
+    torch.cuda.synchronize()
+    g = _np(out)
+    if bf:
+        vmax = np.abs(_np(v)).max()
+        # P is applied as hi + lo bf16 parts (~2^-17 relative), so only the final rounding
+        # and float32 summation remain
+        assert_close_ulps(g, ref, ulps=2, atol=2.0 ** -14 * vmax, what="SA prefill")
+        assert_close_ulps(_np(kc[:, :S]), krot, ulps=1, atol=2.0 ** -20, what="SA cache keys")
+    else:
+        assert rel_err(g, ref) <= 1e-5
+        assert rel_err(_np(kc[:, :S]), krot) <= 1e-6
+    assert torch.equal(vc[:, :S], v)
+    assert torch.isnan(kc[:, S:]).all()
+
+
+def test_seq_attn_causal_perturbation(gpu_lib):
+    D = gpu_lib
+    B, S, H, d = 1, 150, 2, 64
+    q, k, v = (_t((B, S, H, d), 12, j) for j in range(3))
+    cos, sin = D.dreamer_rope_tables(d, S)
+    a = D.dreamer_seq_attn(q, k, v, cos_s=cos, sin_s=sin)
+    k2, v2 = k.clone(), v.clone()
+    k2[:, 100:] += 1.0
+    v2[:, 100:] -= 1.0
+    b = D.dreamer_seq_attn(q, k2, v2, cos_s=cos, sin_s=sin)
+    torch.cuda.synchronize()
+    assert torch.equal(a[:, :100], b[:, :100])
+
+
+@pytest.mark.parametrize("dt,B,P,H,d", [("bf16", 3, 300, 4, 64), ("bf16", 2, 1000, 32, 64),
+                                        ("f32", 2, 50, 4, 16)])
+def test_seq_attn_decode(gpu_lib, dt, B, P, H, d):
+    D = gpu_lib
+    tdt, bf = TD[dt], dt == "bf16"
+    print(f"seq_attn decode {dt} B={B} P={P} H={H} d={d}", flush=True)
+    kc = _t((B, P + 2, H, d), 13, 0, dtype=tdt)
+    vc = _t((B, P + 2, H, d), 13, 1, dtype=tdt)
+    kc[:, P:] = float("nan")
+    vc[:, P:] = float("nan")
+    q, k, v = (_t((B, 1, H, d), 13, 2 + j, dtype=tdt) for j in range(3))
+    cos, sin = D.dreamer_rope_tables(d, P + 1)
+    rkc, rvc = _np(kc), _np(vc)
+    out = D.dreamer_seq_attn(q, k, v, P, kc, vc, cos, sin)
+    ref, krot, _ = oracle.seq_attn(_np(q), _np(k), _np(v), P, rkc, rvc, True, 1e4, bf)
+    torch.cuda.synchronize()
+    if bf:
+        assert_close_ulps(_np(out), ref, ulps=2, atol=2.0 ** -20, what="SA decode")
+        assert_close_ulps(_np(kc[:, P:P + 1]), krot, ulps=1, atol=2.0 ** -20,
+                          what="appended key")
+    else:
+        assert rel_err(_np(out), ref) <= 1e-5
+    assert torch.equal(vc[:, P:P + 1], v)
+    assert torch.isnan(kc[:, P + 1]).all()
+
+
+# ------------------------------------------------------------------------------- routing
+
+@pytest.mark.parametrize("dt,T,h,r,E,k,norm,bias", [
+    ("bf16", 333, 512, 64, 256, 4, True, 0.2),
+    ("f32", 16, 64, 16, 16, 1, False, 0.1),
+    ("bf16", 200, 2048, 64, 4096, 8, True, 0.2),
+    ("bf16", 150, 1024, 64, 16, 1, False, 0.0),
+    ("bf16", 64, 256, 32, 32, 32, True, 0.2),      # k == E: every expert selected
+])
+def test_expert_route(gpu_lib, dt, T, h, r, E, k, norm, bias):
+    D = gpu_lib
+    tdt = TD[dt]
+    print(f"route {dt} T={T} h={h} r={r} E={E} k={k}", flush=True)
+    x = _t((T, h), 21, 0, 1.0, tdt)
+    w_r = _t((r, h), 21, 1, 0.05, tdt)
+    keys = _t((E, r), 21, 2, 0.05, tdt)
+    b = rng.uniform((E,), 21, 3, -bias, bias).cuda() if bias else torch.zeros(E, device="cuda")
+    l, L = 2, 5
+    cos, sin = D.dreamer_rope_tables(r, L)
+    idx, gate, counts = D.dreamer_expert_route(x, w_r, keys, b, k, l, L, cos, sin, 1.0, norm)
+    ridx, rgate, rcounts, z = oracle.expert_route(_np(x), _np(w_r), _np(keys), _np(b), k, l, L,
+                                                  1.0, norm)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy()
+    n_bad, n_ex = routing_mismatch(gi, z, _np(b), k)
+    assert n_bad == 0, f"{n_bad} tokens routed differently ({n_ex} exempt ties)"
+    assert np.array_equal(counts.cpu().numpy(), np.bincount(gi.reshape(-1), minlength=E))
+    # gates by expert id, on tokens with the same set
+    gg = gate.cpu().numpy()
+    for t in range(T):
+        if set(gi[t]) != set(ridx[t]):
+            continue
+        gmap = dict(zip(gi[t], gg[t]))
+        for e, rv in zip(ridx[t], rgate[t]):
+            assert abs(gmap[e] - rv) <= 1e-5 * abs(rv) + 1e-7
+    # descending order of the biased score on the GPU side
+    key = z + _np(b)[None, :]
+    ks = np.take_along_axis(key, gi.astype(np.int64), axis=1)
+    assert (np.diff(ks, axis=1) <= 1e-6).all()
+
+
+def test_expert_route_ties_go_to_lower_index(gpu_lib):
+    D = gpu_lib
+    T, h, r, E = 40, 128, 16, 12
+    x = _t((T, h), 22, 0)
+    w_r = _t((r, h), 22, 1, 0.05)
+    keys = _t((E, r), 22, 2, 0.05)
+    keys[7] = keys[3]
+    keys[9] = keys[3]
+    b = torch.zeros(E, device="cuda")
+    b[3] = b[7] = b[9] = 5.0  # the three identical experts win, in index order
+    cos, sin = D.dreamer_rope_tables(r, 3)
+    idx, _, _ = D.dreamer_expert_route(x, w_r, keys, b, 2, 1, 3, cos, sin)
+    torch.cuda.synchronize()
+    assert (idx[:, 0] == 3).all() and (idx[:, 1] == 7).all()
+
+
+# ------------------------------------------------------------------------------- experts
+
+def _routing(T, E, k, seed, skew=False):
+    g = torch.Generator().manual_seed(seed)
+    idx = torch.stack([torch.randperm(E, generator=g)[:k] for _ in range(T)]).to(torch.int32)
+    if skew:  # a third of the tokens send their first slot to expert 0 (one big group)
+        idx[: T // 3, 0] = 0
+        for t in range(T // 3):
+            row = idx[t]
+            dup = (row[1:] == 0).nonzero()
+            for j in dup.flatten().tolist():
+                row[1 + j] = (E - 1) if row[0] != E - 1 else 1
+    gate = torch.rand((T, k), generator=g) * 0.9 + 0.1
+    return idx.cuda(), gate.cuda()
+
+
+@pytest.mark.parametrize("dt,kind,T,h,f,E,k,skew", [
+    ("bf16", "swiglu", 300, 512, 64, 256, 4, False),
+    ("bf16", "swiglu", 100, 1024, 128, 64, 8, True),
+    ("bf16", "gelu", 77, 256, 64, 8, 2, False),
+    ("bf16", "linear", 130, 256, 0, 16, 1, True),
+    ("f32", "gelu", 16, 64, 32, 16, 1, False),
+    ("f32", "swiglu", 20, 64, 32, 8, 2, False),
+])
+def test_expert_ffn(gpu_lib, dt, kind, T, h, f, E, k, skew):
+    D = gpu_lib
+    tdt, bf = TD[dt], dt == "bf16"
+    print(f"expert_ffn {dt} {kind} T={T} h={h} f={f} E={E} k={k}", flush=True)
+    x = _t((T, h), 31, 0, 1.0, tdt)
+    idx, gate = _routing(T, E, k, 31, skew)
+    res = _t((T, h), 31, 1, 1.0, torch.float32)
+    if kind == "linear":
+        w1, w3, w2 = _t((E, h, h), 31, 2, 0.05, tdt), None, None
+    else:
+        w1 = _t((E, f, h), 31, 2, 0.05, tdt)
+        w3 = _t((E, f, h), 31, 3, 0.05, tdt) if kind == "swiglu" else None
+        w2 = _t((E, h, f), 31, 4, 0.05, tdt)
+    out = D.dreamer_expert_ffn(kind, x, idx, gate, w1, w3, w2, res)
+    ref = oracle.expert_ffn(kind, _np(x), idx.cpu().numpy(), _np(gate), _np(w1),
+                            None if w3 is None else _np(w3), None if w2 is None else _np(w2),
+                            residual=_np(res), bf16=bf)
+    torch.cuda.synchronize()
+    g = _np(out)
+    if bf:
+        dmax = np.abs(ref - _np(res)).max()
+        err = np.abs(g - ref).max()
+        # each of the k slots may differ by one bf16 ulp after rounding
+        assert err <= k * 2.0 ** -7 * dmax + 1e-6 * np.abs(ref).max(), (err, dmax)
+    else:
+        assert rel_err(g, ref) <= 1e-5
+    # no routing: out == residual exactly when every gate is zero
+    out0 = D.dreamer_expert_ffn(kind, x, idx, torch.zeros_like(gate), w1, w3, w2, res)
+    torch.cuda.synchronize()
+    assert torch.equal(out0, res)
+
+
+def test_absorb_shared_exact(gpu_lib):
+    D = gpu_lib
+    we = _t((4, 64, 32), 41, 0, 0.02)
+    ws = _t((64, 32), 41, 1, 0.02)
+    got = D.dreamer_absorb_shared(we, ws)
+    torch.cuda.synchronize()
+    ref = (we.float() + ws.float()[None]).to(torch.bfloat16)
+    assert torch.equal(got, ref)
+
+
+def test_errors_are_reported(gpu_lib):
+    D = gpu_lib
+    q = torch.zeros((4, 2, 64), dtype=torch.bfloat16, device="cuda")
+    kc = torch.zeros((4, 3, 2, 64), dtype=torch.bfloat16, device="cuda")
+    cos, sin = D.dreamer_rope_tables(64, 3)
+    with pytest.raises(D.DreamerError) as ei:
+        D.dreamer_depth_attn(q, q, q, kc, kc, 3, 3, cos, sin)   # l >= L
+    assert ei.value.code == D.E_INVAL
+    q2 = torch.zeros((4, 2, 24), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(D.DreamerError) as ei:
+        D.dreamer_depth_attn(q2, q2, q2, kc[..., :24].contiguous(), kc[..., :24].contiguous(),
+                             0, 3, cos, sin)
+    assert ei.value.code == D.E_UNSUPPORTED
