@@ -216,13 +216,21 @@ static int validate_route(int dtype, int64_t T, int h, int r, int E, int k, int 
   if (k > E || k > 32) return fail(DREAMER_E_UNSUPPORTED, "expert_route: k=%d (E=%d) unsupported", k, E);
   if (r % 8) return fail(DREAMER_E_UNSUPPORTED, "expert_route: r %% 8 != 0");
   if (E > 16384) return fail(DREAMER_E_UNSUPPORTED, "expert_route: E > 16384");
-  if (dtype == DREAMER_BF16 && h % 64) return fail(DREAMER_E_UNSUPPORTED, "expert_route: h %% 64 != 0");
+  if (dtype == DREAMER_BF16) {
+    if (h % 64) return fail(DREAMER_E_UNSUPPORTED, "expert_route: h %% 64 != 0");
+    if (r != 32 && r != 64 && r != 128 && r != 256)
+      return fail(DREAMER_E_UNSUPPORTED, "expert_route: bf16 needs r in {32, 64, 128, 256}");
+    if (E % 16) return fail(DREAMER_E_UNSUPPORTED, "expert_route: bf16 needs E %% 16 == 0");
+  }
   return ok();
 }
 
 size_t dreamer_expert_route_ws_bytes(int64_t T, int r, int E) {
-  (void)E;
-  return (size_t)(T > 0 ? T : 0) * (r > 0 ? r : 0) * 4 + 256;
+  if (T < 0 || r <= 0 || E <= 0) return 0;
+  Bump b(nullptr);
+  b.take_n<float>((size_t)T * r);
+  b.take_n<float>((size_t)T * E);
+  return b.off + 256;
 }
 
 // u = x W_r^T (f32), then the routing kernel.  counts must be zeroed by the caller of
@@ -230,25 +238,28 @@ size_t dreamer_expert_route_ws_bytes(int64_t T, int r, int E) {
 static int route_impl(int dtype, int64_t T, int h, int r, int E, int k, int l, int L,
                       const void* x, int64_t ldx, const void* w_r, const void* keys,
                       const float* bias, float rho, int normalize, const float* cos_r,
-                      const float* sin_r, int32_t* idx, float* gate, int32_t* counts,
-                      float* u, hipStream_t st, const int32_t* idx_in = nullptr) {
-  GemmArgs ga;
-  ga.M = (int)T;
-  ga.N = r;
-  ga.K = h;
-  ga.A = x;
-  ga.lda = ldx;
-  ga.B = w_r;
-  ga.ldb = h;
-  ga.C = u;
-  ga.ldc = r;
-  TB(DREAMER_KC_GEMM);
-  int rc = launch_gemm(ga, dtype, 1, st);
-  TE(DREAMER_KC_GEMM);
-  if (rc) return fail(DREAMER_E_UNSUPPORTED, "router projection: unsupported shape");
+                      const float* sin_r, int32_t* idx, float* gate, float* u, float* z,
+                      hipStream_t st, const int32_t* idx_in = nullptr) {
+  int rc;
+  if (dtype == DREAMER_F32) {  // bf16 computes u inside the scores kernel
+    GemmArgs ga;
+    ga.M = (int)T;
+    ga.N = r;
+    ga.K = h;
+    ga.A = x;
+    ga.lda = ldx;
+    ga.B = w_r;
+    ga.ldb = h;
+    ga.C = u;
+    ga.ldc = r;
+    TB(DREAMER_KC_GEMM);
+    rc = launch_gemm(ga, dtype, 1, st);
+    TE(DREAMER_KC_GEMM);
+    if (rc) return fail(DREAMER_E_UNSUPPORTED, "router projection: unsupported shape");
+  }
   TB(DREAMER_KC_ROUTE);
-  rc = launch_route(dtype, T, r, E, k, l, L, u, keys, bias, rho, normalize, cos_r, sin_r, idx,
-                    gate, counts, idx_in, st);
+  rc = router_scores(dtype, T, h, r, E, l, L, x, ldx, w_r, u, keys, rho, cos_r, sin_r, z, st);
+  if (!rc) rc = router_topk(T, E, k, z, bias, normalize, idx_in, idx, gate, st);
   TE(DREAMER_KC_ROUTE);
   if (rc) return fail(DREAMER_E_UNSUPPORTED, "expert_route: unsupported shape");
   return ok();
@@ -267,16 +278,19 @@ int dreamer_expert_route(int dtype, int64_t T, int h, int r, int E, int k, int l
   const size_t need = dreamer_expert_route_ws_bytes(T, r, E);
   if (!ws || ws_bytes < need) return fail(DREAMER_E_WORKSPACE, "expert_route: workspace %zu < %zu", ws_bytes, need);
   hipStream_t st = S(stream);
-  if (counts) launch_fill_i32(counts, E, 0, st);
+  Bump b(ws);
+  float* u = b.take_n<float>((size_t)T * r);
+  float* z = b.take_n<float>((size_t)T * E);
   rc = route_impl(dtype, T, h, r, E, k, l, L, x, h, w_r, keys, bias, rho, normalize, cos_r,
-                  sin_r, idx, gate, counts, (float*)ws, st);
+                  sin_r, idx, gate, u, z, st);
   if (rc) return rc;
+  if (counts) launch_histogram(idx, T * k, counts, E, st);
   return check_launch("expert_route");
 }
 
 // ------------------------------------------------------------------------ expert FFN
 struct FfnWs {
-  int32_t *counts, *goff, *toff, *cursor, *perm;
+  int32_t *counts, *goff, *toff, *hist, *perm;
   void* slots;
 };
 
@@ -285,7 +299,7 @@ static FfnWs plan_ffn(Bump& b, int dtype, int64_t T, int h_out, int E, int k) {
   w.counts = b.take_n<int32_t>(E);
   w.goff = b.take_n<int32_t>(E + 1);
   w.toff = b.take_n<int32_t>(E + 1);
-  w.cursor = b.take_n<int32_t>(E);
+  w.hist = b.take_n<int32_t>((size_t)std::max(1, perm_blocks(T * k)) * E);
   w.perm = b.take_n<int32_t>((size_t)T * k);
   w.slots = b.take((size_t)T * k * h_out * esize(dtype));
   return w;
@@ -304,7 +318,7 @@ size_t dreamer_expert_ffn_ws_bytes(int dtype, int kind, int64_t T, int h_in, int
 // slots by expert first (histogram unless the counts are already there, scan, scatter).
 static int ffn_slots(int dtype, int kind, int64_t T, int h_in, int f, int h_out, int E, int k,
                      const void* x, const int32_t* idx, const float* gate, const void* w1,
-                     const void* w3, const void* w2, const FfnWs& w, bool have_counts,
+                     const void* w3, const void* w2, const FfnWs& w,
                      hipStream_t st) {
   const int64_t ns = T * k;
   if (dtype == DREAMER_F32) {
@@ -316,13 +330,10 @@ static int ffn_slots(int dtype, int kind, int64_t T, int h_in, int f, int h_out,
     return rc ? fail(DREAMER_E_UNSUPPORTED, "expert_ffn: f32 shape unsupported") : ok();
   }
   TB(DREAMER_KC_PERMUTE);
-  if (!have_counts) {
-    launch_fill_i32(w.counts, E, 0, st);
-    launch_moe_histogram(idx, ns, w.counts, st);
-  }
-  launch_moe_scan(w.counts, E, FFN_TILE_M, w.goff, w.toff, w.cursor, st);
-  launch_moe_scatter(idx, ns, w.goff, w.cursor, w.perm, st);
+  int prc = launch_permute(idx, ns, E, FFN_TILE_M, w.hist, w.counts, w.goff, w.toff, w.perm,
+                           st);
   TE(DREAMER_KC_PERMUTE);
+  if (prc) return fail(DREAMER_E_UNSUPPORTED, "expert_ffn: E too large for the permutation");
   int rc;
   if (kind == DREAMER_FFN_LINEAR) {
     GemmArgs ga;
@@ -390,7 +401,7 @@ int dreamer_expert_ffn(int dtype, int kind, int64_t T, int h_in, int f, int h_ou
   hipStream_t st = S(stream);
   Bump b(ws);
   FfnWs w = plan_ffn(b, dtype, T, h_out, E, k);
-  rc = ffn_slots(dtype, kind, T, h_in, f, h_out, E, k, x, idx, gate, w1, w3, w2, w, false, st);
+  rc = ffn_slots(dtype, kind, T, h_in, f, h_out, E, k, x, idx, gate, w1, w3, w2, w, st);
   if (rc) return rc;
   TB(DREAMER_KC_COMBINE);
   launch_combine_norm(dtype, T, h_out, k, residual, w.slots, out, nullptr, nullptr, 0.f,
@@ -413,10 +424,10 @@ struct LayerWs {
   float *cos_s, *sin_s, *cos_d, *sin_d, *cos_r, *sin_r;
   void *xh, *qkv, *att, *yb;
   float* xh32;  // float32 copy of xhat for the residual (bf16 storage only)
-  float *y, *u, *rgate, *pgate, *zero_pbias;
+  float *y, *u, *z, *rgate, *pgate, *zero_pbias;
   int32_t *ridx, *pidx;
   FfnWs ffn;
-  int32_t *pcounts, *pgoff, *ptoff, *pcursor, *pperm;
+  int32_t *pcounts, *pgoff, *ptoff, *phist, *pperm;
   void *da_k, *da_v, *sa_ws;
   size_t sa_ws_bytes;
 };
@@ -460,9 +471,10 @@ static LayerWs plan_layer(Bump& b, const dreamer_layer_cfg* c, bool need_yb, boo
     w.pcounts = b.take_n<int32_t>(Ep);
     w.pgoff = b.take_n<int32_t>(Ep + 1);
     w.ptoff = b.take_n<int32_t>(Ep + 1);
-    w.pcursor = b.take_n<int32_t>(Ep);
+    w.phist = b.take_n<int32_t>((size_t)std::max(1, perm_blocks(T)) * Ep);
     w.pperm = b.take_n<int32_t>(T);
   }
+  w.z = b.take_n<float>((size_t)T * std::max(c->use_ea ? c->E : 1, c->proj_experts));
   if (need_da) {
     w.da_k = b.take(T * c->L * h * es);
     w.da_v = b.take(T * c->L * h * es);
@@ -579,16 +591,16 @@ int dreamer_layer_forward(const dreamer_layer_cfg* cfg, const dreamer_layer_weig
       const int Ep = c.proj_experts;
       pidx = proj_idx ? proj_idx + (int64_t)l * T : lw.pidx;
       pgate = proj_gate ? proj_gate + (int64_t)l * T : lw.pgate;
-      launch_fill_i32(lw.pcounts, Ep, 0, st);
       rc = route_impl(dt, T, c.h, c.r, Ep, 1, l, L, lw.xh, h, w->w_pr, w->pkeys,
                       w->pbias ? w->pbias : lw.zero_pbias, c.rho, 0, lw.cos_r, lw.sin_r, pidx,
-                      pgate, lw.pcounts, lw.u, st,
+                      pgate, lw.u, lw.z, st,
                       proj_route_in ? proj_route_in + (int64_t)l * T : nullptr);
       if (rc) return rc;
       TB(DREAMER_KC_PERMUTE);
-      launch_moe_scan(lw.pcounts, Ep, 64, lw.pgoff, lw.ptoff, lw.pcursor, st);
-      launch_moe_scatter(pidx, T, lw.pgoff, lw.pcursor, lw.pperm, st);
+      rc = launch_permute(pidx, T, Ep, 64, lw.phist, lw.pcounts, lw.pgoff, lw.ptoff, lw.pperm,
+                          st);
       TE(DREAMER_KC_PERMUTE);
+      if (rc) return fail(DREAMER_E_UNSUPPORTED, "layer: projection permutation");
       gq.b_gstride = 6 * h * h;
       gq.rows = lw.pperm;
       gq.row_scale = pgate;
@@ -658,13 +670,12 @@ int dreamer_layer_forward(const dreamer_layer_cfg* cfg, const dreamer_layer_weig
     if (c.use_ea) {
       int32_t* ridx = route_idx ? route_idx + (size_t)l * T * k : lw.ridx;
       float* rgate = route_gate ? route_gate + (size_t)l * T * k : lw.rgate;
-      launch_fill_i32(lw.ffn.counts, c.E, 0, st);
       rc = route_impl(dt, T, c.h, c.r, c.E, k, l, L, yb, h, w->w_r, w->keys, w->bias, c.rho,
-                      c.normalize_gates, lw.cos_r, lw.sin_r, ridx, rgate, lw.ffn.counts, lw.u,
-                      st, route_in ? route_in + (size_t)l * T * k : nullptr);
+                      c.normalize_gates, lw.cos_r, lw.sin_r, ridx, rgate, lw.u, lw.z, st,
+                      route_in ? route_in + (size_t)l * T * k : nullptr);
       if (rc) return rc;
       rc = ffn_slots(dt, c.ffn_kind, T, c.h, c.f, c.h, c.E, k, yb, ridx, rgate, w->w1, w->w3,
-                     w->w2, lw.ffn, true, st);
+                     w->w2, lw.ffn, st);
       if (rc) return rc;
       TB(DREAMER_KC_COMBINE);
       launch_combine_norm(dt, T, c.h, k, lw.y, lw.ffn.slots, xo, xs, w->g, c.rms_eps, xh_next,

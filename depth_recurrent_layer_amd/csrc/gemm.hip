@@ -15,13 +15,23 @@
 
 namespace dreamer {
 
+// LDS tile layout: rows of BK = 64 bf16 (128 B), 16-byte chunks XOR-swizzled by row
+// (chunk c of row r lives at slot c ^ (r & 7)), so the 16 rows read by one MFMA
+// fragment load hit distinct banks without padding.
+DEV int swz(int row, int kc) { return row * 64 + ((kc ^ (row & 7)) << 3); }
+
 template <typename OutT, typename ResT, int BM, int BN>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
-  constexpr int BK = 64, LD = BK + 8;  // LDS row = 144 B (16-B aligned, spreads banks)
-  constexpr int TM = BM / 32, TN = BN / 32;  // 16x16 tiles per wave (2 x 2 waves)
-  constexpr int ACH = BM * 8 / 256, BCH = BN * 8 / 256;  // 16-B chunks per thread
-  __shared__ __attribute__((aligned(16))) bf16 As[BM * LD];
-  __shared__ __attribute__((aligned(16))) bf16 Bs[BN * LD];
+__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs a) {
+  constexpr int BK = 64;
+  constexpr int TM = BM / 32, TN = BN / 32;              // 16x16 tiles per wave (2 x 2 waves)
+  constexpr int ACH = BM * 8 / 256, BCH = BN * 8 / 256;  // 16-B chunks per thread per tile
+  // A/B tiles during the K loop; the float32 C tile (rows padded by 4) in the epilogue
+  constexpr int LDC = BN + 4;
+  constexpr int AB_BYTES = 2 * (BM + BN) * BK * 2, C_BYTES = BM * LDC * 4;
+  __shared__ __attribute__((aligned(16))) char smem[AB_BYTES > C_BYTES ? AB_BYTES : C_BYTES];
+  bf16 (*As)[BM * BK] = reinterpret_cast<bf16 (*)[BM * BK]>(smem);
+  bf16 (*Bs)[BN * BK] = reinterpret_cast<bf16 (*)[BN * BK]>(smem + 2 * BM * BK * 2);
+  float* Cs = reinterpret_cast<float*>(smem);
   __shared__ int rows_s[BM];
 
   const int tid = threadIdx.x;
@@ -51,42 +61,40 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
   }
   __syncthreads();
 
-  // global -> register staging
-  const bf16* aptr[ACH];
-  const bf16* bptr[BCH];
+  // Thread -> (row, chunk) of the tiles it stages; source rows as 32-bit indices.
+  const int kc = tid & 7, r0 = tid >> 3;  // rows r0 + 32 j
+  int arow[ACH], brow[BCH];
 #pragma unroll
   for (int j = 0; j < ACH; ++j) {
-    int c = tid + 256 * j, row = c >> 3, kc = c & 7;
-    int src = rows_s[row];
-    aptr[j] = src >= 0 ? A + (int64_t)(src / a.row_div) * a.lda + kc * 8 : nullptr;
+    const int src = rows_s[r0 + 32 * j];
+    arow[j] = src >= 0 ? src / a.row_div : -1;
   }
 #pragma unroll
   for (int j = 0; j < BCH; ++j) {
-    int c = tid + 256 * j, row = c >> 3, kc = c & 7;
-    int n = n0 + row;
-    bptr[j] = n < a.N ? B + (int64_t)n * a.ldb + kc * 8 : nullptr;
+    const int n = n0 + r0 + 32 * j;
+    brow[j] = n < a.N ? n : -1;
   }
   bf16x8 ra[ACH], rb[BCH];
   const bf16x8 zero8 = {};
   auto gload = [&](int k0) {
 #pragma unroll
     for (int j = 0; j < ACH; ++j)
-      ra[j] = aptr[j] ? *reinterpret_cast<const bf16x8*>(aptr[j] + k0) : zero8;
+      ra[j] = arow[j] >= 0
+                  ? *reinterpret_cast<const bf16x8*>(A + (int64_t)arow[j] * a.lda + k0 + kc * 8)
+                  : zero8;
 #pragma unroll
     for (int j = 0; j < BCH; ++j)
-      rb[j] = bptr[j] ? *reinterpret_cast<const bf16x8*>(bptr[j] + k0) : zero8;
+      rb[j] = brow[j] >= 0
+                  ? *reinterpret_cast<const bf16x8*>(B + (int64_t)brow[j] * a.ldb + k0 + kc * 8)
+                  : zero8;
   };
-  auto lstore = [&]() {
+  auto lstore = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < ACH; ++j) {
-      int c = tid + 256 * j, row = c >> 3, kc = c & 7;
-      *reinterpret_cast<bf16x8*>(&As[row * LD + kc * 8]) = ra[j];
-    }
+    for (int j = 0; j < ACH; ++j)
+      *reinterpret_cast<bf16x8*>(&As[buf][swz(r0 + 32 * j, kc)]) = ra[j];
 #pragma unroll
-    for (int j = 0; j < BCH; ++j) {
-      int c = tid + 256 * j, row = c >> 3, kc = c & 7;
-      *reinterpret_cast<bf16x8*>(&Bs[row * LD + kc * 8]) = rb[j];
-    }
+    for (int j = 0; j < BCH; ++j)
+      *reinterpret_cast<bf16x8*>(&Bs[buf][swz(r0 + 32 * j, kc)]) = rb[j];
   };
 
   const int lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
@@ -98,56 +106,79 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs a) {
     for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   gload(0);
-  lstore();
+  lstore(0);
   __syncthreads();
+  int buf = 0;
   for (int k0 = 0; k0 < a.K; k0 += BK) {
     const bool more = k0 + BK < a.K;
     if (more) gload(k0 + BK);
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
-      bf16x8 af[TM], bfr[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(
-            &As[(wm * (BM / 2) + i * 16 + lr) * LD + ks * 32 + lg * 8]);
+      bf16x8 bfr[TN];
 #pragma unroll
       for (int j = 0; j < TN; ++j)
         bfr[j] = *reinterpret_cast<const bf16x8*>(
-            &Bs[(wn * (BN / 2) + j * 16 + lr) * LD + ks * 32 + lg * 8]);
+            &Bs[buf][swz(wn * (BN / 2) + j * 16 + lr, ks * 4 + lg)]);
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i) {
+        const bf16x8 af = *reinterpret_cast<const bf16x8*>(
+            &As[buf][swz(wm * (BM / 2) + i * 16 + lr, ks * 4 + lg)]);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(af, bfr[j], acc[i][j]);
+      }
     }
     if (more) {
+      lstore(buf ^ 1);  // the other buffer was last read before the previous barrier
       __syncthreads();
-      lstore();
-      __syncthreads();
+      buf ^= 1;
     }
   }
 
-  // epilogue
+  // epilogue: accumulators -> LDS (float32), then every thread handles 8-column chunks of
+  // whole rows so the residual loads and the output stores are 16-byte and coalesced
+  __syncthreads();  // all waves are done reading the A/B tiles
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        Cs[(wm * (BM / 2) + i * 16 + lg * 4 + v) * LDC + wn * (BN / 2) + j * 16 + lr] =
+            acc[i][j][v];
+  __syncthreads();
   OutT* C = (OutT*)a.C;
   bf16* C2 = (bf16*)a.C2;
   const ResT* R = (const ResT*)a.resid;
+  constexpr int CPR = BN / 8;  // 8-column chunks per row
+  for (int c = tid; c < BM * CPR; c += 256) {
+    const int row = c / CPR, cc = c % CPR;
+    const int orow = rows_s[row];
+    const int n = n0 + cc * 8;
+    if (orow < 0 || n >= a.N) continue;
+    const float sc = a.row_scale ? a.row_scale[orow] : 1.0f;
+    float val[8];
+    const floatx4 c0 = *reinterpret_cast<const floatx4*>(&Cs[row * LDC + cc * 8]);
+    const floatx4 c1 = *reinterpret_cast<const floatx4*>(&Cs[row * LDC + cc * 8 + 4]);
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int ml = wm * (BM / 2) + i * 16 + lg * 4 + v;
-      const int orow = rows_s[ml];
-      if (orow < 0) continue;
-      const float sc = a.row_scale ? a.row_scale[orow] : 1.0f;
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int n = n0 + wn * (BN / 2) + j * 16 + lr;
-        if (n >= a.N) continue;
-        float val = acc[i][j][v] * sc;
-        if (R) val += to_f(R[(int64_t)orow * a.ldr + n]);
-        C[(int64_t)orow * a.ldc + n] = from_f<OutT>(val);
-        if (C2) C2[(int64_t)orow * a.ldc2 + n] = (bf16)val;
-      }
+    for (int e = 0; e < 4; ++e) {
+      val[e] = c0[e] * sc;
+      val[4 + e] = c1[e] * sc;
     }
+    if (R) {
+      float rv[8];
+      load16(R + (int64_t)orow * a.ldr + n, rv);
+      load16(R + (int64_t)orow * a.ldr + n + 4, rv + 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) val[e] += rv[e];
+    }
+    OutT* cp = C + (int64_t)orow * a.ldc + n;
+    if constexpr (sizeof(OutT) == 2) {
+      store16(cp, val);
+    } else {
+      store16(cp, val);
+      store16(cp + 4, val + 4);
+    }
+    if (C2) store16(C2 + (int64_t)orow * a.ldc2 + n, val);
   }
 }
 
@@ -184,7 +215,7 @@ int launch_gemm(const GemmArgs& a, int dtype, int out_f32, hipStream_t st) {
     gemm_f32_kernel<<<grid, 256, 0, st>>>(a);
     return 0;
   }
-  if (a.K % 64 != 0) return -1;
+  if (a.K % 64 != 0 || a.N % 8 != 0) return -1;
   // Tile choice: 128x128 when that still gives >= 2 tiles per CU, else 64-row tiles.
   // Grouped launches use the m-tile size their tile offsets were built with.
   int bm, bn = a.N >= 128 ? 128 : 64;

@@ -232,43 +232,56 @@ int launch_expert_ffn_f32(int kind, int64_t nslots, int k, int h_in, int f, int 
 }
 
 // -------------------------------------------------------------- combine + next RMSNorm
-// Block per token.  x = y + sum_i slots[t*k+i] (fixed slot order), then optional
-// x stores and xhat = x / sqrt(mean(x^2) + eps) * g.
-constexpr int CN_THREADS = 256, CN_MAXV = 16;
-
+// Block per token, one 16-byte chunk of the row per thread.  x = y + sum_i slots[t*k+i]
+// (fixed slot order), then optional x stores and xhat = x / sqrt(mean(x^2) + eps) * g.
 template <typename T>
-__global__ __launch_bounds__(CN_THREADS) void combine_norm_kernel(
+__global__ __launch_bounds__(1024) void combine_norm_kernel(
     int64_t Ttok, int h, int k, const float* __restrict__ y, const T* __restrict__ slots,
     float* __restrict__ x_out, float* __restrict__ x_out2, const T* __restrict__ g, float eps,
     T* __restrict__ xhat, float* __restrict__ xhat32) {
+  constexpr int VEC = Vec16<T>::N;
   __shared__ float red[16];
   const int64_t t = blockIdx.x;
-  float v[CN_MAXV];
+  const int c = threadIdx.x * VEC;
+  const bool act = c < h;
+  float v[VEC];
   float ss = 0.f;
+  if (act) {
+    if (y) {
+      load16(y + t * h + c, v);
+      if constexpr (VEC == 8) load16(y + t * h + c + 4, v + 4);
+    } else {
 #pragma unroll
-  for (int j = 0; j < CN_MAXV; ++j) {
-    const int c = threadIdx.x + j * CN_THREADS;
-    v[j] = 0.f;
-    if (c < h) {
-      float a = y ? y[t * h + c] : 0.f;
-      for (int i = 0; i < k; ++i) a += to_f(slots[(t * k + i) * h + c]);
-      v[j] = a;
-      ss += a * a;
-      if (x_out) x_out[t * h + c] = a;
-      if (x_out2) x_out2[t * h + c] = a;
+      for (int e = 0; e < VEC; ++e) v[e] = 0.f;
+    }
+    for (int i = 0; i < k; ++i) {
+      float sv[VEC];
+      load16(slots + (t * k + i) * h + c, sv);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) v[e] += sv[e];
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) ss += v[e] * v[e];
+    float* outs[2] = {x_out, x_out2};
+#pragma unroll
+    for (int o = 0; o < 2; ++o) {
+      if (!outs[o]) continue;
+      store16(outs[o] + t * h + c, v);
+      if constexpr (VEC == 8) store16(outs[o] + t * h + c + 4, v + 4);
     }
   }
   if (!xhat) return;
   ss = block_sum(ss, red);
+  if (!act) return;
   const float inv = 1.0f / sqrtf(ss / (float)h + eps);
+  float gv[VEC];
+  load16(g + c, gv);
 #pragma unroll
-  for (int j = 0; j < CN_MAXV; ++j) {
-    const int c = threadIdx.x + j * CN_THREADS;
-    if (c < h) {
-      const float xn = v[j] * inv * to_f(g[c]);
-      xhat[t * h + c] = from_f<T>(xn);
-      if (xhat32) xhat32[t * h + c] = xn;
-    }
+  for (int e = 0; e < VEC; ++e) v[e] = v[e] * inv * gv[e];
+  store16(xhat + t * h + c, v);
+  if (xhat32) {
+    store16(xhat32 + t * h + c, v);
+    if constexpr (VEC == 8) store16(xhat32 + t * h + c + 4, v + 4);
   }
 }
 
@@ -276,12 +289,14 @@ void launch_combine_norm(int dtype, int64_t T, int h, int k, const float* y,
                          const void* slots, float* x_out, float* x_out2, const void* g,
                          float eps, void* xhat, float* xhat32, hipStream_t st) {
   if (T <= 0) return;
+  const int vec = dtype == DT_BF16 ? 8 : 4;
+  const int threads = ((h / vec + 63) / 64) * 64;
   if (dtype == DT_BF16)
-    combine_norm_kernel<bf16><<<(unsigned)T, CN_THREADS, 0, st>>>(
+    combine_norm_kernel<bf16><<<(unsigned)T, threads, 0, st>>>(
         T, h, k, y, (const bf16*)slots, x_out, x_out2, (const bf16*)g, eps, (bf16*)xhat,
         xhat32);
   else
-    combine_norm_kernel<float><<<(unsigned)T, CN_THREADS, 0, st>>>(
+    combine_norm_kernel<float><<<(unsigned)T, threads, 0, st>>>(
         T, h, k, y, (const float*)slots, x_out, x_out2, (const float*)g, eps, (float*)xhat,
         xhat32);
 }

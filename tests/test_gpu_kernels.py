@@ -185,7 +185,7 @@ def test_expert_route(gpu_lib, dt, T, h, r, E, k, norm, bias):
 
 def test_expert_route_ties_go_to_lower_index(gpu_lib):
     D = gpu_lib
-    T, h, r, E = 40, 128, 16, 12
+    T, h, r, E = 40, 128, 32, 16
     x = _t((T, h), 22, 0)
     w_r = _t((r, h), 22, 1, 0.05)
     keys = _t((E, r), 22, 2, 0.05)

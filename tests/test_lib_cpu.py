@@ -65,7 +65,7 @@ def test_seq_attn_decode_needs_cache():
 
 def test_workspace_too_small():
     p = C.c_void_p(16)
-    rc = D.lib.dreamer_expert_route(D.BF16, 8, 64, 16, 4, 2, 0, 2, p, p, p, p, 1.0, 1, p, p, p,
+    rc = D.lib.dreamer_expert_route(D.BF16, 8, 64, 32, 16, 2, 0, 2, p, p, p, p, 1.0, 1, p, p, p,
                                     p, None, p, 8, None)
     assert rc == D.E_WORKSPACE
 
