@@ -157,14 +157,14 @@ int dreamer_depth_attn(int dtype, int64_t rows, int H, int d, int l, int L, cons
   hipStream_t st = S(stream);
   TB(DREAMER_KC_DEPTH_ATTN);
   int rc = launch_depth_attn(dtype, rows, H, d, l, L, q, h, k_new, h, v_new, h, k_cache,
-                             v_cache, out, h, cos_d, sin_d, scale, st);
+                             v_cache, out, h, cos_d, sin_d, scale, 1, st);
   TE(DREAMER_KC_DEPTH_ATTN);
   if (rc) return fail(DREAMER_E_UNSUPPORTED, "depth_attn: head dim %d unsupported", d);
   return check_launch("depth_attn");
 }
 
 size_t dreamer_seq_attn_ws_bytes(int dtype, int B, int q_len, int H, int d, int64_t pos0) {
-  return seq_attn_ws(dtype, B, q_len, H, d, pos0);
+  return seq_attn_ws(dtype, B, q_len, H, d, pos0, 0);
 }
 
 static int validate_seq(int dtype, int B, int q_len, int H, int d, int64_t pos0, int64_t cap,
@@ -196,14 +196,15 @@ int dreamer_seq_attn(int dtype, int B, int q_len, int H, int d, int64_t pos0, co
   if (B == 0 || q_len == 0) return ok();
   if (!q || !k_new || !v_new || !out) return fail(DREAMER_E_INVAL, "seq_attn: null pointer");
   if (sa_rope && (!cos_s || !sin_s)) return fail(DREAMER_E_INVAL, "seq_attn: null rope table");
-  const size_t need = seq_attn_ws(dtype, B, q_len, H, d, pos0);
+  const size_t need = seq_attn_ws(dtype, B, q_len, H, d, pos0, 0);
   if (ws_bytes < need || (need && !ws))
     return fail(DREAMER_E_WORKSPACE, "seq_attn: workspace %zu < %zu", ws_bytes, need);
   const int64_t h = (int64_t)H * d;
   hipStream_t st = S(stream);
   TB(DREAMER_KC_SEQ_ATTN);
-  rc = launch_seq_attn(dtype, B, q_len, H, d, pos0, q, h, k_new, h, v_new, h, k_cache,
-                       v_cache, cap, out, h, cos_s, sin_s, scale, sa_rope, ws, ws_bytes, st);
+  rc = launch_seq_attn(dtype, B, q_len, H, d, pos0, q, h, k_new, h, v_new, h, nullptr,
+                       k_cache, v_cache, cap, out, h, cos_s, sin_s, scale, sa_rope, ws,
+                       ws_bytes, st);
   TE(DREAMER_KC_SEQ_ATTN);
   if (rc) return fail(DREAMER_E_UNSUPPORTED, "seq_attn: unsupported shape (%d)", rc);
   return check_launch("seq_attn");
@@ -428,7 +429,7 @@ struct LayerWs {
   int32_t *ridx, *pidx;
   FfnWs ffn;
   int32_t *pcounts, *pgoff, *ptoff, *phist, *pperm;
-  void *da_k, *da_v, *sa_ws;
+  void *da_k, *da_v, *sa_ws, *vt;
   size_t sa_ws_bytes;
 };
 
@@ -479,7 +480,11 @@ static LayerWs plan_layer(Bump& b, const dreamer_layer_cfg* c, bool need_yb, boo
     w.da_k = b.take(T * c->L * h * es);
     w.da_v = b.take(T * c->L * h * es);
   }
-  w.sa_ws_bytes = seq_attn_ws(c->dtype, c->b, c->s, c->H, c->d, c->decode ? c->sa_pos : 0);
+  // bf16 prefill: q/k arrive rotated and v transposed from the QKV epilogue
+  const bool vt_ok = c->dtype == DREAMER_BF16 && !c->decode && c->d == 64 && c->s % 8 == 0;
+  w.vt = vt_ok ? b.take((size_t)T * h * es) : nullptr;
+  w.sa_ws_bytes = seq_attn_ws(c->dtype, c->b, c->s, c->H, c->d, c->decode ? c->sa_pos : 0,
+                              vt_ok ? 1 : 0);
   w.sa_ws = w.sa_ws_bytes ? b.take(w.sa_ws_bytes) : nullptr;
   return w;
 }
@@ -516,7 +521,9 @@ static int validate_layer(const dreamer_layer_cfg* c, const dreamer_layer_weight
     if (rc) return rc;
     if (!w->w_pr || !w->pkeys) return fail(DREAMER_E_INVAL, "layer: null projection router");
   }
-  if (c->dtype == DREAMER_BF16 && c->h % 64) return fail(DREAMER_E_UNSUPPORTED, "layer: h %% 64 != 0");
+  if (c->dtype == DREAMER_BF16 && (c->h % 128 || c->d != 64))
+    return fail(DREAMER_E_UNSUPPORTED, "layer: bf16 needs head dim 64 and h %% 128 == 0");
+  if (c->dtype == DREAMER_F32 && c->h % 8) return fail(DREAMER_E_UNSUPPORTED, "layer: h %% 8 != 0");
   if (!w->g || !w->w_qkv || !w->w_o) return fail(DREAMER_E_INVAL, "layer: null projection weights");
   if (!(c->rope_base > 0.0)) return fail(DREAMER_E_INVAL, "layer: rope_base must be > 0");
   return ok();
@@ -609,10 +616,29 @@ int dreamer_layer_forward(const dreamer_layer_cfg* cfg, const dreamer_layer_weig
       gq.G = Ep;
       gq.tile_m = 64;
     }
+    // q/k leave the projection rotated (SA by position, DA by depth) and rounded once
+    if (dt == DREAMER_BF16) {
+      gq.qkv_h = (int)h;
+      gq.seq = c.s;
+      gq.pos_fixed = c.decode ? (int)c.sa_pos : -1;
+      gq.sa_rope = c.sa_rope;
+      gq.depth_l = l;
+      gq.depth_L = L;
+      gq.cos_s = lw.cos_s;
+      gq.sin_s = lw.sin_s;
+      gq.cos_d = lw.cos_d;
+      gq.sin_d = lw.sin_d;
+      gq.vt = lw.vt;
+    }
     TB(DREAMER_KC_GEMM);
     rc = launch_gemm(gq, dt, 0, st);
     TE(DREAMER_KC_GEMM);
     if (rc) return fail(DREAMER_E_UNSUPPORTED, "layer: QKV projection shape");
+    if (dt == DREAMER_F32) {
+      rc = launch_qkv_rope(dt, T, c.H, c.d, c.s, c.decode ? (int)c.sa_pos : -1, c.sa_rope, l,
+                           L, lw.qkv, lw.cos_s, lw.sin_s, lw.cos_d, lw.sin_d, st);
+      if (rc) return fail(DREAMER_E_UNSUPPORTED, "layer: head dim for RoPE");
+    }
     char* qkv = (char*)lw.qkv;
     char* att = (char*)lw.att;
     // ---- SA at depth l
@@ -620,8 +646,8 @@ int dreamer_layer_forward(const dreamer_layer_cfg* cfg, const dreamer_layer_weig
     void* sv = sa_v ? (char*)sa_v + (size_t)l * c.b * cap * h * es : nullptr;
     TB(DREAMER_KC_SEQ_ATTN);
     rc = launch_seq_attn(dt, c.b, c.s, c.H, c.d, pos0, qkv, 6 * h, qkv + h * es, 6 * h,
-                         qkv + 2 * h * es, 6 * h, sk, sv, cap, att, 2 * h, lw.cos_s, lw.sin_s,
-                         scale, c.sa_rope, lw.sa_ws, lw.sa_ws_bytes, st);
+                         qkv + 2 * h * es, 6 * h, lw.vt, sk, sv, cap, att, 2 * h, lw.cos_s,
+                         lw.sin_s, scale, 0, lw.sa_ws, lw.sa_ws_bytes, st);
     TE(DREAMER_KC_SEQ_ATTN);
     if (rc) return fail(DREAMER_E_UNSUPPORTED, "layer: sequence attention shape (%d)", rc);
     // ---- DA over depths 0..l
@@ -629,7 +655,7 @@ int dreamer_layer_forward(const dreamer_layer_cfg* cfg, const dreamer_layer_weig
       TB(DREAMER_KC_DEPTH_ATTN);
       rc = launch_depth_attn(dt, T, c.H, c.d, l, L, qkv + 3 * h * es, 6 * h, qkv + 4 * h * es,
                              6 * h, qkv + 5 * h * es, 6 * h, DAk, DAv, att + h * es, 2 * h,
-                             lw.cos_d, lw.sin_d, scale, st);
+                             lw.cos_d, lw.sin_d, scale, 0, st);
       TE(DREAMER_KC_DEPTH_ATTN);
       if (rc) return fail(DREAMER_E_UNSUPPORTED, "layer: depth attention shape");
     }

@@ -8,6 +8,14 @@
 
 namespace dreamer {
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int N>
+DEV void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // ------------------------------------------------------------------------- RoPE tables
 __global__ void rope_table_kernel(int D, int npos, double base, float* c, float* s) {
   const int half = D / 2;
@@ -49,10 +57,10 @@ DEV void rope_chunk(float* x, int c, int d, int pos_fwd, int pos_rev, const floa
 
 // ----------------------------------------------------------------------- depth attention
 // One lane per 16-byte chunk of a row; LPH = d / VEC lanes per head (aligned groups in a
-// wave).  Per row and head: rotate q and k_new (depth RoPE, half reversed), store the
-// rotated key and the value into cache slot l, then stream slots 0..l with an online
-// softmax.  The current slot is used from registers.
-template <typename T, int LPH>
+// wave).  Per row and head: (ROPE) rotate q and k_new by depth, half reversed, and round
+// them to storage precision; store the key and the value into cache slot l, then stream
+// slots 0..l with an online softmax.  The current slot is used from registers.
+template <typename T, int LPH, bool ROPE>
 __global__ __launch_bounds__(256) void depth_attn_kernel(
     int64_t rows, int H, int d, int l, int L, const T* __restrict__ q, int64_t ldq,
     const T* __restrict__ kn, int64_t ldk, const T* __restrict__ vn, int64_t ldv,
@@ -65,19 +73,21 @@ __global__ __launch_bounds__(256) void depth_attn_kernel(
   const int64_t row = gid / cpr;
   if (row >= rows) return;  // whole heads leave together (cpr is a multiple of LPH)
   const int chunk = (int)(gid % cpr);
-  const int c = chunk % LPH;
   const int col = chunk * VEC;
 
   float qv[VEC], kv[VEC], vv[VEC];
   load16(q + row * ldq + col, qv);
   load16(kn + row * ldk + col, kv);
   load16(vn + row * ldv + col, vv);
-  rope_chunk<VEC, LPH>(qv, c, d, l, L - 1 - l, cosd, sind);
-  rope_chunk<VEC, LPH>(kv, c, d, l, L - 1 - l, cosd, sind);
+  if constexpr (ROPE) {
+    const int c = chunk % LPH;
+    rope_chunk<VEC, LPH>(qv, c, d, l, L - 1 - l, cosd, sind);
+    rope_chunk<VEC, LPH>(kv, c, d, l, L - 1 - l, cosd, sind);
 #pragma unroll
-  for (int i = 0; i < VEC; ++i) {
-    qv[i] = round_to<T>(qv[i]);
-    kv[i] = round_to<T>(kv[i]);
+    for (int i = 0; i < VEC; ++i) {
+      qv[i] = round_to<T>(qv[i]);
+      kv[i] = round_to<T>(kv[i]);
+    }
   }
   T* krow = kc + row * (int64_t)L * h + col;
   T* vrow = vc + row * (int64_t)L * h + col;
@@ -117,40 +127,112 @@ __global__ __launch_bounds__(256) void depth_attn_kernel(
 int launch_depth_attn(int dtype, int64_t rows, int H, int d, int l, int L, const void* q,
                       int64_t ldq, const void* kn, int64_t ldk, const void* vn, int64_t ldv,
                       void* kc, void* vc, void* out, int64_t ldo, const float* cosd,
-                      const float* sind, float scale, hipStream_t st) {
+                      const float* sind, float scale, int rope, hipStream_t st) {
   const int vec = dtype == DT_BF16 ? 8 : 4;
   const int lph = d / vec;
   const int64_t threads = rows * (int64_t)(H * d / vec);
   if (threads <= 0) return 0;
   const unsigned grid = (unsigned)((threads + 255) / 256);
-#define DA_CASE(T, LP)                                                                  \
-  depth_attn_kernel<T, LP><<<grid, 256, 0, st>>>(                                       \
+#define DA_LAUNCH(T, LP, R)                                                              \
+  depth_attn_kernel<T, LP, R><<<grid, 256, 0, st>>>(                                     \
       rows, H, d, l, L, (const T*)q, ldq, (const T*)kn, ldk, (const T*)vn, ldv, (T*)kc, \
       (T*)vc, (T*)out, ldo, cosd, sind, scale)
+#define DA_CASE(T, LP)                 \
+  if (rope) DA_LAUNCH(T, LP, true);    \
+  else DA_LAUNCH(T, LP, false);        \
+  break;
   if (dtype == DT_BF16) {
     switch (lph) {
-      case 2: DA_CASE(bf16, 2); break;
-      case 4: DA_CASE(bf16, 4); break;
-      case 8: DA_CASE(bf16, 8); break;
-      case 16: DA_CASE(bf16, 16); break;
+      case 2: DA_CASE(bf16, 2)
+      case 4: DA_CASE(bf16, 4)
+      case 8: DA_CASE(bf16, 8)
+      case 16: DA_CASE(bf16, 16)
       default: return -1;
     }
   } else {
     switch (lph) {
-      case 2: DA_CASE(float, 2); break;
-      case 4: DA_CASE(float, 4); break;
-      case 8: DA_CASE(float, 8); break;
-      case 16: DA_CASE(float, 16); break;
-      case 32: DA_CASE(float, 32); break;
+      case 2: DA_CASE(float, 2)
+      case 4: DA_CASE(float, 4)
+      case 8: DA_CASE(float, 8)
+      case 16: DA_CASE(float, 16)
+      case 32: DA_CASE(float, 32)
       default: return -1;
     }
   }
 #undef DA_CASE
+#undef DA_LAUNCH
+  return 0;
+}
+
+// --------------------------------------------- in-place RoPE of a [T, 6h] QKV buffer
+// Rotates SA q/k by sequence position (when sa_rope) and DA q/k by depth; used where
+// the projection kernel does not rotate in its epilogue (float32 storage).
+template <typename T, int LPH>
+__global__ __launch_bounds__(256) void qkv_rope_kernel(int64_t rows, int H, int d, int seq,
+                                                       int pos_fixed, int sa_rope, int l,
+                                                       int L, T* __restrict__ qkv,
+                                                       const float* __restrict__ cs,
+                                                       const float* __restrict__ sn,
+                                                       const float* __restrict__ cd,
+                                                       const float* __restrict__ sd) {
+  constexpr int VEC = Vec16<T>::N;
+  const int h = H * d, cpr = h / VEC;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t unit = gid / cpr;  // (row, section in {SA q, SA k, DA q, DA k})
+  if (unit >= rows * 4) return;
+  const int64_t row = unit >> 2;
+  const int sec = (int)(unit & 3);
+  const int chunk = (int)(gid % cpr), c = chunk % LPH;
+  const int col = (sec < 2 ? sec : sec + 1) * h + chunk * VEC;
+  T* p = qkv + row * 6 * (int64_t)h + col;
+  float x[VEC];
+  load16(p, x);
+  if (sec < 2) {
+    if (!sa_rope) return;  // whole rows of a section leave together
+    const int pos = pos_fixed >= 0 ? pos_fixed : (int)(row % seq);
+    rope_chunk<VEC, LPH>(x, c, d, pos, pos, cs, sn);
+  } else {
+    rope_chunk<VEC, LPH>(x, c, d, l, L - 1 - l, cd, sd);
+  }
+  store16(p, x);
+}
+
+int launch_qkv_rope(int dtype, int64_t rows, int H, int d, int seq, int pos_fixed,
+                    int sa_rope, int l, int L, void* qkv, const float* cs, const float* sn,
+                    const float* cd, const float* sd, hipStream_t st) {
+  const int vec = dtype == DT_BF16 ? 8 : 4;
+  const int lph = d / vec;
+  const int64_t threads = rows * 4 * (int64_t)(H * d / vec);
+  if (threads <= 0) return 0;
+  const unsigned grid = (unsigned)((threads + 255) / 256);
+#define QR_CASE(T, LP)                                                                   \
+  qkv_rope_kernel<T, LP><<<grid, 256, 0, st>>>(rows, H, d, seq, pos_fixed, sa_rope, l, L, \
+                                               (T*)qkv, cs, sn, cd, sd);                 \
+  break;
+  if (dtype == DT_BF16) {
+    switch (lph) {
+      case 2: QR_CASE(bf16, 2)
+      case 4: QR_CASE(bf16, 4)
+      case 8: QR_CASE(bf16, 8)
+      case 16: QR_CASE(bf16, 16)
+      default: return -1;
+    }
+  } else {
+    switch (lph) {
+      case 2: QR_CASE(float, 2)
+      case 4: QR_CASE(float, 4)
+      case 8: QR_CASE(float, 8)
+      case 16: QR_CASE(float, 16)
+      default: return -1;
+    }
+  }
+#undef QR_CASE
   return 0;
 }
 
 // ------------------------------------------------- SA: rotate new keys into a key buffer
-// dst_k[b, pos0 + i] = RoPE_seq(k_new[b, i]) (rounded), dst_v[b, pos0 + i] = v_new[b, i].
+// dst_k[b, pos0 + i] = RoPE_seq(k_new[b, i]) (rounded; a copy when rope == 0),
+// dst_v[b, pos0 + i] = v_new[b, i].
 template <typename T, int LPH>
 __global__ __launch_bounds__(256) void sa_rope_store_kernel(
     int B, int n, int H, int d, int64_t pos0, const T* __restrict__ kn, int64_t ldk,
@@ -196,9 +278,11 @@ __global__ void sa_rows_kernel(int B, int n, int H, int d, int64_t pos0, const T
   if (chunk >= h / VEC) return;
   float qv[VEC];
   load16(q + row * ldq + col, qv);
-  if (rope) rope_chunk<VEC, LPH>(qv, c, d, (int)qpos, (int)qpos, cs, sn);
+  if (rope) {
+    rope_chunk<VEC, LPH>(qv, c, d, (int)qpos, (int)qpos, cs, sn);
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) qv[e] = round_to<T>(qv[e]);
+    for (int e = 0; e < VEC; ++e) qv[e] = round_to<T>(qv[e]);
+  }
   float m = -INFINITY, lsum = 0.f, acc[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
@@ -261,57 +345,67 @@ __global__ void sa_combine_kernel(int64_t nrows, int H, int d, int nsplit,
 }
 
 // ------------------------------------------------------------ SA: MFMA flash prefill
-// bf16, d == 64.  Block = 4 waves = 64 queries of one (batch, head); wave w owns 16.
+// bf16, d == 64, q/k already rotated, v given transposed per (batch, head):
+// vt [B][H][64][S].  Block = 4 waves = 64 queries of one (batch, head); wave w owns 16.
 // S^T = K Q^T (keys on rows) so that every lane owns one query column: the online
 // softmax statistics stay in the lane (plus the 4 lane groups, joined by two shuffles),
-// and P feeds O^T = V^T P^T straight from registers.  K tiles (64 keys) are rotated
-// while being staged into LDS; V tiles are staged transposed.
+// and P feeds O^T = V^T P^T straight from registers.  K and V^T tiles of 64 keys stream
+// through a 3-stage LDS ring filled by direct global->LDS loads (128-byte rows, 16-byte
+// chunks XOR-swizzled by row).  Requires S % 8 == 0.
 namespace fa {
-constexpr int BQ = 64, BKEY = 64, D = 64, LDK = D + 8, LDV = BKEY + 8;
+constexpr int BQ = 64, BKEY = 64, NSTG = 3, TILE = 8192;  // bytes per K or V^T tile
 }
 
-__global__ __launch_bounds__(256) void sa_flash_kernel(
-    int B, int S, int H, const bf16* __restrict__ q, int64_t ldq, const bf16* __restrict__ kn,
-    int64_t ldk, const bf16* __restrict__ vn, int64_t ldv, bf16* __restrict__ out,
-    int64_t ldo, const float* __restrict__ cs, const float* __restrict__ sn, int rope,
+DEV int swz128(int row, int c) { return row * 64 + ((c ^ (row & 7)) << 3); }  // elements
+
+__global__ __launch_bounds__(256, 2) void sa_flash_kernel(
+    int B, int S, int H, const bf16* __restrict__ q, int64_t ldq, const bf16* __restrict__ kk,
+    int64_t ldk, const bf16* __restrict__ vt, bf16* __restrict__ out, int64_t ldo,
     float scale) {
   using namespace fa;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[BKEY * LDK];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[D * LDV];
+  __shared__ __attribute__((aligned(1024))) char stg[NSTG][2 * TILE];
   const int nqb = (S + BQ - 1) / BQ;
   const int qb = nqb - 1 - (int)blockIdx.x;  // heavy (late) query blocks first
   const int head = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int64_t tok0 = (int64_t)b * S;
-  const int hoff = head * D;
-  constexpr int HALF = D / 2;
+  const int hoff = head * 64;
 
   // Q^T fragments: lane (query lr of wave w, group lg) holds dims 8lg..+8 (k-step 0)
-  // and 32+8lg..+8 (k-step 1): one rotate-half pair, rotated in registers.
+  // and 32+8lg..+8 (k-step 1)
   const int qpos = qb * BQ + w * 16 + lr;
   const int qrow = min(qpos, S - 1);
   bf16x8 qf[2];
-  {
-    float a[8], bb[8];
-    load16(q + (tok0 + qrow) * ldq + hoff + lg * 8, a);
-    load16(q + (tok0 + qrow) * ldq + hoff + HALF + lg * 8, bb);
-    if (rope) {
+  qf[0] = *reinterpret_cast<const bf16x8*>(q + (tok0 + qrow) * ldq + hoff + lg * 8);
+  qf[1] = *reinterpret_cast<const bf16x8*>(q + (tok0 + qrow) * ldq + hoff + 32 + lg * 8);
+
+  // loads of one stage: 16 instructions of 1 KiB (8 for K rows, 8 for V^T rows); wave w
+  // issues instructions j = w + 4 i.  Lane -> (row lane/8, slot lane%8) of 8 rows.
+  const int lrow = lane >> 3, slot = lane & 7;
+  const bf16* vbase = vt + ((int64_t)(b * H + head) * 64) * S;
+  auto issue = [&](int t) {
+    char* sb = stg[t % NSTG];
+    const int kbase = t * BKEY;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int p = lg * 8 + i;
-        const float cv = cs[qrow * HALF + p], sv = sn[qrow * HALF + p];
-        const float x = a[i], y = bb[i];
-        a[i] = x * cv - y * sv;
-        bb[i] = y * cv + x * sv;
+    for (int i = 0; i < 4; ++i) {
+      const int j = w + 4 * i;
+      const bf16* src;
+      if (j < 8) {  // K rows (keys)
+        const int key = j * 8 + lrow;
+        const int c = slot ^ (key & 7);
+        const int kp = min(kbase + key, S - 1);
+        src = kk + (tok0 + kp) * ldk + hoff + c * 8;
+      } else {      // V^T rows (dims)
+        const int dim = (j - 8) * 8 + lrow;
+        const int c = slot ^ (dim & 7);
+        const int p0 = min(kbase + c * 8, S - 8);
+        src = vbase + (int64_t)dim * S + p0;
       }
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(sb + j * 1024), 16, 0, 0);
     }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      qf[0][i] = (bf16)a[i];
-      qf[1][i] = (bf16)bb[i];
-    }
-  }
+  };
+
   const float sl2 = scale * 1.44269504088896341f;  // scale * log2(e)
   float m = -INFINITY, lsum = 0.f;
   floatx4 o[4];
@@ -319,52 +413,18 @@ __global__ __launch_bounds__(256) void sa_flash_kernel(
   for (int t = 0; t < 4; ++t) o[t] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   const int qlast = min(qb * BQ + BQ, S) - 1;
+  const int qlim = min(qpos, S - 1);
   const int nkt = qlast / BKEY + 1;
+  issue(0);
+  if (nkt > 1) issue(1);
   for (int kt = 0; kt < nkt; ++kt) {
+    if (kt + 1 < nkt) wait_vm<4>();
+    else wait_vm<0>();
+    __syncthreads();
+    if (kt + 2 < nkt) issue(kt + 2);
+    const bf16* Ks = reinterpret_cast<const bf16*>(stg[kt % NSTG]);
+    const bf16* Vs = Ks + TILE / 2;
     const int kbase = kt * BKEY;
-    __syncthreads();
-    {  // stage K (rotated): thread -> key tid/4, pair part tid%4
-      const int key = tid >> 2, part = tid & 3;
-      const int kp = kbase + key;
-      float a[8], bb[8];
-      if (kp < S) {
-        load16(kn + (tok0 + kp) * ldk + hoff + part * 8, a);
-        load16(kn + (tok0 + kp) * ldk + hoff + HALF + part * 8, bb);
-        if (rope) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int p = part * 8 + i;
-            const float cv = cs[kp * HALF + p], sv = sn[kp * HALF + p];
-            const float x = a[i], y = bb[i];
-            a[i] = x * cv - y * sv;
-            bb[i] = y * cv + x * sv;
-          }
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) a[i] = bb[i] = 0.f;
-      }
-      bf16x8 va, vb;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) { va[i] = (bf16)a[i]; vb[i] = (bf16)bb[i]; }
-      *reinterpret_cast<bf16x8*>(&Ks[key * LDK + part * 8]) = va;
-      *reinterpret_cast<bf16x8*>(&Ks[key * LDK + HALF + part * 8]) = vb;
-    }
-    {  // stage V transposed: thread -> key tid%64, dims 16*(tid/64)..+16
-      const int key = tid & 63, dp = tid >> 6;
-      const int kp = kbase + key;
-      bf16x8 v0 = {}, v1 = {};
-      if (kp < S) {
-        v0 = *reinterpret_cast<const bf16x8*>(vn + (tok0 + kp) * ldv + hoff + dp * 16);
-        v1 = *reinterpret_cast<const bf16x8*>(vn + (tok0 + kp) * ldv + hoff + dp * 16 + 8);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        Vt[(dp * 16 + i) * LDV + key] = v0[i];
-        Vt[(dp * 16 + 8 + i) * LDV + key] = v1[i];
-      }
-    }
-    __syncthreads();
 
     // S^T tiles: 4 key tiles of 16, K = 64 dims in two steps.
     floatx4 sacc[4];
@@ -374,19 +434,18 @@ __global__ __launch_bounds__(256) void sa_flash_kernel(
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(&Ks[(t * 16 + lr) * LDK + ks * 32 + lg * 8]);
+            *reinterpret_cast<const bf16x8*>(&Ks[swz128(t * 16 + lr, ks * 4 + lg)]);
         sacc[t] = mfma16(kf, qf[ks], sacc[t]);
       }
     }
     // mask + tile max (lane holds keys kbase + 16t + 4lg + i for query qpos)
     float tmax = -INFINITY;
-    const int qlim = min(qpos, S - 1);
+    const bool diag = kbase + BKEY - 1 > qb * BQ;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int kp = kbase + t * 16 + lg * 4 + i;
-        if (kp > qlim) sacc[t][i] = -INFINITY;
+        if (diag && kbase + t * 16 + lg * 4 + i > qlim) sacc[t][i] = -INFINITY;
         tmax = fmaxf(tmax, sacc[t][i]);
       }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
@@ -412,15 +471,18 @@ __global__ __launch_bounds__(256) void sa_flash_kernel(
         ph[cc][j] = hi;
         pl[cc][j] = (bf16)(p - (float)hi);
       }
-    // O^T += V^T P^T : 4 dim tiles x 2 key chunks
+    // O^T += V^T P^T : 4 dim tiles x 2 key chunks.  Lane (dim 16t + lr, group lg) takes
+    // keys 32cc + 4lg + 0..3 and 32cc + 16 + 4lg + 0..3 of its V^T row.
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
-        const bf16* vrow = &Vt[(t * 16 + lr) * LDV + cc * 32 + lg * 4];
+        const int dim = t * 16 + lr;
+        const bf16x4 lo4 = *reinterpret_cast<const bf16x4*>(
+            &Vs[swz128(dim, 4 * cc + (lg >> 1)) + (lg & 1) * 4]);
+        const bf16x4 hi4 = *reinterpret_cast<const bf16x4*>(
+            &Vs[swz128(dim, 4 * cc + 2 + (lg >> 1)) + (lg & 1) * 4]);
         bf16x8 vf;
-        const bf16x4 lo4 = *reinterpret_cast<const bf16x4*>(vrow);
-        const bf16x4 hi4 = *reinterpret_cast<const bf16x4*>(vrow + 16);
 #pragma unroll
         for (int j = 0; j < 4; ++j) { vf[j] = lo4[j]; vf[4 + j] = hi4[j]; }
         o[t] = mfma16(vf, ph[cc], o[t]);
@@ -441,12 +503,61 @@ __global__ __launch_bounds__(256) void sa_flash_kernel(
   }
 }
 
+// Prepares flash inputs from unrotated projections: qr/kr [B, S, H, 64] rotated (when
+// rope) and rounded, vt [B][H][64][S].  Thread -> (row, head, chunk pair c < 4).
+__global__ __launch_bounds__(256) void sa_prep_kernel(int B, int S, int H, const bf16* __restrict__ q,
+                                                      int64_t ldq, const bf16* __restrict__ k,
+                                                      int64_t ldk, const bf16* __restrict__ v,
+                                                      int64_t ldv, bf16* __restrict__ qr,
+                                                      bf16* __restrict__ kr, bf16* __restrict__ vt,
+                                                      const float* __restrict__ cs,
+                                                      const float* __restrict__ sn, int rope) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t unit = gid >> 2;  // (row, head)
+  if (unit >= (int64_t)B * S * H) return;
+  const int c = (int)(gid & 3);
+  const int64_t row = unit / H;
+  const int head = (int)(unit % H);
+  const int pos = (int)(row % S);
+  const int64_t h = (int64_t)H * 64;
+  const bf16* srcs[2] = {q + row * ldq, k + row * ldk};
+  bf16* dsts[2] = {qr + row * h, kr + row * h};
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    float lo[8], hi[8];
+    load16(srcs[s] + head * 64 + c * 8, lo);
+    load16(srcs[s] + head * 64 + 32 + c * 8, hi);
+    if (rope) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int pair = c * 8 + e;
+        const float cv = cs[pos * 32 + pair], sv = sn[pos * 32 + pair];
+        const float x = lo[e], y = hi[e];
+        lo[e] = x * cv - y * sv;
+        hi[e] = y * cv + x * sv;
+      }
+    }
+    store16(dsts[s] + head * 64 + c * 8, lo);
+    store16(dsts[s] + head * 64 + 32 + c * 8, hi);
+  }
+  // v^T: this thread writes dims c*16..c*16+15 of (row, head)
+  const int64_t bb = row / S;
+  const bf16* vr = v + row * ldv + head * 64 + c * 16;
+  bf16* vo = vt + ((bb * H + head) * 64 + c * 16) * S + pos;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) vo[(int64_t)e * S] = vr[e];
+}
+
 // ------------------------------------------------------------------------------ launch
 static int lph_of(int dtype, int d) { return d / (dtype == DT_BF16 ? 8 : 4); }
 
 constexpr int SA_SPLIT_SPAN = 256;
 
-size_t seq_attn_ws(int dtype, int B, int q_len, int H, int d, int64_t pos0) {
+static bool flash_ok(int dtype, int d, int q_len) {
+  return dtype == DT_BF16 && d == 64 && q_len % 8 == 0;
+}
+
+size_t seq_attn_ws(int dtype, int B, int q_len, int H, int d, int64_t pos0, int prepared) {
   const size_t es = dtype == DT_BF16 ? 2 : 4;
   const size_t h = (size_t)H * d;
   if (pos0 > 0) {  // decode: split partials
@@ -454,7 +565,7 @@ size_t seq_attn_ws(int dtype, int B, int q_len, int H, int d, int64_t pos0) {
     const size_t rows = (size_t)B * q_len;
     return rows * nsplit * h * 4 + rows * nsplit * H * 2 * 4 + 512;
   }
-  if (dtype == DT_BF16 && d == 64) return 0;  // flash kernel reads q/k/v directly
+  if (flash_ok(dtype, d, q_len)) return prepared ? 0 : 3 * (size_t)B * q_len * h * es + 1024;
   return 2 * (size_t)B * q_len * h * es + 512;  // rotated key / value buffers
 }
 
@@ -513,58 +624,72 @@ static int sa_rows(int lph, int B, int n, int H, int d, int64_t pos0, const void
 
 int launch_seq_attn(int dtype, int B, int q_len, int H, int d, int64_t pos0, const void* q,
                     int64_t ldq, const void* kn, int64_t ldk, const void* vn, int64_t ldv,
-                    void* kc, void* vc, int64_t cap, void* out, int64_t ldo,
-                    const float* cos_s, const float* sin_s, float scale, int sa_rope,
-                    void* ws, size_t ws_bytes, hipStream_t st) {
+                    const void* vt, void* kc, void* vc, int64_t cap, void* out, int64_t ldo,
+                    const float* cos_s, const float* sin_s, float scale, int rope, void* ws,
+                    size_t ws_bytes, hipStream_t st) {
   const int lph = lph_of(dtype, d);
   const size_t es = dtype == DT_BF16 ? 2 : 4;
   const int64_t h = (int64_t)H * d;
   if (B <= 0 || q_len <= 0) return 0;
-  if (ws_bytes < seq_attn_ws(dtype, B, q_len, H, d, pos0)) return -2;
+  const bool prepared = !rope && vt;
+  if (ws_bytes < seq_attn_ws(dtype, B, q_len, H, d, pos0, prepared)) return -2;
   const bool bf = dtype == DT_BF16;
   if (pos0 > 0) {
-    // decode: append the rotated new key/value at pos0, then split-K over 0..pos0
+    // decode: append the (rotated) new key/value at pos0, then split-K over 0..pos0
     int rc = bf ? sa_rope_store<bf16>(lph, B, q_len, H, d, pos0, kn, ldk, vn, ldv, kc, vc,
-                                      cap, cos_s, sin_s, sa_rope, st)
+                                      cap, cos_s, sin_s, rope, st)
                 : sa_rope_store<float>(lph, B, q_len, H, d, pos0, kn, ldk, vn, ldv, kc, vc,
-                                       cap, cos_s, sin_s, sa_rope, st);
+                                       cap, cos_s, sin_s, rope, st);
     if (rc) return rc;
     const int nsplit = (int)((pos0 + 1 + SA_SPLIT_SPAN - 1) / SA_SPLIT_SPAN);
     float* pa = (float*)ws;
     float* pm = pa + (size_t)B * q_len * nsplit * h;
     return bf ? sa_rows<bf16>(lph, B, q_len, H, d, pos0, q, ldq, kc, vc, cap, out, ldo,
-                              cos_s, sin_s, sa_rope, scale, nsplit, SA_SPLIT_SPAN, pa, pm, st)
+                              cos_s, sin_s, rope, scale, nsplit, SA_SPLIT_SPAN, pa, pm, st)
               : sa_rows<float>(lph, B, q_len, H, d, pos0, q, ldq, kc, vc, cap, out, ldo,
-                               cos_s, sin_s, sa_rope, scale, nsplit, SA_SPLIT_SPAN, pa, pm,
-                               st);
+                               cos_s, sin_s, rope, scale, nsplit, SA_SPLIT_SPAN, pa, pm, st);
   }
   // prefill
   if (kc) {
     int rc = bf ? sa_rope_store<bf16>(lph, B, q_len, H, d, 0, kn, ldk, vn, ldv, kc, vc, cap,
-                                      cos_s, sin_s, sa_rope, st)
+                                      cos_s, sin_s, rope, st)
                 : sa_rope_store<float>(lph, B, q_len, H, d, 0, kn, ldk, vn, ldv, kc, vc, cap,
-                                       cos_s, sin_s, sa_rope, st);
+                                       cos_s, sin_s, rope, st);
     if (rc) return rc;
   }
-  if (bf && d == 64) {
+  if (flash_ok(dtype, d, q_len)) {
+    const bf16 *fq = (const bf16*)q, *fk = (const bf16*)kn, *fvt = (const bf16*)vt;
+    int64_t fldq = ldq, fldk = ldk;
+    if (!prepared) {
+      bf16* qr = (bf16*)ws;
+      bf16* kr = qr + (size_t)B * q_len * h;
+      bf16* vtt = kr + (size_t)B * q_len * h;
+      const int64_t units = (int64_t)B * q_len * H * 4;
+      sa_prep_kernel<<<(unsigned)((units + 255) / 256), 256, 0, st>>>(
+          B, q_len, H, (const bf16*)q, ldq, (const bf16*)kn, ldk, (const bf16*)vn, ldv, qr,
+          kr, vtt, cos_s, sin_s, rope);
+      fq = qr;
+      fk = kr;
+      fvt = vtt;
+      fldq = fldk = h;
+    }
     dim3 grid((q_len + fa::BQ - 1) / fa::BQ, H, B);
-    sa_flash_kernel<<<grid, 256, 0, st>>>(B, q_len, H, (const bf16*)q, ldq, (const bf16*)kn,
-                                          ldk, (const bf16*)vn, ldv, (bf16*)out, ldo, cos_s,
-                                          sin_s, sa_rope, scale);
+    sa_flash_kernel<<<grid, 256, 0, st>>>(B, q_len, H, fq, fldq, fk, fldk, fvt, (bf16*)out,
+                                          ldo, scale);
     return 0;
   }
-  // generic: rotated keys into ws, then one row-streaming pass
+  // generic: (rotated) keys into ws, then one row-streaming pass
   char* kb = (char*)ws;
   char* vb = kb + (size_t)B * q_len * h * es;
   int rc = bf ? sa_rope_store<bf16>(lph, B, q_len, H, d, 0, kn, ldk, vn, ldv, kb, vb, q_len,
-                                    cos_s, sin_s, sa_rope, st)
+                                    cos_s, sin_s, rope, st)
               : sa_rope_store<float>(lph, B, q_len, H, d, 0, kn, ldk, vn, ldv, kb, vb, q_len,
-                                     cos_s, sin_s, sa_rope, st);
+                                     cos_s, sin_s, rope, st);
   if (rc) return rc;
   return bf ? sa_rows<bf16>(lph, B, q_len, H, d, 0, q, ldq, kb, vb, q_len, out, ldo, cos_s,
-                            sin_s, sa_rope, scale, 1, q_len, nullptr, nullptr, st)
+                            sin_s, rope, scale, 1, q_len, nullptr, nullptr, st)
             : sa_rows<float>(lph, B, q_len, H, d, 0, q, ldq, kb, vb, q_len, out, ldo, cos_s,
-                             sin_s, sa_rope, scale, 1, q_len, nullptr, nullptr, st);
+                             sin_s, rope, scale, 1, q_len, nullptr, nullptr, st);
 }
 
 }  // namespace dreamer

@@ -1,0 +1,234 @@
+// Fused expert FFN for bf16 storage (SwiGLU or GELU) over routed slots.
+//
+// One block = one 64-row tile of one expert's slots (tiles listed by toff).  GEMM1
+// (x W1^T and, for SwiGLU, x W3^T) streams 32-wide K slices of the gathered token rows and
+// of the expert's weight rows through a multi-stage LDS ring filled by direct
+// global->LDS loads (global_load_lds_dwordx4: no staging registers, several slices in
+// flight per wave).  Slices are stored as 64-byte rows whose 16-byte chunks are
+// XOR-swizzled by row (chunk c of row r at slot c ^ ((r >> 2) & 3)), so the 16 rows
+// one MFMA fragment read touches fall into distinct banks.  Wave w owns hidden columns
+// [w F/4, (w+1) F/4) of both projections, so the activation is lane-local.  The hidden
+// tile goes to LDS (bf16), GEMM2 (H W2^T) runs over 256-column chunks whose gate-scaled
+// bf16 results are staged in LDS and written per slot with 16-byte stores.
+#include "common.h"
+#include "kernels.h"
+
+namespace dreamer {
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Wait until at most N vector-memory operations of this wave are outstanding (gfx9
+// s_waitcnt encoding: vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt left at max).
+template <int N>
+DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+DEV int swz64(int row, int c) { return row * 64 + ((c ^ ((row >> 2) & 3)) << 4); }
+
+template <int F, int KIND>
+struct FfnShape {
+  static constexpr int NW1 = KIND == FFN_SWIGLU ? 2 : 1;  // GEMM1 weight matrices
+  static constexpr int XB = 64 * 64;                       // X slice: 64 rows x 32 bf16
+  static constexpr int WB = F * 64;                        // one weight slice
+  static constexpr int STAGE = XB + NW1 * WB;
+  static constexpr int NI = STAGE / 1024;                  // 1 KiB load instructions
+  static constexpr int LPW = NI / 4;                       // per wave per stage
+  static constexpr int LDH = F + 8;
+  static constexpr int HS_BYTES = 64 * LDH * 2;
+  static constexpr int NS0 = (76 * 1024 - HS_BYTES) / STAGE;
+  static constexpr int NS = NS0 > 8 ? 8 : NS0;             // ring depth (2 blocks / CU)
+  static constexpr int OUT_COLS = 256;                     // GEMM2 chunk
+  static_assert(NI % 4 == 0, "stage must split evenly over 4 waves");
+  static_assert(NS >= 2 && NS * STAGE >= 64 * OUT_COLS * 2, "LDS ring too small");
+};
+
+template <int F, int KIND>
+__global__ __launch_bounds__(256, 2) void expert_ffn_kernel(
+    int k, int h_in, int h_out, int E, const bf16* __restrict__ x,
+    const float* __restrict__ gate, const bf16* __restrict__ w1,
+    const bf16* __restrict__ w3, const bf16* __restrict__ w2, const int32_t* __restrict__ perm,
+    const int32_t* __restrict__ goff, const int32_t* __restrict__ toff,
+    bf16* __restrict__ slots) {
+  using S = FfnShape<F, KIND>;
+  constexpr int NT1 = F / 64;  // 16-col tiles per wave per projection
+  constexpr int KS2 = F / 32;  // k-steps of GEMM2
+  __shared__ __attribute__((aligned(1024))) char stg[S::NS * S::STAGE];
+  __shared__ __attribute__((aligned(16))) bf16 Hs[64 * S::LDH];
+  __shared__ int s_slot[64];
+  __shared__ float s_gate[64];
+
+  const int tile = blockIdx.x;
+  if (tile >= toff[E]) return;
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (toff[mid] <= tile) lo = mid; else hi = mid - 1;
+  }
+  const int e = lo;
+  const int r0 = goff[e] + (tile - toff[e]) * 64, r1 = goff[e + 1];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
+  if (tid < 64) {
+    const int m = r0 + tid;
+    const int s = m < r1 ? perm[m] : -1;
+    s_slot[tid] = s;
+    s_gate[tid] = s >= 0 ? gate[s] : 0.f;
+  }
+  __syncthreads();
+
+  // load descriptors: wave w issues instructions q = w + 4 j of every stage
+  const bf16* src[S::LPW];
+#pragma unroll
+  for (int j = 0; j < S::LPW; ++j) {
+    const int q = w + 4 * j;
+    const int slot = lane & 3;
+    if (q < 4) {  // gathered token rows
+      const int row = q * 16 + (lane >> 2);
+      const int s = s_slot[row] >= 0 ? s_slot[row] : s_slot[0];
+      const int c = slot ^ ((row >> 2) & 3);
+      src[j] = x + (int64_t)(s / k) * h_in + c * 8;
+    } else {      // expert weight rows
+      const int wq = q - 4, m = wq / (F / 16);
+      const int mr = (wq % (F / 16)) * 16 + (lane >> 2);
+      const int c = slot ^ ((mr >> 2) & 3);
+      const bf16* W = m == 0 ? w1 : w3;
+      src[j] = W + ((int64_t)e * F + mr) * h_in + c * 8;
+    }
+  }
+  auto issue = [&](int s) {
+    char* sb = stg + (s % S::NS) * S::STAGE;
+#pragma unroll
+    for (int j = 0; j < S::LPW; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(src[j] + s * 32),
+                                       (lds_void*)(sb + (w + 4 * j) * 1024), 16, 0, 0);
+  };
+
+  floatx4 ag[4][NT1], au[4][NT1];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT1; ++nt) {
+      ag[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      au[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+  const int nst = h_in / 32;
+  for (int s = 0; s < S::NS - 1 && s < nst; ++s) issue(s);
+  for (int s = 0; s < nst; ++s) {
+    if (s + S::NS - 2 < nst) wait_vmcnt<S::LPW * (S::NS - 2)>();
+    else wait_vmcnt<0>();
+    __syncthreads();  // stage s visible to all waves; stage s-1 fully consumed
+    if (s + S::NS - 1 < nst) issue(s + S::NS - 1);
+    const char* sb = stg + (s % S::NS) * S::STAGE;
+    bf16x8 af[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+      af[mt] = *reinterpret_cast<const bf16x8*>(sb + swz64(mt * 16 + lr, lg));
+#pragma unroll
+    for (int nt = 0; nt < NT1; ++nt) {
+      const int col = w * (F / 4) + nt * 16 + lr;
+      const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(sb + S::XB + swz64(col, lg));
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) ag[mt][nt] = mfma16(af[mt], b1, ag[mt][nt]);
+      if constexpr (KIND == FFN_SWIGLU) {
+        const bf16x8 b3 =
+            *reinterpret_cast<const bf16x8*>(sb + S::XB + S::WB + swz64(col, lg));
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) au[mt][nt] = mfma16(af[mt], b3, au[mt][nt]);
+      }
+    }
+  }
+  // activation -> LDS (row mt*16 + 4lg + i, col w*F/4 + nt*16 + lr)
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT1; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float g = ag[mt][nt][i];
+        const float hv = KIND == FFN_SWIGLU ? silu_(g) * au[mt][nt][i] : gelu_erf(g);
+        Hs[(mt * 16 + lg * 4 + i) * S::LDH + w * (F / 4) + nt * 16 + lr] = (bf16)hv;
+      }
+  __syncthreads();
+  bf16x8 hf[4][KS2];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int ks = 0; ks < KS2; ++ks)
+      hf[mt][ks] =
+          *reinterpret_cast<const bf16x8*>(&Hs[(mt * 16 + lr) * S::LDH + ks * 32 + lg * 8]);
+
+  // GEMM2 over 256-column chunks; outputs staged in the (now idle) LDS ring
+  bf16* outst = reinterpret_cast<bf16*>(stg);  // [64][OUT_COLS]
+  const bf16* W2 = w2 + (int64_t)e * h_out * F;
+  for (int nc = 0; nc < h_out; nc += S::OUT_COLS) {
+    const int cbase = nc + w * 64;
+    if (cbase < h_out) {
+      floatx4 acc[4][4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      bf16x8 bfr[4][KS2];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int ks = 0; ks < KS2; ++ks)
+          bfr[nt][ks] = *reinterpret_cast<const bf16x8*>(
+              W2 + (int64_t)(cbase + nt * 16 + lr) * F + ks * 32 + lg * 8);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int ks = 0; ks < KS2; ++ks)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+            acc[mt][nt] = mfma16(hf[mt][ks], bfr[nt][ks], acc[mt][nt]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = mt * 16 + lg * 4 + i;
+          const float gs = s_gate[row];
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt)
+            outst[row * S::OUT_COLS + w * 64 + nt * 16 + lr] = (bf16)(acc[mt][nt][i] * gs);
+        }
+    }
+    __syncthreads();
+    const int ncols = min(S::OUT_COLS, h_out - nc);
+    const int cpr = ncols / 8;
+    for (int c = tid; c < 64 * cpr; c += 256) {
+      const int row = c / cpr, cc = c % cpr;
+      const int s = s_slot[row];
+      if (s >= 0)
+        *reinterpret_cast<bf16x8*>(slots + (int64_t)s * h_out + nc + cc * 8) =
+            *reinterpret_cast<const bf16x8*>(&outst[row * S::OUT_COLS + cc * 8]);
+    }
+    __syncthreads();
+  }
+}
+
+int launch_expert_ffn(int dtype, int kind, int64_t nslots, int k, int h_in, int f, int h_out,
+                      int E, const void* x, const float* gate, const void* w1,
+                      const void* w3, const void* w2, const int32_t* perm,
+                      const int32_t* goff, const int32_t* toff, void* slots,
+                      hipStream_t st) {
+  if (nslots <= 0) return 0;
+  if (dtype == DT_F32) return -1;  // the f32 path uses launch_expert_ffn_f32
+  if (h_in % 64 || h_out % 64) return -1;
+  const unsigned grid = (unsigned)((nslots + FFN_TILE_M - 1) / FFN_TILE_M + E);
+#define EF_CASE(FF, KK)                                                                    \
+  expert_ffn_kernel<FF, KK><<<grid, 256, 0, st>>>(k, h_in, h_out, E, (const bf16*)x, gate, \
+                                                  (const bf16*)w1, (const bf16*)w3,        \
+                                                  (const bf16*)w2, perm, goff, toff,       \
+                                                  (bf16*)slots)
+  if (kind == FFN_SWIGLU && f == 64) EF_CASE(64, FFN_SWIGLU);
+  else if (kind == FFN_SWIGLU && f == 128) EF_CASE(128, FFN_SWIGLU);
+  else if (kind == FFN_GELU && f == 64) EF_CASE(64, FFN_GELU);
+  else if (kind == FFN_GELU && f == 128) EF_CASE(128, FFN_GELU);
+  else return -1;
+#undef EF_CASE
+  return 0;
+}
+
+}  // namespace dreamer

@@ -147,6 +147,85 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs a) {
             acc[i][j][v];
   __syncthreads();
   OutT* C = (OutT*)a.C;
+  if constexpr (BN == 128 && sizeof(OutT) == 2) {
+    if (a.qkv_h) {  // the tile is two heads of one section
+      const int sect = n0 / a.qkv_h, hcol0 = n0 % a.qkv_h;
+      const bool sa_qk = (sect == 0 || sect == 1) && a.sa_rope;
+      const bool da_qk = sect == 3 || sect == 4;
+      // item = (row, head of the tile, chunk c < 4): dims c*8..+8 and 32+c*8..+8 rotate
+      // together (rotate-half pairs)
+      for (int it = tid; it < BM * 8; it += 256) {
+        const int row = it >> 3, hh = (it >> 2) & 1, c = it & 3;
+        const int orow = rows_s[row];
+        if (orow < 0) continue;
+        const float sc = a.row_scale ? a.row_scale[orow] : 1.0f;
+        const int lc = hh * 64 + c * 8;
+        float lo[8], hi[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          lo[e] = Cs[row * LDC + lc + e] * sc;
+          hi[e] = Cs[row * LDC + lc + 32 + e] * sc;
+        }
+        if (sa_qk || da_qk) {
+          int pf, pr;
+          const float *cs, *sn;
+          if (sa_qk) {
+            pf = pr = a.pos_fixed >= 0 ? a.pos_fixed : orow % a.seq;
+            cs = a.cos_s;
+            sn = a.sin_s;
+          } else {
+            pf = a.depth_l;
+            pr = a.depth_L - 1 - a.depth_l;
+            cs = a.cos_d;
+            sn = a.sin_d;
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int pair = c * 8 + e;
+            const int pos = pair < 16 ? pf : pr;
+            const float cv = cs[pos * 32 + pair], sv = sn[pos * 32 + pair];
+            const float x = lo[e], y = hi[e];
+            lo[e] = x * cv - y * sv;
+            hi[e] = y * cv + x * sv;
+          }
+        }
+        OutT* cp = C + (int64_t)orow * a.ldc + n0 + lc;
+        store16(cp, lo);
+        store16(cp + 32, hi);
+      }
+      if (sect == 2 && a.vt) {  // SA v, transposed: item = (column, 8 consecutive rows)
+        constexpr int RG = BM / 8;
+        bf16* vt = (bf16*)a.vt;
+        const int H = a.qkv_h / 64;
+        for (int it = tid; it < RG * BN; it += 256) {
+          const int col = it / RG, rg = it % RG;
+          const int head = (hcol0 + col) >> 6, dim = (hcol0 + col) & 63;
+          const int o0 = rows_s[rg * 8];
+          const bool run = o0 >= 0 && rows_s[rg * 8 + 7] == o0 + 7 && (o0 % a.seq) + 7 < a.seq;
+          if (run) {
+            float vv[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+              const int orow = o0 + r;
+              const float sc = a.row_scale ? a.row_scale[orow] : 1.0f;
+              vv[r] = Cs[(rg * 8 + r) * LDC + col] * sc;
+            }
+            store16(vt + (((int64_t)(o0 / a.seq) * H + head) * 64 + dim) * a.seq + o0 % a.seq,
+                    vv);
+          } else {
+            for (int r = 0; r < 8; ++r) {
+              const int orow = rows_s[rg * 8 + r];
+              if (orow < 0) continue;
+              const float sc = a.row_scale ? a.row_scale[orow] : 1.0f;
+              vt[(((int64_t)(orow / a.seq) * H + head) * 64 + dim) * a.seq + orow % a.seq] =
+                  (bf16)(Cs[(rg * 8 + r) * LDC + col] * sc);
+            }
+          }
+        }
+      }
+      return;
+    }
+  }
   bf16* C2 = (bf16*)a.C2;
   const ResT* R = (const ResT*)a.resid;
   constexpr int CPR = BN / 8;  // 8-column chunks per row
@@ -218,13 +297,26 @@ int launch_gemm(const GemmArgs& a, int dtype, int out_f32, hipStream_t st) {
   if (a.K % 64 != 0 || a.N % 8 != 0) return -1;
   // Tile choice: 128x128 when that still gives >= 2 tiles per CU, else 64-row tiles.
   // Grouped launches use the m-tile size their tile offsets were built with.
-  int bm, bn = a.N >= 128 ? 128 : 64;
+  // Tiles: the largest of 128x128, 64x128, 64x64 that still gives >= 512 blocks (two per
+  // CU); the QKV epilogue needs 128-column tiles.
+  int bm, bn;
+  if (a.qkv_h) {
+    if (a.qkv_h % 128 || out_f32) return -1;
+    bn = 128;
+  } else {
+    bn = a.N >= 128 ? 128 : 64;
+  }
+  auto tiles = [&](int tm, int tn) {
+    return (int64_t)((a.M + tm - 1) / tm) * ((a.N + tn - 1) / tn);
+  };
   if (a.toff) {
     if (a.tile_m != 64) return -1;
     bm = 64;
+  } else if (bn == 128 && tiles(128, 128) >= 512) {
+    bm = 128;
   } else {
-    const int64_t tiles128 = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
-    bm = (bn == 128 && tiles128 >= 512) ? 128 : 64;
+    bm = 64;
+    if (!a.qkv_h && bn == 128 && tiles(64, 128) < 512) bn = 64;
   }
   const int mt = (a.M + bm - 1) / bm + (a.toff ? a.G : 0);
   dim3 grid(mt, (a.N + bn - 1) / bn);

@@ -28,6 +28,18 @@ struct GemmArgs {
   int64_t ldr = 0;
   void* C2 = nullptr;                // optional bf16 (f32 in f32 mode) copy, row stride ldc2
   int64_t ldc2 = 0;
+  // QKV epilogue (bf16, head dim 64, BN = 128): columns are six blocks of qkv_h =
+  // [SA q | SA k | SA v | DA q | DA k | DA v].  SA q/k are rotated by sequence position
+  // (pos_fixed >= 0 ? pos_fixed : out_row % seq) when sa_rope, DA q/k by depth
+  // (pairs < 16 at depth_l, the rest at depth_L-1-depth_l), before the bf16 rounding.
+  // vt (optional): SA v also written transposed, [out_row / seq][head][64][seq].
+  int qkv_h = 0;
+  int seq = 1;
+  int pos_fixed = -1;
+  int sa_rope = 0;
+  int depth_l = 0, depth_L = 1;
+  const float *cos_s = nullptr, *sin_s = nullptr, *cos_d = nullptr, *sin_d = nullptr;
+  void* vt = nullptr;
 };
 
 // out_f32: C is float32 (else storage dtype).  Returns -1 on an unsupported shape.
@@ -37,18 +49,26 @@ int launch_gemm(const GemmArgs& a, int dtype, int out_f32, hipStream_t st);
 void launch_rope_tables(int D, int npos, double base, float* c, float* s, hipStream_t st);
 
 // Depth attention (row strides in elements for q/k/v/out; cache contiguous [rows,L,H,d]).
+// rope: rotate q and k_new by depth here (else they arrive rotated and rounded).
 int launch_depth_attn(int dtype, int64_t rows, int H, int d, int l, int L, const void* q,
                       int64_t ldq, const void* kn, int64_t ldk, const void* vn, int64_t ldv,
                       void* kc, void* vc, void* out, int64_t ldo, const float* cosd,
-                      const float* sind, float scale, hipStream_t st);
+                      const float* sind, float scale, int rope, hipStream_t st);
 
-// Sequence attention.  Workspace bytes needed for (B, q_len, H, d, pos0).
-size_t seq_attn_ws(int dtype, int B, int q_len, int H, int d, int64_t pos0);
+// In-place RoPE of a [rows, 6h] QKV buffer (SA q/k by sequence position, DA q/k by depth).
+int launch_qkv_rope(int dtype, int64_t rows, int H, int d, int seq, int pos_fixed,
+                    int sa_rope, int l, int L, void* qkv, const float* cs, const float* sn,
+                    const float* cd, const float* sd, hipStream_t st);
+
+// Sequence attention.  rope: rotate q/k here by sequence position (else they arrive
+// rotated, or no RoPE is wanted).  vt: v transposed [B][H][64][q_len] when available
+// (prefill, bf16, d = 64); with rope == 0 and vt given the flash kernel needs no ws.
+size_t seq_attn_ws(int dtype, int B, int q_len, int H, int d, int64_t pos0, int prepared);
 int launch_seq_attn(int dtype, int B, int q_len, int H, int d, int64_t pos0, const void* q,
                     int64_t ldq, const void* kn, int64_t ldk, const void* vn, int64_t ldv,
-                    void* kc, void* vc, int64_t cap, void* out, int64_t ldo,
-                    const float* cos_s, const float* sin_s, float scale, int sa_rope,
-                    void* ws, size_t ws_bytes, hipStream_t st);
+                    const void* vt, void* kc, void* vc, int64_t cap, void* out, int64_t ldo,
+                    const float* cos_s, const float* sin_s, float scale, int rope, void* ws,
+                    size_t ws_bytes, hipStream_t st);
 
 // Router scores z [T, E] f32 = rho * RoPE_depth(x W_r^T) . keys.  bf16: u computed inside
 // (u ignored; needs r % 32 == 0, E % 16 == 0); f32: reads u = x W_r^T [T, r].

@@ -318,27 +318,38 @@ def layer_step(cfg, W, x, l, da_k, da_v, sa_k=None, sa_v=None, force_idx=None,
             pidx = np.asarray(force_pidx).reshape(T, 1)
             pgate = sigmoid(np.take_along_axis(pz, pidx, axis=-1))
         pidx, pgate = pidx[:, 0], pgate[:, 0]
-    qkv = st(_project(cfg, W, xhb, "qkv", pidx, pgate, st))
+    qkv = _project(cfg, W, xhb, "qkv", pidx, pgate, st)
     q_sa, k_sa, v_sa, q_da, k_da, v_da = [qkv[:, j * h:(j + 1) * h].reshape(T, H, d)
                                           for j in range(6)]
+    # R21: q and k are rotated from the projection itself and stored once, rotated; v is
+    # stored as projected.  SA rotates by sequence position, DA by depth (R4, R5).
+    pos = np.full(T, float(cfg.sa_pos)) if cfg.decode else (np.arange(T) % s).astype(float)
+    if cfg.sa_rope:
+        q_sa = rope(q_sa, pos[:, None, None], base)
+        k_sa = rope(k_sa, pos[:, None, None], base)
+    q_sa, k_sa, v_sa = st(q_sa), st(k_sa), st(v_sa)
+    q_da = st(depth_rope(q_da, l, L, base))
+    k_da = st(depth_rope(k_da, l, L, base))
+    v_da = st(v_da)
     # SA at depth l only ([PN] equation: SA(x_l)).
     if cfg.decode:
         P = cfg.sa_pos
         a_sa, k_rot, v_app = seq_attn(q_sa.reshape(b, 1, H, d), k_sa.reshape(b, 1, H, d),
                                       v_sa.reshape(b, 1, H, d), P, sa_k[l], sa_v[l],
-                                      cfg.sa_rope, base, bf16)
+                                      False, base, bf16)
         sa_k[l][:, P] = k_rot[:, 0]
         sa_v[l][:, P] = v_app[:, 0]
     else:
         a_sa, k_rot, v_app = seq_attn(q_sa.reshape(b, s, H, d), k_sa.reshape(b, s, H, d),
-                                      v_sa.reshape(b, s, H, d), 0, None, None, cfg.sa_rope,
+                                      v_sa.reshape(b, s, H, d), 0, None, None, False,
                                       base, bf16)
         if sa_k is not None:
             sa_k[l][:, :s] = k_rot
             sa_v[l][:, :s] = v_app
     a_sa = a_sa.reshape(T, h)
     if cfg.use_da:
-        a_da = depth_attn(q_da, k_da, v_da, da_k, da_v, l, L, base, bf16).reshape(T, h)
+        a_da = depth_attn(q_da, k_da, v_da, da_k, da_v, l, L, base, bf16,
+                          use_rope=False).reshape(T, h)
     else:
         a_da = np.zeros((T, h))
     att = np.concatenate([a_sa, a_da], axis=1)
