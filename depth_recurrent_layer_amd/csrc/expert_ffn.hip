@@ -37,7 +37,7 @@ struct FfnShape {
   static constexpr int LPW = NI / 4;                       // per wave per stage
   static constexpr int LDH = F + 8;
   static constexpr int HS_BYTES = 64 * LDH * 2;
-  static constexpr int NS0 = (76 * 1024 - HS_BYTES) / STAGE;
+  static constexpr int NS0 = (78 * 1024 - HS_BYTES) / STAGE;
   static constexpr int NS = NS0 > 8 ? 8 : NS0;             // ring depth (2 blocks / CU)
   static constexpr int OUT_COLS = 256;                     // GEMM2 chunk
   static_assert(NI % 4 == 0, "stage must split evenly over 4 waves");
