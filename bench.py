@@ -22,7 +22,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3       # fp32 vector
 METRIC = "token-depth-steps/sec, Dreamer layer fwd; % of HBM BW / MFMA peak"
-CLASSES = ["gemm", "seq_attn", "depth_attn", "route", "permute", "expert_ffn", "combine"]
+CLASSES = ["qkv_proj", "out_proj", "seq_attn", "depth_attn", "route", "permute", "expert_ffn",
+           "combine"]
 
 
 def parse():
@@ -33,7 +34,39 @@ def parse():
     p.add_argument("--workload", default="small")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--kernel-class", default=None, help="time this class live (default: dominant)")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB MiB (read + write), for scaling "
+                        "the FETCH_SIZE / WRITE_SIZE counters")
     return p.parse_args()
+
+
+def calibrate_copy(mib):
+    """A plain elementwise copy of known size: mib MiB read, mib MiB written per launch."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n * 4}), flush=True)
+
+
+def stored_traffic(kclass, workload):
+    """HBM bytes per launch of one kernel class, from the committed counter summary, or None
+    when the summary is missing or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kclass}_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    try:
+        blob = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    except (IndexError, ValueError):
+        return None
+    from depth_recurrent_layer_amd.profiling import source_digest
+    if blob.get("source_sha256") != source_digest():
+        return None
+    return blob["bytes_per_launch"]
 
 
 def algorithmic_work(cfg, counts_per_depth):
@@ -43,8 +76,8 @@ def algorithmic_work(cfg, counts_per_depth):
     T, h, L, k, f, r, E = cfg.T, cfg.h, cfg.L, cfg.k, cfg.f, cfg.r, cfg.E
     nq = 6 if cfg.use_da else 3
     w = {}
-    w["gemm"] = dict(bound="mfma", flops=L * (2 * T * h * nq * h + 2 * T * (nq // 3) * h * h
-                                                + 2 * T * h * r), launches=3 * L)
+    w["qkv_proj"] = dict(bound="mfma", flops=L * 2 * T * h * nq * h, launches=L)
+    w["out_proj"] = dict(bound="mfma", flops=L * 2 * T * (nq // 3) * h * h, launches=L)
     w["seq_attn"] = dict(bound="mfma", flops=L * 4 * cfg.b * h * (cfg.s * (cfg.s + 1) // 2),
                          launches=L)
     da_bytes = sum(T * h * es * (6 + 2 * l) for l in range(L))
@@ -54,7 +87,7 @@ def algorithmic_work(cfg, counts_per_depth):
     w["expert_ffn"] = dict(bound="hbm", bytes=touched * nw * h * f * es + L * 2 * T * k * h * es,
                            flops=L * 2 * T * k * nw * h * f, launches=L)
     w["combine"] = dict(bound="hbm", bytes=L * T * h * (k * es + 4 + es), launches=L + 1)
-    w["route"] = dict(bound="alu", flops=L * 2 * T * r * E, launches=L)
+    w["route"] = dict(bound="alu", flops=L * 2 * T * (h * r + r * E), launches=L)
     w["permute"] = dict(bound="hbm", bytes=L * T * k * 12, launches=L)
     return w
 
@@ -105,6 +138,9 @@ def main():
     cfg = CONFIGS[args.workload]
     dev = "cuda"
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     W = make_weights(cfg, device=dev)
     G = {k: v.contiguous() for k, v in W.items()}
     if cfg.proj_experts:
@@ -156,6 +192,7 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     value = cfg.T * cfg.L * args.steps / elapsed
     roof = roofline_entry(work[dom], dom_ms / max(n_launch, 1))
+    roof["traffic"] = stored_traffic(dom, cfg.name)
     roof["kernel"] = dom
     roof["launches_timed"] = n_launch
     roof["avg_launch_us"] = round(dom_ms / max(n_launch, 1) * 1e3, 2)

@@ -92,7 +92,7 @@ int dreamer_version(void) { return 100; }
 
 int dreamer_timing_enable(int kclass, int max_launches) {
   dreamer_timing_disable();
-  if (kclass < DREAMER_KC_GEMM || kclass > DREAMER_KC_COMBINE || max_launches <= 0)
+  if (kclass < DREAMER_KC_GEMM || kclass > DREAMER_KC_OUT_PROJ || max_launches <= 0)
     return fail(DREAMER_E_INVAL, "timing_enable: bad class or count");
   g_tm.ev0.resize(max_launches);
   g_tm.ev1.resize(max_launches);
@@ -684,9 +684,9 @@ int dreamer_layer_forward(const dreamer_layer_cfg* cfg, const dreamer_layer_weig
       go.G = c.proj_experts;
       go.tile_m = 64;
     }
-    TB(DREAMER_KC_GEMM);
+    TB(DREAMER_KC_OUT_PROJ);
     rc = launch_gemm(go, dt, 1, st);
-    TE(DREAMER_KC_GEMM);
+    TE(DREAMER_KC_OUT_PROJ);
     if (rc) return fail(DREAMER_E_UNSUPPORTED, "layer: output projection shape");
     // ---- EA on y, residual, next step's RMSNorm
     const bool last = l == L - 1;

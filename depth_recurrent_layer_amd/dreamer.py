@@ -25,8 +25,8 @@ F32, BF16 = 0, 1
 FFN_GELU, FFN_SWIGLU, FFN_LINEAR = 0, 1, 2
 FFN_KINDS = {"gelu": FFN_GELU, "swiglu": FFN_SWIGLU, "linear": FFN_LINEAR}
 MIX_PARTIAL = 0
-KC = {"gemm": 1, "seq_attn": 2, "depth_attn": 3, "route": 4, "permute": 5,
-      "expert_ffn": 6, "combine": 7}
+KC = {"qkv_proj": 1, "seq_attn": 2, "depth_attn": 3, "route": 4, "permute": 5,
+      "expert_ffn": 6, "combine": 7, "out_proj": 8}
 
 _vp, _i64, _i32, _f32, _f64, _sz = C.c_void_p, C.c_int64, C.c_int, C.c_float, C.c_double, C.c_size_t
 

@@ -242,13 +242,14 @@ int dreamer_layer_forward(const dreamer_layer_cfg* cfg, const dreamer_layer_weig
  * launches and their summed duration in milliseconds (it synchronises on the events).
  * Disabled by default; not reentrant (one harness at a time).
  */
-#define DREAMER_KC_GEMM 1
+#define DREAMER_KC_GEMM 1       /* Q/K/V projection (and the float32 router projection) */
 #define DREAMER_KC_SEQ_ATTN 2
 #define DREAMER_KC_DEPTH_ATTN 3
-#define DREAMER_KC_ROUTE 4
+#define DREAMER_KC_ROUTE 4      /* router scores + top-k                               */
 #define DREAMER_KC_PERMUTE 5
 #define DREAMER_KC_EXPERT_FFN 6
-#define DREAMER_KC_COMBINE 7
+#define DREAMER_KC_COMBINE 7    /* combine + RMSNorm (and the first RMSNorm)           */
+#define DREAMER_KC_OUT_PROJ 8   /* output projection + residual                        */
 int dreamer_timing_enable(int kclass, int max_launches);
 int dreamer_timing_read(int* n_launches, double* total_ms);
 int dreamer_timing_disable(void);
