@@ -231,17 +231,25 @@ size_t dreamer_expert_route_ws_bytes(int64_t T, int r, int E) {
   Bump b(nullptr);
   b.take_n<float>((size_t)T * r);
   b.take_n<float>((size_t)T * E);
+  b.take_n<int32_t>((size_t)perm_blocks(T * 32) * E);  // count chunks for any k <= 32
   return b.off + 256;
 }
 
-// u = x W_r^T (f32), then the routing kernel.  counts must be zeroed by the caller of
-// this helper when accumulation from zero is wanted.
+// u = x W_r^T (f32), then the routing kernels (fused scores + selection when it applies).
 static int route_impl(int dtype, int64_t T, int h, int r, int E, int k, int l, int L,
                       const void* x, int64_t ldx, const void* w_r, const void* keys,
                       const float* bias, float rho, int normalize, const float* cos_r,
                       const float* sin_r, int32_t* idx, float* gate, float* u, float* z,
                       hipStream_t st, const int32_t* idx_in = nullptr) {
   int rc;
+  if (router_fused_ok(dtype, T, r, E, k)) {
+    TB(DREAMER_KC_ROUTE);
+    rc = router_route_fused(T, h, r, E, k, l, L, x, ldx, w_r, keys, bias, rho, normalize,
+                            cos_r, sin_r, idx_in, idx, gate, st);
+    TE(DREAMER_KC_ROUTE);
+    if (rc) return fail(DREAMER_E_UNSUPPORTED, "expert_route: unsupported shape");
+    return ok();
+  }
   if (dtype == DREAMER_F32) {  // bf16 computes u inside the scores kernel
     GemmArgs ga;
     ga.M = (int)T;
@@ -282,10 +290,12 @@ int dreamer_expert_route(int dtype, int64_t T, int h, int r, int E, int k, int l
   Bump b(ws);
   float* u = b.take_n<float>((size_t)T * r);
   float* z = b.take_n<float>((size_t)T * E);
+  int32_t* hist = b.take_n<int32_t>((size_t)perm_blocks(T * 32) * E);
   rc = route_impl(dtype, T, h, r, E, k, l, L, x, h, w_r, keys, bias, rho, normalize, cos_r,
                   sin_r, idx, gate, u, z, st);
   if (rc) return rc;
-  if (counts) launch_histogram(idx, T * k, counts, E, st);
+  if (counts && launch_counts(idx, T * k, E, hist, counts, st))
+    return fail(DREAMER_E_UNSUPPORTED, "expert_route: E too large for counts");
   return check_launch("expert_route");
 }
 
@@ -319,8 +329,7 @@ size_t dreamer_expert_ffn_ws_bytes(int dtype, int kind, int64_t T, int h_in, int
 // slots by expert first (histogram unless the counts are already there, scan, scatter).
 static int ffn_slots(int dtype, int kind, int64_t T, int h_in, int f, int h_out, int E, int k,
                      const void* x, const int32_t* idx, const float* gate, const void* w1,
-                     const void* w3, const void* w2, const FfnWs& w,
-                     hipStream_t st) {
+                     const void* w3, const void* w2, const FfnWs& w, hipStream_t st) {
   const int64_t ns = T * k;
   if (dtype == DREAMER_F32) {
     TB(DREAMER_KC_EXPERT_FFN);
@@ -376,6 +385,7 @@ static int validate_ffn(int dtype, int kind, int64_t T, int h_in, int f, int h_o
   if (T < 0 || h_in <= 0 || h_out <= 0 || E <= 0 || k <= 0 || (kind != DREAMER_FFN_LINEAR && f <= 0))
     return fail(DREAMER_E_INVAL, "expert_ffn: bad sizes");
   if (h_out > 4096) return fail(DREAMER_E_UNSUPPORTED, "expert_ffn: h_out > 4096");
+  if (E > PERM_MAX_E) return fail(DREAMER_E_UNSUPPORTED, "expert_ffn: E > %d", PERM_MAX_E);
   if (T * k > INT32_MAX / 2) return fail(DREAMER_E_UNSUPPORTED, "expert_ffn: too many slots");
   if (dtype == DREAMER_BF16) {
     if (h_in % 64 || h_out % 64) return fail(DREAMER_E_UNSUPPORTED, "expert_ffn: bf16 needs h %% 64 == 0");
@@ -472,7 +482,7 @@ static LayerWs plan_layer(Bump& b, const dreamer_layer_cfg* c, bool need_yb, boo
     w.pcounts = b.take_n<int32_t>(Ep);
     w.pgoff = b.take_n<int32_t>(Ep + 1);
     w.ptoff = b.take_n<int32_t>(Ep + 1);
-    w.phist = b.take_n<int32_t>((size_t)std::max(1, perm_blocks(T)) * Ep);
+    w.phist = b.take_n<int32_t>((size_t)perm_blocks(T) * Ep);
     w.pperm = b.take_n<int32_t>(T);
   }
   w.z = b.take_n<float>((size_t)T * std::max(c->use_ea ? c->E : 1, c->proj_experts));
@@ -508,6 +518,7 @@ static int validate_layer(const dreamer_layer_cfg* c, const dreamer_layer_weight
   if (c->use_ea) {
     rc = validate_route(c->dtype, (int64_t)c->b * c->s, c->h, c->r, c->E, c->k, 0, c->L);
     if (rc) return rc;
+
     if (c->ffn_kind != DREAMER_FFN_GELU && c->ffn_kind != DREAMER_FFN_SWIGLU)
       return fail(DREAMER_E_INVAL, "layer: ffn_kind must be GELU or SWIGLU");
     rc = validate_ffn(c->dtype, c->ffn_kind, (int64_t)c->b * c->s, c->h, c->f, c->h, c->E, c->k);

@@ -8,14 +8,6 @@
 
 namespace dreamer {
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-template <int N>
-DEV void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 // ------------------------------------------------------------------------- RoPE tables
 __global__ void rope_table_kernel(int D, int npos, double base, float* c, float* s) {
   const int half = D / 2;
@@ -351,14 +343,22 @@ __global__ void sa_combine_kernel(int64_t nrows, int H, int d, int nsplit,
 // softmax statistics stay in the lane (plus the 4 lane groups, joined by two shuffles),
 // and P feeds O^T = V^T P^T straight from registers.  K and V^T tiles of 64 keys stream
 // through a 3-stage LDS ring filled by direct global->LDS loads (128-byte rows, 16-byte
-// chunks XOR-swizzled by row).  Requires S % 8 == 0.
+// chunks XOR-swizzled by row).  The K tile's rows hold the keys in the order key_of_row,
+// which makes the 8 P values a lane feeds to one MFMA 8 consecutive keys, so each V^T
+// fragment is one 16-byte read.  Requires S % 8 == 0.
 namespace fa {
 constexpr int BQ = 64, BKEY = 64, NSTG = 3, TILE = 8192;  // bytes per K or V^T tile
 }
 
 DEV int swz128(int row, int c) { return row * 64 + ((c ^ (row & 7)) << 3); }  // elements
 
-__global__ __launch_bounds__(256, 2) void sa_flash_kernel(
+// Key (within a 64-key tile) held by K-tile row r = 32 cc + 16 h + 4 g + i: the S^T tile
+// t = 2 cc + h gives lane group g the keys 32 cc + 8 g + 4 h + i.
+DEV int key_of_row(int r) {
+  return (r & 32) + ((r >> 2) & 3) * 8 + ((r >> 4) & 1) * 4 + (r & 3);
+}
+
+__global__ __launch_bounds__(256, 3) void sa_flash_kernel(
     int B, int S, int H, const bf16* __restrict__ q, int64_t ldq, const bf16* __restrict__ kk,
     int64_t ldk, const bf16* __restrict__ vt, bf16* __restrict__ out, int64_t ldo,
     float scale) {
@@ -391,10 +391,10 @@ __global__ __launch_bounds__(256, 2) void sa_flash_kernel(
     for (int i = 0; i < 4; ++i) {
       const int j = w + 4 * i;
       const bf16* src;
-      if (j < 8) {  // K rows (keys)
-        const int key = j * 8 + lrow;
-        const int c = slot ^ (key & 7);
-        const int kp = min(kbase + key, S - 1);
+      if (j < 8) {  // K rows (keys in key_of_row order)
+        const int row = j * 8 + lrow;
+        const int c = slot ^ (row & 7);
+        const int kp = min(kbase + key_of_row(row), S - 1);
         src = kk + (tok0 + kp) * ldk + hoff + c * 8;
       } else {      // V^T rows (dims)
         const int dim = (j - 8) * 8 + lrow;
@@ -415,78 +415,84 @@ __global__ __launch_bounds__(256, 2) void sa_flash_kernel(
   const int qlast = min(qb * BQ + BQ, S) - 1;
   const int qlim = min(qpos, S - 1);
   const int nkt = qlast / BKEY + 1;
+  const uint32_t stg0 = lds_off(stg);
+  // per-lane fragment offsets within a tile (row lr; tile rows 16t + lr follow at 2048 t)
+  const uint32_t kofs0 = 2 * swz128(lr, lg), kofs1 = 2 * swz128(lr, 4 + lg);
+  const uint32_t vofs0 = kofs0, vofs1 = kofs1;
   issue(0);
   if (nkt > 1) issue(1);
+  // The Q fragments, loaded before the ring, are taken through an empty asm statement:
+  // the compiler waits for their loads there (only the ring loads issued later stay
+  // outstanding) and then sees them as plain register values, so their first use inside
+  // the loop does not drain the ring.
+  asm volatile("" : "+v"(qf[0]), "+v"(qf[1]));
   for (int kt = 0; kt < nkt; ++kt) {
-    if (kt + 1 < nkt) wait_vm<4>();
-    else wait_vm<0>();
-    __syncthreads();
+    if (kt + 1 < nkt) wait_vmcnt<4>();
+    else wait_vmcnt<0>();
+    ring_barrier();  // tile kt visible to all waves; tile kt-1 consumed by all
     if (kt + 2 < nkt) issue(kt + 2);
-    const bf16* Ks = reinterpret_cast<const bf16*>(stg[kt % NSTG]);
-    const bf16* Vs = Ks + TILE / 2;
+    const uint32_t ks0 = stg0 + (kt % NSTG) * 2 * TILE, vs0 = ks0 + TILE;
     const int kbase = kt * BKEY;
 
-    // S^T tiles: 4 key tiles of 16, K = 64 dims in two steps.
+    // S^T tiles: 4 key tiles of 16, K = 64 dims in two steps.  Row 16t + lr of a tile
+    // sits 2048 t bytes after row lr (kf[t]: dims 0..31, kf[4 + t]: dims 32..63).
+    bf16x8 kf[8];
+    lds_read_b128_2x4<2048>(kf, ks0 + kofs0, ks0 + kofs1);
     floatx4 sacc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      sacc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(&Ks[swz128(t * 16 + lr, ks * 4 + lg)]);
-        sacc[t] = mfma16(kf, qf[ks], sacc[t]);
-      }
+      sacc[t] = mfma16(kf[t], qf[0], floatx4{0.f, 0.f, 0.f, 0.f});
+      sacc[t] = mfma16(kf[4 + t], qf[1], sacc[t]);
     }
-    // mask + tile max (lane holds keys kbase + 16t + 4lg + i for query qpos)
+    // causal mask on the diagonal tile (lane holds keys kbase + 32(t/2) + 8lg + 4(t%2) + i
+    // for query qpos), then the tile max
+    if (kbase + BKEY - 1 > qb * BQ) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (kbase + (t >> 1) * 32 + lg * 8 + (t & 1) * 4 + i > qlim) sacc[t][i] = -INFINITY;
+    }
     float tmax = -INFINITY;
-    const bool diag = kbase + BKEY - 1 > qb * BQ;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (diag && kbase + t * 16 + lg * 4 + i > qlim) sacc[t][i] = -INFINITY;
-        tmax = fmaxf(tmax, sacc[t][i]);
-      }
+      for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sacc[t][i]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     const float mn = fmaxf(m, tmax);
-    const float corr = exp2f((m - mn) * sl2);
+    const float corr = __builtin_amdgcn_exp2f((m - mn) * sl2);
     m = mn;
     lsum *= corr;
 #pragma unroll
     for (int t = 0; t < 4; ++t) o[t] *= corr;
-    // P^T fragments for the two 32-key chunks (slot j < 4: tile 2c, j >= 4: tile 2c+1).
-    // P = hi + lo, both bf16, so P V keeps ~16 mantissa bits of P (a single bf16 P
-    // would perturb every output by up to 2^-9 max|v|).
+    // P^T fragments for the two 32-key chunks: element j of lane group lg is key
+    // 32cc + 8lg + j (tile 2cc for j < 4, tile 2cc+1 for j >= 4).  P = hi + lo, both bf16,
+    // so P V keeps ~16 mantissa bits of P (a single bf16 P would perturb every output by
+    // up to 2^-9 max|v|).
     bf16x8 ph[2], pl[2];
+    const float msl = mn * sl2;
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float sv = sacc[2 * cc + (j >> 2)][j & 3];
-        const float p = exp2f((sv - mn) * sl2);
+        const float p = __builtin_amdgcn_exp2f(fmaf(sv, sl2, -msl));
         lsum += p;
         const bf16 hi = (bf16)p;
         ph[cc][j] = hi;
         pl[cc][j] = (bf16)(p - (float)hi);
       }
     // O^T += V^T P^T : 4 dim tiles x 2 key chunks.  Lane (dim 16t + lr, group lg) takes
-    // keys 32cc + 4lg + 0..3 and 32cc + 16 + 4lg + 0..3 of its V^T row.
+    // keys 32cc + 8lg + 0..7 of its V^T row: chunk 4cc + lg.
+    bf16x8 vf[8];  // vf[t]: keys 0..31 of dim row 16t + lr, vf[4 + t]: keys 32..63
+    lds_read_b128_2x4<2048>(vf, vs0 + vofs0, vs0 + vofs1);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
-        const int dim = t * 16 + lr;
-        const bf16x4 lo4 = *reinterpret_cast<const bf16x4*>(
-            &Vs[swz128(dim, 4 * cc + (lg >> 1)) + (lg & 1) * 4]);
-        const bf16x4 hi4 = *reinterpret_cast<const bf16x4*>(
-            &Vs[swz128(dim, 4 * cc + 2 + (lg >> 1)) + (lg & 1) * 4]);
-        bf16x8 vf;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) { vf[j] = lo4[j]; vf[4 + j] = hi4[j]; }
-        o[t] = mfma16(vf, ph[cc], o[t]);
-        o[t] = mfma16(vf, pl[cc], o[t]);
+        o[t] = mfma16(vf[cc * 4 + t], ph[cc], o[t]);
+        o[t] = mfma16(vf[cc * 4 + t], pl[cc], o[t]);
       }
   }
   lsum += __shfl_xor(lsum, 16, 64);

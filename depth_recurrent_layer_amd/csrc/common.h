@@ -107,6 +107,125 @@ DEV float silu_(float x) { return x / (1.0f + expf(-x)); }
 
 DEV float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
 
+// LDS pointer type of the direct global->LDS loads (global_load_lds_dwordx4: lane L of
+// one instruction lands 16 bytes at LDS base + 16 L).
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Wait until at most N vector-memory operations of this wave are outstanding (gfx9
+// s_waitcnt encoding: vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt left at max).
+template <int N>
+DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Runtime count: waits until at most n (clamped to [0, 24]) are outstanding.
+DEV void wait_vmcnt_upto(int n) {
+  switch (n < 0 ? 0 : n > 24 ? 24 : n) {
+#define DREAMER_VM_CASE(N) \
+  case N: wait_vmcnt<N>(); break;
+    DREAMER_VM_CASE(0) DREAMER_VM_CASE(1) DREAMER_VM_CASE(2) DREAMER_VM_CASE(3)
+    DREAMER_VM_CASE(4) DREAMER_VM_CASE(5) DREAMER_VM_CASE(6) DREAMER_VM_CASE(7)
+    DREAMER_VM_CASE(8) DREAMER_VM_CASE(9) DREAMER_VM_CASE(10) DREAMER_VM_CASE(11)
+    DREAMER_VM_CASE(12) DREAMER_VM_CASE(13) DREAMER_VM_CASE(14) DREAMER_VM_CASE(15)
+    DREAMER_VM_CASE(16) DREAMER_VM_CASE(17) DREAMER_VM_CASE(18) DREAMER_VM_CASE(19)
+    DREAMER_VM_CASE(20) DREAMER_VM_CASE(21) DREAMER_VM_CASE(22) DREAMER_VM_CASE(23)
+    DREAMER_VM_CASE(24)
+#undef DREAMER_VM_CASE
+  }
+}
+
+// Workgroup barrier for LDS rings filled by direct global->LDS loads.  __syncthreads()
+// would first wait for every outstanding vector-memory load of the wave (its fence
+// covers global memory), draining the loads of later ring stages; here only this wave's
+// LDS operations are waited for (lgkmcnt(0)), so the caller's own vmcnt wait decides
+// which stages must have landed.  The empty asm statements keep the compiler from
+// moving memory accesses across the barrier.
+DEV void ring_barrier() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// LDS tiles of 64-byte rows (32 bf16 of K): chunk c (16 bytes) of row r is stored at slot
+// c ^ ((r >> 1) & 3), so the 8 rows read by 8 consecutive lanes of an MFMA fragment load
+// cover all 32 banks.
+DEV int swz64_slot(int row, int c) { return c ^ ((row >> 1) & 3); }
+DEV int swz64(int row, int c) { return row * 64 + (swz64_slot(row, c) << 4); }
+
+// 32-bit LDS offset of a pointer into a __shared__ array.
+DEV uint32_t lds_off(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// N 16-byte LDS reads (N = 2, 4, 6 or 8) completed within one statement.  Ring stages
+// filled by direct global->LDS loads are read this way: for a plain LDS read the
+// compiler cannot tell that it misses the stages still in flight and would wait for
+// every outstanding load first.  The reads are complete when the statement ends, so no
+// register of it is written later (the caller's vmcnt wait and barrier made the stage
+// visible before).
+template <int N>
+DEV void lds_read_b128(bf16x8 (&x)[N], const uint32_t (&a)[N]) {
+  static_assert(N == 2 || N == 4 || N == 6 || N == 8, "2, 4, 6 or 8 reads");
+  if constexpr (N == 2) {
+    asm volatile(
+        "ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1])
+        : "v"(a[0]), "v"(a[1])
+        : "memory");
+  } else if constexpr (N == 4) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+        : "memory");
+  } else if constexpr (N == 6) {
+    asm volatile(
+        "ds_read_b128 %0, %6\n\tds_read_b128 %1, %7\n\tds_read_b128 %2, %8\n\t"
+        "ds_read_b128 %3, %9\n\tds_read_b128 %4, %10\n\tds_read_b128 %5, %11\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5])
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\tds_read_b128 %2, %10\n\t"
+        "ds_read_b128 %3, %11\n\tds_read_b128 %4, %12\n\tds_read_b128 %5, %13\n\t"
+        "ds_read_b128 %6, %14\n\tds_read_b128 %7, %15\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+          "=&v"(x[6]), "=&v"(x[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+          "v"(a[7])
+        : "memory");
+  }
+}
+
+// Eight 16-byte LDS reads from two base offsets, four each at steps of STRIDE bytes
+// (immediate offsets), completed within the statement like lds_read_b128.
+template <int STRIDE>
+DEV void lds_read_b128_2x4(bf16x8 (&x)[8], uint32_t b0, uint32_t b1) {
+  static_assert(3 * STRIDE < 65536, "ds offset range");
+  asm volatile(
+      "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:%10\n\t"
+      "ds_read_b128 %2, %8 offset:%11\n\tds_read_b128 %3, %8 offset:%12\n\t"
+      "ds_read_b128 %4, %9\n\tds_read_b128 %5, %9 offset:%10\n\t"
+      "ds_read_b128 %6, %9 offset:%11\n\tds_read_b128 %7, %9 offset:%12\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+        "=&v"(x[6]), "=&v"(x[7])
+      : "v"(b0), "v"(b1), "n"(STRIDE), "n"(2 * STRIDE), "n"(3 * STRIDE)
+      : "memory");
+}
+
+// LDS writes of this wave complete and ordered before its following LDS reads (for
+// exchanges between the lanes of one wave; lgkmcnt(0), then a scheduling barrier).
+DEV void wave_lds_sync() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+  __builtin_amdgcn_wave_barrier();
+}
+
 // MFMA 16x16x32 bf16 -> f32 (gfx950).  Lane l holds A[row l%16][k 8(l/16)..+8],
 // B[k 8(l/16)..+8][col l%16]; D lane l holds rows 4(l/16)+i, col l%16, i = 0..3.
 DEV floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) {

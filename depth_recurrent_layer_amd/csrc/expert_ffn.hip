@@ -5,8 +5,8 @@
 // of the expert's weight rows through a multi-stage LDS ring filled by direct
 // global->LDS loads (global_load_lds_dwordx4: no staging registers, several slices in
 // flight per wave).  Slices are stored as 64-byte rows whose 16-byte chunks are
-// XOR-swizzled by row (chunk c of row r at slot c ^ ((r >> 2) & 3)), so the 16 rows
-// one MFMA fragment read touches fall into distinct banks.  Wave w owns hidden columns
+// XOR-swizzled by row (swz64), so the rows one MFMA fragment read touches fall into
+// distinct banks.  Wave w owns hidden columns
 // [w F/4, (w+1) F/4) of both projections, so the activation is lane-local.  The hidden
 // tile goes to LDS (bf16), GEMM2 (H W2^T) runs over 256-column chunks whose gate-scaled
 // bf16 results are staged in LDS and written per slot with 16-byte stores.
@@ -14,18 +14,6 @@
 #include "kernels.h"
 
 namespace dreamer {
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Wait until at most N vector-memory operations of this wave are outstanding (gfx9
-// s_waitcnt encoding: vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt left at max).
-template <int N>
-DEV void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-DEV int swz64(int row, int c) { return row * 64 + ((c ^ ((row >> 2) & 3)) << 4); }
 
 template <int F, int KIND>
 struct FfnShape {
@@ -86,14 +74,12 @@ __global__ __launch_bounds__(256, 2) void expert_ffn_kernel(
     if (q < 4) {  // gathered token rows
       const int row = q * 16 + (lane >> 2);
       const int s = s_slot[row] >= 0 ? s_slot[row] : s_slot[0];
-      const int c = slot ^ ((row >> 2) & 3);
-      src[j] = x + (int64_t)(s / k) * h_in + c * 8;
+      src[j] = x + (int64_t)(s / k) * h_in + swz64_slot(row, slot) * 8;
     } else {      // expert weight rows
       const int wq = q - 4, m = wq / (F / 16);
       const int mr = (wq % (F / 16)) * 16 + (lane >> 2);
-      const int c = slot ^ ((mr >> 2) & 3);
       const bf16* W = m == 0 ? w1 : w3;
-      src[j] = W + ((int64_t)e * F + mr) * h_in + c * 8;
+      src[j] = W + ((int64_t)e * F + mr) * h_in + swz64_slot(mr, slot) * 8;
     }
   }
   auto issue = [&](int s) {
@@ -113,28 +99,36 @@ __global__ __launch_bounds__(256, 2) void expert_ffn_kernel(
       au[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
   const int nst = h_in / 32;
+  const uint32_t stg0 = lds_off(stg);
+  // fragments read per stage: 4 of X, then NT1 of W1 (and NT1 of W3); a GELU tile of
+  // F = 64 reads its single weight fragment twice to make an even count
+  constexpr int NB = NT1 * S::NW1, NR = 4 + (NB == 1 ? 2 : NB);
   for (int s = 0; s < S::NS - 1 && s < nst; ++s) issue(s);
   for (int s = 0; s < nst; ++s) {
-    if (s + S::NS - 2 < nst) wait_vmcnt<S::LPW * (S::NS - 2)>();
-    else wait_vmcnt<0>();
-    __syncthreads();  // stage s visible to all waves; stage s-1 fully consumed
+    wait_vmcnt_upto(S::LPW * min(S::NS - 2, nst - 1 - s));
+    ring_barrier();  // stage s visible to all waves; stage s-1 fully consumed
     if (s + S::NS - 1 < nst) issue(s + S::NS - 1);
-    const char* sb = stg + (s % S::NS) * S::STAGE;
-    bf16x8 af[4];
+    const uint32_t sb = stg0 + (s % S::NS) * S::STAGE;
+    uint32_t ad[NR];
+    bf16x8 fr[NR];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-      af[mt] = *reinterpret_cast<const bf16x8*>(sb + swz64(mt * 16 + lr, lg));
+    for (int mt = 0; mt < 4; ++mt) ad[mt] = sb + swz64(mt * 16 + lr, lg);
 #pragma unroll
     for (int nt = 0; nt < NT1; ++nt) {
       const int col = w * (F / 4) + nt * 16 + lr;
-      const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(sb + S::XB + swz64(col, lg));
+      ad[4 + nt] = sb + S::XB + swz64(col, lg);
+      if constexpr (S::NW1 == 2) ad[4 + NT1 + nt] = sb + S::XB + S::WB + swz64(col, lg);
+    }
+    if constexpr (NB == 1) ad[5] = ad[4];
+    lds_read_b128<NR>(fr, ad);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) ag[mt][nt] = mfma16(af[mt], b1, ag[mt][nt]);
+    for (int nt = 0; nt < NT1; ++nt) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) ag[mt][nt] = mfma16(fr[mt], fr[4 + nt], ag[mt][nt]);
       if constexpr (KIND == FFN_SWIGLU) {
-        const bf16x8 b3 =
-            *reinterpret_cast<const bf16x8*>(sb + S::XB + S::WB + swz64(col, lg));
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) au[mt][nt] = mfma16(af[mt], b3, au[mt][nt]);
+        for (int mt = 0; mt < 4; ++mt)
+          au[mt][nt] = mfma16(fr[mt], fr[4 + NT1 + nt], au[mt][nt]);
       }
     }
   }

@@ -1,8 +1,8 @@
 // C = A . B^T with fused epilogues, for the dense projections (QKV, O, router rank-r
 // projection) and the grouped linear-MoE projections.
 //
-// bf16 path: LDS-tiled MFMA (v_mfma_f32_16x16x32_bf16), 256 threads = 2 x 2 waves,
-// register prefetch of the next K tile while the current one is multiplied.
+// bf16 path: MFMA (v_mfma_f32_16x16x32_bf16) over a multi-stage LDS ring, 256 threads =
+// 2 x 2 waves.
 // f32 path: one thread per output element (used only for small float32 layers).
 //
 // Row model: the kernel walks "positions" m.  Position m reads A row
@@ -15,23 +15,33 @@
 
 namespace dreamer {
 
-// LDS tile layout: rows of BK = 64 bf16 (128 B), 16-byte chunks XOR-swizzled by row
-// (chunk c of row r lives at slot c ^ (r & 7)), so the 16 rows read by one MFMA
-// fragment load hit distinct banks without padding.
-DEV int swz(int row, int kc) { return row * 64 + ((kc ^ (row & 7)) << 3); }
+// K streams through a ring of NS stages of 32-wide K slices filled by direct global->LDS
+// loads (global_load_lds_dwordx4), NS - 1 slices in flight per block.  A stage holds
+// the BM A rows then the BN B rows of one slice as 64-byte rows; the four 16-byte chunks
+// of row r are XOR-swizzled (chunk c at slot c ^ ((r >> 1) & 3)) so the 8 rows read by
+// 8 consecutive lanes of one MFMA fragment load cover all 32 banks.  2 x 2 waves, each
+// owning a WM x WN sub-tile (WM/16 x WN/16 MFMA tiles).  After the K loop every wave
+// stages its own sub-tile in LDS and writes whole rows with 16-byte stores.
+template <int WM, int WN>
+struct GemmShape {
+  static constexpr int BM = 2 * WM, BN = 2 * WN, TM = WM / 16, TN = WN / 16;
+  static constexpr int STAGE = (BM + BN) * 64;  // bytes per K slice
+  static constexpr int NI = (BM + BN) / 16;     // 1 KiB load instructions per stage
+  static constexpr int LPW = NI / 4;            // per wave
+  static constexpr int NS0 = 65536 / STAGE;
+  static constexpr int NS = NS0 > 8 ? 8 : NS0;  // ring depth (two blocks per CU)
+  // epilogue staging per wave: float32 rows of WN (+4), or bf16 rows of WN (+8)
+  static constexpr int LDF = WN + 4, LDB = WN + 8;
+  static constexpr int WAVE_STAGE = WM * LDF * 4;
+  static constexpr int SMEM = NS * STAGE > 4 * WAVE_STAGE ? NS * STAGE : 4 * WAVE_STAGE;
+  static_assert(NI % 4 == 0, "stage must split evenly over 4 waves");
+};
 
-template <typename OutT, typename ResT, int BM, int BN>
+template <typename OutT, int WM, int WN>
 __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs a) {
-  constexpr int BK = 64;
-  constexpr int TM = BM / 32, TN = BN / 32;              // 16x16 tiles per wave (2 x 2 waves)
-  constexpr int ACH = BM * 8 / 256, BCH = BN * 8 / 256;  // 16-B chunks per thread per tile
-  // A/B tiles during the K loop; the float32 C tile (rows padded by 4) in the epilogue
-  constexpr int LDC = BN + 4;
-  constexpr int AB_BYTES = 2 * (BM + BN) * BK * 2, C_BYTES = BM * LDC * 4;
-  __shared__ __attribute__((aligned(16))) char smem[AB_BYTES > C_BYTES ? AB_BYTES : C_BYTES];
-  bf16 (*As)[BM * BK] = reinterpret_cast<bf16 (*)[BM * BK]>(smem);
-  bf16 (*Bs)[BN * BK] = reinterpret_cast<bf16 (*)[BN * BK]>(smem + 2 * BM * BK * 2);
-  float* Cs = reinterpret_cast<float*>(smem);
+  using S = GemmShape<WM, WN>;
+  constexpr int BM = S::BM, BN = S::BN, TM = S::TM, TN = S::TN;
+  __shared__ __attribute__((aligned(1024))) char ring[S::SMEM];
   __shared__ int rows_s[BM];
 
   const int tid = threadIdx.x;
@@ -54,171 +64,168 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs a) {
   const int n0 = blockIdx.y * BN;
   const bf16* __restrict__ A = (const bf16*)a.A;
   const bf16* __restrict__ B = (const bf16*)a.B + (int64_t)g * a.b_gstride;
-
   for (int i = tid; i < BM; i += 256) {
-    int m = m_begin + i;
+    const int m = m_begin + i;
     rows_s[i] = (m < m_end) ? (a.rows ? a.rows[m] : m) : -1;
   }
   __syncthreads();
 
-  // Thread -> (row, chunk) of the tiles it stages; source rows as 32-bit indices.
-  const int kc = tid & 7, r0 = tid >> 3;  // rows r0 + 32 j
-  int arow[ACH], brow[BCH];
+  // load descriptors: wave w issues instructions q = w + 4 j of every stage; lane L of
+  // instruction q fills row 16 q' + L / 4, slot L % 4 of its section
+  const int lane = tid & 63, w = tid >> 6;
+  const bf16* src[S::LPW];
 #pragma unroll
-  for (int j = 0; j < ACH; ++j) {
-    const int src = rows_s[r0 + 32 * j];
-    arow[j] = src >= 0 ? src / a.row_div : -1;
+  for (int j = 0; j < S::LPW; ++j) {
+    const int q = w + 4 * j, slot = lane & 3;
+    if (q < BM / 16) {
+      const int row = q * 16 + (lane >> 2);
+      const int o = rows_s[row] >= 0 ? rows_s[row] : rows_s[0];  // pad rows repeat row 0
+      src[j] = A + (int64_t)(o / a.row_div) * a.lda + (swz64_slot(row, slot) << 3);
+    } else {
+      const int row = (q - BM / 16) * 16 + (lane >> 2);
+      const int n = min(n0 + row, a.N - 1);
+      src[j] = B + (int64_t)n * a.ldb + (swz64_slot(row, slot) << 3);
+    }
   }
+  auto issue = [&](int s) {
+    char* sb = ring + (s % S::NS) * S::STAGE;
 #pragma unroll
-  for (int j = 0; j < BCH; ++j) {
-    const int n = n0 + r0 + 32 * j;
-    brow[j] = n < a.N ? n : -1;
-  }
-  bf16x8 ra[ACH], rb[BCH];
-  const bf16x8 zero8 = {};
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int j = 0; j < ACH; ++j)
-      ra[j] = arow[j] >= 0
-                  ? *reinterpret_cast<const bf16x8*>(A + (int64_t)arow[j] * a.lda + k0 + kc * 8)
-                  : zero8;
-#pragma unroll
-    for (int j = 0; j < BCH; ++j)
-      rb[j] = brow[j] >= 0
-                  ? *reinterpret_cast<const bf16x8*>(B + (int64_t)brow[j] * a.ldb + k0 + kc * 8)
-                  : zero8;
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < ACH; ++j)
-      *reinterpret_cast<bf16x8*>(&As[buf][swz(r0 + 32 * j, kc)]) = ra[j];
-#pragma unroll
-    for (int j = 0; j < BCH; ++j)
-      *reinterpret_cast<bf16x8*>(&Bs[buf][swz(r0 + 32 * j, kc)]) = rb[j];
+    for (int j = 0; j < S::LPW; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(src[j] + s * 32),
+                                       (lds_void*)(sb + (w + 4 * j) * 1024), 16, 0, 0);
   };
 
-  const int lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
-  const int lr = lane & 15, lg = lane >> 4;
+  const int wm = w >> 1, wn = w & 1, lr = lane & 15, lg = lane >> 4;
   floatx4 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  int buf = 0;
-  for (int k0 = 0; k0 < a.K; k0 += BK) {
-    const bool more = k0 + BK < a.K;
-    if (more) gload(k0 + BK);
+  // Epilogue operands that do not depend on the product are fetched before the K loop so
+  // that their latency hides behind it: the rotary table entries of the QKV epilogue
+  // (per row for sequence positions, per pair for depth), or the float32 residual of the
+  // generic epilogue (the 8-column chunks this lane will write).
+  constexpr bool QKV = WN == 64 && sizeof(OutT) == 2;
+  constexpr int CPR = WN / 8, NIT = WM * CPR / 64;  // generic epilogue items per lane
+  const int rw0 = wm * WM, cw0 = n0 + wn * WN;      // this wave's first tile row, column
+  const int sect = a.qkv_h ? cw0 / a.qkv_h : -1;
+  const bool sa_qk = QKV && a.qkv_h && (sect == 0 || sect == 1) && a.sa_rope;
+  const bool da_qk = QKV && a.qkv_h && (sect == 3 || sect == 4);
+  float pc[QKV ? TM : 1][4][2], ps[QKV ? TM : 1][4][2];
+  float rres[QKV ? 1 : NIT][8];
+  if constexpr (QKV) {
+    if (sa_qk || da_qk) {
+      const float* ct = sa_qk ? a.cos_s : a.cos_d;
+      const float* st = sa_qk ? a.sin_s : a.sin_d;
 #pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      bf16x8 bfr[TN];
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(
-            &Bs[buf][swz(wn * (BN / 2) + j * 16 + lr, ks * 4 + lg)]);
+        for (int v = 0; v < 4; ++v) {
+          const int orow = rows_s[rw0 + i * 16 + lg * 4 + v];
+          const int spos = a.pos_fixed >= 0 ? a.pos_fixed : (orow >= 0 ? orow % a.seq : 0);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const bf16x8 af = *reinterpret_cast<const bf16x8*>(
-            &As[buf][swz(wm * (BM / 2) + i * 16 + lr, ks * 4 + lg)]);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(af, bfr[j], acc[i][j]);
-      }
+          for (int j = 0; j < 2; ++j) {  // depth: pairs < 16 at l, the others at L-1-l
+            const int pos = sa_qk ? spos : (j == 0 ? a.depth_l : a.depth_L - 1 - a.depth_l);
+            pc[i][v][j] = ct[pos * 32 + j * 16 + lr];
+            ps[i][v][j] = st[pos * 32 + j * 16 + lr];
+          }
+        }
     }
-    if (more) {
-      lstore(buf ^ 1);  // the other buffer was last read before the previous barrier
-      __syncthreads();
-      buf ^= 1;
+  } else {
+    if (a.resid) {
+#pragma unroll
+      for (int m = 0; m < NIT; ++m) {
+        const int it = lane + 64 * m, rt = it / CPR, n = cw0 + (it % CPR) * 8;
+        const int orow = rows_s[rw0 + rt];
+        if (orow >= 0 && n < a.N) {
+          load16(a.resid + (int64_t)orow * a.ldr + n, rres[m]);
+          load16(a.resid + (int64_t)orow * a.ldr + n + 4, rres[m] + 4);
+        }
+      }
     }
   }
 
-  // epilogue: accumulators -> LDS (float32), then every thread handles 8-column chunks of
-  // whole rows so the residual loads and the output stores are 16-byte and coalesced
-  __syncthreads();  // all waves are done reading the A/B tiles
+  const int nst = a.K / 32;
+  const uint32_t ring0 = lds_off(ring);
+  for (int s = 0; s < S::NS - 1 && s < nst; ++s) issue(s);
+  for (int s = 0; s < nst; ++s) {
+    // stage s has landed once only the later stages' loads are outstanding
+    wait_vmcnt_upto(S::LPW * min(S::NS - 2, nst - 1 - s));
+    ring_barrier();  // stage s visible to every wave; stage s - 1 consumed by every wave
+    if (s + S::NS - 1 < nst) issue(s + S::NS - 1);
+    const uint32_t sb = ring0 + (s % S::NS) * S::STAGE;
+    uint32_t ad[TM + TN];
+    bf16x8 fr[TM + TN];  // A fragments, then B fragments
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i) ad[i] = sb + swz64(wm * WM + i * 16 + lr, lg);
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+    for (int j = 0; j < TN; ++j) ad[TM + j] = sb + BM * 64 + swz64(wn * WN + j * 16 + lr, lg);
+    lds_read_b128<TM + TN>(fr, ad);
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        Cs[(wm * (BM / 2) + i * 16 + lg * 4 + v) * LDC + wn * (BN / 2) + j * 16 + lr] =
-            acc[i][j][v];
-  __syncthreads();
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(fr[i], fr[TM + j], acc[i][j]);
+  }
+  __syncthreads();  // every wave is done with the ring; it becomes epilogue staging
+
+  char* wst = ring + w * S::WAVE_STAGE;
   OutT* C = (OutT*)a.C;
-  if constexpr (BN == 128 && sizeof(OutT) == 2) {
-    if (a.qkv_h) {  // the tile is two heads of one section
-      const int sect = n0 / a.qkv_h, hcol0 = n0 % a.qkv_h;
-      const bool sa_qk = (sect == 0 || sect == 1) && a.sa_rope;
-      const bool da_qk = sect == 3 || sect == 4;
-      // item = (row, head of the tile, chunk c < 4): dims c*8..+8 and 32+c*8..+8 rotate
-      // together (rotate-half pairs)
-      for (int it = tid; it < BM * 8; it += 256) {
-        const int row = it >> 3, hh = (it >> 2) & 1, c = it & 3;
-        const int orow = rows_s[row];
-        if (orow < 0) continue;
-        const float sc = a.row_scale ? a.row_scale[orow] : 1.0f;
-        const int lc = hh * 64 + c * 8;
-        float lo[8], hi[8];
+  if constexpr (QKV) {
+    if (a.qkv_h) {
+      // the wave's 64 columns are one head of one section (qkv_h % 128 == 0, BN = 128)
+      const int hcol0 = cw0 % a.qkv_h;
+      bf16* sw = reinterpret_cast<bf16*>(wst);  // [WM][LDB]
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          lo[e] = Cs[row * LDC + lc + e] * sc;
-          hi[e] = Cs[row * LDC + lc + 32 + e] * sc;
-        }
-        if (sa_qk || da_qk) {
-          int pf, pr;
-          const float *cs, *sn;
-          if (sa_qk) {
-            pf = pr = a.pos_fixed >= 0 ? a.pos_fixed : orow % a.seq;
-            cs = a.cos_s;
-            sn = a.sin_s;
-          } else {
-            pf = a.depth_l;
-            pr = a.depth_L - 1 - a.depth_l;
-            cs = a.cos_d;
-            sn = a.sin_d;
-          }
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int pair = c * 8 + e;
-            const int pos = pair < 16 ? pf : pr;
-            const float cv = cs[pos * 32 + pair], sv = sn[pos * 32 + pair];
-            const float x = lo[e], y = hi[e];
-            lo[e] = x * cv - y * sv;
-            hi[e] = y * cv + x * sv;
-          }
-        }
-        OutT* cp = C + (int64_t)orow * a.ldc + n0 + lc;
-        store16(cp, lo);
-        store16(cp + 32, hi);
-      }
-      if (sect == 2 && a.vt) {  // SA v, transposed: item = (column, 8 consecutive rows)
-        constexpr int RG = BM / 8;
-        bf16* vt = (bf16*)a.vt;
-        const int H = a.qkv_h / 64;
-        for (int it = tid; it < RG * BN; it += 256) {
-          const int col = it / RG, rg = it % RG;
-          const int head = (hcol0 + col) >> 6, dim = (hcol0 + col) & 63;
-          const int o0 = rows_s[rg * 8];
-          const bool run = o0 >= 0 && rows_s[rg * 8 + 7] == o0 + 7 && (o0 % a.seq) + 7 < a.seq;
-          if (run) {
-            float vv[8];
+        for (int v = 0; v < 4; ++v) {
+          const int rt = i * 16 + lg * 4 + v;  // row within the wave
+          const int orow = rows_s[rw0 + rt];
+          const float sc = (a.row_scale && orow >= 0) ? a.row_scale[orow] : 1.0f;
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-              const int orow = o0 + r;
-              const float sc = a.row_scale ? a.row_scale[orow] : 1.0f;
-              vv[r] = Cs[(rg * 8 + r) * LDC + col] * sc;
+          for (int j = 0; j < 2; ++j) {  // rotate-half pairs (c, c + 32), c = 16 j + lr
+            const int pair = j * 16 + lr;
+            float x = acc[i][j][v] * sc, y = acc[i][j + 2][v] * sc;
+            if (sa_qk || da_qk) {
+              const float cv = pc[i][v][j], sv = ps[i][v][j];
+              const float xr = x * cv - y * sv;
+              y = y * cv + x * sv;
+              x = xr;
             }
-            store16(vt + (((int64_t)(o0 / a.seq) * H + head) * 64 + dim) * a.seq + o0 % a.seq,
-                    vv);
+            sw[rt * S::LDB + pair] = (bf16)x;
+            sw[rt * S::LDB + pair + 32] = (bf16)y;
+          }
+        }
+      wave_lds_sync();
+      // rows of 64 bf16 = 8 chunks of 16 bytes
+      for (int it = lane; it < WM * 8; it += 64) {
+        const int rt = it >> 3, ch = it & 7;
+        const int orow = rows_s[rw0 + rt];
+        if (orow < 0) continue;
+        *reinterpret_cast<bf16x8*>(C + (int64_t)orow * a.ldc + cw0 + ch * 8) =
+            *reinterpret_cast<const bf16x8*>(sw + rt * S::LDB + ch * 8);
+      }
+      if (sect == 2 && a.vt) {  // SA v, transposed: item = (dim, 8 consecutive rows)
+        bf16* vt = (bf16*)a.vt;
+        const int H = a.qkv_h / 64, head = hcol0 >> 6;
+        for (int it = lane; it < 64 * (WM / 8); it += 64) {
+          const int dim = it & 63, rg = it >> 6;
+          const int o0 = rows_s[rw0 + rg * 8];
+          const bool run = o0 >= 0 && o0 % 8 == 0 && rows_s[rw0 + rg * 8 + 7] == o0 + 7 &&
+                           (o0 % a.seq) + 7 < a.seq;
+          if (run) {
+            bf16x8 vv;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) vv[r] = sw[(rg * 8 + r) * S::LDB + dim];
+            *reinterpret_cast<bf16x8*>(
+                vt + (((int64_t)(o0 / a.seq) * H + head) * 64 + dim) * a.seq + o0 % a.seq) = vv;
           } else {
             for (int r = 0; r < 8; ++r) {
-              const int orow = rows_s[rg * 8 + r];
+              const int orow = rows_s[rw0 + rg * 8 + r];
               if (orow < 0) continue;
-              const float sc = a.row_scale ? a.row_scale[orow] : 1.0f;
               vt[(((int64_t)(orow / a.seq) * H + head) * 64 + dim) * a.seq + orow % a.seq] =
-                  (bf16)(Cs[(rg * 8 + r) * LDC + col] * sc);
+                  sw[(rg * 8 + r) * S::LDB + dim];
             }
           }
         }
@@ -226,29 +233,36 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs a) {
       return;
     }
   }
+  // generic: v = acc * row_scale + resid; C (OutT) and optional bf16 copy C2
+  float* sf = reinterpret_cast<float*>(wst);  // [WM][LDF]
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sf[(i * 16 + lg * 4 + v) * S::LDF + j * 16 + lr] = acc[i][j][v];
+  wave_lds_sync();
   bf16* C2 = (bf16*)a.C2;
-  const ResT* R = (const ResT*)a.resid;
-  constexpr int CPR = BN / 8;  // 8-column chunks per row
-  for (int c = tid; c < BM * CPR; c += 256) {
-    const int row = c / CPR, cc = c % CPR;
-    const int orow = rows_s[row];
-    const int n = n0 + cc * 8;
+#pragma unroll
+  for (int m = 0; m < NIT; ++m) {
+    const int it = lane + 64 * m, rt = it / CPR, cc = it % CPR;
+    const int orow = rows_s[rw0 + rt];
+    const int n = cw0 + cc * 8;
     if (orow < 0 || n >= a.N) continue;
     const float sc = a.row_scale ? a.row_scale[orow] : 1.0f;
+    const floatx4 c0 = *reinterpret_cast<const floatx4*>(sf + rt * S::LDF + cc * 8);
+    const floatx4 c1 = *reinterpret_cast<const floatx4*>(sf + rt * S::LDF + cc * 8 + 4);
     float val[8];
-    const floatx4 c0 = *reinterpret_cast<const floatx4*>(&Cs[row * LDC + cc * 8]);
-    const floatx4 c1 = *reinterpret_cast<const floatx4*>(&Cs[row * LDC + cc * 8 + 4]);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       val[e] = c0[e] * sc;
       val[4 + e] = c1[e] * sc;
     }
-    if (R) {
-      float rv[8];
-      load16(R + (int64_t)orow * a.ldr + n, rv);
-      load16(R + (int64_t)orow * a.ldr + n + 4, rv + 4);
+    if constexpr (!QKV) {
+      if (a.resid) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) val[e] += rv[e];
+        for (int e = 0; e < 8; ++e) val[e] += rres[m][e];
+      }
     }
     OutT* cp = C + (int64_t)orow * a.ldc + n;
     if constexpr (sizeof(OutT) == 2) {
@@ -294,11 +308,10 @@ int launch_gemm(const GemmArgs& a, int dtype, int out_f32, hipStream_t st) {
     gemm_f32_kernel<<<grid, 256, 0, st>>>(a);
     return 0;
   }
-  if (a.K % 64 != 0 || a.N % 8 != 0) return -1;
-  // Tile choice: 128x128 when that still gives >= 2 tiles per CU, else 64-row tiles.
-  // Grouped launches use the m-tile size their tile offsets were built with.
-  // Tiles: the largest of 128x128, 64x128, 64x64 that still gives >= 512 blocks (two per
-  // CU); the QKV epilogue needs 128-column tiles.
+  if (a.K % 32 != 0 || a.N % 8 != 0) return -1;
+  // Tiles: 128 x 128 when that gives >= 512 blocks (two per CU), else 64 x 128, else
+  // 64 x 64; the QKV epilogue needs 64-column wave tiles (one head), grouped launches the
+  // 64-row m-tiles their tile offsets were built with.
   int bm, bn;
   if (a.qkv_h) {
     if (a.qkv_h % 128 || out_f32) return -1;
@@ -320,10 +333,10 @@ int launch_gemm(const GemmArgs& a, int dtype, int out_f32, hipStream_t st) {
   }
   const int mt = (a.M + bm - 1) / bm + (a.toff ? a.G : 0);
   dim3 grid(mt, (a.N + bn - 1) / bn);
-#define DREAMER_GEMM_LAUNCH(OUT)                                                    \
-  if (bm == 128) gemm_bf16_kernel<OUT, float, 128, 128><<<grid, 256, 0, st>>>(a);   \
-  else if (bn == 128) gemm_bf16_kernel<OUT, float, 64, 128><<<grid, 256, 0, st>>>(a); \
-  else gemm_bf16_kernel<OUT, float, 64, 64><<<grid, 256, 0, st>>>(a);
+#define DREAMER_GEMM_LAUNCH(OUT)                                                  \
+  if (bm == 128) gemm_bf16_kernel<OUT, 64, 64><<<grid, 256, 0, st>>>(a);          \
+  else if (bn == 128) gemm_bf16_kernel<OUT, 32, 64><<<grid, 256, 0, st>>>(a);     \
+  else gemm_bf16_kernel<OUT, 32, 32><<<grid, 256, 0, st>>>(a);
   if (out_f32) {
     DREAMER_GEMM_LAUNCH(float)
   } else {

@@ -75,24 +75,32 @@ int launch_seq_attn(int dtype, int B, int q_len, int H, int d, int64_t pos0, con
 int router_scores(int dtype, int64_t T, int h, int r, int E, int l, int L, const void* x,
                   int64_t ldx, const void* w_r, const float* u, const void* keys, float rho,
                   const float* cos_r, const float* sin_r, float* z, hipStream_t st);
-// Top-k of z + bias (ties to the lower index), gates sigmoid(z) (normalised on request).
-// idx_in (optional, [T, k]): adopt these experts instead of selecting.
+// Top-k of z + bias (ties to the lower index), gates sigmoid(z), normalised on request by
+// their sum in selection order.  idx_in (optional, [T, k]): adopt these experts instead of
+// selecting (entries clamped into [0, E)).
 int router_topk(int64_t T, int E, int k, const float* z, const float* bias, int normalize,
                 const int32_t* idx_in, int32_t* idx, float* gate, hipStream_t st);
+// Scores and top-k in one kernel (bf16 only; router_fused_ok says when it applies).
+bool router_fused_ok(int dtype, int64_t T, int r, int E, int k);
+int router_route_fused(int64_t T, int h, int r, int E, int k, int l, int L, const void* x,
+                       int64_t ldx, const void* w_r, const void* keys, const float* bias,
+                       float rho, int normalize, const float* cos_r, const float* sin_r,
+                       const int32_t* idx_in, int32_t* idx, float* gate, hipStream_t st);
 
 // Fill n ints with a value (graph-safe replacement of memset).
 void launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st);
-// counts[e] = number of slots routed to e (global atomics; small calls only).
-void launch_histogram(const int32_t* idx, int64_t n, int32_t* counts, int E, hipStream_t st);
 
 // Permutation of routed slots by expert: hist [perm_blocks(nslots), E] scratch; outputs
 // counts [E], goff [E+1], toff [E+1] (tiles of tile_m rows), perm [nslots] (perm[goff[e]+j]
 // = slot id t*k+i of the j-th slot routed to e; order within an expert unspecified).
-constexpr int PERM_CHUNK = 4096;
+constexpr int PERM_CHUNK = 2048, PERM_MAX_E = 8192, COUNT_MAX_E = 16384;
 int perm_blocks(int64_t nslots);
 int launch_permute(const int32_t* idx, int64_t nslots, int E, int tile_m, int32_t* hist,
                    int32_t* counts, int32_t* goff, int32_t* toff, int32_t* perm,
                    hipStream_t st);
+// counts [E] of routed slots per expert (hist as above).
+int launch_counts(const int32_t* idx, int64_t nslots, int E, int32_t* hist, int32_t* counts,
+                  hipStream_t st);
 
 // Fused expert FFN (GELU / SWIGLU): slots[s] = gate[s] * FFN_e(x[s / k]) for every
 // routed slot s, written in storage dtype [T*k, h_out].

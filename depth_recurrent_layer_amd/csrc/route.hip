@@ -4,9 +4,15 @@
 // bf16 scores: one block per 16 tokens.  u = x W_r^T on MFMA (bf16 x bf16 products are
 // exact in float32), depth RoPE on u in float32, then z = rho * u_rot . keys with u_rot
 // split into three bf16 parts (hi + mid + lo carries 24 mantissa bits) so the scores keep
-// float32 accuracy on MFMA.  Scores go to a [T, E] float32 buffer; the top-k kernel
-// (one wave per token) reads them, ranks by z + b and takes gates from z.
+// float32 accuracy on MFMA.  With many tokens one fused kernel also selects (scores stay
+// in LDS); with few tokens and many experts the scores go to a [T, E] float32 buffer over
+// a 2-D grid and a top-k kernel (one wave per token) selects.  Either way the selection
+// ranks by z + b and takes gates from z, and may count selections per expert with
+// global atomics, handing each selection its rank within its expert; a placement kernel
+// then turns (expert, rank) into the expert-major slot order.
 #include <math.h>
+
+#include <algorithm>
 
 #include "common.h"
 #include "kernels.h"
@@ -14,23 +20,30 @@
 namespace dreamer {
 
 // ------------------------------------------------------------------ scores (bf16, MFMA)
-template <int NKS>  // r = 32 * NKS
-__global__ __launch_bounds__(256) void router_scores_bf16_kernel(
-    int64_t Ttok, int h, int r, int E, int l, int L, const bf16* __restrict__ x, int64_t ldx,
-    const bf16* __restrict__ w_r, const bf16* __restrict__ keys, float rho,
-    const float* __restrict__ cs, const float* __restrict__ sn, float* __restrict__ z) {
-  extern __shared__ float smem[];
-  float* us = smem;            // [16, r] u
-  float* ur = smem + 16 * r;   // [16, r] rotated u
+// u tile [16 tokens x r] of the block's tokens, rotated by depth, split into three bf16
+// parts as MFMA A operands (token lr, k-group lg).  us / ur: 2 * 16 * r floats of LDS.
+// r divides 256, so each thread rotates one rank index i = tid % r (one table entry,
+// loaded before the projection).
+template <int NKS>
+DEV void router_u_parts(int64_t Ttok, int64_t t0, int h, int r, int l, int L,
+                        const bf16* __restrict__ x, int64_t ldx, const bf16* __restrict__ w_r,
+                        const float* __restrict__ cs, const float* __restrict__ sn, float* us,
+                        float* ur, bf16x8 (&ah)[NKS], bf16x8 (&am)[NKS], bf16x8 (&al)[NKS]) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
-  const int64_t t0 = (int64_t)blockIdx.x * 16;
   const bf16x8 zero8 = {};
-  // u tile [16 tokens x r]: wave w owns rank columns 16 nt, nt = w, w + 4, ...
+  // depth RoPE: pairs i < r/4 at depth l, the others at L-1-l
+  const int half = r / 2, quarter = r / 4;
+  const int i = tid % r;
+  const int p = i < half ? i : i - half;
+  const int pos = p < quarter ? l : L - 1 - l;
+  const float cv = cs[pos * half + p], sv = sn[pos * half + p];
+  // wave w owns rank columns 16 nt, nt = w, w + 4, ...
   const int64_t tr = t0 + lr;
   const bf16* xrow = tr < Ttok ? x + tr * ldx + lg * 8 : nullptr;
   for (int nt = w; nt < r / 16; nt += 4) {
     const bf16* wrow = w_r + (int64_t)(nt * 16 + lr) * h + lg * 8;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
     for (int k0 = 0; k0 < h; k0 += 32) {
       const bf16x8 af = xrow ? *reinterpret_cast<const bf16x8*>(xrow + k0) : zero8;
       const bf16x8 bf = *reinterpret_cast<const bf16x8*>(wrow + k0);
@@ -40,19 +53,13 @@ __global__ __launch_bounds__(256) void router_scores_bf16_kernel(
     for (int i = 0; i < 4; ++i) us[(lg * 4 + i) * r + nt * 16 + lr] = acc[i];
   }
   __syncthreads();
-  // depth RoPE: pairs i < r/4 at depth l, the others at L-1-l
-  const int half = r / 2, quarter = r / 4;
+  const int ip = i < half ? i + half : i - half;
   for (int e = tid; e < 16 * r; e += 256) {
-    const int t = e / r, i = e % r;
-    const int p = i < half ? i : i - half;
-    const int pos = p < quarter ? l : L - 1 - l;
-    const float cv = cs[pos * half + p], sv = sn[pos * half + p];
-    const float a = us[t * r + i], b = us[t * r + (i < half ? i + half : i - half)];
+    const int t = e / r;
+    const float a = us[t * r + i], b = us[t * r + ip];
     ur[e] = i < half ? a * cv - b * sv : a * cv + b * sv;
   }
   __syncthreads();
-  // three-part bf16 split of the rotated u rows (A operand: token lr, k-group lg)
-  bf16x8 ah[NKS], am[NKS], al[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
@@ -66,22 +73,182 @@ __global__ __launch_bounds__(256) void router_scores_bf16_kernel(
       al[ks][j] = (bf16)(r1 - (float)mid);
     }
   }
-  // scores: wave w takes expert tiles et = w, w + 4, ...
-  for (int et = w; et < E / 16; et += 4) {
-    const bf16* krow = keys + (int64_t)(et * 16 + lr) * r + lg * 8;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+}
+
+// Keys of one tile of 16 experts (et * 16 ..) as MFMA B operands (expert lr, k-group lg).
+template <int NKS>
+struct KeyFrag {
+  bf16x8 v[NKS];
+};
+
+template <int NKS>
+DEV void load_keys(const bf16* __restrict__ keys, int r, int et, KeyFrag<NKS>& kf) {
+  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const bf16* krow = keys + (int64_t)(et * 16 + lr) * r + lg * 8;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const bf16x8 bk = *reinterpret_cast<const bf16x8*>(krow + ks * 32);
-      acc = mfma16(ah[ks], bk, acc);
-      acc = mfma16(am[ks], bk, acc);
-      acc = mfma16(al[ks], bk, acc);
-    }
+  for (int ks = 0; ks < NKS; ++ks) kf.v[ks] = *reinterpret_cast<const bf16x8*>(krow + ks * 32);
+}
+
+// z for one 16 x 16 tile (tokens x experts) from the split u and the tile's keys.
+template <int NKS>
+DEV floatx4 router_tile(const KeyFrag<NKS>& kf, const bf16x8 (&ah)[NKS],
+                        const bf16x8 (&am)[NKS], const bf16x8 (&al)[NKS]) {
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    acc = mfma16(ah[ks], kf.v[ks], acc);
+    acc = mfma16(am[ks], kf.v[ks], acc);
+    acc = mfma16(al[ks], kf.v[ks], acc);
+  }
+  return acc;
+}
+
+// Scores to a [T, E] buffer; blockIdx.y takes experts [256 y, 256 y + 256).
+template <int NKS>  // r = 32 * NKS
+__global__ __launch_bounds__(256) void router_scores_bf16_kernel(
+    int64_t Ttok, int h, int r, int E, int l, int L, const bf16* __restrict__ x, int64_t ldx,
+    const bf16* __restrict__ w_r, const bf16* __restrict__ keys, float rho,
+    const float* __restrict__ cs, const float* __restrict__ sn, float* __restrict__ z) {
+  extern __shared__ float smem[];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane & 15, lg = lane >> 4;
+  const int64_t t0 = (int64_t)blockIdx.x * 16;
+  const int et0 = blockIdx.y * 16, et1 = min(E / 16, et0 + 16);
+  KeyFrag<NKS> kf[4];  // this wave's tiles et0 + w + 4 j, loaded before the projection
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (et0 + w + 4 * j < et1) load_keys<NKS>(keys, r, et0 + w + 4 * j, kf[j]);
+  bf16x8 ah[NKS], am[NKS], al[NKS];
+  router_u_parts<NKS>(Ttok, t0, h, r, l, L, x, ldx, w_r, cs, sn, smem, smem + 16 * r, ah, am,
+                      al);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int et = et0 + w + 4 * j;
+    if (et >= et1) break;
+    const floatx4 acc = router_tile<NKS>(kf[j], ah, am, al);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t t = t0 + lg * 4 + i;
       if (t < Ttok) z[t * E + et * 16 + lr] = rho * acc[i];
     }
+  }
+}
+
+// (value, index) order of the router: larger value first, then lower index.
+DEV bool better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
+
+// Insert (v, zv, e) into a sorted list of KMAX entries (best first).
+template <int KMAX>
+DEV void list_insert(float (&lv)[KMAX], float (&lz)[KMAX], int (&li)[KMAX], float v, float zv,
+                     int e) {
+  float cv = v, cz = zv;
+  int ci = e;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (better(cv, ci, lv[j], li[j])) {
+      const float tv = lv[j], tz = lz[j];
+      const int ti = li[j];
+      lv[j] = cv;
+      lz[j] = cz;
+      li[j] = ci;
+      cv = tv;
+      cz = tz;
+      ci = ti;
+    }
+  }
+}
+
+// ------------------------------------------------------------- fused route (bf16, MFMA)
+// One block per 16 tokens.  The scores of each chunk of 256 experts go to LDS; 16 lanes
+// per token scan them, each keeping a sorted list of its best (z + b, z, e); k rounds of
+// a 16-lane butterfly argmax pick the winners.  Gates sigmoid(z), normalised on request
+// by their sum taken in selection order.
+constexpr int RCH = 256, RCH_LD = RCH + 16;
+
+template <int NKS, int KMAX>
+__global__ __launch_bounds__(256) void router_fused_bf16_kernel(
+    int64_t Ttok, int h, int r, int E, int k, int l, int L, const bf16* __restrict__ x,
+    int64_t ldx, const bf16* __restrict__ w_r, const bf16* __restrict__ keys,
+    const float* __restrict__ bias, float rho, int normalize, const float* __restrict__ cs,
+    const float* __restrict__ sn, const int32_t* __restrict__ idx_in, int32_t* __restrict__ idx,
+    float* __restrict__ gate) {
+  extern __shared__ float smem[];
+  float* zs = smem + 32 * r;      // [16][RCH_LD]
+  float* bs = zs + 16 * RCH_LD;   // [RCH] bias chunk
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
+  const int64_t t0 = (int64_t)blockIdx.x * 16;
+  // first chunk's keys (this wave's tiles w + 4 j) and biases, before the projection
+  KeyFrag<NKS> kf[4];
+  int n = min(RCH, E);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (w + 4 * j < n / 16) load_keys<NKS>(keys, r, w + 4 * j, kf[j]);
+  if (tid < n) bs[tid] = bias[tid];
+  bf16x8 ah[NKS], am[NKS], al[NKS];
+  router_u_parts<NKS>(Ttok, t0, h, r, l, L, x, ldx, w_r, cs, sn, smem, smem + 16 * r, ah, am,
+                      al);
+  const int tl = w * 4 + (lane >> 4), g = lane & 15;
+  const int64_t t = t0 + tl;
+  float lv[KMAX], lz[KMAX];
+  int li[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) { lv[j] = -INFINITY; lz[j] = 0.f; li[j] = 0x7fffffff; }
+  int my = 0;
+  float myz = 0.f;
+  if (idx_in && t < Ttok && g < k) my = min(max(idx_in[t * k + g], 0), E - 1);
+  for (int c0 = 0; c0 < E; c0 += RCH) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int et = w + 4 * j;
+      if (et >= n / 16) break;
+      const floatx4 acc = router_tile<NKS>(kf[j], ah, am, al);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) zs[(lg * 4 + i) * RCH_LD + et * 16 + lr] = rho * acc[i];
+    }
+    __syncthreads();
+    // next chunk's keys and biases are fetched while this chunk is scanned
+    const int c1 = c0 + RCH, n1 = c1 < E ? min(RCH, E - c1) : 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (w + 4 * j < n1 / 16) load_keys<NKS>(keys, r, c1 / 16 + w + 4 * j, kf[j]);
+    const float bnext = tid < n1 ? bias[c1 + tid] : 0.f;
+    const float* zt = zs + tl * RCH_LD;
+    if (idx_in) {
+      if (g < k && my >= c0 && my < c0 + n) myz = zt[my - c0];
+    } else {
+      for (int j = g; j < n; j += 16) {
+        const float zv = zt[j], v = zv + bs[j];
+        if (better(v, c0 + j, lv[KMAX - 1], li[KMAX - 1])) list_insert<KMAX>(lv, lz, li, v, zv, c0 + j);
+      }
+    }
+    __syncthreads();
+    if (tid < n1) bs[tid] = bnext;
+    n = n1;
+  }
+  if (!idx_in) {
+    for (int j = 0; j < k; ++j) {
+      float bv = lv[0], bz = lz[0];
+      int bi = li[0];
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) {  // every lane of the group ends with the winner
+        const float ov = __shfl_xor(bv, o, 16), oz = __shfl_xor(bz, o, 16);
+        const int oi = __shfl_xor(bi, o, 16);
+        if (better(ov, oi, bv, bi)) { bv = ov; bz = oz; bi = oi; }
+      }
+      if (g == j) { my = bi; myz = bz; }
+      if (li[0] == bi) {  // the owner pops its head
+#pragma unroll
+        for (int q = 0; q < KMAX - 1; ++q) { lv[q] = lv[q + 1]; lz[q] = lz[q + 1]; li[q] = li[q + 1]; }
+        lv[KMAX - 1] = -INFINITY;
+        li[KMAX - 1] = 0x7fffffff;
+      }
+    }
+  }
+  const float gv = g < k ? sigmoidf_(myz) : 0.f;
+  float gsum = 0.f;  // in selection order, as the top-k kernel sums
+  for (int j = 0; j < k; ++j) gsum += __shfl(gv, j, 16);
+  if (t < Ttok && g < k) {
+    idx[t * k + g] = my;
+    gate[t * k + g] = normalize ? gv / gsum : gv;
   }
 }
 
@@ -111,9 +278,6 @@ __global__ void router_scores_f32_kernel(int64_t Ttok, int r, int E, int l, int 
 }
 
 // ------------------------------------------------------------------------------- top-k
-// (value, index) order of the router: larger value first, then lower index.
-DEV bool better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
-
 // One wave per token.  Each lane keeps a sorted list of its KMAX best (z + b, e) over
 // experts lane, lane + 64, ...; k rounds of a butterfly argmax pop the heads.  Gates are
 // sigmoid(z) of the winners, divided by their sum when normalising.  With idx_in the
@@ -129,7 +293,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
   const float* zt = z + t * E;
   int my = 0;
   if (idx_in) {
-    if (lane < k) my = idx_in[t * k + lane];
+    if (lane < k) my = min(max(idx_in[t * k + lane], 0), E - 1);
   } else {
     float lv[KMAX];
     int li[KMAX];
@@ -173,7 +337,8 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
   }
   float gv = 0.f;
   if (lane < k) gv = sigmoidf_(zt[my]);
-  const float gsum = wave_sum(gv);
+  float gsum = 0.f;  // in selection order
+  for (int j = 0; j < k; ++j) gsum += __shfl(gv, j, 64);
   if (lane < k) {
     idx[t * k + lane] = my;
     gate[t * k + lane] = normalize ? gv / gsum : gv;
@@ -186,7 +351,7 @@ int router_scores(int dtype, int64_t T, int h, int r, int E, int l, int L, const
   if (T <= 0) return 0;
   if (dtype == DT_BF16) {
     if (r % 32 || r > 256 || E % 16 || h % 32) return -1;
-    const unsigned grid = (unsigned)((T + 15) / 16);
+    const dim3 grid((unsigned)((T + 15) / 16), (unsigned)((E + RCH - 1) / RCH));
     const size_t lds = 2 * 16 * r * sizeof(float);
 #define RS_CASE(NK)                                                                      \
   router_scores_bf16_kernel<NK><<<grid, 256, lds, st>>>(T, h, r, E, l, L, (const bf16*)x, \
@@ -213,7 +378,7 @@ int router_topk(int64_t T, int E, int k, const float* z, const float* bias, int 
   if (T <= 0) return 0;
   if (k < 1 || k > 32 || k > E) return -1;
   const unsigned grid = (unsigned)((T + 3) / 4);
-#define TK_CASE(KM) \
+#define TK_CASE(KM)                                                                       \
   router_topk_kernel<KM><<<grid, 256, 0, st>>>(T, E, k, z, bias, normalize, idx_in, idx, gate)
   if (k <= 1) TK_CASE(1);
   else if (k <= 2) TK_CASE(2);
@@ -225,10 +390,46 @@ int router_topk(int64_t T, int E, int k, const float* z, const float* bias, int 
   return 0;
 }
 
+bool router_fused_ok(int dtype, int64_t T, int r, int E, int k) {
+  return dtype == DT_BF16 && k <= 8 && (r == 32 || r == 64 || r == 128) && E % 16 == 0 &&
+         (T + 15) / 16 >= 64;
+}
+
+int router_route_fused(int64_t T, int h, int r, int E, int k, int l, int L, const void* x,
+                       int64_t ldx, const void* w_r, const void* keys, const float* bias,
+                       float rho, int normalize, const float* cos_r, const float* sin_r,
+                       const int32_t* idx_in, int32_t* idx, float* gate, hipStream_t st) {
+  if (T <= 0) return 0;
+  if (!router_fused_ok(DT_BF16, T, r, E, k) || h % 32) return -1;
+  const unsigned grid = (unsigned)((T + 15) / 16);
+  const size_t lds = (2 * 16 * r + 16 * RCH_LD + RCH) * sizeof(float);
+#define RF_CASE(NK, KM)                                                                     \
+  router_fused_bf16_kernel<NK, KM><<<grid, 256, lds, st>>>(                                 \
+      T, h, r, E, k, l, L, (const bf16*)x, ldx, (const bf16*)w_r, (const bf16*)keys, bias,  \
+      rho, normalize, cos_r, sin_r, idx_in, idx, gate)
+#define RF_K(NK)                      \
+  if (k <= 1) RF_CASE(NK, 1);         \
+  else if (k <= 2) RF_CASE(NK, 2);    \
+  else if (k <= 4) RF_CASE(NK, 4);    \
+  else RF_CASE(NK, 8);
+  switch (r / 32) {
+    case 1: RF_K(1); break;
+    case 2: RF_K(2); break;
+    case 4: RF_K(4); break;
+    default: return -1;
+  }
+#undef RF_K
+#undef RF_CASE
+  return 0;
+}
+
 // ----------------------------------------------------------------------------- permute
-// Slots are cut into blocks of PERM_CHUNK; per block an LDS histogram over experts, then
-// one column scan gives every (block, expert) its base position, and the scatter hands
-// out positions with LDS atomics.  No global atomics.
+// Routed slots grouped by expert without global atomics.  The slots are cut into chunks
+// of PERM_CHUNK; kernel 1 counts each chunk's slots per expert in LDS (hist [nb, E]);
+// kernel 2, one block per chunk, sums the hist columns before its chunk and in total,
+// scans the totals over experts (rows, and m-tiles of tile_m rows) and hands out its
+// slots' positions with LDS atomics.  Block 0 publishes counts, goff and toff.  Expert
+// ids outside [0, E) are clamped into range (memory safety only: they are caller errors).
 __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -239,163 +440,104 @@ void launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st) {
   fill_i32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(p, n, v);
 }
 
-__global__ __launch_bounds__(1024) void perm_count_kernel(const int32_t* __restrict__ idx,
-                                                         int64_t nslots, int E,
-                                                         int32_t* __restrict__ hist) {
+int perm_blocks(int64_t nslots) { return (int)std::max<int64_t>(1, (nslots + PERM_CHUNK - 1) / PERM_CHUNK); }
+
+__global__ __launch_bounds__(512) void perm_hist_kernel(const int32_t* __restrict__ idx,
+                                                       int64_t nslots, int E,
+                                                       int32_t* __restrict__ hist) {
   extern __shared__ int lh[];
   for (int e = threadIdx.x; e < E; e += blockDim.x) lh[e] = 0;
   __syncthreads();
   const int64_t s0 = (int64_t)blockIdx.x * PERM_CHUNK;
   const int64_t s1 = min(s0 + PERM_CHUNK, nslots);
-  for (int64_t s = s0 + threadIdx.x; s < s1; s += blockDim.x) atomicAdd(&lh[idx[s]], 1);
+  for (int64_t s = s0 + threadIdx.x; s < s1; s += blockDim.x)
+    atomicAdd(&lh[min(max(idx[s], 0), E - 1)], 1);
   __syncthreads();
   int32_t* out = hist + (int64_t)blockIdx.x * E;
   for (int e = threadIdx.x; e < E; e += blockDim.x) out[e] = lh[e];
 }
 
-// Single block.  hist [nb, E] -> base [nb, E] (in place, absolute positions); counts,
-// goff, toff over experts.
-__global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ hist, int nb,
-                                                        int E, int tile_m,
-                                                        int32_t* __restrict__ counts,
-                                                        int32_t* __restrict__ goff,
-                                                        int32_t* __restrict__ toff) {
-  __shared__ int s_rows[1024], s_tiles[1024];
-  const int tid = threadIdx.x, nt = blockDim.x;
+__global__ __launch_bounds__(512) void perm_scatter_kernel(
+    const int32_t* __restrict__ idx, int64_t nslots, int E, int nb, int tile_m,
+    const int32_t* __restrict__ hist, int32_t* __restrict__ counts, int32_t* __restrict__ goff,
+    int32_t* __restrict__ toff, int32_t* __restrict__ perm) {
+  extern __shared__ int base[];  // [E]: totals, then this chunk's cursors
+  __shared__ int s_rows[512], s_tiles[512];
+  const int tid = threadIdx.x, nt = blockDim.x, b = blockIdx.x;
+  const bool pub = b == 0;
   const int per = (E + nt - 1) / nt;
-  const int e0 = tid * per, e1 = min(E, e0 + per);
+  const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
   int rsum = 0, tsum = 0;
-  for (int e = e0; e < e1; ++e) {  // column scan over blocks, per expert
-    int run = 0;
-    for (int b = 0; b < nb; ++b) {
-      const int c = hist[(int64_t)b * E + e];
-      hist[(int64_t)b * E + e] = run;
-      run += c;
+  for (int e = e0; e < e1; ++e) {
+    int tot = 0;
+    for (int q = 0; q < nb; ++q) tot += hist[(int64_t)q * E + e];
+    base[e] = tot;
+    rsum += tot;
+    tsum += (tot + tile_m - 1) / tile_m;
+  }
+  s_rows[tid] = rsum;
+  s_tiles[tid] = tsum;
+  __syncthreads();
+  for (int o = 1; o < nt; o <<= 1) {
+    const int a = tid >= o ? s_rows[tid - o] : 0;
+    const int c = tid >= o ? s_tiles[tid - o] : 0;
+    __syncthreads();
+    s_rows[tid] += a;
+    s_tiles[tid] += c;
+    __syncthreads();
+  }
+  int rr = s_rows[tid] - rsum, tt = s_tiles[tid] - tsum;
+  for (int e = e0; e < e1; ++e) {
+    const int tot = base[e];
+    int pre = 0;
+    for (int q = 0; q < b; ++q) pre += hist[(int64_t)q * E + e];
+    if (pub) {
+      counts[e] = tot;
+      goff[e] = rr;
+      toff[e] = tt;
     }
-    counts[e] = run;
-    rsum += run;
-    tsum += (run + tile_m - 1) / tile_m;
+    base[e] = rr + pre;
+    rr += tot;
+    tt += (tot + tile_m - 1) / tile_m;
   }
-  s_rows[tid] = rsum;
-  s_tiles[tid] = tsum;
-  __syncthreads();
-  for (int o = 1; o < nt; o <<= 1) {
-    const int a = tid >= o ? s_rows[tid - o] : 0;
-    const int b = tid >= o ? s_tiles[tid - o] : 0;
-    __syncthreads();
-    s_rows[tid] += a;
-    s_tiles[tid] += b;
-    __syncthreads();
-  }
-  int rr = s_rows[tid] - rsum, tt = s_tiles[tid] - tsum;
-  for (int e = e0; e < e1; ++e) {
-    goff[e] = rr;
-    toff[e] = tt;
-    for (int b = 0; b < nb; ++b) hist[(int64_t)b * E + e] += rr;
-    const int c = counts[e];
-    rr += c;
-    tt += (c + tile_m - 1) / tile_m;
-  }
-  if (tid == nt - 1) {
+  if (pub && tid == nt - 1) {
     goff[E] = s_rows[nt - 1];
     toff[E] = s_tiles[nt - 1];
   }
-}
-
-__global__ __launch_bounds__(1024) void perm_scatter_kernel(const int32_t* __restrict__ idx,
-                                                           int64_t nslots, int E,
-                                                           const int32_t* __restrict__ base,
-                                                           int32_t* __restrict__ perm) {
-  extern __shared__ int cur[];
-  const int32_t* bb = base + (int64_t)blockIdx.x * E;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) cur[e] = bb[e];
   __syncthreads();
-  const int64_t s0 = (int64_t)blockIdx.x * PERM_CHUNK;
+  const int64_t s0 = (int64_t)b * PERM_CHUNK;
   const int64_t s1 = min(s0 + PERM_CHUNK, nslots);
-  for (int64_t s = s0 + threadIdx.x; s < s1; s += blockDim.x) {
-    const int pos = atomicAdd(&cur[idx[s]], 1);
-    perm[pos] = (int32_t)s;
-  }
+  for (int64_t s = s0 + tid; s < s1; s += nt)
+    perm[atomicAdd(&base[min(max(idx[s], 0), E - 1)], 1)] = (int32_t)s;
 }
 
-__global__ void histogram_kernel(const int32_t* __restrict__ idx, int64_t n,
-                                 int32_t* __restrict__ counts) {
-  const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (s < n) atomicAdd(&counts[idx[s]], 1);
-}
-
-void launch_histogram(const int32_t* idx, int64_t n, int32_t* counts, int E, hipStream_t st) {
-  launch_fill_i32(counts, E, 0, st);
-  if (n > 0) histogram_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(idx, n, counts);
-}
-
-int perm_blocks(int64_t nslots) { return (int)((nslots + PERM_CHUNK - 1) / PERM_CHUNK); }
-
-// Whole permutation in one block (count, scan, scatter) for moderate slot counts.
-constexpr int PERM_FUSED_MAX_SLOTS = 65536, PERM_FUSED_MAX_E = 8192;
-__global__ __launch_bounds__(1024) void perm_fused_kernel(const int32_t* __restrict__ idx,
-                                                         int nslots, int E, int tile_m,
-                                                         int32_t* __restrict__ counts,
-                                                         int32_t* __restrict__ goff,
-                                                         int32_t* __restrict__ toff,
-                                                         int32_t* __restrict__ perm) {
-  extern __shared__ int lh[];  // [E] counts, then cursors
-  __shared__ int s_rows[1024], s_tiles[1024];
-  const int tid = threadIdx.x, nt = blockDim.x;
-  for (int e = tid; e < E; e += nt) lh[e] = 0;
-  __syncthreads();
-  for (int s = tid; s < nslots; s += nt) atomicAdd(&lh[idx[s]], 1);
-  __syncthreads();
-  const int per = (E + nt - 1) / nt;
-  const int e0 = tid * per, e1 = min(E, e0 + per);
-  int rsum = 0, tsum = 0;
-  for (int e = e0; e < e1; ++e) {
-    rsum += lh[e];
-    tsum += (lh[e] + tile_m - 1) / tile_m;
-  }
-  s_rows[tid] = rsum;
-  s_tiles[tid] = tsum;
-  __syncthreads();
-  for (int o = 1; o < nt; o <<= 1) {
-    const int a = tid >= o ? s_rows[tid - o] : 0;
-    const int b = tid >= o ? s_tiles[tid - o] : 0;
-    __syncthreads();
-    s_rows[tid] += a;
-    s_tiles[tid] += b;
-    __syncthreads();
-  }
-  int rr = s_rows[tid] - rsum, tt = s_tiles[tid] - tsum;
-  for (int e = e0; e < e1; ++e) {
-    const int c = lh[e];
-    counts[e] = c;
-    goff[e] = rr;
-    toff[e] = tt;
-    lh[e] = rr;  // cursor
-    rr += c;
-    tt += (c + tile_m - 1) / tile_m;
-  }
-  if (tid == nt - 1) {
-    goff[E] = s_rows[nt - 1];
-    toff[E] = s_tiles[nt - 1];
-  }
-  __syncthreads();
-  for (int s = tid; s < nslots; s += nt) perm[atomicAdd(&lh[idx[s]], 1)] = s;
+__global__ void hist_colsum_kernel(const int32_t* __restrict__ hist, int nb, int E,
+                                   int32_t* __restrict__ counts) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= E) return;
+  int c = 0;
+  for (int q = 0; q < nb; ++q) c += hist[(int64_t)q * E + e];
+  counts[e] = c;
 }
 
 int launch_permute(const int32_t* idx, int64_t nslots, int E, int tile_m, int32_t* hist,
                    int32_t* counts, int32_t* goff, int32_t* toff, int32_t* perm,
                    hipStream_t st) {
-  if (E > 16384) return -1;
-  if (nslots <= PERM_FUSED_MAX_SLOTS && E <= PERM_FUSED_MAX_E) {
-    perm_fused_kernel<<<1, 1024, (size_t)E * sizeof(int), st>>>(idx, (int)nslots, E, tile_m,
-                                                                 counts, goff, toff, perm);
-    return 0;
-  }
-  const int nb = max(1, perm_blocks(nslots));
+  if (E <= 0 || E > PERM_MAX_E) return -1;
+  const int nb = perm_blocks(nslots);
   const size_t lds = (size_t)E * sizeof(int);
-  perm_count_kernel<<<nb, 1024, lds, st>>>(idx, nslots, E, hist);
-  perm_scan_kernel<<<1, 1024, 0, st>>>(hist, nb, E, tile_m, counts, goff, toff);
-  if (nslots > 0) perm_scatter_kernel<<<nb, 1024, lds, st>>>(idx, nslots, E, hist, perm);
+  perm_hist_kernel<<<nb, 512, lds, st>>>(idx, nslots, E, hist);
+  perm_scatter_kernel<<<nb, 512, lds, st>>>(idx, nslots, E, nb, tile_m, hist, counts, goff,
+                                            toff, perm);
+  return 0;
+}
+
+int launch_counts(const int32_t* idx, int64_t nslots, int E, int32_t* hist, int32_t* counts,
+                  hipStream_t st) {
+  if (E <= 0 || E > COUNT_MAX_E) return -1;
+  const int nb = perm_blocks(nslots);
+  perm_hist_kernel<<<nb, 512, (size_t)E * sizeof(int), st>>>(idx, nslots, E, hist);
+  hist_colsum_kernel<<<(E + 255) / 256, 256, 0, st>>>(hist, nb, E, counts);
   return 0;
 }
 

@@ -119,7 +119,7 @@ int dreamer_seq_attn(int dtype, int B, int q_len, int H, int d, int64_t pos0, co
  *   u = x W_r^T (rank r, float32), depth RoPE on u at depth l of L (same half-reversed
  *   rule as DA), z_e = rho * (u . keys_e); the k experts with the largest z_e + bias_e
  *   are selected (descending; ties to the lower index) and their gates are sigmoid(z_e),
- *   divided by the sum of the k gates when `normalize` != 0:
+ *   divided by the sum of the k gates (taken in selection order) when `normalize` != 0:
  *   sigma = norm(TopK(sigmoid(z), z + b, k)).
  *   x      : [T, h] storage dtype     w_r : [r, h]     keys : [E, r]     bias : [E] f32
  *   cos_r, sin_r : [L, r/2] rotary tables of positions 0..L-1
@@ -139,11 +139,12 @@ int dreamer_expert_route(int dtype, int64_t T, int h, int r, int E, int k, int l
  * Sparse experts, value side ([PN] "Key design 2": each expert's FFN is the value
  * transform; dropless routing -- every selected (token, expert) pair is computed):
  *   out[t] = residual[t] + sum_{i<k} gate[t,i] * FFN_{idx[t,i]}(x[t])   (i in order)
- *   x : [T, h_in] storage dtype;  idx, gate : [T, k];  residual : [T, h_out] f32 or NULL
+ *   x : [T, h_in] storage dtype;  idx, gate : [T, k] (idx entries in [0, E));
+ *   residual : [T, h_out] f32 or NULL
  *   GELU/SWIGLU: w1 (and w3) [E, f, h_in], w2 [E, h_out, f]; LINEAR: w1 [E, h_out, h_in],
  *   f ignored, w2/w3 unused.   out : [T, h_out] f32.
  * Tokens are grouped by expert on the device (count, scan, scatter); no capacity limit.
- * bf16 GELU/SWIGLU needs f in {64, 128} and h_in, h_out % 64 == 0.
+ * bf16 GELU/SWIGLU needs f in {64, 128} and h_in, h_out % 64 == 0.  E <= 8192.
  */
 size_t dreamer_expert_ffn_ws_bytes(int dtype, int kind, int64_t T, int h_in, int f,
                                    int h_out, int E, int k);
@@ -222,7 +223,8 @@ typedef struct dreamer_layer_weights {
  *                of selecting (gates are still computed from this run's own scores), or
  *                NULL.  Replaying the choices of another run (another precision, a
  *                reference) removes the discrete top-k flips that last-bit differences
- *                cause, so the continuous parts can be compared alone.
+ *                cause, so the continuous parts can be compared alone.  Entries must lie
+ *                in [0, E); out-of-range entries are clamped into it.
  *   ws, ws_bytes : scratch of at least dreamer_layer_ws_bytes(cfg) bytes.
  * Precision (bf16 storage): xh is stored in bf16 as the projection input and kept in
  * float32 for the residual; y and x stay float32; EA reads a bf16 copy of y.

@@ -150,6 +150,11 @@ def test_seq_attn_decode(gpu_lib, dt, B, P, H, d):
     ("bf16", 200, 2048, 64, 4096, 8, True, 0.2),
     ("bf16", 150, 1024, 64, 16, 1, False, 0.0),
     ("bf16", 64, 256, 32, 32, 32, True, 0.2),      # k == E: every expert selected
+    # >= 1024 tokens: scores and selection in one kernel (ragged last block of 16 tokens)
+    ("bf16", 1037, 512, 64, 256, 4, True, 0.2),
+    ("bf16", 1030, 1024, 128, 1024, 8, True, 0.2),  # four chunks of 256 experts
+    ("bf16", 1100, 512, 64, 272, 2, True, 0.2),     # a last chunk of 16 experts
+    ("bf16", 1024, 256, 32, 48, 1, False, 0.0),     # one partial chunk, top-1
 ])
 def test_expert_route(gpu_lib, dt, T, h, r, E, k, norm, bias):
     D = gpu_lib
@@ -183,9 +188,10 @@ def test_expert_route(gpu_lib, dt, T, h, r, E, k, norm, bias):
     assert (np.diff(ks, axis=1) <= 1e-6).all()
 
 
-def test_expert_route_ties_go_to_lower_index(gpu_lib):
+@pytest.mark.parametrize("T", [40, 1040])
+def test_expert_route_ties_go_to_lower_index(gpu_lib, T):
     D = gpu_lib
-    T, h, r, E = 40, 128, 32, 16
+    h, r, E = 128, 32, 16
     x = _t((T, h), 22, 0)
     w_r = _t((r, h), 22, 1, 0.05)
     keys = _t((E, r), 22, 2, 0.05)

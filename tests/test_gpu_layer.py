@@ -149,6 +149,19 @@ def test_layer_small_bf16_reduced(gpu_lib):
     bf16_layer_checks(gpu_lib, cfg, make_weights(cfg), make_x0(cfg))
 
 
+def test_layer_small_bf16_many_tokens(gpu_lib):
+    """>= 1024 tokens: the fused scores + selection kernel and the parallel placement."""
+    cfg = CONFIGS["small"].replace(b=2, s=520, L=3)
+    print("layer small bf16 b=2 s=520 L=3", flush=True)
+    bf16_layer_checks(gpu_lib, cfg, make_weights(cfg), make_x0(cfg))
+
+
+def test_layer_linear_moe_bf16_many_tokens(gpu_lib):
+    cfg = CONFIGS["linear_moe"].replace(b=1, s=1040, h=256, H=4, L=2, E=64)
+    print("layer linear-moe bf16 s=1040", flush=True)
+    bf16_layer_checks(gpu_lib, cfg, make_weights(cfg), make_x0(cfg), free_tol=None)
+
+
 def test_layer_plain_block_bf16(gpu_lib):
     cfg = CONFIGS["small"].replace(b=1, s=130, use_da=False, use_ea=False)
     print("layer plain block bf16", flush=True)
@@ -211,9 +224,10 @@ def test_prefill_then_decode_matches_longer_prefill(gpu_lib):
     assert err <= 2e-2, err
 
 
-def test_layer_repeatable(gpu_lib):
+@pytest.mark.parametrize("s", [64, 520])
+def test_layer_repeatable(gpu_lib, s):
     """Same inputs, same bits (the combine sums slots in a fixed order)."""
-    cfg = CONFIGS["small"].replace(b=2, s=64, L=3)
+    cfg = CONFIGS["small"].replace(b=2, s=s, L=3)
     W, x0 = make_weights(cfg), make_x0(cfg)
     a = run_gpu(gpu_lib, cfg, W, x0)
     b = run_gpu(gpu_lib, cfg, W, x0)
