@@ -286,6 +286,48 @@ def _project(cfg, W, x, name, pidx, pgate, st):
     return out
 
 
+def _sa_branch(cfg, W, qkv, l, sa_k, sa_v, st, bf16):
+    """SA at depth l from the SA columns [q | k | v] of a projection ([PN] equation:
+    SA(x_l)).  R21: q and k are rotated from the projection itself and stored once,
+    rotated; v is stored as projected; rotation by sequence position (R5)."""
+    T, h, H, d = cfg.T, cfg.h, cfg.H, cfg.d
+    b, s, base = cfg.b, cfg.s, cfg.rope_base
+    q_sa, k_sa, v_sa = [qkv[:, j * h:(j + 1) * h].reshape(T, H, d) for j in range(3)]
+    pos = np.full(T, float(cfg.sa_pos)) if cfg.decode else (np.arange(T) % s).astype(float)
+    if cfg.sa_rope:
+        q_sa = rope(q_sa, pos[:, None, None], base)
+        k_sa = rope(k_sa, pos[:, None, None], base)
+    q_sa, k_sa, v_sa = st(q_sa), st(k_sa), st(v_sa)
+    if cfg.decode:
+        P = cfg.sa_pos
+        a_sa, k_rot, v_app = seq_attn(q_sa.reshape(b, 1, H, d), k_sa.reshape(b, 1, H, d),
+                                      v_sa.reshape(b, 1, H, d), P, sa_k[l], sa_v[l],
+                                      False, base, bf16)
+        sa_k[l][:, P] = k_rot[:, 0]
+        sa_v[l][:, P] = v_app[:, 0]
+    else:
+        a_sa, k_rot, v_app = seq_attn(q_sa.reshape(b, s, H, d), k_sa.reshape(b, s, H, d),
+                                      v_sa.reshape(b, s, H, d), 0, None, None, False,
+                                      base, bf16)
+        if sa_k is not None:
+            sa_k[l][:, :s] = k_rot
+            sa_v[l][:, :s] = v_app
+    return a_sa.reshape(T, h)
+
+
+def _da_branch(cfg, W, qkv, l, da_k, da_v, st, bf16):
+    """DA over depths 0..l from the DA columns [q | k | v] of a projection (R1, R4, R21:
+    q and k rotated by depth, stored once)."""
+    T, h, H, d, L = cfg.T, cfg.h, cfg.H, cfg.d, cfg.L
+    if not cfg.use_da:
+        return np.zeros((T, h))
+    q_da, k_da, v_da = [qkv[:, (3 + j) * h:(4 + j) * h].reshape(T, H, d) for j in range(3)]
+    q_da = st(depth_rope(q_da, l, L, cfg.rope_base))
+    k_da = st(depth_rope(k_da, l, L, cfg.rope_base))
+    return depth_attn(q_da, k_da, st(v_da), da_k, da_v, l, L, cfg.rope_base, bf16,
+                      use_rope=False).reshape(T, h)
+
+
 def layer_step(cfg, W, x, l, da_k, da_v, sa_k=None, sa_v=None, force_idx=None,
                force_pidx=None):
     """One depth step l ([PN] flowchart: RMSNorm -> DA + SA -> residual -> EA).
@@ -296,12 +338,18 @@ def layer_step(cfg, W, x, l, da_k, da_v, sa_k=None, sa_v=None, force_idx=None,
     Prefill with sa_k given: positions 0..s-1 of depth l are written (prefill -> decode
     handoff).  force_idx / force_pidx adopt externally given routing (the gates still
     come from this step's own scores).
-    Returns dict(x_next, y, yb, idx, gate, pidx, pgate, counts)."""
+
+    cfg.mixture ([PN] ablation of the mixture's parallelism; R22):
+      "partial"  y = x^ + DA(x^) + SA(x^),  x' = y + EA(y)           (the pages' default)
+      "serial"   u = x^ + DA(x^),  v = u + SA(u),  x' = v + EA(v)     (DA -> SA -> EA)
+      "parallel" x' = x^ + DA(x^) + SA(x^) + EA(x^)                   (all three at once)
+    Returns dict(x_next, y, yb, idx, gate, pidx, pgate, counts, z, pz); y / yb is the
+    stream EA reads from (partial, serial) or the attention sum (parallel)."""
     bf16 = cfg.dtype == "bf16"
     st = _store(bf16)
-    T, h, H, d, L = cfg.T, cfg.h, cfg.H, cfg.d, cfg.L
-    b, s = cfg.b, cfg.s
+    T, h, L = cfg.T, cfg.h, cfg.L
     base = cfg.rope_base
+    mix = getattr(cfg, "mixture", "partial")
     # R2: one RMSNorm per step, on the stream itself, at the loop head; x_hat is both
     # the attention input and the residual of the parallel-residual equation.  R20: the
     # residual keeps x_hat at full precision; the projections read its storage copy.
@@ -318,58 +366,39 @@ def layer_step(cfg, W, x, l, da_k, da_v, sa_k=None, sa_v=None, force_idx=None,
             pidx = np.asarray(force_pidx).reshape(T, 1)
             pgate = sigmoid(np.take_along_axis(pz, pidx, axis=-1))
         pidx, pgate = pidx[:, 0], pgate[:, 0]
-    qkv = _project(cfg, W, xhb, "qkv", pidx, pgate, st)
-    q_sa, k_sa, v_sa, q_da, k_da, v_da = [qkv[:, j * h:(j + 1) * h].reshape(T, H, d)
-                                          for j in range(6)]
-    # R21: q and k are rotated from the projection itself and stored once, rotated; v is
-    # stored as projected.  SA rotates by sequence position, DA by depth (R4, R5).
-    pos = np.full(T, float(cfg.sa_pos)) if cfg.decode else (np.arange(T) % s).astype(float)
-    if cfg.sa_rope:
-        q_sa = rope(q_sa, pos[:, None, None], base)
-        k_sa = rope(k_sa, pos[:, None, None], base)
-    q_sa, k_sa, v_sa = st(q_sa), st(k_sa), st(v_sa)
-    q_da = st(depth_rope(q_da, l, L, base))
-    k_da = st(depth_rope(k_da, l, L, base))
-    v_da = st(v_da)
-    # SA at depth l only ([PN] equation: SA(x_l)).
-    if cfg.decode:
-        P = cfg.sa_pos
-        a_sa, k_rot, v_app = seq_attn(q_sa.reshape(b, 1, H, d), k_sa.reshape(b, 1, H, d),
-                                      v_sa.reshape(b, 1, H, d), P, sa_k[l], sa_v[l],
-                                      False, base, bf16)
-        sa_k[l][:, P] = k_rot[:, 0]
-        sa_v[l][:, P] = v_app[:, 0]
+    zero = np.zeros((T, h))
+    if mix == "serial":
+        # R22: DA first on x_hat; its residual sum u feeds SA (through u's storage copy);
+        # the output projections act on one branch at a time ([a_SA | 0], [0 | a_DA]).
+        a_da = _da_branch(cfg, W, _project(cfg, W, xhb, "qkv", pidx, pgate, st), l,
+                          da_k, da_v, st, bf16)
+        u = xh + _project(cfg, W, np.concatenate([zero, a_da], axis=1), "o", pidx, pgate, st)
+        a_sa = _sa_branch(cfg, W, _project(cfg, W, st(u), "qkv", pidx, pgate, st), l,
+                          sa_k, sa_v, st, bf16)
+        y = u + _project(cfg, W, np.concatenate([a_sa, zero], axis=1), "o", pidx, pgate, st)
     else:
-        a_sa, k_rot, v_app = seq_attn(q_sa.reshape(b, s, H, d), k_sa.reshape(b, s, H, d),
-                                      v_sa.reshape(b, s, H, d), 0, None, None, False,
-                                      base, bf16)
-        if sa_k is not None:
-            sa_k[l][:, :s] = k_rot
-            sa_v[l][:, :s] = v_app
-    a_sa = a_sa.reshape(T, h)
-    if cfg.use_da:
-        a_da = depth_attn(q_da, k_da, v_da, da_k, da_v, l, L, base, bf16,
-                          use_rope=False).reshape(T, h)
-    else:
-        a_da = np.zeros((T, h))
-    att = np.concatenate([a_sa, a_da], axis=1)
-    # Parallel residual y = x_l + DA(x_{:l}) + SA(x_l) ([PN] "Key design 1"); the two
-    # output projections act on [a_SA | a_DA] (R6: separate SA and DA projections).
-    y = xh + _project(cfg, W, att, "o", pidx, pgate, st)
+        qkv = _project(cfg, W, xhb, "qkv", pidx, pgate, st)
+        a_sa = _sa_branch(cfg, W, qkv, l, sa_k, sa_v, st, bf16)
+        a_da = _da_branch(cfg, W, qkv, l, da_k, da_v, st, bf16)
+        # Parallel residual y = x_l + DA(x_{:l}) + SA(x_l) ([PN] "Key design 1"); the two
+        # output projections act on [a_SA | a_DA] (R6: separate SA and DA projections).
+        y = xh + _project(cfg, W, np.concatenate([a_sa, a_da], axis=1), "o", pidx, pgate,
+                          st)
     yb = st(y)
     idx = gate = counts = z = None
     x_next = y
     if cfg.use_ea:
-        # R7: EA reads y (no second norm).
-        idx, gate, counts, z = expert_route(yb, W["w_r"], W["keys"], W["bias"], cfg.k, l, L,
-                                            cfg.rho, cfg.normalize, base)
+        # R7: EA reads y (no second norm); in the fully parallel wiring it reads x_hat.
+        ea_in = xhb if mix == "parallel" else yb
+        idx, gate, counts, z = expert_route(ea_in, W["w_r"], W["keys"], W["bias"], cfg.k, l,
+                                            L, cfg.rho, cfg.normalize, base)
         if force_idx is not None:
             idx = np.asarray(force_idx).reshape(T, cfg.k)
             gate = sigmoid(np.take_along_axis(z, idx, axis=-1))
             if cfg.normalize:
                 gate = gate / np.sum(gate, axis=-1, keepdims=True)
             counts = np.bincount(idx.reshape(-1), minlength=cfg.E)
-        x_next = expert_ffn(cfg.ffn, yb, idx, gate, W["w1"], W.get("w3"), W["w2"],
+        x_next = expert_ffn(cfg.ffn, ea_in, idx, gate, W["w1"], W.get("w3"), W["w2"],
                             residual=y, bf16=bf16)
     return dict(x_next=x_next, y=y, yb=yb, idx=idx, gate=gate, pidx=pidx, pgate=pgate,
                 counts=counts, z=z, pz=pz)

@@ -67,6 +67,7 @@ class DreamerConfig:
     rope_base: float = 10000.0
     rms_eps: float = 1e-6
     rho: float = 1.0
+    mixture: str = "partial"  # "partial" (DA+SA, then EA), "serial", "parallel"
 
     @property
     def T(self) -> int:

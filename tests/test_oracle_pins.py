@@ -419,3 +419,79 @@ def test_golden_tiny_regression():
     r = oracle.layer_forward(cfg, W, make_x0(cfg).numpy())
     assert np.allclose(r["x_out"], data["x_out"], atol=1e-12, rtol=0)
     assert np.array_equal(r["idx"], data["idx"])
+
+
+# ------------------------------------------------------------------------ mixture wirings
+
+def _layer(cfg, W=None, x0=None):
+    W = make_weights(cfg) if W is None else W
+    x0 = make_x0(cfg) if x0 is None else x0
+    return oracle.layer_forward(cfg, oracle.prepare_weights(W), x0.numpy())["x_out"]
+
+
+def test_mixtures_coincide_where_their_definitions_do():
+    base = CONFIGS["tiny"].replace(b=2, s=9, L=3)
+    # no DA: serial (DA -> SA -> EA) is the default wiring; no EA: so is the fully
+    # parallel one
+    for mix, kw in (("serial", dict(use_da=False)), ("parallel", dict(use_ea=False))):
+        c = base.replace(**kw)
+        assert np.array_equal(_layer(c.replace(mixture=mix)), _layer(c))
+    # zero output projections: every wiring reduces to x' = x^ + EA(x^) at every depth
+    W = make_weights(base)
+    W["w_o"] = torch.zeros_like(W["w_o"])
+    outs = [_layer(base.replace(mixture=m), W) for m in ("partial", "serial", "parallel")]
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+    # in general the three differ
+    outs = [_layer(base.replace(mixture=m)) for m in ("partial", "serial", "parallel")]
+    for i, j in ((0, 1), (0, 2), (1, 2)):
+        assert np.abs(outs[i] - outs[j]).max() > 1e-3
+
+
+def _sa_torch(u, W, cfg):
+    """Causal SDPA over RoPE'd q, k (complex-rotation form) from rows 0..3h of w_qkv."""
+    h, H, d = cfg.h, cfg.H, cfg.d
+    q, k, v = (u @ W["w_qkv"][j * h:(j + 1) * h].T for j in range(3))
+    pos = (np.arange(cfg.T) % cfg.s).astype(np.float64)[:, None, None]
+    q = _rope_complex(q.reshape(cfg.T, H, d), pos, cfg.rope_base)
+    k = _rope_complex(k.reshape(cfg.T, H, d), pos, cfg.rope_base)
+    sh = lambda a: torch.from_numpy(np.ascontiguousarray(
+        a.reshape(cfg.b, cfg.s, H, d).transpose(0, 2, 1, 3)))
+    att = F.scaled_dot_product_attention(sh(q), sh(k), sh(v), is_causal=True)
+    return att.numpy().transpose(0, 2, 1, 3).reshape(cfg.T, h)
+
+
+def test_serial_wiring_one_depth_closed_form():
+    """L = 1, float32 storage, no EA: DA over one depth returns its value projection, so
+    u = x^ + (x^ W_V^DA) W_O^DA; then x_1 = u + SA(u) W_O^SA with SA as torch SDPA."""
+    cfg = CONFIGS["tiny"].replace(b=2, s=7, L=1, use_ea=False, mixture="serial")
+    W = oracle.prepare_weights(make_weights(cfg))
+    x0 = make_x0(cfg).numpy().reshape(cfg.T, cfg.h)
+    got = oracle.layer_forward(cfg, W, x0)["x_out"]
+    h = cfg.h
+    xh = F.rms_norm(torch.from_numpy(x0.astype(np.float64)), (h,),
+                    torch.from_numpy(W["g"]), eps=cfg.rms_eps).numpy()
+    u = xh + (xh @ W["w_qkv"][5 * h:6 * h].T) @ W["w_o"][:, h:].T
+    ref = u + _sa_torch(u, W, cfg) @ W["w_o"][:, :h].T
+    assert np.allclose(got, ref, atol=1e-11)
+
+
+def test_parallel_wiring_one_depth_closed_form():
+    """L = 1, float32 storage, no DA: x_1 = x^ + SA(x^) W_O^SA + g * FFN_e(x^), with the
+    top-1 expert e and its gate g computed here from the router's definition (depth RoPE
+    at l = 0, L = 1 is the identity)."""
+    cfg = CONFIGS["tiny"].replace(b=2, s=7, L=1, use_da=False, mixture="parallel")
+    W = oracle.prepare_weights(make_weights(cfg))
+    x0 = make_x0(cfg).numpy().reshape(cfg.T, cfg.h)
+    got = oracle.layer_forward(cfg, W, x0)["x_out"]
+    h = cfg.h
+    xh = F.rms_norm(torch.from_numpy(x0.astype(np.float64)), (h,),
+                    torch.from_numpy(W["g"]), eps=cfg.rms_eps).numpy()
+    z = cfg.rho * (xh @ W["w_r"].T) @ W["keys"].T
+    e = np.argmax(z + W["bias"][None, :], axis=1)
+    g = 1.0 / (1.0 + np.exp(-z[np.arange(cfg.T), e]))
+    ffn = np.stack([W["w2"][e[t]] @ (0.5 * (W["w1"][e[t]] @ xh[t]) *
+                                     (1 + np.vectorize(math.erf)((W["w1"][e[t]] @ xh[t]) /
+                                                                 math.sqrt(2))))
+                    for t in range(cfg.T)])
+    ref = xh + _sa_torch(xh, W, cfg) @ W["w_o"][:, :h].T + g[:, None] * ffn
+    assert np.allclose(got, ref, atol=1e-11)
