@@ -5,7 +5,9 @@
 One step = one dreamer_layer_forward over the whole workload (all L depth steps of
 RMSNorm, projections, SA, DA, routing, permutation, expert FFNs and combine) on inputs
 already resident in HBM.  Prints one JSON line.  Inputs are seeded synthetic tensors of
-the workload's shapes (weights N(0, 0.02), tokens N(0, 1)), drawn on the device.
+the workload's shapes (weights N(0, 0.02), tokens N(0, 1)), drawn on the device.  The line
+also carries the per-step time of the three mixture wirings (serial, the default partial
+one, fully parallel) and their throughput relative to the serial wiring.
 """
 from __future__ import annotations
 
@@ -34,6 +36,8 @@ def parse():
     p.add_argument("--workload", default="small")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--kernel-class", default=None, help="time this class live (default: dominant)")
+    p.add_argument("--no-mixtures", action="store_true",
+                   help="skip timing the serial / partial / fully parallel wirings")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (read + write), for scaling "
                         "the FETCH_SIZE / WRITE_SIZE counters")
@@ -104,6 +108,41 @@ def roofline_entry(work, avg_ms):
     ach = work["flops"] / work["launches"] / (avg_ms * 1e-3) / 1e12
     return {"bound": "alu", "achieved": round(ach, 2), "peak": PEAK_FP32_TFLOPS,
             "unit": "TFLOP/s", "frac": round(ach / PEAK_FP32_TFLOPS, 4), "traffic": None}
+
+
+# Relative per-step throughput of the wirings over the serial one, as the pages report it
+# for their model (another machine and model size: context, not a target).
+PAGES_RELATIVE = {"serial": 0.0, "partial": 0.152, "parallel": 0.308}
+
+
+def time_mixtures(D, cfg, G, x0, steps):
+    """ms per forward of the three mixture wirings (the fully parallel one with its EA chain
+    on a side stream) and their throughput relative to the serial wiring."""
+    import torch
+    out = {}
+    x_out = torch.empty((cfg.T, cfg.h), dtype=torch.float32, device="cuda")
+    for mix in ("serial", "partial", "parallel"):
+        lc = D.make_layer_cfg(dtype=cfg.dtype, b=cfg.b, s=cfg.s, h=cfg.h, H=cfg.H, d=cfg.d,
+                              L=cfg.L, E=cfg.E, k=cfg.k, f=cfg.f, r=cfg.r, ffn=cfg.ffn,
+                              normalize=cfg.normalize, proj_experts=cfg.proj_experts,
+                              rope_base=cfg.rope_base, rms_eps=cfg.rms_eps, rho=cfg.rho,
+                              mixture=D.MIXTURES[mix], branch_streams=mix == "parallel")
+        ws = torch.empty(D.layer_ws_bytes(lc), dtype=torch.uint8, device="cuda")
+        for _ in range(3):
+            D.dreamer_layer_forward(lc, G, x0, x_out=x_out, ws=ws)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            D.dreamer_layer_forward(lc, G, x0, x_out=x_out, ws=ws)
+        torch.cuda.synchronize()
+        out[mix] = {"ms_per_step": round((time.perf_counter() - t0) * 1e3 / steps, 4)}
+        del ws
+    for mix in out:
+        out[mix]["relative_throughput_vs_serial"] = round(
+            out["serial"]["ms_per_step"] / out[mix]["ms_per_step"] - 1.0, 4)
+        out[mix]["pages_relative_throughput"] = PAGES_RELATIVE[mix]
+    out["parallel"]["side_stream"] = True
+    return out
 
 
 def cpu_baseline(cfg):
@@ -208,6 +247,8 @@ def main():
         "roofline": roof,
         "kernel_ms_per_step": {c: round(per_class[c][1], 4) for c in CLASSES},
     }
+    if not args.no_mixtures:
+        line["mixtures"] = time_mixtures(D, cfg, G, x0, args.steps)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(line), flush=True)

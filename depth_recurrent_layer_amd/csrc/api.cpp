@@ -7,6 +7,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "../../include/dreamer.h"
@@ -83,6 +84,46 @@ void timing_end(int kclass, hipStream_t st) {
 
 #define TB(kc) timing_begin(kc, st)
 #define TE(kc) timing_end(kc, st)
+
+// ------------------------------------------------------------------------ side streams
+// Non-blocking side streams (default priority) and a fork/join event per device,
+// created on first use and kept until the process ends.  side_fork makes `side` wait for
+// the work queued on `st` so far; side_join makes `st` wait for the work queued on
+// `side`.  A call that forks holds `mu` while it enqueues, so concurrent calls on one
+// device never interleave their event records.
+namespace {
+struct SideStreams {
+  hipStream_t s[1];
+  hipEvent_t ev;
+  std::mutex mu;
+};
+std::mutex g_side_mu;
+SideStreams* g_side[64];
+
+SideStreams* side_streams() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  if (!g_side[dev]) {
+    SideStreams* ss = new SideStreams();
+    for (hipStream_t& x : ss->s)
+      if (hipStreamCreateWithFlags(&x, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&ss->ev, hipEventDisableTiming) != hipSuccess) return nullptr;
+    g_side[dev] = ss;
+  }
+  return g_side[dev];
+}
+
+void side_fork(SideStreams* ss, hipStream_t st, hipStream_t side) {
+  (void)hipEventRecord(ss->ev, st);
+  (void)hipStreamWaitEvent(side, ss->ev, 0);
+}
+
+void side_join(SideStreams* ss, hipStream_t st, hipStream_t side) {
+  (void)hipEventRecord(ss->ev, side);
+  (void)hipStreamWaitEvent(st, ss->ev, 0);
+}
+}  // namespace
 
 extern "C" {
 
@@ -505,7 +546,8 @@ static int validate_layer(const dreamer_layer_cfg* c, const dreamer_layer_weight
   if (c->b <= 0 || c->s <= 0 || c->h <= 0 || c->H <= 0 || c->d <= 0 || c->L <= 0 || c->r <= 0)
     return fail(DREAMER_E_INVAL, "layer: non-positive size");
   if ((int64_t)c->H * c->d != c->h) return fail(DREAMER_E_INVAL, "layer: h != H * d");
-  if (c->mixture != DREAMER_MIX_PARTIAL) return fail(DREAMER_E_UNSUPPORTED, "layer: mixture %d", c->mixture);
+  if (c->mixture < DREAMER_MIX_PARTIAL || c->mixture > DREAMER_MIX_PARALLEL)
+    return fail(DREAMER_E_INVAL, "layer: mixture %d", c->mixture);
   if (c->decode && (c->s != 1 || c->sa_pos <= 0 || c->sa_cap <= c->sa_pos))
     return fail(DREAMER_E_INVAL, "layer: decode needs s == 1, sa_pos > 0, sa_cap > sa_pos");
   if (!c->decode && c->sa_cap < 0) return fail(DREAMER_E_INVAL, "layer: bad sa_cap");
@@ -590,22 +632,26 @@ int dreamer_layer_forward(const dreamer_layer_cfg* cfg, const dreamer_layer_weig
   const float* resid = lw.xh32 ? lw.xh32 : (const float*)lw.xh;
   TE(DREAMER_KC_COMBINE);
 
-  const int nqkv = c.use_da ? 6 : 3;
+  const bool serial = c.mixture == DREAMER_MIX_SERIAL;
+  const bool parallel = c.mixture == DREAMER_MIX_PARALLEL;
+  // With branch_streams, the fully parallel wiring runs its EA chain on a side stream beside
+  // the attention (DA beside SA is not forked: at these sizes the cross-stream
+  // synchronisation costs more than the overlap gains).
+  SideStreams* ss = nullptr;
+  std::unique_lock<std::mutex> side_lock;
+  if (c.branch_streams && parallel && c.use_ea) {
+    ss = side_streams();
+    if (!ss) return fail(DREAMER_E_HIP, "layer: side streams unavailable");
+    side_lock = std::unique_lock<std::mutex>(ss->mu);  // the fork/join event is shared
+  }
+  hipStream_t sd_ea = ss ? ss->s[0] : st;
+  char* qkv = (char*)lw.qkv;
+  char* att = (char*)lw.att;
+
   for (int l = 0; l < L; ++l) {
     int32_t* pidx = nullptr;
     float* pgate = nullptr;
-    // ---- Q/K/V projections (dense, or the top-1 linear MoE sharing one router score)
-    GemmArgs gq;
-    gq.M = (int)T;
-    gq.N = nqkv * (int)h;
-    gq.K = (int)h;
-    gq.A = lw.xh;
-    gq.lda = h;
-    gq.B = w->w_qkv;
-    gq.ldb = h;
-    gq.C = lw.qkv;
-    gq.ldc = 6 * h;
-    if (c.proj_experts) {
+    if (c.proj_experts) {  // top-1 projection router shared by every Q/K/V/O projection
       const int Ep = c.proj_experts;
       pidx = proj_idx ? proj_idx + (int64_t)l * T : lw.pidx;
       pgate = proj_gate ? proj_gate + (int64_t)l * T : lw.pgate;
@@ -619,111 +665,158 @@ int dreamer_layer_forward(const dreamer_layer_cfg* cfg, const dreamer_layer_weig
                           st);
       TE(DREAMER_KC_PERMUTE);
       if (rc) return fail(DREAMER_E_UNSUPPORTED, "layer: projection permutation");
-      gq.b_gstride = 6 * h * h;
-      gq.rows = lw.pperm;
-      gq.row_scale = pgate;
-      gq.goff = lw.pgoff;
-      gq.toff = lw.ptoff;
-      gq.G = Ep;
-      gq.tile_m = 64;
     }
-    // q/k leave the projection rotated (SA by position, DA by depth) and rounded once
-    if (dt == DREAMER_BF16) {
-      gq.qkv_h = (int)h;
-      gq.seq = c.s;
-      gq.pos_fixed = c.decode ? (int)c.sa_pos : -1;
-      gq.sa_rope = c.sa_rope;
-      gq.depth_l = l;
-      gq.depth_L = L;
-      gq.cos_s = lw.cos_s;
-      gq.sin_s = lw.sin_s;
-      gq.cos_d = lw.cos_d;
-      gq.sin_d = lw.sin_d;
-      gq.vt = lw.vt;
-    }
-    TB(DREAMER_KC_GEMM);
-    rc = launch_gemm(gq, dt, 0, st);
-    TE(DREAMER_KC_GEMM);
-    if (rc) return fail(DREAMER_E_UNSUPPORTED, "layer: QKV projection shape");
-    if (dt == DREAMER_F32) {
-      rc = launch_qkv_rope(dt, T, c.H, c.d, c.s, c.decode ? (int)c.sa_pos : -1, c.sa_rope, l,
-                           L, lw.qkv, lw.cos_s, lw.sin_s, lw.cos_d, lw.sin_d, st);
-      if (rc) return fail(DREAMER_E_UNSUPPORTED, "layer: head dim for RoPE");
-    }
-    char* qkv = (char*)lw.qkv;
-    char* att = (char*)lw.att;
-    // ---- SA at depth l
-    void* sk = sa_k ? (char*)sa_k + (size_t)l * c.b * cap * h * es : nullptr;
-    void* sv = sa_v ? (char*)sa_v + (size_t)l * c.b * cap * h * es : nullptr;
-    TB(DREAMER_KC_SEQ_ATTN);
-    rc = launch_seq_attn(dt, c.b, c.s, c.H, c.d, pos0, qkv, 6 * h, qkv + h * es, 6 * h,
-                         qkv + 2 * h * es, 6 * h, lw.vt, sk, sv, cap, att, 2 * h, lw.cos_s,
-                         lw.sin_s, scale, 0, lw.sa_ws, lw.sa_ws_bytes, st);
-    TE(DREAMER_KC_SEQ_ATTN);
-    if (rc) return fail(DREAMER_E_UNSUPPORTED, "layer: sequence attention shape (%d)", rc);
-    // ---- DA over depths 0..l
-    if (c.use_da) {
-      TB(DREAMER_KC_DEPTH_ATTN);
-      rc = launch_depth_attn(dt, T, c.H, c.d, l, L, qkv + 3 * h * es, 6 * h, qkv + 4 * h * es,
-                             6 * h, qkv + 5 * h * es, 6 * h, DAk, DAv, att + h * es, 2 * h,
-                             lw.cos_d, lw.sin_d, scale, 0, st);
-      TE(DREAMER_KC_DEPTH_ATTN);
-      if (rc) return fail(DREAMER_E_UNSUPPORTED, "layer: depth attention shape");
-    }
-    // ---- y = xh + [a_SA | a_DA] W_o^T  (f32, plus the storage copy read by EA)
-    void* yb = y_steps ? (char*)y_steps + (size_t)l * T * h * es : lw.yb;
-    GemmArgs go;
-    go.M = (int)T;
-    go.N = (int)h;
-    go.K = c.use_da ? 2 * (int)h : (int)h;
-    go.A = att;
-    go.lda = 2 * h;
-    go.B = w->w_o;
-    go.ldb = 2 * h;
-    go.C = lw.y;
-    go.ldc = h;
-    go.resid = resid;
-    go.ldr = h;
-    go.C2 = yb;
-    go.ldc2 = h;
-    if (c.proj_experts) {
-      go.b_gstride = 2 * h * h;
-      go.rows = lw.pperm;
-      go.row_scale = pgate;
-      go.goff = lw.pgoff;
-      go.toff = lw.ptoff;
-      go.G = c.proj_experts;
-      go.tile_m = 64;
-    }
-    TB(DREAMER_KC_OUT_PROJ);
-    rc = launch_gemm(go, dt, 1, st);
-    TE(DREAMER_KC_OUT_PROJ);
-    if (rc) return fail(DREAMER_E_UNSUPPORTED, "layer: output projection shape");
-    // ---- EA on y, residual, next step's RMSNorm
     const bool last = l == L - 1;
-    float* xs = x_steps ? x_steps + (size_t)l * T * h : nullptr;
-    float* xo = last ? x_out : nullptr;
-    void* xh_next = last ? nullptr : lw.xh;
+    void* yb = y_steps ? (char*)y_steps + (size_t)l * T * h * es : lw.yb;
+    int32_t* ridx = nullptr;
+    float* rgate = nullptr;
     if (c.use_ea) {
-      int32_t* ridx = route_idx ? route_idx + (size_t)l * T * k : lw.ridx;
-      float* rgate = route_gate ? route_gate + (size_t)l * T * k : lw.rgate;
-      rc = route_impl(dt, T, c.h, c.r, c.E, k, l, L, yb, h, w->w_r, w->keys, w->bias, c.rho,
-                      c.normalize_gates, lw.cos_r, lw.sin_r, ridx, rgate, lw.u, lw.z, st,
-                      route_in ? route_in + (size_t)l * T * k : nullptr);
-      if (rc) return rc;
-      rc = ffn_slots(dt, c.ffn_kind, T, c.h, c.f, c.h, c.E, k, yb, ridx, rgate, w->w1, w->w3,
-                     w->w2, lw.ffn, st);
-      if (rc) return rc;
-      TB(DREAMER_KC_COMBINE);
-      launch_combine_norm(dt, T, c.h, k, lw.y, lw.ffn.slots, xo, xs, w->g, c.rms_eps, xh_next,
-                          last ? nullptr : lw.xh32, st);
-      TE(DREAMER_KC_COMBINE);
-    } else {
-      TB(DREAMER_KC_COMBINE);
-      launch_combine_norm(dt, T, c.h, 0, lw.y, nullptr, xo, xs, w->g, c.rms_eps, xh_next,
-                          last ? nullptr : lw.xh32, st);
-      TE(DREAMER_KC_COMBINE);
+      ridx = route_idx ? route_idx + (size_t)l * T * k : lw.ridx;
+      rgate = route_gate ? route_gate + (size_t)l * T * k : lw.rgate;
     }
+    // EA on `in` (storage dtype), leaving the gate-scaled expert outputs in the slots
+    auto ea = [&](const void* in, hipStream_t es_) -> int {
+      int r2 = route_impl(dt, T, c.h, c.r, c.E, k, l, L, in, h, w->w_r, w->keys, w->bias,
+                          c.rho, c.normalize_gates, lw.cos_r, lw.sin_r, ridx, rgate, lw.u,
+                          lw.z, es_, route_in ? route_in + (size_t)l * T * k : nullptr);
+      if (r2) return r2;
+      return ffn_slots(dt, c.ffn_kind, T, c.h, c.f, c.h, c.E, k, in, ridx, rgate, w->w1,
+                       w->w3, w->w2, lw.ffn, es_);
+    };
+    // Q/K/V projection of sections [sect0, sect0 + nsect) from `in` into qkv
+    auto project_qkv = [&](const void* in, int sect0, int nsect) -> int {
+      GemmArgs gq;
+      gq.M = (int)T;
+      gq.N = nsect * (int)h;
+      gq.K = (int)h;
+      gq.A = in;
+      gq.lda = h;
+      gq.B = (const char*)w->w_qkv + (size_t)sect0 * h * h * es;
+      gq.ldb = h;
+      gq.C = qkv + (size_t)sect0 * h * es;
+      gq.ldc = 6 * h;
+      if (c.proj_experts) {
+        gq.b_gstride = 6 * h * h;
+        gq.rows = lw.pperm;
+        gq.row_scale = pgate;
+        gq.goff = lw.pgoff;
+        gq.toff = lw.ptoff;
+        gq.G = c.proj_experts;
+        gq.tile_m = 64;
+      }
+      // q/k leave the projection rotated (SA by position, DA by depth) and rounded once
+      if (dt == DREAMER_BF16) {
+        gq.qkv_h = (int)h;
+        gq.qkv_sect0 = sect0;
+        gq.seq = c.s;
+        gq.pos_fixed = c.decode ? (int)c.sa_pos : -1;
+        gq.sa_rope = c.sa_rope;
+        gq.depth_l = l;
+        gq.depth_L = L;
+        gq.cos_s = lw.cos_s;
+        gq.sin_s = lw.sin_s;
+        gq.cos_d = lw.cos_d;
+        gq.sin_d = lw.sin_d;
+        gq.vt = lw.vt;
+      }
+      TB(DREAMER_KC_GEMM);
+      int r2 = launch_gemm(gq, dt, 0, st);
+      TE(DREAMER_KC_GEMM);
+      if (r2) return fail(DREAMER_E_UNSUPPORTED, "layer: QKV projection shape");
+      if (dt == DREAMER_F32) {  // rotates every section of the buffer in place
+        r2 = launch_qkv_rope(dt, T, c.H, c.d, c.s, c.decode ? (int)c.sa_pos : -1, c.sa_rope,
+                             l, L, lw.qkv, lw.cos_s, lw.sin_s, lw.cos_d, lw.sin_d, st);
+        if (r2) return fail(DREAMER_E_UNSUPPORTED, "layer: head dim for RoPE");
+      }
+      return ok();
+    };
+    auto run_sa = [&]() -> int {
+      void* sk = sa_k ? (char*)sa_k + (size_t)l * c.b * cap * h * es : nullptr;
+      void* sv = sa_v ? (char*)sa_v + (size_t)l * c.b * cap * h * es : nullptr;
+      TB(DREAMER_KC_SEQ_ATTN);
+      int r2 = launch_seq_attn(dt, c.b, c.s, c.H, c.d, pos0, qkv, 6 * h, qkv + h * es, 6 * h,
+                               qkv + 2 * h * es, 6 * h, lw.vt, sk, sv, cap, att, 2 * h,
+                               lw.cos_s, lw.sin_s, scale, 0, lw.sa_ws, lw.sa_ws_bytes, st);
+      TE(DREAMER_KC_SEQ_ATTN);
+      return r2 ? fail(DREAMER_E_UNSUPPORTED, "layer: sequence attention shape (%d)", r2)
+                : ok();
+    };
+    auto run_da = [&](hipStream_t s_) -> int {
+      timing_begin(DREAMER_KC_DEPTH_ATTN, s_);
+      int r2 = launch_depth_attn(dt, T, c.H, c.d, l, L, qkv + 3 * h * es, 6 * h,
+                                 qkv + 4 * h * es, 6 * h, qkv + 5 * h * es, 6 * h, DAk, DAv,
+                                 att + h * es, 2 * h, lw.cos_d, lw.sin_d, scale, 0, s_);
+      timing_end(DREAMER_KC_DEPTH_ATTN, s_);  // s_: the stream DA runs on
+      return r2 ? fail(DREAMER_E_UNSUPPORTED, "layer: depth attention shape") : ok();
+    };
+    // out = res + a W_o^T over attention columns [col0, col0 + K) (f32, plus a copy in
+    // storage dtype, C2)
+    auto project_o = [&](int col0, int K, const float* res, void* C2) -> int {
+      GemmArgs go;
+      go.M = (int)T;
+      go.N = (int)h;
+      go.K = K;
+      go.A = att + (size_t)col0 * es;
+      go.lda = 2 * h;
+      go.B = (const char*)w->w_o + (size_t)col0 * es;
+      go.ldb = 2 * h;
+      go.C = lw.y;
+      go.ldc = h;
+      go.resid = res;
+      go.ldr = h;
+      go.C2 = C2;
+      go.ldc2 = h;
+      if (c.proj_experts) {
+        go.b_gstride = 2 * h * h;
+        go.rows = lw.pperm;
+        go.row_scale = pgate;
+        go.goff = lw.pgoff;
+        go.toff = lw.ptoff;
+        go.G = c.proj_experts;
+        go.tile_m = 64;
+      }
+      TB(DREAMER_KC_OUT_PROJ);
+      int r2 = launch_gemm(go, dt, 1, st);
+      TE(DREAMER_KC_OUT_PROJ);
+      return r2 ? fail(DREAMER_E_UNSUPPORTED, "layer: output projection shape") : ok();
+    };
+
+    if (parallel && c.use_ea) {  // EA reads xh: it starts with the step
+      if (ss) side_fork(ss, st, sd_ea);
+      if ((rc = ea(lw.xh, sd_ea))) return rc;
+    }
+    if (serial) {
+      // u = xh + DA(xh) into y (f32) and its storage copy into xh; then v = u + SA(u)
+      const float* res = resid;
+      if (c.use_da) {
+        if ((rc = project_qkv(lw.xh, 3, 3)) || (rc = run_da(st)) ||
+            (rc = project_o((int)h, (int)h, resid, lw.xh)))
+          return rc;
+        res = lw.y;
+      }
+      if ((rc = project_qkv(lw.xh, 0, 3)) || (rc = run_sa()) ||
+          (rc = project_o(0, (int)h, res, yb)))
+        return rc;
+    } else {
+      // y = xh + [a_SA | a_DA] W_o^T
+      if ((rc = project_qkv(lw.xh, 0, c.use_da ? 6 : 3))) return rc;
+      if ((rc = run_sa())) return rc;
+      if (c.use_da && (rc = run_da(st))) return rc;
+      if ((rc = project_o(0, c.use_da ? 2 * (int)h : (int)h, resid, yb))) return rc;
+    }
+    if (c.use_ea) {
+      if (parallel) {
+        if (ss) side_join(ss, st, sd_ea);
+      }
+      else if ((rc = ea(yb, st))) return rc;
+    }
+    // x_{l+1} = y + sum of the slots; the next step's RMSNorm
+    float* xs = x_steps ? x_steps + (size_t)l * T * h : nullptr;
+    TB(DREAMER_KC_COMBINE);
+    launch_combine_norm(dt, T, c.h, c.use_ea ? k : 0, lw.y, c.use_ea ? lw.ffn.slots : nullptr,
+                        last ? x_out : nullptr, xs, w->g, c.rms_eps, last ? nullptr : lw.xh,
+                        last ? nullptr : lw.xh32, st);
+    TE(DREAMER_KC_COMBINE);
   }
   return check_launch("layer_forward");
 }

@@ -109,7 +109,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs a) {
   constexpr bool QKV = WN == 64 && sizeof(OutT) == 2;
   constexpr int CPR = WN / 8, NIT = WM * CPR / 64;  // generic epilogue items per lane
   const int rw0 = wm * WM, cw0 = n0 + wn * WN;      // this wave's first tile row, column
-  const int sect = a.qkv_h ? cw0 / a.qkv_h : -1;
+  const int sect = a.qkv_h ? a.qkv_sect0 + cw0 / a.qkv_h : -1;
   const bool sa_qk = QKV && a.qkv_h && (sect == 0 || sect == 1) && a.sa_rope;
   const bool da_qk = QKV && a.qkv_h && (sect == 3 || sect == 4);
   float pc[QKV ? TM : 1][4][2], ps[QKV ? TM : 1][4][2];

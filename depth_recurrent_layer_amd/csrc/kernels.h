@@ -34,6 +34,7 @@ struct GemmArgs {
   // (pairs < 16 at depth_l, the rest at depth_L-1-depth_l), before the bf16 rounding.
   // vt (optional): SA v also written transposed, [out_row / seq][head][64][seq].
   int qkv_h = 0;
+  int qkv_sect0 = 0;                 // section of output column 0 (3: a DA-only projection)
   int seq = 1;
   int pos_fixed = -1;
   int sa_rope = 0;

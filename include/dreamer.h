@@ -161,8 +161,21 @@ int dreamer_expert_ffn(int dtype, int kind, int64_t T, int h_in, int f, int h_ou
 int dreamer_absorb_shared(int dtype, int64_t n_experts, int64_t n, const void* w_e,
                           const void* w_shared, void* out, dreamer_stream_t stream);
 
-/* Mixture wirings of one depth step. */
-#define DREAMER_MIX_PARTIAL 0 /* y = x + DA(x) + SA(x);  x' = y + EA(y)   (default) */
+/* Mixture wirings of one depth step ([PN] ablation of the mixture's parallelism; the
+ * pages name the three wirings and their relative step throughput, not the formulas;
+ * these are the plainest readings with one RMSNorm per step, xh = RMSNorm(x_l) * g):
+ *   PARTIAL   y = xh + DA(xh) + SA(xh);       x' = y + EA(y)        (default)
+ *   SERIAL    u = xh + DA(xh);  v = u + SA(u);  x' = v + EA(v)     (DA -> SA -> EA)
+ *   PARALLEL  x' = xh + DA(xh) + SA(xh) + EA(xh)                   (all three at once)
+ * DA(.) / SA(.) include their halves of the output projection.  With branch_streams set,
+ * PARALLEL runs its EA chain (router, grouping, experts) concurrently with the attention
+ * on a side stream of the library (created once per device, default priority) forked
+ * from and joined back into the caller's stream; otherwise, and for the other wirings,
+ * everything runs in order on the caller's stream.  Results are the same bits either
+ * way.  Calls that fork on one device serialise their enqueueing on a host mutex. */
+#define DREAMER_MIX_PARTIAL 0
+#define DREAMER_MIX_SERIAL 1
+#define DREAMER_MIX_PARALLEL 2
 
 typedef struct dreamer_layer_cfg {
   int dtype;            /* DREAMER_F32 / DREAMER_BF16                                */
@@ -175,13 +188,14 @@ typedef struct dreamer_layer_cfg {
   int use_da, use_ea;   /* 0 disables depth attention / expert attention             */
   int sa_rope;          /* sequence RoPE on SA q and k                               */
   int proj_experts;     /* 0: dense Q/K/V/O; >0: top-1 linear MoE with this many experts */
-  int mixture;          /* DREAMER_MIX_PARTIAL                                       */
+  int mixture;          /* DREAMER_MIX_PARTIAL / _SERIAL / _PARALLEL                  */
   int decode;           /* 0: prefill of s tokens; 1: one new token per sequence      */
   int64_t sa_pos;       /* decode: position of the new token (positions 0..sa_pos-1 cached) */
   int64_t sa_cap;       /* SA cache capacity per sequence (decode: > sa_pos; prefill: >= s) */
   double rope_base;     /* rotary base (SA, DA and routers)                           */
   float rms_eps;        /* RMSNorm epsilon                                           */
   float rho;            /* router score scale                                        */
+  int branch_streams;   /* 1: PARALLEL's EA chain on a side stream (see above)          */
 } dreamer_layer_cfg;
 
 typedef struct dreamer_layer_weights {
@@ -209,6 +223,7 @@ typedef struct dreamer_layer_weights {
  *     a_SA = SA(xh) at depth l,  a_DA = DA(xh) over depths 0..l
  *     y = xh + [a_SA | a_DA] W_o^T
  *     x_{l+1} = y + sum_i gate_i FFN_{idx_i}(y)   (router on y)
+ *   (that is the PARTIAL wiring; SERIAL and PARALLEL as defined above)
  *   x_in  : [T, h] f32 (T = b*s; decode T = b)     x_out : [T, h] f32 = x_L
  *   route_idx, route_gate : [L, T, k] per-depth EA routing, or NULL
  *   proj_idx, proj_gate   : [L, T] per-depth projection routing (MoE), or NULL

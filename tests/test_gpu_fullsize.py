@@ -74,10 +74,11 @@ def compare_with_oracle(D, cfg, W, G, x0, ref, sa_cache_fn=None, sa_cap=0):
     assert agree >= 0.5
 
 
-def test_small_full_vs_oracle(gpu_lib):
+@pytest.mark.parametrize("mixture", ["partial", "serial", "parallel"])
+def test_small_full_vs_oracle(gpu_lib, mixture):
     D = gpu_lib
-    cfg = CONFIGS["small"]
-    print("full small workload", flush=True)
+    cfg = CONFIGS["small"].replace(mixture=mixture)
+    print(f"full small workload, {mixture} wiring", flush=True)
     W = make_weights(cfg, device="cuda")
     G = gpu_weights(D, cfg, W)
     x0 = make_x0(cfg, device="cuda")

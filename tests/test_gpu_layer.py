@@ -18,10 +18,11 @@ from synth.configs import make_sa_cache
 pytestmark = pytest.mark.gpu
 
 
-def run_gpu(D, cfg, W, x0, sa_cache=None, sa_cap=0, replay=None):
-    """replay: an oracle result whose expert choices the GPU adopts (route_in)."""
+def run_gpu(D, cfg, W, x0, sa_cache=None, sa_cap=0, replay=None, streams=False):
+    """replay: an oracle result whose expert choices the GPU adopts (route_in);
+    streams: independent branches on the library's side streams."""
     G = gpu_weights(D, cfg, W)
-    lc = lib_cfg(D, cfg, sa_cap=sa_cap)
+    lc = lib_cfg(D, cfg, sa_cap=sa_cap, streams=streams)
     T = cfg.T
     x = x0.reshape(T, cfg.h).float().cuda().contiguous()
     route = proj = None
@@ -182,10 +183,12 @@ def test_layer_deep_bf16_reduced(gpu_lib):
 
 # -------------------------------------------------------------------------------- decode
 
+@pytest.mark.parametrize("mixture", ["partial", "serial", "parallel"])
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_layer_decode_reduced(gpu_lib, dt):
-    cfg = CONFIGS["decode"].replace(dtype=dt, b=4, sa_pos=150, h=256, H=4, L=6, E=64)
-    print(f"layer decode {dt}", flush=True)
+def test_layer_decode_reduced(gpu_lib, dt, mixture):
+    cfg = CONFIGS["decode"].replace(dtype=dt, b=4, sa_pos=150, h=256, H=4, L=6, E=64,
+                                    mixture=mixture)
+    print(f"layer decode {dt} {mixture}", flush=True)
     W, x0 = make_weights(cfg), make_x0(cfg)
     cap = cfg.sa_pos + 1
     sk = torch.full((cfg.L, cfg.b, cap, cfg.H, cfg.d), float("nan"), dtype=cfg.torch_dtype)
@@ -235,3 +238,67 @@ def test_layer_repeatable(gpu_lib, s):
     # replaying a run's own expert choices reproduces it bit for bit
     c = run_gpu(gpu_lib, cfg, W, x0, replay=a)
     assert np.array_equal(a["x_out"], c["x_out"]) and np.array_equal(a["gate"], c["gate"])
+
+
+# ------------------------------------------------------------------- mixture wirings
+
+@pytest.mark.parametrize("variant", ["full", "no_da", "no_ea"])
+@pytest.mark.parametrize("mixture", ["serial", "parallel"])
+def test_layer_mixture_tiny_fp32(gpu_lib, mixture, variant):
+    base = CONFIGS["tiny"].replace(b=2, s=19, mixture=mixture)
+    cfg = {"full": base, "no_da": base.replace(use_da=False),
+           "no_ea": base.replace(use_ea=False)}[variant]
+    print(f"layer tiny f32 {mixture} {variant}", flush=True)
+    W, x0 = make_weights(cfg), make_x0(cfg)
+    gpu = run_gpu(gpu_lib, cfg, W, x0)
+    ref = run_ref(cfg, W, x0)
+    assert rel_err(gpu["x_out"], ref["x_out"]) <= 1e-5
+    if cfg.use_ea:
+        check_routing(cfg, W, gpu, ref, exact=True)
+
+
+@pytest.mark.parametrize("mixture", ["serial", "parallel"])
+def test_layer_mixture_small_shape_fp32(gpu_lib, mixture):
+    cfg = CONFIGS["small"].replace(dtype="f32", b=1, s=96, mixture=mixture)
+    print(f"layer small-shape f32 {mixture}", flush=True)
+    W, x0 = make_weights(cfg), make_x0(cfg)
+    gpu = run_gpu(gpu_lib, cfg, W, x0)
+    ref = run_ref(cfg, W, x0)
+    assert rel_err(gpu["x_out"], ref["x_out"]) <= 1e-5
+    check_routing(cfg, W, gpu, ref, exact=True)
+
+
+@pytest.mark.parametrize("s", [96, 520])
+@pytest.mark.parametrize("mixture", ["serial", "parallel"])
+def test_layer_mixture_small_bf16(gpu_lib, mixture, s):
+    cfg = CONFIGS["small"].replace(b=2, s=s, L=4 if s < 512 else 3, mixture=mixture)
+    print(f"layer small bf16 {mixture} s={s}", flush=True)
+    bf16_layer_checks(gpu_lib, cfg, make_weights(cfg), make_x0(cfg))
+
+
+@pytest.mark.parametrize("mixture", ["serial", "parallel"])
+def test_layer_mixture_linear_moe_bf16(gpu_lib, mixture):
+    cfg = CONFIGS["linear_moe"].replace(b=1, s=96, h=256, H=4, L=4, E=64, mixture=mixture)
+    print(f"layer linear-moe bf16 {mixture}", flush=True)
+    bf16_layer_checks(gpu_lib, cfg, make_weights(cfg), make_x0(cfg), free_tol=None)
+
+
+@pytest.mark.parametrize("mixture", ["serial", "parallel"])
+def test_layer_mixture_repeatable(gpu_lib, mixture):
+    """Concurrent branches on side streams still give the same bits every run."""
+    cfg = CONFIGS["small"].replace(b=2, s=520, L=3, mixture=mixture)
+    W, x0 = make_weights(cfg), make_x0(cfg)
+    a = run_gpu(gpu_lib, cfg, W, x0)
+    b = run_gpu(gpu_lib, cfg, W, x0)
+    assert np.array_equal(a["x_out"], b["x_out"]) and np.array_equal(a["idx"], b["idx"])
+
+
+@pytest.mark.parametrize("mixture", ["partial", "serial", "parallel"])
+def test_layer_branch_streams_same_bits(gpu_lib, mixture):
+    """Independent branches on side streams give the same bits as one stream."""
+    cfg = CONFIGS["small"].replace(b=2, s=520, L=3, mixture=mixture)
+    print(f"layer branch streams {mixture}", flush=True)
+    W, x0 = make_weights(cfg), make_x0(cfg)
+    a = run_gpu(gpu_lib, cfg, W, x0)
+    b = run_gpu(gpu_lib, cfg, W, x0, streams=True)
+    assert np.array_equal(a["x_out"], b["x_out"]) and np.array_equal(a["idx"], b["idx"])
