@@ -36,6 +36,8 @@ def parse():
     p.add_argument("--workload", default="small")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--kernel-class", default=None, help="time this class live (default: dominant)")
+    p.add_argument("--decode-tokens", type=int, default=8,
+                   help="decode workloads: tokens per step (one multi-token decode call)")
     p.add_argument("--no-mixtures", action="store_true",
                    help="skip timing the serial / partial / fully parallel wirings")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -73,26 +75,38 @@ def stored_traffic(kclass, workload):
     return blob["bytes_per_launch"]
 
 
-def algorithmic_work(cfg, counts_per_depth):
-    """Algorithmic bytes / flops per forward for each kernel class (what the method must
-    move or compute, not what the kernels happen to move)."""
+def algorithmic_work(cfg, counts_per_depth, reps=1):
+    """Algorithmic bytes / flops per step for each kernel class (what the method must move
+    or compute, not what the kernels happen to move).  Decode: a step is `reps` tokens,
+    token j attending over sa_pos + j + 1 cached positions."""
     es = 2 if cfg.dtype == "bf16" else 4
     T, h, L, k, f, r, E = cfg.T, cfg.h, cfg.L, cfg.k, cfg.f, cfg.r, cfg.E
     nq = 6 if cfg.use_da else 3
     w = {}
     w["qkv_proj"] = dict(bound="mfma", flops=L * 2 * T * h * nq * h, launches=L)
     w["out_proj"] = dict(bound="mfma", flops=L * 2 * T * (nq // 3) * h * h, launches=L)
-    w["seq_attn"] = dict(bound="mfma", flops=L * 4 * cfg.b * h * (cfg.s * (cfg.s + 1) // 2),
-                         launches=L)
+    if cfg.decode:  # every cached key and value of every depth read once per token
+        w["seq_attn"] = dict(bound="hbm", bytes=sum(L * cfg.b * (cfg.sa_pos + j + 1) * 2 * h * es
+                                                    for j in range(reps)), launches=L * reps)
+    else:
+        w["seq_attn"] = dict(bound="mfma", flops=L * 4 * cfg.b * h * (cfg.s * (cfg.s + 1) // 2),
+                             launches=L)
     da_bytes = sum(T * h * es * (6 + 2 * l) for l in range(L))
     w["depth_attn"] = dict(bound="hbm", bytes=da_bytes, launches=L)
-    touched = sum(int((c > 0).sum()) for c in counts_per_depth)
     nw = 3 if cfg.ffn == "swiglu" else 2
-    w["expert_ffn"] = dict(bound="hbm", bytes=touched * nw * h * f * es + L * 2 * T * k * h * es,
+    w["expert_ffn"] = dict(bound="hbm", bytes=L * 2 * T * k * h * es,
                            flops=L * 2 * T * k * nw * h * f, launches=L)
     w["combine"] = dict(bound="hbm", bytes=L * T * h * (k * es + 4 + es), launches=L + 1)
     w["route"] = dict(bound="alu", flops=L * 2 * T * (h * r + r * E), launches=L)
     w["permute"] = dict(bound="hbm", bytes=L * T * k * 12, launches=L)
+    for name, v in w.items():
+        if name != "seq_attn" or not cfg.decode:
+            for key in ("bytes", "flops", "launches"):
+                if key in v:
+                    v[key] *= reps
+    # expert weights: each (token pass, depth) reads the matrices of the experts it touches
+    touched = sum(int((c > 0).sum()) for c in counts_per_depth)
+    w["expert_ffn"]["bytes"] += touched * nw * h * f * es
     return w
 
 
@@ -180,36 +194,61 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
         return
+    reps = args.decode_tokens if cfg.decode else 1
     W = make_weights(cfg, device=dev)
     G = {k: v.contiguous() for k, v in W.items()}
     if cfg.proj_experts:
         G["w_qkv"] = D.dreamer_absorb_shared(G.pop("w_qkv_e"), G.pop("w_qkv_sh"))
         G["w_o"] = D.dreamer_absorb_shared(G.pop("w_o_e"), G.pop("w_o_sh"))
     x0 = make_x0(cfg, device=dev).reshape(cfg.T, cfg.h).contiguous()
+    cap = cfg.sa_pos + reps if cfg.decode else 0
     lc = D.make_layer_cfg(dtype=cfg.dtype, b=cfg.b, s=cfg.s, h=cfg.h, H=cfg.H, d=cfg.d, L=cfg.L,
                           E=cfg.E, k=cfg.k, f=cfg.f, r=cfg.r, ffn=cfg.ffn,
                           normalize=cfg.normalize, proj_experts=cfg.proj_experts,
+                          decode=cfg.decode, sa_pos=cfg.sa_pos, sa_cap=cap,
                           rope_base=cfg.rope_base, rms_eps=cfg.rms_eps, rho=cfg.rho)
-    ws = torch.empty(D.layer_ws_bytes(lc), dtype=torch.uint8, device=dev)
-    x_out = torch.empty((cfg.T, cfg.h), dtype=torch.float32, device=dev)
-    route = (torch.empty((cfg.L, cfg.T, cfg.k), dtype=torch.int32, device=dev),
-             torch.empty((cfg.L, cfg.T, cfg.k), dtype=torch.float32, device=dev))
+    if cfg.decode:
+        # SA caches [L, b, cap, H, d]: positions 0..sa_pos-1 seeded N(0, 1) (already
+        # rotated keys / values); every step appends its `reps` tokens after them
+        from synth.configs import make_sa_cache
+        sa = []
+        for which in ("k", "v"):
+            c = torch.empty((cfg.L, cfg.b, cap, cfg.H, cfg.d), dtype=cfg.torch_dtype, device=dev)
+            for l0 in range(cfg.L):
+                c[l0, :, :cfg.sa_pos] = make_sa_cache(cfg, which, dev, l0=l0, nl=1)[0]
+            sa.append(c)
+        xs = make_x0(cfg.replace(b=cfg.b * reps), device=dev).reshape(reps, cfg.b, cfg.h)
+        xs = xs.float().contiguous()
+        ws = torch.empty(D.decode_ws_bytes(lc, reps), dtype=torch.uint8, device=dev)
+        x_out = torch.empty_like(xs)
+        route = (torch.empty((reps, cfg.L, cfg.b, cfg.k), dtype=torch.int32, device=dev),
+                 torch.empty((reps, cfg.L, cfg.b, cfg.k), dtype=torch.float32, device=dev))
 
-    def step(with_route=False):
-        D.dreamer_layer_forward(lc, G, x0, x_out=x_out, ws=ws,
-                                route=route if with_route else None)
+        def step(with_route=False):
+            D.dreamer_decode_tokens(lc, G, xs, tuple(sa), x_out=x_out, ws=ws,
+                                    route=route if with_route else None)
+    else:
+        ws = torch.empty(D.layer_ws_bytes(lc), dtype=torch.uint8, device=dev)
+        x_out = torch.empty((cfg.T, cfg.h), dtype=torch.float32, device=dev)
+        route = (torch.empty((cfg.L, cfg.T, cfg.k), dtype=torch.int32, device=dev),
+                 torch.empty((cfg.L, cfg.T, cfg.k), dtype=torch.float32, device=dev))
+
+        def step(with_route=False):
+            D.dreamer_layer_forward(lc, G, x0, x_out=x_out, ws=ws,
+                                    route=route if with_route else None)
 
     step(with_route=True)
     torch.cuda.synchronize()
-    counts = [np.bincount(route[0][l].cpu().numpy().reshape(-1), minlength=cfg.E)
+    ridx = route[0].cpu().numpy().reshape(reps, cfg.L, -1)
+    counts = [np.bincount(ridx[j, l], minlength=cfg.E) for j in range(reps)
               for l in range(cfg.L)]
-    work = algorithmic_work(cfg, counts)
+    work = algorithmic_work(cfg, counts, reps)
     for _ in range(args.warmup):
         step()
     # dominant kernel class: one instrumented forward per class (untimed)
     per_class = {}
     for kc in CLASSES:
-        D.timing_enable(kc, 4 * cfg.L + 8)
+        D.timing_enable(kc, 4 * cfg.L * reps + 8)
         step()
         n, ms = D.timing_read()
         D.timing_disable()
@@ -229,7 +268,7 @@ def main():
     n_launch, dom_ms = D.timing_read()
     D.timing_disable()
     ms_per_step = elapsed * 1e3 / args.steps
-    value = cfg.T * cfg.L * args.steps / elapsed
+    value = cfg.T * cfg.L * reps * args.steps / elapsed
     roof = roofline_entry(work[dom], dom_ms / max(n_launch, 1))
     roof["traffic"] = stored_traffic(dom, cfg.name)
     roof["kernel"] = dom
@@ -242,14 +281,16 @@ def main():
         "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {cfg.dtype} Dreamer layer forward b={cfg.b} s={cfg.s} "
                                f"h={cfg.h} heads={cfg.H}x{cfg.d} L={cfg.L} E={cfg.E} top-{cfg.k} "
-                               f"{cfg.ffn} f={cfg.f} r={cfg.r}",
-                   "tokens": cfg.T, "depths": cfg.L, "parallelism": "single GPU"},
+                               f"{cfg.ffn} f={cfg.f} r={cfg.r}" +
+                               (f", decode of {reps} tokens per step after {cfg.sa_pos} cached "
+                                f"positions" if cfg.decode else ""),
+                   "tokens": cfg.T * reps, "depths": cfg.L, "parallelism": "single GPU"},
         "roofline": roof,
         "kernel_ms_per_step": {c: round(per_class[c][1], 4) for c in CLASSES},
     }
-    if not args.no_mixtures:
+    if not args.no_mixtures and not cfg.decode:
         line["mixtures"] = time_mixtures(D, cfg, G, x0, args.steps)
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not cfg.decode:
         line["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(line), flush=True)
 

@@ -589,30 +589,16 @@ size_t dreamer_layer_ws_bytes(const dreamer_layer_cfg* cfg) {
   return b.off + 256;
 }
 
-int dreamer_layer_forward(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* w,
-                          const float* x_in, float* x_out, int32_t* route_idx,
-                          float* route_gate, int32_t* proj_idx, float* proj_gate,
-                          float* x_steps, void* y_steps, void* da_k, void* da_v, void* sa_k,
-                          void* sa_v, const int32_t* route_in, const int32_t* proj_route_in,
-                          void* ws, size_t ws_bytes, dreamer_stream_t stream) {
-  int rc = validate_layer(cfg, w);
-  if (rc) return rc;
+// The L depth steps of one call on a planned workspace.  table_npos > 0: build the rotary
+// tables first (sequence table with table_npos positions); 0: they are already there.
+static int layer_run(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* w,
+                     const LayerWs& lw, int64_t table_npos, const float* x_in, float* x_out,
+                     int32_t* route_idx, float* route_gate, int32_t* proj_idx,
+                     float* proj_gate, float* x_steps, void* y_steps, void* da_k, void* da_v,
+                     void* sa_k, void* sa_v, const int32_t* route_in,
+                     const int32_t* proj_route_in, hipStream_t st) {
   const dreamer_layer_cfg& c = *cfg;
-  if (!x_in || !x_out) return fail(DREAMER_E_INVAL, "layer: null x_in / x_out");
-  if (c.decode && (!sa_k || !sa_v)) return fail(DREAMER_E_INVAL, "layer: decode needs sa_k / sa_v");
-  if ((da_k == nullptr) != (da_v == nullptr)) return fail(DREAMER_E_INVAL, "layer: da_k / da_v must both be given");
-  if ((sa_k == nullptr) != (sa_v == nullptr)) return fail(DREAMER_E_INVAL, "layer: sa_k / sa_v must both be given");
-  if ((route_idx == nullptr) != (route_gate == nullptr) ||
-      (proj_idx == nullptr) != (proj_gate == nullptr))
-    return fail(DREAMER_E_INVAL, "layer: routing outputs must come in (idx, gate) pairs");
-  if (sa_k && !c.decode && c.sa_cap < c.s) return fail(DREAMER_E_INVAL, "layer: sa_cap < s");
-  const size_t need = dreamer_layer_ws_bytes(cfg);
-  if (!ws || ws_bytes < need) return fail(DREAMER_E_WORKSPACE, "layer: workspace %zu < %zu", ws_bytes, need);
-
-  hipStream_t st = S(stream);
-  Bump b(ws);
-  LayerWs lw = plan_layer(b, cfg, y_steps == nullptr, route_idx == nullptr,
-                          proj_idx == nullptr, da_k == nullptr);
+  int rc = 0;
   const int dt = c.dtype;
   const size_t es = esize(dt);
   const int64_t T = (int64_t)c.b * c.s, h = c.h;
@@ -623,10 +609,12 @@ int dreamer_layer_forward(const dreamer_layer_cfg* cfg, const dreamer_layer_weig
   const int64_t cap = sa_k ? c.sa_cap : 0;
   const int64_t pos0 = c.decode ? c.sa_pos : 0;
 
-  launch_rope_tables(c.d, (int)sa_npos(cfg), c.rope_base, lw.cos_s, lw.sin_s, st);
-  launch_rope_tables(c.d, L, c.rope_base, lw.cos_d, lw.sin_d, st);
-  launch_rope_tables(c.r, L, c.rope_base, lw.cos_r, lw.sin_r, st);
-  if (c.proj_experts) launch_fill_i32((int32_t*)lw.zero_pbias, c.proj_experts, 0, st);
+  if (table_npos > 0) {  // rotary tables (and the zero projection bias), once per call
+    launch_rope_tables(c.d, (int)table_npos, c.rope_base, lw.cos_s, lw.sin_s, st);
+    launch_rope_tables(c.d, L, c.rope_base, lw.cos_d, lw.sin_d, st);
+    launch_rope_tables(c.r, L, c.rope_base, lw.cos_r, lw.sin_r, st);
+    if (c.proj_experts) launch_fill_i32((int32_t*)lw.zero_pbias, c.proj_experts, 0, st);
+  }
   TB(DREAMER_KC_COMBINE);
   launch_rmsnorm(dt, T, c.h, x_in, w->g, c.rms_eps, lw.xh, lw.xh32, st);
   const float* resid = lw.xh32 ? lw.xh32 : (const float*)lw.xh;
@@ -818,7 +806,84 @@ int dreamer_layer_forward(const dreamer_layer_cfg* cfg, const dreamer_layer_weig
                         last ? nullptr : lw.xh32, st);
     TE(DREAMER_KC_COMBINE);
   }
+  return ok();
+}
+
+int dreamer_layer_forward(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* w,
+                          const float* x_in, float* x_out, int32_t* route_idx,
+                          float* route_gate, int32_t* proj_idx, float* proj_gate,
+                          float* x_steps, void* y_steps, void* da_k, void* da_v, void* sa_k,
+                          void* sa_v, const int32_t* route_in, const int32_t* proj_route_in,
+                          void* ws, size_t ws_bytes, dreamer_stream_t stream) {
+  int rc = validate_layer(cfg, w);
+  if (rc) return rc;
+  const dreamer_layer_cfg& c = *cfg;
+  if (!x_in || !x_out) return fail(DREAMER_E_INVAL, "layer: null x_in / x_out");
+  if (c.decode && (!sa_k || !sa_v)) return fail(DREAMER_E_INVAL, "layer: decode needs sa_k / sa_v");
+  if ((da_k == nullptr) != (da_v == nullptr)) return fail(DREAMER_E_INVAL, "layer: da_k / da_v must both be given");
+  if ((sa_k == nullptr) != (sa_v == nullptr)) return fail(DREAMER_E_INVAL, "layer: sa_k / sa_v must both be given");
+  if ((route_idx == nullptr) != (route_gate == nullptr) ||
+      (proj_idx == nullptr) != (proj_gate == nullptr))
+    return fail(DREAMER_E_INVAL, "layer: routing outputs must come in (idx, gate) pairs");
+  if (sa_k && !c.decode && c.sa_cap < c.s) return fail(DREAMER_E_INVAL, "layer: sa_cap < s");
+  const size_t need = dreamer_layer_ws_bytes(cfg);
+  if (!ws || ws_bytes < need) return fail(DREAMER_E_WORKSPACE, "layer: workspace %zu < %zu", ws_bytes, need);
+
+  Bump b(ws);
+  LayerWs lw = plan_layer(b, cfg, y_steps == nullptr, route_idx == nullptr,
+                          proj_idx == nullptr, da_k == nullptr);
+  rc = layer_run(cfg, w, lw, sa_npos(cfg), x_in, x_out, route_idx, route_gate, proj_idx,
+                 proj_gate, x_steps, y_steps, da_k, da_v, sa_k, sa_v, route_in, proj_route_in,
+                 S(stream));
+  if (rc) return rc;
   return check_launch("layer_forward");
+}
+
+// Multi-token decode: n_tokens consecutive decode steps; token j sits at position
+// sa_pos + j, appends its keys / values to the SA caches and overwrites the DA slots.  The
+// workspace is planned for the last token's position (every buffer covers the earlier
+// ones) and the rotary tables are built once.
+static dreamer_layer_cfg last_token_cfg(const dreamer_layer_cfg* cfg, int n_tokens) {
+  dreamer_layer_cfg m = *cfg;
+  m.sa_pos = cfg->sa_pos + n_tokens - 1;
+  return m;
+}
+
+size_t dreamer_decode_ws_bytes(const dreamer_layer_cfg* cfg, int n_tokens) {
+  if (!cfg || n_tokens <= 0) return 0;
+  const dreamer_layer_cfg m = last_token_cfg(cfg, n_tokens);
+  return dreamer_layer_ws_bytes(&m);
+}
+
+int dreamer_decode_tokens(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* w,
+                          int n_tokens, const float* x_in, float* x_out, int32_t* route_idx,
+                          float* route_gate, void* da_k, void* da_v, void* sa_k, void* sa_v,
+                          void* ws, size_t ws_bytes, dreamer_stream_t stream) {
+  if (!cfg || n_tokens <= 0) return fail(DREAMER_E_INVAL, "decode_tokens: null cfg or n_tokens <= 0");
+  if (!cfg->decode) return fail(DREAMER_E_INVAL, "decode_tokens: cfg.decode must be 1");
+  const dreamer_layer_cfg m = last_token_cfg(cfg, n_tokens);
+  int rc = validate_layer(cfg, w);
+  if (rc) return rc;
+  if ((rc = validate_layer(&m, w))) return rc;  // sa_cap covers the last position
+  if (!x_in || !x_out || !sa_k || !sa_v) return fail(DREAMER_E_INVAL, "decode_tokens: null x_in / x_out / SA caches");
+  if ((da_k == nullptr) != (da_v == nullptr)) return fail(DREAMER_E_INVAL, "decode_tokens: da_k / da_v must both be given");
+  if ((route_idx == nullptr) != (route_gate == nullptr))
+    return fail(DREAMER_E_INVAL, "decode_tokens: route_idx / route_gate must both be given");
+  const size_t need = dreamer_decode_ws_bytes(cfg, n_tokens);
+  if (!ws || ws_bytes < need) return fail(DREAMER_E_WORKSPACE, "decode_tokens: workspace %zu < %zu", ws_bytes, need);
+  Bump b(ws);
+  LayerWs lw = plan_layer(b, &m, true, route_idx == nullptr, true, da_k == nullptr);
+  const int64_t bh = (int64_t)cfg->b * cfg->h, blk = (int64_t)cfg->L * cfg->b * cfg->k;
+  for (int j = 0; j < n_tokens; ++j) {
+    dreamer_layer_cfg cj = *cfg;
+    cj.sa_pos = cfg->sa_pos + j;
+    rc = layer_run(&cj, w, lw, j == 0 ? sa_npos(&m) : 0, x_in + j * bh, x_out + j * bh,
+                   route_idx ? route_idx + j * blk : nullptr,
+                   route_gate ? route_gate + j * blk : nullptr, nullptr, nullptr, nullptr,
+                   nullptr, da_k, da_v, sa_k, sa_v, nullptr, nullptr, S(stream));
+    if (rc) return rc;
+  }
+  return check_launch("decode_tokens");
 }
 
 }  // extern "C"

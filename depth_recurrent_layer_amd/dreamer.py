@@ -74,6 +74,9 @@ _sig("dreamer_layer_ws_bytes", _sz, [C.POINTER(LayerCfg)])
 _sig("dreamer_layer_forward", _i32, [C.POINTER(LayerCfg), C.POINTER(LayerWeights), _vp, _vp,
                                      _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                      _vp, _vp, _sz, _vp])
+_sig("dreamer_decode_ws_bytes", _sz, [C.POINTER(LayerCfg), _i32])
+_sig("dreamer_decode_tokens", _i32, [C.POINTER(LayerCfg), C.POINTER(LayerWeights), _i32, _vp,
+                                     _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp])
 _sig("dreamer_timing_enable", _i32, [_i32, _i32])
 _sig("dreamer_timing_read", _i32, [C.POINTER(_i32), C.POINTER(_f64)])
 _sig("dreamer_timing_disable", _i32, [])
@@ -83,7 +86,7 @@ EXPORTS = ["dreamer_last_error", "dreamer_version", "dreamer_rope_tables", "drea
            "dreamer_seq_attn_ws_bytes", "dreamer_seq_attn", "dreamer_expert_route_ws_bytes",
            "dreamer_expert_route", "dreamer_expert_ffn_ws_bytes", "dreamer_expert_ffn",
            "dreamer_absorb_shared", "dreamer_layer_ws_bytes", "dreamer_layer_forward",
-           "dreamer_timing_enable", "dreamer_timing_read", "dreamer_timing_disable"]
+           "dreamer_decode_ws_bytes", "dreamer_decode_tokens", "dreamer_timing_enable", "dreamer_timing_read", "dreamer_timing_disable"]
 
 
 class DreamerError(RuntimeError):
@@ -255,6 +258,31 @@ def dreamer_layer_forward(cfg: LayerCfg, weights: dict, x_in, *, x_out=None, rou
                                      _p(rg), _p(pi), _p(pg), _p(x_steps), _p(y_steps), _p(dk),
                                      _p(dv), _p(sk), _p(sv), _p(route_in), _p(proj_route_in),
                                      _p(ws), ws.numel(), _stream()))
+    return x_out
+
+
+def decode_ws_bytes(cfg: LayerCfg, n_tokens: int) -> int:
+    return int(lib.dreamer_decode_ws_bytes(C.byref(cfg), n_tokens))
+
+
+def dreamer_decode_tokens(cfg: LayerCfg, weights: dict, x_in, sa_cache, *, x_out=None,
+                          route=None, da_cache=None, ws=None):
+    """n decode steps: x_in [n, b, h] f32 (token j at position cfg.sa_pos + j),
+    sa_cache=(k, v) [L, b, cap, H, d] appended in place, route=(idx, gate)
+    [n, L, b, k], da_cache=(k, v) [b, L, H, d].  Returns x_out [n, b, h] f32."""
+    W = LayerWeights(**{n: (weights[n].data_ptr() if weights.get(n) is not None else None)
+                        for n, _ in LayerWeights._fields_})
+    _dev(x_in, *[v for v in weights.values() if torch.is_tensor(v)])
+    n = x_in.shape[0]
+    x_out = torch.empty_like(x_in, dtype=torch.float32) if x_out is None else x_out
+    if ws is None:
+        ws = _ws(decode_ws_bytes(cfg, n), x_in.device)
+    ri, rg = route if route is not None else (None, None)
+    dk, dv = da_cache if da_cache is not None else (None, None)
+    sk, sv = sa_cache
+    _check(lib.dreamer_decode_tokens(C.byref(cfg), C.byref(W), n, _p(x_in), _p(x_out), _p(ri),
+                                     _p(rg), _p(dk), _p(dv), _p(sk), _p(sv), _p(ws), ws.numel(),
+                                     _stream()))
     return x_out
 
 

@@ -253,6 +253,29 @@ int dreamer_layer_forward(const dreamer_layer_cfg* cfg, const dreamer_layer_weig
                           void* ws, size_t ws_bytes, dreamer_stream_t stream);
 
 /*
+ * Multi-token decode ([PN] inference: the SA key/value cache persists across tokens, one
+ * per depth; the DA cache is addressed only within one token's depth steps and the next
+ * token overwrites it): n_tokens consecutive decode steps of b sequences, token j at
+ * position cfg->sa_pos + j.  The same as n_tokens calls of dreamer_layer_forward with
+ * decode = 1 and sa_pos incremented (same bits); the rotary tables are built once.
+ *   cfg   : decode = 1, s = 1, sa_pos = P0 > 0 (positions 0..P0-1 cached),
+ *           sa_cap >= P0 + n_tokens
+ *   x_in  : [n_tokens, b, h] f32, token j of every sequence (its embedding; this layer
+ *           has no head, so the caller supplies the next inputs)
+ *   x_out : [n_tokens, b, h] f32, x_L of every token
+ *   route_idx, route_gate : [n_tokens, L, b, k] per-token EA routing, or NULL
+ *   da_k, da_v : [b, L, H, d] DA caches reused by every token, or NULL (kept in ws)
+ *   sa_k, sa_v : [L, b, sa_cap, H, d]; positions P0..P0+n_tokens-1 are appended
+ *   ws, ws_bytes : scratch of at least dreamer_decode_ws_bytes(cfg, n_tokens) bytes
+ * Errors as dreamer_layer_forward; a failure part-way leaves the earlier tokens done.
+ */
+size_t dreamer_decode_ws_bytes(const dreamer_layer_cfg* cfg, int n_tokens);
+int dreamer_decode_tokens(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* w,
+                          int n_tokens, const float* x_in, float* x_out, int32_t* route_idx,
+                          float* route_gate, void* da_k, void* da_v, void* sa_k, void* sa_v,
+                          void* ws, size_t ws_bytes, dreamer_stream_t stream);
+
+/*
  * Kernel timing, for measurement harnesses.  When enabled, every launch of the kernel
  * class `kclass` (DREAMER_KC_*) made by the library on a stream is bracketed by two HIP
  * events recorded on that stream; dreamer_timing_read returns the number of bracketed

@@ -439,3 +439,28 @@ def layer_forward(cfg, W, x0, sa_k=None, sa_v=None, force_idx=None, force_pidx=N
     if return_steps:
         out["steps"] = steps
     return out
+
+
+def decode_tokens(cfg, W, xs, sa_k, sa_v, return_steps=False):
+    """n consecutive decode steps ([PN] inference: SA keys / values persist across tokens
+    per depth, DA's cache lives only within one token's depth steps).  xs: [n, b, h]; token
+    j runs at position cfg.sa_pos + j with a fresh (NaN) DA cache and appends to
+    sa_k / sa_v [L, b, cap, H, d] in place.  Returns dict(x_out [n, b, h], idx [n, L, b, k],
+    gate, steps (optional))."""
+    xs = np.asarray(xs, np.float64)
+    outs, idxs, gates, steps = [], [], [], []
+    for j in range(xs.shape[0]):
+        cj = cfg.replace(sa_pos=cfg.sa_pos + j)
+        r = layer_forward(cj, W, xs[j], sa_k, sa_v, return_steps=return_steps)
+        outs.append(r["x_out"])
+        if cfg.use_ea:
+            idxs.append(r["idx"])
+            gates.append(r["gate"])
+        if return_steps:
+            steps.append(r["steps"])
+    out = dict(x_out=np.stack(outs))
+    if cfg.use_ea:
+        out["idx"], out["gate"] = np.stack(idxs), np.stack(gates)
+    if return_steps:
+        out["steps"] = steps
+    return out

@@ -302,3 +302,97 @@ def test_layer_branch_streams_same_bits(gpu_lib, mixture):
     a = run_gpu(gpu_lib, cfg, W, x0)
     b = run_gpu(gpu_lib, cfg, W, x0, streams=True)
     assert np.array_equal(a["x_out"], b["x_out"]) and np.array_equal(a["idx"], b["idx"])
+
+
+# ------------------------------------------------------------------ multi-token decode
+
+def _decode_setup(dt, n, s=40, b=3):
+    base = CONFIGS["decode"].replace(dtype=dt, h=256, H=4, L=4, E=32)
+    pre = base.replace(decode=False, b=b, s=s + n, sa_pos=0)
+    W, x0 = make_weights(pre), make_x0(pre)            # [b, s+n, h]
+    return base, pre, W, x0
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_decode_tokens_matches_oracle_loop(gpu_lib, dt):
+    """Prefill of s tokens on the GPU writes the SA caches; n decode steps in one call;
+    the oracle runs the same prefill and decode loop on its own caches."""
+    D = gpu_lib
+    n, s, b = 4, 40, 3
+    base, pre, W, x0 = _decode_setup(dt, n, s, b)
+    print(f"decode loop {dt} n={n}", flush=True)
+    short = pre.replace(s=s)
+    cap = s + n
+    tdt = short.torch_dtype
+    sk = torch.full((short.L, b, cap, short.H, short.d), float("nan"), dtype=tdt, device="cuda")
+    sv = torch.full_like(sk, float("nan"))
+    run_gpu(D, short, W, x0[:, :s].contiguous(), sa_cache=(sk, sv), sa_cap=cap)
+    dec = base.replace(b=b, s=1, decode=True, sa_pos=s)
+    G = gpu_weights(D, dec, W)
+    xs = x0[:, s:].transpose(0, 1).contiguous().float().cuda()   # [n, b, h]
+    route = (torch.empty((n, dec.L, b, dec.k), dtype=torch.int32, device="cuda"),
+             torch.empty((n, dec.L, b, dec.k), dtype=torch.float32, device="cuda"))
+    out = D.dreamer_decode_tokens(lib_cfg(D, dec, sa_cap=cap), G, xs, (sk, sv), route=route)
+    torch.cuda.synchronize()
+    assert torch.isfinite(sk).all() and torch.isfinite(sv).all()   # every position written
+    Wn = oracle.prepare_weights(W, big_as_f32=True)
+    rk = np.full((short.L, b, cap, short.H, short.d), np.nan)
+    rv = np.full_like(rk, np.nan)
+    oracle.layer_forward(short, Wn, x0[:, :s].numpy(), rk, rv)
+    ref = oracle.decode_tokens(dec, Wn, x0[:, s:].transpose(0, 1).numpy(), rk, rv,
+                               return_steps=True)
+    got = out.cpu().double().numpy()
+    if dt == "f32":
+        assert rel_err(got, ref["x_out"]) <= 1e-5
+        bias = W["bias"].float().numpy()
+        for j in range(n):
+            for l in range(dec.L):
+                n_bad, _ = routing_mismatch(route[0][j, l].cpu().numpy(),
+                                            ref["steps"][j][l]["z"], bias, dec.k)
+                assert n_bad == 0
+    else:
+        for j in range(n):
+            err = np.abs(rms_normed(got[j]) - rms_normed(ref["x_out"][j])).max()
+            assert err <= 2e-2, (j, err)
+
+
+def test_decode_tokens_same_bits_as_single_steps(gpu_lib):
+    D = gpu_lib
+    n, s, b = 3, 24, 2
+    base, pre, W, x0 = _decode_setup("bf16", n, s, b)
+    short = pre.replace(s=s)
+    cap = s + n
+    sk = torch.zeros((short.L, b, cap, short.H, short.d), dtype=torch.bfloat16, device="cuda")
+    sv = torch.zeros_like(sk)
+    run_gpu(D, short, W, x0[:, :s].contiguous(), sa_cache=(sk, sv), sa_cap=cap)
+    sk2, sv2 = sk.clone(), sv.clone()
+    dec = base.replace(b=b, s=1, decode=True, sa_pos=s)
+    G = gpu_weights(D, dec, W)
+    xs = x0[:, s:].transpose(0, 1).contiguous().float().cuda()
+    loop = D.dreamer_decode_tokens(lib_cfg(D, dec, sa_cap=cap), G, xs, (sk, sv))
+    steps = [D.dreamer_layer_forward(lib_cfg(D, dec.replace(sa_pos=s + j), sa_cap=cap), G,
+                                     xs[j].contiguous(), sa_cache=(sk2, sv2))
+             for j in range(n)]
+    torch.cuda.synchronize()
+    assert torch.equal(loop, torch.stack(steps))
+    assert torch.equal(sk, sk2) and torch.equal(sv, sv2)
+
+
+def test_prefill_then_decode_loop_matches_longer_prefill(gpu_lib):
+    D = gpu_lib
+    n, s, b = 5, 40, 3
+    base, pre, W, x0 = _decode_setup("bf16", n, s, b)
+    full = run_gpu(D, pre, W, x0)["x_out"].reshape(b, s + n, -1)
+    short = pre.replace(s=s)
+    cap = s + n
+    sk = torch.full((short.L, b, cap, short.H, short.d), float("nan"), dtype=torch.bfloat16,
+                    device="cuda")
+    sv = torch.full_like(sk, float("nan"))
+    run_gpu(D, short, W, x0[:, :s].contiguous(), sa_cache=(sk, sv), sa_cap=cap)
+    dec = base.replace(b=b, s=1, decode=True, sa_pos=s)
+    xs = x0[:, s:].transpose(0, 1).contiguous().float().cuda()
+    out = D.dreamer_decode_tokens(lib_cfg(D, dec, sa_cap=cap), gpu_weights(D, dec, W), xs,
+                                  (sk, sv)).cpu().double().numpy()
+    for j in range(n):
+        err = np.abs(rms_normed(out[j]) - rms_normed(full[:, s + j])).max()
+        assert err <= 2e-2, (j, err)

@@ -388,6 +388,30 @@ def test_prefill_then_decode_equals_longer_prefill(bf16):
     assert np.allclose(out, full[:, s], atol=3e-2 if bf16 else 1e-11)
 
 
+@pytest.mark.parametrize("bf16", [False, True])
+def test_decode_loop_equals_longer_prefill(bf16):
+    """Prefill of s tokens (writing the SA caches), then n decode steps = a prefill of
+    s + n tokens, token by token (causality), and one step = one decode call."""
+    base_cfg = CONFIGS["decode"].replace(h=64, H=4, d=16, L=3, E=16, k=2, f=16, r=16,
+                                         dtype="bf16" if bf16 else "f32")
+    s, n, b = 6, 4, 2
+    pre = base_cfg.replace(decode=False, b=b, s=s + n, sa_pos=0)
+    W = oracle.prepare_weights(make_weights(pre))
+    x0 = make_x0(pre).numpy()                      # [b, s+n, h]
+    full = oracle.layer_forward(pre, W, x0)["x_out"].reshape(b, s + n, -1)
+    cap = s + n
+    sk = np.full((pre.L, b, cap, pre.H, pre.d), np.nan)
+    sv = np.full_like(sk, np.nan)
+    oracle.layer_forward(pre.replace(s=s), W, x0[:, :s], sa_k=sk, sa_v=sv)
+    dec = base_cfg.replace(b=b, s=1, decode=True, sa_pos=s)
+    k0, v0 = sk.copy(), sv.copy()
+    got = oracle.decode_tokens(dec, W, x0[:, s:].transpose(1, 0, 2), sk, sv)["x_out"]
+    assert np.allclose(got.transpose(1, 0, 2), full[:, s:], atol=3e-2 if bf16 else 1e-11)
+    assert np.isfinite(sk[:, :, :cap]).all()       # every position appended
+    one = oracle.layer_forward(dec, W, x0[:, s], sa_k=k0, sa_v=v0)["x_out"]
+    assert np.array_equal(one, got[0])
+
+
 def test_decode_da_cache_overwritten_before_read():
     cfg = CONFIGS["decode"].replace(h=64, H=4, d=16, L=3, E=8, k=2, f=8, r=16, b=2, sa_pos=3,
                                     dtype="f32")
