@@ -214,6 +214,32 @@ def bias_update(bias, counts, lam):
     return np.asarray(bias, np.float64) + lam * np.sign(np.median(N) - N)
 
 
+def route_counts(idx, E):
+    """Selections per expert: idx [..., n] (the routing of one depth, or [L, T, k] for all
+    depths with the trailing dims flattened per leading index) -> counts [..., E]."""
+    idx = np.asarray(idx)
+    lead = idx.shape[:-2] if idx.ndim > 2 else ()
+    flat = idx.reshape(int(np.prod(lead)) if lead else 1, -1)
+    out = np.stack([np.bincount(r, minlength=E) for r in flat])
+    return out.reshape(*lead, E) if lead else out[0]
+
+
+def expert_usage(counts):
+    """Usage statistics of per-expert selection counts ([PN] analysis of expert usage:
+    unique experts per depth, Lorenz curve and Gini coefficient of the load).
+    counts [E] -> dict(distinct = #experts selected at least once, max_over_mean,
+    gini = sum_i sum_j |N_i - N_j| / (2 E^2 mean(N)) (the mean-difference definition),
+    lorenz = cumulative share of all selections held by the 1, 2, .., E least used
+    experts)."""
+    N = np.asarray(counts, np.float64)
+    E = N.size
+    mean = N.mean()
+    gini = np.abs(N[:, None] - N[None, :]).sum() / (2.0 * E * E * mean)
+    lorenz = np.cumsum(np.sort(N)) / N.sum()
+    return dict(distinct=int((N > 0).sum()), max_over_mean=float(N.max() / mean),
+                gini=float(gini), lorenz=lorenz)
+
+
 # ------------------------------------------------------------------------------ experts
 
 

@@ -270,10 +270,44 @@ def test_route_scores_closed_form_small_rank():
 
 
 def test_bias_update_zero_sum_sign():
-    N = np.array([5, 1, 9, 3, 4, 7, 2])   # distinct counts
+    # odd E: median 4 -> experts above it lose lam, below gain lam, the median one stays
+    N = np.array([5, 1, 9, 3, 4, 7, 2])
     b = oracle.bias_update(np.zeros(7), N, 0.1)
-    assert np.isclose(b.sum(), 0.0)  # odd E, distinct counts: as many above as below the median
-    assert np.allclose(b, 0.1 * np.sign(np.median(N) - N))
+    assert np.allclose(b, [-0.1, 0.1, -0.1, 0.1, 0.0, -0.1, 0.1], atol=1e-15)
+    assert np.isclose(b.sum(), 0.0)  # distinct counts: as many above as below the median
+    # even E: the median is the mean of the two middle counts (2.5 here)
+    b = oracle.bias_update(np.array([1.0, -1.0, 0.5, 0.0]), np.array([1, 2, 3, 10]), 0.25)
+    assert np.allclose(b, [1.25, -0.75, 0.25, -0.25], atol=1e-15)
+    # all loads equal: nothing moves
+    assert np.array_equal(oracle.bias_update(np.ones(5), np.full(5, 7), 0.3), np.ones(5))
+
+
+def test_usage_statistics_closed_forms():
+    u = oracle.expert_usage([0, 0, 1, 3])   # hand count: sum |Ni - Nj| = 20, E = 4, mean 1
+    assert np.isclose(u["gini"], 20 / 32) and u["distinct"] == 2 and u["max_over_mean"] == 3
+    assert np.allclose(u["lorenz"], [0, 0, 0.25, 1.0])
+    assert oracle.expert_usage(np.full(64, 5))["gini"] == 0.0         # perfectly even
+    one = np.zeros(50)
+    one[7] = 100
+    assert np.isclose(oracle.expert_usage(one)["gini"], 49 / 50)       # one expert holds all
+    # two other definitions agree on random loads: 1 - 2 * (area under the Lorenz curve,
+    # trapezoids from (0, 0)), and the sorted-rank form 2 sum i x_(i) / (E sum x) - (E+1)/E
+    r = np.random.default_rng(5)
+    N = r.integers(0, 300, size=257)
+    u = oracle.expert_usage(N)
+    E = N.size
+    Lz = np.concatenate([[0.0], u["lorenz"]])
+    area = np.sum((Lz[1:] + Lz[:-1]) / 2) / E
+    assert np.isclose(u["gini"], 1 - 2 * area, atol=1e-12)
+    xs = np.sort(N).astype(np.float64)
+    rank_form = 2 * np.sum(np.arange(1, E + 1) * xs) / (E * xs.sum()) - (E + 1) / E
+    assert np.isclose(u["gini"], rank_form, atol=1e-12)
+
+
+def test_route_counts_per_depth():
+    idx = np.array([[[0, 2], [2, 1]], [[3, 3], [0, 1]]])     # [L=2, T=2, k=2]
+    assert np.array_equal(oracle.route_counts(idx, 4), [[1, 1, 2, 0], [1, 1, 0, 2]])
+    assert np.array_equal(oracle.route_counts(idx[0], 4), [1, 1, 2, 0])
 
 
 # -------------------------------------------------------------------------------- experts
