@@ -159,6 +159,41 @@ def time_mixtures(D, cfg, G, x0, steps):
     return out
 
 
+def usage_report(D, cfg, G, x0, lc, route, iters=20, lam=0.01):
+    """Expert usage of the workload's routing (distinct experts and Gini per depth, global
+    Gini over all depths), then `iters` rounds of forward -> counts over all depths ->
+    b <- b + lam * sign(median(N) - N) on a copy of the bias, with the global Gini before
+    and after and the time of one counts + update round."""
+    import torch
+    E, L = cfg.E, cfg.L
+    per_depth = D.dreamer_route_counts(route[0].contiguous(), E, n_sets=L)
+    st = D.dreamer_expert_usage(per_depth).cpu()
+    glob = D.dreamer_expert_usage(per_depth.sum(0, keepdim=True).to(torch.int32).contiguous())
+    out = {"distinct_per_depth": [int(v) for v in st[:, 0]],
+           "gini_per_depth": [round(float(v), 4) for v in st[:, 2]],
+           "max_over_mean_per_depth": [round(float(v), 2) for v in st[:, 1]],
+           "global_gini": round(float(glob[0, 2]), 4),
+           "pages_global_gini": 0.075}
+    Gb = dict(G)
+    Gb["bias"] = G["bias"].clone()
+    x_out = torch.empty((cfg.T, cfg.h), dtype=torch.float32, device="cuda")
+    ginis, t_upd = [], []
+    for _ in range(iters):
+        D.dreamer_layer_forward(lc, Gb, x0, x_out=x_out, route=route)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        counts = D.dreamer_route_counts(route[0].contiguous(), E)
+        D.dreamer_bias_update(counts[0], Gb["bias"], lam)
+        torch.cuda.synchronize()
+        t_upd.append(time.perf_counter() - t0)
+        ginis.append(float(D.dreamer_expert_usage(counts)[0, 2]))
+    out["balancing"] = {"lambda": lam, "iterations": iters,
+                        "global_gini_first": round(ginis[0], 4),
+                        "global_gini_last": round(ginis[-1], 4),
+                        "counts_and_update_us": round(1e6 * sorted(t_upd)[len(t_upd) // 2], 1)}
+    return out
+
+
 def cpu_baseline(cfg):
     """The CPU oracle, as it stands, on the full workload (bounded: ~10 s here)."""
     import oracle
@@ -290,6 +325,8 @@ def main():
     }
     if not args.no_mixtures and not cfg.decode:
         line["mixtures"] = time_mixtures(D, cfg, G, x0, args.steps)
+    if not cfg.decode:
+        line["expert_usage"] = usage_report(D, cfg, G, x0, lc, route)
     if not args.no_cpu_baseline and not cfg.decode:
         line["cpu_baseline"] = cpu_baseline(cfg)
     print(json.dumps(line), flush=True)

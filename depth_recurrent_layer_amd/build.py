@@ -13,7 +13,8 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdreamer.so")
-SOURCES = ["gemm.hip", "attn.hip", "route.hip", "expert_ffn.hip", "moe.hip", "api.cpp"]
+SOURCES = ["gemm.hip", "attn.hip", "route.hip", "expert_ffn.hip", "moe.hip", "usage.hip",
+           "api.cpp"]
 ARCH = "gfx950"
 
 

@@ -839,6 +839,34 @@ int dreamer_layer_forward(const dreamer_layer_cfg* cfg, const dreamer_layer_weig
   return check_launch("layer_forward");
 }
 
+// ------------------------------------------------------------ expert-load bookkeeping
+int dreamer_route_counts(const int32_t* idx, int64_t n_sets, int64_t per_set, int E,
+                         int32_t* counts, dreamer_stream_t stream) {
+  if (n_sets <= 0 || per_set < 0 || E <= 0 || !counts || (per_set > 0 && !idx))
+    return fail(DREAMER_E_INVAL, "route_counts: bad arguments");
+  if (E > COUNT_MAX_E || n_sets > 65535)
+    return fail(DREAMER_E_UNSUPPORTED, "route_counts: E > %d or more than 65535 sets", COUNT_MAX_E);
+  if (launch_route_counts(idx, n_sets, per_set, E, counts, S(stream)))
+    return fail(DREAMER_E_UNSUPPORTED, "route_counts: unsupported shape");
+  return check_launch("route_counts");
+}
+
+int dreamer_bias_update(const int32_t* counts, int E, float lambda, float* bias,
+                        dreamer_stream_t stream) {
+  if (E <= 0 || !counts || !bias) return fail(DREAMER_E_INVAL, "bias_update: bad arguments");
+  launch_bias_update(counts, E, lambda, bias, S(stream));
+  return check_launch("bias_update");
+}
+
+int dreamer_expert_usage(const int32_t* counts, int64_t n_sets, int E, float* stats,
+                         dreamer_stream_t stream) {
+  if (n_sets <= 0 || E <= 0 || !counts || !stats)
+    return fail(DREAMER_E_INVAL, "expert_usage: bad arguments");
+  if (launch_expert_usage(counts, n_sets, E, stats, S(stream)))
+    return fail(DREAMER_E_UNSUPPORTED, "expert_usage: E > %d or more than 65535 sets", PERM_MAX_E);
+  return check_launch("expert_usage");
+}
+
 // Multi-token decode: n_tokens consecutive decode steps; token j sits at position
 // sa_pos + j, appends its keys / values to the SA caches and overwrites the DA slots.  The
 // workspace is planned for the last token's position (every buffer covers the earlier

@@ -103,6 +103,15 @@ int launch_permute(const int32_t* idx, int64_t nslots, int E, int tile_m, int32_
 int launch_counts(const int32_t* idx, int64_t nslots, int E, int32_t* hist, int32_t* counts,
                   hipStream_t st);
 
+// counts [n_sets, E] (zeroed here) of the expert ids idx [n_sets, per_set] (E <= COUNT_MAX_E).
+int launch_route_counts(const int32_t* idx, int64_t n_sets, int64_t per_set, int E,
+                        int32_t* counts, hipStream_t st);
+// bias[e] += lam * sign(median(counts) - counts[e]).
+void launch_bias_update(const int32_t* counts, int E, float lam, float* bias, hipStream_t st);
+// stats [n_sets, 3] = {distinct experts, max / mean, Gini} of counts [n_sets, E] (E <= PERM_MAX_E).
+int launch_expert_usage(const int32_t* counts, int64_t n_sets, int E, float* stats,
+                        hipStream_t st);
+
 // Fused expert FFN (GELU / SWIGLU): slots[s] = gate[s] * FFN_e(x[s / k]) for every
 // routed slot s, written in storage dtype [T*k, h_out].
 int launch_expert_ffn(int dtype, int kind, int64_t nslots, int k, int h_in, int f, int h_out,

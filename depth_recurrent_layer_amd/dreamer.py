@@ -74,6 +74,9 @@ _sig("dreamer_layer_ws_bytes", _sz, [C.POINTER(LayerCfg)])
 _sig("dreamer_layer_forward", _i32, [C.POINTER(LayerCfg), C.POINTER(LayerWeights), _vp, _vp,
                                      _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                      _vp, _vp, _sz, _vp])
+_sig("dreamer_route_counts", _i32, [_vp, _i64, _i64, _i32, _vp, _vp])
+_sig("dreamer_bias_update", _i32, [_vp, _i32, _f32, _vp, _vp])
+_sig("dreamer_expert_usage", _i32, [_vp, _i64, _i32, _vp, _vp])
 _sig("dreamer_decode_ws_bytes", _sz, [C.POINTER(LayerCfg), _i32])
 _sig("dreamer_decode_tokens", _i32, [C.POINTER(LayerCfg), C.POINTER(LayerWeights), _i32, _vp,
                                      _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp])
@@ -86,6 +89,7 @@ EXPORTS = ["dreamer_last_error", "dreamer_version", "dreamer_rope_tables", "drea
            "dreamer_seq_attn_ws_bytes", "dreamer_seq_attn", "dreamer_expert_route_ws_bytes",
            "dreamer_expert_route", "dreamer_expert_ffn_ws_bytes", "dreamer_expert_ffn",
            "dreamer_absorb_shared", "dreamer_layer_ws_bytes", "dreamer_layer_forward",
+           "dreamer_route_counts", "dreamer_bias_update", "dreamer_expert_usage",
            "dreamer_decode_ws_bytes", "dreamer_decode_tokens", "dreamer_timing_enable", "dreamer_timing_read", "dreamer_timing_disable"]
 
 
@@ -259,6 +263,34 @@ def dreamer_layer_forward(cfg: LayerCfg, weights: dict, x_in, *, x_out=None, rou
                                      _p(dv), _p(sk), _p(sv), _p(route_in), _p(proj_route_in),
                                      _p(ws), ws.numel(), _stream()))
     return x_out
+
+
+def dreamer_route_counts(idx, E: int, n_sets: int = 1):
+    """Selections per expert of int32 expert ids idx (n_sets equal sets, flattened):
+    returns counts [n_sets, E] int32."""
+    _dev(idx)
+    if idx.dtype != torch.int32 or not idx.is_contiguous():
+        raise TypeError("idx must be a contiguous int32 tensor")
+    counts = torch.empty((n_sets, E), dtype=torch.int32, device=idx.device)
+    _check(lib.dreamer_route_counts(_p(idx), n_sets, idx.numel() // n_sets, E, _p(counts),
+                                    _stream()))
+    return counts
+
+
+def dreamer_bias_update(counts, bias, lam: float):
+    """bias += lam * sign(median(counts) - counts), in place (counts [E] int32, bias [E] f32)."""
+    _dev(counts, bias)
+    _check(lib.dreamer_bias_update(_p(counts), bias.numel(), float(lam), _p(bias), _stream()))
+    return bias
+
+
+def dreamer_expert_usage(counts):
+    """counts [n_sets, E] int32 -> stats [n_sets, 3] f32 = (distinct, max/mean, Gini)."""
+    _dev(counts)
+    c = counts.reshape(-1, counts.shape[-1]).contiguous()
+    stats = torch.empty((c.shape[0], 3), dtype=torch.float32, device=c.device)
+    _check(lib.dreamer_expert_usage(_p(c), c.shape[0], c.shape[1], _p(stats), _stream()))
+    return stats
 
 
 def decode_ws_bytes(cfg: LayerCfg, n_tokens: int) -> int:

@@ -154,6 +154,29 @@ int dreamer_expert_ffn(int dtype, int kind, int64_t T, int h_in, int f, int h_ou
                        float* out, void* ws, size_t ws_bytes, dreamer_stream_t stream);
 
 /*
+ * Expert-load bookkeeping ([PN] "Key design 2": the router bias is nudged by the sign of
+ * the difference between the median usage count and each expert's count; [PN] analysis
+ * of expert usage: unique experts per depth, Lorenz curve and Gini coefficient).
+ *
+ * dreamer_route_counts: counts[s, e] = #{j : idx[s * per_set + j] == e} for every set s
+ *   (e.g. one set per depth of a [L, T, k] routing, per_set = T * k; or one set over all
+ *   depths).  idx entries must lie in [0, E) (others are clamped into it).
+ *   counts : [n_sets, E] int32 out (overwritten).  E <= 16384, n_sets <= 65535.
+ * dreamer_bias_update: bias[e] += lambda * sign(median(counts) - counts[e]), in place;
+ *   the median of an even count is the mean of the two middle values.  counts : [E].
+ * dreamer_expert_usage: stats[s] = {number of experts with count > 0, max / mean count,
+ *   Gini = sum_i sum_j |N_i - N_j| / (2 E^2 mean)} (0 for an all-zero set; the pair sum
+ *   is exact in 64-bit integers).  counts : [n_sets, E], stats : [n_sets, 3] f32.
+ *   E <= 8192, n_sets <= 65535.
+ */
+int dreamer_route_counts(const int32_t* idx, int64_t n_sets, int64_t per_set, int E,
+                         int32_t* counts, dreamer_stream_t stream);
+int dreamer_bias_update(const int32_t* counts, int E, float lambda, float* bias,
+                        dreamer_stream_t stream);
+int dreamer_expert_usage(const int32_t* counts, int64_t n_sets, int E, float* stats,
+                         dreamer_stream_t stream);
+
+/*
  * Offline absorption of the shared projection expert ([PN] "Key design 3"):
  *   out[e] = W_e + W_shared for e < n_experts; w_e/out: [n_experts, n], w_shared: [n].
  * bf16: out = bf16(float(W_e) + float(W_shared)).  out may alias w_e.

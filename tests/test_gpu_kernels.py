@@ -284,3 +284,67 @@ def test_errors_are_reported(gpu_lib):
         D.dreamer_depth_attn(q2, q2, q2, kc[..., :24].contiguous(), kc[..., :24].contiguous(),
                              0, 3, cos, sin)
     assert ei.value.code == D.E_UNSUPPORTED
+
+
+# ------------------------------------------------------------- expert-load bookkeeping
+
+def test_route_counts_match_oracle(gpu_lib):
+    D = gpu_lib
+    g = torch.Generator().manual_seed(3)
+    L, n, E = 3, 5000, 300
+    idx = torch.randint(0, E, (L, n), generator=g, dtype=torch.int32)
+    idx[1, :2000] = 7                                         # one hot expert
+    got = D.dreamer_route_counts(idx.cuda(), E, n_sets=L).cpu().numpy()
+    assert np.array_equal(got, oracle.route_counts(idx.numpy()[:, None, :], E))
+    one = D.dreamer_route_counts(idx.reshape(-1).cuda(), E).cpu().numpy()[0]
+    assert np.array_equal(one, np.bincount(idx.numpy().reshape(-1), minlength=E))
+
+
+@pytest.mark.parametrize("E", [257, 256, 4096])
+def test_bias_update_matches_oracle(gpu_lib, E):
+    D = gpu_lib
+    g = torch.Generator().manual_seed(E)
+    counts = torch.randint(0, 40, (E,), generator=g, dtype=torch.int32)   # many ties
+    bias = (torch.rand(E, generator=g) - 0.5) * 0.4
+    lam = 0.01
+    got = D.dreamer_bias_update(counts.cuda(), bias.clone().cuda(), lam).cpu().numpy()
+    sgn = np.sign(np.median(counts.numpy()) - counts.numpy())
+    want32 = (bias.numpy() + np.float32(lam) * sgn.astype(np.float32)).astype(np.float32)
+    assert np.array_equal(got, want32)                        # same float32 operations
+    ref = oracle.bias_update(bias.numpy().astype(np.float64), counts.numpy(), lam)
+    assert np.abs(got - ref).max() <= 1e-7
+
+
+def test_expert_usage_matches_oracle(gpu_lib):
+    D = gpu_lib
+    g = torch.Generator().manual_seed(9)
+    sets = [torch.randint(0, 50, (256,), generator=g), torch.zeros(256, dtype=torch.int64),
+            torch.full((256,), 4)]
+    sets[1][17] = 1000                                        # one expert holds everything
+    counts = torch.stack(sets).to(torch.int32)
+    got = D.dreamer_expert_usage(counts.cuda()).cpu().numpy()
+    for s in range(3):
+        ref = oracle.expert_usage(counts[s].numpy())
+        assert got[s, 0] == ref["distinct"]
+        assert abs(got[s, 1] - ref["max_over_mean"]) <= 1e-6 * ref["max_over_mean"]
+        assert abs(got[s, 2] - ref["gini"]) <= 1e-6 * max(ref["gini"], 1e-6)
+    assert got[2, 2] == 0.0
+
+
+def test_bias_balancing_reduces_imbalance(gpu_lib):
+    """Repeated b <- b + lam sign(median(N) - N) on a fixed batch evens the load out."""
+    D = gpu_lib
+    T, h, r, E, k = 2048, 256, 64, 64, 2
+    x = _t((T, h), 31, 0, 1.0, torch.bfloat16)
+    w_r = _t((r, h), 31, 1, 0.05, torch.bfloat16)
+    keys = _t((E, r), 31, 2, 0.3, torch.bfloat16)
+    bias = torch.zeros(E, device="cuda")
+    cos, sin = D.dreamer_rope_tables(r, 4)
+    ginis = []
+    for it in range(40):
+        idx, _, counts = D.dreamer_expert_route(x, w_r, keys, bias, k, 1, 4, cos, sin, 1.0, True)
+        ginis.append(float(D.dreamer_expert_usage(counts.reshape(1, E))[0, 2]))
+        D.dreamer_bias_update(counts, bias, 0.02)
+    torch.cuda.synchronize()
+    print(f"Gini {ginis[0]:.3f} -> {ginis[-1]:.3f}")
+    assert ginis[0] > 0.1 and min(ginis[-5:]) < 0.6 * ginis[0]

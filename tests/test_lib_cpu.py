@@ -91,3 +91,26 @@ def test_layer_ws_and_validation():
 
 def test_timing_enable_rejects_bad_class():
     assert D.lib.dreamer_timing_enable(99, 4) == D.E_INVAL
+
+
+def test_load_bookkeeping_validation():
+    p = C.c_void_p(16)
+    assert D.lib.dreamer_route_counts(p, 1, 10, 20000, p, None) == D.E_UNSUPPORTED
+    assert D.lib.dreamer_route_counts(None, 1, 10, 8, p, None) == D.E_INVAL
+    assert D.lib.dreamer_bias_update(None, 8, 0.1, p, None) == D.E_INVAL
+    assert D.lib.dreamer_expert_usage(p, 2, 9000, p, None) == D.E_UNSUPPORTED
+    assert D.lib.dreamer_expert_usage(p, 0, 8, p, None) == D.E_INVAL
+
+
+def test_decode_tokens_validation():
+    cfg = D.make_layer_cfg(dtype="bf16", b=4, s=1, h=256, H=4, d=64, L=2, E=32, k=2, f=64, r=64,
+                           decode=True, sa_pos=10, sa_cap=12)
+    W = D.LayerWeights()
+    # 3 tokens need positions 10..12: sa_cap 12 is too small
+    rc = D.lib.dreamer_decode_tokens(C.byref(cfg), C.byref(W), 3, None, None, None, None, None,
+                                     None, None, None, None, 0, None)
+    assert rc == D.E_INVAL
+    cfg.decode = 0
+    rc = D.lib.dreamer_decode_tokens(C.byref(cfg), C.byref(W), 1, None, None, None, None, None,
+                                     None, None, None, None, 0, None)
+    assert rc == D.E_INVAL and b"decode" in D.lib.dreamer_last_error()
