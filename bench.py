@@ -38,6 +38,7 @@ def parse():
     p.add_argument("--kernel-class", default=None, help="time this class live (default: dominant)")
     p.add_argument("--decode-tokens", type=int, default=8,
                    help="decode workloads: tokens per step (one multi-token decode call)")
+    p.add_argument("--no-usage", action="store_true", help="skip the expert-usage report")
     p.add_argument("--no-mixtures", action="store_true",
                    help="skip timing the serial / partial / fully parallel wirings")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -325,7 +326,7 @@ def main():
     }
     if not args.no_mixtures and not cfg.decode:
         line["mixtures"] = time_mixtures(D, cfg, G, x0, args.steps)
-    if not cfg.decode:
+    if not cfg.decode and not args.no_usage:
         line["expert_usage"] = usage_report(D, cfg, G, x0, lc, route)
     if not args.no_cpu_baseline and not cfg.decode:
         line["cpu_baseline"] = cpu_baseline(cfg)

@@ -343,6 +343,8 @@ int dreamer_expert_route(int dtype, int64_t T, int h, int r, int E, int k, int l
 // ------------------------------------------------------------------------ expert FFN
 struct FfnWs {
   int32_t *counts, *goff, *toff, *hist, *perm;
+  float* pgate;  // gates in expert-major order
+  int4* tiles;   // m-tile descriptors
   void* slots;
 };
 
@@ -353,6 +355,8 @@ static FfnWs plan_ffn(Bump& b, int dtype, int64_t T, int h_out, int E, int k) {
   w.toff = b.take_n<int32_t>(E + 1);
   w.hist = b.take_n<int32_t>((size_t)std::max(1, perm_blocks(T * k)) * E);
   w.perm = b.take_n<int32_t>((size_t)T * k);
+  w.pgate = b.take_n<float>((size_t)T * k);
+  w.tiles = b.take_n<int4>((size_t)tile_bound(T * k, E, FFN_TILE_M));
   w.slots = b.take((size_t)T * k * h_out * esize(dtype));
   return w;
 }
@@ -382,7 +386,7 @@ static int ffn_slots(int dtype, int kind, int64_t T, int h_in, int f, int h_out,
   }
   TB(DREAMER_KC_PERMUTE);
   int prc = launch_permute(idx, ns, E, FFN_TILE_M, w.hist, w.counts, w.goff, w.toff, w.perm,
-                           st);
+                           st, gate, w.pgate, w.tiles);
   TE(DREAMER_KC_PERMUTE);
   if (prc) return fail(DREAMER_E_UNSUPPORTED, "expert_ffn: E too large for the permutation");
   int rc;
@@ -410,8 +414,8 @@ static int ffn_slots(int dtype, int kind, int64_t T, int h_in, int f, int h_out,
     TE(DREAMER_KC_EXPERT_FFN);
   } else {
     TB(DREAMER_KC_EXPERT_FFN);
-    rc = launch_expert_ffn(dtype, kind, ns, k, h_in, f, h_out, E, x, gate, w1, w3, w2, w.perm,
-                           w.goff, w.toff, w.slots, st);
+    rc = launch_expert_ffn(dtype, kind, ns, k, h_in, f, h_out, E, x, w1, w3, w2, w.perm,
+                           w.pgate, w.tiles, w.toff, w.slots, st);
     TE(DREAMER_KC_EXPERT_FFN);
   }
   return rc ? fail(DREAMER_E_UNSUPPORTED, "expert_ffn: shape unsupported (f=%d h_in=%d h_out=%d)",

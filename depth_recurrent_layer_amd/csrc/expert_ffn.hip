@@ -8,8 +8,8 @@
 // XOR-swizzled by row (swz64), so the rows one MFMA fragment read touches fall into
 // distinct banks.  Wave w owns hidden columns
 // [w F/4, (w+1) F/4) of both projections, so the activation is lane-local.  The hidden
-// tile goes to LDS (bf16), GEMM2 (H W2^T) runs over 256-column chunks whose gate-scaled
-// bf16 results are staged in LDS and written per slot with 16-byte stores.
+// tile goes to LDS (bf16); GEMM2 runs transposed (W2 H^T) over 64-column chunks so every
+// lane holds 4 consecutive gate-scaled outputs of one slot and stores them directly.
 #include "common.h"
 #include "kernels.h"
 
@@ -27,17 +27,16 @@ struct FfnShape {
   static constexpr int HS_BYTES = 64 * LDH * 2;
   static constexpr int NS0 = (78 * 1024 - HS_BYTES) / STAGE;
   static constexpr int NS = NS0 > 8 ? 8 : NS0;             // ring depth (2 blocks / CU)
-  static constexpr int OUT_COLS = 256;                     // GEMM2 chunk
   static_assert(NI % 4 == 0, "stage must split evenly over 4 waves");
-  static_assert(NS >= 2 && NS * STAGE >= 64 * OUT_COLS * 2, "LDS ring too small");
+  static_assert(NS >= 2, "LDS ring too small");
 };
 
 template <int F, int KIND>
 __global__ __launch_bounds__(256, 2) void expert_ffn_kernel(
     int k, int h_in, int h_out, int E, const bf16* __restrict__ x,
-    const float* __restrict__ gate, const bf16* __restrict__ w1,
-    const bf16* __restrict__ w3, const bf16* __restrict__ w2, const int32_t* __restrict__ perm,
-    const int32_t* __restrict__ goff, const int32_t* __restrict__ toff,
+    const bf16* __restrict__ w1, const bf16* __restrict__ w3, const bf16* __restrict__ w2,
+    const int32_t* __restrict__ perm, const float* __restrict__ pgate,
+    const int4* __restrict__ tiles, const int32_t* __restrict__ ntiles,
     bf16* __restrict__ slots) {
   using S = FfnShape<F, KIND>;
   constexpr int NT1 = F / 64;  // 16-col tiles per wave per projection
@@ -47,21 +46,40 @@ __global__ __launch_bounds__(256, 2) void expert_ffn_kernel(
   __shared__ int s_slot[64];
   __shared__ float s_gate[64];
 
+  // tile descriptor and tile count in one round trip, then slot ids and gates (stored in
+  // expert-major order by the permutation) in another
   const int tile = blockIdx.x;
-  if (tile >= toff[E]) return;
-  int lo = 0, hi = E - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (toff[mid] <= tile) lo = mid; else hi = mid - 1;
-  }
-  const int e = lo;
-  const int r0 = goff[e] + (tile - toff[e]) * 64, r1 = goff[e + 1];
+  const int n_tiles = *ntiles;
+  const int4 td = tiles[tile];  // past the last tile: not used
+  if (tile >= n_tiles) return;
+  const int e = td.x, r0 = td.y, r1 = td.z;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
   if (tid < 64) {
     const int m = r0 + tid;
-    const int s = m < r1 ? perm[m] : -1;
-    s_slot[tid] = s;
-    s_gate[tid] = s >= 0 ? gate[s] : 0.f;
+    const bool in = m < r1;
+    s_slot[tid] = in ? perm[m] : -1;
+    s_gate[tid] = in ? pgate[m] : 0.f;
+  }
+  // GEMM2's first W2 fragments depend on the expert only: fetched now, used after GEMM1
+  constexpr bool PREFETCH = KS2 <= 2;  // register room for two chunks' fragments
+  const bf16* W2 = w2 + (int64_t)e * h_out * F;
+  auto load_w2 = [&](int nc, bf16x8 (&fr)[4][KS2]) {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < KS2; ++ks)
+        fr[nt][ks] = *reinterpret_cast<const bf16x8*>(
+            W2 + (int64_t)(nc + nt * 16 + lr) * F + ks * 32 + lg * 8);
+  };
+  bf16x8 wf[4][KS2];
+  if (PREFETCH && w * 64 < h_out) load_w2(w * 64, wf);
+  // the W2 fragments are taken through an empty asm statement: the compiler waits for
+  // them here, before the ring starts, instead of draining the ring at their first use
+  if constexpr (PREFETCH) {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < KS2; ++ks) asm volatile("" : "+v"(wf[nt][ks]));
   }
   __syncthreads();
 
@@ -152,70 +170,69 @@ __global__ __launch_bounds__(256, 2) void expert_ffn_kernel(
       hf[mt][ks] =
           *reinterpret_cast<const bf16x8*>(&Hs[(mt * 16 + lr) * S::LDH + ks * 32 + lg * 8]);
 
-  // GEMM2 over 256-column chunks; outputs staged in the (now idle) LDS ring
-  bf16* outst = reinterpret_cast<bf16*>(stg);  // [64][OUT_COLS]
-  const bf16* W2 = w2 + (int64_t)e * h_out * F;
-  for (int nc = 0; nc < h_out; nc += S::OUT_COLS) {
-    const int cbase = nc + w * 64;
-    if (cbase < h_out) {
-      floatx4 acc[4][4];
+  // GEMM2 transposed, O^T = W2 H^T: the A operand is W2's rows (output columns), the B
+  // operand the hidden rows, so a lane ends with 4 consecutive output columns of one slot,
+  // scaled by the slot's gate and stored as 8 bytes straight into the slot row.  Wave w
+  // takes the 64-column chunks w, w + 4, ...; the next chunk's W2 fragments are loaded
+  // while the current one is multiplied.
+  int sl[4];
+  float gs[4];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-      bf16x8 bfr[4][KS2];
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-        for (int ks = 0; ks < KS2; ++ks)
-          bfr[nt][ks] = *reinterpret_cast<const bf16x8*>(
-              W2 + (int64_t)(cbase + nt * 16 + lr) * F + ks * 32 + lg * 8);
+  for (int mt = 0; mt < 4; ++mt) {
+    sl[mt] = s_slot[mt * 16 + lr];
+    gs[mt] = s_gate[mt * 16 + lr];
+  }
+  for (int nc = w * 64; nc < h_out; nc += 256) {
+    bf16x8 cur[4][KS2];
+    if constexpr (PREFETCH) {
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int ks = 0; ks < KS2; ++ks)
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-            acc[mt][nt] = mfma16(hf[mt][ks], bfr[nt][ks], acc[mt][nt]);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = mt * 16 + lg * 4 + i;
-          const float gs = s_gate[row];
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt)
-            outst[row * S::OUT_COLS + w * 64 + nt * 16 + lr] = (bf16)(acc[mt][nt][i] * gs);
-        }
+        for (int ks = 0; ks < KS2; ++ks) cur[nt][ks] = wf[nt][ks];
+      if (nc + 256 < h_out) load_w2(nc + 256, wf);
+    } else {
+      load_w2(nc, cur);
     }
-    __syncthreads();
-    const int ncols = min(S::OUT_COLS, h_out - nc);
-    const int cpr = ncols / 8;
-    for (int c = tid; c < 64 * cpr; c += 256) {
-      const int row = c / cpr, cc = c % cpr;
-      const int s = s_slot[row];
-      if (s >= 0)
-        *reinterpret_cast<bf16x8*>(slots + (int64_t)s * h_out + nc + cc * 8) =
-            *reinterpret_cast<const bf16x8*>(&outst[row * S::OUT_COLS + cc * 8]);
+    floatx4 acc[4][4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) acc[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS2; ++ks)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          acc[nt][mt] = mfma16(cur[nt][ks], hf[mt][ks], acc[nt][mt]);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      if (sl[mt] < 0) continue;
+      bf16* orow = slots + (int64_t)sl[mt] * h_out + nc + lg * 4;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        bf16x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = (bf16)(acc[nt][mt][i] * gs[mt]);
+        *reinterpret_cast<bf16x4*>(orow + nt * 16) = v;
+      }
     }
-    __syncthreads();
   }
 }
 
 int launch_expert_ffn(int dtype, int kind, int64_t nslots, int k, int h_in, int f, int h_out,
-                      int E, const void* x, const float* gate, const void* w1,
-                      const void* w3, const void* w2, const int32_t* perm,
-                      const int32_t* goff, const int32_t* toff, void* slots,
-                      hipStream_t st) {
+                      int E, const void* x, const void* w1, const void* w3, const void* w2,
+                      const int32_t* perm, const float* pgate, const int4* tiles,
+                      const int32_t* toff, void* slots, hipStream_t st) {
   if (nslots <= 0) return 0;
   if (dtype == DT_F32) return -1;  // the f32 path uses launch_expert_ffn_f32
   if (h_in % 64 || h_out % 64) return -1;
   const unsigned grid = (unsigned)((nslots + FFN_TILE_M - 1) / FFN_TILE_M + E);
-#define EF_CASE(FF, KK)                                                                    \
-  expert_ffn_kernel<FF, KK><<<grid, 256, 0, st>>>(k, h_in, h_out, E, (const bf16*)x, gate, \
-                                                  (const bf16*)w1, (const bf16*)w3,        \
-                                                  (const bf16*)w2, perm, goff, toff,       \
-                                                  (bf16*)slots)
+#define EF_CASE(FF, KK)                                                                  \
+  expert_ffn_kernel<FF, KK><<<grid, 256, 0, st>>>(k, h_in, h_out, E, (const bf16*)x,     \
+                                                  (const bf16*)w1, (const bf16*)w3,      \
+                                                  (const bf16*)w2, perm, pgate, tiles,   \
+                                                  toff + E, (bf16*)slots)
   if (kind == FFN_SWIGLU && f == 64) EF_CASE(64, FFN_SWIGLU);
   else if (kind == FFN_SWIGLU && f == 128) EF_CASE(128, FFN_SWIGLU);
   else if (kind == FFN_GELU && f == 64) EF_CASE(64, FFN_GELU);

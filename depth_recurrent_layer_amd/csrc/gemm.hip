@@ -22,13 +22,17 @@ namespace dreamer {
 // 8 consecutive lanes of one MFMA fragment load cover all 32 banks.  2 x 2 waves, each
 // owning a WM x WN sub-tile (WM/16 x WN/16 MFMA tiles).  After the K loop every wave
 // stages its own sub-tile in LDS and writes whole rows with 16-byte stores.
+#ifndef DREAMER_GEMM_RING_BYTES
+#define DREAMER_GEMM_RING_BYTES 65536  // ring budget per block (two blocks per CU)
+#endif
+
 template <int WM, int WN>
 struct GemmShape {
   static constexpr int BM = 2 * WM, BN = 2 * WN, TM = WM / 16, TN = WN / 16;
   static constexpr int STAGE = (BM + BN) * 64;  // bytes per K slice
   static constexpr int NI = (BM + BN) / 16;     // 1 KiB load instructions per stage
   static constexpr int LPW = NI / 4;            // per wave
-  static constexpr int NS0 = 65536 / STAGE;
+  static constexpr int NS0 = DREAMER_GEMM_RING_BYTES / STAGE;
   static constexpr int NS = NS0 > 8 ? 8 : NS0;  // ring depth (two blocks per CU)
   // epilogue staging per wave: float32 rows of WN (+4), or bf16 rows of WN (+8)
   static constexpr int LDF = WN + 4, LDB = WN + 8;

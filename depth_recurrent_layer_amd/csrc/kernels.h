@@ -94,11 +94,16 @@ void launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st);
 // Permutation of routed slots by expert: hist [perm_blocks(nslots), E] scratch; outputs
 // counts [E], goff [E+1], toff [E+1] (tiles of tile_m rows), perm [nslots] (perm[goff[e]+j]
 // = slot id t*k+i of the j-th slot routed to e; order within an expert unspecified).
+// Optional: pgate [nslots] = gate in the same order (gate given), and tiles
+// [tile_bound(nslots, E, tile_m)] = {expert, first row, end of the expert's rows, 0} per
+// m-tile (the first toff[E] entries are written).
 constexpr int PERM_CHUNK = 2048, PERM_MAX_E = 8192, COUNT_MAX_E = 16384;
 int perm_blocks(int64_t nslots);
 int launch_permute(const int32_t* idx, int64_t nslots, int E, int tile_m, int32_t* hist,
                    int32_t* counts, int32_t* goff, int32_t* toff, int32_t* perm,
-                   hipStream_t st);
+                   hipStream_t st, const float* gate = nullptr, float* pgate = nullptr,
+                   int4* tiles = nullptr);
+inline int64_t tile_bound(int64_t nslots, int E, int tile_m) { return nslots / tile_m + E + 1; }
 // counts [E] of routed slots per expert (hist as above).
 int launch_counts(const int32_t* idx, int64_t nslots, int E, int32_t* hist, int32_t* counts,
                   hipStream_t st);
@@ -114,11 +119,11 @@ int launch_expert_usage(const int32_t* counts, int64_t n_sets, int E, float* sta
 
 // Fused expert FFN (GELU / SWIGLU): slots[s] = gate[s] * FFN_e(x[s / k]) for every
 // routed slot s, written in storage dtype [T*k, h_out].
+// perm / pgate / tiles / toff from launch_permute (tile_m = FFN_TILE_M).
 int launch_expert_ffn(int dtype, int kind, int64_t nslots, int k, int h_in, int f, int h_out,
-                      int E, const void* x, const float* gate, const void* w1,
-                      const void* w3, const void* w2, const int32_t* perm,
-                      const int32_t* goff, const int32_t* toff, void* slots,
-                      hipStream_t st);
+                      int E, const void* x, const void* w1, const void* w3, const void* w2,
+                      const int32_t* perm, const float* pgate, const int4* tiles,
+                      const int32_t* toff, void* slots, hipStream_t st);
 constexpr int FFN_TILE_M = 64;
 // float32 per-slot expert FFN (any kind, any f): slots[s] = gate[s] * FFN_idx[s](x[s/k]).
 int launch_expert_ffn_f32(int kind, int64_t nslots, int k, int h_in, int f, int h_out,

@@ -37,17 +37,24 @@ DEV void router_u_parts(int64_t Ttok, int64_t t0, int h, int r, int l, int L,
   const int p = i < half ? i : i - half;
   const int pos = p < quarter ? l : L - 1 - l;
   const float cv = cs[pos * half + p], sv = sn[pos * half + p];
-  // wave w owns rank columns 16 nt, nt = w, w + 4, ...
-  const int64_t tr = t0 + lr;
-  const bf16* xrow = tr < Ttok ? x + tr * ldx + lg * 8 : nullptr;
+  // wave w owns rank columns 16 nt, nt = w, w + 4, ...  Rows past the last token read
+  // the last token (their u is never used).  Loads go out in batches of 8 k-steps before
+  // their MFMAs, so a batch costs one memory round trip.
+  const int64_t tr = t0 + lr < Ttok ? t0 + lr : Ttok - 1;
+  const bf16* xrow = x + tr * ldx + lg * 8;
   for (int nt = w; nt < r / 16; nt += 4) {
     const bf16* wrow = w_r + (int64_t)(nt * 16 + lr) * h + lg * 8;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-    for (int k0 = 0; k0 < h; k0 += 32) {
-      const bf16x8 af = xrow ? *reinterpret_cast<const bf16x8*>(xrow + k0) : zero8;
-      const bf16x8 bf = *reinterpret_cast<const bf16x8*>(wrow + k0);
-      acc = mfma16(af, bf, acc);
+    for (int k0 = 0; k0 < h; k0 += 8 * 32) {
+      bf16x8 af[8], bf[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bool in = k0 + 32 * j < h;
+        af[j] = in ? *reinterpret_cast<const bf16x8*>(xrow + k0 + 32 * j) : zero8;
+        bf[j] = in ? *reinterpret_cast<const bf16x8*>(wrow + k0 + 32 * j) : zero8;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc = mfma16(af[j], bf[j], acc);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) us[(lg * 4 + i) * r + nt * 16 + lr] = acc[i];
@@ -460,7 +467,8 @@ __global__ __launch_bounds__(512) void perm_hist_kernel(const int32_t* __restric
 __global__ __launch_bounds__(512) void perm_scatter_kernel(
     const int32_t* __restrict__ idx, int64_t nslots, int E, int nb, int tile_m,
     const int32_t* __restrict__ hist, int32_t* __restrict__ counts, int32_t* __restrict__ goff,
-    int32_t* __restrict__ toff, int32_t* __restrict__ perm) {
+    int32_t* __restrict__ toff, int32_t* __restrict__ perm, const float* __restrict__ gate,
+    float* __restrict__ pgate, int4* __restrict__ tiles) {
   extern __shared__ int base[];  // [E]: totals, then this chunk's cursors
   __shared__ int s_rows[512], s_tiles[512];
   const int tid = threadIdx.x, nt = blockDim.x, b = blockIdx.x;
@@ -495,6 +503,8 @@ __global__ __launch_bounds__(512) void perm_scatter_kernel(
       counts[e] = tot;
       goff[e] = rr;
       toff[e] = tt;
+      if (tiles)  // one descriptor per m-tile: expert, first row, end of the expert's rows
+        for (int q = 0; q * tile_m < tot; ++q) tiles[tt + q] = make_int4(e, rr + q * tile_m, rr + tot, 0);
     }
     base[e] = rr + pre;
     rr += tot;
@@ -507,8 +517,11 @@ __global__ __launch_bounds__(512) void perm_scatter_kernel(
   __syncthreads();
   const int64_t s0 = (int64_t)b * PERM_CHUNK;
   const int64_t s1 = min(s0 + PERM_CHUNK, nslots);
-  for (int64_t s = s0 + tid; s < s1; s += nt)
-    perm[atomicAdd(&base[min(max(idx[s], 0), E - 1)], 1)] = (int32_t)s;
+  for (int64_t s = s0 + tid; s < s1; s += nt) {
+    const int pos = atomicAdd(&base[min(max(idx[s], 0), E - 1)], 1);
+    perm[pos] = (int32_t)s;
+    if (pgate) pgate[pos] = gate[s];
+  }
 }
 
 __global__ void hist_colsum_kernel(const int32_t* __restrict__ hist, int nb, int E,
@@ -522,13 +535,13 @@ __global__ void hist_colsum_kernel(const int32_t* __restrict__ hist, int nb, int
 
 int launch_permute(const int32_t* idx, int64_t nslots, int E, int tile_m, int32_t* hist,
                    int32_t* counts, int32_t* goff, int32_t* toff, int32_t* perm,
-                   hipStream_t st) {
+                   hipStream_t st, const float* gate, float* pgate, int4* tiles) {
   if (E <= 0 || E > PERM_MAX_E) return -1;
   const int nb = perm_blocks(nslots);
   const size_t lds = (size_t)E * sizeof(int);
   perm_hist_kernel<<<nb, 512, lds, st>>>(idx, nslots, E, hist);
   perm_scatter_kernel<<<nb, 512, lds, st>>>(idx, nslots, E, nb, tile_m, hist, counts, goff,
-                                            toff, perm);
+                                            toff, perm, gate, pgate, tiles);
   return 0;
 }
 
