@@ -478,6 +478,7 @@ int dreamer_absorb_shared(int dtype, int64_t n_experts, int64_t n, const void* w
 // ------------------------------------------------------------------------------ layer
 struct LayerWs {
   float *cos_s, *sin_s, *cos_d, *sin_d, *cos_r, *sin_r;
+  float4 *rope_s4, *rope_d4;  // interleaved head-dim-64 tables of the bf16 QKV epilogue
   void *xh, *qkv, *att, *yb;
   float* xh32;  // float32 copy of xhat for the residual (bf16 storage only)
   float *y, *u, *z, *rgate, *pgate, *zero_pbias;
@@ -497,12 +498,19 @@ static LayerWs plan_layer(Bump& b, const dreamer_layer_cfg* c, bool need_yb, boo
   const size_t es = esize(c->dtype);
   const int64_t h = c->h;
   const int64_t npos = sa_npos(c);
-  w.cos_s = b.take_n<float>(npos * (c->d / 2));
-  w.sin_s = b.take_n<float>(npos * (c->d / 2));
-  w.cos_d = b.take_n<float>((size_t)c->L * (c->d / 2));
-  w.sin_d = b.take_n<float>((size_t)c->L * (c->d / 2));
+  // rotary tables: the router's (depth, rank r); q / k rotate in the bf16 QKV epilogue
+  // (interleaved tables) or in a float32 pass (split tables)
   w.cos_r = b.take_n<float>((size_t)c->L * (c->r / 2));
   w.sin_r = b.take_n<float>((size_t)c->L * (c->r / 2));
+  if (c->dtype == DREAMER_BF16) {
+    w.rope_s4 = b.take_n<float4>(npos * 16);
+    w.rope_d4 = b.take_n<float4>((size_t)c->L * 16);
+  } else {
+    w.cos_s = b.take_n<float>(npos * (c->d / 2));
+    w.sin_s = b.take_n<float>(npos * (c->d / 2));
+    w.cos_d = b.take_n<float>((size_t)c->L * (c->d / 2));
+    w.sin_d = b.take_n<float>((size_t)c->L * (c->d / 2));
+  }
   w.xh = b.take(T * h * es);
   w.xh32 = c->dtype == DREAMER_BF16 ? b.take_n<float>(T * h) : nullptr;
   w.qkv = b.take(T * 6 * h * es);
@@ -614,9 +622,17 @@ static int layer_run(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* 
   const int64_t pos0 = c.decode ? c.sa_pos : 0;
 
   if (table_npos > 0) {  // rotary tables (and the zero projection bias), once per call
-    launch_rope_tables(c.d, (int)table_npos, c.rope_base, lw.cos_s, lw.sin_s, st);
-    launch_rope_tables(c.d, L, c.rope_base, lw.cos_d, lw.sin_d, st);
-    launch_rope_tables(c.r, L, c.rope_base, lw.cos_r, lw.sin_r, st);
+    RopeJobs jobs;
+    jobs.base = c.rope_base;
+    jobs.add_split(c.r, L, lw.cos_r, lw.sin_r);
+    if (lw.rope_s4) {
+      jobs.add_t4((int)table_npos, lw.rope_s4);
+      jobs.add_t4(L, lw.rope_d4);
+    } else {
+      jobs.add_split(c.d, (int)table_npos, lw.cos_s, lw.sin_s);
+      jobs.add_split(c.d, L, lw.cos_d, lw.sin_d);
+    }
+    launch_rope_jobs(jobs, st);
     if (c.proj_experts) launch_fill_i32((int32_t*)lw.zero_pbias, c.proj_experts, 0, st);
   }
   TB(DREAMER_KC_COMBINE);
@@ -705,10 +721,8 @@ static int layer_run(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* 
         gq.sa_rope = c.sa_rope;
         gq.depth_l = l;
         gq.depth_L = L;
-        gq.cos_s = lw.cos_s;
-        gq.sin_s = lw.sin_s;
-        gq.cos_d = lw.cos_d;
-        gq.sin_d = lw.sin_d;
+        gq.rope_s4 = lw.rope_s4;
+        gq.rope_d4 = lw.rope_d4;
         gq.vt = lw.vt;
       }
       TB(DREAMER_KC_GEMM);

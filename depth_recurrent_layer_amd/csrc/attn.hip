@@ -9,21 +9,48 @@
 namespace dreamer {
 
 // ------------------------------------------------------------------------- RoPE tables
-__global__ void rope_table_kernel(int D, int npos, double base, float* c, float* s) {
-  const int half = D / 2;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)npos * half) return;
-  const int p = (int)(i / half), j = (int)(i % half);
-  const double theta = pow(base, -2.0 * (double)j / (double)D);
-  const double ang = (double)p * theta;
-  c[i] = (float)cos(ang);
-  s[i] = (float)sin(ang);
+// Split tables of head dim D: c[p * D/2 + j] = cos(p th_j), s[...] = sin(p th_j), with
+// th_j = base^(-2j/D), evaluated in float64 and rounded once.
+// Interleaved tables of head dim 64 (the QKV epilogue's): t[p * 16 + j] =
+// (cos p th_j, cos p th_{j+16}, sin p th_j, sin p th_{j+16}), the same values.
+// One launch fills every table of a RopeJobs set: thread i walks the jobs in order.
+__global__ void rope_jobs_kernel(RopeJobs jobs) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (int q = 0; q < jobs.n; ++q) {
+    const RopeJob& jb = jobs.j[q];
+    const int per = jb.t4 ? 16 : jb.D / 2;
+    const int64_t n = (int64_t)jb.npos * per;
+    if (i >= n) {
+      i -= n;
+      continue;
+    }
+    const int p = (int)(i / per), j = (int)(i % per);
+    if (jb.t4) {
+      const double a0 = (double)p * pow(jobs.base, -2.0 * (double)j / 64.0);
+      const double a1 = (double)p * pow(jobs.base, -2.0 * (double)(j + 16) / 64.0);
+      jb.t4[i] = make_float4((float)cos(a0), (float)cos(a1), (float)sin(a0), (float)sin(a1));
+    } else {
+      const double ang = (double)p * pow(jobs.base, -2.0 * (double)j / (double)jb.D);
+      jb.c[i] = (float)cos(ang);
+      jb.s[i] = (float)sin(ang);
+    }
+    return;
+  }
+}
+
+void launch_rope_jobs(const RopeJobs& jobs, hipStream_t st) {
+  int64_t n = 0;
+  for (int q = 0; q < jobs.n; ++q)
+    n += (int64_t)jobs.j[q].npos * (jobs.j[q].t4 ? 16 : jobs.j[q].D / 2);
+  if (n <= 0) return;
+  rope_jobs_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(jobs);
 }
 
 void launch_rope_tables(int D, int npos, double base, float* c, float* s, hipStream_t st) {
-  const int64_t n = (int64_t)npos * (D / 2);
-  if (n <= 0) return;
-  rope_table_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(D, npos, base, c, s);
+  RopeJobs jobs;
+  jobs.base = base;
+  jobs.add_split(D, npos, c, s);
+  launch_rope_jobs(jobs, st);
 }
 
 // Rotate one 16-byte chunk in place.  The lane holds dims [c*VEC, c*VEC+VEC) of a head

@@ -159,7 +159,7 @@ DEV uint32_t lds_off(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-// N 16-byte LDS reads (N = 2, 4, 6 or 8) completed within one statement.  Ring stages
+// N 16-byte LDS reads (N = 2, 4, 6, 8 or 12) completed within one statement.  Ring stages
 // filled by direct global->LDS loads are read this way: for a plain LDS read the
 // compiler cannot tell that it misses the stages still in flight and would wait for
 // every outstanding load first.  The reads are complete when the statement ends, so no
@@ -167,7 +167,7 @@ DEV uint32_t lds_off(const void* p) {
 // visible before).
 template <int N>
 DEV void lds_read_b128(bf16x8 (&x)[N], const uint32_t (&a)[N]) {
-  static_assert(N == 2 || N == 4 || N == 6 || N == 8, "2, 4, 6 or 8 reads");
+  static_assert(N == 2 || N == 4 || N == 6 || N == 8 || N == 12, "2, 4, 6, 8 or 12 reads");
   if constexpr (N == 2) {
     asm volatile(
         "ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
@@ -188,6 +188,18 @@ DEV void lds_read_b128(bf16x8 (&x)[N], const uint32_t (&a)[N]) {
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5])
         : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5])
+        : "memory");
+  } else if constexpr (N == 12) {
+    asm volatile(
+        "ds_read_b128 %0, %12\n\tds_read_b128 %1, %13\n\tds_read_b128 %2, %14\n\t"
+        "ds_read_b128 %3, %15\n\tds_read_b128 %4, %16\n\tds_read_b128 %5, %17\n\t"
+        "ds_read_b128 %6, %18\n\tds_read_b128 %7, %19\n\tds_read_b128 %8, %20\n\t"
+        "ds_read_b128 %9, %21\n\tds_read_b128 %10, %22\n\tds_read_b128 %11, %23\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+          "=&v"(x[6]), "=&v"(x[7]), "=&v"(x[8]), "=&v"(x[9]), "=&v"(x[10]), "=&v"(x[11])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+          "v"(a[7]), "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11])
         : "memory");
   } else {
     asm volatile(

@@ -26,24 +26,29 @@ namespace dreamer {
 #define DREAMER_GEMM_RING_BYTES 65536  // ring budget per block (two blocks per CU)
 #endif
 
-template <int WM, int WN>
+// QKVONLY: an instance for the Q/K/V projection only (bf16 output, QKV epilogue), whose
+// epilogue staging is bf16 and therefore smaller.  RING: LDS budget of the K ring; OCC:
+// blocks per CU the instance is built for.
+template <int WM, int WN, bool QKVONLY, int RING>
 struct GemmShape {
   static constexpr int BM = 2 * WM, BN = 2 * WN, TM = WM / 16, TN = WN / 16;
   static constexpr int STAGE = (BM + BN) * 64;  // bytes per K slice
   static constexpr int NI = (BM + BN) / 16;     // 1 KiB load instructions per stage
   static constexpr int LPW = NI / 4;            // per wave
-  static constexpr int NS0 = DREAMER_GEMM_RING_BYTES / STAGE;
-  static constexpr int NS = NS0 > 8 ? 8 : NS0;  // ring depth (two blocks per CU)
+  static constexpr int NS0 = RING / STAGE;
+  static constexpr int NS = NS0 > 8 ? 8 : NS0;  // ring depth
   // epilogue staging per wave: float32 rows of WN (+4), or bf16 rows of WN (+8)
   static constexpr int LDF = WN + 4, LDB = WN + 8;
-  static constexpr int WAVE_STAGE = WM * LDF * 4;
+  static constexpr int WAVE_STAGE = QKVONLY ? WM * LDB * 2 : WM * LDF * 4;
   static constexpr int SMEM = NS * STAGE > 4 * WAVE_STAGE ? NS * STAGE : 4 * WAVE_STAGE;
   static_assert(NI % 4 == 0, "stage must split evenly over 4 waves");
+  static_assert(NS >= 2, "ring too small");
 };
 
-template <typename OutT, int WM, int WN>
-__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs a) {
-  using S = GemmShape<WM, WN>;
+template <typename OutT, int WM, int WN, bool QKVONLY = false,
+          int RING = DREAMER_GEMM_RING_BYTES, int OCC = 2>
+__global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(GemmArgs a) {
+  using S = GemmShape<WM, WN, QKVONLY, RING>;
   constexpr int BM = S::BM, BN = S::BN, TM = S::TM, TN = S::TN;
   __shared__ __attribute__((aligned(1024))) char ring[S::SMEM];
   __shared__ int rows_s[BM];
@@ -116,26 +121,27 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs a) {
   const int sect = a.qkv_h ? a.qkv_sect0 + cw0 / a.qkv_h : -1;
   const bool sa_qk = QKV && a.qkv_h && (sect == 0 || sect == 1) && a.sa_rope;
   const bool da_qk = QKV && a.qkv_h && (sect == 3 || sect == 4);
-  float pc[QKV ? TM : 1][4][2], ps[QKV ? TM : 1][4][2];
+  // Rotary table entries (interleaved RopeJobs t4 layout, one 16-byte load gives a lane the
+  // cos / sin of both its pairs lr and lr + 16): the sequence rotation per row position;
+  // the depth rotation at l for pairs < 16 and at L-1-l for the others.  They are loaded
+  // after the ring's first stages (so stage 0 does not wait for them) when registers allow,
+  // else in the epilogue.
+  auto row_pos = [&](int i, int v) {
+    const int orow = rows_s[rw0 + i * 16 + lg * 4 + v];
+    return a.pos_fixed >= 0 ? a.pos_fixed : (orow >= 0 ? orow % a.seq : 0);
+  };
+  constexpr bool PRE_TAB = QKV && TM * OCC <= 8;  // register room for the row entries
+  float4 tq[PRE_TAB ? TM : 1][4];
+  float4 td0 = {}, td1 = {};
+  int n_tab = 0;  // table loads issued behind the ring's first stages
+  auto load_seq_tables = [&](float4 (&t)[PRE_TAB ? TM : 1][4]) {
+#pragma unroll
+    for (int i = 0; i < (PRE_TAB ? TM : 1); ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) t[i][v] = a.rope_s4[row_pos(i, v) * 16 + lr];
+  };
   float rres[QKV ? 1 : NIT][8];
   if constexpr (QKV) {
-    if (sa_qk || da_qk) {
-      const float* ct = sa_qk ? a.cos_s : a.cos_d;
-      const float* st = sa_qk ? a.sin_s : a.sin_d;
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int orow = rows_s[rw0 + i * 16 + lg * 4 + v];
-          const int spos = a.pos_fixed >= 0 ? a.pos_fixed : (orow >= 0 ? orow % a.seq : 0);
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {  // depth: pairs < 16 at l, the others at L-1-l
-            const int pos = sa_qk ? spos : (j == 0 ? a.depth_l : a.depth_L - 1 - a.depth_l);
-            pc[i][v][j] = ct[pos * 32 + j * 16 + lr];
-            ps[i][v][j] = st[pos * 32 + j * 16 + lr];
-          }
-        }
-    }
   } else {
     if (a.resid) {
 #pragma unroll
@@ -153,9 +159,20 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs a) {
   const int nst = a.K / 32;
   const uint32_t ring0 = lds_off(ring);
   for (int s = 0; s < S::NS - 1 && s < nst; ++s) issue(s);
+  if constexpr (QKV) {
+    if (da_qk) {
+      td0 = a.rope_d4[a.depth_l * 16 + lr];
+      td1 = a.rope_d4[(a.depth_L - 1 - a.depth_l) * 16 + lr];
+      n_tab = 2;
+    } else if (PRE_TAB && sa_qk) {
+      load_seq_tables(tq);
+      n_tab = TM * 4;
+    }
+  }
   for (int s = 0; s < nst; ++s) {
-    // stage s has landed once only the later stages' loads are outstanding
-    wait_vmcnt_upto(S::LPW * min(S::NS - 2, nst - 1 - s));
+    // stage s has landed once only the loads issued after it are outstanding: the later
+    // stages', and the table loads while s is one of the stages issued before them
+    wait_vmcnt_upto(S::LPW * min(S::NS - 2, nst - 1 - s) + (s <= S::NS - 2 ? n_tab : 0));
     ring_barrier();  // stage s visible to every wave; stage s - 1 consumed by every wave
     if (s + S::NS - 1 < nst) issue(s + S::NS - 1);
     const uint32_t sb = ring0 + (s % S::NS) * S::STAGE;
@@ -181,7 +198,13 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs a) {
       const int hcol0 = cw0 % a.qkv_h;
       bf16* sw = reinterpret_cast<bf16*>(wst);  // [WM][LDB]
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i) {
+        float4 ti[4];  // this m-tile's sequence-rotation entries, one per row
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          if constexpr (PRE_TAB) ti[v] = tq[i][v];
+          else if (sa_qk) ti[v] = a.rope_s4[row_pos(i, v) * 16 + lr];
+        }
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int rt = i * 16 + lg * 4 + v;  // row within the wave
@@ -192,7 +215,15 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs a) {
             const int pair = j * 16 + lr;
             float x = acc[i][j][v] * sc, y = acc[i][j + 2][v] * sc;
             if (sa_qk || da_qk) {
-              const float cv = pc[i][v][j], sv = ps[i][v][j];
+              float cv, sv;
+              if (sa_qk) {
+                const float4 t = ti[v];
+                cv = j == 0 ? t.x : t.y;
+                sv = j == 0 ? t.z : t.w;
+              } else {
+                cv = j == 0 ? td0.x : td1.y;
+                sv = j == 0 ? td0.z : td1.w;
+              }
               const float xr = x * cv - y * sv;
               y = y * cv + x * sv;
               x = xr;
@@ -201,6 +232,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs a) {
             sw[rt * S::LDB + pair + 32] = (bf16)y;
           }
         }
+      }
       wave_lds_sync();
       // rows of 64 bf16 = 8 chunks of 16 bytes
       for (int it = lane; it < WM * 8; it += 64) {
@@ -237,6 +269,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs a) {
       return;
     }
   }
+  if constexpr (QKVONLY) return;
   // generic: v = acc * row_scale + resid; C (OutT) and optional bf16 copy C2
   float* sf = reinterpret_cast<float*>(wst);  // [WM][LDF]
 #pragma unroll
@@ -318,7 +351,7 @@ int launch_gemm(const GemmArgs& a, int dtype, int out_f32, hipStream_t st) {
   // 64-row m-tiles their tile offsets were built with.
   int bm, bn;
   if (a.qkv_h) {
-    if (a.qkv_h % 128 || out_f32) return -1;
+    if (a.qkv_h % 128 || out_f32 || !a.rope_d4 || (a.sa_rope && !a.rope_s4)) return -1;
     bn = 128;
   } else {
     bn = a.N >= 128 ? 128 : 64;
@@ -337,6 +370,19 @@ int launch_gemm(const GemmArgs& a, int dtype, int out_f32, hipStream_t st) {
   }
   const int mt = (a.M + bm - 1) / bm + (a.toff ? a.G : 0);
   dim3 grid(mt, (a.N + bn - 1) / bn);
+  // QKV projections with the rotary epilogue: 256 x 128 tiles at two blocks per CU once
+  // they fill the chip, else 128 x 128 tiles at three per CU (one round for up to 768
+  // tiles); small M keeps the 64 x 128 tiles chosen above.
+  if (a.qkv_h && !a.toff && tiles(256, 128) >= 512) {
+    dim3 g2((a.M + 255) / 256, (a.N + 127) / 128);
+    gemm_bf16_kernel<bf16, 128, 64, true, 73728, 2><<<g2, 256, 0, st>>>(a);
+    return 0;
+  }
+  if (a.qkv_h && !a.toff && tiles(128, 128) >= 256) {
+    dim3 g3((a.M + 127) / 128, (a.N + 127) / 128);
+    gemm_bf16_kernel<bf16, 64, 64, true, 49152, 3><<<g3, 256, 0, st>>>(a);
+    return 0;
+  }
 #define DREAMER_GEMM_LAUNCH(OUT)                                                  \
   if (bm == 128) gemm_bf16_kernel<OUT, 64, 64><<<grid, 256, 0, st>>>(a);          \
   else if (bn == 128) gemm_bf16_kernel<OUT, 32, 64><<<grid, 256, 0, st>>>(a);     \

@@ -39,7 +39,8 @@ struct GemmArgs {
   int pos_fixed = -1;
   int sa_rope = 0;
   int depth_l = 0, depth_L = 1;
-  const float *cos_s = nullptr, *sin_s = nullptr, *cos_d = nullptr, *sin_d = nullptr;
+  const float4* rope_s4 = nullptr;  // interleaved rotary tables (RopeJobs t4): sequence positions,
+  const float4* rope_d4 = nullptr;  // and depths 0..depth_L-1
   void* vt = nullptr;
 };
 
@@ -48,6 +49,22 @@ int launch_gemm(const GemmArgs& a, int dtype, int out_f32, hipStream_t st);
 
 // RoPE tables in float64 math: cos/sin [npos, D/2].
 void launch_rope_tables(int D, int npos, double base, float* c, float* s, hipStream_t st);
+// The same values for D = 64, interleaved [npos][16] float4 (cos j, cos j+16, sin j, sin j+16).
+// Rotary tables built in one launch (up to four): split cos / sin tables of head dim D, or
+// (t4 set) the interleaved head-dim-64 table of the QKV epilogue.
+struct RopeJob {
+  int D = 0, npos = 0;
+  float *c = nullptr, *s = nullptr;
+  float4* t4 = nullptr;
+};
+struct RopeJobs {
+  RopeJob j[4];
+  int n = 0;
+  double base = 10000.0;
+  void add_split(int D, int npos, float* c, float* s) { j[n++] = RopeJob{D, npos, c, s, nullptr}; }
+  void add_t4(int npos, float4* t) { j[n++] = RopeJob{64, npos, nullptr, nullptr, t}; }
+};
+void launch_rope_jobs(const RopeJobs& jobs, hipStream_t st);
 
 // Depth attention (row strides in elements for q/k/v/out; cache contiguous [rows,L,H,d]).
 // rope: rotate q and k_new by depth here (else they arrive rotated and rounded).
