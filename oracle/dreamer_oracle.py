@@ -14,7 +14,8 @@ Attention Mixtures: Giving Latent Reasoning the Attention it Deserves"):
           depth RoPE with half the dims reversed, the parallel-residual equation),
           "Key design 2" (expert attention, the gate equation, the bias update),
           "Key design 3" (linear-MoE projections, the shared-expert identity),
-          "Loss / training" (RMSNorm on the residual stream), ablation table.
+          "Loss / training" (RMSNorm on the residual stream), ablation table,
+          "Limitations and outlook" (windowed / dilated depth attention as future work).
   [GS-de] gist.science German technical summary, section "Methodik: Dreamer-Framework".
   [GS-nl] gist.science Dutch technical summary, section "Methodologie: Dreamer Framework".
 
@@ -149,15 +150,27 @@ def seq_attn(q, k_new, v_new, pos0=0, k_cache=None, v_cache=None, sa_rope=True,
 # ----------------------------------------------------------------------- depth attention
 
 
+def depth_keys(l, window=0, dilation=0):
+    """Depth slots read by DA at depth l (R26: the local-window plus dilated sparse depth
+    attention that [PN] "Limitations and outlook" proposes as future work).  window 0: every depth 0..l.  window
+    w > 0: the w most recent depths l-w+1..l, plus, when dilation D > 0, every older depth
+    j with (l - j) divisible by D.  The current depth is always read."""
+    if window <= 0:
+        return np.arange(l + 1)
+    return np.array([j for j in range(l + 1)
+                     if l - j < window or (dilation > 0 and (l - j) % dilation == 0)])
+
+
 def depth_attn(q, k_new, v_new, k_cache, v_cache, l, L, base=10000.0, bf16=False,
-               use_rope=True):
+               use_rope=True, window=0, dilation=0):
     """Depth attention DA at depth l ([PN] "Key design 1"; [GS-de]/[GS-nl] DA bullets).
 
     Each of the R rows (tokens, b*s flattened) attends over its own keys at depths
     0..l (R1: inclusive of the current depth), with depth RoPE (half reversed, R4) on
     q and on the new key.  The rotated new key and the value are written into slot l
     of k_cache/v_cache ([R, L, H, d], modified in place), so the cache never depends on
-    the sequence length; slots > l are never read.
+    the sequence length; slots > l are never read.  window / dilation restrict the keys
+    to depth_keys(l, window, dilation) (R26).
     Returns out [R, H, d]."""
     st = _store(bf16)
     q = np.asarray(q, np.float64)
@@ -168,8 +181,9 @@ def depth_attn(q, k_new, v_new, k_cache, v_cache, l, L, base=10000.0, bf16=False
         k_new = st(depth_rope(k_new, l, L, base))
     k_cache[:, l] = k_new
     v_cache[:, l] = np.asarray(v_new, np.float64)
-    K = np.asarray(k_cache[:, :l + 1], np.float64)   # [R, l+1, H, d]
-    V = np.asarray(v_cache[:, :l + 1], np.float64)
+    keys = depth_keys(l, window, dilation)
+    K = np.asarray(k_cache[:, keys], np.float64)   # [R, n_keys, H, d]
+    V = np.asarray(v_cache[:, keys], np.float64)
     # s[r, h, j] = q[r, h] . K[r, j, h] / sqrt(d)
     s = np.matmul(q[:, :, None, :], K.transpose(0, 2, 3, 1))[:, :, 0, :] / np.sqrt(d)
     p_ = softmax_lastdim(s)
@@ -351,7 +365,8 @@ def _da_branch(cfg, W, qkv, l, da_k, da_v, st, bf16):
     q_da = st(depth_rope(q_da, l, L, cfg.rope_base))
     k_da = st(depth_rope(k_da, l, L, cfg.rope_base))
     return depth_attn(q_da, k_da, st(v_da), da_k, da_v, l, L, cfg.rope_base, bf16,
-                      use_rope=False).reshape(T, h)
+                      use_rope=False, window=getattr(cfg, "da_window", 0),
+                      dilation=getattr(cfg, "da_dilation", 0)).reshape(T, h)
 
 
 def layer_step(cfg, W, x, l, da_k, da_v, sa_k=None, sa_v=None, force_idx=None,

@@ -68,6 +68,8 @@ class DreamerConfig:
     rms_eps: float = 1e-6
     rho: float = 1.0
     mixture: str = "partial"  # "partial" (DA+SA, then EA), "serial", "parallel"
+    da_window: int = 0        # DA over the most recent depths only (0: all depths)
+    da_dilation: int = 0      # with a window: also every da_dilation-th older depth
 
     @property
     def T(self) -> int:

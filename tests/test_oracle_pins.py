@@ -177,6 +177,50 @@ def test_depth_attn_ignores_future_slots_and_constant_values():
     assert np.allclose(out, 0.75, atol=1e-14)
 
 
+# Windowed / dilated depth attention (R26): keys of depth l are the `window` most recent
+# depths plus every `dilation`-th older one.  Key sets written out by hand for L = 10,
+# window 2, dilation 3.
+_KEYS_W2_D3 = [[0], [0, 1], [1, 2], [0, 2, 3], [1, 3, 4], [2, 4, 5], [0, 3, 5, 6],
+               [1, 4, 6, 7], [2, 5, 7, 8], [0, 3, 6, 8, 9]]
+
+
+def test_depth_keys_hand_enumerated():
+    for l, keys in enumerate(_KEYS_W2_D3):
+        assert list(oracle.depth_keys(l, 2, 3)) == keys
+    assert list(oracle.depth_keys(5)) == [0, 1, 2, 3, 4, 5]
+    assert list(oracle.depth_keys(5, 3)) == [3, 4, 5]
+    assert list(oracle.depth_keys(7, 1, 2)) == [1, 3, 5, 7]
+    assert list(oracle.depth_keys(2, 5)) == [0, 1, 2]          # window wider than l + 1
+    assert list(oracle.depth_keys(6, 2, 1)) == list(range(7))  # dilation 1: every depth
+    assert list(oracle.depth_keys(0, 1, 4)) == [0]
+
+
+def test_windowed_depth_attn_equals_masked_sdpa():
+    r = np.random.default_rng(41)
+    R, H, d, L = 5, 2, 8, 10
+    q, k, v = r.standard_normal((3, R, L, H, d))
+    kc, vc = np.full((R, L, H, d), np.nan), np.full((R, L, H, d), np.nan)
+    outs = np.stack([oracle.depth_attn(q[:, l], k[:, l], v[:, l], kc, vc, l, L, use_rope=False,
+                                       window=2, dilation=3) for l in range(L)], axis=1)
+    mask = torch.zeros((L, L), dtype=torch.bool)
+    for l, keys in enumerate(_KEYS_W2_D3):
+        mask[l, keys] = True
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a.transpose(0, 2, 1, 3)))
+    ref = F.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=mask)
+    assert np.allclose(outs, ref.numpy().transpose(0, 2, 1, 3), atol=1e-12)
+
+
+def test_window_one_depth_attn_returns_v_exactly():
+    r = np.random.default_rng(42)
+    R, H, d, L, l = 6, 2, 16, 8, 5
+    kc, vc = r.standard_normal((2, R, L, H, d))
+    q, k, v = r.standard_normal((3, R, H, d))
+    for bf16 in (False, True):
+        vv = oracle.bf16_round(v) if bf16 else v
+        out = oracle.depth_attn(q, k, vv, kc.copy(), vc.copy(), l, L, bf16=bf16, window=1)
+        assert np.array_equal(out, vv)
+
+
 def test_seq_attn_equals_sdpa_and_causality():
     r = np.random.default_rng(6)
     B, n, H, d = 2, 9, 3, 8
@@ -399,6 +443,20 @@ def test_layer_batch_independence():
     a = oracle.layer_forward(cfg, W, x0)["x_out"].reshape(3, 6, -1)
     b = oracle.layer_forward(cfg, W, x0[[2, 0, 1]])["x_out"].reshape(3, 6, -1)
     assert np.allclose(b, a[[2, 0, 1]], atol=1e-13)
+
+
+def test_layer_depth_window_special_cases():
+    # a window covering every depth is the full DA; a window of one makes DA return the
+    # token's own value, the same layer as DA with keys restricted to the current slot
+    cfg = CONFIGS["tiny"].replace(b=2, s=5, L=5)
+    W = oracle.prepare_weights(make_weights(cfg))
+    x0 = make_x0(cfg).numpy()
+    full = oracle.layer_forward(cfg, W, x0)["x_out"]
+    wide = oracle.layer_forward(cfg.replace(da_window=cfg.L, da_dilation=2), W, x0)["x_out"]
+    assert np.array_equal(full, wide)
+    one = oracle.layer_forward(cfg.replace(da_window=1), W, x0)["x_out"]
+    dil = oracle.layer_forward(cfg.replace(da_window=2, da_dilation=2), W, x0)["x_out"]
+    assert not np.allclose(one, full) and not np.allclose(dil, full)
 
 
 @pytest.mark.parametrize("bf16", [False, True])
