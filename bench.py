@@ -41,6 +41,12 @@ def parse():
     p.add_argument("--no-usage", action="store_true", help="skip the expert-usage report")
     p.add_argument("--no-mixtures", action="store_true",
                    help="skip timing the serial / partial / fully parallel wirings")
+    p.add_argument("--no-depth-windows", action="store_true",
+                   help="skip timing windowed / dilated depth attention")
+    p.add_argument("--da-window", type=int, default=None,
+                   help="DA over the most recent depths only (0: all; default: workload's)")
+    p.add_argument("--da-dilation", type=int, default=None,
+                   help="with a window: also every N-th older depth")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (read + write), for scaling "
                         "the FETCH_SIZE / WRITE_SIZE counters")
@@ -92,7 +98,9 @@ def algorithmic_work(cfg, counts_per_depth, reps=1):
     else:
         w["seq_attn"] = dict(bound="mfma", flops=L * 4 * cfg.b * h * (cfg.s * (cfg.s + 1) // 2),
                              launches=L)
-    da_bytes = sum(T * h * es * (6 + 2 * l) for l in range(L))
+    # q, k, v in, key and value stored, output out: 6 rows; 2 per older slot read
+    da_bytes = sum(T * h * es * (6 + 2 * (n_depth_keys(l, cfg.da_window, cfg.da_dilation) - 1))
+                   for l in range(L))
     w["depth_attn"] = dict(bound="hbm", bytes=da_bytes, launches=L)
     nw = 3 if cfg.ffn == "swiglu" else 2
     w["expert_ffn"] = dict(bound="hbm", bytes=L * 2 * T * k * h * es,
@@ -109,6 +117,18 @@ def algorithmic_work(cfg, counts_per_depth, reps=1):
     touched = sum(int((c > 0).sum()) for c in counts_per_depth)
     w["expert_ffn"]["bytes"] += touched * nw * h * f * es
     return w
+
+
+def n_depth_keys(l, window, dilation):
+    """Depth slots DA reads at depth l: all l + 1 without a window, else the window's
+    min(window, l + 1) plus the older slots at multiples of the dilation."""
+    if window <= 0:
+        return l + 1
+    older = l - window + 1  # slots 0..l-window lie outside the window
+    n = min(window, l + 1)
+    if dilation > 0 and older > 0:
+        n += l // dilation - (window - 1) // dilation  # multiples in [window, l]
+    return n
 
 
 def roofline_entry(work, avg_ms):
@@ -137,11 +157,7 @@ def time_mixtures(D, cfg, G, x0, steps):
     out = {}
     x_out = torch.empty((cfg.T, cfg.h), dtype=torch.float32, device="cuda")
     for mix in ("serial", "partial", "parallel"):
-        lc = D.make_layer_cfg(dtype=cfg.dtype, b=cfg.b, s=cfg.s, h=cfg.h, H=cfg.H, d=cfg.d,
-                              L=cfg.L, E=cfg.E, k=cfg.k, f=cfg.f, r=cfg.r, ffn=cfg.ffn,
-                              normalize=cfg.normalize, proj_experts=cfg.proj_experts,
-                              rope_base=cfg.rope_base, rms_eps=cfg.rms_eps, rho=cfg.rho,
-                              mixture=D.MIXTURES[mix], branch_streams=mix == "parallel")
+        lc = layer_cfg(D, cfg, mixture=mix)
         ws = torch.empty(D.layer_ws_bytes(lc), dtype=torch.uint8, device="cuda")
         for _ in range(3):
             D.dreamer_layer_forward(lc, G, x0, x_out=x_out, ws=ws)
@@ -158,6 +174,51 @@ def time_mixtures(D, cfg, G, x0, steps):
         out[mix]["pages_relative_throughput"] = PAGES_RELATIVE[mix]
     out["parallel"]["side_stream"] = True
     return out
+
+
+# DA key sets timed beside the full one: (window, dilation)
+DEPTH_WINDOWS = [(0, 0), (4, 4), (2, 0)]
+
+
+def time_depth_windows(D, cfg, G, x0, steps):
+    """Windowed / dilated depth attention: ms per forward, DA kernel ms per forward and the
+    algorithmic DA bytes per forward for each (window, dilation) of DEPTH_WINDOWS."""
+    import torch
+    out = {}
+    x_out = torch.empty((cfg.T, cfg.h), dtype=torch.float32, device="cuda")
+    for w, dil in DEPTH_WINDOWS:
+        c = cfg.replace(da_window=w, da_dilation=dil)
+        lc = layer_cfg(D, c)
+        ws = torch.empty(D.layer_ws_bytes(lc), dtype=torch.uint8, device="cuda")
+        for _ in range(3):
+            D.dreamer_layer_forward(lc, G, x0, x_out=x_out, ws=ws)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            D.dreamer_layer_forward(lc, G, x0, x_out=x_out, ws=ws)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        D.timing_enable("depth_attn", c.L + 8)
+        D.dreamer_layer_forward(lc, G, x0, x_out=x_out, ws=ws)
+        _, da_ms = D.timing_read()
+        D.timing_disable()
+        da_bytes = algorithmic_work(c, [])["depth_attn"]["bytes"]
+        out[f"window{w}_dilation{dil}"] = {
+            "ms_per_step": round(ms, 4), "depth_attn_ms_per_step": round(da_ms, 4),
+            "depth_attn_bytes_per_step": da_bytes,
+            "depth_attn_GBps": round(da_bytes / (da_ms * 1e-3) / 1e9, 1)}
+        del ws
+    return out
+
+
+def layer_cfg(D, cfg, cap=0, mixture="partial"):
+    return D.make_layer_cfg(dtype=cfg.dtype, b=cfg.b, s=cfg.s, h=cfg.h, H=cfg.H, d=cfg.d,
+                            L=cfg.L, E=cfg.E, k=cfg.k, f=cfg.f, r=cfg.r, ffn=cfg.ffn,
+                            normalize=cfg.normalize, proj_experts=cfg.proj_experts,
+                            decode=cfg.decode, sa_pos=cfg.sa_pos, sa_cap=cap,
+                            rope_base=cfg.rope_base, rms_eps=cfg.rms_eps, rho=cfg.rho,
+                            mixture=D.MIXTURES[mixture], branch_streams=mixture == "parallel",
+                            da_window=cfg.da_window, da_dilation=cfg.da_dilation)
 
 
 def usage_report(D, cfg, G, x0, lc, route, iters=20, lam=0.01):
@@ -225,6 +286,10 @@ def main():
     from synth import CONFIGS, make_weights, make_x0
 
     cfg = CONFIGS[args.workload]
+    if args.da_window is not None:
+        cfg = cfg.replace(da_window=args.da_window)
+    if args.da_dilation is not None:
+        cfg = cfg.replace(da_dilation=args.da_dilation)
     dev = "cuda"
     torch.cuda.set_device(0)
     if args.calibrate_copy:
@@ -238,11 +303,7 @@ def main():
         G["w_o"] = D.dreamer_absorb_shared(G.pop("w_o_e"), G.pop("w_o_sh"))
     x0 = make_x0(cfg, device=dev).reshape(cfg.T, cfg.h).contiguous()
     cap = cfg.sa_pos + reps if cfg.decode else 0
-    lc = D.make_layer_cfg(dtype=cfg.dtype, b=cfg.b, s=cfg.s, h=cfg.h, H=cfg.H, d=cfg.d, L=cfg.L,
-                          E=cfg.E, k=cfg.k, f=cfg.f, r=cfg.r, ffn=cfg.ffn,
-                          normalize=cfg.normalize, proj_experts=cfg.proj_experts,
-                          decode=cfg.decode, sa_pos=cfg.sa_pos, sa_cap=cap,
-                          rope_base=cfg.rope_base, rms_eps=cfg.rms_eps, rho=cfg.rho)
+    lc = layer_cfg(D, cfg, cap=cap)
     if cfg.decode:
         # SA caches [L, b, cap, H, d]: positions 0..sa_pos-1 seeded N(0, 1) (already
         # rotated keys / values); every step appends its `reps` tokens after them
@@ -326,6 +387,8 @@ def main():
     }
     if not args.no_mixtures and not cfg.decode:
         line["mixtures"] = time_mixtures(D, cfg, G, x0, args.steps)
+    if not args.no_depth_windows and not cfg.decode:
+        line["depth_windows"] = time_depth_windows(D, cfg, G, x0, args.steps)
     if not cfg.decode and not args.no_usage:
         line["expert_usage"] = usage_report(D, cfg, G, x0, lc, route)
     if not args.no_cpu_baseline and not cfg.decode:

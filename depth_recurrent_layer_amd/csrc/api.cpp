@@ -184,7 +184,19 @@ int dreamer_depth_attn(int dtype, int64_t rows, int H, int d, int l, int L, cons
                        const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                        void* out, const float* cos_d, const float* sin_d, float scale,
                        dreamer_stream_t stream) {
+  return dreamer_depth_attn_windowed(dtype, rows, H, d, l, L, q, k_new, v_new, k_cache,
+                                     v_cache, out, cos_d, sin_d, scale, 0, 0, stream);
+}
+
+int dreamer_depth_attn_windowed(int dtype, int64_t rows, int H, int d, int l, int L,
+                                const void* q, const void* k_new, const void* v_new,
+                                void* k_cache, void* v_cache, void* out, const float* cos_d,
+                                const float* sin_d, float scale, int window, int dilation,
+                                dreamer_stream_t stream) {
   if (!dtype_ok(dtype)) return fail(DREAMER_E_INVAL, "depth_attn: bad dtype");
+  if (window < 0 || dilation < 0)
+    return fail(DREAMER_E_INVAL, "depth_attn: negative window (%d) or dilation (%d)", window,
+                dilation);
   if (rows < 0 || H <= 0 || d <= 0 || L <= 0 || l < 0 || l >= L)
     return fail(DREAMER_E_INVAL, "depth_attn: bad sizes (rows=%lld H=%d d=%d l=%d L=%d)",
                 (long long)rows, H, d, l, L);
@@ -198,7 +210,7 @@ int dreamer_depth_attn(int dtype, int64_t rows, int H, int d, int l, int L, cons
   hipStream_t st = S(stream);
   TB(DREAMER_KC_DEPTH_ATTN);
   int rc = launch_depth_attn(dtype, rows, H, d, l, L, q, h, k_new, h, v_new, h, k_cache,
-                             v_cache, out, h, cos_d, sin_d, scale, 1, st);
+                             v_cache, out, h, cos_d, sin_d, scale, 1, st, window, dilation);
   TE(DREAMER_KC_DEPTH_ATTN);
   if (rc) return fail(DREAMER_E_UNSUPPORTED, "depth_attn: head dim %d unsupported", d);
   return check_launch("depth_attn");
@@ -560,6 +572,9 @@ static int validate_layer(const dreamer_layer_cfg* c, const dreamer_layer_weight
   if ((int64_t)c->H * c->d != c->h) return fail(DREAMER_E_INVAL, "layer: h != H * d");
   if (c->mixture < DREAMER_MIX_PARTIAL || c->mixture > DREAMER_MIX_PARALLEL)
     return fail(DREAMER_E_INVAL, "layer: mixture %d", c->mixture);
+  if (c->da_window < 0 || c->da_dilation < 0)
+    return fail(DREAMER_E_INVAL, "layer: negative da_window (%d) or da_dilation (%d)",
+                c->da_window, c->da_dilation);
   if (c->decode && (c->s != 1 || c->sa_pos <= 0 || c->sa_cap <= c->sa_pos))
     return fail(DREAMER_E_INVAL, "layer: decode needs s == 1, sa_pos > 0, sa_cap > sa_pos");
   if (!c->decode && c->sa_cap < 0) return fail(DREAMER_E_INVAL, "layer: bad sa_cap");
@@ -751,7 +766,8 @@ static int layer_run(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* 
       timing_begin(DREAMER_KC_DEPTH_ATTN, s_);
       int r2 = launch_depth_attn(dt, T, c.H, c.d, l, L, qkv + 3 * h * es, 6 * h,
                                  qkv + 4 * h * es, 6 * h, qkv + 5 * h * es, 6 * h, DAk, DAv,
-                                 att + h * es, 2 * h, lw.cos_d, lw.sin_d, scale, 0, s_);
+                                 att + h * es, 2 * h, lw.cos_d, lw.sin_d, scale, 0, s_,
+                                 c.da_window, c.da_dilation);
       timing_end(DREAMER_KC_DEPTH_ATTN, s_);  // s_: the stream DA runs on
       return r2 ? fail(DREAMER_E_UNSUPPORTED, "layer: depth attention shape") : ok();
     };

@@ -79,12 +79,15 @@ DEV void rope_chunk(float* x, int c, int d, int pos_fwd, int pos_rev, const floa
 // wave).  Per row and head: (ROPE) rotate q and k_new by depth, half reversed, and round
 // them to storage precision; store the key and the value into cache slot l, then stream
 // slots 0..l with an online softmax.  The current slot is used from registers.
+// window > 0 keeps only the slots l-window+1..l and, with dilation > 0, the older slots j
+// with (l - j) divisible by dilation; the skipped slots are never loaded.
 template <typename T, int LPH, bool ROPE>
 __global__ __launch_bounds__(256) void depth_attn_kernel(
     int64_t rows, int H, int d, int l, int L, const T* __restrict__ q, int64_t ldq,
     const T* __restrict__ kn, int64_t ldk, const T* __restrict__ vn, int64_t ldv,
     T* __restrict__ kc, T* __restrict__ vc, T* __restrict__ out, int64_t ldo,
-    const float* __restrict__ cosd, const float* __restrict__ sind, float scale) {
+    const float* __restrict__ cosd, const float* __restrict__ sind, float scale, int window,
+    int dilation) {
   constexpr int VEC = Vec16<T>::N;
   const int h = H * d;
   const int cpr = h / VEC;  // chunks per row
@@ -117,6 +120,7 @@ __global__ __launch_bounds__(256) void depth_attn_kernel(
 #pragma unroll
   for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
   for (int j = 0; j <= l; ++j) {
+    if (window > 0 && l - j >= window && (dilation <= 0 || (l - j) % dilation)) continue;
     float kj[VEC], vj[VEC];
     if (j < l) {
       load16(krow + (int64_t)j * h, kj);
@@ -146,7 +150,8 @@ __global__ __launch_bounds__(256) void depth_attn_kernel(
 int launch_depth_attn(int dtype, int64_t rows, int H, int d, int l, int L, const void* q,
                       int64_t ldq, const void* kn, int64_t ldk, const void* vn, int64_t ldv,
                       void* kc, void* vc, void* out, int64_t ldo, const float* cosd,
-                      const float* sind, float scale, int rope, hipStream_t st) {
+                      const float* sind, float scale, int rope, hipStream_t st, int window,
+                      int dilation) {
   const int vec = dtype == DT_BF16 ? 8 : 4;
   const int lph = d / vec;
   const int64_t threads = rows * (int64_t)(H * d / vec);
@@ -155,7 +160,7 @@ int launch_depth_attn(int dtype, int64_t rows, int H, int d, int l, int L, const
 #define DA_LAUNCH(T, LP, R)                                                              \
   depth_attn_kernel<T, LP, R><<<grid, 256, 0, st>>>(                                     \
       rows, H, d, l, L, (const T*)q, ldq, (const T*)kn, ldk, (const T*)vn, ldv, (T*)kc, \
-      (T*)vc, (T*)out, ldo, cosd, sind, scale)
+      (T*)vc, (T*)out, ldo, cosd, sind, scale, window, dilation)
 #define DA_CASE(T, LP)                 \
   if (rope) DA_LAUNCH(T, LP, true);    \
   else DA_LAUNCH(T, LP, false);        \

@@ -71,7 +71,8 @@ void launch_rope_jobs(const RopeJobs& jobs, hipStream_t st);
 int launch_depth_attn(int dtype, int64_t rows, int H, int d, int l, int L, const void* q,
                       int64_t ldq, const void* kn, int64_t ldk, const void* vn, int64_t ldv,
                       void* kc, void* vc, void* out, int64_t ldo, const float* cosd,
-                      const float* sind, float scale, int rope, hipStream_t st);
+                      const float* sind, float scale, int rope, hipStream_t st,
+                      int window = 0, int dilation = 0);
 
 // In-place RoPE of a [rows, 6h] QKV buffer (SA q/k by sequence position, DA q/k by depth).
 int launch_qkv_rope(int dtype, int64_t rows, int H, int d, int seq, int pos_fixed,

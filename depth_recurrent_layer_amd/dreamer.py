@@ -39,7 +39,7 @@ class LayerCfg(C.Structure):
                 ("use_ea", _i32), ("sa_rope", _i32), ("proj_experts", _i32),
                 ("mixture", _i32), ("decode", _i32), ("sa_pos", _i64), ("sa_cap", _i64),
                 ("rope_base", _f64), ("rms_eps", _f32), ("rho", _f32),
-                ("branch_streams", _i32)]
+                ("branch_streams", _i32), ("da_window", _i32), ("da_dilation", _i32)]
 
 
 class LayerWeights(C.Structure):
@@ -59,6 +59,8 @@ _sig("dreamer_version", _i32, [])
 _sig("dreamer_rope_tables", _i32, [_i32, _i32, _f64, _vp, _vp, _vp])
 _sig("dreamer_depth_attn", _i32, [_i32, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
                                   _vp, _vp, _vp, _f32, _vp])
+_sig("dreamer_depth_attn_windowed", _i32, [_i32, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
+                                           _vp, _vp, _vp, _vp, _vp, _f32, _i32, _i32, _vp])
 _sig("dreamer_seq_attn_ws_bytes", _sz, [_i32, _i32, _i32, _i32, _i32, _i64])
 _sig("dreamer_seq_attn", _i32, [_i32, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp,
                                 _i64, _vp, _vp, _vp, _f32, _i32, _vp, _sz, _vp])
@@ -86,6 +88,7 @@ _sig("dreamer_timing_disable", _i32, [])
 
 # every symbol the header declares (checked by the CPU tests)
 EXPORTS = ["dreamer_last_error", "dreamer_version", "dreamer_rope_tables", "dreamer_depth_attn",
+           "dreamer_depth_attn_windowed",
            "dreamer_seq_attn_ws_bytes", "dreamer_seq_attn", "dreamer_expert_route_ws_bytes",
            "dreamer_expert_route", "dreamer_expert_ffn_ws_bytes", "dreamer_expert_ffn",
            "dreamer_absorb_shared", "dreamer_layer_ws_bytes", "dreamer_layer_forward",
@@ -143,15 +146,19 @@ def dreamer_rope_tables(D, npos, base=10000.0, device="cuda"):
 
 
 def dreamer_depth_attn(q, k_new, v_new, k_cache, v_cache, l, L, cos_d, sin_d, scale=None,
-                       out=None):
-    """q, k_new, v_new [rows, H, d]; caches [rows, L, H, d] (slot l written)."""
+                       out=None, window=None, dilation=0):
+    """q, k_new, v_new [rows, H, d]; caches [rows, L, H, d] (slot l written).  window /
+    dilation (not None) call dreamer_depth_attn_windowed."""
     _dev(q, k_new, v_new, k_cache, v_cache, cos_d, sin_d)
     rows, H, d = q.shape
     out = torch.empty_like(q) if out is None else out
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    _check(lib.dreamer_depth_attn(_dt(q), rows, H, d, l, L, _p(q), _p(k_new), _p(v_new),
-                                  _p(k_cache), _p(v_cache), _p(out), _p(cos_d), _p(sin_d),
-                                  float(scale), _stream()))
+    args = (_dt(q), rows, H, d, l, L, _p(q), _p(k_new), _p(v_new), _p(k_cache), _p(v_cache),
+            _p(out), _p(cos_d), _p(sin_d), float(scale))
+    if window is None:
+        _check(lib.dreamer_depth_attn(*args, _stream()))
+    else:
+        _check(lib.dreamer_depth_attn_windowed(*args, int(window), int(dilation), _stream()))
     return out
 
 
@@ -220,14 +227,16 @@ def dreamer_absorb_shared(w_e, w_shared):
 def make_layer_cfg(*, dtype, b, s, h, H, d, L, E, k, f, r, ffn="swiglu", normalize=True,
                    use_da=True, use_ea=True, sa_rope=True, proj_experts=0, decode=False,
                    sa_pos=0, sa_cap=0, rope_base=10000.0, rms_eps=1e-6, rho=1.0,
-                   mixture=MIX_PARTIAL, branch_streams=False) -> LayerCfg:
+                   mixture=MIX_PARTIAL, branch_streams=False, da_window=0,
+                   da_dilation=0) -> LayerCfg:
     return LayerCfg(dtype=BF16 if dtype in ("bf16", BF16) else F32, b=b, s=s, h=h, H=H, d=d,
                     L=L, E=E, k=k, f=f, r=r, ffn_kind=FFN_KINDS[ffn] if isinstance(ffn, str) else ffn,
                     normalize_gates=int(bool(normalize)), use_da=int(bool(use_da)),
                     use_ea=int(bool(use_ea)), sa_rope=int(bool(sa_rope)),
                     proj_experts=proj_experts, mixture=mixture, decode=int(bool(decode)),
                     sa_pos=sa_pos, sa_cap=sa_cap, rope_base=rope_base, rms_eps=rms_eps, rho=rho,
-                    branch_streams=int(bool(branch_streams)))
+                    branch_streams=int(bool(branch_streams)), da_window=da_window,
+                    da_dilation=da_dilation)
 
 
 def layer_ws_bytes(cfg: LayerCfg) -> int:

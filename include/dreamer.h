@@ -95,6 +95,22 @@ int dreamer_depth_attn(int dtype, int64_t rows, int H, int d, int l, int L, cons
                        dreamer_stream_t stream);
 
 /*
+ * Windowed / dilated depth attention ([PN] "Limitations and outlook" proposes local
+ * sliding windows combined with dilated sparse depth attention to cut the memory traffic
+ * of deep recurrences; the pages give no formula, this is the plainest reading):
+ * as dreamer_depth_attn, but depth l reads only the slots j <= l with l - j < window, and,
+ * when dilation > 0, the older slots with (l - j) % dilation == 0.  The current slot is
+ * always read; window == 0 is dreamer_depth_attn (dilation ignored).  Skipped slots are
+ * never loaded, and slot l is still written, so the cache layout is unchanged.
+ * Errors: DREAMER_E_INVAL for window < 0 or dilation < 0, otherwise as dreamer_depth_attn.
+ */
+int dreamer_depth_attn_windowed(int dtype, int64_t rows, int H, int d, int l, int L,
+                                const void* q, const void* k_new, const void* v_new,
+                                void* k_cache, void* v_cache, void* out, const float* cos_d,
+                                const float* sin_d, float scale, int window, int dilation,
+                                dreamer_stream_t stream);
+
+/*
  * Causal sequence attention SA at one depth ([PN] parallel-residual equation, SA(x_l);
  * [GS-de] "standard self-attention along the token sequence").
  *   q, k_new, v_new : [B, q_len, H, d] projections of tokens at positions pos0..pos0+q_len-1
@@ -219,6 +235,9 @@ typedef struct dreamer_layer_cfg {
   float rms_eps;        /* RMSNorm epsilon                                           */
   float rho;            /* router score scale                                        */
   int branch_streams;   /* 1: PARALLEL's EA chain on a side stream (see above)          */
+  int da_window;        /* 0: DA over every depth 0..l; w > 0: only the w most recent  */
+  int da_dilation;      /* with da_window > 0 and this > 0: also every da_dilation-th
+                           older depth (see dreamer_depth_attn_windowed)               */
 } dreamer_layer_cfg;
 
 typedef struct dreamer_layer_weights {

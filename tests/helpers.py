@@ -42,7 +42,8 @@ def lib_cfg(D, cfg, sa_cap=0, streams=False):
                             sa_rope=cfg.sa_rope, proj_experts=cfg.proj_experts,
                             decode=cfg.decode, sa_pos=cfg.sa_pos, sa_cap=sa_cap,
                             rope_base=cfg.rope_base, rms_eps=cfg.rms_eps, rho=cfg.rho,
-                            mixture=D.MIXTURES[cfg.mixture], branch_streams=streams)
+                            mixture=D.MIXTURES[cfg.mixture], branch_streams=streams,
+                            da_window=cfg.da_window, da_dilation=cfg.da_dilation)
 
 
 def gpu_weights(D, cfg, W):

@@ -36,22 +36,41 @@ TD = {"bf16": torch.bfloat16, "f32": torch.float32}
                                            ("bf16", 32, 64, 70, 64), ("bf16", 4, 16, 50, 5),
                                            ("f32", 2, 64, 9, 3)])
 def test_depth_attn(gpu_lib, dt, H, d, rows, L):
-    D = gpu_lib
+    _depth_attn_case(gpu_lib, dt, H, d, rows, L)
+
+
+# windowed / dilated key sets: window 3 dilation 4 over 12 depths, window 2 dilation 3,
+# window 1 (DA returns v), a window without dilation, a window wider than L
+@pytest.mark.parametrize("dt,H,d,rows,L,window,dilation", [
+    ("bf16", 8, 64, 300, 12, 3, 4), ("f32", 4, 16, 37, 10, 2, 3), ("bf16", 4, 64, 70, 9, 1, 0),
+    ("f32", 2, 16, 20, 6, 3, 0), ("bf16", 8, 64, 100, 8, 9, 2)])
+def test_depth_attn_windowed(gpu_lib, dt, H, d, rows, L, window, dilation):
+    _depth_attn_case(gpu_lib, dt, H, d, rows, L, window, dilation)
+
+
+def _depth_attn_case(D, dt, H, d, rows, L, window=None, dilation=0):
     tdt, bf = TD[dt], dt == "bf16"
-    print(f"depth_attn {dt} H={H} d={d} rows={rows} L={L}", flush=True)
+    print(f"depth_attn {dt} H={H} d={d} rows={rows} L={L} window={window} dilation={dilation}",
+          flush=True)
     cos, sin = D.dreamer_rope_tables(d, L)
     kc = torch.full((rows, L, H, d), float("nan"), dtype=tdt, device="cuda")
     vc = torch.full_like(kc, float("nan"))
+    kc_full, vc_full = kc.clone(), vc.clone()
     rk = np.full((rows, L, H, d), np.nan)
     rv = np.full_like(rk, np.nan)
     for l in range(L):
         q, k, v = (_t((rows, H, d), 7, 100 + 3 * l + j, dtype=tdt) for j in range(3))
-        out = D.dreamer_depth_attn(q, k, v, kc, vc, l, L, cos, sin)
-        ref = oracle.depth_attn(_np(q), _np(k), _np(v), rk, rv, l, L, bf16=bf)
+        out = D.dreamer_depth_attn(q, k, v, kc, vc, l, L, cos, sin, window=window,
+                                   dilation=dilation)
+        ref = oracle.depth_attn(_np(q), _np(k), _np(v), rk, rv, l, L, bf16=bf,
+                                window=window or 0, dilation=dilation)
         torch.cuda.synchronize()
         g = _np(out)
-        if l == 0:
-            assert torch.equal(out, v), "depth 0 must return v exactly"
+        if l == 0 or window == 1:
+            assert torch.equal(out, v), "a single key must return v exactly"
+        if window is not None and window >= L:
+            full = D.dreamer_depth_attn(q, k, v, kc_full, vc_full, l, L, cos, sin)
+            assert torch.equal(out, full), "a window over every depth is the full DA"
         assert np.isfinite(g).all()
         if bf:
             # rotated q and k are a bf16 storage point rounded independently on each side;
@@ -284,6 +303,9 @@ def test_errors_are_reported(gpu_lib):
         D.dreamer_depth_attn(q2, q2, q2, kc[..., :24].contiguous(), kc[..., :24].contiguous(),
                              0, 3, cos, sin)
     assert ei.value.code == D.E_UNSUPPORTED
+    with pytest.raises(D.DreamerError) as ei:
+        D.dreamer_depth_attn(q, q, q, kc, kc, 1, 3, cos, sin, window=-1)
+    assert ei.value.code == D.E_INVAL
 
 
 # ------------------------------------------------------------- expert-load bookkeeping

@@ -181,6 +181,42 @@ def test_layer_deep_bf16_reduced(gpu_lib):
     bf16_layer_checks(gpu_lib, cfg, make_weights(cfg), make_x0(cfg))
 
 
+# ------------------------------------------------------------- windowed / dilated DA
+
+@pytest.mark.parametrize("window,dilation", [(2, 3), (1, 0), (3, 0)])
+def test_layer_depth_window_fp32(gpu_lib, window, dilation):
+    cfg = CONFIGS["tiny"].replace(b=2, s=21, L=9, da_window=window, da_dilation=dilation)
+    print(f"layer tiny f32 L=9 DA window {window} dilation {dilation}", flush=True)
+    W, x0 = make_weights(cfg), make_x0(cfg)
+    gpu = run_gpu(gpu_lib, cfg, W, x0)
+    ref = run_ref(cfg, W, x0)
+    assert rel_err(gpu["x_out"], ref["x_out"]) <= 1e-5
+    check_routing(cfg, W, gpu, ref, exact=True)
+
+
+def test_layer_depth_window_deep_bf16(gpu_lib):
+    cfg = CONFIGS["deep"].replace(b=1, s=80, h=256, H=4, E=128, da_window=8, da_dilation=8)
+    print("layer deep bf16 reduced, DA window 8 dilation 8", flush=True)
+    bf16_layer_checks(gpu_lib, cfg, make_weights(cfg), make_x0(cfg))
+
+
+def test_layer_depth_window_decode_fp32(gpu_lib):
+    cfg = CONFIGS["decode"].replace(dtype="f32", b=3, sa_pos=70, h=256, H=4, L=7, E=64,
+                                    da_window=2, da_dilation=2)
+    print("layer decode f32, DA window 2 dilation 2", flush=True)
+    W, x0 = make_weights(cfg), make_x0(cfg)
+    cap = cfg.sa_pos + 1
+    sk = torch.full((cfg.L, cfg.b, cap, cfg.H, cfg.d), float("nan"), dtype=cfg.torch_dtype)
+    sv = torch.full_like(sk, float("nan"))
+    sk[:, :, :cfg.sa_pos] = make_sa_cache(cfg, "k")
+    sv[:, :, :cfg.sa_pos] = make_sa_cache(cfg, "v")
+    rsk, rsv = sk.double().numpy().copy(), sv.double().numpy().copy()
+    gpu = run_gpu(gpu_lib, cfg, W, x0, sa_cache=(sk.cuda(), sv.cuda()), sa_cap=cap)
+    ref = run_ref(cfg, W, x0, rsk, rsv)
+    assert rel_err(gpu["x_out"], ref["x_out"]) <= 1e-5
+    check_routing(cfg, W, gpu, ref, exact=True)
+
+
 # -------------------------------------------------------------------------------- decode
 
 @pytest.mark.parametrize("mixture", ["partial", "serial", "parallel"])

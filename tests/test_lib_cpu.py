@@ -43,6 +43,26 @@ def test_depth_attn_rejects_head_dim():
     assert rc == D.E_UNSUPPORTED
 
 
+def test_depth_attn_windowed_rejects_negative_window():
+    p = C.c_void_p(16)
+    for w, dil in ((-1, 0), (2, -3)):
+        rc = D.lib.dreamer_depth_attn_windowed(D.BF16, 4, 2, 64, 1, 5, p, p, p, p, p, p, p, p,
+                                               0.1, w, dil, None)
+        assert rc == D.E_INVAL
+        assert b"window" in D.lib.dreamer_last_error()
+
+
+def test_layer_rejects_negative_depth_window():
+    cfg = D.make_layer_cfg(dtype="bf16", b=8, s=512, h=512, H=8, d=64, L=8, E=256, k=4, f=64,
+                           r=64, da_window=-2)
+    W = D.LayerWeights()
+    rc = D.lib.dreamer_layer_forward(C.byref(cfg), C.byref(W), None, None, None, None, None,
+                                     None, None, None, None, None, None, None, None, None, None,
+                                     0, None)
+    assert rc == D.E_INVAL
+    assert b"da_window" in D.lib.dreamer_last_error()
+
+
 def test_route_rejects_k_above_E():
     rc = D.lib.dreamer_expert_route(D.BF16, 8, 64, 16, 4, 5, 0, 2, None, None, None, None, 1.0,
                                     1, None, None, None, None, None, None, 0, None)
