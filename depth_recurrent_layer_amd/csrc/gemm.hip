@@ -15,41 +15,49 @@
 
 namespace dreamer {
 
-// K streams through a ring of NS stages of 32-wide K slices filled by direct global->LDS
-// loads (global_load_lds_dwordx4), NS - 1 slices in flight per block.  A stage holds
-// the BM A rows then the BN B rows of one slice as 64-byte rows; the four 16-byte chunks
-// of row r are XOR-swizzled (chunk c at slot c ^ ((r >> 1) & 3)) so the 8 rows read by
-// 8 consecutive lanes of one MFMA fragment load cover all 32 banks.  2 x 2 waves, each
-// owning a WM x WN sub-tile (WM/16 x WN/16 MFMA tiles).  After the K loop every wave
-// stages its own sub-tile in LDS and writes whole rows with 16-byte stores.
-#ifndef DREAMER_GEMM_RING_BYTES
-#define DREAMER_GEMM_RING_BYTES 65536  // ring budget per block (two blocks per CU)
-#endif
-
-// QKVONLY: an instance for the Q/K/V projection only (bf16 output, QKV epilogue), whose
-// epilogue staging is bf16 and therefore smaller.  RING: LDS budget of the K ring; OCC:
-// blocks per CU the instance is built for.
-template <int WM, int WN, bool QKVONLY, int RING>
-struct GemmShape {
-  static constexpr int BM = 2 * WM, BN = 2 * WN, TM = WM / 16, TN = WN / 16;
-  static constexpr int STAGE = (BM + BN) * 64;  // bytes per K slice
-  static constexpr int NI = (BM + BN) / 16;     // 1 KiB load instructions per stage
-  static constexpr int LPW = NI / 4;            // per wave
-  static constexpr int NS0 = RING / STAGE;
-  static constexpr int NS = NS0 > 8 ? 8 : NS0;  // ring depth
+// K streams through a ring of NS stages filled by direct global->LDS loads
+// (global_load_lds_dwordx4), NS - 1 stages in flight per block.  A stage holds a K slice
+// of BKB bytes (32 or 64 elements) of the BM A rows, then of the BN B rows; the 16-byte
+// chunks of row r are XOR-swizzled (chunk c at slot c ^ ((r >> 1) & (BKB/16 - 1))) so the
+// rows read by consecutive lanes of one MFMA fragment load cover all banks.  128-byte
+// slices read whole cache lines and stream from L2 markedly faster than 64-byte ones.
+// WGM x WGN waves, each owning a WM x WN sub-tile (WM/16 x WN/16 MFMA tiles).  After the
+// K loop every wave stages its own sub-tile in LDS and writes whole rows with 16-byte
+// stores.  QKVONLY: an instance for the Q/K/V projection only (bf16 output, QKV
+// epilogue), whose epilogue staging is bf16 and therefore smaller.  OCC: blocks per CU
+// the instance is built for.
+template <int WM_, int WN_, int WGM_, int WGN_, int BKB_, int NS_, int OCC_, bool QKVONLY_>
+struct GemmCfg {
+  static constexpr int WM = WM_, WN = WN_, WGM = WGM_, WGN = WGN_, BKB = BKB_, NS = NS_;
+  static constexpr int OCC = OCC_;
+  static constexpr bool QKVONLY = QKVONLY_;
+  static constexpr int NW = WGM * WGN, NT = 64 * NW;
+  static constexpr int BM = WGM * WM, BN = WGN * WN, TM = WM / 16, TN = WN / 16;
+  static constexpr int CPR = BKB / 16, RPI = 64 / CPR;  // chunks per row, rows per load
+  static constexpr int KSUB = BKB / 64;                 // 32-wide MFMA k-steps per stage
+  static constexpr int STAGE = (BM + BN) * BKB;         // bytes per K slice
+  static constexpr int NI = STAGE / 1024;               // 1 KiB load instructions per stage
+  static constexpr int LPW = NI / NW;                   // per wave
   // epilogue staging per wave: float32 rows of WN (+4), or bf16 rows of WN (+8)
   static constexpr int LDF = WN + 4, LDB = WN + 8;
   static constexpr int WAVE_STAGE = QKVONLY ? WM * LDB * 2 : WM * LDF * 4;
-  static constexpr int SMEM = NS * STAGE > 4 * WAVE_STAGE ? NS * STAGE : 4 * WAVE_STAGE;
-  static_assert(NI % 4 == 0, "stage must split evenly over 4 waves");
-  static_assert(NS >= 2, "ring too small");
+  static constexpr int SMEM = NS * STAGE > NW * WAVE_STAGE ? NS * STAGE : NW * WAVE_STAGE;
+  static_assert(BKB == 64 || BKB == 128, "64- or 128-byte K slices");
+  static_assert(NI % NW == 0, "stage must split evenly over the waves");
+  static_assert(BM % RPI == 0, "A rows must fill whole load instructions");
+  static_assert(NS >= 2 && SMEM <= 160 * 1024, "ring");
 };
 
-template <typename OutT, int WM, int WN, bool QKVONLY = false,
-          int RING = DREAMER_GEMM_RING_BYTES, int OCC = 2>
-__global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(GemmArgs a) {
-  using S = GemmShape<WM, WN, QKVONLY, RING>;
-  constexpr int BM = S::BM, BN = S::BN, TM = S::TM, TN = S::TN;
+DEV int gemm_swz(int bkb, int row, int c) {
+  return bkb == 64 ? (c ^ ((row >> 1) & 3)) : (c ^ ((row >> 1) & 7));
+}
+
+template <typename OutT, typename CFG>
+__global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_bf16_kernel(GemmArgs a) {
+  using S = CFG;
+  constexpr int BM = S::BM, BN = S::BN, TM = S::TM, TN = S::TN, WM = S::WM, WN = S::WN;
+  constexpr int BKB = S::BKB, NW = S::NW;
+  constexpr bool QKVONLY = S::QKVONLY;
   __shared__ __attribute__((aligned(1024))) char ring[S::SMEM];
   __shared__ int rows_s[BM];
 
@@ -73,38 +81,38 @@ __global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(GemmArgs a) {
   const int n0 = blockIdx.y * BN;
   const bf16* __restrict__ A = (const bf16*)a.A;
   const bf16* __restrict__ B = (const bf16*)a.B + (int64_t)g * a.b_gstride;
-  for (int i = tid; i < BM; i += 256) {
+  for (int i = tid; i < BM; i += S::NT) {
     const int m = m_begin + i;
     rows_s[i] = (m < m_end) ? (a.rows ? a.rows[m] : m) : -1;
   }
   __syncthreads();
 
-  // load descriptors: wave w issues instructions q = w + 4 j of every stage; lane L of
-  // instruction q fills row 16 q' + L / 4, slot L % 4 of its section
+  // load descriptors: wave w issues instructions q = w + NW j of every stage; lane L of
+  // instruction q fills row RPI q' + L / CPR, slot L % CPR of its section
   const int lane = tid & 63, w = tid >> 6;
   const bf16* src[S::LPW];
 #pragma unroll
   for (int j = 0; j < S::LPW; ++j) {
-    const int q = w + 4 * j, slot = lane & 3;
-    if (q < BM / 16) {
-      const int row = q * 16 + (lane >> 2);
+    const int q = w + NW * j, slot = lane % S::CPR;
+    if (q < BM / S::RPI) {
+      const int row = q * S::RPI + lane / S::CPR;
       const int o = rows_s[row] >= 0 ? rows_s[row] : rows_s[0];  // pad rows repeat row 0
-      src[j] = A + (int64_t)(o / a.row_div) * a.lda + (swz64_slot(row, slot) << 3);
+      src[j] = A + (int64_t)(o / a.row_div) * a.lda + (gemm_swz(BKB, row, slot) << 3);
     } else {
-      const int row = (q - BM / 16) * 16 + (lane >> 2);
+      const int row = (q - BM / S::RPI) * S::RPI + lane / S::CPR;
       const int n = min(n0 + row, a.N - 1);
-      src[j] = B + (int64_t)n * a.ldb + (swz64_slot(row, slot) << 3);
+      src[j] = B + (int64_t)n * a.ldb + (gemm_swz(BKB, row, slot) << 3);
     }
   }
   auto issue = [&](int s) {
     char* sb = ring + (s % S::NS) * S::STAGE;
 #pragma unroll
     for (int j = 0; j < S::LPW; ++j)
-      __builtin_amdgcn_global_load_lds((const void*)(src[j] + s * 32),
-                                       (lds_void*)(sb + (w + 4 * j) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(src[j] + s * (BKB / 2)),
+                                       (lds_void*)(sb + (w + NW * j) * 1024), 16, 0, 0);
   };
 
-  const int wm = w >> 1, wn = w & 1, lr = lane & 15, lg = lane >> 4;
+  const int wm = w / S::WGN, wn = w % S::WGN, lr = lane & 15, lg = lane >> 4;
   floatx4 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -130,7 +138,8 @@ __global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(GemmArgs a) {
     const int orow = rows_s[rw0 + i * 16 + lg * 4 + v];
     return a.pos_fixed >= 0 ? a.pos_fixed : (orow >= 0 ? orow % a.seq : 0);
   };
-  constexpr bool PRE_TAB = QKV && TM * OCC <= 8;  // register room for the row entries
+  // register room for the row entries: 4 TM float4 per lane at NW * OCC / 4 waves per SIMD
+  constexpr bool PRE_TAB = QKV && TM * (NW * S::OCC / 4) <= 8;
   float4 tq[PRE_TAB ? TM : 1][4];
   float4 td0 = {}, td1 = {};
   int n_tab = 0;  // table loads issued behind the ring's first stages
@@ -156,7 +165,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(GemmArgs a) {
     }
   }
 
-  const int nst = a.K / 32;
+  const int nst = a.K / (BKB / 2);
   const uint32_t ring0 = lds_off(ring);
   for (int s = 0; s < S::NS - 1 && s < nst; ++s) issue(s);
   if constexpr (QKV) {
@@ -176,17 +185,29 @@ __global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(GemmArgs a) {
     ring_barrier();  // stage s visible to every wave; stage s - 1 consumed by every wave
     if (s + S::NS - 1 < nst) issue(s + S::NS - 1);
     const uint32_t sb = ring0 + (s % S::NS) * S::STAGE;
-    uint32_t ad[TM + TN];
-    bf16x8 fr[TM + TN];  // A fragments, then B fragments
 #pragma unroll
-    for (int i = 0; i < TM; ++i) ad[i] = sb + swz64(wm * WM + i * 16 + lr, lg);
+    for (int kh = 0; kh < S::KSUB; ++kh) {
+      // the swizzle slot depends on the row only through lr, so fragments i (j) of one
+      // k-step sit 16 rows apart: one base address per operand, immediate offsets
+      const int slot = gemm_swz(BKB, lr, kh * 4 + lg);
+      const uint32_t abase = sb + (wm * WM + lr) * BKB + (slot << 4);
+      const uint32_t bbase = sb + (BM + wn * WN + lr) * BKB + (slot << 4);
+      bf16x8 fr[TM + TN];  // A fragments, then B fragments
+      if constexpr (TM == 4 && TN == 4) {
+        lds_read_b128_2x4<16 * BKB>(fr, abase, bbase);
+      } else {
+        uint32_t ad[TM + TN];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) ad[TM + j] = sb + BM * 64 + swz64(wn * WN + j * 16 + lr, lg);
-    lds_read_b128<TM + TN>(fr, ad);
+        for (int i = 0; i < TM; ++i) ad[i] = abase + i * 16 * BKB;
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+        for (int j = 0; j < TN; ++j) ad[TM + j] = bbase + j * 16 * BKB;
+        lds_read_b128<TM + TN>(fr, ad);
+      }
 #pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(fr[i], fr[TM + j], acc[i][j]);
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(fr[i], fr[TM + j], acc[i][j]);
+    }
   }
   __syncthreads();  // every wave is done with the ring; it becomes epilogue staging
 
@@ -346,47 +367,53 @@ int launch_gemm(const GemmArgs& a, int dtype, int out_f32, hipStream_t st) {
     return 0;
   }
   if (a.K % 32 != 0 || a.N % 8 != 0) return -1;
-  // Tiles: 128 x 128 when that gives >= 512 blocks (two per CU), else 64 x 128, else
-  // 64 x 64; the QKV epilogue needs 64-column wave tiles (one head), grouped launches the
-  // 64-row m-tiles their tile offsets were built with.
-  int bm, bn;
-  if (a.qkv_h) {
-    if (a.qkv_h % 128 || out_f32 || !a.rope_d4 || (a.sa_rope && !a.rope_s4)) return -1;
-    bn = 128;
-  } else {
-    bn = a.N >= 128 ? 128 : 64;
-  }
+  const bool k64 = a.K % 64 == 0;  // 128-byte K slices
   auto tiles = [&](int tm, int tn) {
     return (int64_t)((a.M + tm - 1) / tm) * ((a.N + tn - 1) / tn);
   };
+  auto grid_of = [&](int bm, int bn) {
+    return dim3((a.M + bm - 1) / bm + (a.toff ? a.G : 0), (a.N + bn - 1) / bn);
+  };
+  // QKV projections with the rotary epilogue (64-column wave tiles, one head each):
+  // 128 x 128 tiles of 8 waves at two blocks per CU; few rows, and grouped launches (whose
+  // tile offsets were built for 64-row m-tiles), take 64 x 128 tiles of 4 waves.
+  if (a.qkv_h) {
+    if (a.qkv_h % 128 || out_f32 || !a.rope_d4 || (a.sa_rope && !a.rope_s4)) return -1;
+    if (a.toff && a.tile_m != 64) return -1;
+    if (a.toff || tiles(128, 128) < 256) {
+      if (k64)
+        gemm_bf16_kernel<bf16, GemmCfg<32, 64, 2, 2, 128, 3, 2, false>><<<grid_of(64, 128), 256, 0, st>>>(a);
+      else
+        gemm_bf16_kernel<bf16, GemmCfg<32, 64, 2, 2, 64, 5, 2, false>><<<grid_of(64, 128), 256, 0, st>>>(a);
+    } else if (k64) {
+      gemm_bf16_kernel<bf16, GemmCfg<32, 64, 4, 2, 128, 2, 2, true>><<<grid_of(128, 128), 512, 0, st>>>(a);
+    } else {
+      gemm_bf16_kernel<bf16, GemmCfg<64, 64, 2, 2, 64, 3, 3, true>><<<grid_of(128, 128), 256, 0, st>>>(a);
+    }
+    return 0;
+  }
+  // Generic: 128 x 128 tiles when that gives >= 512 blocks (two per CU), else 64 x 128,
+  // else 64 x 64; grouped launches use 64-row m-tiles.
+  const int bn = a.N >= 128 ? 128 : 64;
+  int bm = 64, bnn = bn;
   if (a.toff) {
     if (a.tile_m != 64) return -1;
-    bm = 64;
   } else if (bn == 128 && tiles(128, 128) >= 512) {
     bm = 128;
-  } else {
-    bm = 64;
-    if (!a.qkv_h && bn == 128 && tiles(64, 128) < 512) bn = 64;
+  } else if (bn == 128 && tiles(64, 128) < 512) {
+    bnn = 64;
   }
-  const int mt = (a.M + bm - 1) / bm + (a.toff ? a.G : 0);
-  dim3 grid(mt, (a.N + bn - 1) / bn);
-  // QKV projections with the rotary epilogue: 256 x 128 tiles at two blocks per CU once
-  // they fill the chip, else 128 x 128 tiles at three per CU (one round for up to 768
-  // tiles); small M keeps the 64 x 128 tiles chosen above.
-  if (a.qkv_h && !a.toff && tiles(256, 128) >= 512) {
-    dim3 g2((a.M + 255) / 256, (a.N + 127) / 128);
-    gemm_bf16_kernel<bf16, 128, 64, true, 73728, 2><<<g2, 256, 0, st>>>(a);
-    return 0;
+#define DREAMER_GEMM_LAUNCH(OUT)                                                               \
+  if (bm == 128) {                                                                            \
+    if (k64) gemm_bf16_kernel<OUT, GemmCfg<64, 64, 2, 2, 128, 2, 2, false>><<<grid_of(128, 128), 256, 0, st>>>(a); \
+    else gemm_bf16_kernel<OUT, GemmCfg<64, 64, 2, 2, 64, 4, 2, false>><<<grid_of(128, 128), 256, 0, st>>>(a);      \
+  } else if (bnn == 128) {                                                                    \
+    if (k64) gemm_bf16_kernel<OUT, GemmCfg<32, 64, 2, 2, 128, 3, 2, false>><<<grid_of(64, 128), 256, 0, st>>>(a);  \
+    else gemm_bf16_kernel<OUT, GemmCfg<32, 64, 2, 2, 64, 5, 2, false>><<<grid_of(64, 128), 256, 0, st>>>(a);       \
+  } else {                                                                                    \
+    if (k64) gemm_bf16_kernel<OUT, GemmCfg<32, 32, 2, 2, 128, 4, 2, false>><<<grid_of(64, 64), 256, 0, st>>>(a);   \
+    else gemm_bf16_kernel<OUT, GemmCfg<32, 32, 2, 2, 64, 8, 2, false>><<<grid_of(64, 64), 256, 0, st>>>(a);        \
   }
-  if (a.qkv_h && !a.toff && tiles(128, 128) >= 256) {
-    dim3 g3((a.M + 127) / 128, (a.N + 127) / 128);
-    gemm_bf16_kernel<bf16, 64, 64, true, 49152, 3><<<g3, 256, 0, st>>>(a);
-    return 0;
-  }
-#define DREAMER_GEMM_LAUNCH(OUT)                                                  \
-  if (bm == 128) gemm_bf16_kernel<OUT, 64, 64><<<grid, 256, 0, st>>>(a);          \
-  else if (bn == 128) gemm_bf16_kernel<OUT, 32, 64><<<grid, 256, 0, st>>>(a);     \
-  else gemm_bf16_kernel<OUT, 32, 32><<<grid, 256, 0, st>>>(a);
   if (out_f32) {
     DREAMER_GEMM_LAUNCH(float)
   } else {

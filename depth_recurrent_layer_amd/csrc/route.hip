@@ -464,41 +464,47 @@ __global__ __launch_bounds__(512) void perm_hist_kernel(const int32_t* __restric
   for (int e = threadIdx.x; e < E; e += blockDim.x) out[e] = lh[e];
 }
 
-__global__ __launch_bounds__(512) void perm_scatter_kernel(
-    const int32_t* __restrict__ idx, int64_t nslots, int E, int nb, int tile_m,
-    const int32_t* __restrict__ hist, int32_t* __restrict__ counts, int32_t* __restrict__ goff,
-    int32_t* __restrict__ toff, int32_t* __restrict__ perm, const float* __restrict__ gate,
-    float* __restrict__ pgate, int4* __restrict__ tiles) {
-  extern __shared__ int base[];  // [E]: totals, then this chunk's cursors
-  __shared__ int s_rows[512], s_tiles[512];
-  const int tid = threadIdx.x, nt = blockDim.x, b = blockIdx.x;
-  const bool pub = b == 0;
+// Expert offsets from the per-expert totals in base[E] (LDS): every thread owns a
+// contiguous range of experts; a wavefront scan (lane shuffles) plus one pass over the
+// wave totals gives each range its first row and first m-tile.  base[e] becomes e's
+// first row plus prev[e] (the rows of e in earlier chunks, or nullptr); with pub,
+// counts / goff / toff and the tile descriptors are written.  s_wave: 32 ints.
+DEV void expert_offsets(int* base, const int* prev, int E, int tile_m, bool pub,
+                        int32_t* __restrict__ counts, int32_t* __restrict__ goff,
+                        int32_t* __restrict__ toff, int4* __restrict__ tiles, int* s_wave) {
+  const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, w = tid >> 6;
   const int per = (E + nt - 1) / nt;
   const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
   int rsum = 0, tsum = 0;
   for (int e = e0; e < e1; ++e) {
-    int tot = 0;
-    for (int q = 0; q < nb; ++q) tot += hist[(int64_t)q * E + e];
-    base[e] = tot;
-    rsum += tot;
-    tsum += (tot + tile_m - 1) / tile_m;
+    rsum += base[e];
+    tsum += (base[e] + tile_m - 1) / tile_m;
   }
-  s_rows[tid] = rsum;
-  s_tiles[tid] = tsum;
+  int r = rsum, t = tsum;  // inclusive scans within the wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int a = __shfl_up(r, o, 64), c = __shfl_up(t, o, 64);
+    if (lane >= o) {
+      r += a;
+      t += c;
+    }
+  }
+  if (lane == 63) {
+    s_wave[w] = r;
+    s_wave[16 + w] = t;
+  }
   __syncthreads();
-  for (int o = 1; o < nt; o <<= 1) {
-    const int a = tid >= o ? s_rows[tid - o] : 0;
-    const int c = tid >= o ? s_tiles[tid - o] : 0;
-    __syncthreads();
-    s_rows[tid] += a;
-    s_tiles[tid] += c;
-    __syncthreads();
+  int rr = r - rsum, tt = t - tsum, rtot = 0, ttot = 0;
+  for (int q = 0; q < (nt >> 6); ++q) {
+    if (q < w) {
+      rr += s_wave[q];
+      tt += s_wave[16 + q];
+    }
+    rtot += s_wave[q];
+    ttot += s_wave[16 + q];
   }
-  int rr = s_rows[tid] - rsum, tt = s_tiles[tid] - tsum;
   for (int e = e0; e < e1; ++e) {
     const int tot = base[e];
-    int pre = 0;
-    for (int q = 0; q < b; ++q) pre += hist[(int64_t)q * E + e];
     if (pub) {
       counts[e] = tot;
       goff[e] = rr;
@@ -506,22 +512,60 @@ __global__ __launch_bounds__(512) void perm_scatter_kernel(
       if (tiles)  // one descriptor per m-tile: expert, first row, end of the expert's rows
         for (int q = 0; q * tile_m < tot; ++q) tiles[tt + q] = make_int4(e, rr + q * tile_m, rr + tot, 0);
     }
-    base[e] = rr + pre;
+    base[e] = rr + (prev ? prev[e] : 0);
     rr += tot;
     tt += (tot + tile_m - 1) / tile_m;
   }
-  if (pub && tid == nt - 1) {
-    goff[E] = s_rows[nt - 1];
-    toff[E] = s_tiles[nt - 1];
+  if (pub && tid == 0) {
+    goff[E] = rtot;
+    toff[E] = ttot;
   }
   __syncthreads();
+}
+
+// One block of PERM_THREADS per chunk: the chunk's experts and gates are loaded first
+// (their latency overlaps the histogram reads), then the totals and the rows of each
+// expert in earlier chunks, the offsets, and the scatter from registers.
+constexpr int PERM_THREADS = 512, PERM_PER = PERM_CHUNK / PERM_THREADS;
+
+__global__ __launch_bounds__(PERM_THREADS) void perm_scatter_kernel(
+    const int32_t* __restrict__ idx, int64_t nslots, int E, int nb, int tile_m,
+    const int32_t* __restrict__ hist, int32_t* __restrict__ counts, int32_t* __restrict__ goff,
+    int32_t* __restrict__ toff, int32_t* __restrict__ perm, const float* __restrict__ gate,
+    float* __restrict__ pgate, int4* __restrict__ tiles) {
+  extern __shared__ int sh[];  // base [E] (totals, then cursors), prev [E]
+  int* base = sh;
+  int* prev = sh + E;
+  __shared__ int s_wave[32];
+  const int tid = threadIdx.x, b = blockIdx.x;
   const int64_t s0 = (int64_t)b * PERM_CHUNK;
-  const int64_t s1 = min(s0 + PERM_CHUNK, nslots);
-  for (int64_t s = s0 + tid; s < s1; s += nt) {
-    const int pos = atomicAdd(&base[min(max(idx[s], 0), E - 1)], 1);
-    perm[pos] = (int32_t)s;
-    if (pgate) pgate[pos] = gate[s];
+  int ex[PERM_PER];
+  float gv[PERM_PER];
+#pragma unroll
+  for (int j = 0; j < PERM_PER; ++j) {
+    const int64_t s = s0 + j * PERM_THREADS + tid;
+    ex[j] = s < nslots ? min(max(idx[s], 0), E - 1) : -1;
+    gv[j] = (pgate && s < nslots) ? gate[s] : 0.f;
   }
+  for (int e = tid; e < E; e += PERM_THREADS) {
+    int tot = 0, pre = 0;
+    for (int q = 0; q < nb; ++q) {
+      const int v = hist[(int64_t)q * E + e];
+      tot += v;
+      pre += q < b ? v : 0;
+    }
+    base[e] = tot;
+    prev[e] = pre;
+  }
+  __syncthreads();
+  expert_offsets(base, prev, E, tile_m, b == 0, counts, goff, toff, tiles, s_wave);
+#pragma unroll
+  for (int j = 0; j < PERM_PER; ++j)
+    if (ex[j] >= 0) {
+      const int pos = atomicAdd(&base[ex[j]], 1);
+      perm[pos] = (int32_t)(s0 + j * PERM_THREADS + tid);
+      if (pgate) pgate[pos] = gv[j];
+    }
 }
 
 __global__ void hist_colsum_kernel(const int32_t* __restrict__ hist, int nb, int E,
@@ -537,11 +581,12 @@ int launch_permute(const int32_t* idx, int64_t nslots, int E, int tile_m, int32_
                    int32_t* counts, int32_t* goff, int32_t* toff, int32_t* perm,
                    hipStream_t st, const float* gate, float* pgate, int4* tiles) {
   if (E <= 0 || E > PERM_MAX_E) return -1;
-  const int nb = perm_blocks(nslots);
   const size_t lds = (size_t)E * sizeof(int);
+  const int nb = perm_blocks(nslots);
   perm_hist_kernel<<<nb, 512, lds, st>>>(idx, nslots, E, hist);
-  perm_scatter_kernel<<<nb, 512, lds, st>>>(idx, nslots, E, nb, tile_m, hist, counts, goff,
-                                            toff, perm, gate, pgate, tiles);
+  perm_scatter_kernel<<<nb, PERM_THREADS, 2 * lds, st>>>(idx, nslots, E, nb, tile_m, hist,
+                                                         counts, goff, toff, perm, gate, pgate,
+                                                         tiles);
   return 0;
 }
 

@@ -247,6 +247,7 @@ def _routing(T, E, k, seed, skew=False):
     ("bf16", "linear", 130, 256, 0, 16, 1, True),
     ("f32", "gelu", 16, 64, 32, 16, 1, False),
     ("f32", "swiglu", 20, 64, 32, 8, 2, False),
+    ("bf16", "swiglu", 4500, 256, 64, 64, 8, True),   # > 32768 slots: chunked grouping
 ])
 def test_expert_ffn(gpu_lib, dt, kind, T, h, f, E, k, skew):
     D = gpu_lib
@@ -278,6 +279,24 @@ def test_expert_ffn(gpu_lib, dt, kind, T, h, f, E, k, skew):
     out0 = D.dreamer_expert_ffn(kind, x, idx, torch.zeros_like(gate), w1, w3, w2, res)
     torch.cuda.synchronize()
     assert torch.equal(out0, res)
+
+
+def test_expert_ffn_grouping_paths_same_bits(gpu_lib):
+    # 4500 tokens x top-8 are grouped by the chunked kernels, the first 4000 tokens (32000
+    # slots) by the one-block kernel: every token's output is the same bits either way
+    D = gpu_lib
+    T, h, f, E, k = 4500, 256, 64, 64, 8
+    x = _t((T, h), 33, 0, 1.0, torch.bfloat16)
+    idx, gate = _routing(T, E, k, 33, True)
+    res = _t((T, h), 33, 1, 1.0, torch.float32)
+    w1, w3 = _t((E, f, h), 33, 2, 0.05, torch.bfloat16), _t((E, f, h), 33, 3, 0.05, torch.bfloat16)
+    w2 = _t((E, h, f), 33, 4, 0.05, torch.bfloat16)
+    full = D.dreamer_expert_ffn("swiglu", x, idx, gate, w1, w3, w2, res)
+    n = 4000
+    part = D.dreamer_expert_ffn("swiglu", x[:n].contiguous(), idx[:n].contiguous(),
+                                gate[:n].contiguous(), w1, w3, w2, res[:n].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(full[:n], part)
 
 
 def test_absorb_shared_exact(gpu_lib):
