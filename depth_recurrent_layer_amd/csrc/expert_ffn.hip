@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256, 2) void expert_ffn_kernel(
     int k, int h_in, int h_out, int E, const bf16* __restrict__ x,
     const bf16* __restrict__ w1, const bf16* __restrict__ w3, const bf16* __restrict__ w2,
     const int32_t* __restrict__ perm, const float* __restrict__ pgate,
-    const int4* __restrict__ tiles, const int32_t* __restrict__ ntiles,
+    const int4* __restrict__ tiles, int tile_cap, const int32_t* __restrict__ ntiles,
     bf16* __restrict__ slots) {
   using S = FfnShape<F, KIND>;
   constexpr int NT1 = F / 64;  // 16-col tiles per wave per projection
@@ -46,12 +46,16 @@ __global__ __launch_bounds__(256, 2) void expert_ffn_kernel(
   __shared__ int s_slot[64];
   __shared__ float s_gate[64];
 
-  // tile descriptor and tile count in one round trip, then slot ids and gates (stored in
-  // expert-major order by the permutation) in another
-  const int tile = blockIdx.x;
+  // Blocks reach the 8 XCDs round-robin; block b takes tile (b % 8) * per + b / 8, so each
+  // XCD works through one contiguous range of tiles, where consecutive tiles mostly share
+  // an expert whose weights then stay in that XCD's L2.  The tile count and a descriptor
+  // (clamped into the array, used only for a real tile) come in one round trip, then the
+  // slot ids and gates (stored in expert-major order by the permutation) in another.
   const int n_tiles = *ntiles;
-  const int4 td = tiles[tile];  // past the last tile: not used
-  if (tile >= n_tiles) return;
+  const int b = blockIdx.x, per = (n_tiles + 7) / 8;
+  const int tile = (b & 7) * per + (b >> 3);
+  const int4 td = tiles[min(tile, tile_cap - 1)];
+  if ((b >> 3) >= per || tile >= n_tiles) return;
   const int e = td.x, r0 = td.y, r1 = td.z;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
   if (tid < 64) {
@@ -227,12 +231,14 @@ int launch_expert_ffn(int dtype, int kind, int64_t nslots, int k, int h_in, int 
   if (nslots <= 0) return 0;
   if (dtype == DT_F32) return -1;  // the f32 path uses launch_expert_ffn_f32
   if (h_in % 64 || h_out % 64) return -1;
-  const unsigned grid = (unsigned)((nslots + FFN_TILE_M - 1) / FFN_TILE_M + E);
+  // every tile index below the bound has a block (a multiple of the 8 XCDs)
+  const int64_t cap = tile_bound(nslots, E, FFN_TILE_M);
+  const unsigned grid = (unsigned)((cap + 7) / 8 * 8);
 #define EF_CASE(FF, KK)                                                                  \
   expert_ffn_kernel<FF, KK><<<grid, 256, 0, st>>>(k, h_in, h_out, E, (const bf16*)x,     \
                                                   (const bf16*)w1, (const bf16*)w3,      \
                                                   (const bf16*)w2, perm, pgate, tiles,   \
-                                                  toff + E, (bf16*)slots)
+                                                  (int)cap, toff + E, (bf16*)slots)
   if (kind == FFN_SWIGLU && f == 64) EF_CASE(64, FFN_SWIGLU);
   else if (kind == FFN_SWIGLU && f == 128) EF_CASE(128, FFN_SWIGLU);
   else if (kind == FFN_GELU && f == 64) EF_CASE(64, FFN_GELU);
