@@ -355,7 +355,7 @@ int dreamer_expert_route(int dtype, int64_t T, int h, int r, int E, int k, int l
 // ------------------------------------------------------------------------ expert FFN
 struct FfnWs {
   int32_t *counts, *goff, *toff, *hist, *perm;
-  float* pgate;  // gates in expert-major order
+  float* pgate;  // gates in expert-major order (tile-padded for the fused FFN)
   int4* tiles;   // m-tile descriptors
   void* slots;
 };
@@ -366,8 +366,10 @@ static FfnWs plan_ffn(Bump& b, int dtype, int64_t T, int h_out, int E, int k) {
   w.goff = b.take_n<int32_t>(E + 1);
   w.toff = b.take_n<int32_t>(E + 1);
   w.hist = b.take_n<int32_t>((size_t)std::max(1, perm_blocks(T * k)) * E);
-  w.perm = b.take_n<int32_t>((size_t)T * k);
-  w.pgate = b.take_n<float>((size_t)T * k);
+  // compact (grouped GEMM) or tile-padded (fused FFN) expert-major order
+  const size_t npad = (size_t)tile_bound(T * k, E, FFN_TILE_M) * FFN_TILE_M;
+  w.perm = b.take_n<int32_t>(npad);
+  w.pgate = b.take_n<float>(npad);
   w.tiles = b.take_n<int4>((size_t)tile_bound(T * k, E, FFN_TILE_M));
   w.slots = b.take((size_t)T * k * h_out * esize(dtype));
   return w;
@@ -397,8 +399,10 @@ static int ffn_slots(int dtype, int kind, int64_t T, int h_in, int f, int h_out,
     return rc ? fail(DREAMER_E_UNSUPPORTED, "expert_ffn: f32 shape unsupported") : ok();
   }
   TB(DREAMER_KC_PERMUTE);
+  const bool fused = kind != DREAMER_FFN_LINEAR;
   int prc = launch_permute(idx, ns, E, FFN_TILE_M, w.hist, w.counts, w.goff, w.toff, w.perm,
-                           st, gate, w.pgate, w.tiles);
+                           st, fused ? gate : nullptr, fused ? w.pgate : nullptr,
+                           fused ? w.tiles : nullptr, fused ? 1 : 0);
   TE(DREAMER_KC_PERMUTE);
   if (prc) return fail(DREAMER_E_UNSUPPORTED, "expert_ffn: E too large for the permutation");
   int rc;

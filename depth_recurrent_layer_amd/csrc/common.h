@@ -119,9 +119,10 @@ DEV void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Runtime count: waits until at most n (clamped to [0, 24]) are outstanding.
+// Runtime count: waits until at most n (clamped to [0, 63], the counter's range) are
+// outstanding.
 DEV void wait_vmcnt_upto(int n) {
-  switch (n < 0 ? 0 : n > 24 ? 24 : n) {
+  switch (n < 0 ? 0 : n > 63 ? 63 : n) {
 #define DREAMER_VM_CASE(N) \
   case N: wait_vmcnt<N>(); break;
     DREAMER_VM_CASE(0) DREAMER_VM_CASE(1) DREAMER_VM_CASE(2) DREAMER_VM_CASE(3)
@@ -130,9 +131,26 @@ DEV void wait_vmcnt_upto(int n) {
     DREAMER_VM_CASE(12) DREAMER_VM_CASE(13) DREAMER_VM_CASE(14) DREAMER_VM_CASE(15)
     DREAMER_VM_CASE(16) DREAMER_VM_CASE(17) DREAMER_VM_CASE(18) DREAMER_VM_CASE(19)
     DREAMER_VM_CASE(20) DREAMER_VM_CASE(21) DREAMER_VM_CASE(22) DREAMER_VM_CASE(23)
-    DREAMER_VM_CASE(24)
+    DREAMER_VM_CASE(24) DREAMER_VM_CASE(25) DREAMER_VM_CASE(26) DREAMER_VM_CASE(27)
+    DREAMER_VM_CASE(28) DREAMER_VM_CASE(29) DREAMER_VM_CASE(30) DREAMER_VM_CASE(31)
+    DREAMER_VM_CASE(32) DREAMER_VM_CASE(33) DREAMER_VM_CASE(34) DREAMER_VM_CASE(35)
+    DREAMER_VM_CASE(36) DREAMER_VM_CASE(37) DREAMER_VM_CASE(38) DREAMER_VM_CASE(39)
+    DREAMER_VM_CASE(40) DREAMER_VM_CASE(41) DREAMER_VM_CASE(42) DREAMER_VM_CASE(43)
+    DREAMER_VM_CASE(44) DREAMER_VM_CASE(45) DREAMER_VM_CASE(46) DREAMER_VM_CASE(47)
+    DREAMER_VM_CASE(48) DREAMER_VM_CASE(49) DREAMER_VM_CASE(50) DREAMER_VM_CASE(51)
+    DREAMER_VM_CASE(52) DREAMER_VM_CASE(53) DREAMER_VM_CASE(54) DREAMER_VM_CASE(55)
+    DREAMER_VM_CASE(56) DREAMER_VM_CASE(57) DREAMER_VM_CASE(58) DREAMER_VM_CASE(59)
+    DREAMER_VM_CASE(60) DREAMER_VM_CASE(61) DREAMER_VM_CASE(62) DREAMER_VM_CASE(63)
 #undef DREAMER_VM_CASE
   }
+}
+
+// One 8-byte global store issued as exactly one instruction (global_store_dwordx2), for
+// code that counts its outstanding vector-memory operations itself: a store is one more
+// operation ahead of the loads issued after it.  Nothing stored this way is read back by
+// the issuing kernel.
+DEV void store_b64_counted(void* p, bf16x4 v) {
+  asm volatile("global_store_dwordx2 %0, %1, off" : : "v"(p), "v"(v) : "memory");
 }
 
 // Workgroup barrier for LDS rings filled by direct global->LDS loads.  __syncthreads()
@@ -159,7 +177,7 @@ DEV uint32_t lds_off(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-// N 16-byte LDS reads (N = 2, 4, 6, 8 or 12) completed within one statement.  Ring stages
+// N 16-byte LDS reads (1 <= N <= 24) completed within one statement.  Ring stages
 // filled by direct global->LDS loads are read this way: for a plain LDS read the
 // compiler cannot tell that it misses the stages still in flight and would wait for
 // every outstanding load first.  The reads are complete when the statement ends, so no
@@ -167,12 +185,24 @@ DEV uint32_t lds_off(const void* p) {
 // visible before).
 template <int N>
 DEV void lds_read_b128(bf16x8 (&x)[N], const uint32_t (&a)[N]) {
-  static_assert(N == 2 || N == 4 || N == 6 || N == 8 || N == 12, "2, 4, 6, 8 or 12 reads");
-  if constexpr (N == 2) {
+  static_assert(N >= 1 && N <= 24, "1 to 24 reads");
+  if constexpr (N == 1) {
+    asm volatile(
+        "ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0])
+        : "v"(a[0])
+        : "memory");
+  } else if constexpr (N == 2) {
     asm volatile(
         "ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
         : "=&v"(x[0]), "=&v"(x[1])
         : "v"(a[0]), "v"(a[1])
+        : "memory");
+  } else if constexpr (N == 3) {
+    asm volatile(
+        "ds_read_b128 %0, %3\n\tds_read_b128 %1, %4\n\tds_read_b128 %2, %5\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2])
         : "memory");
   } else if constexpr (N == 4) {
     asm volatile(
@@ -181,27 +211,30 @@ DEV void lds_read_b128(bf16x8 (&x)[N], const uint32_t (&a)[N]) {
         : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
         : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
         : "memory");
+  } else if constexpr (N == 5) {
+    asm volatile(
+        "ds_read_b128 %0, %5\n\tds_read_b128 %1, %6\n\tds_read_b128 %2, %7\n\t"
+        "ds_read_b128 %3, %8\n\tds_read_b128 %4, %9\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4])
+        : "memory");
   } else if constexpr (N == 6) {
     asm volatile(
         "ds_read_b128 %0, %6\n\tds_read_b128 %1, %7\n\tds_read_b128 %2, %8\n\t"
-        "ds_read_b128 %3, %9\n\tds_read_b128 %4, %10\n\tds_read_b128 %5, %11\n\t"
-        "s_waitcnt lgkmcnt(0)"
+        "ds_read_b128 %3, %9\n\tds_read_b128 %4, %10\n\tds_read_b128 %5, %11\n\ts_waitcnt lgkmcnt(0)"
         : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5])
         : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5])
         : "memory");
-  } else if constexpr (N == 12) {
+  } else if constexpr (N == 7) {
     asm volatile(
-        "ds_read_b128 %0, %12\n\tds_read_b128 %1, %13\n\tds_read_b128 %2, %14\n\t"
-        "ds_read_b128 %3, %15\n\tds_read_b128 %4, %16\n\tds_read_b128 %5, %17\n\t"
-        "ds_read_b128 %6, %18\n\tds_read_b128 %7, %19\n\tds_read_b128 %8, %20\n\t"
-        "ds_read_b128 %9, %21\n\tds_read_b128 %10, %22\n\tds_read_b128 %11, %23\n\t"
-        "s_waitcnt lgkmcnt(0)"
+        "ds_read_b128 %0, %7\n\tds_read_b128 %1, %8\n\tds_read_b128 %2, %9\n\t"
+        "ds_read_b128 %3, %10\n\tds_read_b128 %4, %11\n\tds_read_b128 %5, %12\n\t"
+        "ds_read_b128 %6, %13\n\ts_waitcnt lgkmcnt(0)"
         : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
-          "=&v"(x[6]), "=&v"(x[7]), "=&v"(x[8]), "=&v"(x[9]), "=&v"(x[10]), "=&v"(x[11])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
-          "v"(a[7]), "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11])
+          "=&v"(x[6])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6])
         : "memory");
-  } else {
+  } else if constexpr (N == 8) {
     asm volatile(
         "ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\tds_read_b128 %2, %10\n\t"
         "ds_read_b128 %3, %11\n\tds_read_b128 %4, %12\n\tds_read_b128 %5, %13\n\t"
@@ -210,6 +243,242 @@ DEV void lds_read_b128(bf16x8 (&x)[N], const uint32_t (&a)[N]) {
           "=&v"(x[6]), "=&v"(x[7])
         : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
           "v"(a[7])
+        : "memory");
+  } else if constexpr (N == 9) {
+    asm volatile(
+        "ds_read_b128 %0, %9\n\tds_read_b128 %1, %10\n\tds_read_b128 %2, %11\n\t"
+        "ds_read_b128 %3, %12\n\tds_read_b128 %4, %13\n\tds_read_b128 %5, %14\n\t"
+        "ds_read_b128 %6, %15\n\tds_read_b128 %7, %16\n\tds_read_b128 %8, %17\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+          "=&v"(x[6]), "=&v"(x[7]), "=&v"(x[8])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+          "v"(a[7]), "v"(a[8])
+        : "memory");
+  } else if constexpr (N == 10) {
+    asm volatile(
+        "ds_read_b128 %0, %10\n\tds_read_b128 %1, %11\n\tds_read_b128 %2, %12\n\t"
+        "ds_read_b128 %3, %13\n\tds_read_b128 %4, %14\n\tds_read_b128 %5, %15\n\t"
+        "ds_read_b128 %6, %16\n\tds_read_b128 %7, %17\n\tds_read_b128 %8, %18\n\t"
+        "ds_read_b128 %9, %19\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+          "=&v"(x[6]), "=&v"(x[7]), "=&v"(x[8]), "=&v"(x[9])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+          "v"(a[7]), "v"(a[8]), "v"(a[9])
+        : "memory");
+  } else if constexpr (N == 11) {
+    asm volatile(
+        "ds_read_b128 %0, %11\n\tds_read_b128 %1, %12\n\tds_read_b128 %2, %13\n\t"
+        "ds_read_b128 %3, %14\n\tds_read_b128 %4, %15\n\tds_read_b128 %5, %16\n\t"
+        "ds_read_b128 %6, %17\n\tds_read_b128 %7, %18\n\tds_read_b128 %8, %19\n\t"
+        "ds_read_b128 %9, %20\n\tds_read_b128 %10, %21\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+          "=&v"(x[6]), "=&v"(x[7]), "=&v"(x[8]), "=&v"(x[9]), "=&v"(x[10])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+          "v"(a[7]), "v"(a[8]), "v"(a[9]), "v"(a[10])
+        : "memory");
+  } else if constexpr (N == 12) {
+    asm volatile(
+        "ds_read_b128 %0, %12\n\tds_read_b128 %1, %13\n\tds_read_b128 %2, %14\n\t"
+        "ds_read_b128 %3, %15\n\tds_read_b128 %4, %16\n\tds_read_b128 %5, %17\n\t"
+        "ds_read_b128 %6, %18\n\tds_read_b128 %7, %19\n\tds_read_b128 %8, %20\n\t"
+        "ds_read_b128 %9, %21\n\tds_read_b128 %10, %22\n\tds_read_b128 %11, %23\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+          "=&v"(x[6]), "=&v"(x[7]), "=&v"(x[8]), "=&v"(x[9]), "=&v"(x[10]), "=&v"(x[11])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+          "v"(a[7]), "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11])
+        : "memory");
+  } else if constexpr (N == 13) {
+    asm volatile(
+        "ds_read_b128 %0, %13\n\tds_read_b128 %1, %14\n\tds_read_b128 %2, %15\n\t"
+        "ds_read_b128 %3, %16\n\tds_read_b128 %4, %17\n\tds_read_b128 %5, %18\n\t"
+        "ds_read_b128 %6, %19\n\tds_read_b128 %7, %20\n\tds_read_b128 %8, %21\n\t"
+        "ds_read_b128 %9, %22\n\tds_read_b128 %10, %23\n\tds_read_b128 %11, %24\n\t"
+        "ds_read_b128 %12, %25\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+          "=&v"(x[6]), "=&v"(x[7]), "=&v"(x[8]), "=&v"(x[9]), "=&v"(x[10]), "=&v"(x[11]),
+          "=&v"(x[12])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+          "v"(a[7]), "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12])
+        : "memory");
+  } else if constexpr (N == 14) {
+    asm volatile(
+        "ds_read_b128 %0, %14\n\tds_read_b128 %1, %15\n\tds_read_b128 %2, %16\n\t"
+        "ds_read_b128 %3, %17\n\tds_read_b128 %4, %18\n\tds_read_b128 %5, %19\n\t"
+        "ds_read_b128 %6, %20\n\tds_read_b128 %7, %21\n\tds_read_b128 %8, %22\n\t"
+        "ds_read_b128 %9, %23\n\tds_read_b128 %10, %24\n\tds_read_b128 %11, %25\n\t"
+        "ds_read_b128 %12, %26\n\tds_read_b128 %13, %27\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+          "=&v"(x[6]), "=&v"(x[7]), "=&v"(x[8]), "=&v"(x[9]), "=&v"(x[10]), "=&v"(x[11]),
+          "=&v"(x[12]), "=&v"(x[13])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+          "v"(a[7]), "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13])
+        : "memory");
+  } else if constexpr (N == 15) {
+    asm volatile(
+        "ds_read_b128 %0, %15\n\tds_read_b128 %1, %16\n\tds_read_b128 %2, %17\n\t"
+        "ds_read_b128 %3, %18\n\tds_read_b128 %4, %19\n\tds_read_b128 %5, %20\n\t"
+        "ds_read_b128 %6, %21\n\tds_read_b128 %7, %22\n\tds_read_b128 %8, %23\n\t"
+        "ds_read_b128 %9, %24\n\tds_read_b128 %10, %25\n\tds_read_b128 %11, %26\n\t"
+        "ds_read_b128 %12, %27\n\tds_read_b128 %13, %28\n\tds_read_b128 %14, %29\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+          "=&v"(x[6]), "=&v"(x[7]), "=&v"(x[8]), "=&v"(x[9]), "=&v"(x[10]), "=&v"(x[11]),
+          "=&v"(x[12]), "=&v"(x[13]), "=&v"(x[14])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+          "v"(a[7]), "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]),
+          "v"(a[14])
+        : "memory");
+  } else if constexpr (N == 16) {
+    asm volatile(
+        "ds_read_b128 %0, %16\n\tds_read_b128 %1, %17\n\tds_read_b128 %2, %18\n\t"
+        "ds_read_b128 %3, %19\n\tds_read_b128 %4, %20\n\tds_read_b128 %5, %21\n\t"
+        "ds_read_b128 %6, %22\n\tds_read_b128 %7, %23\n\tds_read_b128 %8, %24\n\t"
+        "ds_read_b128 %9, %25\n\tds_read_b128 %10, %26\n\tds_read_b128 %11, %27\n\t"
+        "ds_read_b128 %12, %28\n\tds_read_b128 %13, %29\n\tds_read_b128 %14, %30\n\t"
+        "ds_read_b128 %15, %31\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+          "=&v"(x[6]), "=&v"(x[7]), "=&v"(x[8]), "=&v"(x[9]), "=&v"(x[10]), "=&v"(x[11]),
+          "=&v"(x[12]), "=&v"(x[13]), "=&v"(x[14]), "=&v"(x[15])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+          "v"(a[7]), "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]),
+          "v"(a[14]), "v"(a[15])
+        : "memory");
+  } else if constexpr (N == 17) {
+    asm volatile(
+        "ds_read_b128 %0, %17\n\tds_read_b128 %1, %18\n\tds_read_b128 %2, %19\n\t"
+        "ds_read_b128 %3, %20\n\tds_read_b128 %4, %21\n\tds_read_b128 %5, %22\n\t"
+        "ds_read_b128 %6, %23\n\tds_read_b128 %7, %24\n\tds_read_b128 %8, %25\n\t"
+        "ds_read_b128 %9, %26\n\tds_read_b128 %10, %27\n\tds_read_b128 %11, %28\n\t"
+        "ds_read_b128 %12, %29\n\tds_read_b128 %13, %30\n\tds_read_b128 %14, %31\n\t"
+        "ds_read_b128 %15, %32\n\tds_read_b128 %16, %33\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+          "=&v"(x[6]), "=&v"(x[7]), "=&v"(x[8]), "=&v"(x[9]), "=&v"(x[10]), "=&v"(x[11]),
+          "=&v"(x[12]), "=&v"(x[13]), "=&v"(x[14]), "=&v"(x[15]), "=&v"(x[16])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+          "v"(a[7]), "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]),
+          "v"(a[14]), "v"(a[15]), "v"(a[16])
+        : "memory");
+  } else if constexpr (N == 18) {
+    asm volatile(
+        "ds_read_b128 %0, %18\n\tds_read_b128 %1, %19\n\tds_read_b128 %2, %20\n\t"
+        "ds_read_b128 %3, %21\n\tds_read_b128 %4, %22\n\tds_read_b128 %5, %23\n\t"
+        "ds_read_b128 %6, %24\n\tds_read_b128 %7, %25\n\tds_read_b128 %8, %26\n\t"
+        "ds_read_b128 %9, %27\n\tds_read_b128 %10, %28\n\tds_read_b128 %11, %29\n\t"
+        "ds_read_b128 %12, %30\n\tds_read_b128 %13, %31\n\tds_read_b128 %14, %32\n\t"
+        "ds_read_b128 %15, %33\n\tds_read_b128 %16, %34\n\tds_read_b128 %17, %35\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+          "=&v"(x[6]), "=&v"(x[7]), "=&v"(x[8]), "=&v"(x[9]), "=&v"(x[10]), "=&v"(x[11]),
+          "=&v"(x[12]), "=&v"(x[13]), "=&v"(x[14]), "=&v"(x[15]), "=&v"(x[16]), "=&v"(x[17])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+          "v"(a[7]), "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]),
+          "v"(a[14]), "v"(a[15]), "v"(a[16]), "v"(a[17])
+        : "memory");
+  } else if constexpr (N == 19) {
+    asm volatile(
+        "ds_read_b128 %0, %19\n\tds_read_b128 %1, %20\n\tds_read_b128 %2, %21\n\t"
+        "ds_read_b128 %3, %22\n\tds_read_b128 %4, %23\n\tds_read_b128 %5, %24\n\t"
+        "ds_read_b128 %6, %25\n\tds_read_b128 %7, %26\n\tds_read_b128 %8, %27\n\t"
+        "ds_read_b128 %9, %28\n\tds_read_b128 %10, %29\n\tds_read_b128 %11, %30\n\t"
+        "ds_read_b128 %12, %31\n\tds_read_b128 %13, %32\n\tds_read_b128 %14, %33\n\t"
+        "ds_read_b128 %15, %34\n\tds_read_b128 %16, %35\n\tds_read_b128 %17, %36\n\t"
+        "ds_read_b128 %18, %37\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+          "=&v"(x[6]), "=&v"(x[7]), "=&v"(x[8]), "=&v"(x[9]), "=&v"(x[10]), "=&v"(x[11]),
+          "=&v"(x[12]), "=&v"(x[13]), "=&v"(x[14]), "=&v"(x[15]), "=&v"(x[16]), "=&v"(x[17]),
+          "=&v"(x[18])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+          "v"(a[7]), "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]),
+          "v"(a[14]), "v"(a[15]), "v"(a[16]), "v"(a[17]), "v"(a[18])
+        : "memory");
+  } else if constexpr (N == 20) {
+    asm volatile(
+        "ds_read_b128 %0, %20\n\tds_read_b128 %1, %21\n\tds_read_b128 %2, %22\n\t"
+        "ds_read_b128 %3, %23\n\tds_read_b128 %4, %24\n\tds_read_b128 %5, %25\n\t"
+        "ds_read_b128 %6, %26\n\tds_read_b128 %7, %27\n\tds_read_b128 %8, %28\n\t"
+        "ds_read_b128 %9, %29\n\tds_read_b128 %10, %30\n\tds_read_b128 %11, %31\n\t"
+        "ds_read_b128 %12, %32\n\tds_read_b128 %13, %33\n\tds_read_b128 %14, %34\n\t"
+        "ds_read_b128 %15, %35\n\tds_read_b128 %16, %36\n\tds_read_b128 %17, %37\n\t"
+        "ds_read_b128 %18, %38\n\tds_read_b128 %19, %39\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+          "=&v"(x[6]), "=&v"(x[7]), "=&v"(x[8]), "=&v"(x[9]), "=&v"(x[10]), "=&v"(x[11]),
+          "=&v"(x[12]), "=&v"(x[13]), "=&v"(x[14]), "=&v"(x[15]), "=&v"(x[16]), "=&v"(x[17]),
+          "=&v"(x[18]), "=&v"(x[19])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+          "v"(a[7]), "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]),
+          "v"(a[14]), "v"(a[15]), "v"(a[16]), "v"(a[17]), "v"(a[18]), "v"(a[19])
+        : "memory");
+  } else if constexpr (N == 21) {
+    asm volatile(
+        "ds_read_b128 %0, %21\n\tds_read_b128 %1, %22\n\tds_read_b128 %2, %23\n\t"
+        "ds_read_b128 %3, %24\n\tds_read_b128 %4, %25\n\tds_read_b128 %5, %26\n\t"
+        "ds_read_b128 %6, %27\n\tds_read_b128 %7, %28\n\tds_read_b128 %8, %29\n\t"
+        "ds_read_b128 %9, %30\n\tds_read_b128 %10, %31\n\tds_read_b128 %11, %32\n\t"
+        "ds_read_b128 %12, %33\n\tds_read_b128 %13, %34\n\tds_read_b128 %14, %35\n\t"
+        "ds_read_b128 %15, %36\n\tds_read_b128 %16, %37\n\tds_read_b128 %17, %38\n\t"
+        "ds_read_b128 %18, %39\n\tds_read_b128 %19, %40\n\tds_read_b128 %20, %41\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+          "=&v"(x[6]), "=&v"(x[7]), "=&v"(x[8]), "=&v"(x[9]), "=&v"(x[10]), "=&v"(x[11]),
+          "=&v"(x[12]), "=&v"(x[13]), "=&v"(x[14]), "=&v"(x[15]), "=&v"(x[16]), "=&v"(x[17]),
+          "=&v"(x[18]), "=&v"(x[19]), "=&v"(x[20])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+          "v"(a[7]), "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]),
+          "v"(a[14]), "v"(a[15]), "v"(a[16]), "v"(a[17]), "v"(a[18]), "v"(a[19]), "v"(a[20])
+        : "memory");
+  } else if constexpr (N == 22) {
+    asm volatile(
+        "ds_read_b128 %0, %22\n\tds_read_b128 %1, %23\n\tds_read_b128 %2, %24\n\t"
+        "ds_read_b128 %3, %25\n\tds_read_b128 %4, %26\n\tds_read_b128 %5, %27\n\t"
+        "ds_read_b128 %6, %28\n\tds_read_b128 %7, %29\n\tds_read_b128 %8, %30\n\t"
+        "ds_read_b128 %9, %31\n\tds_read_b128 %10, %32\n\tds_read_b128 %11, %33\n\t"
+        "ds_read_b128 %12, %34\n\tds_read_b128 %13, %35\n\tds_read_b128 %14, %36\n\t"
+        "ds_read_b128 %15, %37\n\tds_read_b128 %16, %38\n\tds_read_b128 %17, %39\n\t"
+        "ds_read_b128 %18, %40\n\tds_read_b128 %19, %41\n\tds_read_b128 %20, %42\n\t"
+        "ds_read_b128 %21, %43\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+          "=&v"(x[6]), "=&v"(x[7]), "=&v"(x[8]), "=&v"(x[9]), "=&v"(x[10]), "=&v"(x[11]),
+          "=&v"(x[12]), "=&v"(x[13]), "=&v"(x[14]), "=&v"(x[15]), "=&v"(x[16]), "=&v"(x[17]),
+          "=&v"(x[18]), "=&v"(x[19]), "=&v"(x[20]), "=&v"(x[21])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+          "v"(a[7]), "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]),
+          "v"(a[14]), "v"(a[15]), "v"(a[16]), "v"(a[17]), "v"(a[18]), "v"(a[19]), "v"(a[20]),
+          "v"(a[21])
+        : "memory");
+  } else if constexpr (N == 23) {
+    asm volatile(
+        "ds_read_b128 %0, %23\n\tds_read_b128 %1, %24\n\tds_read_b128 %2, %25\n\t"
+        "ds_read_b128 %3, %26\n\tds_read_b128 %4, %27\n\tds_read_b128 %5, %28\n\t"
+        "ds_read_b128 %6, %29\n\tds_read_b128 %7, %30\n\tds_read_b128 %8, %31\n\t"
+        "ds_read_b128 %9, %32\n\tds_read_b128 %10, %33\n\tds_read_b128 %11, %34\n\t"
+        "ds_read_b128 %12, %35\n\tds_read_b128 %13, %36\n\tds_read_b128 %14, %37\n\t"
+        "ds_read_b128 %15, %38\n\tds_read_b128 %16, %39\n\tds_read_b128 %17, %40\n\t"
+        "ds_read_b128 %18, %41\n\tds_read_b128 %19, %42\n\tds_read_b128 %20, %43\n\t"
+        "ds_read_b128 %21, %44\n\tds_read_b128 %22, %45\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+          "=&v"(x[6]), "=&v"(x[7]), "=&v"(x[8]), "=&v"(x[9]), "=&v"(x[10]), "=&v"(x[11]),
+          "=&v"(x[12]), "=&v"(x[13]), "=&v"(x[14]), "=&v"(x[15]), "=&v"(x[16]), "=&v"(x[17]),
+          "=&v"(x[18]), "=&v"(x[19]), "=&v"(x[20]), "=&v"(x[21]), "=&v"(x[22])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+          "v"(a[7]), "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]),
+          "v"(a[14]), "v"(a[15]), "v"(a[16]), "v"(a[17]), "v"(a[18]), "v"(a[19]), "v"(a[20]),
+          "v"(a[21]), "v"(a[22])
+        : "memory");
+  } else if constexpr (N == 24) {
+    asm volatile(
+        "ds_read_b128 %0, %24\n\tds_read_b128 %1, %25\n\tds_read_b128 %2, %26\n\t"
+        "ds_read_b128 %3, %27\n\tds_read_b128 %4, %28\n\tds_read_b128 %5, %29\n\t"
+        "ds_read_b128 %6, %30\n\tds_read_b128 %7, %31\n\tds_read_b128 %8, %32\n\t"
+        "ds_read_b128 %9, %33\n\tds_read_b128 %10, %34\n\tds_read_b128 %11, %35\n\t"
+        "ds_read_b128 %12, %36\n\tds_read_b128 %13, %37\n\tds_read_b128 %14, %38\n\t"
+        "ds_read_b128 %15, %39\n\tds_read_b128 %16, %40\n\tds_read_b128 %17, %41\n\t"
+        "ds_read_b128 %18, %42\n\tds_read_b128 %19, %43\n\tds_read_b128 %20, %44\n\t"
+        "ds_read_b128 %21, %45\n\tds_read_b128 %22, %46\n\tds_read_b128 %23, %47\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+          "=&v"(x[6]), "=&v"(x[7]), "=&v"(x[8]), "=&v"(x[9]), "=&v"(x[10]), "=&v"(x[11]),
+          "=&v"(x[12]), "=&v"(x[13]), "=&v"(x[14]), "=&v"(x[15]), "=&v"(x[16]), "=&v"(x[17]),
+          "=&v"(x[18]), "=&v"(x[19]), "=&v"(x[20]), "=&v"(x[21]), "=&v"(x[22]), "=&v"(x[23])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+          "v"(a[7]), "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]),
+          "v"(a[14]), "v"(a[15]), "v"(a[16]), "v"(a[17]), "v"(a[18]), "v"(a[19]), "v"(a[20]),
+          "v"(a[21]), "v"(a[22]), "v"(a[23])
         : "memory");
   }
 }

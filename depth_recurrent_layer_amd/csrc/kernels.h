@@ -114,13 +114,15 @@ void launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st);
 // = slot id t*k+i of the j-th slot routed to e; order within an expert unspecified).
 // Optional: pgate [nslots] = gate in the same order (gate given), and tiles
 // [tile_bound(nslots, E, tile_m)] = {expert, first row, end of the expert's rows, 0} per
-// m-tile (the first toff[E] entries are written).
+// m-tile (the first toff[E] entries are written).  pad: perm and pgate are tile-padded
+// instead ([tile_bound * tile_m]: row j of m-tile t at t * tile_m + j; the rows past an
+// expert's end in its last tile are left unwritten).
 constexpr int PERM_CHUNK = 2048, PERM_MAX_E = 8192, COUNT_MAX_E = 16384;
 int perm_blocks(int64_t nslots);
 int launch_permute(const int32_t* idx, int64_t nslots, int E, int tile_m, int32_t* hist,
                    int32_t* counts, int32_t* goff, int32_t* toff, int32_t* perm,
                    hipStream_t st, const float* gate = nullptr, float* pgate = nullptr,
-                   int4* tiles = nullptr);
+                   int4* tiles = nullptr, int pad = 0);
 inline int64_t tile_bound(int64_t nslots, int E, int tile_m) { return nslots / tile_m + E + 1; }
 // counts [E] of routed slots per expert (hist as above).
 int launch_counts(const int32_t* idx, int64_t nslots, int E, int32_t* hist, int32_t* counts,

@@ -21,7 +21,9 @@ namespace dreamer {
 
 // ------------------------------------------------------------------ scores (bf16, MFMA)
 // u tile [16 tokens x r] of the block's tokens, rotated by depth, split into three bf16
-// parts as MFMA A operands (token lr, k-group lg).  us / ur: 2 * 16 * r floats of LDS.
+// parts as MFMA A operands (token lr, k-group lg).  us / ur: 2 * 16 * (r + 4) floats of
+// LDS; rows are padded by 4 floats so that the 16 rows of a fragment read (and of the
+// projection's stores) start in distinct banks.
 // r divides 256, so each thread rotates one rank index i = tid % r (one table entry,
 // loaded before the projection).
 template <int NKS>
@@ -57,21 +59,24 @@ DEV void router_u_parts(int64_t Ttok, int64_t t0, int h, int r, int l, int L,
       for (int j = 0; j < 8; ++j) acc = mfma16(af[j], bf[j], acc);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) us[(lg * 4 + i) * r + nt * 16 + lr] = acc[i];
+    for (int i = 0; i < 4; ++i) us[(lg * 4 + i) * (r + 4) + nt * 16 + lr] = acc[i];
   }
   __syncthreads();
   const int ip = i < half ? i + half : i - half;
   for (int e = tid; e < 16 * r; e += 256) {
     const int t = e / r;
-    const float a = us[t * r + i], b = us[t * r + ip];
-    ur[e] = i < half ? a * cv - b * sv : a * cv + b * sv;
+    const float a = us[t * (r + 4) + i], b = us[t * (r + 4) + ip];
+    ur[t * (r + 4) + i] = i < half ? a * cv - b * sv : a * cv + b * sv;
   }
   __syncthreads();
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
+    const float4* src = reinterpret_cast<const float4*>(ur + lr * (r + 4) + ks * 32 + lg * 8);
+    const float4 q0 = src[0], q1 = src[1];
+    const float uv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float v = ur[lr * r + ks * 32 + lg * 8 + j];
+      const float v = uv[j];
       const bf16 hi = (bf16)v;
       const float r1 = v - (float)hi;
       const bf16 mid = (bf16)r1;
@@ -125,8 +130,8 @@ __global__ __launch_bounds__(256) void router_scores_bf16_kernel(
   for (int j = 0; j < 4; ++j)
     if (et0 + w + 4 * j < et1) load_keys<NKS>(keys, r, et0 + w + 4 * j, kf[j]);
   bf16x8 ah[NKS], am[NKS], al[NKS];
-  router_u_parts<NKS>(Ttok, t0, h, r, l, L, x, ldx, w_r, cs, sn, smem, smem + 16 * r, ah, am,
-                      al);
+  router_u_parts<NKS>(Ttok, t0, h, r, l, L, x, ldx, w_r, cs, sn, smem, smem + 16 * (r + 4), ah,
+                      am, al);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int et = et0 + w + 4 * j;
@@ -169,7 +174,9 @@ DEV void list_insert(float (&lv)[KMAX], float (&lz)[KMAX], int (&li)[KMAX], floa
 // per token scan them, each keeping a sorted list of its best (z + b, z, e); k rounds of
 // a 16-lane butterfly argmax pick the winners.  Gates sigmoid(z), normalised on request
 // by their sum taken in selection order.
-constexpr int RCH = 256, RCH_LD = RCH + 16;
+// score rows padded to RCH + 20 floats: a wave's stores of 4 x 16 fragment rows and its
+// 4 x 16-lane row scans both spread over the banks (at most 2-way on the scans)
+constexpr int RCH = 256, RCH_LD = RCH + 20;
 
 template <int NKS, int KMAX>
 __global__ __launch_bounds__(256) void router_fused_bf16_kernel(
@@ -179,7 +186,7 @@ __global__ __launch_bounds__(256) void router_fused_bf16_kernel(
     const float* __restrict__ sn, const int32_t* __restrict__ idx_in, int32_t* __restrict__ idx,
     float* __restrict__ gate) {
   extern __shared__ float smem[];
-  float* zs = smem + 32 * r;      // [16][RCH_LD]
+  float* zs = smem + 32 * (r + 4);  // [16][RCH_LD]
   float* bs = zs + 16 * RCH_LD;   // [RCH] bias chunk
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
   const int64_t t0 = (int64_t)blockIdx.x * 16;
@@ -191,8 +198,8 @@ __global__ __launch_bounds__(256) void router_fused_bf16_kernel(
     if (w + 4 * j < n / 16) load_keys<NKS>(keys, r, w + 4 * j, kf[j]);
   if (tid < n) bs[tid] = bias[tid];
   bf16x8 ah[NKS], am[NKS], al[NKS];
-  router_u_parts<NKS>(Ttok, t0, h, r, l, L, x, ldx, w_r, cs, sn, smem, smem + 16 * r, ah, am,
-                      al);
+  router_u_parts<NKS>(Ttok, t0, h, r, l, L, x, ldx, w_r, cs, sn, smem, smem + 16 * (r + 4), ah,
+                      am, al);
   const int tl = w * 4 + (lane >> 4), g = lane & 15;
   const int64_t t = t0 + tl;
   float lv[KMAX], lz[KMAX];
@@ -359,7 +366,7 @@ int router_scores(int dtype, int64_t T, int h, int r, int E, int l, int L, const
   if (dtype == DT_BF16) {
     if (r % 32 || r > 256 || E % 16 || h % 32) return -1;
     const dim3 grid((unsigned)((T + 15) / 16), (unsigned)((E + RCH - 1) / RCH));
-    const size_t lds = 2 * 16 * r * sizeof(float);
+    const size_t lds = 2 * 16 * (r + 4) * sizeof(float);
 #define RS_CASE(NK)                                                                      \
   router_scores_bf16_kernel<NK><<<grid, 256, lds, st>>>(T, h, r, E, l, L, (const bf16*)x, \
                                                         ldx, (const bf16*)w_r,            \
@@ -409,7 +416,7 @@ int router_route_fused(int64_t T, int h, int r, int E, int k, int l, int L, cons
   if (T <= 0) return 0;
   if (!router_fused_ok(DT_BF16, T, r, E, k) || h % 32) return -1;
   const unsigned grid = (unsigned)((T + 15) / 16);
-  const size_t lds = (2 * 16 * r + 16 * RCH_LD + RCH) * sizeof(float);
+  const size_t lds = (2 * 16 * (r + 4) + 16 * RCH_LD + RCH) * sizeof(float);
 #define RF_CASE(NK, KM)                                                                     \
   router_fused_bf16_kernel<NK, KM><<<grid, 256, lds, st>>>(                                 \
       T, h, r, E, k, l, L, (const bf16*)x, ldx, (const bf16*)w_r, (const bf16*)keys, bias,  \
@@ -468,8 +475,9 @@ __global__ __launch_bounds__(512) void perm_hist_kernel(const int32_t* __restric
 // contiguous range of experts; a wavefront scan (lane shuffles) plus one pass over the
 // wave totals gives each range its first row and first m-tile.  base[e] becomes e's
 // first row plus prev[e] (the rows of e in earlier chunks, or nullptr); with pub,
-// counts / goff / toff and the tile descriptors are written.  s_wave: 32 ints.
-DEV void expert_offsets(int* base, const int* prev, int E, int tile_m, bool pub,
+// counts / goff / toff and the tile descriptors are written; with pad, prev[e] becomes
+// the shift from e's compact positions to its tile-padded ones.  s_wave: 32 ints.
+DEV void expert_offsets(int* base, int* prev, int E, int tile_m, bool pub, bool pad,
                         int32_t* __restrict__ counts, int32_t* __restrict__ goff,
                         int32_t* __restrict__ toff, int4* __restrict__ tiles, int* s_wave) {
   const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, w = tid >> 6;
@@ -513,6 +521,7 @@ DEV void expert_offsets(int* base, const int* prev, int E, int tile_m, bool pub,
         for (int q = 0; q * tile_m < tot; ++q) tiles[tt + q] = make_int4(e, rr + q * tile_m, rr + tot, 0);
     }
     base[e] = rr + (prev ? prev[e] : 0);
+    if (pad) prev[e] = tt * tile_m - rr;
     rr += tot;
     tt += (tot + tile_m - 1) / tile_m;
   }
@@ -525,14 +534,16 @@ DEV void expert_offsets(int* base, const int* prev, int E, int tile_m, bool pub,
 
 // One block of PERM_THREADS per chunk: the chunk's experts and gates are loaded first
 // (their latency overlaps the histogram reads), then the totals and the rows of each
-// expert in earlier chunks, the offsets, and the scatter from registers.
+// expert in earlier chunks, the offsets, and the scatter from registers.  pad: slot ids
+// and gates go to tile-padded positions (m-tile t of the expert-major order owns
+// positions t * tile_m ..), the layout the expert FFN reads per tile.
 constexpr int PERM_THREADS = 512, PERM_PER = PERM_CHUNK / PERM_THREADS;
 
 __global__ __launch_bounds__(PERM_THREADS) void perm_scatter_kernel(
     const int32_t* __restrict__ idx, int64_t nslots, int E, int nb, int tile_m,
     const int32_t* __restrict__ hist, int32_t* __restrict__ counts, int32_t* __restrict__ goff,
     int32_t* __restrict__ toff, int32_t* __restrict__ perm, const float* __restrict__ gate,
-    float* __restrict__ pgate, int4* __restrict__ tiles) {
+    float* __restrict__ pgate, int4* __restrict__ tiles, int pad) {
   extern __shared__ int sh[];  // base [E] (totals, then cursors), prev [E]
   int* base = sh;
   int* prev = sh + E;
@@ -558,11 +569,11 @@ __global__ __launch_bounds__(PERM_THREADS) void perm_scatter_kernel(
     prev[e] = pre;
   }
   __syncthreads();
-  expert_offsets(base, prev, E, tile_m, b == 0, counts, goff, toff, tiles, s_wave);
+  expert_offsets(base, prev, E, tile_m, b == 0, pad != 0, counts, goff, toff, tiles, s_wave);
 #pragma unroll
   for (int j = 0; j < PERM_PER; ++j)
     if (ex[j] >= 0) {
-      const int pos = atomicAdd(&base[ex[j]], 1);
+      const int pos = atomicAdd(&base[ex[j]], 1) + (pad ? prev[ex[j]] : 0);
       perm[pos] = (int32_t)(s0 + j * PERM_THREADS + tid);
       if (pgate) pgate[pos] = gv[j];
     }
@@ -579,14 +590,14 @@ __global__ void hist_colsum_kernel(const int32_t* __restrict__ hist, int nb, int
 
 int launch_permute(const int32_t* idx, int64_t nslots, int E, int tile_m, int32_t* hist,
                    int32_t* counts, int32_t* goff, int32_t* toff, int32_t* perm,
-                   hipStream_t st, const float* gate, float* pgate, int4* tiles) {
+                   hipStream_t st, const float* gate, float* pgate, int4* tiles, int pad) {
   if (E <= 0 || E > PERM_MAX_E) return -1;
   const size_t lds = (size_t)E * sizeof(int);
   const int nb = perm_blocks(nslots);
   perm_hist_kernel<<<nb, 512, lds, st>>>(idx, nslots, E, hist);
   perm_scatter_kernel<<<nb, PERM_THREADS, 2 * lds, st>>>(idx, nslots, E, nb, tile_m, hist,
                                                          counts, goff, toff, perm, gate, pgate,
-                                                         tiles);
+                                                         tiles, pad);
   return 0;
 }
 
