@@ -120,30 +120,18 @@ DEV void wait_vmcnt() {
 }
 
 // Runtime count: waits until at most n (clamped to [0, 63], the counter's range) are
-// outstanding.
-DEV void wait_vmcnt_upto(int n) {
-  switch (n < 0 ? 0 : n > 63 ? 63 : n) {
-#define DREAMER_VM_CASE(N) \
-  case N: wait_vmcnt<N>(); break;
-    DREAMER_VM_CASE(0) DREAMER_VM_CASE(1) DREAMER_VM_CASE(2) DREAMER_VM_CASE(3)
-    DREAMER_VM_CASE(4) DREAMER_VM_CASE(5) DREAMER_VM_CASE(6) DREAMER_VM_CASE(7)
-    DREAMER_VM_CASE(8) DREAMER_VM_CASE(9) DREAMER_VM_CASE(10) DREAMER_VM_CASE(11)
-    DREAMER_VM_CASE(12) DREAMER_VM_CASE(13) DREAMER_VM_CASE(14) DREAMER_VM_CASE(15)
-    DREAMER_VM_CASE(16) DREAMER_VM_CASE(17) DREAMER_VM_CASE(18) DREAMER_VM_CASE(19)
-    DREAMER_VM_CASE(20) DREAMER_VM_CASE(21) DREAMER_VM_CASE(22) DREAMER_VM_CASE(23)
-    DREAMER_VM_CASE(24) DREAMER_VM_CASE(25) DREAMER_VM_CASE(26) DREAMER_VM_CASE(27)
-    DREAMER_VM_CASE(28) DREAMER_VM_CASE(29) DREAMER_VM_CASE(30) DREAMER_VM_CASE(31)
-    DREAMER_VM_CASE(32) DREAMER_VM_CASE(33) DREAMER_VM_CASE(34) DREAMER_VM_CASE(35)
-    DREAMER_VM_CASE(36) DREAMER_VM_CASE(37) DREAMER_VM_CASE(38) DREAMER_VM_CASE(39)
-    DREAMER_VM_CASE(40) DREAMER_VM_CASE(41) DREAMER_VM_CASE(42) DREAMER_VM_CASE(43)
-    DREAMER_VM_CASE(44) DREAMER_VM_CASE(45) DREAMER_VM_CASE(46) DREAMER_VM_CASE(47)
-    DREAMER_VM_CASE(48) DREAMER_VM_CASE(49) DREAMER_VM_CASE(50) DREAMER_VM_CASE(51)
-    DREAMER_VM_CASE(52) DREAMER_VM_CASE(53) DREAMER_VM_CASE(54) DREAMER_VM_CASE(55)
-    DREAMER_VM_CASE(56) DREAMER_VM_CASE(57) DREAMER_VM_CASE(58) DREAMER_VM_CASE(59)
-    DREAMER_VM_CASE(60) DREAMER_VM_CASE(61) DREAMER_VM_CASE(62) DREAMER_VM_CASE(63)
-#undef DREAMER_VM_CASE
+// outstanding; a binary search over the immediate forms (six compares).
+template <int LO, int HI>
+DEV void wait_vmcnt_range(int n) {
+  if constexpr (LO == HI) {
+    wait_vmcnt<LO>();
+  } else {
+    constexpr int MID = (LO + HI) / 2;
+    if (n <= MID) wait_vmcnt_range<LO, MID>(n);
+    else wait_vmcnt_range<MID + 1, HI>(n);
   }
 }
+DEV void wait_vmcnt_upto(int n) { wait_vmcnt_range<0, 63>(n < 0 ? 0 : n > 63 ? 63 : n); }
 
 // One 8-byte global store issued as exactly one instruction (global_store_dwordx2), for
 // code that counts its outstanding vector-memory operations itself: a store is one more
