@@ -77,7 +77,7 @@ def stored_traffic(kclass, workload):
     except (IndexError, ValueError):
         return None
     from depth_recurrent_layer_amd.profiling import source_digest
-    if blob.get("source_sha256") != source_digest():
+    if blob.get("source_sha256") != source_digest(kclass):
         return None
     return blob["bytes_per_launch"]
 

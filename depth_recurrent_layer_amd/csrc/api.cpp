@@ -137,8 +137,11 @@ int dreamer_timing_enable(int kclass, int max_launches) {
     return fail(DREAMER_E_INVAL, "timing_enable: bad class or count");
   g_tm.ev0.resize(max_launches);
   g_tm.ev1.resize(max_launches);
+  // timing-only events: no system-scope fence (cache writeback) at each record, which
+  // would both inflate and perturb the bracketed launch
   for (int i = 0; i < max_launches; ++i) {
-    if (hipEventCreate(&g_tm.ev0[i]) != hipSuccess || hipEventCreate(&g_tm.ev1[i]) != hipSuccess)
+    if (hipEventCreateWithFlags(&g_tm.ev0[i], hipEventDisableSystemFence) != hipSuccess ||
+        hipEventCreateWithFlags(&g_tm.ev1[i], hipEventDisableSystemFence) != hipSuccess)
       return fail(DREAMER_E_HIP, "timing_enable: hipEventCreate failed");
   }
   g_tm.max = max_launches;

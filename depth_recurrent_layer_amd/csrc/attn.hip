@@ -43,7 +43,7 @@ void launch_rope_jobs(const RopeJobs& jobs, hipStream_t st) {
   for (int q = 0; q < jobs.n; ++q)
     n += (int64_t)jobs.j[q].npos * (jobs.j[q].t4 ? 16 : jobs.j[q].D / 2);
   if (n <= 0) return;
-  rope_jobs_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(jobs);
+  dlaunch(rope_jobs_kernel, (unsigned)((n + 255) / 256), 256, 0, st, jobs);
 }
 
 void launch_rope_tables(int D, int npos, double base, float* c, float* s, hipStream_t st) {
@@ -158,7 +158,7 @@ int launch_depth_attn(int dtype, int64_t rows, int H, int d, int l, int L, const
   if (threads <= 0) return 0;
   const unsigned grid = (unsigned)((threads + 255) / 256);
 #define DA_LAUNCH(T, LP, R)                                                              \
-  depth_attn_kernel<T, LP, R><<<grid, 256, 0, st>>>(                                     \
+  dlaunch(depth_attn_kernel<T, LP, R>, grid, 256, 0, st,                                      \
       rows, H, d, l, L, (const T*)q, ldq, (const T*)kn, ldk, (const T*)vn, ldv, (T*)kc, \
       (T*)vc, (T*)out, ldo, cosd, sind, scale, window, dilation)
 #define DA_CASE(T, LP)                 \
@@ -230,7 +230,7 @@ int launch_qkv_rope(int dtype, int64_t rows, int H, int d, int seq, int pos_fixe
   if (threads <= 0) return 0;
   const unsigned grid = (unsigned)((threads + 255) / 256);
 #define QR_CASE(T, LP)                                                                   \
-  qkv_rope_kernel<T, LP><<<grid, 256, 0, st>>>(rows, H, d, seq, pos_fixed, sa_rope, l, L, \
+  dlaunch(qkv_rope_kernel<T, LP>, grid, 256, 0, st, rows, H, d, seq, pos_fixed, sa_rope, l, L, \
                                                (T*)qkv, cs, sn, cd, sd);                 \
   break;
   if (dtype == DT_BF16) {
@@ -616,7 +616,7 @@ static int sa_rope_store(int lph, int B, int n, int H, int d, int64_t pos0, cons
   const int64_t threads = (int64_t)B * n * (H * d / VEC);
   const unsigned grid = (unsigned)((threads + 255) / 256);
 #define RS_CASE(LP)                                                                  \
-  sa_rope_store_kernel<T, LP><<<grid, 256, 0, st>>>(B, n, H, d, pos0, (const T*)kn, \
+  dlaunch(sa_rope_store_kernel<T, LP>, grid, 256, 0, st, B, n, H, d, pos0, (const T*)kn, \
                                                     ldk, (const T*)vn, ldv, (T*)dk,  \
                                                     (T*)dv, cap, cs, sn, rope)
   switch (lph) {
@@ -641,7 +641,7 @@ static int sa_rows(int lph, int B, int n, int H, int d, int64_t pos0, const void
   if (blk > 1024) return -1;
   dim3 grid(nsplit, (unsigned)((int64_t)B * n));
 #define SR_CASE(LP)                                                                    \
-  sa_rows_kernel<T, LP><<<grid, blk, 0, st>>>(B, n, H, d, pos0, (const T*)q, ldq,      \
+  dlaunch(sa_rows_kernel<T, LP>, grid, blk, 0, st, B, n, H, d, pos0, (const T*)q, ldq,      \
                                               (const T*)kb, (const T*)vb, cap, (T*)out, \
                                               ldo, cs, sn, rope, scale, nsplit, span, pa, pm)
   switch (lph) {
@@ -654,7 +654,7 @@ static int sa_rows(int lph, int B, int n, int H, int d, int64_t pos0, const void
 #undef SR_CASE
   if (nsplit > 1) {
     const int64_t tot = (int64_t)B * n * H * d;
-    sa_combine_kernel<T><<<(unsigned)((tot + 255) / 256), 256, 0, st>>>(
+    dlaunch(sa_combine_kernel<T>, (unsigned)((tot + 255) / 256), 256, 0, st,
         (int64_t)B * n, H, d, nsplit, pa, pm, (T*)out, ldo);
   }
   return 0;
@@ -703,7 +703,7 @@ int launch_seq_attn(int dtype, int B, int q_len, int H, int d, int64_t pos0, con
       bf16* kr = qr + (size_t)B * q_len * h;
       bf16* vtt = kr + (size_t)B * q_len * h;
       const int64_t units = (int64_t)B * q_len * H * 4;
-      sa_prep_kernel<<<(unsigned)((units + 255) / 256), 256, 0, st>>>(
+      dlaunch(sa_prep_kernel, (unsigned)((units + 255) / 256), 256, 0, st,
           B, q_len, H, (const bf16*)q, ldq, (const bf16*)kn, ldk, (const bf16*)vn, ldv, qr,
           kr, vtt, cos_s, sin_s, rope);
       fq = qr;
@@ -712,7 +712,7 @@ int launch_seq_attn(int dtype, int B, int q_len, int H, int d, int64_t pos0, con
       fldq = fldk = h;
     }
     dim3 grid((q_len + fa::BQ - 1) / fa::BQ, H, B);
-    sa_flash_kernel<<<grid, 256, 0, st>>>(B, q_len, H, fq, fldq, fk, fldk, fvt, (bf16*)out,
+    dlaunch(sa_flash_kernel, grid, 256, 0, st, B, q_len, H, fq, fldq, fk, fldk, fvt, (bf16*)out,
                                           ldo, scale);
     return 0;
   }

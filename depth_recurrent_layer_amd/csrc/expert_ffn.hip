@@ -252,7 +252,7 @@ int launch_expert_ffn(int dtype, int kind, int64_t nslots, int k, int h_in, int 
   const int64_t cap = tile_bound(nslots, E, FFN_TILE_M);
   const unsigned grid = (unsigned)((cap + 7) / 8 * 8);
 #define EF_CASE(FF, KK)                                                                     \
-  expert_ffn_kernel<FF, KK><<<grid, 256, 0, st>>>(k, h_in, h_out, (const bf16*)x,           \
+  dlaunch(expert_ffn_kernel<FF, KK>, grid, 256, 0, st, k, h_in, h_out, (const bf16*)x,           \
                                                   (const bf16*)w1, (const bf16*)w3,         \
                                                   (const bf16*)w2, perm, pgate, tiles,      \
                                                   (int)cap, toff + E, (bf16*)slots)

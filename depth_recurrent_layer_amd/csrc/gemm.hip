@@ -363,7 +363,7 @@ int launch_gemm(const GemmArgs& a, int dtype, int out_f32, hipStream_t st) {
   if (a.M <= 0 || a.N <= 0) return 0;
   if (dtype == DT_F32) {
     dim3 grid((a.N + 15) / 16, (a.M + 15) / 16);
-    gemm_f32_kernel<<<grid, 256, 0, st>>>(a);
+    dlaunch(gemm_f32_kernel, grid, 256, 0, st, a);
     return 0;
   }
   if (a.K % 32 != 0 || a.N % 8 != 0) return -1;
@@ -382,13 +382,13 @@ int launch_gemm(const GemmArgs& a, int dtype, int out_f32, hipStream_t st) {
     if (a.toff && a.tile_m != 64) return -1;
     if (a.toff || tiles(128, 128) < 256) {
       if (k64)
-        gemm_bf16_kernel<bf16, GemmCfg<32, 64, 2, 2, 128, 3, 2, false>><<<grid_of(64, 128), 256, 0, st>>>(a);
+        dlaunch(gemm_bf16_kernel<bf16, GemmCfg<32, 64, 2, 2, 128, 3, 2, false>>, grid_of(64, 128), 256, 0, st, a);
       else
-        gemm_bf16_kernel<bf16, GemmCfg<32, 64, 2, 2, 64, 5, 2, false>><<<grid_of(64, 128), 256, 0, st>>>(a);
+        dlaunch(gemm_bf16_kernel<bf16, GemmCfg<32, 64, 2, 2, 64, 5, 2, false>>, grid_of(64, 128), 256, 0, st, a);
     } else if (k64) {
-      gemm_bf16_kernel<bf16, GemmCfg<32, 64, 4, 2, 128, 2, 2, true>><<<grid_of(128, 128), 512, 0, st>>>(a);
+      dlaunch(gemm_bf16_kernel<bf16, GemmCfg<32, 64, 4, 2, 128, 2, 2, true>>, grid_of(128, 128), 512, 0, st, a);
     } else {
-      gemm_bf16_kernel<bf16, GemmCfg<64, 64, 2, 2, 64, 3, 3, true>><<<grid_of(128, 128), 256, 0, st>>>(a);
+      dlaunch(gemm_bf16_kernel<bf16, GemmCfg<64, 64, 2, 2, 64, 3, 3, true>>, grid_of(128, 128), 256, 0, st, a);
     }
     return 0;
   }
@@ -405,14 +405,14 @@ int launch_gemm(const GemmArgs& a, int dtype, int out_f32, hipStream_t st) {
   }
 #define DREAMER_GEMM_LAUNCH(OUT)                                                               \
   if (bm == 128) {                                                                            \
-    if (k64) gemm_bf16_kernel<OUT, GemmCfg<64, 64, 2, 2, 128, 2, 2, false>><<<grid_of(128, 128), 256, 0, st>>>(a); \
-    else gemm_bf16_kernel<OUT, GemmCfg<64, 64, 2, 2, 64, 4, 2, false>><<<grid_of(128, 128), 256, 0, st>>>(a);      \
+    if (k64) dlaunch(gemm_bf16_kernel<OUT, GemmCfg<64, 64, 2, 2, 128, 2, 2, false>>, grid_of(128, 128), 256, 0, st, a); \
+    else dlaunch(gemm_bf16_kernel<OUT, GemmCfg<64, 64, 2, 2, 64, 4, 2, false>>, grid_of(128, 128), 256, 0, st, a);      \
   } else if (bnn == 128) {                                                                    \
-    if (k64) gemm_bf16_kernel<OUT, GemmCfg<32, 64, 2, 2, 128, 3, 2, false>><<<grid_of(64, 128), 256, 0, st>>>(a);  \
-    else gemm_bf16_kernel<OUT, GemmCfg<32, 64, 2, 2, 64, 5, 2, false>><<<grid_of(64, 128), 256, 0, st>>>(a);       \
+    if (k64) dlaunch(gemm_bf16_kernel<OUT, GemmCfg<32, 64, 2, 2, 128, 3, 2, false>>, grid_of(64, 128), 256, 0, st, a);  \
+    else dlaunch(gemm_bf16_kernel<OUT, GemmCfg<32, 64, 2, 2, 64, 5, 2, false>>, grid_of(64, 128), 256, 0, st, a);       \
   } else {                                                                                    \
-    if (k64) gemm_bf16_kernel<OUT, GemmCfg<32, 32, 2, 2, 128, 4, 2, false>><<<grid_of(64, 64), 256, 0, st>>>(a);   \
-    else gemm_bf16_kernel<OUT, GemmCfg<32, 32, 2, 2, 64, 8, 2, false>><<<grid_of(64, 64), 256, 0, st>>>(a);        \
+    if (k64) dlaunch(gemm_bf16_kernel<OUT, GemmCfg<32, 32, 2, 2, 128, 4, 2, false>>, grid_of(64, 64), 256, 0, st, a);   \
+    else dlaunch(gemm_bf16_kernel<OUT, GemmCfg<32, 32, 2, 2, 64, 8, 2, false>>, grid_of(64, 64), 256, 0, st, a);        \
   }
   if (out_f32) {
     DREAMER_GEMM_LAUNCH(float)

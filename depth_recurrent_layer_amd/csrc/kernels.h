@@ -5,6 +5,13 @@
 
 namespace dreamer {
 
+// Every kernel of the library is launched through dlaunch (one place to hook launches).
+template <typename... P, typename... A>
+void dlaunch(void (*kernel)(P...), dim3 grid, dim3 block, size_t shm, hipStream_t st,
+             A... args) {
+  kernel<<<grid, block, shm, st>>>(args...);
+}
+
 enum { DT_F32 = 0, DT_BF16 = 1 };
 enum { FFN_GELU = 0, FFN_SWIGLU = 1, FFN_LINEAR = 2 };
 

@@ -59,7 +59,7 @@ int launch_expert_ffn_f32(int kind, int64_t nslots, int k, int h_in, int f, int 
   if (nslots <= 0) return 0;
   const size_t lds = (size_t)(kind == FFN_LINEAR ? 1 : f) * sizeof(float);
   if (lds > 65536) return -1;
-  expert_ffn_f32_kernel<<<(unsigned)nslots, 256, lds, st>>>(nslots, k, kind, h_in, f, h_out,
+  dlaunch(expert_ffn_f32_kernel, (unsigned)nslots, 256, lds, st, nslots, k, kind, h_in, f, h_out,
                                                             x, idx, gate, w1, w3, w2, slots);
   return 0;
 }
@@ -125,11 +125,11 @@ void launch_combine_norm(int dtype, int64_t T, int h, int k, const float* y,
   const int vec = dtype == DT_BF16 ? 8 : 4;
   const int threads = ((h / vec + 63) / 64) * 64;
   if (dtype == DT_BF16)
-    combine_norm_kernel<bf16><<<(unsigned)T, threads, 0, st>>>(
+    dlaunch(combine_norm_kernel<bf16>, (unsigned)T, threads, 0, st,
         T, h, k, y, (const bf16*)slots, x_out, x_out2, (const bf16*)g, eps, (bf16*)xhat,
         xhat32);
   else
-    combine_norm_kernel<float><<<(unsigned)T, threads, 0, st>>>(
+    dlaunch(combine_norm_kernel<float>, (unsigned)T, threads, 0, st,
         T, h, k, y, (const float*)slots, x_out, x_out2, (const float*)g, eps, (float*)xhat,
         xhat32);
 }
@@ -154,10 +154,10 @@ void launch_absorb(int dtype, int64_t ne, int64_t n, const void* we, const void*
   if (tot <= 0) return;
   const unsigned grid = (unsigned)((tot + 255) / 256);
   if (dtype == DT_BF16)
-    absorb_kernel<bf16><<<grid, 256, 0, st>>>(ne, n, (const bf16*)we, (const bf16*)wsh,
+    dlaunch(absorb_kernel<bf16>, grid, 256, 0, st, ne, n, (const bf16*)we, (const bf16*)wsh,
                                                (bf16*)out);
   else
-    absorb_kernel<float><<<grid, 256, 0, st>>>(ne, n, (const float*)we, (const float*)wsh,
+    dlaunch(absorb_kernel<float>, grid, 256, 0, st, ne, n, (const float*)we, (const float*)wsh,
                                                 (float*)out);
 }
 

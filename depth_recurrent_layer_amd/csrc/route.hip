@@ -368,7 +368,7 @@ int router_scores(int dtype, int64_t T, int h, int r, int E, int l, int L, const
     const dim3 grid((unsigned)((T + 15) / 16), (unsigned)((E + RCH - 1) / RCH));
     const size_t lds = 2 * 16 * (r + 4) * sizeof(float);
 #define RS_CASE(NK)                                                                      \
-  router_scores_bf16_kernel<NK><<<grid, 256, lds, st>>>(T, h, r, E, l, L, (const bf16*)x, \
+  dlaunch(router_scores_bf16_kernel<NK>, grid, 256, lds, st, T, h, r, E, l, L, (const bf16*)x, \
                                                         ldx, (const bf16*)w_r,            \
                                                         (const bf16*)keys, rho, cos_r, sin_r, z)
     switch (r / 32) {
@@ -381,7 +381,7 @@ int router_scores(int dtype, int64_t T, int h, int r, int E, int l, int L, const
 #undef RS_CASE
   } else {
     const int64_t n = T * E;
-    router_scores_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(
+    dlaunch(router_scores_f32_kernel, (unsigned)((n + 255) / 256), 256, 0, st,
         T, r, E, l, L, u, (const float*)keys, rho, cos_r, sin_r, z);
   }
   return 0;
@@ -393,7 +393,7 @@ int router_topk(int64_t T, int E, int k, const float* z, const float* bias, int 
   if (k < 1 || k > 32 || k > E) return -1;
   const unsigned grid = (unsigned)((T + 3) / 4);
 #define TK_CASE(KM)                                                                       \
-  router_topk_kernel<KM><<<grid, 256, 0, st>>>(T, E, k, z, bias, normalize, idx_in, idx, gate)
+  dlaunch(router_topk_kernel<KM>, grid, 256, 0, st, T, E, k, z, bias, normalize, idx_in, idx, gate)
   if (k <= 1) TK_CASE(1);
   else if (k <= 2) TK_CASE(2);
   else if (k <= 4) TK_CASE(4);
@@ -418,7 +418,7 @@ int router_route_fused(int64_t T, int h, int r, int E, int k, int l, int L, cons
   const unsigned grid = (unsigned)((T + 15) / 16);
   const size_t lds = (2 * 16 * (r + 4) + 16 * RCH_LD + RCH) * sizeof(float);
 #define RF_CASE(NK, KM)                                                                     \
-  router_fused_bf16_kernel<NK, KM><<<grid, 256, lds, st>>>(                                 \
+  dlaunch(router_fused_bf16_kernel<NK, KM>, grid, 256, lds, st,                                  \
       T, h, r, E, k, l, L, (const bf16*)x, ldx, (const bf16*)w_r, (const bf16*)keys, bias,  \
       rho, normalize, cos_r, sin_r, idx_in, idx, gate)
 #define RF_K(NK)                      \
@@ -451,7 +451,7 @@ __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
 
 void launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st) {
   if (n <= 0) return;
-  fill_i32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(p, n, v);
+  dlaunch(fill_i32_kernel, (unsigned)((n + 255) / 256), 256, 0, st, p, n, v);
 }
 
 int perm_blocks(int64_t nslots) { return (int)std::max<int64_t>(1, (nslots + PERM_CHUNK - 1) / PERM_CHUNK); }
@@ -594,8 +594,8 @@ int launch_permute(const int32_t* idx, int64_t nslots, int E, int tile_m, int32_
   if (E <= 0 || E > PERM_MAX_E) return -1;
   const size_t lds = (size_t)E * sizeof(int);
   const int nb = perm_blocks(nslots);
-  perm_hist_kernel<<<nb, 512, lds, st>>>(idx, nslots, E, hist);
-  perm_scatter_kernel<<<nb, PERM_THREADS, 2 * lds, st>>>(idx, nslots, E, nb, tile_m, hist,
+  dlaunch(perm_hist_kernel, nb, 512, lds, st, idx, nslots, E, hist);
+  dlaunch(perm_scatter_kernel, nb, PERM_THREADS, 2 * lds, st, idx, nslots, E, nb, tile_m, hist,
                                                          counts, goff, toff, perm, gate, pgate,
                                                          tiles, pad);
   return 0;
@@ -605,8 +605,8 @@ int launch_counts(const int32_t* idx, int64_t nslots, int E, int32_t* hist, int3
                   hipStream_t st) {
   if (E <= 0 || E > COUNT_MAX_E) return -1;
   const int nb = perm_blocks(nslots);
-  perm_hist_kernel<<<nb, 512, (size_t)E * sizeof(int), st>>>(idx, nslots, E, hist);
-  hist_colsum_kernel<<<(E + 255) / 256, 256, 0, st>>>(hist, nb, E, counts);
+  dlaunch(perm_hist_kernel, nb, 512, (size_t)E * sizeof(int), st, idx, nslots, E, hist);
+  dlaunch(hist_colsum_kernel, (E + 255) / 256, 256, 0, st, hist, nb, E, counts);
   return 0;
 }
 

@@ -38,7 +38,7 @@ int launch_route_counts(const int32_t* idx, int64_t n_sets, int64_t per_set, int
   launch_fill_i32(counts, n_sets * E, 0, st);
   if (per_set <= 0) return 0;
   const dim3 grid((unsigned)((per_set + COUNT_CHUNK - 1) / COUNT_CHUNK), (unsigned)n_sets);
-  route_counts_kernel<<<grid, 512, (size_t)E * sizeof(int), st>>>(idx, per_set, E, counts);
+  dlaunch(route_counts_kernel, grid, 512, (size_t)E * sizeof(int), st, idx, per_set, E, counts);
   return 0;
 }
 
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(1024) void bias_update_kernel(const int32_t* __rest
 
 void launch_bias_update(const int32_t* counts, int E, float lam, float* bias, hipStream_t st) {
   if (E <= 0) return;
-  bias_update_kernel<<<1, 1024, 0, st>>>(counts, E, lam, bias);
+  dlaunch(bias_update_kernel, 1, 1024, 0, st, counts, E, lam, bias);
 }
 
 // stats[set] = {distinct experts, max / mean, Gini}
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(1024) void usage_kernel(const int32_t* __restrict__
 int launch_expert_usage(const int32_t* counts, int64_t n_sets, int E, float* stats,
                         hipStream_t st) {
   if (E <= 0 || E > PERM_MAX_E || n_sets <= 0 || n_sets > 65535) return -1;
-  usage_kernel<<<(unsigned)n_sets, 1024, (size_t)E * sizeof(int), st>>>(counts, E, stats);
+  dlaunch(usage_kernel, (unsigned)n_sets, 1024, (size_t)E * sizeof(int), st, counts, E, stats);
   return 0;
 }
 

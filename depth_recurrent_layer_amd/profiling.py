@@ -1,16 +1,21 @@
 """Helpers to turn rocprofv3 CSV output into short summaries (kernel times, HBM traffic).
 
     python -m depth_recurrent_layer_amd.profiling stats <kernel_stats.csv> <title> <command>
+    python -m depth_recurrent_layer_amd.profiling launches <kernel_trace.csv> <title> <command>
     python -m depth_recurrent_layer_amd.profiling traffic <class> <kernel substring>
         <fetch_counter.csv> <write_counter.csv> <copy_fetch.csv> <copy_write.csv> <copy_bytes>
         <command...>
+    python -m depth_recurrent_layer_amd.profiling traffic-all <workload> <out dir>
+        <fetch_counter.csv> <write_counter.csv> <copy_fetch.csv> <copy_write.csv> <copy_bytes>
+        <command...>
 
-Both print markdown; the traffic summary ends in a json block that the benchmark reads.
+All print markdown (traffic-all writes one file per kernel class); a traffic summary ends
+in a json block that the benchmark reads.
 
 FETCH_SIZE / WRITE_SIZE are read per dispatch (KiB) and scaled by what the same counters
-report for a plain device copy of known size.  The summary records a digest of the kernel
-sources; a later source change makes the stored traffic stale (the benchmark then reports
-null).
+report for a plain device copy of known size.  The summary records a digest of the
+sources of its kernel class; a later change to them makes the stored traffic stale (the
+benchmark then reports null).
 """
 from __future__ import annotations
 
@@ -22,16 +27,38 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 
+# Sources of each timed kernel class (besides the shared device header), and the
+# kernel-name substring that picks its dispatches in a counter file of the small workload.
+CLASS_SOURCES = {
+    "qkv_proj": ["gemm.hip"], "out_proj": ["gemm.hip"], "seq_attn": ["attn.hip"],
+    "depth_attn": ["attn.hip"], "route": ["route.hip"], "expert_ffn": ["expert_ffn.hip"],
+    "combine": ["moe.hip"],
+}
+SHARED_SOURCES = ["common.h"]
+CLASS_KERNELS = {
+    "qkv_proj": "Li32ELi64ELi4ELi2ELi128ELi2ELi2ELb1",  # the 8-wave QKV instance (mangled)
+    "out_proj": "GemmCfg<32, 32, 2, 2, 128, 4, 2, false>",
+    "seq_attn": "sa_flash_kernel",
+    "depth_attn": "depth_attn_kernel",
+    "route": "router_fused_bf16_kernel",
+    "expert_ffn": "expert_ffn_kernel",
+    "combine": "combine_norm_kernel",
+}
 
-def source_digest() -> str:
-    """sha256 over the library sources (any kernel change invalidates stored counters)."""
+
+def source_digest(kclass: str | None = None) -> str:
+    """sha256 over the sources of one kernel class (every library source when None): a
+    change to them invalidates that class's stored counters."""
     h = hashlib.sha256()
     csrc = os.path.join(HERE, "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(csrc, name), "rb") as fh:
-                h.update(name.encode())
-                h.update(fh.read())
+    if kclass is None:
+        names = sorted(n for n in os.listdir(csrc) if n.endswith((".hip", ".h", ".cpp")))
+    else:
+        names = sorted(CLASS_SOURCES[kclass] + SHARED_SOURCES)
+    for name in names:
+        with open(os.path.join(csrc, name), "rb") as fh:
+            h.update(name.encode())
+            h.update(fh.read())
     return h.hexdigest()
 
 
@@ -45,6 +72,29 @@ def kernel_stats_md(csv_path: str, title: str, command: str, top: int = 16) -> s
         out.append(f"| `{n}` | {r['Calls']} | {int(r['TotalDurationNs']) / 1e3:.1f} | "
                    f"{float(r['AverageNs']) / 1e3:.2f} | {int(r['MinNs']) / 1e3:.2f} | "
                    f"{int(r['MaxNs']) / 1e3:.2f} | {r['Percentage']} |")
+    return "\n".join(out) + "\n"
+
+
+def launch_stats_md(trace_csv: str, title: str, command: str, top: int = 24) -> str:
+    """Per (kernel, grid) durations from a kernel trace: one kernel launched with several
+    shapes (the projections of the different wirings, say) gets one row per shape."""
+    groups = {}
+    for r in csv.DictReader(open(trace_csv)):
+        grid = (f"{int(r['Grid_Size_X']) // max(1, int(r['Workgroup_Size_X']))}x"
+                f"{int(r['Grid_Size_Y']) // max(1, int(r['Workgroup_Size_Y']))}"
+                f"x{int(r['Workgroup_Size_X'])}")
+        key = (r["Kernel_Name"], grid)
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    total = sum(sum(v) for v in groups.values())
+    rows = sorted(groups.items(), key=lambda kv: -sum(kv[1]))[:top]
+    out = [f"# {title}", "", "Command (repository root, one MI355X):", "", "```", command, "```",
+           "", "Durations per kernel and launch shape (blocks x, blocks y, threads per block).",
+           "", "| kernel | shape | calls | total us | avg us | min us | max us | % |",
+           "|---|---|---|---|---|---|---|---|"]
+    for (name, grid), d in rows:
+        n = name if len(name) < 90 else name[:87] + "..."
+        out.append(f"| `{n}` | {grid} | {len(d)} | {sum(d) / 1e3:.1f} | {sum(d) / len(d) / 1e3:.2f} "
+                   f"| {min(d) / 1e3:.2f} | {max(d) / 1e3:.2f} | {100.0 * sum(d) / total:.2f} |")
     return "\n".join(out) + "\n"
 
 
@@ -74,25 +124,39 @@ def traffic_summary(kclass, kernel_substr, fetch_csv, write_csv, copy_fetch_csv,
     return {"class": kclass, "kernel": kernel_substr, "dispatches": len(f),
             "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
             "bytes_per_launch": fetch + write, "copy_scale_fetch": kf, "copy_scale_write": kw,
-            "copy_bytes": copy_bytes, "source_sha256": source_digest(), "command": command}
+            "copy_bytes": copy_bytes, "source_sha256": source_digest(kclass), "command": command}
+
+
+def traffic_md(s) -> str:
+    out = [f"# HBM traffic of `{s['kernel']}` ({s['class']})", "",
+           "FETCH_SIZE and WRITE_SIZE (KiB per dispatch) from two separate rocprofv3 --pmc "
+           "runs, scaled by the same counters over a plain device copy of "
+           f"{s['copy_bytes'] / 2**20:.0f} MiB (fetch x{s['copy_scale_fetch']:.4f}, "
+           f"write x{s['copy_scale_write']:.4f}).", "",
+           f"- dispatches: {s['dispatches']}",
+           f"- fetch per launch: {s['fetch_bytes_per_launch'] / 2**20:.2f} MiB",
+           f"- write per launch: {s['write_bytes_per_launch'] / 2**20:.2f} MiB",
+           f"- commands: {s['command']}", "", "```json", json.dumps(s, indent=1), "```"]
+    return "\n".join(out) + "\n"
 
 
 if __name__ == "__main__":
     mode = sys.argv[1]
     if mode == "stats":
         sys.stdout.write(kernel_stats_md(sys.argv[2], sys.argv[3], sys.argv[4]))
+    elif mode == "launches":
+        sys.stdout.write(launch_stats_md(sys.argv[2], sys.argv[3], sys.argv[4]))
     elif mode == "traffic":
         s = traffic_summary(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6],
                             sys.argv[7], float(sys.argv[8]), " ".join(sys.argv[9:]))
-        print(f"# HBM traffic of `{s['kernel']}` ({s['class']})\n")
-        print("FETCH_SIZE and WRITE_SIZE (KiB per dispatch) from two separate rocprofv3 --pmc "
-              "runs, scaled by the same counters over a plain device copy of "
-              f"{s['copy_bytes'] / 2**20:.0f} MiB (fetch x{s['copy_scale_fetch']:.4f}, "
-              f"write x{s['copy_scale_write']:.4f}).\n")
-        print(f"- dispatches: {s['dispatches']}")
-        print(f"- fetch per launch: {s['fetch_bytes_per_launch'] / 2**20:.2f} MiB")
-        print(f"- write per launch: {s['write_bytes_per_launch'] / 2**20:.2f} MiB")
-        print(f"- commands: {s['command']}\n")
-        print("```json\n" + json.dumps(s, indent=1) + "\n```")
+        sys.stdout.write(traffic_md(s))
+    elif mode == "traffic-all":
+        workload, out_dir = sys.argv[2], sys.argv[3]
+        for kclass, kname in CLASS_KERNELS.items():
+            s = traffic_summary(kclass, kname, sys.argv[4], sys.argv[5], sys.argv[6],
+                                sys.argv[7], float(sys.argv[8]), " ".join(sys.argv[9:]))
+            with open(os.path.join(out_dir, f"{kclass}_{workload}_hbm_traffic.md"), "w") as fh:
+                fh.write(traffic_md(s))
+            print(kclass, s["dispatches"], round(s["bytes_per_launch"] / 2**20, 2), "MiB")
     else:
         raise SystemExit(__doc__)

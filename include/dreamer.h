@@ -320,9 +320,11 @@ int dreamer_decode_tokens(const dreamer_layer_cfg* cfg, const dreamer_layer_weig
 /*
  * Kernel timing, for measurement harnesses.  When enabled, every launch of the kernel
  * class `kclass` (DREAMER_KC_*) made by the library on a stream is bracketed by two HIP
- * events recorded on that stream; dreamer_timing_read returns the number of bracketed
- * launches and their summed duration in milliseconds (it synchronises on the events).
- * Disabled by default; not reentrant (one harness at a time).
+ * events recorded on that stream (timing-only events, without a system-scope fence; the
+ * bracket holds the kernel's dispatch as well as its execution); dreamer_timing_read
+ * returns the number of bracketed launches and their summed duration in milliseconds (it
+ * synchronises on the events).  Disabled by default; not reentrant (one harness at a
+ * time).
  */
 #define DREAMER_KC_GEMM 1       /* Q/K/V projection (and the float32 router projection) */
 #define DREAMER_KC_SEQ_ATTN 2
