@@ -413,28 +413,34 @@ __global__ __launch_bounds__(256, 3) void sa_flash_kernel(
   qf[1] = *reinterpret_cast<const bf16x8*>(q + (tok0 + qrow) * ldq + hoff + 32 + lg * 8);
 
   // loads of one stage: 16 instructions of 1 KiB (8 for K rows, 8 for V^T rows); wave w
-  // issues instructions j = w + 4 i.  Lane -> (row lane/8, slot lane%8) of 8 rows.
+  // issues instructions j = w + 4 i (i < 2: K rows, i >= 2: V^T rows).  Lane -> (row
+  // lane/8, slot lane%8) of 8 rows.  Tiles inside the sequence advance precomputed
+  // pointers by one tile; the last, partial tile clamps its rows into the sequence.
   const int lrow = lane >> 3, slot = lane & 7;
   const bf16* vbase = vt + ((int64_t)(b * H + head) * 64) * S;
+  auto tile_src = [&](int i, int kbase) -> const bf16* {
+    const int j = w + 4 * i;
+    if (i < 2) {  // K rows (keys in key_of_row order)
+      const int row = j * 8 + lrow;
+      const int kp = min(kbase + key_of_row(row), S - 1);
+      return kk + (tok0 + kp) * ldk + hoff + (slot ^ (row & 7)) * 8;
+    }
+    const int dim = (j - 8) * 8 + lrow;  // V^T rows (dims)
+    const int p0 = min(kbase + (slot ^ (dim & 7)) * 8, S - 8);
+    return vbase + (int64_t)dim * S + p0;
+  };
+  const bf16* src0[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) src0[i] = tile_src(i, 0);
   auto issue = [&](int t) {
     char* sb = stg[t % NSTG];
     const int kbase = t * BKEY;
+    const bool whole = kbase + BKEY <= S;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int j = w + 4 * i;
-      const bf16* src;
-      if (j < 8) {  // K rows (keys in key_of_row order)
-        const int row = j * 8 + lrow;
-        const int c = slot ^ (row & 7);
-        const int kp = min(kbase + key_of_row(row), S - 1);
-        src = kk + (tok0 + kp) * ldk + hoff + c * 8;
-      } else {      // V^T rows (dims)
-        const int dim = (j - 8) * 8 + lrow;
-        const int c = slot ^ (dim & 7);
-        const int p0 = min(kbase + c * 8, S - 8);
-        src = vbase + (int64_t)dim * S + p0;
-      }
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(sb + j * 1024), 16, 0, 0);
+      const bf16* src = whole ? src0[i] + (int64_t)kbase * (i < 2 ? ldk : 1) : tile_src(i, kbase);
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(sb + (w + 4 * i) * 1024),
+                                       16, 0, 0);
     }
   };
 
@@ -490,31 +496,30 @@ __global__ __launch_bounds__(256, 3) void sa_flash_kernel(
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sacc[t][i]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    tmax = max_xor32(max_xor16(tmax));
     const float mn = fmaxf(m, tmax);
-    const float corr = __builtin_amdgcn_exp2f((m - mn) * sl2);
-    m = mn;
-    lsum *= corr;
+    if (__any(mn > m)) {  // rescale only when some query's running max moved
+      const float corr = __builtin_amdgcn_exp2f((m - mn) * sl2);
+      m = mn;
+      lsum *= corr;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) o[t] *= corr;
+      for (int t = 0; t < 4; ++t) o[t] *= corr;
+    }
     // P^T fragments for the two 32-key chunks: element j of lane group lg is key
-    // 32cc + 8lg + j (tile 2cc for j < 4, tile 2cc+1 for j >= 4).  P = hi + lo, both bf16,
-    // so P V keeps ~16 mantissa bits of P (a single bf16 P would perturb every output by
-    // up to 2^-9 max|v|).
-    bf16x8 ph[2], pl[2];
+    // 32cc + 8lg + j (tile 2cc for j < 4, tile 2cc+1 for j >= 4).  P is rounded to bf16
+    // (pairwise conversions) for the MFMA; the softmax denominator sums P in float32.
+    bf16x8 ph[2];
     const float msl = mn * sl2;
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
+    for (int cc = 0; cc < 2; ++cc) {
+      floatx8 pv;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float sv = sacc[2 * cc + (j >> 2)][j & 3];
-        const float p = __builtin_amdgcn_exp2f(fmaf(sv, sl2, -msl));
-        lsum += p;
-        const bf16 hi = (bf16)p;
-        ph[cc][j] = hi;
-        pl[cc][j] = (bf16)(p - (float)hi);
+        pv[j] = __builtin_amdgcn_exp2f(fmaf(sacc[2 * cc + (j >> 2)][j & 3], sl2, -msl));
+        lsum += pv[j];
       }
+      ph[cc] = __builtin_convertvector(pv, bf16x8);
+    }
     // O^T += V^T P^T : 4 dim tiles x 2 key chunks.  Lane (dim 16t + lr, group lg) takes
     // keys 32cc + 8lg + 0..7 of its V^T row: chunk 4cc + lg.
     bf16x8 vf[8];  // vf[t]: keys 0..31 of dim row 16t + lr, vf[4 + t]: keys 32..63
@@ -522,13 +527,9 @@ __global__ __launch_bounds__(256, 3) void sa_flash_kernel(
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        o[t] = mfma16(vf[cc * 4 + t], ph[cc], o[t]);
-        o[t] = mfma16(vf[cc * 4 + t], pl[cc], o[t]);
-      }
+      for (int cc = 0; cc < 2; ++cc) o[t] = mfma16(vf[cc * 4 + t], ph[cc], o[t]);
   }
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
+  lsum = sum_xor32(sum_xor16(lsum));
   if (qpos >= S) return;
   const float inv = 1.0f / lsum;
   bf16* orow = out + (tok0 + qpos) * ldo + hoff;

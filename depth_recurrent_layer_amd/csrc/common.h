@@ -7,6 +7,7 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 #define DEV __device__ __forceinline__
@@ -100,6 +101,31 @@ DEV float block_sum(float v, float* red) {
 }
 
 DEV float fast_exp(float x) { return __expf(x); }
+
+// Reductions across lanes l ^ 16 and l ^ 32 with the gfx950 lane-swap instructions (no
+// trip through LDS as a general shuffle would take): with both operands x, the swap
+// returns x of the partner half-row (half-wave) in one result and this lane's own
+// half-row's x in the other, in some order, so max / sum of the pair is symmetric.
+DEV float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+DEV float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+DEV float sum_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+DEV float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 DEV float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
 

@@ -110,9 +110,9 @@ def test_seq_attn_prefill(gpu_lib, dt, B, S, H, d, rope):
     g = _np(out)
     if bf:
         vmax = np.abs(_np(v)).max()
-        # P is applied as hi + lo bf16 parts (~2^-17 relative), so only the final rounding
-        # and float32 summation remain
-        assert_close_ulps(g, ref, ulps=2, atol=2.0 ** -14 * vmax, what="SA prefill")
+        # P enters the P V product rounded to bf16 (relative error <= 2^-9 per weight), so
+        # an output moves by at most 2^-9 max|v| beyond its own final rounding
+        assert_close_ulps(g, ref, ulps=2, atol=2.0 ** -8 * vmax, what="SA prefill")
         assert_close_ulps(_np(kc[:, :S]), krot, ulps=1, atol=2.0 ** -20, what="SA cache keys")
     else:
         assert rel_err(g, ref) <= 1e-5
