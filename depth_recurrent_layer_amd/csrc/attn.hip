@@ -116,30 +116,55 @@ __global__ __launch_bounds__(256) void depth_attn_kernel(
   store16(krow + (int64_t)l * h, kv);
   store16(vrow + (int64_t)l * h, vv);
 
-  float m = -INFINITY, lsum = 0.f, acc[VEC];
-#pragma unroll
-  for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
-  for (int j = 0; j <= l; ++j) {
-    if (window > 0 && l - j >= window && (dilation <= 0 || (l - j) % dilation)) continue;
-    float kj[VEC], vj[VEC];
-    if (j < l) {
-      load16(krow + (int64_t)j * h, kj);
-      load16(vrow + (int64_t)j * h, vj);
-    } else {
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) { kj[i] = kv[i]; vj[i] = vv[i]; }
-    }
+  // The current slot first (from registers), so the running max starts finite; then the
+  // older slots in batches of NB whose loads are issued together (the key test is the
+  // same for every lane, so whole waves take or skip a slot).
+  float m, lsum = 1.f, acc[VEC];
+  {
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) s = fmaf(qv[i], kj[i], s);
-    s = group_sum<LPH>(s) * scale;
-    const float mn = fmaxf(m, s);
-    const float corr = expf(m - mn);  // exp(-inf) = 0 on the first key
-    const float p = expf(s - mn);
-    lsum = lsum * corr + p;
+    for (int i = 0; i < VEC; ++i) {
+      s = fmaf(qv[i], kv[i], s);
+      acc[i] = vv[i];
+    }
+    m = group_sum<LPH>(s) * scale;
+  }
+  constexpr int NB = 4;
+  for (int j0 = 0; j0 < l; j0 += NB) {
+    float kj[NB][VEC], vj[NB][VEC];
+    bool use[NB];
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) acc[i] = acc[i] * corr + p * vj[i];
-    m = mn;
+    for (int b = 0; b < NB; ++b) {
+      const int j = j0 + b;
+      use[b] = j < l && !(window > 0 && l - j >= window && (dilation <= 0 || (l - j) % dilation));
+      if (use[b]) {
+        load16(krow + (int64_t)j * h, kj[b]);
+        load16(vrow + (int64_t)j * h, vj[b]);
+      }
+    }
+    float s[NB], bm = m;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (!use[b]) continue;
+      float t = 0.f;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) t = fmaf(qv[i], kj[b][i], t);
+      s[b] = group_sum<LPH>(t) * scale;
+      bm = fmaxf(bm, s[b]);
+    }
+    const float corr = __expf(m - bm);
+    lsum *= corr;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) acc[i] *= corr;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (!use[b]) continue;
+      const float p = __expf(s[b] - bm);
+      lsum += p;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc[i] = fmaf(p, vj[b][i], acc[i]);
+    }
+    m = bm;
   }
   const float inv = 1.0f / lsum;
 #pragma unroll

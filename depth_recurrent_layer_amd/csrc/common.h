@@ -69,39 +69,6 @@ DEV void store16(T* p, const float* in) {
   }
 }
 
-DEV float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-DEV float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-
-// Sum over aligned groups of G lanes (G a power of two <= 64).
-template <int G>
-DEV float group_sum(float v) {
-#pragma unroll
-  for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
-// Block-wide sum (blockDim.x a multiple of 64, <= 1024); `red` holds >= 16 floats.
-DEV float block_sum(float v, float* red) {
-  v = wave_sum(v);
-  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
-  float s = 0.f;
-  for (int i = 0; i < nw; ++i) s += red[i];
-  return s;
-}
-
-DEV float fast_exp(float x) { return __expf(x); }
-
 // Reductions across lanes l ^ 16 and l ^ 32 with the gfx950 lane-swap instructions (no
 // trip through LDS as a general shuffle would take): with both operands x, the swap
 // returns x of the partner half-row (half-wave) in one result and this lane's own
@@ -126,6 +93,58 @@ DEV float sum_xor32(float v) {
                                                   false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+
+DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Sum over aligned groups of G lanes (G a power of two <= 64), every lane ending with its
+// group's sum: within 16 lanes by DPP lane permutes on the VALU (swap neighbours, swap
+// pairs, mirror within 8, mirror within 16: each step adds the partner subgroup's sum),
+// across 16 and 32 lanes by the lane-swap instructions.
+DEV float dpp_add(float v, int ctrl) {
+  int o = 0;
+  switch (ctrl) {  // the control word must be an immediate
+    case 0xB1: o = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false); break;
+    case 0x4E: o = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false); break;
+    case 0x141: o = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false); break;
+    default: o = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false); break;
+  }
+  return v + __int_as_float(o);
+}
+template <int G>
+DEV float group_sum(float v) {
+  static_assert(G >= 1 && G <= 64 && (G & (G - 1)) == 0, "power of two up to 64");
+  if constexpr (G >= 2) v = dpp_add(v, 0xB1);   // lane ^ 1
+  if constexpr (G >= 4) v = dpp_add(v, 0x4E);   // lane ^ 2 (pairs of a quad)
+  if constexpr (G >= 8) v = dpp_add(v, 0x141);  // lane 7 - i of its 8: the other quad
+  if constexpr (G >= 16) v = dpp_add(v, 0x140); // lane 15 - i of its 16: the other 8
+  if constexpr (G >= 32) v = sum_xor16(v);
+  if constexpr (G >= 64) v = sum_xor32(v);
+  return v;
+}
+
+// Block-wide sum (blockDim.x a multiple of 64, <= 1024); `red` holds >= 16 floats.
+DEV float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float s = 0.f;
+  for (int i = 0; i < nw; ++i) s += red[i];
+  return s;
+}
+
+DEV float fast_exp(float x) { return __expf(x); }
+
 
 DEV float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
 
