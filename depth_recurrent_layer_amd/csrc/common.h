@@ -109,15 +109,28 @@ DEV float wave_max(float v) {
 // group's sum: within 16 lanes by DPP lane permutes on the VALU (swap neighbours, swap
 // pairs, mirror within 8, mirror within 16: each step adds the partner subgroup's sum),
 // across 16 and 32 lanes by the lane-swap instructions.
+template <int CTRL>
+DEV int dpp_get(int v) {  // the value of the partner lane CTRL selects
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+DEV float dpp_get(float v) {
+  return __int_as_float(dpp_get<CTRL>(__float_as_int(v)));
+}
 DEV float dpp_add(float v, int ctrl) {
-  int o = 0;
   switch (ctrl) {  // the control word must be an immediate
-    case 0xB1: o = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false); break;
-    case 0x4E: o = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false); break;
-    case 0x141: o = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false); break;
-    default: o = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false); break;
+    case 0xB1: return v + dpp_get<0xB1>(v);
+    case 0x4E: return v + dpp_get<0x4E>(v);
+    case 0x141: return v + dpp_get<0x141>(v);
+    default: return v + dpp_get<0x140>(v);
   }
-  return v + __int_as_float(o);
+}
+// Max over aligned groups of 16 lanes (the same DPP steps as group_sum).
+DEV float group_max16(float v) {
+  v = fmaxf(v, dpp_get<0xB1>(v));
+  v = fmaxf(v, dpp_get<0x4E>(v));
+  v = fmaxf(v, dpp_get<0x141>(v));
+  return fmaxf(v, dpp_get<0x140>(v));
 }
 template <int G>
 DEV float group_sum(float v) {

@@ -21,57 +21,78 @@ namespace dreamer {
 
 // ------------------------------------------------------------------ scores (bf16, MFMA)
 // u tile [16 tokens x r] of the block's tokens, rotated by depth, split into three bf16
-// parts as MFMA A operands (token lr, k-group lg).  us / ur: 2 * 16 * (r + 4) floats of
-// LDS; rows are padded by 4 floats so that the 16 rows of a fragment read (and of the
-// projection's stores) start in distinct banks.
+// parts as MFMA A operands (token lr, k-group lg).  The projection is split over the
+// block's 4 waves by k: wave w takes the k-steps (of 32) w, w + 4, ..., all r / 16 column
+// tiles, so each x fragment is loaded once; the 4 partial tiles go to part [4][16][r + 4]
+// in LDS and are summed in wave order.  ur: [16][r + 4].  Rows are padded by 4 floats so
+// that the 16 rows of a fragment read (and of the partial stores) start in distinct banks.
 // r divides 256, so each thread rotates one rank index i = tid % r (one table entry,
 // loaded before the projection).
 template <int NKS>
 DEV void router_u_parts(int64_t Ttok, int64_t t0, int h, int r, int l, int L,
                         const bf16* __restrict__ x, int64_t ldx, const bf16* __restrict__ w_r,
-                        const float* __restrict__ cs, const float* __restrict__ sn, float* us,
+                        const float* __restrict__ cs, const float* __restrict__ sn, float* part,
                         float* ur, bf16x8 (&ah)[NKS], bf16x8 (&am)[NKS], bf16x8 (&al)[NKS]) {
+  constexpr int NT = 2 * NKS;           // r / 16 column tiles
+  constexpr int KB = NT <= 4 ? 4 : 2;   // k-steps per batch of loads (KB x (1 + NT) x 16 B)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
-  const bf16x8 zero8 = {};
+  const int rp = r + 4;
   // depth RoPE: pairs i < r/4 at depth l, the others at L-1-l
   const int half = r / 2, quarter = r / 4;
   const int i = tid % r;
   const int p = i < half ? i : i - half;
   const int pos = p < quarter ? l : L - 1 - l;
   const float cv = cs[pos * half + p], sv = sn[pos * half + p];
-  // wave w owns rank columns 16 nt, nt = w, w + 4, ...  Rows past the last token read
-  // the last token (their u is never used).  Loads go out in batches of 8 k-steps before
-  // their MFMAs, so a batch costs one memory round trip.
+  // Rows past the last token read the last token (their u is never used).  A batch's
+  // loads all go out before its MFMAs (one memory round trip per batch); k-steps past the
+  // wave's last are clamped loads that are not used.  Token block t0 / 16 starts at batch
+  // (t0 / 16) % batches: concurrent blocks read different parts of W_r (the order is a
+  // function of the token block alone, so every kernel computing u for a token sums in
+  // the same order).
   const int64_t tr = t0 + lr < Ttok ? t0 + lr : Ttok - 1;
   const bf16* xrow = x + tr * ldx + lg * 8;
-  for (int nt = w; nt < r / 16; nt += 4) {
-    const bf16* wrow = w_r + (int64_t)(nt * 16 + lr) * h + lg * 8;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < h; k0 += 8 * 32) {
-      bf16x8 af[8], bf[8];
+  const bf16* wrow = w_r + (int64_t)lr * h + lg * 8;
+  const int nkw = (h / 32 - w + 3) / 4;  // this wave's k-steps
+  const int nbat = (nkw + KB - 1) / KB;
+  const int rot = nbat > 0 ? (int)((t0 / 16) % nbat) : 0;
+  floatx4 acc[NT];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const bool in = k0 + 32 * j < h;
-        af[j] = in ? *reinterpret_cast<const bf16x8*>(xrow + k0 + 32 * j) : zero8;
-        bf[j] = in ? *reinterpret_cast<const bf16x8*>(wrow + k0 + 32 * j) : zero8;
-      }
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int bq = 0; bq < nbat; ++bq) {
+    const int b0 = ((bq + rot) % nbat) * KB;
+    bf16x8 af[KB], bf[KB][NT];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc = mfma16(af[j], bf[j], acc);
+    for (int j = 0; j < KB; ++j) {
+      const int k0 = (w + 4 * min(b0 + j, nkw - 1)) * 32;
+      af[j] = *reinterpret_cast<const bf16x8*>(xrow + k0);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        bf[j][nt] = *reinterpret_cast<const bf16x8*>(wrow + (int64_t)nt * 16 * h + k0);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) us[(lg * 4 + i) * (r + 4) + nt * 16 + lr] = acc[i];
+    for (int j = 0; j < KB; ++j)
+      if (b0 + j < nkw) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma16(af[j], bf[j][nt], acc[nt]);
+      }
   }
+  float* pw = part + w * 16 * rp;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pw[(lg * 4 + q) * rp + nt * 16 + lr] = acc[nt][q];
   __syncthreads();
   const int ip = i < half ? i + half : i - half;
   for (int e = tid; e < 16 * r; e += 256) {
-    const int t = e / r;
-    const float a = us[t * (r + 4) + i], b = us[t * (r + 4) + ip];
-    ur[t * (r + 4) + i] = i < half ? a * cv - b * sv : a * cv + b * sv;
+    const float* pt = part + (e / r) * rp;
+    const float a = ((pt[i] + pt[16 * rp + i]) + pt[32 * rp + i]) + pt[48 * rp + i];
+    const float b = ((pt[ip] + pt[16 * rp + ip]) + pt[32 * rp + ip]) + pt[48 * rp + ip];
+    ur[(e / r) * rp + i] = i < half ? a * cv - b * sv : a * cv + b * sv;
   }
   __syncthreads();
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
-    const float4* src = reinterpret_cast<const float4*>(ur + lr * (r + 4) + ks * 32 + lg * 8);
+    const float4* src = reinterpret_cast<const float4*>(ur + lr * rp + ks * 32 + lg * 8);
     const float4 q0 = src[0], q1 = src[1];
     const float uv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
 #pragma unroll
@@ -130,7 +151,7 @@ __global__ __launch_bounds__(256) void router_scores_bf16_kernel(
   for (int j = 0; j < 4; ++j)
     if (et0 + w + 4 * j < et1) load_keys<NKS>(keys, r, et0 + w + 4 * j, kf[j]);
   bf16x8 ah[NKS], am[NKS], al[NKS];
-  router_u_parts<NKS>(Ttok, t0, h, r, l, L, x, ldx, w_r, cs, sn, smem, smem + 16 * (r + 4), ah,
+  router_u_parts<NKS>(Ttok, t0, h, r, l, L, x, ldx, w_r, cs, sn, smem + 16 * (r + 4), smem, ah,
                       am, al);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -148,37 +169,30 @@ __global__ __launch_bounds__(256) void router_scores_bf16_kernel(
 // (value, index) order of the router: larger value first, then lower index.
 DEV bool better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
 
-// Insert (v, zv, e) into a sorted list of KMAX entries (best first).
-template <int KMAX>
-DEV void list_insert(float (&lv)[KMAX], float (&lz)[KMAX], int (&li)[KMAX], float v, float zv,
-                     int e) {
-  float cv = v, cz = zv;
-  int ci = e;
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    if (better(cv, ci, lv[j], li[j])) {
-      const float tv = lv[j], tz = lz[j];
-      const int ti = li[j];
-      lv[j] = cv;
-      lz[j] = cz;
-      li[j] = ci;
-      cv = tv;
-      cz = tz;
-      ci = ti;
-    }
-  }
-}
-
 // ------------------------------------------------------------- fused route (bf16, MFMA)
-// One block per 16 tokens.  The scores of each chunk of 256 experts go to LDS; 16 lanes
-// per token scan them, each keeping a sorted list of its best (z + b, z, e); k rounds of
-// a 16-lane butterfly argmax pick the winners.  Gates sigmoid(z), normalised on request
-// by their sum taken in selection order.
+// One block per 16 tokens, 16 lanes per token.  The scores of each chunk of 256 experts go
+// to LDS.  The token's best k so far are held across its 16 lanes, lane g holding the g-th
+// best (z + b, z, e).  Each chunk, a lane reads its 16 values (experts c0 + g + 16 q) and
+// flags those that are not below tau, a value under which nothing can be selected: tau is
+// the larger of the current k-th best and the k-th largest of the 16 lanes' chunk maxima
+// (both leave at least k better values above anything below them).  The flagged
+// candidates are then inserted one per token per step: the token's group takes its first
+// flagged lane's first candidate, every lane compares it with its entry, and entries that
+// lose to it move down one lane (a row shift).  Candidates are few once the list holds
+// good values (about k / c of a chunk's values pass in chunk c on random data), so the
+// selection costs a compare per value.  Gates sigmoid(z), normalised on request by their
+// sum taken in selection order.
 // score rows padded to RCH + 20 floats: a wave's stores of 4 x 16 fragment rows and its
-// 4 x 16-lane row scans both spread over the banks (at most 2-way on the scans)
+// 4 x 16-lane row reads both spread over the banks (at most 2-way on the reads)
 constexpr int RCH = 256, RCH_LD = RCH + 20;
 
-template <int NKS, int KMAX>
+// The value of the lane one below in the same 16-lane row; lane 0 of a row gets `first`.
+DEV int row_shr1(int v, int first) { return __builtin_amdgcn_update_dpp(first, v, 0x111, 0xF, 0xF, false); }
+DEV float row_shr1(float v, float first) {
+  return __int_as_float(row_shr1(__float_as_int(v), __float_as_int(first)));
+}
+
+template <int NKS>
 __global__ __launch_bounds__(256) void router_fused_bf16_kernel(
     int64_t Ttok, int h, int r, int E, int k, int l, int L, const bf16* __restrict__ x,
     int64_t ldx, const bf16* __restrict__ w_r, const bf16* __restrict__ keys,
@@ -186,30 +200,32 @@ __global__ __launch_bounds__(256) void router_fused_bf16_kernel(
     const float* __restrict__ sn, const int32_t* __restrict__ idx_in, int32_t* __restrict__ idx,
     float* __restrict__ gate) {
   extern __shared__ float smem[];
-  float* zs = smem + 32 * (r + 4);  // [16][RCH_LD]
-  float* bs = zs + 16 * RCH_LD;   // [RCH] bias chunk
+  float* bs = smem + 16 * (r + 4);  // [RCH] bias chunk (after u's [16][r + 4])
+  float* zs = bs + RCH;  // [16][RCH_LD] scores; first the projection's partial tiles
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
   const int64_t t0 = (int64_t)blockIdx.x * 16;
-  // first chunk's keys (this wave's tiles w + 4 j) and biases, before the projection
+  // Chunks of RCH experts in the order rot, rot + 1, ... (rot = block % chunks): concurrent
+  // blocks read different parts of the key table (the selection does not depend on the
+  // order).  The first chunk's keys (this wave's tiles w + 4 j) and biases are loaded
+  // before the projection; tile indices are clamped into the key table (tiles past the
+  // chunk are not used), so the loads are unconditional.
+  const int nch = (E + RCH - 1) / RCH, rot = (int)(blockIdx.x % nch);
   KeyFrag<NKS> kf[4];
-  int n = min(RCH, E);
+  int c0 = rot * RCH, n = min(RCH, E - c0);
+  const int ntile = E / 16;
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    if (w + 4 * j < n / 16) load_keys<NKS>(keys, r, w + 4 * j, kf[j]);
-  if (tid < n) bs[tid] = bias[tid];
+  for (int j = 0; j < 4; ++j) load_keys<NKS>(keys, r, min(c0 / 16 + w + 4 * j, ntile - 1), kf[j]);
+  if (tid < n) bs[tid] = bias[c0 + tid];
   bf16x8 ah[NKS], am[NKS], al[NKS];
-  router_u_parts<NKS>(Ttok, t0, h, r, l, L, x, ldx, w_r, cs, sn, smem, smem + 16 * (r + 4), ah,
-                      am, al);
+  router_u_parts<NKS>(Ttok, t0, h, r, l, L, x, ldx, w_r, cs, sn, zs, smem, ah, am, al);
   const int tl = w * 4 + (lane >> 4), g = lane & 15;
   const int64_t t = t0 + tl;
-  float lv[KMAX], lz[KMAX];
-  int li[KMAX];
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) { lv[j] = -INFINITY; lz[j] = 0.f; li[j] = 0x7fffffff; }
+  float lv = -INFINITY, lz = 0.f;  // this lane's entry of the token's list
+  int li = 0x7fffffff;
   int my = 0;
   float myz = 0.f;
   if (idx_in && t < Ttok && g < k) my = min(max(idx_in[t * k + g], 0), E - 1);
-  for (int c0 = 0; c0 < E; c0 += RCH) {
+  for (int ci = 0; ci < nch; ++ci) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int et = w + 4 * j;
@@ -220,42 +236,62 @@ __global__ __launch_bounds__(256) void router_fused_bf16_kernel(
     }
     __syncthreads();
     // next chunk's keys and biases are fetched while this chunk is scanned
-    const int c1 = c0 + RCH, n1 = c1 < E ? min(RCH, E - c1) : 0;
+    const int c1 = ((ci + 1 + rot) % nch) * RCH, n1 = ci + 1 < nch ? min(RCH, E - c1) : 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      if (w + 4 * j < n1 / 16) load_keys<NKS>(keys, r, c1 / 16 + w + 4 * j, kf[j]);
+      load_keys<NKS>(keys, r, min(c1 / 16 + w + 4 * j, ntile - 1), kf[j]);
     const float bnext = tid < n1 ? bias[c1 + tid] : 0.f;
     const float* zt = zs + tl * RCH_LD;
     if (idx_in) {
       if (g < k && my >= c0 && my < c0 + n) myz = zt[my - c0];
     } else {
-      for (int j = g; j < n; j += 16) {
-        const float zv = zt[j], v = zv + bs[j];
-        if (better(v, c0 + j, lv[KMAX - 1], li[KMAX - 1])) list_insert<KMAX>(lv, lz, li, v, zv, c0 + j);
+      float vr[RCH / 16];
+      float lmax = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < RCH / 16; ++q) {
+        const int j = min(g + 16 * q, n - 1);  // n is a multiple of 16
+        vr[q] = zt[j] + bs[j];
+        lmax = fmaxf(lmax, vr[q]);
+      }
+      // k rounds of a group max over the lane maxima, each dropping the lanes that hold
+      // the round's max (equal maxima dropped together only lower the bound)
+      float tau = __shfl(lv, k - 1, 16), cut = -INFINITY;
+      for (int j = 0; j < k; ++j) {
+        cut = group_max16(lmax);
+        if (lmax == cut) lmax = -INFINITY;
+      }
+      tau = fmaxf(tau, cut);
+      unsigned m = 0;
+#pragma unroll
+      for (int q = 0; q < RCH / 16; ++q)
+        if (16 * q < n && vr[q] >= tau) m |= 1u << q;
+      for (;;) {
+        const uint64_t act = __ballot(m != 0);
+        if (!act) break;  // the same in every lane
+        const unsigned gm = (unsigned)(act >> (lane & 48)) & 0xFFFFu;  // my group's lanes
+        const int src = gm ? __builtin_ctz(gm) : 0;
+        const unsigned ms = __shfl(m, src, 16);
+        const int jc = gm ? src + 16 * __builtin_ctz(ms) : 0;
+        if (gm && g == src) m &= m - 1;
+        const float cz = zt[jc], cv = cz + bs[jc];
+        const int ce = c0 + jc;
+        const bool keep = !gm || better(lv, li, cv, ce);
+        const int pk = row_shr1(keep ? 1 : 0, 1);
+        const float pv = row_shr1(lv, 0.f), pz = row_shr1(lz, 0.f);
+        const int pi = row_shr1(li, 0);
+        lv = keep ? lv : (pk ? cv : pv);
+        lz = keep ? lz : (pk ? cz : pz);
+        li = keep ? li : (pk ? ce : pi);
       }
     }
     __syncthreads();
     if (tid < n1) bs[tid] = bnext;
+    c0 = c1;
     n = n1;
   }
   if (!idx_in) {
-    for (int j = 0; j < k; ++j) {
-      float bv = lv[0], bz = lz[0];
-      int bi = li[0];
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) {  // every lane of the group ends with the winner
-        const float ov = __shfl_xor(bv, o, 16), oz = __shfl_xor(bz, o, 16);
-        const int oi = __shfl_xor(bi, o, 16);
-        if (better(ov, oi, bv, bi)) { bv = ov; bz = oz; bi = oi; }
-      }
-      if (g == j) { my = bi; myz = bz; }
-      if (li[0] == bi) {  // the owner pops its head
-#pragma unroll
-        for (int q = 0; q < KMAX - 1; ++q) { lv[q] = lv[q + 1]; lz[q] = lz[q + 1]; li[q] = li[q + 1]; }
-        lv[KMAX - 1] = -INFINITY;
-        li[KMAX - 1] = 0x7fffffff;
-      }
-    }
+    my = min(max(li, 0), E - 1);  // entries past the k-th are not used
+    myz = lz;
   }
   const float gv = g < k ? sigmoidf_(myz) : 0.f;
   float gsum = 0.f;  // in selection order, as the top-k kernel sums
@@ -313,22 +349,28 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
     int li[KMAX];
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) { lv[j] = -INFINITY; li[j] = 0x7fffffff; }
-    for (int e = lane; e < E; e += 64) {
+    // values below tau, the largest KMAX-th best of the 64 lane lists, cannot be selected
+    // (see the fused kernel); tau is refreshed after every 4 values of a lane
+    float tau = -INFINITY;
+    for (int e0 = 0; e0 < E; e0 += 64) {  // the same iterations in every lane
+      if ((e0 & 255) == 0 && e0 > 0)
+        tau = fmaxf(tau, max_xor32(max_xor16(group_max16(lv[KMAX - 1]))));
+      const int e = e0 + lane;
+      if (e >= E) continue;
       const float v = zt[e] + bias[e];
-      if (!better(v, e, lv[KMAX - 1], li[KMAX - 1])) continue;
-      // insert into the sorted list (unrolled bubble from the tail)
+      if (v < tau || !better(v, e, lv[KMAX - 1], li[KMAX - 1])) continue;
+      // insert into the sorted list (selects: straight-line compares and moves)
       float cv = v;
       int ci = e;
 #pragma unroll
       for (int j = 0; j < KMAX; ++j) {
-        if (better(cv, ci, lv[j], li[j])) {
-          const float tv = lv[j];
-          const int ti = li[j];
-          lv[j] = cv;
-          li[j] = ci;
-          cv = tv;
-          ci = ti;
-        }
+        const bool b = better(cv, ci, lv[j], li[j]);
+        const float nv = b ? cv : lv[j];
+        const int ni = b ? ci : li[j];
+        cv = b ? lv[j] : cv;
+        ci = b ? li[j] : ci;
+        lv[j] = nv;
+        li[j] = ni;
       }
     }
     for (int j = 0; j < k; ++j) {
@@ -366,7 +408,7 @@ int router_scores(int dtype, int64_t T, int h, int r, int E, int l, int L, const
   if (dtype == DT_BF16) {
     if (r % 32 || r > 256 || E % 16 || h % 32) return -1;
     const dim3 grid((unsigned)((T + 15) / 16), (unsigned)((E + RCH - 1) / RCH));
-    const size_t lds = 2 * 16 * (r + 4) * sizeof(float);
+    const size_t lds = 5 * 16 * (r + 4) * sizeof(float);
 #define RS_CASE(NK)                                                                      \
   dlaunch(router_scores_bf16_kernel<NK>, grid, 256, lds, st, T, h, r, E, l, L, (const bf16*)x, \
                                                         ldx, (const bf16*)w_r,            \
@@ -416,16 +458,11 @@ int router_route_fused(int64_t T, int h, int r, int E, int k, int l, int L, cons
   if (T <= 0) return 0;
   if (!router_fused_ok(DT_BF16, T, r, E, k) || h % 32) return -1;
   const unsigned grid = (unsigned)((T + 15) / 16);
-  const size_t lds = (2 * 16 * (r + 4) + 16 * RCH_LD + RCH) * sizeof(float);
-#define RF_CASE(NK, KM)                                                                     \
-  dlaunch(router_fused_bf16_kernel<NK, KM>, grid, 256, lds, st,                                  \
-      T, h, r, E, k, l, L, (const bf16*)x, ldx, (const bf16*)w_r, (const bf16*)keys, bias,  \
-      rho, normalize, cos_r, sin_r, idx_in, idx, gate)
-#define RF_K(NK)                      \
-  if (k <= 1) RF_CASE(NK, 1);         \
-  else if (k <= 2) RF_CASE(NK, 2);    \
-  else if (k <= 4) RF_CASE(NK, 4);    \
-  else RF_CASE(NK, 8);
+  const size_t lds = (16 * (r + 4) + RCH + std::max(16 * RCH_LD, 64 * (r + 4))) * sizeof(float);
+#define RF_K(NK)                                                                          \
+  dlaunch(router_fused_bf16_kernel<NK>, grid, 256, lds, st, T, h, r, E, k, l, L, (const bf16*)x, \
+          ldx, (const bf16*)w_r, (const bf16*)keys, bias, rho, normalize, cos_r, sin_r, idx_in, \
+          idx, gate)
   switch (r / 32) {
     case 1: RF_K(1); break;
     case 2: RF_K(2); break;
@@ -433,7 +470,6 @@ int router_route_fused(int64_t T, int h, int r, int E, int k, int l, int L, cons
     default: return -1;
   }
 #undef RF_K
-#undef RF_CASE
   return 0;
 }
 
@@ -558,15 +594,34 @@ __global__ __launch_bounds__(PERM_THREADS) void perm_scatter_kernel(
     ex[j] = s < nslots ? min(max(idx[s], 0), E - 1) : -1;
     gv[j] = (pgate && s < nslots) ? gate[s] : 0.f;
   }
-  for (int e = tid; e < E; e += PERM_THREADS) {
-    int tot = 0, pre = 0;
-    for (int q = 0; q < nb; ++q) {
-      const int v = hist[(int64_t)q * E + e];
-      tot += v;
-      pre += q < b ? v : 0;
+  // column sums of hist over 4 experts per thread, 8 chunk rows at a time: 32 loads in
+  // flight (clamped addresses, unused values dropped)
+  for (int eb = 0; eb < E; eb += 4 * PERM_THREADS) {
+    int tot[4] = {0, 0, 0, 0}, pre[4] = {0, 0, 0, 0};
+    for (int q0 = 0; q0 < nb; q0 += 8) {
+      int v[4][8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          v[j][u] = hist[(int64_t)min(q0 + u, nb - 1) * E + min(eb + j * PERM_THREADS + tid, E - 1)];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int vv = q0 + u < nb ? v[j][u] : 0;
+          tot[j] += vv;
+          pre[j] += q0 + u < b ? vv : 0;
+        }
     }
-    base[e] = tot;
-    prev[e] = pre;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = eb + j * PERM_THREADS + tid;
+      if (e < E) {
+        base[e] = tot[j];
+        prev[e] = pre[j];
+      }
+    }
   }
   __syncthreads();
   expert_offsets(base, prev, E, tile_m, b == 0, pad != 0, counts, goff, toff, tiles, s_wave);
@@ -584,7 +639,13 @@ __global__ void hist_colsum_kernel(const int32_t* __restrict__ hist, int nb, int
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= E) return;
   int c = 0;
-  for (int q = 0; q < nb; ++q) c += hist[(int64_t)q * E + e];
+  for (int q0 = 0; q0 < nb; q0 += 8) {  // 8 loads in flight
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = hist[(int64_t)min(q0 + u, nb - 1) * E + e];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) c += q0 + u < nb ? v[u] : 0;
+  }
   counts[e] = c;
 }
 
