@@ -380,7 +380,9 @@ int launch_gemm(const GemmArgs& a, int dtype, int out_f32, hipStream_t st) {
   if (a.qkv_h) {
     if (a.qkv_h % 128 || out_f32 || !a.rope_d4 || (a.sa_rope && !a.rope_s4)) return -1;
     if (a.toff && a.tile_m != 64) return -1;
-    if (a.toff || tiles(128, 128) < 256) {
+    if (!a.toff && k64 && tiles(256, 256) >= 256) {
+      dlaunch(gemm_bf16_kernel<bf16, GemmCfg<64, 64, 4, 4, 64, 4, 1, true>>, grid_of(256, 256), 1024, 0, st, a);
+    } else if (a.toff || tiles(128, 128) < 256) {
       if (k64)
         dlaunch(gemm_bf16_kernel<bf16, GemmCfg<32, 64, 2, 2, 128, 3, 2, false>>, grid_of(64, 128), 256, 0, st, a);
       else
