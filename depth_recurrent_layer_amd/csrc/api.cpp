@@ -296,12 +296,13 @@ static int route_impl(int dtype, int64_t T, int h, int r, int E, int k, int l, i
                       const void* x, int64_t ldx, const void* w_r, const void* keys,
                       const float* bias, float rho, int normalize, const float* cos_r,
                       const float* sin_r, int32_t* idx, float* gate, float* u, float* z,
-                      hipStream_t st, const int32_t* idx_in = nullptr) {
+                      hipStream_t st, const int32_t* idx_in = nullptr,
+                      int32_t* hist = nullptr) {
   int rc;
-  if (router_fused_ok(dtype, T, r, E, k)) {
+  if (router_fused_ok(dtype, T, r, E, k)) {  // counts the permutation's histograms if hist
     TB(DREAMER_KC_ROUTE);
     rc = router_route_fused(T, h, r, E, k, l, L, x, ldx, w_r, keys, bias, rho, normalize,
-                            cos_r, sin_r, idx_in, idx, gate, st);
+                            cos_r, sin_r, idx_in, idx, gate, st, hist);
     TE(DREAMER_KC_ROUTE);
     if (rc) return fail(DREAMER_E_UNSUPPORTED, "expert_route: unsupported shape");
     return ok();
@@ -391,7 +392,8 @@ size_t dreamer_expert_ffn_ws_bytes(int dtype, int kind, int64_t T, int h_in, int
 // slots by expert first (histogram unless the counts are already there, scan, scatter).
 static int ffn_slots(int dtype, int kind, int64_t T, int h_in, int f, int h_out, int E, int k,
                      const void* x, const int32_t* idx, const float* gate, const void* w1,
-                     const void* w3, const void* w2, const FfnWs& w, hipStream_t st) {
+                     const void* w3, const void* w2, const FfnWs& w, hipStream_t st,
+                     int32_t* hist_ready = nullptr, int32_t* zero_next = nullptr) {
   const int64_t ns = T * k;
   if (dtype == DREAMER_F32) {
     TB(DREAMER_KC_EXPERT_FFN);
@@ -403,9 +405,11 @@ static int ffn_slots(int dtype, int kind, int64_t T, int h_in, int f, int h_out,
   }
   TB(DREAMER_KC_PERMUTE);
   const bool fused = kind != DREAMER_FFN_LINEAR;
-  int prc = launch_permute(idx, ns, E, FFN_TILE_M, w.hist, w.counts, w.goff, w.toff, w.perm,
-                           st, fused ? gate : nullptr, fused ? w.pgate : nullptr,
-                           fused ? w.tiles : nullptr, fused ? 1 : 0);
+  // hist_ready: the router has counted the chunk histograms into that buffer
+  int prc = launch_permute(idx, ns, E, FFN_TILE_M, hist_ready ? hist_ready : w.hist, w.counts,
+                           w.goff, w.toff, w.perm, st, fused ? gate : nullptr,
+                           fused ? w.pgate : nullptr, fused ? w.tiles : nullptr, fused ? 1 : 0,
+                           hist_ready != nullptr, zero_next);
   TE(DREAMER_KC_PERMUTE);
   if (prc) return fail(DREAMER_E_UNSUPPORTED, "expert_ffn: E too large for the permutation");
   int rc;
@@ -503,6 +507,7 @@ struct LayerWs {
   float *y, *u, *z, *rgate, *pgate, *zero_pbias;
   int32_t *ridx, *pidx;
   FfnWs ffn;
+  int32_t* hist2;  // second chunk-histogram buffer (depths alternate; see layer_run)
   int32_t *pcounts, *pgoff, *ptoff, *phist, *pperm;
   void *da_k, *da_v, *sa_ws, *vt;
   size_t sa_ws_bytes;
@@ -543,6 +548,7 @@ static LayerWs plan_layer(Bump& b, const dreamer_layer_cfg* c, bool need_yb, boo
       w.rgate = b.take_n<float>(T * c->k);
     }
     w.ffn = plan_ffn(b, c->dtype, T, c->h, c->E, c->k);
+    w.hist2 = b.take_n<int32_t>((size_t)std::max(1, perm_blocks(T * c->k)) * c->E);
   }
   if (c->proj_experts) {
     const int Ep = c->proj_experts;
@@ -675,6 +681,10 @@ static int layer_run(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* 
     side_lock = std::unique_lock<std::mutex>(ss->mu);  // the fork/join event is shared
   }
   hipStream_t sd_ea = ss ? ss->s[0] : st;
+  // the fused router (bf16) counts the permutation's histograms
+  const bool fused_hist = c.use_ea && router_fused_ok(dt, T, c.r, c.E, k);
+  if (fused_hist)
+    launch_fill_i32(lw.ffn.hist, (int64_t)std::max(1, perm_blocks(T * k)) * c.E, 0, st);
   char* qkv = (char*)lw.qkv;
   char* att = (char*)lw.att;
 
@@ -705,13 +715,18 @@ static int layer_run(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* 
       rgate = route_gate ? route_gate + (size_t)l * T * k : lw.rgate;
     }
     // EA on `in` (storage dtype), leaving the gate-scaled expert outputs in the slots
+    // With the fused router the permutation's chunk histograms are counted during the
+    // selection, into the buffer of this depth's parity; the scatter then clears the
+    // other buffer for the next depth (the first was cleared before depth 0).
     auto ea = [&](const void* in, hipStream_t es_) -> int {
+      int32_t* hcur = fused_hist ? ((l & 1) ? lw.hist2 : lw.ffn.hist) : nullptr;
+      int32_t* hnext = fused_hist ? ((l & 1) ? lw.ffn.hist : lw.hist2) : nullptr;
       int r2 = route_impl(dt, T, c.h, c.r, c.E, k, l, L, in, h, w->w_r, w->keys, w->bias,
                           c.rho, c.normalize_gates, lw.cos_r, lw.sin_r, ridx, rgate, lw.u,
-                          lw.z, es_, route_in ? route_in + (size_t)l * T * k : nullptr);
+                          lw.z, es_, route_in ? route_in + (size_t)l * T * k : nullptr, hcur);
       if (r2) return r2;
       return ffn_slots(dt, c.ffn_kind, T, c.h, c.f, c.h, c.E, k, in, ridx, rgate, w->w1,
-                       w->w3, w->w2, lw.ffn, es_);
+                       w->w3, w->w2, lw.ffn, es_, hcur, hnext);
     };
     // Q/K/V projection of sections [sect0, sect0 + nsect) from `in` into qkv
     auto project_qkv = [&](const void* in, int sect0, int nsect) -> int {

@@ -107,11 +107,15 @@ int router_scores(int dtype, int64_t T, int h, int r, int E, int l, int L, const
 int router_topk(int64_t T, int E, int k, const float* z, const float* bias, int normalize,
                 const int32_t* idx_in, int32_t* idx, float* gate, hipStream_t st);
 // Scores and top-k in one kernel (bf16 only; router_fused_ok says when it applies).
+// hist (optional, [perm_blocks(T * k), E], zero on entry): the permutation's chunk
+// histograms are counted here with global atomics (slot t * k + j in chunk
+// (t * k + j) / PERM_CHUNK), so launch_permute can skip its histogram kernel.
 bool router_fused_ok(int dtype, int64_t T, int r, int E, int k);
 int router_route_fused(int64_t T, int h, int r, int E, int k, int l, int L, const void* x,
                        int64_t ldx, const void* w_r, const void* keys, const float* bias,
                        float rho, int normalize, const float* cos_r, const float* sin_r,
-                       const int32_t* idx_in, int32_t* idx, float* gate, hipStream_t st);
+                       const int32_t* idx_in, int32_t* idx, float* gate, hipStream_t st,
+                       int32_t* hist = nullptr);
 
 // Fill n ints with a value (graph-safe replacement of memset).
 void launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st);
@@ -123,13 +127,16 @@ void launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st);
 // [tile_bound(nslots, E, tile_m)] = {expert, first row, end of the expert's rows, 0} per
 // m-tile (the first toff[E] entries are written).  pad: perm and pgate are tile-padded
 // instead ([tile_bound * tile_m]: row j of m-tile t at t * tile_m + j; the rows past an
-// expert's end in its last tile are left unwritten).
+// expert's end in its last tile are left unwritten).  hist_ready: hist already holds the
+// chunk histograms (counted by the fused router); zero_next (optional): another buffer
+// of the hist shape that the scatter clears, ready for the next histogram.
 constexpr int PERM_CHUNK = 2048, PERM_MAX_E = 8192, COUNT_MAX_E = 16384;
 int perm_blocks(int64_t nslots);
 int launch_permute(const int32_t* idx, int64_t nslots, int E, int tile_m, int32_t* hist,
                    int32_t* counts, int32_t* goff, int32_t* toff, int32_t* perm,
                    hipStream_t st, const float* gate = nullptr, float* pgate = nullptr,
-                   int4* tiles = nullptr, int pad = 0);
+                   int4* tiles = nullptr, int pad = 0, bool hist_ready = false,
+                   int32_t* zero_next = nullptr);
 inline int64_t tile_bound(int64_t nslots, int E, int tile_m) { return nslots / tile_m + E + 1; }
 // counts [E] of routed slots per expert (hist as above).
 int launch_counts(const int32_t* idx, int64_t nslots, int E, int32_t* hist, int32_t* counts,

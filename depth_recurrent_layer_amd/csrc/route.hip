@@ -198,7 +198,7 @@ __global__ __launch_bounds__(256) void router_fused_bf16_kernel(
     int64_t ldx, const bf16* __restrict__ w_r, const bf16* __restrict__ keys,
     const float* __restrict__ bias, float rho, int normalize, const float* __restrict__ cs,
     const float* __restrict__ sn, const int32_t* __restrict__ idx_in, int32_t* __restrict__ idx,
-    float* __restrict__ gate) {
+    float* __restrict__ gate, int32_t* __restrict__ hist) {
   extern __shared__ float smem[];
   float* bs = smem + 16 * (r + 4);  // [RCH] bias chunk (after u's [16][r + 4])
   float* zs = bs + RCH;  // [16][RCH_LD] scores; first the projection's partial tiles
@@ -299,6 +299,7 @@ __global__ __launch_bounds__(256) void router_fused_bf16_kernel(
   if (t < Ttok && g < k) {
     idx[t * k + g] = my;
     gate[t * k + g] = normalize ? gv / gsum : gv;
+    if (hist) atomicAdd(&hist[((t * k + g) / PERM_CHUNK) * E + my], 1);
   }
 }
 
@@ -454,7 +455,8 @@ bool router_fused_ok(int dtype, int64_t T, int r, int E, int k) {
 int router_route_fused(int64_t T, int h, int r, int E, int k, int l, int L, const void* x,
                        int64_t ldx, const void* w_r, const void* keys, const float* bias,
                        float rho, int normalize, const float* cos_r, const float* sin_r,
-                       const int32_t* idx_in, int32_t* idx, float* gate, hipStream_t st) {
+                       const int32_t* idx_in, int32_t* idx, float* gate, hipStream_t st,
+                       int32_t* hist) {
   if (T <= 0) return 0;
   if (!router_fused_ok(DT_BF16, T, r, E, k) || h % 32) return -1;
   const unsigned grid = (unsigned)((T + 15) / 16);
@@ -462,7 +464,7 @@ int router_route_fused(int64_t T, int h, int r, int E, int k, int l, int L, cons
 #define RF_K(NK)                                                                          \
   dlaunch(router_fused_bf16_kernel<NK>, grid, 256, lds, st, T, h, r, E, k, l, L, (const bf16*)x, \
           ldx, (const bf16*)w_r, (const bf16*)keys, bias, rho, normalize, cos_r, sin_r, idx_in, \
-          idx, gate)
+          idx, gate, hist)
   switch (r / 32) {
     case 1: RF_K(1); break;
     case 2: RF_K(2); break;
@@ -474,8 +476,9 @@ int router_route_fused(int64_t T, int h, int r, int E, int k, int l, int L, cons
 }
 
 // ----------------------------------------------------------------------------- permute
-// Routed slots grouped by expert without global atomics.  The slots are cut into chunks
-// of PERM_CHUNK; kernel 1 counts each chunk's slots per expert in LDS (hist [nb, E]);
+// Routed slots grouped by expert.  The slots are cut into chunks of PERM_CHUNK; kernel 1
+// counts each chunk's slots per expert in LDS (hist [nb, E]; in the layer the fused
+// router counts them instead, with global atomics, and kernel 1 is skipped);
 // kernel 2, one block per chunk, sums the hist columns before its chunk and in total,
 // scans the totals over experts (rows, and m-tiles of tile_m rows) and hands out its
 // slots' positions with LDS atomics.  Block 0 publishes counts, goff and toff.  Expert
@@ -579,7 +582,7 @@ __global__ __launch_bounds__(PERM_THREADS) void perm_scatter_kernel(
     const int32_t* __restrict__ idx, int64_t nslots, int E, int nb, int tile_m,
     const int32_t* __restrict__ hist, int32_t* __restrict__ counts, int32_t* __restrict__ goff,
     int32_t* __restrict__ toff, int32_t* __restrict__ perm, const float* __restrict__ gate,
-    float* __restrict__ pgate, int4* __restrict__ tiles, int pad) {
+    float* __restrict__ pgate, int4* __restrict__ tiles, int pad, int32_t* __restrict__ zero_next) {
   extern __shared__ int sh[];  // base [E] (totals, then cursors), prev [E]
   int* base = sh;
   int* prev = sh + E;
@@ -632,6 +635,9 @@ __global__ __launch_bounds__(PERM_THREADS) void perm_scatter_kernel(
       perm[pos] = (int32_t)(s0 + j * PERM_THREADS + tid);
       if (pgate) pgate[pos] = gv[j];
     }
+  if (zero_next)
+    for (int64_t i = (int64_t)b * PERM_THREADS + tid; i < (int64_t)nb * E; i += (int64_t)nb * PERM_THREADS)
+      zero_next[i] = 0;
 }
 
 __global__ void hist_colsum_kernel(const int32_t* __restrict__ hist, int nb, int E,
@@ -651,14 +657,14 @@ __global__ void hist_colsum_kernel(const int32_t* __restrict__ hist, int nb, int
 
 int launch_permute(const int32_t* idx, int64_t nslots, int E, int tile_m, int32_t* hist,
                    int32_t* counts, int32_t* goff, int32_t* toff, int32_t* perm,
-                   hipStream_t st, const float* gate, float* pgate, int4* tiles, int pad) {
+                   hipStream_t st, const float* gate, float* pgate, int4* tiles, int pad,
+                   bool hist_ready, int32_t* zero_next) {
   if (E <= 0 || E > PERM_MAX_E) return -1;
   const size_t lds = (size_t)E * sizeof(int);
   const int nb = perm_blocks(nslots);
-  dlaunch(perm_hist_kernel, nb, 512, lds, st, idx, nslots, E, hist);
+  if (!hist_ready) dlaunch(perm_hist_kernel, nb, 512, lds, st, idx, nslots, E, hist);
   dlaunch(perm_scatter_kernel, nb, PERM_THREADS, 2 * lds, st, idx, nslots, E, nb, tile_m, hist,
-                                                         counts, goff, toff, perm, gate, pgate,
-                                                         tiles, pad);
+          counts, goff, toff, perm, gate, pgate, tiles, pad, zero_next);
   return 0;
 }
 
