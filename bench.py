@@ -24,8 +24,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3       # fp32 vector
 METRIC = "token-depth-steps/sec, Dreamer layer fwd; % of HBM BW / MFMA peak"
-CLASSES = ["qkv_proj", "out_proj", "seq_attn", "depth_attn", "route", "permute", "expert_ffn",
-           "combine"]
+CLASSES = ["qkv_proj", "out_proj", "seq_attn", "depth_attn", "attention", "route", "permute",
+           "expert_ffn", "combine"]
 
 
 def parse():
@@ -102,6 +102,9 @@ def algorithmic_work(cfg, counts_per_depth, reps=1):
     da_bytes = sum(T * h * es * (6 + 2 * (n_depth_keys(l, cfg.da_window, cfg.da_dilation) - 1))
                    for l in range(L))
     w["depth_attn"] = dict(bound="hbm", bytes=da_bytes, launches=L)
+    # SA and DA in one launch: priced by its SA flops alone against the MFMA peak (a lower
+    # bound of its fraction: the DA share of the launch is not counted)
+    w["attention"] = dict(bound="mfma", flops=w["seq_attn"].get("flops", 0), launches=L)
     nw = 3 if cfg.ffn == "swiglu" else 2
     w["expert_ffn"] = dict(bound="hbm", bytes=L * 2 * T * k * h * es,
                            flops=L * 2 * T * k * nw * h * f, launches=L)
@@ -182,13 +185,14 @@ DEPTH_WINDOWS = [(0, 0), (4, 4), (2, 0)]
 
 def time_depth_windows(D, cfg, G, x0, steps):
     """Windowed / dilated depth attention: ms per forward, DA kernel ms per forward and the
-    algorithmic DA bytes per forward for each (window, dilation) of DEPTH_WINDOWS."""
+    algorithmic DA bytes per forward for each (window, dilation) of DEPTH_WINDOWS.  DA runs
+    in its own launches here (fuse_attn off) so that its time can be taken alone."""
     import torch
     out = {}
     x_out = torch.empty((cfg.T, cfg.h), dtype=torch.float32, device="cuda")
     for w, dil in DEPTH_WINDOWS:
         c = cfg.replace(da_window=w, da_dilation=dil)
-        lc = layer_cfg(D, c)
+        lc = layer_cfg(D, c, fuse_attn=False)
         ws = torch.empty(D.layer_ws_bytes(lc), dtype=torch.uint8, device="cuda")
         for _ in range(3):
             D.dreamer_layer_forward(lc, G, x0, x_out=x_out, ws=ws)
@@ -211,14 +215,15 @@ def time_depth_windows(D, cfg, G, x0, steps):
     return out
 
 
-def layer_cfg(D, cfg, cap=0, mixture="partial"):
+def layer_cfg(D, cfg, cap=0, mixture="partial", fuse_attn=True):
     return D.make_layer_cfg(dtype=cfg.dtype, b=cfg.b, s=cfg.s, h=cfg.h, H=cfg.H, d=cfg.d,
                             L=cfg.L, E=cfg.E, k=cfg.k, f=cfg.f, r=cfg.r, ffn=cfg.ffn,
                             normalize=cfg.normalize, proj_experts=cfg.proj_experts,
                             decode=cfg.decode, sa_pos=cfg.sa_pos, sa_cap=cap,
                             rope_base=cfg.rope_base, rms_eps=cfg.rms_eps, rho=cfg.rho,
                             mixture=D.MIXTURES[mixture], branch_streams=mixture == "parallel",
-                            da_window=cfg.da_window, da_dilation=cfg.da_dilation)
+                            da_window=cfg.da_window, da_dilation=cfg.da_dilation,
+                            fuse_attn=fuse_attn)
 
 
 def usage_report(D, cfg, G, x0, lc, route, iters=20, lam=0.01):

@@ -82,6 +82,19 @@ void timing_end(int kclass, hipStream_t st) {
 }
 }  // namespace dreamer
 
+// compute units of the current device (cached per device)
+static int cu_count() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 #define TB(kc) timing_begin(kc, st)
 #define TE(kc) timing_end(kc, st)
 
@@ -133,7 +146,7 @@ int dreamer_version(void) { return 100; }
 
 int dreamer_timing_enable(int kclass, int max_launches) {
   dreamer_timing_disable();
-  if (kclass < DREAMER_KC_GEMM || kclass > DREAMER_KC_OUT_PROJ || max_launches <= 0)
+  if (kclass < DREAMER_KC_GEMM || kclass > DREAMER_KC_ATTN || max_launches <= 0)
     return fail(DREAMER_E_INVAL, "timing_enable: bad class or count");
   g_tm.ev0.resize(max_launches);
   g_tm.ev1.resize(max_launches);
@@ -681,6 +694,11 @@ static int layer_run(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* 
     side_lock = std::unique_lock<std::mutex>(ss->mu);  // the fork/join event is shared
   }
   hipStream_t sd_ea = ss ? ss->s[0] : st;
+  // SA and DA in one launch where the flash grid alone would leave CUs idle in its tail:
+  // its blocks (query blocks x heads x batch) fit the GPU at three per CU
+  const bool pair_attn = c.fuse_attn && c.use_da && !serial && !sa_k && !c.decode &&
+                         attn_pair_ok(dt, c.b, c.s, c.H, c.d, 0, lw.vt) &&
+                         (int64_t)((c.s + 63) / 64) * c.H * c.b <= 3 * (int64_t)cu_count();
   // the fused router (bf16) counts the permutation's histograms
   const bool fused_hist = c.use_ea && router_fused_ok(dt, T, c.r, c.E, k);
   if (fused_hist)
@@ -844,8 +862,18 @@ static int layer_run(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* 
     } else {
       // y = xh + [a_SA | a_DA] W_o^T
       if ((rc = project_qkv(lw.xh, 0, c.use_da ? 6 : 3))) return rc;
-      if ((rc = run_sa())) return rc;
-      if (c.use_da && (rc = run_da(st))) return rc;
+      if (pair_attn) {
+        TB(DREAMER_KC_ATTN);
+        int r2 = launch_attn_pair(c.b, c.s, c.H, l, L, qkv, qkv + h * es, lw.vt,
+                                  qkv + 3 * h * es, qkv + 4 * h * es, qkv + 5 * h * es, 6 * h,
+                                  DAk, DAv, att, att + h * es, 2 * h, scale, c.da_window,
+                                  c.da_dilation, st);
+        TE(DREAMER_KC_ATTN);
+        if (r2) return fail(DREAMER_E_UNSUPPORTED, "layer: paired attention shape");
+      } else {
+        if ((rc = run_sa())) return rc;
+        if (c.use_da && (rc = run_da(st))) return rc;
+      }
       if ((rc = project_o(0, c.use_da ? 2 * (int)h : (int)h, resid, yb))) return rc;
     }
     if (c.use_ea) {

@@ -81,17 +81,18 @@ DEV void rope_chunk(float* x, int c, int d, int pos_fwd, int pos_rev, const floa
 // slots 0..l with an online softmax.  The current slot is used from registers.
 // window > 0 keeps only the slots l-window+1..l and, with dilation > 0, the older slots j
 // with (l - j) divisible by dilation; the skipped slots are never loaded.
+// Block blk of 256 threads (the body of depth_attn_kernel and of the paired launch).
 template <typename T, int LPH, bool ROPE>
-__global__ __launch_bounds__(256) void depth_attn_kernel(
-    int64_t rows, int H, int d, int l, int L, const T* __restrict__ q, int64_t ldq,
-    const T* __restrict__ kn, int64_t ldk, const T* __restrict__ vn, int64_t ldv,
+DEV void depth_attn_block(
+    int64_t blk, int64_t rows, int H, int d, int l, int L, const T* __restrict__ q,
+    int64_t ldq, const T* __restrict__ kn, int64_t ldk, const T* __restrict__ vn, int64_t ldv,
     T* __restrict__ kc, T* __restrict__ vc, T* __restrict__ out, int64_t ldo,
     const float* __restrict__ cosd, const float* __restrict__ sind, float scale, int window,
     int dilation) {
   constexpr int VEC = Vec16<T>::N;
   const int h = H * d;
   const int cpr = h / VEC;  // chunks per row
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t gid = blk * 256 + threadIdx.x;
   const int64_t row = gid / cpr;
   if (row >= rows) return;  // whole heads leave together (cpr is a multiple of LPH)
   const int chunk = (int)(gid % cpr);
@@ -170,6 +171,17 @@ __global__ __launch_bounds__(256) void depth_attn_kernel(
 #pragma unroll
   for (int i = 0; i < VEC; ++i) acc[i] *= inv;
   store16(out + row * ldo + col, acc);
+}
+
+template <typename T, int LPH, bool ROPE>
+__global__ __launch_bounds__(256) void depth_attn_kernel(
+    int64_t rows, int H, int d, int l, int L, const T* __restrict__ q, int64_t ldq,
+    const T* __restrict__ kn, int64_t ldk, const T* __restrict__ vn, int64_t ldv,
+    T* __restrict__ kc, T* __restrict__ vc, T* __restrict__ out, int64_t ldo,
+    const float* __restrict__ cosd, const float* __restrict__ sind, float scale, int window,
+    int dilation) {
+  depth_attn_block<T, LPH, ROPE>(blockIdx.x, rows, H, d, l, L, q, ldq, kn, ldk, vn, ldv, kc, vc,
+                                 out, ldo, cosd, sind, scale, window, dilation);
 }
 
 int launch_depth_attn(int dtype, int64_t rows, int H, int d, int l, int L, const void* q,
@@ -415,15 +427,15 @@ DEV int key_of_row(int r) {
   return (r & 32) + ((r >> 2) & 3) * 8 + ((r >> 4) & 1) * 4 + (r & 3);
 }
 
-__global__ __launch_bounds__(256, 3) void sa_flash_kernel(
-    int B, int S, int H, const bf16* __restrict__ q, int64_t ldq, const bf16* __restrict__ kk,
-    int64_t ldk, const bf16* __restrict__ vt, bf16* __restrict__ out, int64_t ldo,
-    float scale) {
+// Query block qbx (counted from the last: heavy blocks first), head, batch b; stg: the
+// block's 3 x 16 KiB ring in LDS (1 KiB aligned).
+DEV void sa_flash_block(int qbx, int head, int b, int S, int H, const bf16* __restrict__ q,
+                        int64_t ldq, const bf16* __restrict__ kk, int64_t ldk,
+                        const bf16* __restrict__ vt, bf16* __restrict__ out, int64_t ldo,
+                        float scale, char (*stg)[2 * fa::TILE]) {
   using namespace fa;
-  __shared__ __attribute__((aligned(1024))) char stg[NSTG][2 * TILE];
   const int nqb = (S + BQ - 1) / BQ;
-  const int qb = nqb - 1 - (int)blockIdx.x;  // heavy (late) query blocks first
-  const int head = blockIdx.y, b = blockIdx.z;
+  const int qb = nqb - 1 - qbx;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int64_t tok0 = (int64_t)b * S;
@@ -478,7 +490,7 @@ __global__ __launch_bounds__(256, 3) void sa_flash_kernel(
   const int qlast = min(qb * BQ + BQ, S) - 1;
   const int qlim = min(qpos, S - 1);
   const int nkt = qlast / BKEY + 1;
-  const uint32_t stg0 = lds_off(stg);
+  const uint32_t stg0 = lds_off(stg[0]);
   // per-lane fragment offsets within a tile (row lr; tile rows 16t + lr follow at 2048 t)
   const uint32_t kofs0 = 2 * swz128(lr, lg), kofs1 = 2 * swz128(lr, 4 + lg);
   const uint32_t vofs0 = kofs0, vofs1 = kofs1;
@@ -564,6 +576,56 @@ __global__ __launch_bounds__(256, 3) void sa_flash_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = (bf16)(o[t][i] * inv);
     *reinterpret_cast<bf16x4*>(orow + t * 16 + lg * 4) = v;
+  }
+}
+
+__global__ __launch_bounds__(256, 3) void sa_flash_kernel(
+    int B, int S, int H, const bf16* __restrict__ q, int64_t ldq, const bf16* __restrict__ kk,
+    int64_t ldk, const bf16* __restrict__ vt, bf16* __restrict__ out, int64_t ldo,
+    float scale) {
+  __shared__ __attribute__((aligned(1024))) char stg[fa::NSTG][2 * fa::TILE];
+  sa_flash_block(blockIdx.x, blockIdx.y, blockIdx.z, S, H, q, ldq, kk, ldk, vt, out, ldo, scale,
+                 stg);
+}
+
+// SA (flash, prepared inputs) and DA (bf16, head dim 64, inputs already rotated) of one
+// depth in one launch: blocks [0, nsa) are the flash blocks in the flash grid's order,
+// the rest the depth-attention blocks.  The two write disjoint outputs and read only the
+// projections, so the DA blocks fill the CUs that the causal flash grid leaves idle in
+// its tail (its last query blocks are the longest).
+struct SaFlashArgs {
+  int S, H;
+  const bf16* q;
+  int64_t ldq;
+  const bf16* kk;
+  int64_t ldk;
+  const bf16* vt;
+  bf16* out;
+  int64_t ldo;
+  float scale;
+};
+struct DaArgs {
+  int64_t rows;
+  int H, l, L;
+  const bf16 *q, *kn, *vn;
+  int64_t ldq, ldk, ldv;
+  bf16 *kc, *vc, *out;
+  int64_t ldo;
+  float scale;
+  int window, dilation;
+};
+
+__global__ __launch_bounds__(256, 3) void attn_pair_kernel(SaFlashArgs sa, DaArgs da, int nsa) {
+  __shared__ __attribute__((aligned(1024))) char stg[fa::NSTG][2 * fa::TILE];
+  const int bi = blockIdx.x;
+  if (bi < nsa) {
+    const int nqb = (sa.S + fa::BQ - 1) / fa::BQ;
+    sa_flash_block(bi % nqb, (bi / nqb) % sa.H, bi / (nqb * sa.H), sa.S, sa.H, sa.q, sa.ldq,
+                   sa.kk, sa.ldk, sa.vt, sa.out, sa.ldo, sa.scale, stg);
+  } else {
+    depth_attn_block<bf16, 8, false>(bi - nsa, da.rows, da.H, 64, da.l, da.L, da.q, da.ldq, da.kn,
+                                     da.ldk, da.vn, da.ldv, da.kc, da.vc, da.out, da.ldo, nullptr,
+                                     nullptr, da.scale, da.window, da.dilation);
   }
 }
 
@@ -754,6 +816,28 @@ int launch_seq_attn(int dtype, int B, int q_len, int H, int d, int64_t pos0, con
                             sin_s, rope, scale, 1, q_len, nullptr, nullptr, st)
             : sa_rows<float>(lph, B, q_len, H, d, 0, q, ldq, kb, vb, q_len, out, ldo, cos_s,
                              sin_s, rope, scale, 1, q_len, nullptr, nullptr, st);
+}
+
+bool attn_pair_ok(int dtype, int B, int q_len, int H, int d, int64_t pos0, const void* vt) {
+  return dtype == DT_BF16 && d == 64 && pos0 == 0 && vt && B > 0 && flash_ok(dtype, d, q_len);
+}
+
+int launch_attn_pair(int B, int S, int H, int l, int L, const void* q, const void* k,
+                     const void* vt, const void* dq, const void* dk, const void* dv,
+                     int64_t ldqkv, void* dkc, void* dvc, void* out_sa, void* out_da,
+                     int64_t ldo, float scale, int window, int dilation, hipStream_t st) {
+  if (!attn_pair_ok(DT_BF16, B, S, H, 64, 0, vt)) return -1;
+  const int nqb = (S + fa::BQ - 1) / fa::BQ;
+  const int64_t nsa = (int64_t)nqb * H * B;
+  const int64_t rows = (int64_t)B * S;
+  const int64_t nda = (rows * H * 8 + 255) / 256;  // 8 lanes per head of 64
+  if (nsa + nda > 0x7fffffff) return -1;
+  SaFlashArgs sa{S, H, (const bf16*)q, ldqkv, (const bf16*)k, ldqkv, (const bf16*)vt,
+                 (bf16*)out_sa, ldo, scale};
+  DaArgs da{rows, H, l, L, (const bf16*)dq, (const bf16*)dk, (const bf16*)dv, ldqkv, ldqkv,
+            ldqkv, (bf16*)dkc, (bf16*)dvc, (bf16*)out_da, ldo, scale, window, dilation};
+  dlaunch(attn_pair_kernel, (unsigned)(nsa + nda), 256, 0, st, sa, da, (int)nsa);
+  return 0;
 }
 
 }  // namespace dreamer

@@ -95,6 +95,15 @@ int launch_seq_attn(int dtype, int B, int q_len, int H, int d, int64_t pos0, con
                     const void* vt, void* kc, void* vc, int64_t cap, void* out, int64_t ldo,
                     const float* cos_s, const float* sin_s, float scale, int rope, void* ws,
                     size_t ws_bytes, hipStream_t st);
+// SA and DA of one depth in one launch (bf16 prefill, head dim 64, flash-prepared SA
+// inputs: rotated q / k rows and v transposed; DA q / k already rotated): the flash grid's
+// blocks first, then the DA blocks.  q, k: SA rows; dq, dk, dv: the DA projections; all
+// with row stride ldqkv; outputs with stride ldo.  attn_pair_ok says when it applies.
+bool attn_pair_ok(int dtype, int B, int q_len, int H, int d, int64_t pos0, const void* vt);
+int launch_attn_pair(int B, int S, int H, int l, int L, const void* q, const void* k,
+                     const void* vt, const void* dq, const void* dk, const void* dv,
+                     int64_t ldqkv, void* dkc, void* dvc, void* out_sa, void* out_da,
+                     int64_t ldo, float scale, int window, int dilation, hipStream_t st);
 
 // Router scores z [T, E] f32 = rho * RoPE_depth(x W_r^T) . keys.  bf16: u computed inside
 // (u ignored; needs r % 32 == 0, E % 16 == 0); f32: reads u = x W_r^T [T, r].

@@ -27,7 +27,7 @@ FFN_KINDS = {"gelu": FFN_GELU, "swiglu": FFN_SWIGLU, "linear": FFN_LINEAR}
 MIX_PARTIAL, MIX_SERIAL, MIX_PARALLEL = 0, 1, 2
 MIXTURES = {"partial": MIX_PARTIAL, "serial": MIX_SERIAL, "parallel": MIX_PARALLEL}
 KC = {"qkv_proj": 1, "seq_attn": 2, "depth_attn": 3, "route": 4, "permute": 5,
-      "expert_ffn": 6, "combine": 7, "out_proj": 8}
+      "expert_ffn": 6, "combine": 7, "out_proj": 8, "attention": 9}
 
 _vp, _i64, _i32, _f32, _f64, _sz = C.c_void_p, C.c_int64, C.c_int, C.c_float, C.c_double, C.c_size_t
 
@@ -39,7 +39,8 @@ class LayerCfg(C.Structure):
                 ("use_ea", _i32), ("sa_rope", _i32), ("proj_experts", _i32),
                 ("mixture", _i32), ("decode", _i32), ("sa_pos", _i64), ("sa_cap", _i64),
                 ("rope_base", _f64), ("rms_eps", _f32), ("rho", _f32),
-                ("branch_streams", _i32), ("da_window", _i32), ("da_dilation", _i32)]
+                ("branch_streams", _i32), ("da_window", _i32), ("da_dilation", _i32),
+                ("fuse_attn", _i32)]
 
 
 class LayerWeights(C.Structure):
@@ -228,7 +229,7 @@ def make_layer_cfg(*, dtype, b, s, h, H, d, L, E, k, f, r, ffn="swiglu", normali
                    use_da=True, use_ea=True, sa_rope=True, proj_experts=0, decode=False,
                    sa_pos=0, sa_cap=0, rope_base=10000.0, rms_eps=1e-6, rho=1.0,
                    mixture=MIX_PARTIAL, branch_streams=False, da_window=0,
-                   da_dilation=0) -> LayerCfg:
+                   da_dilation=0, fuse_attn=True) -> LayerCfg:
     return LayerCfg(dtype=BF16 if dtype in ("bf16", BF16) else F32, b=b, s=s, h=h, H=H, d=d,
                     L=L, E=E, k=k, f=f, r=r, ffn_kind=FFN_KINDS[ffn] if isinstance(ffn, str) else ffn,
                     normalize_gates=int(bool(normalize)), use_da=int(bool(use_da)),
@@ -236,7 +237,7 @@ def make_layer_cfg(*, dtype, b, s, h, H, d, L, E, k, f, r, ffn="swiglu", normali
                     proj_experts=proj_experts, mixture=mixture, decode=int(bool(decode)),
                     sa_pos=sa_pos, sa_cap=sa_cap, rope_base=rope_base, rms_eps=rms_eps, rho=rho,
                     branch_streams=int(bool(branch_streams)), da_window=da_window,
-                    da_dilation=da_dilation)
+                    da_dilation=da_dilation, fuse_attn=int(bool(fuse_attn)))
 
 
 def layer_ws_bytes(cfg: LayerCfg) -> int:

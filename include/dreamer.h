@@ -238,6 +238,11 @@ typedef struct dreamer_layer_cfg {
   int da_window;        /* 0: DA over every depth 0..l; w > 0: only the w most recent  */
   int da_dilation;      /* with da_window > 0 and this > 0: also every da_dilation-th
                            older depth (see dreamer_depth_attn_windowed)               */
+  int fuse_attn;        /* 1: SA and DA of a depth may share one launch (bf16 prefill,
+                           PARTIAL / PARALLEL, head dim 64, no SA cache output, and the
+                           causal flash grid fits the GPU in one round): the DA blocks
+                           fill the CUs the flash grid's tail leaves idle.  Same bits
+                           either way; timed as DREAMER_KC_ATTN.  0: separate launches */
 } dreamer_layer_cfg;
 
 typedef struct dreamer_layer_weights {
@@ -334,6 +339,7 @@ int dreamer_decode_tokens(const dreamer_layer_cfg* cfg, const dreamer_layer_weig
 #define DREAMER_KC_EXPERT_FFN 6
 #define DREAMER_KC_COMBINE 7    /* combine + RMSNorm (and the first RMSNorm)           */
 #define DREAMER_KC_OUT_PROJ 8   /* output projection + residual                        */
+#define DREAMER_KC_ATTN 9       /* SA and DA in one launch (dreamer_layer_cfg.fuse_attn) */
 int dreamer_timing_enable(int kclass, int max_launches);
 int dreamer_timing_read(int* n_launches, double* total_ms);
 int dreamer_timing_disable(void);

@@ -35,7 +35,7 @@ def rms_normed(x):
     return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + 1e-6)
 
 
-def lib_cfg(D, cfg, sa_cap=0, streams=False):
+def lib_cfg(D, cfg, sa_cap=0, streams=False, fuse_attn=True):
     return D.make_layer_cfg(dtype=cfg.dtype, b=cfg.b, s=cfg.s, h=cfg.h, H=cfg.H, d=cfg.d, L=cfg.L,
                             E=cfg.E, k=cfg.k, f=cfg.f, r=cfg.r, ffn=cfg.ffn,
                             normalize=cfg.normalize, use_da=cfg.use_da, use_ea=cfg.use_ea,
@@ -43,7 +43,8 @@ def lib_cfg(D, cfg, sa_cap=0, streams=False):
                             decode=cfg.decode, sa_pos=cfg.sa_pos, sa_cap=sa_cap,
                             rope_base=cfg.rope_base, rms_eps=cfg.rms_eps, rho=cfg.rho,
                             mixture=D.MIXTURES[cfg.mixture], branch_streams=streams,
-                            da_window=cfg.da_window, da_dilation=cfg.da_dilation)
+                            da_window=cfg.da_window, da_dilation=cfg.da_dilation,
+                            fuse_attn=fuse_attn)
 
 
 def gpu_weights(D, cfg, W):

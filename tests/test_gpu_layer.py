@@ -18,11 +18,13 @@ from synth.configs import make_sa_cache
 pytestmark = pytest.mark.gpu
 
 
-def run_gpu(D, cfg, W, x0, sa_cache=None, sa_cap=0, replay=None, streams=False):
+def run_gpu(D, cfg, W, x0, sa_cache=None, sa_cap=0, replay=None, streams=False,
+            fuse_attn=True):
     """replay: an oracle result whose expert choices the GPU adopts (route_in);
-    streams: independent branches on the library's side streams."""
+    streams: independent branches on the library's side streams; fuse_attn: SA and DA
+    of a depth may share one launch."""
     G = gpu_weights(D, cfg, W)
-    lc = lib_cfg(D, cfg, sa_cap=sa_cap, streams=streams)
+    lc = lib_cfg(D, cfg, sa_cap=sa_cap, streams=streams, fuse_attn=fuse_attn)
     T = cfg.T
     x = x0.reshape(T, cfg.h).float().cuda().contiguous()
     route = proj = None
@@ -338,6 +340,27 @@ def test_layer_branch_streams_same_bits(gpu_lib, mixture):
     a = run_gpu(gpu_lib, cfg, W, x0)
     b = run_gpu(gpu_lib, cfg, W, x0, streams=True)
     assert np.array_equal(a["x_out"], b["x_out"]) and np.array_equal(a["idx"], b["idx"])
+
+
+@pytest.mark.parametrize("mixture,window,dilation", [("partial", 0, 0), ("parallel", 0, 0),
+                                                     ("partial", 2, 3)])
+def test_layer_paired_attention_same_bits(gpu_lib, mixture, window, dilation):
+    """SA and DA in one launch give the same bits as separate launches, and the paired
+    launch is the one that runs (one per depth, no separate SA / DA launches)."""
+    D = gpu_lib
+    cfg = CONFIGS["small"].replace(b=2, s=96, L=5, mixture=mixture, da_window=window,
+                                   da_dilation=dilation)
+    print(f"layer paired attention {mixture} window {window} dilation {dilation}", flush=True)
+    W, x0 = make_weights(cfg), make_x0(cfg)
+    a = run_gpu(D, cfg, W, x0, fuse_attn=False)
+    counts = {}
+    for kc in ("attention", "seq_attn", "depth_attn"):
+        D.timing_enable(kc, 64)
+        b = run_gpu(D, cfg, W, x0, fuse_attn=True)
+        counts[kc] = D.timing_read()[0]
+        D.timing_disable()
+        assert np.array_equal(a["x_out"], b["x_out"]) and np.array_equal(a["idx"], b["idx"])
+    assert counts == {"attention": cfg.L, "seq_attn": 0, "depth_attn": 0}, counts
 
 
 # ------------------------------------------------------------------ multi-token decode
