@@ -22,17 +22,21 @@
 
 namespace dreamer {
 
-#ifndef DREAMER_FFN_LDS
-#define DREAMER_FFN_LDS (78 * 1024)  // ring budget per block (two blocks per CU)
-#endif
-#ifndef DREAMER_FFN_OCC
-#define DREAMER_FFN_OCC 2
+// Blocks per CU and the ring's LDS budget per block: narrow experts (f <= 64, 128-byte K
+// slices, 24 KiB stages) run three blocks per CU on a two-stage ring (measured faster at
+// the small workload's ~400 tiles than two blocks on three stages); wider ones two blocks
+// on 78 KiB.
+#ifndef DREAMER_FFN_NARROW_F
+#define DREAMER_FFN_NARROW_F 64
 #endif
 
 template <int F, int KIND>
 struct FfnCfg {
   static constexpr int NW1 = KIND == FFN_SWIGLU ? 2 : 1;  // GEMM1 weight matrices
-  static constexpr int BKB = F <= 64 ? 128 : 64;          // bytes of a GEMM1 K slice row
+  static constexpr bool NARROW = F <= DREAMER_FFN_NARROW_F;
+  static constexpr int OCC = NARROW ? 3 : 2;                       // blocks per CU
+  static constexpr int LDS = NARROW ? 52 * 1024 : 78 * 1024;       // ring budget per block
+  static constexpr int BKB = NARROW ? 128 : 64;           // bytes of a GEMM1 K slice row
   static constexpr int KSUB = BKB / 64;                   // 32-wide k-steps per slice
   static constexpr int CPR = BKB / 16, RPI = 64 / CPR;    // chunks per row, rows per load
   static constexpr int XB = 64 * BKB;                     // token rows of one slice
@@ -54,7 +58,7 @@ struct FfnCfg {
   static constexpr int fit_ns(int ns) {
     return ns <= 2 || (ns - 2) * LPWM + (ns - 1) * NT2 <= 63 ? ns : fit_ns(ns - 1);
   }
-  static constexpr int NS0 = DREAMER_FFN_LDS / STAGE;
+  static constexpr int NS0 = LDS / STAGE;
   static constexpr int NS = fit_ns(NS0 > 8 ? 8 : NS0);
   static_assert(NI1 % 4 == 0 && NI2 % 4 == 0, "stages must split evenly over 4 waves");
   static_assert(NS >= 2, "LDS ring too small");
@@ -66,7 +70,7 @@ DEV int ffn_swz(int rb, int row, int c) {
 }
 
 template <int F, int KIND>
-__global__ __launch_bounds__(256, DREAMER_FFN_OCC) void expert_ffn_kernel(
+__global__ __launch_bounds__(256, (FfnCfg<F, KIND>::OCC)) void expert_ffn_kernel(
     int k, int h_in, int h_out, const bf16* __restrict__ x, const bf16* __restrict__ w1,
     const bf16* __restrict__ w3, const bf16* __restrict__ w2, const int32_t* __restrict__ perm,
     const float* __restrict__ pgate, const int4* __restrict__ tiles, int tile_cap,
