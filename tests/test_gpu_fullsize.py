@@ -99,11 +99,16 @@ def test_prefill_full_prefix(gpu_lib, name, prefix):
     full, route_full, _ = gpu_forward(D, cfg, G, x0)
     assert torch.isfinite(full).all()
     pcfg = cfg.replace(b=1, s=prefix)
+    # bit-identical prefixes: causality and batch independence of the whole GPU path; the
+    # last sequence's prefix lies in other row tiles of every full-size launch
+    for bi in sorted({0, cfg.b - 1}):
+        xb = x0[bi:bi + 1, :prefix].contiguous()
+        part_b, route_b, _ = gpu_forward(D, pcfg, G, xb)
+        r0 = bi * cfg.s
+        assert torch.equal(full[r0:r0 + prefix], part_b), f"sequence {bi}"
+        assert torch.equal(route_full[0][:, r0:r0 + prefix], route_b[0]), f"sequence {bi}"
+        del part_b, route_b
     x0p = x0[:1, :prefix].contiguous()
-    part, route_part, _ = gpu_forward(D, pcfg, G, x0p)
-    # bit-identical prefix: causality and batch independence of the whole GPU path
-    assert torch.equal(full[:prefix], part)
-    assert torch.equal(route_full[0][:, :prefix], route_part[0])
     del full, route_full
     _free()
     ref = oracle_run(pcfg, W, x0p.cpu())
