@@ -31,8 +31,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # kernel-name substring that picks its dispatches in a counter file of the small workload.
 CLASS_SOURCES = {
     "qkv_proj": ["gemm.hip"], "out_proj": ["gemm.hip"], "seq_attn": ["attn.hip"],
-    "depth_attn": ["attn.hip"], "route": ["route.hip"], "expert_ffn": ["expert_ffn.hip"],
-    "combine": ["moe.hip"],
+    "depth_attn": ["attn.hip"], "attention": ["attn.hip"], "route": ["route.hip"],
+    "expert_ffn": ["expert_ffn.hip"], "combine": ["moe.hip"],
 }
 SHARED_SOURCES = ["common.h"]
 CLASS_KERNELS = {
@@ -40,6 +40,7 @@ CLASS_KERNELS = {
     "out_proj": "GemmCfg<32, 32, 2, 2, 128, 4, 2, false>",
     "seq_attn": "sa_flash_kernel",
     "depth_attn": "depth_attn_kernel",
+    "attention": "attn_pair_kernel",   # SA and DA in one launch
     "route": "router_fused_bf16_kernel",
     "expert_ffn": "expert_ffn_kernel",
     "combine": "combine_norm_kernel",
@@ -119,6 +120,8 @@ def traffic_summary(kclass, kernel_substr, fetch_csv, write_csv, copy_fetch_csv,
     kw = copy_bytes / (max(copy_w) * 1024.0)
     f = counter_per_dispatch(fetch_csv, "FETCH_SIZE", kernel_substr)
     w = counter_per_dispatch(write_csv, "WRITE_SIZE", kernel_substr)
+    if not f or not w:
+        return None  # the class did not run in the profiled command
     fetch = sum(f) / len(f) * 1024.0 * kf
     write = sum(w) / len(w) * 1024.0 * kw
     return {"class": kclass, "kernel": kernel_substr, "dispatches": len(f),
@@ -155,7 +158,13 @@ if __name__ == "__main__":
         for kclass, kname in CLASS_KERNELS.items():
             s = traffic_summary(kclass, kname, sys.argv[4], sys.argv[5], sys.argv[6],
                                 sys.argv[7], float(sys.argv[8]), " ".join(sys.argv[9:]))
-            with open(os.path.join(out_dir, f"{kclass}_{workload}_hbm_traffic.md"), "w") as fh:
+            path = os.path.join(out_dir, f"{kclass}_{workload}_hbm_traffic.md")
+            if s is None:  # no dispatches of this class: drop an older summary
+                if os.path.exists(path):
+                    os.remove(path)
+                print(kclass, "not run")
+                continue
+            with open(path, "w") as fh:
                 fh.write(traffic_md(s))
             print(kclass, s["dispatches"], round(s["bytes_per_launch"] / 2**20, 2), "MiB")
     else:
