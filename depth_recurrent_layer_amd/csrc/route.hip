@@ -402,6 +402,136 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
   }
 }
 
+// Top-k for k <= 16, one wave per token.  The wave's four 16-lane groups take the
+// experts in four contiguous quarters; each group keeps its quarter's best k across its
+// lanes (lane g: the g-th best) with the fused kernel's selection (chunks of 16 values per
+// lane, values below tau flagged off, candidates inserted one per step by a row shift).
+// A step takes one candidate in every group: each lane offers its lowest flagged value,
+// and the group's first offering lane is read with readlane (the lane numbers come from
+// the wave's ballot, so they are the same in every lane).  The next chunk's scores are
+// loaded while a chunk is selected.  Group 0 then takes in the other groups' entries that
+// are not below its k-th best: the top k of the union of the quarters' top k lists is
+// the top k of all experts.
+DEV void topk_row_insert(float& lv, float& lz, int& li, bool none, float cv, float cz, int ce) {
+  const bool keep = none || better(lv, li, cv, ce);
+  const int pk = row_shr1(keep ? 1 : 0, 1);
+  const float pv = row_shr1(lv, 0.f), pz = row_shr1(lz, 0.f);
+  const int pi = row_shr1(li, 0);
+  lv = keep ? lv : (pk ? cv : pv);
+  lz = keep ? lz : (pk ? cz : pz);
+  li = keep ? li : (pk ? ce : pi);
+}
+
+__global__ __launch_bounds__(256) void router_topk16_kernel(
+    int64_t Ttok, int E, int k, const float* __restrict__ z, const float* __restrict__ bias,
+    int normalize, const int32_t* __restrict__ idx_in, int32_t* __restrict__ idx,
+    float* __restrict__ gate) {
+  const int lane = threadIdx.x & 63, G = lane >> 4, g = lane & 15;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= Ttok) return;  // the whole wave
+  const float* zt = z + t * E;
+  int my = 0;
+  float myz = 0.f;
+  if (idx_in) {
+    if (lane < k) {
+      my = min(max(idx_in[t * k + lane], 0), E - 1);
+      myz = zt[my];
+    }
+  } else {
+    constexpr int NQ = RCH / 16;
+    const int eq = (E + 63) / 64 * 16;  // quarter length (a multiple of 16)
+    const int e1 = min(E, (G + 1) * eq);
+    float lv = -INFINITY, lz = 0.f;
+    int li = 0x7fffffff;
+    float zn[NQ], bn[NQ];  // the next chunk's scores and biases (clamped reads)
+    auto load = [&](int c0) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const int e = min(c0 + g + 16 * q, E - 1);
+        zn[q] = zt[e];
+        bn[q] = bias[e];
+      }
+    };
+    load(G * eq);
+    for (int c0 = G * eq; c0 < (G + 1) * eq; c0 += RCH) {  // same trip count in every group
+      float vr[NQ], zr[NQ];
+      float lmax = -INFINITY;
+      unsigned m = 0;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const bool in = c0 + g + 16 * q < e1;
+        zr[q] = zn[q];
+        vr[q] = in ? zn[q] + bn[q] : -INFINITY;
+        lmax = fmaxf(lmax, vr[q]);
+        m |= (in ? 1u : 0u) << q;
+      }
+      if (c0 + RCH < (G + 1) * eq) load(c0 + RCH);
+      float tau = __shfl(lv, k - 1, 16), cut = -INFINITY;
+      for (int j = 0; j < k; ++j) {
+        cut = group_max16(lmax);
+        if (lmax == cut) lmax = -INFINITY;
+      }
+      tau = fmaxf(tau, cut);
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+        if (!(vr[q] >= tau)) m &= ~(1u << q);
+      for (;;) {
+        const uint64_t act = __ballot(m != 0);
+        if (!act) break;  // the same in every lane
+        const int qn = m ? __builtin_ctz(m) : 0;
+        float ov = vr[0], oz = zr[0];
+#pragma unroll
+        for (int q = 1; q < NQ; ++q)
+          if (qn == q) {
+            ov = vr[q];
+            oz = zr[q];
+          }
+        const int oe = c0 + g + 16 * qn;
+        float cv = 0.f, cz = 0.f;
+        int ce = 0;
+        bool none = true;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {  // group q4's first offering lane
+          const unsigned gm = (unsigned)(act >> (16 * q4)) & 0xFFFFu;
+          if (!gm) continue;
+          const int sl = 16 * q4 + __builtin_ctz(gm);
+          const float v4 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ov), sl));
+          const float z4 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(oz), sl));
+          const int e4 = __builtin_amdgcn_readlane(oe, sl);
+          if (G == q4) {
+            cv = v4;
+            cz = z4;
+            ce = e4;
+            none = false;
+            if (lane == sl) m &= m - 1;
+          }
+        }
+        topk_row_insert(lv, lz, li, none, cv, cz, ce);
+      }
+    }
+    // group 0 takes in the entries of groups 1..3 that are not below its k-th best
+    const float tau0 = __shfl(lv, k - 1, 64);
+    uint64_t bal = __ballot(G > 0 && g < k && lv >= tau0);
+    while (bal) {  // the same in every lane
+      const int sl = __builtin_ctzll(bal);
+      bal &= bal - 1;
+      const float cv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv), sl));
+      const float cz = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lz), sl));
+      const int ce = __builtin_amdgcn_readlane(li, sl);
+      topk_row_insert(lv, lz, li, G != 0, cv, cz, ce);
+    }
+    my = min(max(li, 0), E - 1);  // lanes 0..k-1 (group 0) hold the selection in order
+    myz = lz;
+  }
+  const float gv = lane < k ? sigmoidf_(myz) : 0.f;
+  float gsum = 0.f;  // in selection order
+  for (int j = 0; j < k; ++j) gsum += __shfl(gv, j, 64);
+  if (lane < k) {
+    idx[t * k + lane] = my;
+    gate[t * k + lane] = normalize ? gv / gsum : gv;
+  }
+}
+
 int router_scores(int dtype, int64_t T, int h, int r, int E, int l, int L, const void* x,
                   int64_t ldx, const void* w_r, const float* u, const void* keys, float rho,
                   const float* cos_r, const float* sin_r, float* z, hipStream_t st) {
@@ -437,12 +567,10 @@ int router_topk(int64_t T, int E, int k, const float* z, const float* bias, int 
   const unsigned grid = (unsigned)((T + 3) / 4);
 #define TK_CASE(KM)                                                                       \
   dlaunch(router_topk_kernel<KM>, grid, 256, 0, st, T, E, k, z, bias, normalize, idx_in, idx, gate)
-  if (k <= 1) TK_CASE(1);
-  else if (k <= 2) TK_CASE(2);
-  else if (k <= 4) TK_CASE(4);
-  else if (k <= 8) TK_CASE(8);
-  else if (k <= 16) TK_CASE(16);
-  else TK_CASE(32);
+  if (k <= 16)
+    dlaunch(router_topk16_kernel, grid, 256, 0, st, T, E, k, z, bias, normalize, idx_in, idx, gate);
+  else
+    TK_CASE(32);
 #undef TK_CASE
   return 0;
 }
