@@ -169,6 +169,8 @@ def test_seq_attn_decode(gpu_lib, dt, B, P, H, d):
     ("bf16", 200, 2048, 64, 4096, 8, True, 0.2),
     ("bf16", 150, 1024, 64, 16, 1, False, 0.0),
     ("bf16", 64, 256, 32, 32, 32, True, 0.2),      # k == E: every expert selected
+    ("bf16", 120, 512, 64, 112, 16, True, 0.2),    # k = 16, a partial last expert quarter
+    ("f32", 50, 64, 16, 100, 13, True, 0.1),       # E not a multiple of 16, odd k
     # >= 1024 tokens: scores and selection in one kernel (ragged last block of 16 tokens)
     ("bf16", 1037, 512, 64, 256, 4, True, 0.2),
     ("bf16", 1030, 1024, 128, 1024, 8, True, 0.2),  # four chunks of 256 experts
@@ -207,21 +209,26 @@ def test_expert_route(gpu_lib, dt, T, h, r, E, k, norm, bias):
     assert (np.diff(ks, axis=1) <= 1e-6).all()
 
 
-@pytest.mark.parametrize("T", [40, 1040])
-def test_expert_route_ties_go_to_lower_index(gpu_lib, T):
+@pytest.mark.parametrize("T,E,tied", [(40, 16, (3, 7, 9)), (1040, 16, (3, 7, 9)),
+                                       (40, 256, (5, 70, 200)), (1040, 512, (5, 300, 260))])
+def test_expert_route_ties_go_to_lower_index(gpu_lib, T, E, tied):
+    """Identical experts (same key, same bias) in one or in different expert chunks or
+    quarters of the selection: they win in index order."""
     D = gpu_lib
-    h, r, E = 128, 32, 16
+    h, r = 128, 32
     x = _t((T, h), 22, 0)
     w_r = _t((r, h), 22, 1, 0.05)
     keys = _t((E, r), 22, 2, 0.05)
-    keys[7] = keys[3]
-    keys[9] = keys[3]
+    for e in tied[1:]:
+        keys[e] = keys[tied[0]]
     b = torch.zeros(E, device="cuda")
-    b[3] = b[7] = b[9] = 5.0  # the three identical experts win, in index order
+    for e in tied:
+        b[e] = 5.0  # the identical experts win, in index order
     cos, sin = D.dreamer_rope_tables(r, 3)
     idx, _, _ = D.dreamer_expert_route(x, w_r, keys, b, 2, 1, 3, cos, sin)
     torch.cuda.synchronize()
-    assert (idx[:, 0] == 3).all() and (idx[:, 1] == 7).all()
+    first, second = sorted(tied)[:2]
+    assert (idx[:, 0] == first).all() and (idx[:, 1] == second).all()
 
 
 # ------------------------------------------------------------------------------- experts
