@@ -466,26 +466,53 @@ DEV void sa_flash_block(int qbx, int head, int b, int S, int H, const bf16* __re
     const int p0 = min(kbase + (slot ^ (dim & 7)) * 8, S - 8);
     return vbase + (int64_t)dim * S + p0;
   };
-  const bf16* src0[4];
+  // whole tiles: a base the same in every lane (advanced by the tile) plus this lane's
+  // 32-bit byte offset, so the per-tile address work is scalar
+  const char* kb_u = reinterpret_cast<const char*>(kk + tok0 * ldk + hoff);
+  const char* vb_u = reinterpret_cast<const char*>(vbase);
+  uint32_t loff[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) src0[i] = tile_src(i, 0);
+  for (int i = 0; i < 4; ++i) {
+    const int j = w + 4 * i;
+    if (i < 2) {
+      const int row = j * 8 + lrow;
+      loff[i] = (uint32_t)((key_of_row(row) * ldk + (slot ^ (row & 7)) * 8) * 2);
+    } else {
+      const int dim = (j - 8) * 8 + lrow;
+      loff[i] = (uint32_t)(((int64_t)dim * S + (slot ^ (dim & 7)) * 8) * 2);
+    }
+  }
   auto issue = [&](int t) {
     char* sb = stg[t % NSTG];
     const int kbase = t * BKEY;
     const bool whole = kbase + BKEY <= S;
+    const char* kt_u = kb_u + (int64_t)kbase * ldk * 2;
+    const char* vt_u = vb_u + (int64_t)kbase * 2;
+    if (whole) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bf16* src = whole ? src0[i] + (int64_t)kbase * (i < 2 ? ldk : 1) : tile_src(i, kbase);
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(sb + (w + 4 * i) * 1024),
-                                       16, 0, 0);
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)((i < 2 ? kt_u : vt_u) + loff[i]),
+                                         (lds_void*)(sb + (w + 4 * i) * 1024), 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)tile_src(i, kbase),
+                                         (lds_void*)(sb + (w + 4 * i) * 1024), 16, 0, 0);
     }
   };
 
   const float sl2 = scale * 1.44269504088896341f;  // scale * log2(e)
-  float m = -INFINITY, lsum = 0.f;
+  float m = -INFINITY;
   floatx4 o[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) o[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // The softmax denominator comes from the P.V MFMAs: an extra A fragment whose row 0 is
+  // all ones turns that row of the product into the sum of the (bf16) P of each query,
+  // held by the lane of group 0 that owns the query (element 0 of osum).
+  floatx4 osum = {0.f, 0.f, 0.f, 0.f};
+  bf16x8 ones;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ones[j] = (bf16)(lr == 0 ? 1.f : 0.f);
 
   const int qlast = min(qb * BQ + BQ, S) - 1;
   const int qlim = min(qpos, S - 1);
@@ -538,23 +565,21 @@ DEV void sa_flash_block(int qbx, int head, int b, int S, int H, const bf16* __re
     if (__any(mn > m)) {  // rescale only when some query's running max moved
       const float corr = __builtin_amdgcn_exp2f((m - mn) * sl2);
       m = mn;
-      lsum *= corr;
+      osum *= corr;
 #pragma unroll
       for (int t = 0; t < 4; ++t) o[t] *= corr;
     }
     // P^T fragments for the two 32-key chunks: element j of lane group lg is key
     // 32cc + 8lg + j (tile 2cc for j < 4, tile 2cc+1 for j >= 4).  P is rounded to bf16
-    // (pairwise conversions) for the MFMA; the softmax denominator sums P in float32.
+    // (pairwise conversions) for the MFMA, numerator and denominator alike.
     bf16x8 ph[2];
     const float msl = mn * sl2;
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
       floatx8 pv;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < 8; ++j)
         pv[j] = __builtin_amdgcn_exp2f(fmaf(sacc[2 * cc + (j >> 2)][j & 3], sl2, -msl));
-        lsum += pv[j];
-      }
       ph[cc] = __builtin_convertvector(pv, bf16x8);
     }
     // O^T += V^T P^T : 4 dim tiles x 2 key chunks.  Lane (dim 16t + lr, group lg) takes
@@ -565,8 +590,10 @@ DEV void sa_flash_block(int qbx, int head, int b, int S, int H, const bf16* __re
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) o[t] = mfma16(vf[cc * 4 + t], ph[cc], o[t]);
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) osum = mfma16(ones, ph[cc], osum);
   }
-  lsum = sum_xor32(sum_xor16(lsum));
+  const float lsum = __shfl(osum[0], lr, 64);  // from the group-0 lane of this query
   if (qpos >= S) return;
   const float inv = 1.0f / lsum;
   bf16* orow = out + (tok0 + qpos) * ldo + hoff;
