@@ -581,8 +581,11 @@ static LayerWs plan_layer(Bump& b, const dreamer_layer_cfg* c, bool need_yb, boo
     w.da_k = b.take(T * c->L * h * es);
     w.da_v = b.take(T * c->L * h * es);
   }
-  // bf16 prefill: q/k arrive rotated and v transposed from the QKV epilogue
-  const bool vt_ok = c->dtype == DREAMER_BF16 && !c->decode && c->d == 64 && c->s % 8 == 0;
+  // bf16 prefill: q/k arrive rotated and v transposed from the QKV epilogue (not with the
+  // grouped linear-MoE projections: their rows are in expert order, so the transposed v
+  // would be written element by element; SA then transposes v in its own preparation pass)
+  const bool vt_ok = c->dtype == DREAMER_BF16 && !c->decode && c->d == 64 && c->s % 8 == 0 &&
+                     c->proj_experts == 0;
   w.vt = vt_ok ? b.take((size_t)T * h * es) : nullptr;
   w.sa_ws_bytes = seq_attn_ws(c->dtype, c->b, c->s, c->H, c->d, c->decode ? c->sa_pos : 0,
                               vt_ok ? 1 : 0);
@@ -719,7 +722,7 @@ static int layer_run(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* 
                       proj_route_in ? proj_route_in + (int64_t)l * T : nullptr);
       if (rc) return rc;
       TB(DREAMER_KC_PERMUTE);
-      rc = launch_permute(pidx, T, Ep, 64, lw.phist, lw.pcounts, lw.pgoff, lw.ptoff, lw.pperm,
+      rc = launch_permute(pidx, T, Ep, PROJ_TILE_M, lw.phist, lw.pcounts, lw.pgoff, lw.ptoff, lw.pperm,
                           st);
       TE(DREAMER_KC_PERMUTE);
       if (rc) return fail(DREAMER_E_UNSUPPORTED, "layer: projection permutation");
@@ -765,7 +768,7 @@ static int layer_run(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* 
         gq.goff = lw.pgoff;
         gq.toff = lw.ptoff;
         gq.G = c.proj_experts;
-        gq.tile_m = 64;
+        gq.tile_m = PROJ_TILE_M;
       }
       // q/k leave the projection rotated (SA by position, DA by depth) and rounded once
       if (dt == DREAMER_BF16) {
@@ -835,7 +838,7 @@ static int layer_run(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* 
         go.goff = lw.pgoff;
         go.toff = lw.ptoff;
         go.G = c.proj_experts;
-        go.tile_m = 64;
+        go.tile_m = PROJ_TILE_M;
       }
       TB(DREAMER_KC_OUT_PROJ);
       int r2 = launch_gemm(go, dt, 1, st);

@@ -656,6 +656,33 @@ __global__ __launch_bounds__(256, 3) void attn_pair_kernel(SaFlashArgs sa, DaArg
   }
 }
 
+// v [B, S, H, 64] (row stride ldv) -> vt [B][H][64][S] through LDS: one block per (64
+// positions, head, batch); 16-byte loads of whole rows and 16-byte stores of position runs.
+__global__ __launch_bounds__(256) void v_transpose_kernel(int S, int H, const bf16* __restrict__ v,
+                                                          int64_t ldv, bf16* __restrict__ vt) {
+  __shared__ bf16 tile[64][64 + 8];  // [position][dim]
+  const int p0 = blockIdx.x * 64, head = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {  // 64 rows x 8 chunks
+    const int it = tid + 256 * u, r = it >> 3, ch = it & 7;
+    const int p = min(p0 + r, S - 1);
+    const bf16x8 x =
+        *reinterpret_cast<const bf16x8*>(v + ((int64_t)b * S + p) * ldv + head * 64 + ch * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile[r][ch * 8 + e] = x[e];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {  // 64 dims x 8 runs of 8 positions
+    const int it = tid + 256 * u, dim = it >> 3, ch = it & 7;
+    if (p0 + ch * 8 >= S) continue;  // S % 8 == 0: runs are whole or absent
+    bf16x8 y;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = tile[ch * 8 + e][dim];
+    *reinterpret_cast<bf16x8*>(vt + (((int64_t)b * H + head) * 64 + dim) * S + p0 + ch * 8) = y;
+  }
+}
+
 // Prepares flash inputs from unrotated projections: qr/kr [B, S, H, 64] rotated (when
 // rope) and rounded, vt [B][H][64][S].  Thread -> (row, head, chunk pair c < 4).
 __global__ __launch_bounds__(256) void sa_prep_kernel(int B, int S, int H, const bf16* __restrict__ q,
@@ -813,7 +840,12 @@ int launch_seq_attn(int dtype, int B, int q_len, int H, int d, int64_t pos0, con
   if (flash_ok(dtype, d, q_len)) {
     const bf16 *fq = (const bf16*)q, *fk = (const bf16*)kn, *fvt = (const bf16*)vt;
     int64_t fldq = ldq, fldk = ldk;
-    if (!prepared) {
+    if (!prepared && !rope) {  // rotated (or unrotated by choice) q / k: only v^T needed
+      bf16* vtt = (bf16*)ws + 2 * (size_t)B * q_len * h;
+      dlaunch(v_transpose_kernel, dim3((q_len + 63) / 64, H, B), 256, 0, st, q_len, H,
+              (const bf16*)vn, ldv, vtt);
+      fvt = vtt;
+    } else if (!prepared) {
       bf16* qr = (bf16*)ws;
       bf16* kr = qr + (size_t)B * q_len * h;
       bf16* vtt = kr + (size_t)B * q_len * h;

@@ -63,7 +63,10 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_bf16_kernel(GemmArgs a
 
   const int tid = threadIdx.x;
   int g = 0, m_begin, m_end;
-  const int mtile = blockIdx.x;
+  // grouped launches with many n-tiles run them fastest (n_fast): consecutive blocks
+  // (spread over the XCDs) share one m-tile's rows, and each XCD sees the same n-tiles of
+  // a group's weights for all of that group's m-tiles
+  const int mtile = a.n_fast ? blockIdx.y : blockIdx.x;
   if (a.toff) {
     if (mtile >= a.toff[a.G]) return;
     int lo = 0, hi = a.G - 1;  // largest g with toff[g] <= mtile
@@ -78,7 +81,7 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_bf16_kernel(GemmArgs a
     m_begin = mtile * BM;
     m_end = a.M;
   }
-  const int n0 = blockIdx.y * BN;
+  const int n0 = (a.n_fast ? blockIdx.x : blockIdx.y) * BN;
   const bf16* __restrict__ A = (const bf16*)a.A;
   const bf16* __restrict__ B = (const bf16*)a.B + (int64_t)g * a.b_gstride;
   for (int i = tid; i < BM; i += S::NT) {
@@ -359,7 +362,9 @@ __global__ void gemm_f32_kernel(GemmArgs a) {
   if (a.C2) ((float*)a.C2)[(int64_t)orow * a.ldc2 + n] = val;
 }
 
-int launch_gemm(const GemmArgs& a, int dtype, int out_f32, hipStream_t st) {
+int launch_gemm(const GemmArgs& a_in, int dtype, int out_f32, hipStream_t st) {
+  GemmArgs a = a_in;
+  a.n_fast = a.toff && a.N >= 16 * 128;  // grouped with many n-tiles: n fastest (see the kernel)
   if (a.M <= 0 || a.N <= 0) return 0;
   if (dtype == DT_F32) {
     dim3 grid((a.N + 15) / 16, (a.M + 15) / 16);
@@ -372,17 +377,19 @@ int launch_gemm(const GemmArgs& a, int dtype, int out_f32, hipStream_t st) {
     return (int64_t)((a.M + tm - 1) / tm) * ((a.N + tn - 1) / tn);
   };
   auto grid_of = [&](int bm, int bn) {
-    return dim3((a.M + bm - 1) / bm + (a.toff ? a.G : 0), (a.N + bn - 1) / bn);
+    const int nm = (a.M + bm - 1) / bm + (a.toff ? a.G : 0), nn = (a.N + bn - 1) / bn;
+    return a.n_fast ? dim3(nn, nm) : dim3(nm, nn);
   };
   // QKV projections with the rotary epilogue (64-column wave tiles, one head each):
-  // 128 x 128 tiles of 8 waves at two blocks per CU; few rows, and grouped launches (whose
-  // tile offsets were built for 64-row m-tiles), take 64 x 128 tiles of 4 waves.
+  // 128 x 128 tiles of 8 waves at two blocks per CU; few rows, and grouped launches whose
+  // tile offsets were built for 64-row m-tiles, take 64 x 128 tiles of 4 waves (grouped
+  // launches built for 128-row m-tiles take the 128 x 128 tiles).
   if (a.qkv_h) {
     if (a.qkv_h % 128 || out_f32 || !a.rope_d4 || (a.sa_rope && !a.rope_s4)) return -1;
-    if (a.toff && a.tile_m != 64) return -1;
+    if (a.toff && a.tile_m != 64 && a.tile_m != 128) return -1;
     if (!a.toff && k64 && tiles(256, 256) >= 256) {
       dlaunch(gemm_bf16_kernel<bf16, GemmCfg<64, 64, 4, 4, 64, 4, 1, true>>, grid_of(256, 256), 1024, 0, st, a);
-    } else if (a.toff || tiles(128, 128) < 256) {
+    } else if (a.toff ? a.tile_m == 64 : tiles(128, 128) < 256) {
       if (k64)
         dlaunch(gemm_bf16_kernel<bf16, GemmCfg<32, 64, 2, 2, 128, 3, 2, false>>, grid_of(64, 128), 256, 0, st, a);
       else
@@ -395,11 +402,13 @@ int launch_gemm(const GemmArgs& a, int dtype, int out_f32, hipStream_t st) {
     return 0;
   }
   // Generic: 128 x 128 tiles when that gives >= 512 blocks (two per CU), else 64 x 128,
-  // else 64 x 64; grouped launches use 64-row m-tiles.
+  // else 64 x 64; grouped launches use m-tiles of their tile_m rows (64, or 128 with
+  // 128-column tiles).
   const int bn = a.N >= 128 ? 128 : 64;
   int bm = 64, bnn = bn;
   if (a.toff) {
-    if (a.tile_m != 64) return -1;
+    if (a.tile_m == 128 && bn == 128) bm = 128;
+    else if (a.tile_m != 64) return -1;
   } else if (bn == 128 && tiles(128, 128) >= 512) {
     bm = 128;
   } else if (bn == 128 && tiles(64, 128) < 512) {

@@ -29,6 +29,7 @@ struct GemmArgs {
   const int* toff = nullptr;         // [G+1] m-tile offsets of groups (device, tile_m rows)
   int G = 1;
   int tile_m = 64;                   // rows per m-tile used to build toff
+  int n_fast = 0;                    // set by launch_gemm: grouped grid runs n-tiles fastest
   void* C = nullptr;                 // OutT, row stride ldc
   int64_t ldc = 0;
   const float* resid = nullptr;      // float32 residual, row stride ldr
@@ -168,6 +169,8 @@ int launch_expert_ffn(int dtype, int kind, int64_t nslots, int k, int h_in, int 
                       const int32_t* perm, const float* pgate, const int4* tiles,
                       const int32_t* toff, void* slots, hipStream_t st);
 constexpr int FFN_TILE_M = 64;
+// m-tile rows of the grouped (top-1 linear-MoE) Q/K/V/O projections
+constexpr int PROJ_TILE_M = 128;
 // float32 per-slot expert FFN (any kind, any f): slots[s] = gate[s] * FFN_idx[s](x[s/k]).
 int launch_expert_ffn_f32(int kind, int64_t nslots, int k, int h_in, int f, int h_out,
                           const float* x, const int32_t* idx, const float* gate,
