@@ -7,9 +7,9 @@
 // float32 accuracy on MFMA.  With many tokens one fused kernel also selects (scores stay
 // in LDS); with few tokens and many experts the scores go to a [T, E] float32 buffer over
 // a 2-D grid and a top-k kernel (one wave per token) selects.  Either way the selection
-// ranks by z + b and takes gates from z, and may count selections per expert with
-// global atomics, handing each selection its rank within its expert; a placement kernel
-// then turns (expert, rank) into the expert-major slot order.
+// ranks by z + b (ties to the lower expert index) and takes gates from z.  The fused
+// kernel can also count the permutation's chunk histograms (global atomics); the
+// permutation kernels then scan them and scatter the slots into expert-major order.
 #include <math.h>
 
 #include <algorithm>
@@ -329,10 +329,10 @@ __global__ void router_scores_f32_kernel(int64_t Ttok, int r, int E, int l, int 
 }
 
 // ------------------------------------------------------------------------------- top-k
-// One wave per token.  Each lane keeps a sorted list of its KMAX best (z + b, e) over
-// experts lane, lane + 64, ...; k rounds of a butterfly argmax pop the heads.  Gates are
-// sigmoid(z) of the winners, divided by their sum when normalising.  With idx_in the
-// given experts are adopted instead.
+// Top-k for 16 < k <= 32.  One wave per token.  Each lane keeps a sorted list of its KMAX
+// best (z + b, e) over experts lane, lane + 64, ...; k rounds of a butterfly argmax pop
+// the heads.  Gates are sigmoid(z) of the winners, divided by their sum when normalising.
+// With idx_in the given experts are adopted instead.
 template <int KMAX>
 __global__ __launch_bounds__(256) void router_topk_kernel(
     int64_t Ttok, int E, int k, const float* __restrict__ z, const float* __restrict__ bias,
