@@ -1,8 +1,9 @@
 // C = A . B^T with fused epilogues, for the dense projections (QKV, O, router rank-r
 // projection) and the grouped linear-MoE projections.
 //
-// bf16 path: MFMA (v_mfma_f32_16x16x32_bf16) over a multi-stage LDS ring, 256 threads =
-// 2 x 2 waves.
+// bf16 path: MFMA (v_mfma_f32_16x16x32_bf16) over a multi-stage LDS ring; the tile,
+// wave grid, slice width, ring depth and blocks per CU come from a GemmCfg instance
+// chosen per launch shape (launch_gemm).
 // f32 path: one thread per output element (used only for small float32 layers).
 //
 // Row model: the kernel walks "positions" m.  Position m reads A row
