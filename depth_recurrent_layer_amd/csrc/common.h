@@ -199,6 +199,13 @@ DEV void store_b64_counted(void* p, bf16x4 v) {
   asm volatile("global_store_dwordx2 %0, %1, off" : : "v"(p), "v"(v) : "memory");
 }
 
+// 8-byte LDS write that the compiler does not see as an LDS access: a plain store into
+// a ring that direct global->LDS loads still fill would first wait for all of them
+// (vmcnt(0)).  Completed by the next lgkmcnt wait (ring_barrier has one).
+DEV void lds_write_b64(uint32_t addr, bf16x4 v) {
+  asm volatile("ds_write_b64 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+
 // Workgroup barrier for LDS rings filled by direct global->LDS loads.  __syncthreads()
 // would first wait for every outstanding vector-memory load of the wave (its fence
 // covers global memory), draining the loads of later ring stages; here only this wave's

@@ -1,19 +1,18 @@
 // Fused expert FFN for bf16 storage (SwiGLU or GELU) over routed slots.
 //
-// One block = one 64-row m-tile of one expert's slots; wave w owns tile rows
-// [16 w, 16 w + 16).  A single ring of LDS stages, filled by direct global->LDS loads
-// (global_load_lds_dwordx4, several stages in flight), streams everything the tile
-// reads: first GEMM1's K slices (the gathered token rows and the expert's W1 / W3 rows),
-// then GEMM2's slices of W2 rows (output columns), so W2 is already in flight while
-// GEMM1 finishes.
+// One block = one 64-row m-tile of one expert's slots, four waves.  A single ring of LDS
+// stages, filled by direct global->LDS loads (global_load_lds_dwordx4, several stages in
+// flight), streams everything the tile reads: first GEMM1's K slices (the gathered token
+// rows and the expert's W1 / W3 rows), then GEMM2's slices of W2 rows (output columns),
+// so W2 is already in flight while GEMM1 finishes.
 //
-// GEMM1 runs transposed, H^T = W X^T: the weight rows are the MFMA A operand, so a lane
-// ends with hidden units of one token row.  The weight rows are loaded in a permuted
-// order (LDS row 16 t + 4 g + i holds hidden unit 32 (t/2) + 8 g + 4 (t%2) + i) that
-// makes those hidden units exactly the 8 consecutive ones GEMM2's B fragment needs: the
-// activation goes from the accumulators straight into GEMM2's operand registers.
-// GEMM2 runs transposed too, O^T = W2 H^T: every lane holds 4 consecutive gate-scaled
-// outputs of one slot and stores them as 8 bytes.
+// The waves split the weights, not the token rows, so that every weight fragment is read
+// from LDS by one wave only: in GEMM1, H^T = W X^T, wave w owns F/4 hidden units (the
+// weight rows are the MFMA A operand) for all 64 token rows; the activation goes through
+// LDS once (64 x F bf16, in the ring stage GEMM1 has just finished with) and every wave
+// keeps all of it in registers as GEMM2's B operand.  In GEMM2, O^T = W2 H^T, wave w owns
+// a quarter of each stage's output columns for all token rows; every lane holds 4
+// consecutive gate-scaled outputs of one slot and stores them as 8 bytes.
 //
 // Slices are XOR-swizzled by row in 16-byte chunks so that the 16 rows one fragment
 // read touches fall into distinct banks.
@@ -24,8 +23,8 @@ namespace dreamer {
 
 // Blocks per CU and the ring's LDS budget per block: narrow experts (f <= 64, 128-byte K
 // slices, 24 KiB stages) run three blocks per CU on a two-stage ring (measured faster at
-// the small workload's ~400 tiles than two blocks on three stages); wider ones two blocks
-// on 78 KiB.
+// the small workload's ~400 tiles than two blocks on three stages, and than 64-byte
+// slices on four stages); wider ones two blocks on 78 KiB.
 #ifndef DREAMER_FFN_NARROW_F
 #define DREAMER_FFN_NARROW_F 64
 #endif
@@ -41,16 +40,22 @@ struct FfnCfg {
   static constexpr int CPR = BKB / 16, RPI = 64 / CPR;    // chunks per row, rows per load
   static constexpr int XB = 64 * BKB;                     // token rows of one slice
   static constexpr int WB = F * BKB;                      // one weight's rows of one slice
-  static constexpr int STAGE = XB + NW1 * WB;             // bytes per ring stage
-  // GEMM2 stage: C2 W2 rows (output columns) of F elements, as many as fit a stage
+  static constexpr int STAGE1 = XB + NW1 * WB;            // bytes GEMM1 loads per stage
+  // GEMM2 stage: C2 W2 rows (output columns) of F elements, 16 or 32 per wave
   static constexpr int RB2 = 2 * F;
-  static constexpr int C2 = 128 * RB2 <= STAGE ? 128 : (64 * RB2 <= STAGE ? 64 : 32);
+  static constexpr int C2 = 128 * RB2 <= STAGE1 ? 128 : 64;
+  static constexpr int CT = C2 / 64;                      // column tiles per wave and stage
+  // the activation exchange: 64 token rows of F bf16, rows padded by 16 bytes
+  static constexpr int HS = 2 * F + 16;
+  static constexpr int HB = (64 * HS + 1023) / 1024 * 1024;
+  static constexpr int STAGE = STAGE1 > C2 * RB2 ? (STAGE1 > HB ? STAGE1 : HB)
+                                                 : (C2 * RB2 > HB ? C2 * RB2 : HB);
   static constexpr int CPR2 = RB2 / 16, RPI2 = 64 / CPR2;
-  static constexpr int NI1 = STAGE / 1024, LPW1 = NI1 / 4;  // load instructions
+  static constexpr int NI1 = STAGE1 / 1024, LPW1 = NI1 / 4;  // load instructions
   static constexpr int NI2 = C2 * RB2 / 1024, LPW2 = NI2 / 4;
-  static constexpr int NT1 = F / 16;            // GEMM1 m-tiles (16 hidden units) per weight
+  static constexpr int HT = F / 64;             // GEMM1 hidden tiles per wave and weight
   static constexpr int KS2 = F / 32;            // GEMM2 k-steps
-  static constexpr int NT2 = C2 / 16;           // GEMM2 output-column tiles per stage
+  static constexpr int NT2 = 4 * CT;            // GEMM2 stores per wave and stage (at most)
   // ring depth: what the LDS budget holds, at most 8, and few enough stages that the
   // operations outstanding behind a stage (the loads of NS - 2 stages, the output stores
   // of NS - 1 iterations) stay within the vmcnt counter's range
@@ -61,6 +66,7 @@ struct FfnCfg {
   static constexpr int NS0 = LDS / STAGE;
   static constexpr int NS = fit_ns(NS0 > 8 ? 8 : NS0);
   static_assert(NI1 % 4 == 0 && NI2 % 4 == 0, "stages must split evenly over 4 waves");
+  static_assert(STAGE1 % 1024 == 0 && STAGE % 1024 == 0, "stages are whole load rows");
   static_assert(NS >= 2, "LDS ring too small");
 };
 
@@ -91,20 +97,24 @@ __global__ __launch_bounds__(256, (FfnCfg<F, KIND>::OCC)) void expert_ffn_kernel
   const int tile = (b & 7) * per + (b >> 3);
   const int tc = min(tile, tile_cap - 1);
   const int4 td = tiles[tc];
-  const int pslot = perm[tc * 64 + (tid & 63)];          // row tid (first wave)
-  const int oslot = perm[tc * 64 + w * 16 + lr];         // this lane's output row
-  float gate = pgate[tc * 64 + w * 16 + lr];
+  const int pslot = perm[tc * 64 + (tid & 63)];  // row tid (first wave)
+  float gate[4];  // gates of this lane's output rows 16 tt + lr
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) gate[tt] = pgate[tc * 64 + tt * 16 + lr];
   if ((b >> 3) >= per || tile >= n_tiles) return;
   const int e = td.x, nrows = min(64, td.z - td.y);
-  const int sl = w * 16 + lr < nrows ? oslot : -1;
   if (tid < 64) s_slot[tid] = tid < nrows ? pslot : -1;
-  // the gate is taken through an empty asm statement: the compiler waits for it here,
-  // before the ring starts, instead of draining the ring at its first use
-  asm volatile("" : "+v"(gate));
+  // the gates are taken through an empty asm statement: the compiler waits for them here,
+  // before the ring starts, instead of draining the ring at their first use
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) asm volatile("" : "+v"(gate[tt]));
   __syncthreads();
+  int sl[4];  // output slot of row 16 tt + lr (-1: pad row)
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) sl[tt] = s_slot[tt * 16 + lr];
 
   // load descriptors: wave w issues instructions q = w + 4 j of every stage
-  const bf16* src1[S::LPW1];  // GEMM1: token rows, then W1 (and W3) rows, permuted
+  const bf16* src1[S::LPW1];  // GEMM1: token rows, then W1 (and W3) rows
 #pragma unroll
   for (int j = 0; j < S::LPW1; ++j) {
     const int q = w + 4 * j, slot = lane % S::CPR;
@@ -113,11 +123,9 @@ __global__ __launch_bounds__(256, (FfnCfg<F, KIND>::OCC)) void expert_ffn_kernel
       const int s = s_slot[row] >= 0 ? s_slot[row] : s_slot[0];  // pad rows repeat row 0
       src1[j] = x + (int64_t)(s / k) * h_in + ffn_swz(BKB, row, slot) * 8;
     } else {
-      const int wr = (row - 64) % F, m = (row - 64) / F;
-      const int t = wr >> 4, g = (wr >> 2) & 3, i = wr & 3;
-      const int hu = 32 * (t >> 1) + 8 * g + 4 * (t & 1) + i;  // hidden unit of LDS row wr
+      const int hu = (row - 64) % F, m = (row - 64) / F;  // hidden unit, weight
       const bf16* W = m == 0 ? w1 : w3;
-      src1[j] = W + ((int64_t)e * F + hu) * h_in + ffn_swz(BKB, wr, slot) * 8;
+      src1[j] = W + ((int64_t)e * F + hu) * h_in + ffn_swz(BKB, hu, slot) * 8;
     }
   }
   const bf16* src2[S::LPW2];  // GEMM2: W2 rows (output columns) of the first chunk
@@ -144,101 +152,142 @@ __global__ __launch_bounds__(256, (FfnCfg<F, KIND>::OCC)) void expert_ffn_kernel
     }
   };
 
-  floatx4 ag[S::NT1], au[S::NT1];
-#pragma unroll
-  for (int t = 0; t < S::NT1; ++t) {
-    ag[t] = floatx4{0.f, 0.f, 0.f, 0.f};
-    au[t] = floatx4{0.f, 0.f, 0.f, 0.f};
-  }
-  bf16x8 hf[S::KS2];  // GEMM2 B operand: this lane's row, hidden units 32 s + 8 lg + j
-  const uint32_t stg0 = lds_off(stg);
   // Stage s has landed once at most the operations issued after its loads are
   // outstanding: the loads of stages s+1 .. s+NS-2 and the output stores of the GEMM2
-  // iterations from the one that issued stage s on (NT2 counted store instructions per
-  // iteration, in waves that own a slot row).
-  const int nst_w = w * 16 < nrows ? S::NT2 : 0;
-  for (int s = 0; s < S::NS - 1 && s < ntot; ++s) issue(s);
-  for (int s = 0; s < ntot; ++s) {
+  // iterations from the one that issued stage s on (CT store instructions per token
+  // tile that holds a slot row, per iteration; the same count in every wave).
+  const int nst_w = S::CT * ((nrows + 15) / 16);
+  auto wait_stage = [&](int s) {
     int later = 0;
     for (int t = s + 1; t < s + S::NS - 1 && t < ntot; ++t) later += t < n1 ? S::LPW1 : S::LPW2;
     later += nst_w * max(0, s - max(n1, s - S::NS + 1));
     wait_vmcnt_upto(later);
     ring_barrier();  // stage s visible to all waves; stage s-1 fully consumed
+  };
+  const uint32_t stg0 = lds_off(stg);
+  for (int s = 0; s < S::NS - 1 && s < ntot; ++s) issue(s);
+
+  // GEMM1 accumulators: hidden tile w * HT + j of weight 1 (ag) and 3 (au), token tile tt
+  floatx4 ag[S::HT][4], au[S::HT][4];
+#pragma unroll
+  for (int j = 0; j < S::HT; ++j)
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      ag[j][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      au[j][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+  for (int s = 0; s < n1; ++s) {
+    wait_stage(s);
     if (s + S::NS - 1 < ntot) issue(s + S::NS - 1);
     const uint32_t sb = stg0 + (s % S::NS) * S::STAGE;
-    if (s < n1) {
-      // every fragment of the stage in one read group (one LDS round trip per stage):
-      // per k-step the X fragment, then NT1 fragments of each weight
-      constexpr int PER = 1 + S::NW1 * S::NT1, NR = S::KSUB * PER;
-      bf16x8 fr[NR];
-      uint32_t ad[NR];
+    // every fragment of the stage in one read group (one LDS round trip per stage):
+    // per k-step the 4 token-row fragments, then HT fragments of each weight
+    constexpr int PER = 4 + S::NW1 * S::HT, NR = S::KSUB * PER;
+    bf16x8 fr[NR];
+    uint32_t ad[NR];
 #pragma unroll
-      for (int kh = 0; kh < S::KSUB; ++kh) {
-        // fragments 16 rows apart share the swizzle slot (it depends on lr only)
-        const int slot = ffn_swz(BKB, lr, kh * 4 + lg);
-        const uint32_t wa = sb + S::XB + lr * BKB + (slot << 4);
-        ad[kh * PER] = sb + (w * 16 + lr) * BKB + (slot << 4);
+    for (int kh = 0; kh < S::KSUB; ++kh) {
+      // fragments 16 rows apart share the swizzle slot (it depends on lr only)
+      const int slot = ffn_swz(BKB, lr, kh * 4 + lg);
+      const uint32_t xa = sb + lr * BKB + (slot << 4);
+      const uint32_t wa = sb + S::XB + (w * S::HT * 16 + lr) * BKB + (slot << 4);
 #pragma unroll
-        for (int m = 0; m < S::NW1; ++m)
+      for (int tt = 0; tt < 4; ++tt) ad[kh * PER + tt] = xa + tt * 16 * BKB;
 #pragma unroll
-          for (int t = 0; t < S::NT1; ++t)
-            ad[kh * PER + 1 + m * S::NT1 + t] = wa + m * S::WB + t * 16 * BKB;
-      }
-      lds_read_b128<NR>(fr, ad);
+      for (int m = 0; m < S::NW1; ++m)
 #pragma unroll
-      for (int kh = 0; kh < S::KSUB; ++kh)
-#pragma unroll
-        for (int t = 0; t < S::NT1; ++t) {
-          ag[t] = mfma16(fr[kh * PER + 1 + t], fr[kh * PER], ag[t]);
-          if constexpr (KIND == FFN_SWIGLU)
-            au[t] = mfma16(fr[kh * PER + 1 + S::NT1 + t], fr[kh * PER], au[t]);
-        }
-      continue;
+        for (int j = 0; j < S::HT; ++j)
+          ad[kh * PER + 4 + m * S::HT + j] = wa + m * S::WB + j * 16 * BKB;
     }
-    if (s == n1) {
-      // activation: accumulator tile t, element i is hidden unit 32 (t/2) + 8 lg +
-      // 4 (t%2) + i of row w*16 + lr, i.e. element 4 (t%2) + i of GEMM2 k-step t/2
+    lds_read_b128<NR>(fr, ad);
 #pragma unroll
-      for (int t = 0; t < S::NT1; ++t)
+    for (int kh = 0; kh < S::KSUB; ++kh)
+#pragma unroll
+      for (int j = 0; j < S::HT; ++j)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          ag[j][tt] = mfma16(fr[kh * PER + 4 + j], fr[kh * PER + tt], ag[j][tt]);
+          if constexpr (KIND == FFN_SWIGLU)
+            au[j][tt] = mfma16(fr[kh * PER + 4 + S::HT + j], fr[kh * PER + tt], au[j][tt]);
+        }
+  }
+
+  // Activation through LDS, in the stage GEMM1 finished last (slot (n1 - 1) % NS, whose
+  // next load, stage n1 + NS - 1, is issued by the first GEMM2 iteration, after a barrier
+  // that follows every wave's read of the activation): accumulator element i of (j, tt)
+  // is hidden unit 16 (w HT + j) + 4 lg + i of row 16 tt + lr; four consecutive units are
+  // written as 8 bytes.
+  bf16x8 hf[4][S::KS2];  // GEMM2 B operand: row 16 tt + lr, hidden units 32 ks + 8 lg + i
+  {
+    const int hs = (n1 + S::NS - 1) % S::NS;
+    const uint32_t hb = stg0 + hs * S::STAGE;
+    ring_barrier();  // every wave is done with GEMM1's last stage
+#pragma unroll
+    for (int j = 0; j < S::HT; ++j)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        bf16x4 hv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float g = ag[t][i];
-          const float hv = KIND == FFN_SWIGLU ? silu_(g) * au[t][i] : gelu_erf(g);
-          hf[t >> 1][4 * (t & 1) + i] = (bf16)hv;
+          const float g = ag[j][tt][i];
+          hv[i] = (bf16)(KIND == FFN_SWIGLU ? silu_(g) * au[j][tt][i] : gelu_erf(g));
         }
-    }
-    // GEMM2 stage: output columns nc .. nc + C2 of this wave's 16 rows
-    const int nc = (s - n1) * S::C2;
-    floatx4 acc[S::NT2];
+        lds_write_b64(hb + (tt * 16 + lr) * S::HS + ((w * S::HT + j) * 16 + lg * 4) * 2, hv);
+      }
+    ring_barrier();  // the whole activation written
+    constexpr int NR = 4 * S::KS2;
+    uint32_t ad[NR];
 #pragma unroll
-    for (int nt = 0; nt < S::NT2; ++nt) acc[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int ks = 0; ks < S::KS2; ++ks)
+        ad[tt * S::KS2 + ks] = hb + (tt * 16 + lr) * S::HS + (ks * 32 + lg * 8) * 2;
+    lds_read_b128<NR>(reinterpret_cast<bf16x8(&)[NR]>(hf), ad);
+  }
+
+  for (int s = n1; s < ntot; ++s) {
+    wait_stage(s);  // at s = n1 also: every wave holds the activation
+    if (s + S::NS - 1 < ntot) issue(s + S::NS - 1);
+    const uint32_t sb = stg0 + (s % S::NS) * S::STAGE;
+    // GEMM2 stage: output columns nc + 16 (w CT + c) .. + 16 of all token rows
+    const int nc = (s - n1) * S::C2;
+    floatx4 acc[S::CT][4];
+#pragma unroll
+    for (int c = 0; c < S::CT; ++c)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) acc[c][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
     {
-      constexpr int NR = S::KS2 * S::NT2;  // all W2 fragments of the stage in one group
+      constexpr int NR = S::KS2 * S::CT;  // this wave's W2 fragments of the stage
       bf16x8 fw[NR];
       uint32_t ad[NR];
 #pragma unroll
       for (int ks = 0; ks < S::KS2; ++ks) {
         const int slot = ffn_swz(RB2, lr, ks * 4 + lg);
-        const uint32_t base = sb + lr * RB2 + (slot << 4);
+        const uint32_t base = sb + (w * S::CT * 16 + lr) * RB2 + (slot << 4);
 #pragma unroll
-        for (int nt = 0; nt < S::NT2; ++nt) ad[ks * S::NT2 + nt] = base + nt * 16 * RB2;
+        for (int c = 0; c < S::CT; ++c) ad[ks * S::CT + c] = base + c * 16 * RB2;
       }
       lds_read_b128<NR>(fw, ad);
 #pragma unroll
       for (int ks = 0; ks < S::KS2; ++ks)
 #pragma unroll
-        for (int nt = 0; nt < S::NT2; ++nt)
-          acc[nt] = mfma16(fw[ks * S::NT2 + nt], hf[ks], acc[nt]);
+        for (int c = 0; c < S::CT; ++c)
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt)
+            acc[c][tt] = mfma16(fw[ks * S::CT + c], hf[tt][ks], acc[c][tt]);
     }
-    if (nst_w) {  // wave-uniform; row 16 w is a slot row, so some lanes store
-      if (sl >= 0) {
-        bf16* orow = slots + (int64_t)sl * h_out + nc + lg * 4;
 #pragma unroll
-        for (int nt = 0; nt < S::NT2; ++nt) {
-          bf16x4 v;
+    for (int tt = 0; tt < 4; ++tt) {
+      if (tt * 16 < nrows) {  // uniform; row 16 tt is a slot row, so some lanes store
+        if (sl[tt] >= 0) {
+          bf16* orow = slots + (int64_t)sl[tt] * h_out + nc + w * S::CT * 16 + lg * 4;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = (bf16)(acc[nt][i] * gate);
-          store_b64_counted(orow + nt * 16, v);
+          for (int c = 0; c < S::CT; ++c) {
+            bf16x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = (bf16)(acc[c][tt][i] * gate[tt]);
+            store_b64_counted(orow + c * 16, v);
+          }
         }
       }
     }

@@ -140,7 +140,7 @@ void launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st);
 // expert's end in its last tile are left unwritten).  hist_ready: hist already holds the
 // chunk histograms (counted by the fused router); zero_next (optional): another buffer
 // of the hist shape that the scatter clears, ready for the next histogram.
-constexpr int PERM_CHUNK = 2048, PERM_MAX_E = 8192, COUNT_MAX_E = 16384;
+constexpr int PERM_CHUNK = 1024, PERM_MAX_E = 8192, COUNT_MAX_E = 16384;
 int perm_blocks(int64_t nslots);
 int launch_permute(const int32_t* idx, int64_t nslots, int E, int tile_m, int32_t* hist,
                    int32_t* counts, int32_t* goff, int32_t* toff, int32_t* perm,
