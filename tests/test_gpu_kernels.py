@@ -251,6 +251,8 @@ def _routing(T, E, k, seed, skew=False):
     ("bf16", "swiglu", 300, 512, 64, 256, 4, False),
     ("bf16", "swiglu", 100, 1024, 128, 64, 8, True),
     ("bf16", "gelu", 77, 256, 64, 8, 2, False),
+    ("bf16", "gelu", 150, 512, 128, 16, 4, True),     # wide GELU: activation-sized stages
+    ("bf16", "swiglu", 64, 2048, 128, 8, 2, False),   # long GEMM1 K loop
     ("bf16", "linear", 130, 256, 0, 16, 1, True),
     ("f32", "gelu", 16, 64, 32, 16, 1, False),
     ("f32", "swiglu", 20, 64, 32, 8, 2, False),
