@@ -261,17 +261,30 @@ def usage_report(D, cfg, G, x0, lc, route, iters=20, lam=0.01):
     return out
 
 
-def cpu_baseline(cfg, min_seconds=10.0, max_reps=8):
-    """The CPU oracle, as it stands, on a bounded sample of the workload: the whole
-    workload when it is small (the default one), else the first sequence's first 256
-    tokens; forwards repeated until about min_seconds of CPU work."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, W_dev, min_seconds=10.0, max_reps=8):
+    """The CPU oracle (libdreamer_ref: plain float64 C++17 + OpenMP, one thread per host
+    core this process may run on), as it stands, timed with a steady clock around its
+    layer forward on a bounded sample of the workload: the whole workload when it is small,
+    else the first sequence's first 128 tokens over all L depths; forwards repeated until
+    about min_seconds of CPU work.  W_dev: the workload's weights (the bench's device
+    copies, brought to the host)."""
     import oracle
-    from synth import make_weights, make_x0
-    from threadpoolctl import threadpool_info
+    from synth import make_x0
     whole = cfg.T * cfg.h * cfg.L <= 2 ** 26
-    nb, s_len = (cfg.b, cfg.s) if whole else (1, min(cfg.s, 256))
+    nb, s_len = (cfg.b, cfg.s) if whole else (1, min(cfg.s, 128))
     sample = cfg.replace(b=nb, s=s_len)
-    W = oracle.prepare_weights(make_weights(cfg), big_as_f32=True)
+    W = oracle.prepare_weights({k: v.cpu() for k, v in W_dev.items()}, big_as_f32=True)
     x0 = make_x0(cfg, b0=0, nb=nb, s_len=s_len).reshape(nb * s_len, cfg.h).numpy()
     reps, t0 = 0, time.perf_counter()
     while True:
@@ -280,12 +293,12 @@ def cpu_baseline(cfg, min_seconds=10.0, max_reps=8):
         dt = time.perf_counter() - t0
         if dt >= min_seconds or reps >= max_reps:
             break
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     what = (f"full {cfg.name} workload (b={cfg.b}, s={cfg.s}, L={cfg.L})" if whole else
             f"{cfg.name} workload, first sequence, first {s_len} tokens, L={cfg.L}")
     return {"value": round(nb * s_len * cfg.L * reps / dt, 2), "unit": "token-depth-steps/s",
-            "cores": threads, "kind": "oracle",
-            "sample": f"{what}, {reps} forward(s) in {dt:.1f} s, float64 numpy with bf16 "
+            "cores": oracle.THREADS, "kind": "oracle",
+            "sample": f"{what}, {reps} forward(s) in {dt:.1f} s; C++ oracle (float64, "
+                      f"OpenMP, {oracle.THREADS} threads on {_cpu_model()}) with bf16 "
                       f"storage emulation"}
 
 
@@ -408,7 +421,7 @@ def main():
     if not cfg.decode and not args.no_usage:
         line["expert_usage"] = usage_report(D, cfg, G, x0, lc, route)
     if not args.no_cpu_baseline and not cfg.decode:
-        line["cpu_baseline"] = cpu_baseline(cfg)
+        line["cpu_baseline"] = cpu_baseline(cfg, W)
     print(json.dumps(line), flush=True)
 
 

@@ -728,7 +728,10 @@ static int layer_run(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* 
       if (rc) return fail(DREAMER_E_UNSUPPORTED, "layer: projection permutation");
     }
     const bool last = l == L - 1;
-    void* yb = y_steps ? (char*)y_steps + (size_t)l * T * h * es : lw.yb;
+    // the storage copy of y feeds the router (PARTIAL, SERIAL); the fully parallel wiring's
+    // router reads xh, so no copy of y is stored there
+    void* y_out = y_steps ? (char*)y_steps + (size_t)l * T * h * es : nullptr;
+    void* yb = parallel ? nullptr : (y_out ? y_out : lw.yb);
     int32_t* ridx = nullptr;
     float* rgate = nullptr;
     if (c.use_ea) {
@@ -885,6 +888,10 @@ static int layer_run(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* 
       }
       else if ((rc = ea(yb, st))) return rc;
     }
+    if (parallel && y_out &&  // the router input of this step (xh) before it is replaced
+        hipMemcpyAsync(y_out, lw.xh, (size_t)T * h * es, hipMemcpyDeviceToDevice, st) !=
+            hipSuccess)
+      return fail(DREAMER_E_HIP, "layer: copy of the router input");
     // x_{l+1} = y + sum of the slots; the next step's RMSNorm
     float* xs = x_steps ? x_steps + (size_t)l * T * h : nullptr;
     TB(DREAMER_KC_COMBINE);

@@ -11,10 +11,11 @@
  *   [GS-de] gist.science German technical summary, "Methodik: Dreamer-Framework".
  *
  * Conventions shared by every entry point
- *   - Every tensor pointer is DEVICE memory owned by the caller.  The library never
- *     allocates, frees or synchronises; scratch space is passed in as `ws`/`ws_bytes`
- *     (query the size with the matching *_ws_bytes function).  Tables and weights are
- *     read only.
+ *   - Every tensor pointer is DEVICE memory owned by the caller.  No entry point
+ *     allocates or frees device memory: scratch space is passed in as `ws`/`ws_bytes`
+ *     (query the size with the matching *_ws_bytes function).  No entry point waits for
+ *     the device, except dreamer_timing_read, which synchronises on its timing events.
+ *     Tables and weights are read only.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = null stream).  The
  *     return value reports host-side validation and launch errors only; a fault inside
  *     a kernel surfaces at the caller's next synchronisation.
@@ -29,8 +30,13 @@
  *     size), DREAMER_E_UNSUPPORTED (a shape the kernels do not cover), DREAMER_E_WORKSPACE
  *     (ws too small), DREAMER_E_HIP (launch error).  dreamer_last_error() then returns a
  *     static, thread-local description.
- *   - The library is stateless and reentrant; calls that share output or ws buffers on
- *     different streams race.
+ *   - Library state, process-wide and kept until the process ends: (1) per device, one
+ *     side stream (default priority) and one fork/join event, created by the first
+ *     PARALLEL layer call with branch_streams (see below) and guarded by a mutex; (2) the
+ *     kernel-timing state of dreamer_timing_* (one harness at a time, not thread-safe);
+ *     (3) the thread-local error text.  Nothing else is kept between calls: calls on
+ *     different streams may run concurrently, but calls that share output or ws buffers
+ *     race.
  */
 #ifndef DREAMER_H
 #define DREAMER_H
@@ -275,7 +281,8 @@ typedef struct dreamer_layer_weights {
  *   route_idx, route_gate : [L, T, k] per-depth EA routing, or NULL
  *   proj_idx, proj_gate   : [L, T] per-depth projection routing (MoE), or NULL
  *   x_steps : [L, T, h] f32, x_{l+1} after every step, or NULL
- *   y_steps : [L, T, h] storage dtype, the router input y of every step, or NULL
+ *   y_steps : [L, T, h] storage dtype, the EA router input of every step (the storage
+ *             copy of y; of xh in the PARALLEL wiring), or NULL
  *   da_k, da_v : [T, L, H, d] DA caches, or NULL (then kept in ws); their old contents
  *                are never read
  *   sa_k, sa_v : [L, b, sa_cap, H, d] per-depth SA caches of rotated keys / values.

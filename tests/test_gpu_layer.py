@@ -1,17 +1,23 @@
-"""GPU parity of dreamer_layer_forward against the free-running CPU oracle on the same
-seeded inputs (no GPU value is ever fed to the oracle).
+"""GPU parity of dreamer_layer_forward against the CPU oracle on the same seeded inputs.
 
 float32 storage: max|err|/max|ref| <= 1e-5 on x_L and routing sets identical at every
-depth except oracle ties within 1e-6.  bf16 storage: max |RMSNorm(x_L^gpu) -
-RMSNorm(x_L^ref)| <= 2e-2 (unit gain); routing is compared and the agreement rate is
-bounded from below, since a bf16 storage difference of one ulp moves a router score by
-~1e-5 and flips the tokens whose top-k margin is smaller than that."""
+depth except oracle ties within 1e-6 (free-running on both sides).  bf16 storage:
+max |RMSNorm(x_L^gpu) - RMSNorm(x_L^ref)| <= 2e-2 (unit gain) with the oracle's expert
+choices replayed on the GPU; and in a free-running GPU run, at every depth, (1) the EA
+selection equals the oracle router's on the GPU's own router input (ties within 1e-6
+exempt), (2) at depth 0 every token whose oracle top-k margin exceeds the score change
+the two runs' different router inputs can cause selects the same set as the free-running
+oracle, (3) the top-1 projection selection (linear MoE) equals the oracle's wherever the
+margin exceeds what bf16 rounding of the recomputed x_hat can move.  GPU values (the
+router inputs, the stream x_l) are fed to the oracle only in (1) and (3), to recompute a
+selection."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from helpers import gpu_weights, lib_cfg, rel_err, rms_normed, routing_mismatch
+from helpers import check_free_routing, gpu_weights, lib_cfg, rel_err, rms_normed, \
+    routing_mismatch
 from synth import CONFIGS, make_weights, make_x0, rng
 from synth.configs import make_sa_cache
 
@@ -19,14 +25,19 @@ pytestmark = pytest.mark.gpu
 
 
 def run_gpu(D, cfg, W, x0, sa_cache=None, sa_cap=0, replay=None, streams=False,
-            fuse_attn=True):
+            fuse_attn=True, steps=False):
     """replay: an oracle result whose expert choices the GPU adopts (route_in);
     streams: independent branches on the library's side streams; fuse_attn: SA and DA
-    of a depth may share one launch."""
+    of a depth may share one launch; steps: also return x_steps (x_{l+1}, float32) and
+    y_steps (the EA router input of every depth)."""
     G = gpu_weights(D, cfg, W)
     lc = lib_cfg(D, cfg, sa_cap=sa_cap, streams=streams, fuse_attn=fuse_attn)
     T = cfg.T
     x = x0.reshape(T, cfg.h).float().cuda().contiguous()
+    xs = ys = None
+    if steps:
+        xs = torch.empty((cfg.L, T, cfg.h), dtype=torch.float32, device="cuda")
+        ys = torch.empty((cfg.L, T, cfg.h), dtype=cfg.torch_dtype, device="cuda")
     route = proj = None
     if cfg.use_ea:
         route = (torch.empty((cfg.L, T, cfg.k), dtype=torch.int32, device="cuda"),
@@ -41,13 +52,17 @@ def run_gpu(D, cfg, W, x0, sa_cache=None, sa_cap=0, replay=None, streams=False,
         if cfg.proj_experts:
             pin = torch.from_numpy(np.ascontiguousarray(replay["pidx"]).astype(np.int32)).cuda()
     out = D.dreamer_layer_forward(lc, G, x, route=route, proj_route=proj, sa_cache=sa_cache,
-                                  route_in=rin, proj_route_in=pin)
+                                  route_in=rin, proj_route_in=pin, x_steps=xs, y_steps=ys)
     torch.cuda.synchronize()
     res = {"x_out": out.cpu().numpy().astype(np.float64)}
     if route is not None:
         res["idx"], res["gate"] = route[0].cpu().numpy(), route[1].cpu().numpy()
     if proj is not None:
         res["pidx"] = proj[0].cpu().numpy()
+    if steps:
+        res["x_steps"] = xs.cpu().numpy().astype(np.float64)
+        res["y_steps"] = ys.float().cpu().numpy().astype(np.float64)
+        res["x0"] = x.cpu().numpy().astype(np.float64)
     return res
 
 
@@ -57,16 +72,13 @@ def run_ref(cfg, W, x0, sa_k=None, sa_v=None):
                                 return_steps=True)
 
 
-def check_routing(cfg, W, gpu, ref, exact):
-    """exact: every non-tie token identical.  Else returns the worst per-depth agreement."""
+def check_routing(cfg, W, gpu, ref):
+    """Free-running float32 runs: every token's selected set equals the free-running
+    oracle's at every depth, except oracle ties within 1e-6."""
     bias = W["bias"].float().numpy()
-    worst = 1.0
     for l in range(cfg.L):
         n_bad, n_ex = routing_mismatch(gpu["idx"][l], ref["steps"][l]["z"], bias, cfg.k)
-        if exact:
-            assert n_bad == 0, f"depth {l}: {n_bad} tokens routed differently ({n_ex} ties)"
-        worst = min(worst, 1.0 - n_bad / cfg.T)
-    return worst
+        assert n_bad == 0, f"depth {l}: {n_bad} tokens routed differently ({n_ex} ties)"
 
 
 def check_bf16(gpu, ref, tol=2e-2):
@@ -84,7 +96,7 @@ def test_layer_tiny_fp32(gpu_lib):
     gpu = run_gpu(gpu_lib, cfg, W, x0)
     ref = run_ref(cfg, W, x0)
     assert rel_err(gpu["x_out"], ref["x_out"]) <= 1e-5
-    check_routing(cfg, W, gpu, ref, exact=True)
+    check_routing(cfg, W, gpu, ref)
     assert np.abs(gpu["gate"] - ref["gate"]).max() <= 1e-5
 
 
@@ -108,7 +120,7 @@ def test_layer_small_shape_fp32_routing_exact(gpu_lib):
     gpu = run_gpu(gpu_lib, cfg, W, x0)
     ref = run_ref(cfg, W, x0)
     assert rel_err(gpu["x_out"], ref["x_out"]) <= 1e-5
-    check_routing(cfg, W, gpu, ref, exact=True)
+    check_routing(cfg, W, gpu, ref)
 
 
 def test_layer_linear_moe_shape_fp32(gpu_lib):
@@ -118,30 +130,49 @@ def test_layer_linear_moe_shape_fp32(gpu_lib):
     gpu = run_gpu(gpu_lib, cfg, W, x0)
     ref = run_ref(cfg, W, x0)
     assert rel_err(gpu["x_out"], ref["x_out"]) <= 1e-5
-    check_routing(cfg, W, gpu, ref, exact=True)
+    check_routing(cfg, W, gpu, ref)
     assert np.array_equal(gpu["pidx"], np.stack([s["pidx"] for s in ref["steps"]]))
 
 
+
+def test_linear_moe_gate_half_equals_scaled_dense(gpu_lib):
+    """All projection keys zero: every projection score is 0, so every token takes expert 0
+    (ties go to the lower index) with gate sigmoid(0) = 1/2, and the linear-MoE layer
+    ([PN] "Key design 3": sigma x W_e + max(sigma_hat) x W_sh) equals the dense layer with
+    W = (W_0 + W_sh) / 2 for Q/K/V and for O.  A dropped or doubled gate fails this."""
+    D = gpu_lib
+    cfg = CONFIGS["linear_moe"].replace(dtype="f32", b=1, s=70, h=256, H=4, L=3, E=64, f=128)
+    print("layer linear-moe f32, zero projection keys", flush=True)
+    W, x0 = make_weights(cfg), make_x0(cfg)
+    W["pkeys"] = torch.zeros_like(W["pkeys"])
+    moe = run_gpu(D, cfg, W, x0)
+    assert (moe["pidx"] == 0).all()
+    dcfg = cfg.replace(proj_experts=0)
+    Wd = {k_: v for k_, v in W.items()
+          if k_ not in ("w_qkv_e", "w_qkv_sh", "w_o_e", "w_o_sh", "w_pr", "pkeys")}
+    Wd["w_qkv"] = 0.5 * (W["w_qkv_e"][0] + W["w_qkv_sh"])
+    Wd["w_o"] = 0.5 * (W["w_o_e"][0] + W["w_o_sh"])
+    dense = run_gpu(D, dcfg, Wd, x0)
+    assert rel_err(moe["x_out"], dense["x_out"]) <= 1e-5
+    ref = run_ref(cfg, W, x0)
+    assert (ref["pidx"] == 0).all() and np.all(ref["pgate"] == 0.5)
+    assert rel_err(moe["x_out"], ref["x_out"]) <= 1e-5
+
 # ---------------------------------------------------------------------------------- bf16
 
-def bf16_layer_checks(D, cfg, W, x0, min_agree=0.9, free_tol=0.1):
+def bf16_layer_checks(D, cfg, W, x0, free_tol=0.1):
     """(a) replay: the GPU adopts the oracle's expert choices -> RMSNorm'd x_L within 2e-2;
-    (b) free-running: routing agreement per depth >= min_agree, and a loose bound on x_L
+    (b) free-running: the selection checks of check_free_routing, and a loose bound on x_L
     (a flipped expert moves that token by its gate times an expert output, and a flipped
     top-1 projection expert changes a token's whole Q/K/V, so the 2e-2 bound applies to
     the replayed run; free_tol=None skips the bound)."""
     ref = run_ref(cfg, W, x0)
     rep = run_gpu(D, cfg, W, x0, replay=ref)
     err_rep = check_bf16(rep, ref)
-    gpu = run_gpu(D, cfg, W, x0)
+    gpu = run_gpu(D, cfg, W, x0, steps=True)
     err_free = np.abs(rms_normed(gpu["x_out"]) - rms_normed(ref["x_out"])).max()
-    agree = check_routing(cfg, W, gpu, ref, exact=False) if cfg.use_ea else 1.0
-    pagree = 1.0
-    if cfg.proj_experts:
-        pagree = float(np.mean(gpu["pidx"] == np.stack([s["pidx"] for s in ref["steps"]])))
-    print(f"replay err {err_rep:.3e}; free-running err {err_free:.3e}, worst routing "
-          f"agreement {agree:.4f}, projection agreement {pagree:.4f}")
-    assert agree >= min_agree and pagree >= min_agree
+    print(f"replay err {err_rep:.3e}; free-running err {err_free:.3e}", flush=True)
+    check_free_routing(cfg, W, gpu, ref)
     if free_tol is not None:
         assert err_free <= free_tol, f"free-running normed err {err_free:.3e}"
 
@@ -193,7 +224,7 @@ def test_layer_depth_window_fp32(gpu_lib, window, dilation):
     gpu = run_gpu(gpu_lib, cfg, W, x0)
     ref = run_ref(cfg, W, x0)
     assert rel_err(gpu["x_out"], ref["x_out"]) <= 1e-5
-    check_routing(cfg, W, gpu, ref, exact=True)
+    check_routing(cfg, W, gpu, ref)
 
 
 def test_layer_depth_window_deep_bf16(gpu_lib):
@@ -216,7 +247,7 @@ def test_layer_depth_window_decode_fp32(gpu_lib):
     gpu = run_gpu(gpu_lib, cfg, W, x0, sa_cache=(sk.cuda(), sv.cuda()), sa_cap=cap)
     ref = run_ref(cfg, W, x0, rsk, rsv)
     assert rel_err(gpu["x_out"], ref["x_out"]) <= 1e-5
-    check_routing(cfg, W, gpu, ref, exact=True)
+    check_routing(cfg, W, gpu, ref)
 
 
 # -------------------------------------------------------------------------------- decode
@@ -235,14 +266,15 @@ def test_layer_decode_reduced(gpu_lib, dt, mixture):
     sv[:, :, :cfg.sa_pos] = make_sa_cache(cfg, "v")
     rsk, rsv = sk.double().numpy().copy(), sv.double().numpy().copy()
     gk, gv = sk.cuda(), sv.cuda()
-    gpu = run_gpu(gpu_lib, cfg, W, x0, sa_cache=(gk, gv), sa_cap=cap)
+    gpu = run_gpu(gpu_lib, cfg, W, x0, sa_cache=(gk, gv), sa_cap=cap, steps=dt == "bf16")
     ref = run_ref(cfg, W, x0, rsk, rsv)
     if dt == "f32":
         assert rel_err(gpu["x_out"], ref["x_out"]) <= 1e-5
-        check_routing(cfg, W, gpu, ref, exact=True)
+        check_routing(cfg, W, gpu, ref)
         assert rel_err(gv[:, :, cfg.sa_pos].cpu().double().numpy(), rsv[:, :, cfg.sa_pos]) <= 1e-5
     else:
         check_bf16(gpu, ref)
+        check_free_routing(cfg, W, gpu, ref)
     assert torch.isfinite(gk[:, :, cfg.sa_pos]).all()
 
 
@@ -292,7 +324,7 @@ def test_layer_mixture_tiny_fp32(gpu_lib, mixture, variant):
     ref = run_ref(cfg, W, x0)
     assert rel_err(gpu["x_out"], ref["x_out"]) <= 1e-5
     if cfg.use_ea:
-        check_routing(cfg, W, gpu, ref, exact=True)
+        check_routing(cfg, W, gpu, ref)
 
 
 @pytest.mark.parametrize("mixture", ["serial", "parallel"])
@@ -303,7 +335,7 @@ def test_layer_mixture_small_shape_fp32(gpu_lib, mixture):
     gpu = run_gpu(gpu_lib, cfg, W, x0)
     ref = run_ref(cfg, W, x0)
     assert rel_err(gpu["x_out"], ref["x_out"]) <= 1e-5
-    check_routing(cfg, W, gpu, ref, exact=True)
+    check_routing(cfg, W, gpu, ref)
 
 
 @pytest.mark.parametrize("s", [96, 520])

@@ -565,8 +565,13 @@ def test_mixtures_coincide_where_their_definitions_do():
 
 def _sa_torch(u, W, cfg):
     """Causal SDPA over RoPE'd q, k (complex-rotation form) from rows 0..3h of w_qkv."""
+    h = cfg.h
+    return _sa_torch_qkv(*(u @ W["w_qkv"][j * h:(j + 1) * h].T for j in range(3)), cfg)
+
+
+def _sa_torch_qkv(q, k, v, cfg):
+    """Causal SDPA of projections q, k, v [T, h] after RoPE (complex-rotation form)."""
     h, H, d = cfg.h, cfg.H, cfg.d
-    q, k, v = (u @ W["w_qkv"][j * h:(j + 1) * h].T for j in range(3))
     pos = (np.arange(cfg.T) % cfg.s).astype(np.float64)[:, None, None]
     q = _rope_complex(q.reshape(cfg.T, H, d), pos, cfg.rope_base)
     k = _rope_complex(k.reshape(cfg.T, H, d), pos, cfg.rope_base)
@@ -611,3 +616,39 @@ def test_parallel_wiring_one_depth_closed_form():
                     for t in range(cfg.T)])
     ref = xh + _sa_torch(xh, W, cfg) @ W["w_o"][:, :h].T + g[:, None] * ffn
     assert np.allclose(got, ref, atol=1e-11)
+
+
+# ------------------------------------------------------------ linear-MoE projections
+
+def test_linear_moe_one_depth_closed_form():
+    """L = 1, float32 storage, no EA ([PN] "Key design 3"; reading R12).  The projection
+    router's scores come from its definition, z = rho (x^ W_P^T) K_P^T (depth RoPE at
+    l = 0 of L = 1 rotates by zero); each token takes e* = argmax z with gate
+    sigma = sigmoid(z_e*), and every projection is sigma x (W_e* + W_sh).  DA over one
+    depth returns its value projection; SA is torch SDPA.  Dropping sigma, or using the
+    gate of another expert, fails this."""
+    cfg = CONFIGS["linear_moe"].replace(b=2, s=7, h=32, H=2, d=16, L=1, E=8, k=2, f=8, r=8,
+                                        proj_experts=4, dtype="f32", use_ea=False)
+    W = oracle.prepare_weights(make_weights(cfg))
+    x0 = make_x0(cfg).numpy().reshape(cfg.T, cfg.h)
+    got = oracle.layer_forward(cfg, W, x0)
+    h, T = cfg.h, cfg.T
+    xh = F.rms_norm(torch.from_numpy(x0.astype(np.float64)), (h,),
+                    torch.from_numpy(W["g"]), eps=cfg.rms_eps).numpy()
+    z = cfg.rho * (xh @ W["w_pr"].T) @ W["pkeys"].T
+    e = np.argmax(z, axis=1)
+    assert len(set(e.tolist())) > 1            # the per-token expert choice matters here
+    sig = 1.0 / (1.0 + np.exp(-z[np.arange(T), e]))
+    assert np.array_equal(got["pidx"][0], e)
+    assert np.allclose(got["pgate"][0], sig, atol=1e-15)
+
+    def layer(gate):
+        Wq = W["w_qkv_e"][e] + W["w_qkv_sh"][None]           # [T, 6h, h], per token
+        qkv = gate[:, None] * np.einsum("tnj,tj->tn", Wq, xh)
+        a_sa = _sa_torch_qkv(qkv[:, :h], qkv[:, h:2 * h], qkv[:, 2 * h:3 * h], cfg)
+        att = np.concatenate([a_sa, qkv[:, 5 * h:6 * h]], axis=1)
+        Wo = W["w_o_e"][e] + W["w_o_sh"][None]              # [T, h, 2h]
+        return xh + gate[:, None] * np.einsum("tnj,tj->tn", Wo, att)
+
+    assert np.allclose(got["x_out"], layer(sig), atol=1e-11)
+    assert np.abs(layer(np.ones(T)) - got["x_out"]).max() > 1e-3     # sigma is not vacuous
