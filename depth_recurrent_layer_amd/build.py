@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdreamer.so")
 SOURCES = ["gemm.hip", "attn.hip", "route.hip", "expert_ffn.hip", "moe.hip", "usage.hip",
-           "api.cpp"]
+           "noalloc.hip", "api.cpp"]
 ARCH = "gfx950"
 
 

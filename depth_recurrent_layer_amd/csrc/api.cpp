@@ -71,6 +71,14 @@ struct Timing {
 }  // namespace
 
 namespace dreamer {
+int api_fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
 void timing_begin(int kclass, hipStream_t st) {
   if (g_tm.kclass == kclass && g_tm.n < g_tm.max) (void)hipEventRecord(g_tm.ev0[g_tm.n], st);
 }

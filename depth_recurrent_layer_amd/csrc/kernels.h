@@ -194,5 +194,7 @@ void launch_absorb(int dtype, int64_t ne, int64_t n, const void* we, const void*
 // Kernel-class timing hooks (api.cpp).
 void timing_begin(int kclass, hipStream_t st);
 void timing_end(int kclass, hipStream_t st);
+// Records the thread's error text (dreamer_last_error) and returns `code`.
+int api_fail(int code, const char* fmt, ...);
 
 }  // namespace dreamer

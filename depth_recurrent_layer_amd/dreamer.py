@@ -65,6 +65,8 @@ _sig("dreamer_depth_attn_windowed", _i32, [_i32, _i64, _i32, _i32, _i32, _i32, _
 _sig("dreamer_seq_attn_ws_bytes", _sz, [_i32, _i32, _i32, _i32, _i32, _i64])
 _sig("dreamer_seq_attn", _i32, [_i32, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp,
                                 _i64, _vp, _vp, _vp, _f32, _i32, _vp, _sz, _vp])
+_sig("dreamer_seq_attn_noalloc", _i32, [_i32, _i32, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp,
+                                        _vp, _i64, _vp, _vp, _vp, _f32, _i32, _vp])
 _sig("dreamer_expert_route_ws_bytes", _sz, [_i64, _i32, _i32])
 _sig("dreamer_expert_route", _i32, [_i32, _i64, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp,
                                     _vp, _vp, _f32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
@@ -90,7 +92,8 @@ _sig("dreamer_timing_disable", _i32, [])
 # every symbol the header declares (checked by the CPU tests)
 EXPORTS = ["dreamer_last_error", "dreamer_version", "dreamer_rope_tables", "dreamer_depth_attn",
            "dreamer_depth_attn_windowed",
-           "dreamer_seq_attn_ws_bytes", "dreamer_seq_attn", "dreamer_expert_route_ws_bytes",
+           "dreamer_seq_attn_ws_bytes", "dreamer_seq_attn", "dreamer_seq_attn_noalloc",
+           "dreamer_expert_route_ws_bytes",
            "dreamer_expert_route", "dreamer_expert_ffn_ws_bytes", "dreamer_expert_ffn",
            "dreamer_absorb_shared", "dreamer_layer_ws_bytes", "dreamer_layer_forward",
            "dreamer_route_counts", "dreamer_bias_update", "dreamer_expert_usage",
@@ -177,6 +180,22 @@ def dreamer_seq_attn(q, k_new, v_new, pos0=0, k_cache=None, v_cache=None, cos_s=
     _check(lib.dreamer_seq_attn(dt, B, n, H, d, pos0, _p(q), _p(k_new), _p(v_new), _p(k_cache),
                                 _p(v_cache), cap, _p(out), _p(cos_s), _p(sin_s), float(scale),
                                 int(bool(sa_rope)), _p(ws), ws.numel(), _stream()))
+    return out
+
+
+def dreamer_seq_attn_noalloc(q, k_new, v_new, pos0=0, k_cache=None, v_cache=None, cos_s=None,
+                             sin_s=None, scale=None, sa_rope=True, out=None):
+    """dreamer_seq_attn on the library's fixed scratch (no workspace).  The library
+    allocates nothing; `out` is allocated here only when not given."""
+    _dev(q, k_new, v_new, k_cache, v_cache, cos_s, sin_s)
+    B, n, H, d = q.shape
+    out = torch.empty_like(q) if out is None else out
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    cap = 0 if k_cache is None else k_cache.shape[1]
+    _check(lib.dreamer_seq_attn_noalloc(_dt(q), B, n, H, d, pos0, _p(q), _p(k_new), _p(v_new),
+                                        _p(k_cache), _p(v_cache), cap, _p(out), _p(cos_s),
+                                        _p(sin_s), float(scale), int(bool(sa_rope)),
+                                        _stream()))
     return out
 
 

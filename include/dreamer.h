@@ -137,6 +137,26 @@ int dreamer_seq_attn(int dtype, int B, int q_len, int H, int d, int64_t pos0, co
                      dreamer_stream_t stream);
 
 /*
+ * dreamer_seq_attn without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, semantics and results as dreamer_seq_attn; its scratch
+ * is a fixed device array inside the library of DREAMER_NOALLOC_SCRATCH_BYTES (64 MiB),
+ * one copy per GPU, kept until the process ends (its address is looked up on the first
+ * call on each device).  Shapes whose dreamer_seq_attn_ws_bytes exceeds that limit are
+ * rejected with DREAMER_E_WORKSPACE before anything is launched (for example decode of
+ * 64 sequences x 32 heads x 64 over 4096 cached positions needs about 9 MB; bf16 prefill
+ * with RoPE needs 6 * B * q_len * H * d bytes).  Nothing is allocated or freed.  Every
+ * call on one GPU shares that GPU's array: calls that may overlap on one GPU (different
+ * streams, or host threads) race and must be serialised by the caller.
+ */
+#define DREAMER_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int dreamer_seq_attn_noalloc(int dtype, int B, int q_len, int H, int d, int64_t pos0,
+                             const void* q, const void* k_new, const void* v_new,
+                             void* k_cache, void* v_cache, int64_t cap, void* out,
+                             const float* cos_s, const float* sin_s, float scale, int sa_rope,
+                             dreamer_stream_t stream);
+
+/*
  * Expert-attention router ([PN] "Key design 2"; [GS-de] "Routing"):
  *   u = x W_r^T (rank r, float32), depth RoPE on u at depth l of L (same half-reversed
  *   rule as DA), z_e = rho * (u . keys_e); the k experts with the largest z_e + bias_e

@@ -134,3 +134,13 @@ def test_decode_tokens_validation():
     rc = D.lib.dreamer_decode_tokens(C.byref(cfg), C.byref(W), 1, None, None, None, None, None,
                                      None, None, None, None, 0, None)
     assert rc == D.E_INVAL and b"decode" in D.lib.dreamer_last_error()
+
+
+def test_seq_attn_noalloc_rejects_shapes_beyond_its_scratch():
+    """bf16 prefill with RoPE needs 6 B q_len H d bytes of scratch: 4 x 4096 x 16 x 64 needs
+    96 MiB, more than the fixed 64 MiB; rejected before anything touches the device."""
+    p = C.c_void_p(16)  # never dereferenced: the size check fails first
+    rc = D.lib.dreamer_seq_attn_noalloc(D.BF16, 4, 4096, 16, 64, 0, p, p, p, None, None, 0, p,
+                                        p, p, 0.125, 1, None)
+    assert rc == D.E_WORKSPACE
+    assert b"scratch" in D.lib.dreamer_last_error()
