@@ -1,13 +1,22 @@
 """Throughput of the Dreamer layer forward on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload small] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload deep] [--no-cpu-baseline]
 
 One step = one dreamer_layer_forward over the whole workload (all L depth steps of
 RMSNorm, projections, SA, DA, routing, permutation, expert FFNs and combine) on inputs
-already resident in HBM.  Prints one JSON line.  Inputs are seeded synthetic tensors of
-the workload's shapes (weights N(0, 0.02), tokens N(0, 1)), drawn on the device.  The line
+already resident in HBM.  The default workload is the largest one that fits one GPU, the
+deep recurrence (b=2, s=4096, h=2048, 32 heads x 64, L=64, E=2048 top-8, Zipf-skewed
+router bias).  Prints one JSON line.  Inputs are seeded synthetic tensors of the
+workload's shapes (weights N(0, 0.02), tokens N(0, 1)), drawn on the device.
+
+Timed region: exactly K forwards between two device synchronisations (value and
+ms_per_step from the wall clock), with a HIP event pair around every forward (the median
+is reported too) and the launches of the dominant kernel class bracketed by HIP events on
+their stream (roofline.achieved).  Before it, one instrumented forward per kernel class
+gives each class's time and its fraction of its binding roofline (classes).  The line
 also carries the per-step time of the three mixture wirings (serial, the default partial
-one, fully parallel) and their throughput relative to the serial wiring.
+one, fully parallel) and their throughput relative to the serial wiring, windowed depth
+attention, the expert-usage statistics, and the CPU oracle on a bounded sample.
 """
 from __future__ import annotations
 
@@ -33,7 +42,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="small")
+    p.add_argument("--workload", default="deep")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--kernel-class", default=None, help="time this class live (default: dominant)")
     p.add_argument("--decode-tokens", type=int, default=8,
@@ -122,6 +131,22 @@ def algorithmic_work(cfg, counts_per_depth, reps=1):
     return w
 
 
+def class_report(work, per_class):
+    """Per kernel class: ms per step from its instrumented forward (the event brackets add
+    a few microseconds per launch), and the fraction of its binding roofline that its
+    average launch reaches."""
+    out = {}
+    for c, (n, ms) in per_class.items():
+        if n == 0:
+            continue
+        e = {"ms_per_step": round(ms, 4), "launches": n}
+        if c in work and ("bytes" in work[c] or "flops" in work[c]):
+            r = roofline_entry(work[c], ms / n)
+            e.update(bound=r["bound"], achieved=r["achieved"], unit=r["unit"], frac=r["frac"])
+        out[c] = e
+    return out
+
+
 def n_depth_keys(l, window, dilation):
     """Depth slots DA reads at depth l: all l + 1 without a window, else the window's
     min(window, l + 1) plus the older slots at multiples of the dilation."""
@@ -154,8 +179,9 @@ PAGES_RELATIVE = {"serial": 0.0, "partial": 0.152, "parallel": 0.308}
 
 
 def time_mixtures(D, cfg, G, x0, steps):
-    """ms per forward of the three mixture wirings (the fully parallel one with its EA chain
-    on a side stream) and their throughput relative to the serial wiring."""
+    """ms per forward of the three mixture wirings (independent branches on side streams:
+    DA beside SA in the partial and fully parallel ones, the EA chain too in the fully
+    parallel one) and their throughput relative to the serial wiring."""
     import torch
     out = {}
     x_out = torch.empty((cfg.T, cfg.h), dtype=torch.float32, device="cuda")
@@ -221,7 +247,7 @@ def layer_cfg(D, cfg, cap=0, mixture="partial", fuse_attn=True):
                             normalize=cfg.normalize, proj_experts=cfg.proj_experts,
                             decode=cfg.decode, sa_pos=cfg.sa_pos, sa_cap=cap,
                             rope_base=cfg.rope_base, rms_eps=cfg.rms_eps, rho=cfg.rho,
-                            mixture=D.MIXTURES[mixture], branch_streams=mixture == "parallel",
+                            mixture=D.MIXTURES[mixture], branch_streams=True,
                             da_window=cfg.da_window, da_dilation=cfg.da_dilation,
                             fuse_attn=fuse_attn)
 
@@ -383,17 +409,25 @@ def main():
     if dom not in work or ("bytes" not in work[dom] and "flops" not in work[dom]):
         dom = "expert_ffn"
 
-    # timed region: K forwards, the dominant class bracketed by HIP events on its stream
+    # timed region: K forwards, an event pair around each, the dominant class's launches
+    # bracketed by HIP events on their stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
     D.timing_enable(dom, args.steps * work[dom]["launches"] + 8)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for e0, e1 in ev:
+        e0.record()
         step()
+        e1.record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     n_launch, dom_ms = D.timing_read()
     D.timing_disable()
     ms_per_step = elapsed * 1e3 / args.steps
+    ev_ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    ms_median = ev_ms[len(ev_ms) // 2] if len(ev_ms) % 2 else \
+        0.5 * (ev_ms[len(ev_ms) // 2 - 1] + ev_ms[len(ev_ms) // 2])
     value = cfg.T * cfg.L * reps * args.steps / elapsed
     roof = roofline_entry(work[dom], dom_ms / max(n_launch, 1))
     roof["traffic"] = stored_traffic(dom, cfg.name)
@@ -412,7 +446,8 @@ def main():
                                 f"positions" if cfg.decode else ""),
                    "tokens": cfg.T * reps, "depths": cfg.L, "parallelism": "single GPU"},
         "roofline": roof,
-        "kernel_ms_per_step": {c: round(per_class[c][1], 4) for c in CLASSES},
+        "ms_per_step_event_median": round(ms_median, 4),
+        "classes": class_report(work, per_class),
     }
     if not args.no_mixtures and not cfg.decode:
         line["mixtures"] = time_mixtures(D, cfg, G, x0, args.steps)

@@ -114,7 +114,7 @@ static int cu_count() {
 // device never interleave their event records.
 namespace {
 struct SideStreams {
-  hipStream_t s[1];
+  hipStream_t s[2];  // [0]: the fully parallel wiring's EA chain, [1]: depth attention
   hipEvent_t ev;
   std::mutex mu;
 };
@@ -697,19 +697,24 @@ static int layer_run(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* 
   // With branch_streams, the fully parallel wiring runs its EA chain on a side stream beside
   // the attention (DA beside SA is not forked: at these sizes the cross-stream
   // synchronisation costs more than the overlap gains).
-  SideStreams* ss = nullptr;
-  std::unique_lock<std::mutex> side_lock;
-  if (c.branch_streams && parallel && c.use_ea) {
-    ss = side_streams();
-    if (!ss) return fail(DREAMER_E_HIP, "layer: side streams unavailable");
-    side_lock = std::unique_lock<std::mutex>(ss->mu);  // the fork/join event is shared
-  }
-  hipStream_t sd_ea = ss ? ss->s[0] : st;
   // SA and DA in one launch where the flash grid alone would leave CUs idle in its tail:
   // its blocks (query blocks x heads x batch) fit the GPU at three per CU
   const bool pair_attn = c.fuse_attn && c.use_da && !serial && !sa_k && !c.decode &&
                          attn_pair_ok(dt, c.b, c.s, c.H, c.d, 0, lw.vt) &&
                          (int64_t)((c.s + 63) / 64) * c.H * c.b <= 3 * (int64_t)cu_count();
+  // Otherwise, with branch_streams, DA (bound by memory bandwidth) runs on a side stream
+  // beside SA (bound by the matrix cores and the vector ALU) in prefill: the two read
+  // only the projections and write disjoint outputs.
+  const bool da_side = c.branch_streams && c.use_da && !serial && !pair_attn && !c.decode;
+  SideStreams* ss = nullptr;
+  std::unique_lock<std::mutex> side_lock;
+  if ((c.branch_streams && parallel && c.use_ea) || da_side) {
+    ss = side_streams();
+    if (!ss) return fail(DREAMER_E_HIP, "layer: side streams unavailable");
+    side_lock = std::unique_lock<std::mutex>(ss->mu);  // the fork/join event is shared
+  }
+  hipStream_t sd_ea = (ss && parallel && c.use_ea) ? ss->s[0] : st;
+  hipStream_t sd_da = da_side ? ss->s[1] : st;
   // the fused router (bf16) counts the permutation's histograms
   const bool fused_hist = c.use_ea && router_fused_ok(dt, T, c.r, c.E, k);
   if (fused_hist)
@@ -884,6 +889,11 @@ static int layer_run(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* 
                                   c.da_dilation, st);
         TE(DREAMER_KC_ATTN);
         if (r2) return fail(DREAMER_E_UNSUPPORTED, "layer: paired attention shape");
+      } else if (da_side) {
+        side_fork(ss, st, sd_da);  // after the projection
+        if ((rc = run_da(sd_da))) return rc;
+        if ((rc = run_sa())) return rc;
+        side_join(ss, st, sd_da);  // before the output projection
       } else {
         if ((rc = run_sa())) return rc;
         if (c.use_da && (rc = run_da(st))) return rc;

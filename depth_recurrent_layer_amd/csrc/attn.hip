@@ -3,6 +3,8 @@
 // shapes outside the MFMA kernel.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -477,6 +479,9 @@ __global__ void sa_combine_kernel(int64_t nrows, int H, int d, int nsplit,
 namespace fa {
 constexpr int BQ = 64, BKEY = 64, NSTG = 3, TILE = 8192;  // bytes per K or V^T tile
 }
+// Largest excess (exp2 units) of a score over its query's reference maximum before the
+// flash kernels rescale: P stays <= 2^8.
+constexpr float SA_LAZY = 8.0f;
 
 DEV int swz128(int row, int c) { return row * 64 + ((c ^ (row & 7)) << 3); }  // elements
 
@@ -561,6 +566,7 @@ DEV void sa_flash_block(int qbx, int head, int b, int S, int H, const bf16* __re
   };
 
   const float sl2 = scale * 1.44269504088896341f;  // scale * log2(e)
+  const float lazy_thr = SA_LAZY / sl2;             // in score units
   float m = -INFINITY;
   floatx4 o[4];
 #pragma unroll
@@ -614,14 +620,17 @@ DEV void sa_flash_block(int qbx, int head, int b, int S, int H, const bf16* __re
         for (int i = 0; i < 4; ++i)
           if (kbase + (t >> 1) * 32 + lg * 8 + (t & 1) * 4 + i > qlim) sacc[t][i] = -INFINITY;
     }
-    float tmax = -INFINITY;
+    // Lazy rescaling: the reference m of each query moves only when one of this tile's
+    // scores exceeds it by more than SA_LAZY (2^8 in exp2 units), so P <= 256; softmax
+    // is invariant to the reference, and the rescale (a cross-lane max, one exp2 and 20
+    // multiplications) is skipped in almost every tile.
+    float lmax = -INFINITY;  // this lane's 16 scores
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sacc[t][i]);
-    tmax = max_xor32(max_xor16(tmax));
-    const float mn = fmaxf(m, tmax);
-    if (__any(mn > m)) {  // rescale only when some query's running max moved
+      for (int i = 0; i < 4; ++i) lmax = fmaxf(lmax, sacc[t][i]);
+    if (__any(lmax > m + lazy_thr)) {
+      const float mn = fmaxf(m, max_xor32(max_xor16(lmax)));
       const float corr = __builtin_amdgcn_exp2f((m - mn) * sl2);
       m = mn;
       osum *= corr;
@@ -632,7 +641,7 @@ DEV void sa_flash_block(int qbx, int head, int b, int S, int H, const bf16* __re
     // 32cc + 8lg + j (tile 2cc for j < 4, tile 2cc+1 for j >= 4).  P is rounded to bf16
     // (pairwise conversions) for the MFMA, numerator and denominator alike.
     bf16x8 ph[2];
-    const float msl = mn * sl2;
+    const float msl = m * sl2;
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
       floatx8 pv;
@@ -672,6 +681,210 @@ __global__ __launch_bounds__(256, 3) void sa_flash_kernel(
   __shared__ __attribute__((aligned(1024))) char stg[fa::NSTG][2 * fa::TILE];
   sa_flash_block(blockIdx.x, blockIdx.y, blockIdx.z, S, H, q, ldq, kk, ldk, vt, out, ldo, scale,
                  stg);
+}
+
+// Flash SA with two 16-query sets per wave, 128 queries per block of 4 waves: every K and
+// V^T fragment a wave reads from the LDS ring feeds the MFMAs of both sets, half the LDS
+// bytes and half the per-tile ring and address work per product of the one-set kernel
+// above (whose ring, fragment layout and key order it keeps).  Per query the arithmetic
+// is that kernel's, in the same order (same tiles, MFMAs, and rescale decisions taken per
+// 16-query set over the same 16 queries), so the outputs are the same bits.  Key tiles
+// below the block's first query need no mask and run in the first loop; the (at most
+// two) diagonal tiles run in a second loop with the causal mask.  Set 0 also runs the
+// block's last tile when it lies past all of its queries: every score is masked there,
+// nothing exceeds the reference maximum, and P = 0 adds nothing.
+namespace fa2 {
+constexpr int QS = 2, BQ = 64 * QS;
+}
+
+__global__ __launch_bounds__(256, 3) void sa_flash2_kernel(
+    int B, int S, int H, const bf16* __restrict__ q, int64_t ldq, const bf16* __restrict__ kk,
+    int64_t ldk, const bf16* __restrict__ vt, bf16* __restrict__ out, int64_t ldo,
+    float scale) {
+  using namespace fa;
+  constexpr int QS = fa2::QS, BQ2 = fa2::BQ;
+  __shared__ __attribute__((aligned(1024))) char stg[NSTG][2 * TILE];
+  const int nqb = (S + BQ2 - 1) / BQ2;
+  const int qb = nqb - 1 - (int)blockIdx.x;  // heavy (late) query blocks first
+  const int head = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int64_t tok0 = (int64_t)b * S;
+  const int hoff = head * 64;
+  const int q0 = qb * BQ2;
+
+  // set s of wave w: queries q0 + 64 s + 16 w + lr; Q^T fragments as in the one-set kernel
+  int qpos[QS], qlim[QS];
+  bf16x8 qf[QS][2];
+#pragma unroll
+  for (int s = 0; s < QS; ++s) {
+    qpos[s] = q0 + 64 * s + 16 * w + lr;
+    qlim[s] = min(qpos[s], S - 1);
+    const bf16* qr = q + (tok0 + qlim[s]) * ldq + hoff + lg * 8;
+    qf[s][0] = *reinterpret_cast<const bf16x8*>(qr);
+    qf[s][1] = *reinterpret_cast<const bf16x8*>(qr + 32);
+  }
+
+  // ring loads of one 64-key stage, as in the one-set kernel
+  const int lrow = lane >> 3, slot = lane & 7;
+  const bf16* vbase = vt + ((int64_t)(b * H + head) * 64) * S;
+  auto tile_src = [&](int i, int kbase) -> const bf16* {
+    const int j = w + 4 * i;
+    if (i < 2) {
+      const int row = j * 8 + lrow;
+      const int kp = min(kbase + key_of_row(row), S - 1);
+      return kk + (tok0 + kp) * ldk + hoff + (slot ^ (row & 7)) * 8;
+    }
+    const int dim = (j - 8) * 8 + lrow;
+    const int p0 = min(kbase + (slot ^ (dim & 7)) * 8, S - 8);
+    return vbase + (int64_t)dim * S + p0;
+  };
+  const char* kb_u = reinterpret_cast<const char*>(kk + tok0 * ldk + hoff);
+  const char* vb_u = reinterpret_cast<const char*>(vbase);
+  uint32_t loff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int j = w + 4 * i;
+    if (i < 2) {
+      const int row = j * 8 + lrow;
+      loff[i] = (uint32_t)((key_of_row(row) * ldk + (slot ^ (row & 7)) * 8) * 2);
+    } else {
+      const int dim = (j - 8) * 8 + lrow;
+      loff[i] = (uint32_t)(((int64_t)dim * S + (slot ^ (dim & 7)) * 8) * 2);
+    }
+  }
+  auto issue = [&](int t) {
+    char* sb = stg[t % NSTG];
+    const int kbase = t * BKEY;
+    const char* kt_u = kb_u + (int64_t)kbase * ldk * 2;
+    const char* vt_u = vb_u + (int64_t)kbase * 2;
+    if (kbase + BKEY <= S) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)((i < 2 ? kt_u : vt_u) + loff[i]),
+                                         (lds_void*)(sb + (w + 4 * i) * 1024), 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)tile_src(i, kbase),
+                                         (lds_void*)(sb + (w + 4 * i) * 1024), 16, 0, 0);
+    }
+  };
+
+  const float sl2 = scale * 1.44269504088896341f;  // scale * log2(e)
+  const float lazy_thr = SA_LAZY / sl2;             // in score units
+  float m[QS];
+  floatx4 o[QS][4], osum[QS];
+#pragma unroll
+  for (int s = 0; s < QS; ++s) {
+    m[s] = -INFINITY;
+    osum[s] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) o[s][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+  bf16x8 ones;  // row 0 all ones: the P.V MFMAs' extra product is the softmax denominator
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ones[j] = (bf16)(lr == 0 ? 1.f : 0.f);
+
+  const int nkt = (min(q0 + BQ2, S) - 1) / BKEY + 1;
+  const int nfull = min(q0 / BKEY, nkt);  // tiles whose keys all precede query q0
+  const uint32_t stg0 = lds_off(stg[0]);
+  const uint32_t kofs0 = 2 * swz128(lr, lg), kofs1 = 2 * swz128(lr, 4 + lg);
+  issue(0);
+  if (nkt > 1) issue(1);
+  asm volatile("" : "+v"(qf[0][0]), "+v"(qf[0][1]), "+v"(qf[1][0]), "+v"(qf[1][1]));
+
+  auto tile = [&](int kt, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    if (kt + 1 < nkt) wait_vmcnt<4>();
+    else wait_vmcnt<0>();
+    ring_barrier();  // tile kt visible to all waves; tile kt-1 consumed by all
+    if (kt + 2 < nkt) issue(kt + 2);
+    const uint32_t ks0 = stg0 + (kt % NSTG) * 2 * TILE, vs0 = ks0 + TILE;
+    const int kbase = kt * BKEY;
+    // kf[t] / kf[4 + t]: K rows 16t + lr, dims 0..31 / 32..63; vf[4cc + t]: V^T row
+    // (dim) 16t + lr, keys 32cc + 8lg + 0..7.  K first, V^T after the score MFMAs are
+    // issued (fewer live registers: three waves per SIMD).
+    bf16x8 kf[8], vf[8];
+    lds_read_b128_2x4<2048>(kf, ks0 + kofs0, ks0 + kofs1);
+    floatx4 sacc[QS][4];
+#pragma unroll
+    for (int s = 0; s < QS; ++s)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        sacc[s][t] = mfma16(kf[t], qf[s][0], floatx4{0.f, 0.f, 0.f, 0.f});
+        sacc[s][t] = mfma16(kf[4 + t], qf[s][1], sacc[s][t]);
+      }
+    lds_read_b128_2x4<2048>(vf, vs0 + kofs0, vs0 + kofs1);
+    if constexpr (MASK) {
+#pragma unroll
+      for (int s = 0; s < QS; ++s)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (kbase + (t >> 1) * 32 + lg * 8 + (t & 1) * 4 + i > qlim[s])
+              sacc[s][t][i] = -INFINITY;
+    }
+    // lazy rescaling per 16-query set, decided as in the one-set kernel
+    float lmax[QS];
+#pragma unroll
+    for (int s = 0; s < QS; ++s) {
+      lmax[s] = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lmax[s] = fmaxf(lmax[s], sacc[s][t][i]);
+    }
+#pragma unroll
+    for (int s = 0; s < QS; ++s) {
+      if (__any(lmax[s] > m[s] + lazy_thr)) {
+        const float mn = fmaxf(m[s], max_xor32(max_xor16(lmax[s])));
+        const float corr = __builtin_amdgcn_exp2f((m[s] - mn) * sl2);
+        m[s] = mn;
+        osum[s] *= corr;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) o[s][t] *= corr;
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < QS; ++s) {
+      bf16x8 ph[2];
+      const float msl = m[s] * sl2;
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        floatx8 pv;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          pv[j] = __builtin_amdgcn_exp2f(fmaf(sacc[s][2 * cc + (j >> 2)][j & 3], sl2, -msl));
+        ph[cc] = __builtin_convertvector(pv, bf16x8);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) o[s][t] = mfma16(vf[cc * 4 + t], ph[cc], o[s][t]);
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) osum[s] = mfma16(ones, ph[cc], osum[s]);
+    }
+  };
+  int kt = 0;
+  for (; kt < nfull; ++kt) tile(kt, std::false_type{});
+  for (; kt < nkt; ++kt) tile(kt, std::true_type{});
+
+#pragma unroll
+  for (int s = 0; s < QS; ++s) {
+    const float lsum = __shfl(osum[s][0], lr, 64);  // from the group-0 lane of this query
+    if (qpos[s] >= S) continue;
+    const float inv = 1.0f / lsum;
+    bf16* orow = out + (tok0 + qpos[s]) * ldo + hoff;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      bf16x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = (bf16)(o[s][t][i] * inv);
+      *reinterpret_cast<bf16x4*>(orow + t * 16 + lg * 4) = v;
+    }
+  }
 }
 
 // SA (flash, prepared inputs) and DA (bf16, head dim 64, inputs already rotated) of one
@@ -916,6 +1129,12 @@ int launch_seq_attn(int dtype, int B, int q_len, int H, int d, int64_t pos0, con
       fk = kr;
       fvt = vtt;
       fldq = fldk = h;
+    }
+    if (q_len > fa::BQ) {  // two query sets per wave once a block has more than 64 rows
+      dim3 grid((q_len + fa2::BQ - 1) / fa2::BQ, H, B);
+      dlaunch(sa_flash2_kernel, grid, 256, 0, st, B, q_len, H, fq, fldq, fk, fldk, fvt,
+              (bf16*)out, ldo, scale);
+      return 0;
     }
     dim3 grid((q_len + fa::BQ - 1) / fa::BQ, H, B);
     dlaunch(sa_flash_kernel, grid, 256, 0, st, B, q_len, H, fq, fldq, fk, fldk, fvt, (bf16*)out,

@@ -30,9 +30,9 @@
  *     size), DREAMER_E_UNSUPPORTED (a shape the kernels do not cover), DREAMER_E_WORKSPACE
  *     (ws too small), DREAMER_E_HIP (launch error).  dreamer_last_error() then returns a
  *     static, thread-local description.
- *   - Library state, process-wide and kept until the process ends: (1) per device, one
- *     side stream (default priority) and one fork/join event, created by the first
- *     PARALLEL layer call with branch_streams (see below) and guarded by a mutex; (2) the
+ *   - Library state, process-wide and kept until the process ends: (1) per device, two
+ *     side streams (default priority) and one fork/join event, created by the first
+ *     layer call that forks with branch_streams (see below) and guarded by a mutex; (2) the
  *     kernel-timing state of dreamer_timing_* (one harness at a time, not thread-safe);
  *     (3) the thread-local error text.  Nothing else is kept between calls: calls on
  *     different streams may run concurrently, but calls that share output or ws buffers
@@ -233,11 +233,13 @@ int dreamer_absorb_shared(int dtype, int64_t n_experts, int64_t n, const void* w
  *   SERIAL    u = xh + DA(xh);  v = u + SA(u);  x' = v + EA(v)     (DA -> SA -> EA)
  *   PARALLEL  x' = xh + DA(xh) + SA(xh) + EA(xh)                   (all three at once)
  * DA(.) / SA(.) include their halves of the output projection.  With branch_streams set,
- * PARALLEL runs its EA chain (router, grouping, experts) concurrently with the attention
- * on a side stream of the library (created once per device, default priority) forked
- * from and joined back into the caller's stream; otherwise, and for the other wirings,
- * everything runs in order on the caller's stream.  Results are the same bits either
- * way.  Calls that fork on one device serialise their enqueueing on a host mutex. */
+ * the independent branches of a step run concurrently on side streams of the library
+ * (two per device, created once, default priority) forked from and joined back into the
+ * caller's stream: in PARTIAL and PARALLEL prefill, DA beside SA (unless the two share
+ * one launch, see fuse_attn); in PARALLEL, also the EA chain (router, grouping, experts)
+ * beside the attention.  Otherwise, and for SERIAL, everything runs in order on the
+ * caller's stream.  Results are the same bits either way.  Calls that fork on one device
+ * serialise their enqueueing on a host mutex. */
 #define DREAMER_MIX_PARTIAL 0
 #define DREAMER_MIX_SERIAL 1
 #define DREAMER_MIX_PARALLEL 2
@@ -260,7 +262,7 @@ typedef struct dreamer_layer_cfg {
   double rope_base;     /* rotary base (SA, DA and routers)                           */
   float rms_eps;        /* RMSNorm epsilon                                           */
   float rho;            /* router score scale                                        */
-  int branch_streams;   /* 1: PARALLEL's EA chain on a side stream (see above)          */
+  int branch_streams;   /* 1: independent branches on side streams (see above)         */
   int da_window;        /* 0: DA over every depth 0..l; w > 0: only the w most recent  */
   int da_dilation;      /* with da_window > 0 and this > 0: also every da_dilation-th
                            older depth (see dreamer_depth_attn_windowed)               */

@@ -30,8 +30,10 @@ def _free():
 
 
 def gpu_forward(D, cfg, G, x0, sa_cache=None, sa_cap=0, replay=None, steps=False):
-    """steps: also return x_steps (f32) and y_steps (EA router inputs) on the device."""
-    lc = lib_cfg(D, cfg, sa_cap=sa_cap)
+    """The benchmark's launch configuration (independent branches on side streams, SA and
+    DA in one launch where that applies).  steps: also return x_steps (f32) and y_steps
+    (EA router inputs) on the device."""
+    lc = lib_cfg(D, cfg, sa_cap=sa_cap, streams=True)
     T = cfg.T
     x = x0.reshape(T, cfg.h).float().contiguous()
     route = (torch.empty((cfg.L, T, cfg.k), dtype=torch.int32, device="cuda"),

@@ -94,7 +94,13 @@ def _depth_attn_case(D, dt, H, d, rows, L, window=None, dilation=0):
                                              ("bf16", 1, 64, 2, 64, False),
                                              ("bf16", 3, 1, 2, 64, True),
                                              ("f32", 2, 37, 4, 16, True),
-                                             ("bf16", 2, 45, 2, 16, True)])
+                                             ("bf16", 2, 45, 2, 16, True),
+                                             # two query sets per wave (> 64 rows): a
+                                             # ragged last block, one set past the end,
+                                             # and a long sequence of 32 blocks
+                                             ("bf16", 2, 300, 4, 64, True),
+                                             ("bf16", 1, 72, 2, 64, False),
+                                             ("bf16", 1, 4096, 2, 64, True)])
 def test_seq_attn_prefill(gpu_lib, dt, B, S, H, d, rope):
     D = gpu_lib
     tdt, bf = TD[dt], dt == "bf16"

@@ -363,14 +363,16 @@ def test_layer_mixture_repeatable(gpu_lib, mixture):
     assert np.array_equal(a["x_out"], b["x_out"]) and np.array_equal(a["idx"], b["idx"])
 
 
+@pytest.mark.parametrize("fuse_attn", [True, False])
 @pytest.mark.parametrize("mixture", ["partial", "serial", "parallel"])
-def test_layer_branch_streams_same_bits(gpu_lib, mixture):
-    """Independent branches on side streams give the same bits as one stream."""
+def test_layer_branch_streams_same_bits(gpu_lib, mixture, fuse_attn):
+    """Independent branches on side streams give the same bits as one stream (without
+    fuse_attn, DA runs on its side stream beside SA)."""
     cfg = CONFIGS["small"].replace(b=2, s=520, L=3, mixture=mixture)
-    print(f"layer branch streams {mixture}", flush=True)
+    print(f"layer branch streams {mixture} fuse_attn={fuse_attn}", flush=True)
     W, x0 = make_weights(cfg), make_x0(cfg)
-    a = run_gpu(gpu_lib, cfg, W, x0)
-    b = run_gpu(gpu_lib, cfg, W, x0, streams=True)
+    a = run_gpu(gpu_lib, cfg, W, x0, fuse_attn=fuse_attn)
+    b = run_gpu(gpu_lib, cfg, W, x0, streams=True, fuse_attn=fuse_attn)
     assert np.array_equal(a["x_out"], b["x_out"]) and np.array_equal(a["idx"], b["idx"])
 
 
