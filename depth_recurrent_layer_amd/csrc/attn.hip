@@ -704,9 +704,16 @@ __global__ __launch_bounds__(256, 3) void sa_flash2_kernel(
   using namespace fa;
   constexpr int QS = fa2::QS, BQ2 = fa2::BQ;
   __shared__ __attribute__((aligned(1024))) char stg[NSTG][2 * TILE];
+  // Blocks reach the 8 XCDs round-robin.  XCD x takes the (batch, head) pairs p with
+  // p % 8 == x, one pair's query blocks after the other (heavy, late ones first), so a
+  // pair's K and V^T are read into one XCD's L2 only.
   const int nqb = (S + BQ2 - 1) / BQ2;
-  const int qb = nqb - 1 - (int)blockIdx.x;  // heavy (late) query blocks first
-  const int head = blockIdx.y, b = blockIdx.z;
+  const int npairs = B * H, ppx = (npairs + 7) / 8;
+  const int xcd = (int)blockIdx.x & 7, j = (int)blockIdx.x >> 3;
+  const int pair = xcd + 8 * (j / nqb);
+  if (j >= ppx * nqb || pair >= npairs) return;
+  const int qb = nqb - 1 - j % nqb;
+  const int head = pair % H, b = pair / H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int64_t tok0 = (int64_t)b * S;
@@ -1131,9 +1138,11 @@ int launch_seq_attn(int dtype, int B, int q_len, int H, int d, int64_t pos0, con
       fldq = fldk = h;
     }
     if (q_len > fa::BQ) {  // two query sets per wave once a block has more than 64 rows
-      dim3 grid((q_len + fa2::BQ - 1) / fa2::BQ, H, B);
-      dlaunch(sa_flash2_kernel, grid, 256, 0, st, B, q_len, H, fq, fldq, fk, fldk, fvt,
-              (bf16*)out, ldo, scale);
+      const int64_t nqb = (q_len + fa2::BQ - 1) / fa2::BQ;
+      const int64_t ppx = ((int64_t)B * H + 7) / 8;  // (batch, head) pairs per XCD
+      if (8 * ppx * nqb > 0x7fffffff) return -1;
+      dlaunch(sa_flash2_kernel, (unsigned)(8 * ppx * nqb), 256, 0, st, B, q_len, H, fq, fldq,
+              fk, fldk, fvt, (bf16*)out, ldo, scale);
       return 0;
     }
     dim3 grid((q_len + fa::BQ - 1) / fa::BQ, H, B);
