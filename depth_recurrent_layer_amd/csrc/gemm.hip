@@ -382,14 +382,17 @@ int launch_gemm(const GemmArgs& a_in, int dtype, int out_f32, hipStream_t st) {
     return a.n_fast ? dim3(nn, nm) : dim3(nm, nn);
   };
   // QKV projections with the rotary epilogue (64-column wave tiles, one head each):
-  // 128 x 128 tiles of 8 waves at two blocks per CU; few rows, and grouped launches whose
+  // launches of at least one 256 x 256 tile per CU take those tiles, 16 waves in one block
+  // per CU on a two-stage ring of 128-byte K slices (two k-steps, 32 MFMAs per wave, per
+  // barrier: measured 3% faster at the deep shape than four stages of 64-byte slices);
+  // else 128 x 128 tiles of 8 waves at two blocks per CU; few rows, and grouped launches whose
   // tile offsets were built for 64-row m-tiles, take 64 x 128 tiles of 4 waves (grouped
   // launches built for 128-row m-tiles take the 128 x 128 tiles).
   if (a.qkv_h) {
     if (a.qkv_h % 128 || out_f32 || !a.rope_d4 || (a.sa_rope && !a.rope_s4)) return -1;
     if (a.toff && a.tile_m != 64 && a.tile_m != 128) return -1;
     if (!a.toff && k64 && tiles(256, 256) >= 256) {
-      dlaunch(gemm_bf16_kernel<bf16, GemmCfg<64, 64, 4, 4, 64, 4, 1, true>>, grid_of(256, 256), 1024, 0, st, a);
+      dlaunch(gemm_bf16_kernel<bf16, GemmCfg<64, 64, 4, 4, 128, 2, 1, true>>, grid_of(256, 256), 1024, 0, st, a);
     } else if (a.toff ? a.tile_m == 64 : tiles(128, 128) < 256) {
       if (k64)
         dlaunch(gemm_bf16_kernel<bf16, GemmCfg<32, 64, 2, 2, 128, 3, 2, false>>, grid_of(64, 128), 256, 0, st, a);

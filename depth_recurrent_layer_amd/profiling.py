@@ -8,6 +8,8 @@
     python -m depth_recurrent_layer_amd.profiling traffic-all <workload> <out dir>
         <fetch_counter.csv> <write_counter.csv> <copy_fetch.csv> <copy_write.csv> <copy_bytes>
         <command...>
+    python -m depth_recurrent_layer_amd.profiling mfma <workload> <out dir> <counter.csv>
+        <command...>
 
 All print markdown (traffic-all writes one file per kernel class); a traffic summary ends
 in a json block that the benchmark reads.
@@ -27,24 +29,39 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 
-# Sources of each timed kernel class (besides the shared device header), and the
-# kernel-name substring that picks its dispatches in a counter file of the small workload.
+# Sources of each timed kernel class (besides the shared device header), and per workload
+# the kernel-name substring that picks a class's dispatches in a counter file (the
+# launches choose their GEMM instances and the attention kernels by shape).
 CLASS_SOURCES = {
     "qkv_proj": ["gemm.hip"], "out_proj": ["gemm.hip"], "seq_attn": ["attn.hip"],
     "depth_attn": ["attn.hip"], "attention": ["attn.hip"], "route": ["route.hip"],
     "expert_ffn": ["expert_ffn.hip"], "combine": ["moe.hip"],
 }
 SHARED_SOURCES = ["common.h"]
-CLASS_KERNELS = {
-    "qkv_proj": "Li32ELi64ELi4ELi2ELi128ELi2ELi2ELb1",  # the 8-wave QKV instance (mangled)
-    "out_proj": "GemmCfg<32, 32, 2, 2, 128, 4, 2, false>",
-    "seq_attn": "sa_flash_kernel",
-    "depth_attn": "depth_attn_kernel",
-    "attention": "attn_pair_kernel",   # SA and DA in one launch
-    "route": "router_fused_bf16_kernel",
-    "expert_ffn": "expert_ffn_kernel",
-    "combine": "combine_norm_kernel",
+WORKLOAD_KERNELS = {
+    "small": {
+        "qkv_proj": "Li32ELi64ELi4ELi2ELi128ELi2ELi2ELb1",  # the 8-wave QKV instance (mangled)
+        "out_proj": "GemmCfg<32, 32, 2, 2, 128, 4, 2, false>",
+        "seq_attn": "sa_flash_kernel",
+        "depth_attn": "depth_attn_kernel",
+        "attention": "attn_pair_kernel",   # SA and DA in one launch
+        "route": "router_fused_bf16_kernel",
+        "expert_ffn": "expert_ffn_kernel",
+        "combine": "combine_norm_kernel",
+    },
+    "deep": {
+        "qkv_proj": "Li64ELi64ELi4ELi4ELi128ELi2ELi1ELb1",  # the 16-wave 256 x 256 instance
+        "out_proj": "GemmCfg<64, 64, 2, 2, 128, 2, 2, false>",
+        "seq_attn": "sa_flash2_kernel",    # two query sets per wave
+        "depth_attn": "depth_attn_kernel",
+        "route": "router_fused_bf16_kernel",
+        "expert_ffn": "expert_ffn_kernel",
+        "combine": "combine_norm_kernel",
+    },
 }
+# classes bound by the matrix cores (their MFMA-busy share is summarised)
+MFMA_CLASSES = ["qkv_proj", "out_proj", "seq_attn", "attention", "expert_ffn"]
+CLASS_KERNELS = WORKLOAD_KERNELS["small"]
 
 
 def source_digest(kclass: str | None = None) -> str:
@@ -130,6 +147,47 @@ def traffic_summary(kclass, kernel_substr, fetch_csv, write_csv, copy_fetch_csv,
             "copy_bytes": copy_bytes, "source_sha256": source_digest(kclass), "command": command}
 
 
+def counters_per_class(csv_path: str, kernels: dict) -> dict:
+    """Per kernel class: {counter: value summed over the class's dispatches}, and the
+    dispatch count."""
+    out = {}
+    for r in csv.DictReader(open(csv_path)):
+        name = r.get("Kernel_Name", "")
+        for kclass, sub in kernels.items():
+            if sub in name:
+                d = out.setdefault(kclass, {"dispatches": set()})
+                d["dispatches"].add(r.get("Dispatch_Id") or r.get("Correlation_Id"))
+                c = r["Counter_Name"]
+                d[c] = d.get(c, 0.0) + float(r["Counter_Value"])
+                break
+    for d in out.values():
+        d["dispatches"] = len(d["dispatches"])
+    return out
+
+
+def mfma_busy_md(kclass, workload, d, kernel, command) -> str:
+    """SQ_VALU_MFMA_BUSY_CYCLES over the busy cycles of the CUs' four SIMDs
+    (4 x SQ_BUSY_CU_CYCLES): the share of cycles in which a SIMD's matrix core works,
+    while the kernel occupies the CU."""
+    busy = d["SQ_VALU_MFMA_BUSY_CYCLES"] / (4.0 * d["SQ_BUSY_CU_CYCLES"])
+    per = {k: v / d["dispatches"] for k, v in d.items() if k != "dispatches"}
+    s = {"class": kclass, "workload": workload, "kernel": kernel,
+         "dispatches": d["dispatches"], "mfma_busy": busy, "per_dispatch": per,
+         "source_sha256": source_digest(kclass), "command": command}
+    if per.get("SQ_INSTS_MFMA"):
+        s["valu_per_mfma"] = per.get("SQ_INSTS_VALU", 0.0) / per["SQ_INSTS_MFMA"]
+    out = [f"# MFMA busy share of `{kernel}` ({kclass}, {workload} workload)", "",
+           "SQ_VALU_MFMA_BUSY_CYCLES / (4 x SQ_BUSY_CU_CYCLES), summed over the class's "
+           "dispatches in one rocprofv3 --pmc run: the share of the cycles in which a CU "
+           "runs the kernel that its four SIMDs' matrix cores are busy.", "",
+           f"- dispatches: {d['dispatches']}",
+           f"- MFMA busy: {busy:.3f}"]
+    if "valu_per_mfma" in s:
+        out.append(f"- VALU instructions per MFMA instruction: {s['valu_per_mfma']:.2f}")
+    out += [f"- command: {command}", "", "```json", json.dumps(s, indent=1), "```"]
+    return "\n".join(out) + "\n"
+
+
 def traffic_md(s) -> str:
     out = [f"# HBM traffic of `{s['kernel']}` ({s['class']})", "",
            "FETCH_SIZE and WRITE_SIZE (KiB per dispatch) from two separate rocprofv3 --pmc "
@@ -153,9 +211,22 @@ if __name__ == "__main__":
         s = traffic_summary(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6],
                             sys.argv[7], float(sys.argv[8]), " ".join(sys.argv[9:]))
         sys.stdout.write(traffic_md(s))
+    elif mode == "mfma":
+        workload, out_dir, pmc_csv = sys.argv[2], sys.argv[3], sys.argv[4]
+        kernels = WORKLOAD_KERNELS[workload]
+        per = counters_per_class(pmc_csv, kernels)
+        for kclass in MFMA_CLASSES:
+            if kclass not in per or "SQ_VALU_MFMA_BUSY_CYCLES" not in per[kclass]:
+                continue
+            path = os.path.join(out_dir, f"{kclass}_{workload}_mfma_busy.md")
+            md = mfma_busy_md(kclass, workload, per[kclass], kernels[kclass],
+                              " ".join(sys.argv[5:]))
+            with open(path, "w") as fh:
+                fh.write(md)
+            print(kclass, md.splitlines()[5])
     elif mode == "traffic-all":
         workload, out_dir = sys.argv[2], sys.argv[3]
-        for kclass, kname in CLASS_KERNELS.items():
+        for kclass, kname in WORKLOAD_KERNELS[workload].items():
             s = traffic_summary(kclass, kname, sys.argv[4], sys.argv[5], sys.argv[6],
                                 sys.argv[7], float(sys.argv[8]), " ".join(sys.argv[9:]))
             path = os.path.join(out_dir, f"{kclass}_{workload}_hbm_traffic.md")
