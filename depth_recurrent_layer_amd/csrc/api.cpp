@@ -7,7 +7,6 @@
 #include <stdio.h>
 #include <string.h>
 
-#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -92,18 +91,17 @@ void timing_end(int kclass, hipStream_t st) {
 }  // namespace dreamer
 
 // compute units of the current device (cached per device)
-int dreamer::device_cus() {
-  static std::atomic<int> cus[64];
+static int cu_count() {
+  static int cus[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int n = cus[dev].load(std::memory_order_relaxed);
-  if (n <= 0) {
+  if (!cus[dev]) {
+    int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev].store(n, std::memory_order_relaxed);
+    cus[dev] = n;
   }
-  return n;
+  return cus[dev];
 }
-static int cu_count() { return dreamer::device_cus(); }
 
 #define TB(kc) timing_begin(kc, st)
 #define TE(kc) timing_end(kc, st)
@@ -391,7 +389,7 @@ static FfnWs plan_ffn(Bump& b, int dtype, int64_t T, int h_out, int E, int k) {
   FfnWs w;
   w.counts = b.take_n<int32_t>(E);
   w.goff = b.take_n<int32_t>(E + 1);
-  w.toff = b.take_n<int32_t>(E + 1 + FFN_XCDS);  // + the FFN's per-XCD tile counters
+  w.toff = b.take_n<int32_t>(E + 1);
   w.hist = b.take_n<int32_t>((size_t)std::max(1, perm_blocks(T * k)) * E);
   // compact (grouped GEMM) or tile-padded (fused FFN) expert-major order
   const size_t npad = (size_t)tile_bound(T * k, E, FFN_TILE_M) * FFN_TILE_M;

@@ -133,7 +133,10 @@ DEV void depth_attn_block(
     }
     m = group_sum<LPH>(s) * scale;
   }
-  constexpr int NB = 4;
+  // batches of two slots (two batches, eight 16-byte loads, in flight): measured faster
+  // than four at the deep workload, most at the first depths, where a batch of four
+  // mostly re-reads clamped slots
+  constexpr int NB = 2;
   // One batch of NB slots from raw 16-byte chunks: scores, one max and rescale for the
   // batch, then the weighted values (slots j >= l, or outside the key set, are skipped).
   typedef uint32_t raw16 __attribute__((ext_vector_type(4)));

@@ -1,7 +1,6 @@
 // Fused expert FFN for bf16 storage (SwiGLU or GELU) over routed slots.
 //
-// A block of four waves computes 64-row m-tiles of one expert's slots, one after the
-// other (persistent blocks take tiles from per-XCD queues).  A single ring of LDS
+// One block = one 64-row m-tile of one expert's slots, four waves.  A single ring of LDS
 // stages, filled by direct global->LDS loads (global_load_lds_dwordx4, several stages in
 // flight), streams everything the tile reads: first GEMM1's K slices (the gathered token
 // rows and the expert's W1 / W3 rows), then GEMM2's slices of W2 rows (output columns),
@@ -17,8 +16,6 @@
 //
 // Slices are XOR-swizzled by row in 16-byte chunks so that the 16 rows one fragment
 // read touches fall into distinct banks.
-#include <algorithm>
-
 #include "common.h"
 #include "kernels.h"
 
@@ -83,261 +80,235 @@ __global__ __launch_bounds__(256, (FfnCfg<F, KIND>::OCC)) void expert_ffn_kernel
     int k, int h_in, int h_out, const bf16* __restrict__ x, const bf16* __restrict__ w1,
     const bf16* __restrict__ w3, const bf16* __restrict__ w2, const int32_t* __restrict__ perm,
     const float* __restrict__ pgate, const int4* __restrict__ tiles, int tile_cap,
-    const int32_t* __restrict__ ntiles, int32_t* __restrict__ queue, bf16* __restrict__ slots) {
+    const int32_t* __restrict__ ntiles, bf16* __restrict__ slots) {
   using S = FfnCfg<F, KIND>;
   constexpr int BKB = S::BKB, RB2 = S::RB2;
   __shared__ __attribute__((aligned(1024))) char stg[S::NS * S::STAGE];
   __shared__ int s_slot[64];
-  __shared__ int s_tile;
 
-  // Persistent blocks, a few per CU.  The expert-major tile list is cut into FFN_XCDS
-  // equal ranges, one per XCD (blocks reach the XCDs round-robin, so block b sits on XCD
-  // b % FFN_XCDS): consecutive tiles mostly share an expert, whose weights then stay in
-  // that XCD's L2.  A block takes its XCD's tiles in order from that range's counter and,
-  // once the range is used up, the remaining tiles of the other ranges: a range whose
-  // tiles re-read one hot expert from L2 runs faster than one of single-tile experts
-  // streamed from HBM, and its blocks then take over the others' work instead of idling.
-  const int n_tiles = min(*ntiles, tile_cap);
-  const int xcd = (int)(blockIdx.x % FFN_XCDS);
-  unsigned dry = 0;  // (thread 0) ranges found used up
-  for (;;) {
-    // the lane indices pass through an empty asm statement once per tile, so that the
-    // addresses derived from them are computed per tile instead of being hoisted out of
-    // the tile loop and held in registers across it
-    int tid = threadIdx.x;
-    asm volatile("" : "+v"(tid));
-    const int lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
-    __syncthreads();  // every wave is done with the previous tile's ring stages and s_tile
-    if (tid == 0) {
-      int t = -1;
-      for (int q = 0; q < FFN_XCDS && t < 0; ++q) {
-        const int r = (xcd + q) % FFN_XCDS;
-        if ((dry >> r) & 1u) continue;
-        const int lo = (int)((int64_t)n_tiles * r / FFN_XCDS);
-        const int hi = (int)((int64_t)n_tiles * (r + 1) / FFN_XCDS);
-        const int i = atomicAdd(queue + r, 1);
-        if (i < hi - lo) t = lo + i;
-        else dry |= 1u << r;
-      }
-      s_tile = t;
+  // Blocks reach the 8 XCDs round-robin; block b takes tile (b % 8) * per + b / 8, so each
+  // XCD works through one contiguous range of tiles, where consecutive tiles mostly share
+  // an expert whose weights then stay in that XCD's L2.  The tile count, the descriptor
+  // and the tile's slot ids and gates (tile-padded by the permutation) come in one round
+  // trip; indices are clamped into the arrays and the values used only for a real tile.
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
+  const int n_tiles = *ntiles;
+  const int b = blockIdx.x, per = (n_tiles + 7) / 8;
+  const int tile = (b & 7) * per + (b >> 3);
+  const int tc = min(tile, tile_cap - 1);
+  const int4 td = tiles[tc];
+  const int pslot = perm[tc * 64 + (tid & 63)];  // row tid (first wave)
+  float gate[4];  // gates of this lane's output rows 16 tt + lr
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) gate[tt] = pgate[tc * 64 + tt * 16 + lr];
+  if ((b >> 3) >= per || tile >= n_tiles) return;
+  const int e = td.x, nrows = min(64, td.z - td.y);
+  if (tid < 64) s_slot[tid] = tid < nrows ? pslot : -1;
+  // the gates are taken through an empty asm statement: the compiler waits for them here,
+  // before the ring starts, instead of draining the ring at their first use
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) asm volatile("" : "+v"(gate[tt]));
+  __syncthreads();
+  int sl[4];  // output slot of row 16 tt + lr (-1: pad row)
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) sl[tt] = s_slot[tt * 16 + lr];
+
+  // load descriptors: wave w issues instructions q = w + 4 j of every stage
+  const bf16* src1[S::LPW1];  // GEMM1: token rows, then W1 (and W3) rows
+#pragma unroll
+  for (int j = 0; j < S::LPW1; ++j) {
+    const int q = w + 4 * j, slot = lane % S::CPR;
+    const int row = q * S::RPI + lane / S::CPR;  // row of the stage
+    if (row < 64) {
+      const int s = s_slot[row] >= 0 ? s_slot[row] : s_slot[0];  // pad rows repeat row 0
+      src1[j] = x + (int64_t)(s / k) * h_in + ffn_swz(BKB, row, slot) * 8;
+    } else {
+      const int hu = (row - 64) % F, m = (row - 64) / F;  // hidden unit, weight
+      const bf16* W = m == 0 ? w1 : w3;
+      src1[j] = W + ((int64_t)e * F + hu) * h_in + ffn_swz(BKB, hu, slot) * 8;
     }
-    __syncthreads();
-    const int tile = s_tile;
-    if (tile < 0) break;  // every range used up (the same in every wave)
-    // the descriptor and the tile's slot ids and gates (tile-padded by the permutation)
-    const int4 td = tiles[tile];
-    const int pslot = perm[tile * 64 + (tid & 63)];  // row tid (first wave)
-    float gate[4];  // gates of this lane's output rows 16 tt + lr
+  }
+  const bf16* src2[S::LPW2];  // GEMM2: W2 rows (output columns) of the first chunk
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) gate[tt] = pgate[tile * 64 + tt * 16 + lr];
-    const int e = td.x, nrows = min(64, td.z - td.y);
-    if (tid < 64) s_slot[tid] = tid < nrows ? pslot : -1;
-    // the gates are taken through an empty asm statement: the compiler waits for them here,
-    // before the ring starts, instead of draining the ring at their first use
+  for (int j = 0; j < S::LPW2; ++j) {
+    const int q = w + 4 * j, slot = lane % S::CPR2;
+    const int row = q * S::RPI2 + lane / S::CPR2;
+    src2[j] = w2 + ((int64_t)e * h_out + row) * F + ffn_swz(RB2, row, slot) * 8;
+  }
+  const int n1 = h_in * 2 / BKB, n2 = h_out / S::C2, ntot = n1 + n2;
+  auto issue = [&](int s) {
+    char* sb = stg + (s % S::NS) * S::STAGE;
+    if (s < n1) {
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) asm volatile("" : "+v"(gate[tt]));
-    __syncthreads();
-    int sl[4];  // output slot of row 16 tt + lr (-1: pad row)
+      for (int j = 0; j < S::LPW1; ++j)
+        __builtin_amdgcn_global_load_lds((const void*)(src1[j] + s * (BKB / 2)),
+                                         (lds_void*)(sb + (w + 4 * j) * 1024), 16, 0, 0);
+    } else {
+      const int64_t o = (int64_t)(s - n1) * S::C2 * F;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) sl[tt] = s_slot[tt * 16 + lr];
-
-    // load descriptors: wave w issues instructions q = w + 4 j of every stage
-    const bf16* src1[S::LPW1];  // GEMM1: token rows, then W1 (and W3) rows
-#pragma unroll
-    for (int j = 0; j < S::LPW1; ++j) {
-      const int q = w + 4 * j, slot = lane % S::CPR;
-      const int row = q * S::RPI + lane / S::CPR;  // row of the stage
-      if (row < 64) {
-        const int s = s_slot[row] >= 0 ? s_slot[row] : s_slot[0];  // pad rows repeat row 0
-        src1[j] = x + (int64_t)(s / k) * h_in + ffn_swz(BKB, row, slot) * 8;
-      } else {
-        const int hu = (row - 64) % F, m = (row - 64) / F;  // hidden unit, weight
-        const bf16* W = m == 0 ? w1 : w3;
-        src1[j] = W + ((int64_t)e * F + hu) * h_in + ffn_swz(BKB, hu, slot) * 8;
-      }
+      for (int j = 0; j < S::LPW2; ++j)
+        __builtin_amdgcn_global_load_lds((const void*)(src2[j] + o),
+                                         (lds_void*)(sb + (w + 4 * j) * 1024), 16, 0, 0);
     }
-    const bf16* src2[S::LPW2];  // GEMM2: W2 rows (output columns) of the first chunk
+  };
+
+  // Stage s has landed once at most the operations issued after its loads are
+  // outstanding: the loads of stages s+1 .. s+NS-2 and the output stores of the GEMM2
+  // iterations from the one that issued stage s on (CT store instructions per token
+  // tile that holds a slot row, per iteration; the same count in every wave).
+  const int nst_w = S::CT * ((nrows + 15) / 16);
+  auto wait_stage = [&](int s) {
+    int later = 0;
+    for (int t = s + 1; t < s + S::NS - 1 && t < ntot; ++t) later += t < n1 ? S::LPW1 : S::LPW2;
+    later += nst_w * max(0, s - max(n1, s - S::NS + 1));
+    wait_vmcnt_upto(later);
+    ring_barrier();  // stage s visible to all waves; stage s-1 fully consumed
+  };
+  const uint32_t stg0 = lds_off(stg);
+  for (int s = 0; s < S::NS - 1 && s < ntot; ++s) issue(s);
+
+  // GEMM1 accumulators: hidden tile w * HT + j of weight 1 (ag) and 3 (au), token tile tt
+  floatx4 ag[S::HT][4], au[S::HT][4];
 #pragma unroll
-    for (int j = 0; j < S::LPW2; ++j) {
-      const int q = w + 4 * j, slot = lane % S::CPR2;
-      const int row = q * S::RPI2 + lane / S::CPR2;
-      src2[j] = w2 + ((int64_t)e * h_out + row) * F + ffn_swz(RB2, row, slot) * 8;
+  for (int j = 0; j < S::HT; ++j)
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      ag[j][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      au[j][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
-    const int n1 = h_in * 2 / BKB, n2 = h_out / S::C2, ntot = n1 + n2;
-    auto issue = [&](int s) {
-      char* sb = stg + (s % S::NS) * S::STAGE;
-      if (s < n1) {
+  for (int s = 0; s < n1; ++s) {
+    wait_stage(s);
+    if (s + S::NS - 1 < ntot) issue(s + S::NS - 1);
+    const uint32_t sb = stg0 + (s % S::NS) * S::STAGE;
+    // every fragment of the stage in one read group (one LDS round trip per stage):
+    // per k-step the 4 token-row fragments, then HT fragments of each weight
+    constexpr int PER = 4 + S::NW1 * S::HT, NR = S::KSUB * PER;
+    bf16x8 fr[NR];
+    uint32_t ad[NR];
 #pragma unroll
-        for (int j = 0; j < S::LPW1; ++j)
-          __builtin_amdgcn_global_load_lds((const void*)(src1[j] + s * (BKB / 2)),
-                                           (lds_void*)(sb + (w + 4 * j) * 1024), 16, 0, 0);
-      } else {
-        const int64_t o = (int64_t)(s - n1) * S::C2 * F;
+    for (int kh = 0; kh < S::KSUB; ++kh) {
+      // fragments 16 rows apart share the swizzle slot (it depends on lr only)
+      const int slot = ffn_swz(BKB, lr, kh * 4 + lg);
+      const uint32_t xa = sb + lr * BKB + (slot << 4);
+      const uint32_t wa = sb + S::XB + (w * S::HT * 16 + lr) * BKB + (slot << 4);
 #pragma unroll
-        for (int j = 0; j < S::LPW2; ++j)
-          __builtin_amdgcn_global_load_lds((const void*)(src2[j] + o),
-                                           (lds_void*)(sb + (w + 4 * j) * 1024), 16, 0, 0);
-      }
-    };
-
-    // Stage s has landed once at most the operations issued after its loads are
-    // outstanding: the loads of stages s+1 .. s+NS-2 and the output stores of the GEMM2
-    // iterations from the one that issued stage s on (CT store instructions per token
-    // tile that holds a slot row, per iteration; the same count in every wave).
-    const int nst_w = S::CT * ((nrows + 15) / 16);
-    auto wait_stage = [&](int s) {
-      int later = 0;
-      for (int t = s + 1; t < s + S::NS - 1 && t < ntot; ++t) later += t < n1 ? S::LPW1 : S::LPW2;
-      later += nst_w * max(0, s - max(n1, s - S::NS + 1));
-      wait_vmcnt_upto(later);
-      ring_barrier();  // stage s visible to all waves; stage s-1 fully consumed
-    };
-    const uint32_t stg0 = lds_off(stg);
-    for (int s = 0; s < S::NS - 1 && s < ntot; ++s) issue(s);
-
-    // GEMM1 accumulators: hidden tile w * HT + j of weight 1 (ag) and 3 (au), token tile tt
-    floatx4 ag[S::HT][4], au[S::HT][4];
+      for (int tt = 0; tt < 4; ++tt) ad[kh * PER + tt] = xa + tt * 16 * BKB;
 #pragma unroll
-    for (int j = 0; j < S::HT; ++j)
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        ag[j][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        au[j][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-      }
-    for (int s = 0; s < n1; ++s) {
-      wait_stage(s);
-      if (s + S::NS - 1 < ntot) issue(s + S::NS - 1);
-      const uint32_t sb = stg0 + (s % S::NS) * S::STAGE;
-      // every fragment of the stage in one read group (one LDS round trip per stage):
-      // per k-step the 4 token-row fragments, then HT fragments of each weight
-      constexpr int PER = 4 + S::NW1 * S::HT, NR = S::KSUB * PER;
-      bf16x8 fr[NR];
-      uint32_t ad[NR];
-#pragma unroll
-      for (int kh = 0; kh < S::KSUB; ++kh) {
-        // fragments 16 rows apart share the swizzle slot (it depends on lr only)
-        const int slot = ffn_swz(BKB, lr, kh * 4 + lg);
-        const uint32_t xa = sb + lr * BKB + (slot << 4);
-        const uint32_t wa = sb + S::XB + (w * S::HT * 16 + lr) * BKB + (slot << 4);
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) ad[kh * PER + tt] = xa + tt * 16 * BKB;
-#pragma unroll
-        for (int m = 0; m < S::NW1; ++m)
-#pragma unroll
-          for (int j = 0; j < S::HT; ++j)
-            ad[kh * PER + 4 + m * S::HT + j] = wa + m * S::WB + j * 16 * BKB;
-      }
-      lds_read_b128<NR>(fr, ad);
-#pragma unroll
-      for (int kh = 0; kh < S::KSUB; ++kh)
+      for (int m = 0; m < S::NW1; ++m)
 #pragma unroll
         for (int j = 0; j < S::HT; ++j)
-#pragma unroll
-          for (int tt = 0; tt < 4; ++tt) {
-            ag[j][tt] = mfma16(fr[kh * PER + 4 + j], fr[kh * PER + tt], ag[j][tt]);
-            if constexpr (KIND == FFN_SWIGLU)
-              au[j][tt] = mfma16(fr[kh * PER + 4 + S::HT + j], fr[kh * PER + tt], au[j][tt]);
-          }
+          ad[kh * PER + 4 + m * S::HT + j] = wa + m * S::WB + j * 16 * BKB;
     }
-
-    // Activation through LDS, in the stage GEMM1 finished last (slot (n1 - 1) % NS, whose
-    // next load, stage n1 + NS - 1, is issued by the first GEMM2 iteration, after a barrier
-    // that follows every wave's read of the activation): accumulator element i of (j, tt)
-    // is hidden unit 16 (w HT + j) + 4 lg + i of row 16 tt + lr; four consecutive units are
-    // written as 8 bytes.
-    bf16x8 hf[4][S::KS2];  // GEMM2 B operand: row 16 tt + lr, hidden units 32 ks + 8 lg + i
-    {
-      const int hs = (n1 + S::NS - 1) % S::NS;
-      const uint32_t hb = stg0 + hs * S::STAGE;
-      ring_barrier();  // every wave is done with GEMM1's last stage
+    lds_read_b128<NR>(fr, ad);
+#pragma unroll
+    for (int kh = 0; kh < S::KSUB; ++kh)
 #pragma unroll
       for (int j = 0; j < S::HT; ++j)
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
-          bf16x4 hv;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float g = ag[j][tt][i];
-            hv[i] = (bf16)(KIND == FFN_SWIGLU ? silu_(g) * au[j][tt][i] : gelu_erf(g));
-          }
-          lds_write_b64(hb + (tt * 16 + lr) * S::HS + ((w * S::HT + j) * 16 + lg * 4) * 2, hv);
+          ag[j][tt] = mfma16(fr[kh * PER + 4 + j], fr[kh * PER + tt], ag[j][tt]);
+          if constexpr (KIND == FFN_SWIGLU)
+            au[j][tt] = mfma16(fr[kh * PER + 4 + S::HT + j], fr[kh * PER + tt], au[j][tt]);
         }
-      ring_barrier();  // the whole activation written
-      constexpr int NR = 4 * S::KS2;
-      uint32_t ad[NR];
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int ks = 0; ks < S::KS2; ++ks)
-          ad[tt * S::KS2 + ks] = hb + (tt * 16 + lr) * S::HS + (ks * 32 + lg * 8) * 2;
-      lds_read_b128<NR>(reinterpret_cast<bf16x8(&)[NR]>(hf), ad);
-    }
+  }
 
-    for (int s = n1; s < ntot; ++s) {
-      wait_stage(s);  // at s = n1 also: every wave holds the activation
-      if (s + S::NS - 1 < ntot) issue(s + S::NS - 1);
-      const uint32_t sb = stg0 + (s % S::NS) * S::STAGE;
-      // GEMM2 stage: output columns nc + 16 (w CT + c) .. + 16 of all token rows
-      const int nc = (s - n1) * S::C2;
-      floatx4 acc[S::CT][4];
+  // Activation through LDS, in the stage GEMM1 finished last (slot (n1 - 1) % NS, whose
+  // next load, stage n1 + NS - 1, is issued by the first GEMM2 iteration, after a barrier
+  // that follows every wave's read of the activation): accumulator element i of (j, tt)
+  // is hidden unit 16 (w HT + j) + 4 lg + i of row 16 tt + lr; four consecutive units are
+  // written as 8 bytes.
+  bf16x8 hf[4][S::KS2];  // GEMM2 B operand: row 16 tt + lr, hidden units 32 ks + 8 lg + i
+  {
+    const int hs = (n1 + S::NS - 1) % S::NS;
+    const uint32_t hb = stg0 + hs * S::STAGE;
+    ring_barrier();  // every wave is done with GEMM1's last stage
 #pragma unroll
-      for (int c = 0; c < S::CT; ++c)
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) acc[c][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-      {
-        constexpr int NR = S::KS2 * S::CT;  // this wave's W2 fragments of the stage
-        bf16x8 fw[NR];
-        uint32_t ad[NR];
-#pragma unroll
-        for (int ks = 0; ks < S::KS2; ++ks) {
-          const int slot = ffn_swz(RB2, lr, ks * 4 + lg);
-          const uint32_t base = sb + (w * S::CT * 16 + lr) * RB2 + (slot << 4);
-#pragma unroll
-          for (int c = 0; c < S::CT; ++c) ad[ks * S::CT + c] = base + c * 16 * RB2;
-        }
-        lds_read_b128<NR>(fw, ad);
-#pragma unroll
-        for (int ks = 0; ks < S::KS2; ++ks)
-#pragma unroll
-          for (int c = 0; c < S::CT; ++c)
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt)
-              acc[c][tt] = mfma16(fw[ks * S::CT + c], hf[tt][ks], acc[c][tt]);
-      }
+    for (int j = 0; j < S::HT; ++j)
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
-        if (tt * 16 < nrows) {  // uniform; row 16 tt is a slot row, so some lanes store
-          if (sl[tt] >= 0) {
-            bf16* orow = slots + (int64_t)sl[tt] * h_out + nc + w * S::CT * 16 + lg * 4;
+        bf16x4 hv;
 #pragma unroll
-            for (int c = 0; c < S::CT; ++c) {
-              bf16x4 v;
+        for (int i = 0; i < 4; ++i) {
+          const float g = ag[j][tt][i];
+          hv[i] = (bf16)(KIND == FFN_SWIGLU ? silu_(g) * au[j][tt][i] : gelu_erf(g));
+        }
+        lds_write_b64(hb + (tt * 16 + lr) * S::HS + ((w * S::HT + j) * 16 + lg * 4) * 2, hv);
+      }
+    ring_barrier();  // the whole activation written
+    constexpr int NR = 4 * S::KS2;
+    uint32_t ad[NR];
 #pragma unroll
-              for (int i = 0; i < 4; ++i) v[i] = (bf16)(acc[c][tt][i] * gate[tt]);
-              store_b64_counted(orow + c * 16, v);
-            }
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int ks = 0; ks < S::KS2; ++ks)
+        ad[tt * S::KS2 + ks] = hb + (tt * 16 + lr) * S::HS + (ks * 32 + lg * 8) * 2;
+    lds_read_b128<NR>(reinterpret_cast<bf16x8(&)[NR]>(hf), ad);
+  }
+
+  for (int s = n1; s < ntot; ++s) {
+    wait_stage(s);  // at s = n1 also: every wave holds the activation
+    if (s + S::NS - 1 < ntot) issue(s + S::NS - 1);
+    const uint32_t sb = stg0 + (s % S::NS) * S::STAGE;
+    // GEMM2 stage: output columns nc + 16 (w CT + c) .. + 16 of all token rows
+    const int nc = (s - n1) * S::C2;
+    floatx4 acc[S::CT][4];
+#pragma unroll
+    for (int c = 0; c < S::CT; ++c)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) acc[c][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    {
+      constexpr int NR = S::KS2 * S::CT;  // this wave's W2 fragments of the stage
+      bf16x8 fw[NR];
+      uint32_t ad[NR];
+#pragma unroll
+      for (int ks = 0; ks < S::KS2; ++ks) {
+        const int slot = ffn_swz(RB2, lr, ks * 4 + lg);
+        const uint32_t base = sb + (w * S::CT * 16 + lr) * RB2 + (slot << 4);
+#pragma unroll
+        for (int c = 0; c < S::CT; ++c) ad[ks * S::CT + c] = base + c * 16 * RB2;
+      }
+      lds_read_b128<NR>(fw, ad);
+#pragma unroll
+      for (int ks = 0; ks < S::KS2; ++ks)
+#pragma unroll
+        for (int c = 0; c < S::CT; ++c)
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt)
+            acc[c][tt] = mfma16(fw[ks * S::CT + c], hf[tt][ks], acc[c][tt]);
+    }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      if (tt * 16 < nrows) {  // uniform; row 16 tt is a slot row, so some lanes store
+        if (sl[tt] >= 0) {
+          bf16* orow = slots + (int64_t)sl[tt] * h_out + nc + w * S::CT * 16 + lg * 4;
+#pragma unroll
+          for (int c = 0; c < S::CT; ++c) {
+            bf16x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = (bf16)(acc[c][tt][i] * gate[tt]);
+            store_b64_counted(orow + c * 16, v);
           }
         }
       }
     }
-  }  // next tile
+  }
 }
 
 int launch_expert_ffn(int dtype, int kind, int64_t nslots, int k, int h_in, int f, int h_out,
                       int E, const void* x, const void* w1, const void* w3, const void* w2,
                       const int32_t* perm, const float* pgate, const int4* tiles,
-                      int32_t* toff, void* slots, hipStream_t st) {
+                      const int32_t* toff, void* slots, hipStream_t st) {
   if (nslots <= 0) return 0;
   if (dtype == DT_F32) return -1;  // the f32 path uses launch_expert_ffn_f32
   if (h_in % 64 || h_out % 128) return -1;
+  // every tile index below the bound has a block (a multiple of the 8 XCDs)
   const int64_t cap = tile_bound(nslots, E, FFN_TILE_M);
-  // as many persistent blocks as the CUs hold at once, a whole number per XCD
-  const int per_xcd = std::max(1, device_cus() / FFN_XCDS);
+  const unsigned grid = (unsigned)((cap + 7) / 8 * 8);
 #define EF_CASE(FF, KK)                                                                     \
-  dlaunch(expert_ffn_kernel<FF, KK>,                                                        \
-          (unsigned)(FFN_XCDS * per_xcd * FfnCfg<FF, KK>::OCC), 256, 0, st, k, h_in, h_out, \
-          (const bf16*)x, (const bf16*)w1, (const bf16*)w3, (const bf16*)w2, perm, pgate,   \
-          tiles, (int)cap, toff + E, toff + E + 1, (bf16*)slots)
+  dlaunch(expert_ffn_kernel<FF, KK>, grid, 256, 0, st, k, h_in, h_out, (const bf16*)x,           \
+                                                  (const bf16*)w1, (const bf16*)w3,         \
+                                                  (const bf16*)w2, perm, pgate, tiles,      \
+                                                  (int)cap, toff + E, (bf16*)slots)
   if (kind == FFN_SWIGLU && f == 64) EF_CASE(64, FFN_SWIGLU);
   else if (kind == FFN_SWIGLU && f == 128) EF_CASE(128, FFN_SWIGLU);
   else if (kind == FFN_GELU && f == 64) EF_CASE(64, FFN_GELU);

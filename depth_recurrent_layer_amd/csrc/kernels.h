@@ -135,14 +135,12 @@ void launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st);
 // = slot id t*k+i of the j-th slot routed to e; order within an expert unspecified).
 // Optional: pgate [nslots] = gate in the same order (gate given), and tiles
 // [tile_bound(nslots, E, tile_m)] = {expert, first row, end of the expert's rows, 0} per
-// m-tile (the first toff[E] entries are written; toff then has E + 1 + FFN_XCDS entries,
-// the last FFN_XCDS of them the fused FFN's tile counters, cleared here).  pad: perm and pgate are tile-padded
+// m-tile (the first toff[E] entries are written).  pad: perm and pgate are tile-padded
 // instead ([tile_bound * tile_m]: row j of m-tile t at t * tile_m + j; the rows past an
 // expert's end in its last tile are left unwritten).  hist_ready: hist already holds the
 // chunk histograms (counted by the fused router); zero_next (optional): another buffer
 // of the hist shape that the scatter clears, ready for the next histogram.
 constexpr int PERM_CHUNK = 1024, PERM_MAX_E = 8192, COUNT_MAX_E = 16384;
-constexpr int FFN_XCDS = 8;  // per-XCD tile queues of the fused expert FFN
 int perm_blocks(int64_t nslots);
 int launch_permute(const int32_t* idx, int64_t nslots, int E, int tile_m, int32_t* hist,
                    int32_t* counts, int32_t* goff, int32_t* toff, int32_t* perm,
@@ -165,14 +163,11 @@ int launch_expert_usage(const int32_t* counts, int64_t n_sets, int E, float* sta
 
 // Fused expert FFN (GELU / SWIGLU): slots[s] = gate[s] * FFN_e(x[s / k]) for every
 // routed slot s, written in storage dtype [T*k, h_out].
-// perm / pgate / tiles / toff from launch_permute (tile_m = FFN_TILE_M); the kernel
-// advances the tile counters at toff + E + 1.
+// perm / pgate / tiles / toff from launch_permute (tile_m = FFN_TILE_M).
 int launch_expert_ffn(int dtype, int kind, int64_t nslots, int k, int h_in, int f, int h_out,
                       int E, const void* x, const void* w1, const void* w3, const void* w2,
                       const int32_t* perm, const float* pgate, const int4* tiles,
-                      int32_t* toff, void* slots, hipStream_t st);
-// Compute units of the current device (cached per device).
-int device_cus();
+                      const int32_t* toff, void* slots, hipStream_t st);
 constexpr int FFN_TILE_M = 64;
 // m-tile rows of the grouped (top-1 linear-MoE) Q/K/V/O projections
 constexpr int PROJ_TILE_M = 128;

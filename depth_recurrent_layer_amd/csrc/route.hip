@@ -696,9 +696,6 @@ DEV void expert_offsets(int* base, int* prev, int E, int tile_m, bool pub, bool 
     goff[E] = rtot;
     toff[E] = ttot;
   }
-  // with tile descriptors, toff[E + 1 .. E + 8] are the fused expert FFN's per-XCD tile
-  // counters: cleared here, ahead of the FFN launch that takes tiles with them
-  if (pub && tiles && tid < FFN_XCDS) toff[E + 1 + tid] = 0;
   __syncthreads();
 }
 
