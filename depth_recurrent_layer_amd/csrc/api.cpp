@@ -702,10 +702,17 @@ static int layer_run(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* 
   const bool pair_attn = c.fuse_attn && c.use_da && !serial && !sa_k && !c.decode &&
                          attn_pair_ok(dt, c.b, c.s, c.H, c.d, 0, lw.vt) &&
                          (int64_t)((c.s + 63) / 64) * c.H * c.b <= 3 * (int64_t)cu_count();
+  // Larger flash grids (query blocks of 128 rows): SA and DA blocks interleaved in one
+  // launch, so that every CU runs both (DA streams HBM while SA keeps the matrix cores
+  // and the VALU busy)
+  const bool pair2_attn = c.fuse_attn && c.use_da && !serial && !sa_k && !c.decode &&
+                          !pair_attn && c.s > 64 &&
+                          attn_pair_ok(dt, c.b, c.s, c.H, c.d, 0, lw.vt);
   // Otherwise, with branch_streams, DA (bound by memory bandwidth) runs on a side stream
   // beside SA (bound by the matrix cores and the vector ALU) in prefill: the two read
   // only the projections and write disjoint outputs.
-  const bool da_side = c.branch_streams && c.use_da && !serial && !pair_attn && !c.decode;
+  const bool da_side = c.branch_streams && c.use_da && !serial && !pair_attn && !pair2_attn &&
+                       !c.decode;
   SideStreams* ss = nullptr;
   std::unique_lock<std::mutex> side_lock;
   if ((c.branch_streams && parallel && c.use_ea) || da_side) {
@@ -887,6 +894,14 @@ static int layer_run(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* 
                                   qkv + 3 * h * es, qkv + 4 * h * es, qkv + 5 * h * es, 6 * h,
                                   DAk, DAv, att, att + h * es, 2 * h, scale, c.da_window,
                                   c.da_dilation, st);
+        TE(DREAMER_KC_ATTN);
+        if (r2) return fail(DREAMER_E_UNSUPPORTED, "layer: paired attention shape");
+      } else if (pair2_attn) {
+        TB(DREAMER_KC_ATTN);
+        int r2 = launch_attn_pair2(c.b, c.s, c.H, l, L, qkv, qkv + h * es, lw.vt,
+                                   qkv + 3 * h * es, qkv + 4 * h * es, qkv + 5 * h * es, 6 * h,
+                                   DAk, DAv, att, att + h * es, 2 * h, scale, c.da_window,
+                                   c.da_dilation, st);
         TE(DREAMER_KC_ATTN);
         if (r2) return fail(DREAMER_E_UNSUPPORTED, "layer: paired attention shape");
       } else if (da_side) {

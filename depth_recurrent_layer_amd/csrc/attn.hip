@@ -85,7 +85,7 @@ DEV void rope_chunk(float* x, int c, int d, int pos_fwd, int pos_rev, const floa
 // with (l - j) divisible by dilation; the skipped slots are never loaded.
 // Block blk of 256 threads (the body of depth_attn_kernel and of the paired launch).
 // NT: the cache's older slots are read with nontemporal loads.
-template <typename T, int LPH, bool ROPE, bool NT = false>
+template <typename T, int LPH, bool ROPE, bool NT = false, int NB_ = 2>
 DEV void depth_attn_block(
     int64_t blk, int64_t rows, int H, int d, int l, int L, const T* __restrict__ q,
     int64_t ldq, const T* __restrict__ kn, int64_t ldk, const T* __restrict__ vn, int64_t ldv,
@@ -133,10 +133,10 @@ DEV void depth_attn_block(
     }
     m = group_sum<LPH>(s) * scale;
   }
-  // batches of two slots (two batches, eight 16-byte loads, in flight): measured faster
-  // than four at the deep workload, most at the first depths, where a batch of four
-  // mostly re-reads clamped slots
-  constexpr int NB = 2;
+  // NB_ slots per batch (two batches in flight).  Two (eight 16-byte loads in flight) was
+  // measured faster than four at the deep workload in DA's own launch, most at the first
+  // depths, where a batch of four mostly re-reads clamped slots.
+  constexpr int NB = NB_;
   // One batch of NB slots from raw 16-byte chunks: scores, one max and rescale for the
   // batch, then the weighted values (slots j >= l, or outside the key set, are skipped).
   typedef uint32_t raw16 __attribute__((ext_vector_type(4)));
@@ -700,19 +700,17 @@ namespace fa2 {
 constexpr int QS = 2, BQ = 64 * QS;
 }
 
-__global__ __launch_bounds__(256, 3) void sa_flash2_kernel(
-    int B, int S, int H, const bf16* __restrict__ q, int64_t ldq, const bf16* __restrict__ kk,
-    int64_t ldk, const bf16* __restrict__ vt, bf16* __restrict__ out, int64_t ldo,
-    float scale) {
+// Work item (xcd, j) of the two-set flash grid: the (batch, head) pairs p with p % 8 == xcd,
+// one pair's query blocks after the other (heavy, late ones first); items past the grid
+// return.  stg: the block's ring (3 x 16 KiB, 1 KiB aligned).
+DEV void sa_flash2_block(int xcd, int j, int B, int S, int H, const bf16* __restrict__ q,
+                         int64_t ldq, const bf16* __restrict__ kk, int64_t ldk,
+                         const bf16* __restrict__ vt, bf16* __restrict__ out, int64_t ldo,
+                         float scale, char (*stg)[2 * fa::TILE]) {
   using namespace fa;
   constexpr int QS = fa2::QS, BQ2 = fa2::BQ;
-  __shared__ __attribute__((aligned(1024))) char stg[NSTG][2 * TILE];
-  // Blocks reach the 8 XCDs round-robin.  XCD x takes the (batch, head) pairs p with
-  // p % 8 == x, one pair's query blocks after the other (heavy, late ones first), so a
-  // pair's K and V^T are read into one XCD's L2 only.
   const int nqb = (S + BQ2 - 1) / BQ2;
   const int npairs = B * H, ppx = (npairs + 7) / 8;
-  const int xcd = (int)blockIdx.x & 7, j = (int)blockIdx.x >> 3;
   const int pair = xcd + 8 * (j / nqb);
   if (j >= ppx * nqb || pair >= npairs) return;
   const int qb = nqb - 1 - j % nqb;
@@ -897,6 +895,17 @@ __global__ __launch_bounds__(256, 3) void sa_flash2_kernel(
   }
 }
 
+// Blocks reach the 8 XCDs round-robin: block b is item (b % 8, b / 8), so a pair's K and
+// V^T are read into one XCD's L2 only.
+__global__ __launch_bounds__(256, 3) void sa_flash2_kernel(
+    int B, int S, int H, const bf16* __restrict__ q, int64_t ldq, const bf16* __restrict__ kk,
+    int64_t ldk, const bf16* __restrict__ vt, bf16* __restrict__ out, int64_t ldo,
+    float scale) {
+  __shared__ __attribute__((aligned(1024))) char stg[fa::NSTG][2 * fa::TILE];
+  sa_flash2_block((int)blockIdx.x & 7, (int)blockIdx.x >> 3, B, S, H, q, ldq, kk, ldk, vt, out,
+                  ldo, scale, stg);
+}
+
 // SA (flash, prepared inputs) and DA (bf16, head dim 64, inputs already rotated) of one
 // depth in one launch: blocks [0, nsa) are the flash blocks in the flash grid's order,
 // the rest the depth-attention blocks.  The two write disjoint outputs and read only the
@@ -935,6 +944,32 @@ __global__ __launch_bounds__(256, 3) void attn_pair_kernel(SaFlashArgs sa, DaArg
     depth_attn_block<bf16, 8, false>(bi - nsa, da.rows, da.H, 64, da.l, da.L, da.q, da.ldq, da.kn,
                                      da.ldk, da.vn, da.ldv, da.kc, da.vc, da.out, da.ldo, nullptr,
                                      nullptr, da.scale, da.window, da.dilation);
+  }
+}
+
+// SA (the two-set flash grid) and DA of one depth in one launch, the two kinds of block
+// interleaved in proportion: block i is flash block k = floor(i nsa / n) when
+// floor((i + 1) nsa / n) > k, else DA block i - k.  The dispatcher hands each freed slot
+// to the next block, so every CU keeps running both kinds (matrix-core and VALU work
+// beside HBM streaming) and the two finish together; in separate launches on two streams
+// SA's blocks hold all registers of the CUs they occupy and the two split the CUs.  Flash
+// block k is item (k % 8, k / 8): a fixed XCD per (batch, head) pair whenever the flash
+// blocks' spacing is constant (n / nsa an odd integer), as at the deep workload.  The DA
+// blocks batch their slots as DA's own launch does (the same bits).
+template <bool NT>
+__global__ __launch_bounds__(256, 3) void attn_pair2_kernel(SaFlashArgs sa, DaArgs da, int B,
+                                                            int64_t nsa, int64_t n) {
+  __shared__ __attribute__((aligned(1024))) char stg[fa::NSTG][2 * fa::TILE];
+  const int64_t i = blockIdx.x;
+  const int64_t k = i * nsa / n;
+  if ((i + 1) * nsa / n > k) {
+    sa_flash2_block((int)(k & 7), (int)(k >> 3), B, sa.S, sa.H, sa.q, sa.ldq, sa.kk, sa.ldk,
+                    sa.vt, sa.out, sa.ldo, sa.scale, stg);
+  } else {
+    depth_attn_block<bf16, 8, false, NT>(i - k, da.rows, da.H, 64, da.l, da.L, da.q, da.ldq,
+                                            da.kn, da.ldk, da.vn, da.ldv, da.kc, da.vc, da.out,
+                                            da.ldo, nullptr, nullptr, da.scale, da.window,
+                                            da.dilation);
   }
 }
 
@@ -1186,6 +1221,29 @@ int launch_attn_pair(int B, int S, int H, int l, int L, const void* q, const voi
   DaArgs da{rows, H, l, L, (const bf16*)dq, (const bf16*)dk, (const bf16*)dv, ldqkv, ldqkv,
             ldqkv, (bf16*)dkc, (bf16*)dvc, (bf16*)out_da, ldo, scale, window, dilation};
   dlaunch(attn_pair_kernel, (unsigned)(nsa + nda), 256, 0, st, sa, da, (int)nsa);
+  return 0;
+}
+
+int launch_attn_pair2(int B, int S, int H, int l, int L, const void* q, const void* k,
+                      const void* vt, const void* dq, const void* dk, const void* dv,
+                      int64_t ldqkv, void* dkc, void* dvc, void* out_sa, void* out_da,
+                      int64_t ldo, float scale, int window, int dilation, hipStream_t st) {
+  if (!attn_pair_ok(DT_BF16, B, S, H, 64, 0, vt) || S <= fa::BQ) return -1;
+  const int64_t nqb = (S + fa2::BQ - 1) / fa2::BQ;
+  const int64_t nsa = 8 * (((int64_t)B * H + 7) / 8) * nqb;  // the two-set flash grid
+  const int64_t rows = (int64_t)B * S;
+  const int64_t nda = (rows * H * 8 + 255) / 256;  // 8 lanes per head of 64
+  if (nsa + nda > 0x7fffffff) return -1;
+  SaFlashArgs sa{S, H, (const bf16*)q, ldqkv, (const bf16*)k, ldqkv, (const bf16*)vt,
+                 (bf16*)out_sa, ldo, scale};
+  DaArgs da{rows, H, l, L, (const bf16*)dq, (const bf16*)dk, (const bf16*)dv, ldqkv, ldqkv,
+            ldqkv, (bf16*)dkc, (bf16*)dvc, (bf16*)out_da, ldo, scale, window, dilation};
+  // nontemporal cache reads once the K and V caches exceed 256 MiB (as depth_attn)
+  const bool nt = 2 * rows * (int64_t)L * H * 64 * 2 > ((int64_t)256 << 20);
+  if (nt)
+    dlaunch(attn_pair2_kernel<true>, (unsigned)(nsa + nda), 256, 0, st, sa, da, B, nsa, nsa + nda);
+  else
+    dlaunch(attn_pair2_kernel<false>, (unsigned)(nsa + nda), 256, 0, st, sa, da, B, nsa, nsa + nda);
   return 0;
 }
 

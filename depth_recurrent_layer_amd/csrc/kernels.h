@@ -105,6 +105,12 @@ int launch_attn_pair(int B, int S, int H, int l, int L, const void* q, const voi
                      const void* vt, const void* dq, const void* dk, const void* dv,
                      int64_t ldqkv, void* dkc, void* dvc, void* out_sa, void* out_da,
                      int64_t ldo, float scale, int window, int dilation, hipStream_t st);
+// The same for query blocks of more than 64 rows (the two-set flash grid), the two kinds
+// of block interleaved in proportion in one launch; -1 when S <= 64 or unsupported.
+int launch_attn_pair2(int B, int S, int H, int l, int L, const void* q, const void* k,
+                      const void* vt, const void* dq, const void* dk, const void* dv,
+                      int64_t ldqkv, void* dkc, void* dvc, void* out_sa, void* out_da,
+                      int64_t ldo, float scale, int window, int dilation, hipStream_t st);
 
 // Router scores z [T, E] f32 = rho * RoPE_depth(x W_r^T) . keys.  bf16: u computed inside
 // (u ignored; needs r % 32 == 0, E % 16 == 0); f32: reads u = x W_r^T [T, r].

@@ -376,15 +376,22 @@ def test_layer_branch_streams_same_bits(gpu_lib, mixture, fuse_attn):
     assert np.array_equal(a["x_out"], b["x_out"]) and np.array_equal(a["idx"], b["idx"])
 
 
-@pytest.mark.parametrize("mixture,window,dilation", [("partial", 0, 0), ("parallel", 0, 0),
-                                                     ("partial", 2, 3)])
-def test_layer_paired_attention_same_bits(gpu_lib, mixture, window, dilation):
+@pytest.mark.parametrize("mixture,window,dilation,shape", [
+    ("partial", 0, 0, "one_round"), ("parallel", 0, 0, "one_round"),
+    ("partial", 2, 3, "one_round"),
+    # more flash blocks than the GPU holds at once (1024 of 64 queries, > 3 per CU on up
+    # to 341 CUs): the interleaved launch of the two-set flash grid; 2000 positions leave
+    # a ragged last query block, and 512 flash among 2512 blocks an uneven interleave
+    ("partial", 0, 0, "interleaved"), ("parallel", 2, 3, "interleaved")])
+def test_layer_paired_attention_same_bits(gpu_lib, mixture, window, dilation, shape):
     """SA and DA in one launch give the same bits as separate launches, and the paired
     launch is the one that runs (one per depth, no separate SA / DA launches)."""
     D = gpu_lib
-    cfg = CONFIGS["small"].replace(b=2, s=96, L=5, mixture=mixture, da_window=window,
+    b, s, L = (2, 96, 5) if shape == "one_round" else (4, 2000, 3)
+    cfg = CONFIGS["small"].replace(b=b, s=s, L=L, mixture=mixture, da_window=window,
                                    da_dilation=dilation)
-    print(f"layer paired attention {mixture} window {window} dilation {dilation}", flush=True)
+    print(f"layer paired attention {shape} {mixture} window {window} dilation {dilation}",
+          flush=True)
     W, x0 = make_weights(cfg), make_x0(cfg)
     a = run_gpu(D, cfg, W, x0, fuse_attn=False)
     counts = {}
