@@ -39,14 +39,21 @@ struct GemmCfg {
   static constexpr int STAGE = (BM + BN) * BKB;         // bytes per K slice
   static constexpr int NI = STAGE / 1024;               // 1 KiB load instructions per stage
   static constexpr int LPW = NI / NW;                   // per wave
-  // epilogue staging per wave: float32 rows of WN (+4), or bf16 rows of WN (+8)
+  // epilogue staging per wave: float32 rows of WN (+4), or bf16 rows of WN (+8); the
+  // float32 tile in EPASS passes of WM / EPASS rows when the whole tile of every wave
+  // would not fit the LDS
   static constexpr int LDF = WN + 4, LDB = WN + 8;
-  static constexpr int WAVE_STAGE = QKVONLY ? WM * LDB * 2 : WM * LDF * 4;
+  static constexpr int EPASS = QKVONLY || NW * WM * LDF * 4 + BM * 4 <= 160 * 1024 ? 1 : 2;
+  static constexpr int WAVE_STAGE = QKVONLY ? WM * LDB * 2 : WM / EPASS * LDF * 4;
+  // the float32 residual of the generic epilogue is fetched before the K loop only with
+  // at most two waves per SIMD (it holds 2 WM WN / 64 registers through the loop)
+  static constexpr bool PRE_RES = NW * OCC <= 8;
   static constexpr int SMEM = NS * STAGE > NW * WAVE_STAGE ? NS * STAGE : NW * WAVE_STAGE;
   static_assert(BKB == 64 || BKB == 128, "64- or 128-byte K slices");
   static_assert(NI % NW == 0, "stage must split evenly over the waves");
   static_assert(BM % RPI == 0, "A rows must fill whole load instructions");
   static_assert(NS >= 2 && SMEM <= 160 * 1024, "ring");
+  static_assert(TM % EPASS == 0, "epilogue passes of whole m-tiles");
 };
 
 DEV int gemm_swz(int bkb, int row, int c) {
@@ -153,8 +160,8 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_bf16_kernel(GemmArgs a
 #pragma unroll
       for (int v = 0; v < 4; ++v) t[i][v] = a.rope_s4[row_pos(i, v) * 16 + lr];
   };
-  float rres[QKV ? 1 : NIT][8];
-  if constexpr (QKV) {
+  float rres[QKV || !S::PRE_RES ? 1 : NIT][8];
+  if constexpr (QKV || !S::PRE_RES) {
   } else {
     if (a.resid) {
 #pragma unroll
@@ -295,45 +302,64 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_bf16_kernel(GemmArgs a
     }
   }
   if constexpr (QKVONLY) return;
-  // generic: v = acc * row_scale + resid; C (OutT) and optional bf16 copy C2
-  float* sf = reinterpret_cast<float*>(wst);  // [WM][LDF]
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) sf[(i * 16 + lg * 4 + v) * S::LDF + j * 16 + lr] = acc[i][j][v];
-  wave_lds_sync();
+  // generic: v = acc * row_scale + resid; C (OutT) and optional bf16 copy C2.  Pass p
+  // stages m-tiles p TM / EPASS .. and writes their rows (item m of the wave's tile is
+  // row (lane + 64 m) / CPR, chunk (lane + 64 m) % CPR).
+  constexpr int EP = S::EPASS, PTM = TM / EP, PNIT = NIT / EP;
+  static_assert(NIT % EP == 0 && PNIT * 64 / CPR == PTM * 16, "a pass holds whole rows");
+  float* sf = reinterpret_cast<float*>(wst);  // [WM / EPASS][LDF]
   bf16* C2 = (bf16*)a.C2;
 #pragma unroll
-  for (int m = 0; m < NIT; ++m) {
-    const int it = lane + 64 * m, rt = it / CPR, cc = it % CPR;
-    const int orow = rows_s[rw0 + rt];
-    const int n = cw0 + cc * 8;
-    if (orow < 0 || n >= a.N) continue;
-    const float sc = a.row_scale ? a.row_scale[orow] : 1.0f;
-    const floatx4 c0 = *reinterpret_cast<const floatx4*>(sf + rt * S::LDF + cc * 8);
-    const floatx4 c1 = *reinterpret_cast<const floatx4*>(sf + rt * S::LDF + cc * 8 + 4);
-    float val[8];
+  for (int p = 0; p < EP; ++p) {
+    if (p) wave_lds_sync();  // the previous pass's rows are read before they are replaced
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      val[e] = c0[e] * sc;
-      val[4 + e] = c1[e] * sc;
-    }
-    if constexpr (!QKV) {
-      if (a.resid) {
+    for (int i = 0; i < PTM; ++i)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) val[e] += rres[m][e];
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          sf[(i * 16 + lg * 4 + v) * S::LDF + j * 16 + lr] = acc[p * PTM + i][j][v];
+    wave_lds_sync();
+#pragma unroll
+    for (int mm = 0; mm < PNIT; ++mm) {
+      const int m = p * PNIT + mm;
+      const int it = lane + 64 * m, rt = it / CPR, cc = it % CPR;
+      const int rs = rt - p * PTM * 16;  // row in the staged pass
+      const int orow = rows_s[rw0 + rt];
+      const int n = cw0 + cc * 8;
+      if (orow < 0 || n >= a.N) continue;
+      const float sc = a.row_scale ? a.row_scale[orow] : 1.0f;
+      const floatx4 c0 = *reinterpret_cast<const floatx4*>(sf + rs * S::LDF + cc * 8);
+      const floatx4 c1 = *reinterpret_cast<const floatx4*>(sf + rs * S::LDF + cc * 8 + 4);
+      float val[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        val[e] = c0[e] * sc;
+        val[4 + e] = c1[e] * sc;
       }
+      if constexpr (!QKV) {
+        if (a.resid) {
+          if constexpr (S::PRE_RES) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) val[e] += rres[m][e];
+          } else {
+            float r[8];
+            load16(a.resid + (int64_t)orow * a.ldr + n, r);
+            load16(a.resid + (int64_t)orow * a.ldr + n + 4, r + 4);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) val[e] += r[e];
+          }
+        }
+      }
+      OutT* cp = C + (int64_t)orow * a.ldc + n;
+      if constexpr (sizeof(OutT) == 2) {
+        store16(cp, val);
+      } else {
+        store16(cp, val);
+        store16(cp + 4, val + 4);
+      }
+      if (C2) store16(C2 + (int64_t)orow * a.ldc2 + n, val);
     }
-    OutT* cp = C + (int64_t)orow * a.ldc + n;
-    if constexpr (sizeof(OutT) == 2) {
-      store16(cp, val);
-    } else {
-      store16(cp, val);
-      store16(cp + 4, val + 4);
-    }
-    if (C2) store16(C2 + (int64_t)orow * a.ldc2 + n, val);
   }
 }
 
@@ -410,6 +436,13 @@ int launch_gemm(const GemmArgs& a_in, int dtype, int out_f32, hipStream_t st) {
   // 128-column tiles).
   const int bn = a.N >= 128 ? 128 : 64;
   int bm = 64, bnn = bn;
+  // float32 output, at least one 256 x 256 tile per CU: those tiles, as the QKV
+  // projection (16 waves of 64 x 64, 128-byte slices on two stages; the epilogue in two
+  // passes of 32 rows, the residual read there)
+  if (out_f32 && !a.toff && k64 && a.N % 256 == 0 && tiles(256, 256) >= 256) {
+    dlaunch(gemm_bf16_kernel<float, GemmCfg<64, 64, 4, 4, 128, 2, 1, false>>, grid_of(256, 256), 1024, 0, st, a);
+    return 0;
+  }
   if (a.toff) {
     if (a.tile_m == 128 && bn == 128) bm = 128;
     else if (a.tile_m != 64) return -1;

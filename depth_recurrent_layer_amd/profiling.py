@@ -51,7 +51,7 @@ WORKLOAD_KERNELS = {
     },
     "deep": {
         "qkv_proj": "Li64ELi64ELi4ELi4ELi128ELi2ELi1ELb1",  # the 16-wave 256 x 256 instance
-        "out_proj": "GemmCfg<64, 64, 2, 2, 128, 2, 2, false>",
+        "out_proj": "GemmCfg<64, 64, 4, 4, 128, 2, 1, false>",  # float output, 256 x 256
         "seq_attn": "sa_flash2_kernel",    # two query sets per wave (separate launches)
         "depth_attn": "depth_attn_kernel",
         "attention": "attn_pair2_kernel",  # SA and DA blocks interleaved in one launch
