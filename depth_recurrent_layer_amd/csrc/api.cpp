@@ -7,6 +7,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -91,17 +92,18 @@ void timing_end(int kclass, hipStream_t st) {
 }  // namespace dreamer
 
 // compute units of the current device (cached per device)
-static int cu_count() {
-  static int cus[64] = {0};
+int dreamer::device_cus() {
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cus[dev]) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
+static int cu_count() { return dreamer::device_cus(); }
 
 #define TB(kc) timing_begin(kc, st)
 #define TE(kc) timing_end(kc, st)
@@ -532,6 +534,8 @@ struct LayerWs {
   int32_t *pcounts, *pgoff, *ptoff, *phist, *pperm;
   void *da_k, *da_v, *sa_ws, *vt;
   size_t sa_ws_bytes;
+  float* split_ws;  // decode: split-K partial products of the projections
+  int64_t split_elems;
 };
 
 static int64_t sa_npos(const dreamer_layer_cfg* c) { return c->decode ? c->sa_pos + 1 : c->s; }
@@ -595,6 +599,12 @@ static LayerWs plan_layer(Bump& b, const dreamer_layer_cfg* c, bool need_yb, boo
   const bool vt_ok = c->dtype == DREAMER_BF16 && !c->decode && c->d == 64 && c->s % 8 == 0 &&
                      c->proj_experts == 0;
   w.vt = vt_ok ? b.take((size_t)T * h * es) : nullptr;
+  // decode: the output projection of a few rows splits K over the CUs (up to 16 partial
+  // products [T, h])
+  if (c->decode && c->dtype == DREAMER_BF16) {
+    w.split_elems = 16 * T * h;
+    w.split_ws = b.take_n<float>((size_t)w.split_elems);
+  }
   w.sa_ws_bytes = seq_attn_ws(c->dtype, c->b, c->s, c->H, c->d, c->decode ? c->sa_pos : 0,
                               vt_ok ? 1 : 0);
   w.sa_ws = w.sa_ws_bytes ? b.take(w.sa_ws_bytes) : nullptr;
@@ -854,6 +864,8 @@ static int layer_run(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* 
       go.ldr = h;
       go.C2 = C2;
       go.ldc2 = h;
+      go.split_ws = lw.split_ws;
+      go.split_elems = lw.split_elems;
       if (c.proj_experts) {
         go.b_gstride = 2 * h * h;
         go.rows = lw.pperm;

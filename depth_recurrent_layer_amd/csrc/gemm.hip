@@ -90,8 +90,11 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_bf16_kernel(GemmArgs a
     m_end = a.M;
   }
   const int n0 = (a.n_fast ? blockIdx.x : blockIdx.y) * BN;
-  const bf16* __restrict__ A = (const bf16*)a.A;
-  const bf16* __restrict__ B = (const bf16*)a.B + (int64_t)g * a.b_gstride;
+  // split-K partial launch: block z takes K columns [z K, (z + 1) K) and writes partial
+  // product z (float32, [M, ldc]) of a stack of ksplit
+  const int64_t kz = a.ksplit > 1 ? (int64_t)blockIdx.z * a.K : 0;
+  const bf16* __restrict__ A = (const bf16*)a.A + kz;
+  const bf16* __restrict__ B = (const bf16*)a.B + (int64_t)g * a.b_gstride + kz;
   for (int i = tid; i < BM; i += S::NT) {
     const int m = m_begin + i;
     rows_s[i] = (m < m_end) ? (a.rows ? a.rows[m] : m) : -1;
@@ -223,7 +226,7 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_bf16_kernel(GemmArgs a
   __syncthreads();  // every wave is done with the ring; it becomes epilogue staging
 
   char* wst = ring + w * S::WAVE_STAGE;
-  OutT* C = (OutT*)a.C;
+  OutT* C = (OutT*)a.C + (a.ksplit > 1 ? (int64_t)blockIdx.z * a.M * a.ldc : 0);
   if constexpr (QKV) {
     if (a.qkv_h) {
       // the wave's 64 columns are one head of one section (qkv_h % 128 == 0, BN = 128)
@@ -389,6 +392,50 @@ __global__ void gemm_f32_kernel(GemmArgs a) {
   if (a.C2) ((float*)a.C2)[(int64_t)orow * a.ldc2 + n] = val;
 }
 
+// Split-K second pass, generic epilogue: out = (sum of the ksplit partials, in order) *
+// row_scale + resid; C (float32 or bf16) and optional bf16 copy C2.  One thread per 4
+// columns.
+template <typename OutT>
+__global__ void splitk_reduce_kernel(int M, int N, int ksplit, const float* __restrict__ part,
+                                     const float* __restrict__ row_scale,
+                                     const float* __restrict__ resid, int64_t ldr,
+                                     OutT* __restrict__ C, int64_t ldc, bf16* __restrict__ C2,
+                                     int64_t ldc2) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int nq = N / 4;
+  if (i >= (int64_t)M * nq) return;
+  const int m = (int)(i / nq), n = (int)(i % nq) * 4;
+  floatx4 v = *reinterpret_cast<const floatx4*>(part + (int64_t)m * N + n);
+  for (int z = 1; z < ksplit; ++z)
+    v += *reinterpret_cast<const floatx4*>(part + ((int64_t)z * M + m) * N + n);
+  const float sc = row_scale ? row_scale[m] : 1.0f;
+  float o[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = v[e] * sc + (resid ? resid[(int64_t)m * ldr + n + e] : 0.f);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) C[(int64_t)m * ldc + n + e] = (OutT)o[e];
+  if (C2) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) C2[(int64_t)m * ldc2 + n + e] = (bf16)o[e];
+  }
+}
+
+// Split count for a few-row dense launch with the generic epilogue: the number of
+// 64-element K slices per part stays whole, and the grid of 64 x 64 tiles reaches about
+// two blocks per CU.  (The QKV projection of the decode workload, 96 tiles of 64 x 128,
+// was measured no faster split.)
+static int choose_split(const GemmArgs& a) {
+  if (a.qkv_h || a.toff || a.rows || a.row_div != 1 || !a.split_ws || a.M > 64 || a.K % 64)
+    return 1;
+  const int64_t tiles = (a.N + 63) / 64;
+  const int64_t want = 2 * (int64_t)device_cus();
+  int sp = 1;
+  while (sp < 32 && tiles * sp < want && (a.K / 64) % (2 * sp) == 0 &&
+         (int64_t)2 * sp * a.M * a.N <= a.split_elems)
+    sp *= 2;
+  return sp;
+}
+
 int launch_gemm(const GemmArgs& a_in, int dtype, int out_f32, hipStream_t st) {
   GemmArgs a = a_in;
   a.n_fast = a.toff && a.N >= 16 * 128;  // grouped with many n-tiles: n fastest (see the kernel)
@@ -399,6 +446,33 @@ int launch_gemm(const GemmArgs& a_in, int dtype, int out_f32, hipStream_t st) {
     return 0;
   }
   if (a.K % 32 != 0 || a.N % 8 != 0) return -1;
+  if (dtype == DT_BF16 && a.ksplit == 1) {
+    const int sp = choose_split(a);
+    if (sp > 1) {  // partial products of K / sp columns each, then the epilogue pass
+      GemmArgs p = a;
+      p.K = a.K / sp;
+      p.ksplit = sp;
+      p.C = a.split_ws;
+      p.ldc = a.N;
+      p.resid = nullptr;
+      p.row_scale = nullptr;
+      p.C2 = nullptr;
+      p.qkv_h = 0;
+      dim3 grid((a.M + 63) / 64, (a.N + 63) / 64, sp);
+      dlaunch(gemm_bf16_kernel<float, GemmCfg<32, 32, 2, 2, 128, 4, 2, false>>, grid, 256, 0,
+              st, p);
+      const int64_t n = (int64_t)a.M * (a.N / 4);
+      if (out_f32)
+        dlaunch(splitk_reduce_kernel<float>, (unsigned)((n + 255) / 256), 256, 0, st, a.M, a.N,
+                sp, (const float*)a.split_ws, a.row_scale, a.resid, a.ldr, (float*)a.C, a.ldc,
+                (bf16*)a.C2, a.ldc2);
+      else
+        dlaunch(splitk_reduce_kernel<bf16>, (unsigned)((n + 255) / 256), 256, 0, st, a.M, a.N,
+                sp, (const float*)a.split_ws, a.row_scale, a.resid, a.ldr, (bf16*)a.C, a.ldc,
+                (bf16*)a.C2, a.ldc2);
+      return 0;
+    }
+  }
   const bool k64 = a.K % 64 == 0;  // 128-byte K slices
   auto tiles = [&](int tm, int tn) {
     return (int64_t)((a.M + tm - 1) / tm) * ((a.N + tn - 1) / tn);

@@ -50,10 +50,19 @@ struct GemmArgs {
   const float4* rope_s4 = nullptr;  // interleaved rotary tables (RopeJobs t4): sequence positions,
   const float4* rope_d4 = nullptr;  // and depths 0..depth_L-1
   void* vt = nullptr;
+  // Split-K for few rows (dense, no row gather, generic epilogue): float32 scratch of
+  // split_elems elements for partial products; launch_gemm splits K when the grid would
+  // leave CUs idle and the partials fit, and then sums them in a fixed order in a second
+  // pass that applies the epilogue.  ksplit: set by launch_gemm for the partial launch.
+  float* split_ws = nullptr;
+  int64_t split_elems = 0;
+  int ksplit = 1;
 };
 
 // out_f32: C is float32 (else storage dtype).  Returns -1 on an unsupported shape.
 int launch_gemm(const GemmArgs& a, int dtype, int out_f32, hipStream_t st);
+// Compute units of the current device (cached per device).
+int device_cus();
 
 // RoPE tables in float64 math: cos/sin [npos, D/2].
 void launch_rope_tables(int D, int npos, double base, float* c, float* s, hipStream_t st);
