@@ -182,8 +182,12 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_bf16_kernel(GemmArgs a
   const int nst = a.K / (BKB / 2);
   const uint32_t ring0 = lds_off(ring);
   for (int s = 0; s < S::NS - 1 && s < nst; ++s) issue(s);
+  // the depth-rotation entries too are fetched behind the first stages, with at most two
+  // waves per SIMD (with more, their registers would be held through the K loop by too
+  // many waves), else in the epilogue
+  constexpr bool PRE_DTAB = NW * S::OCC <= 8;
   if constexpr (QKV) {
-    if (da_qk) {
+    if (PRE_DTAB && da_qk) {
       td0 = a.rope_d4[a.depth_l * 16 + lr];
       td1 = a.rope_d4[(a.depth_L - 1 - a.depth_l) * 16 + lr];
       n_tab = 2;
@@ -229,6 +233,10 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_bf16_kernel(GemmArgs a
   OutT* C = (OutT*)a.C + (a.ksplit > 1 ? (int64_t)blockIdx.z * a.M * a.ldc : 0);
   if constexpr (QKV) {
     if (a.qkv_h) {
+      if (!PRE_DTAB && da_qk) {
+        td0 = a.rope_d4[a.depth_l * 16 + lr];
+        td1 = a.rope_d4[(a.depth_L - 1 - a.depth_l) * 16 + lr];
+      }
       // the wave's 64 columns are one head of one section (qkv_h % 128 == 0, BN = 128)
       const int hcol0 = cw0 % a.qkv_h;
       bf16* sw = reinterpret_cast<bf16*>(wst);  // [WM][LDB]
