@@ -111,9 +111,11 @@ def algorithmic_work(cfg, counts_per_depth, reps=1):
     da_bytes = sum(T * h * es * (6 + 2 * (n_depth_keys(l, cfg.da_window, cfg.da_dilation) - 1))
                    for l in range(L))
     w["depth_attn"] = dict(bound="hbm", bytes=da_bytes, launches=L)
-    # SA and DA in one launch: priced by its SA flops alone against the MFMA peak (a lower
-    # bound of its fraction: the DA share of the launch is not counted)
-    w["attention"] = dict(bound="mfma", flops=w["seq_attn"].get("flops", 0), launches=L)
+    # SA and DA in one launch: priced by its SA flops against the MFMA peak, and (reported
+    # beside it) by its DA bytes against the HBM peak; each is a lower bound of the
+    # launch's use of that resource
+    w["attention"] = dict(bound="mfma", flops=w["seq_attn"].get("flops", 0), launches=L,
+                          bytes=da_bytes)
     nw = 3 if cfg.ffn == "swiglu" else 2
     w["expert_ffn"] = dict(bound="hbm", bytes=L * 2 * T * k * h * es,
                            flops=L * 2 * T * k * nw * h * f, launches=L)
@@ -143,6 +145,9 @@ def class_report(work, per_class):
         if c in work and ("bytes" in work[c] or "flops" in work[c]):
             r = roofline_entry(work[c], ms / n)
             e.update(bound=r["bound"], achieved=r["achieved"], unit=r["unit"], frac=r["frac"])
+            if r["bound"] != "hbm" and "bytes" in work[c]:  # a launch that also streams HBM
+                hb = roofline_entry(dict(work[c], bound="hbm"), ms / n)
+                e.update(hbm_achieved=hb["achieved"], hbm_frac=hb["frac"])
         out[c] = e
     return out
 
