@@ -24,7 +24,8 @@ namespace dreamer {
 // Blocks per CU and the ring's LDS budget per block: narrow experts (f <= 64, 128-byte K
 // slices, 24 KiB stages) run three blocks per CU on a two-stage ring (measured faster at
 // the small workload's ~400 tiles than two blocks on three stages, and than 64-byte
-// slices on four stages); wider ones two blocks on 78 KiB.
+// slices on four stages); wider ones two blocks on 80 KiB, two stages of 128-byte slices
+// (whole cache lines: half the L2 requests of 64-byte slices for the same bytes).
 #ifndef DREAMER_FFN_NARROW_F
 #define DREAMER_FFN_NARROW_F 64
 #endif
@@ -34,8 +35,8 @@ struct FfnCfg {
   static constexpr int NW1 = KIND == FFN_SWIGLU ? 2 : 1;  // GEMM1 weight matrices
   static constexpr bool NARROW = F <= DREAMER_FFN_NARROW_F;
   static constexpr int OCC = NARROW ? 3 : 2;                       // blocks per CU
-  static constexpr int LDS = NARROW ? 52 * 1024 : 78 * 1024;       // ring budget per block
-  static constexpr int BKB = NARROW ? 128 : 64;           // bytes of a GEMM1 K slice row
+  static constexpr int LDS = NARROW ? 52 * 1024 : 80 * 1024;       // ring budget per block
+  static constexpr int BKB = 128;                         // bytes of a GEMM1 K slice row
   static constexpr int KSUB = BKB / 64;                   // 32-wide k-steps per slice
   static constexpr int CPR = BKB / 16, RPI = 64 / CPR;    // chunks per row, rows per load
   static constexpr int XB = 64 * BKB;                     // token rows of one slice
@@ -84,7 +85,6 @@ __global__ __launch_bounds__(256, (FfnCfg<F, KIND>::OCC)) void expert_ffn_kernel
   using S = FfnCfg<F, KIND>;
   constexpr int BKB = S::BKB, RB2 = S::RB2;
   __shared__ __attribute__((aligned(1024))) char stg[S::NS * S::STAGE];
-  __shared__ int s_slot[64];
 
   // Blocks reach the 8 XCDs round-robin; block b takes tile (b % 8) * per + b / 8, so each
   // XCD works through one contiguous range of tiles, where consecutive tiles mostly share
@@ -97,21 +97,31 @@ __global__ __launch_bounds__(256, (FfnCfg<F, KIND>::OCC)) void expert_ffn_kernel
   const int tile = (b & 7) * per + (b >> 3);
   const int tc = min(tile, tile_cap - 1);
   const int4 td = tiles[tc];
-  const int pslot = perm[tc * 64 + (tid & 63)];  // row tid (first wave)
+  // the tile's slot ids: the rows this lane gathers (GEMM1 instructions j < XROWS of the
+  // token section), then its output rows 16 tt + lr; pad rows (past nrows) are resolved
+  // below
+  constexpr int XROWS = (64 / S::RPI + 3) / 4;  // token-row instructions per wave (at most)
+  int xs[XROWS], sl[4];
+#pragma unroll
+  for (int j = 0; j < XROWS; ++j) xs[j] = perm[tc * 64 + min(63, (w + 4 * j) * S::RPI + lane / S::CPR)];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) sl[tt] = perm[tc * 64 + tt * 16 + lr];
+  int slot0 = perm[tc * 64];
   float gate[4];  // gates of this lane's output rows 16 tt + lr
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt) gate[tt] = pgate[tc * 64 + tt * 16 + lr];
   if ((b >> 3) >= per || tile >= n_tiles) return;
   const int e = td.x, nrows = min(64, td.z - td.y);
-  if (tid < 64) s_slot[tid] = tid < nrows ? pslot : -1;
-  // the gates are taken through an empty asm statement: the compiler waits for them here,
-  // before the ring starts, instead of draining the ring at their first use
+  // the slot ids and gates are taken through empty asm statements: the compiler waits for
+  // them here, before the ring starts, instead of draining the ring at their first use
 #pragma unroll
-  for (int tt = 0; tt < 4; ++tt) asm volatile("" : "+v"(gate[tt]));
-  __syncthreads();
-  int sl[4];  // output slot of row 16 tt + lr (-1: pad row)
+  for (int tt = 0; tt < 4; ++tt) {
+    asm volatile("" : "+v"(gate[tt]), "+v"(sl[tt]));
+    if (tt * 16 + lr >= nrows) sl[tt] = -1;  // pad row
+  }
 #pragma unroll
-  for (int tt = 0; tt < 4; ++tt) sl[tt] = s_slot[tt * 16 + lr];
+  for (int j = 0; j < XROWS; ++j) asm volatile("" : "+v"(xs[j]));
+  asm volatile("" : "+v"(slot0));
 
   // load descriptors: wave w issues instructions q = w + 4 j of every stage
   const bf16* src1[S::LPW1];  // GEMM1: token rows, then W1 (and W3) rows
@@ -120,7 +130,8 @@ __global__ __launch_bounds__(256, (FfnCfg<F, KIND>::OCC)) void expert_ffn_kernel
     const int q = w + 4 * j, slot = lane % S::CPR;
     const int row = q * S::RPI + lane / S::CPR;  // row of the stage
     if (row < 64) {
-      const int s = s_slot[row] >= 0 ? s_slot[row] : s_slot[0];  // pad rows repeat row 0
+      // (row < 64 only for j < XROWS; pad rows repeat row 0)
+      const int s = row < nrows ? xs[j < XROWS ? j : 0] : slot0;
       src1[j] = x + (int64_t)(s / k) * h_in + ffn_swz(BKB, row, slot) * 8;
     } else {
       const int hu = (row - 64) % F, m = (row - 64) / F;  // hidden unit, weight
