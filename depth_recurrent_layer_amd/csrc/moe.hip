@@ -2,6 +2,8 @@
 // and the shared-expert absorption helper.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -80,6 +82,25 @@ __global__ __launch_bounds__(1024) void combine_norm_kernel(
   float v[VEC];
   float ss = 0.f;
   if (act) {
+    // The slots in groups of 8, all loads of a group issued before the first sum (a loop
+    // over k waits for each load in turn), the first group before the residual; past k a
+    // load repeats the last slot and is not summed, so no load sits behind a branch.  The
+    // sums keep the order residual, slot 0, 1, ...
+    using RawV = typename std::conditional<sizeof(T) == 2, bf16x8, floatx4>::type;
+    auto load_group = [&](RawV (&raw)[8], int i0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        raw[i] = *reinterpret_cast<const RawV*>(slots + (t * k + min(i0 + i, k - 1)) * h + c);
+    };
+    auto add_group = [&](const RawV (&raw)[8], int i0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (i0 + i < k)
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) v[e] += (float)raw[i][e];
+    };
+    RawV raw[8];
+    if (k > 0) load_group(raw, 0);
     if (y) {
       load16(y + t * h + c, v);
       if constexpr (VEC == 8) load16(y + t * h + c + 4, v + 4);
@@ -87,11 +108,10 @@ __global__ __launch_bounds__(1024) void combine_norm_kernel(
 #pragma unroll
       for (int e = 0; e < VEC; ++e) v[e] = 0.f;
     }
-    for (int i = 0; i < k; ++i) {
-      float sv[VEC];
-      load16(slots + (t * k + i) * h + c, sv);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) v[e] += sv[e];
+    if (k > 0) add_group(raw, 0);
+    for (int i0 = 8; i0 < k; i0 += 8) {
+      load_group(raw, i0);
+      add_group(raw, i0);
     }
 #pragma unroll
     for (int e = 0; e < VEC; ++e) ss += v[e] * v[e];
