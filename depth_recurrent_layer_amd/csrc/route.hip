@@ -606,11 +606,12 @@ int router_route_fused(int64_t T, int h, int r, int E, int k, int l, int L, cons
 // ----------------------------------------------------------------------------- permute
 // Routed slots grouped by expert.  The slots are cut into chunks of PERM_CHUNK; kernel 1
 // counts each chunk's slots per expert in LDS (hist [nb, E]; in the layer the fused
-// router counts them instead, with global atomics, and kernel 1 is skipped);
-// kernel 2, one block per chunk, sums the hist columns before its chunk and in total,
-// scans the totals over experts (rows, and m-tiles of tile_m rows) and hands out its
-// slots' positions with LDS atomics.  Block 0 publishes counts, goff and toff.  Expert
-// ids outside [0, E) are clamped into range (memory safety only: they are caller errors).
+// router counts them instead, with global atomics, and kernel 1 is skipped); kernel 2
+// turns hist, in place, into each chunk's rows of every expert in earlier chunks and
+// writes the totals to counts; kernel 3, one block per chunk, scans the totals over
+// experts (rows, and m-tiles of tile_m rows) and hands out its slots' positions with LDS
+// atomics.  Block 0 of kernel 3 publishes goff and toff.  Expert ids outside [0, E) are
+// clamped into range (memory safety only: they are caller errors).
 __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -638,12 +639,49 @@ __global__ __launch_bounds__(512) void perm_hist_kernel(const int32_t* __restric
   for (int e = threadIdx.x; e < E; e += blockDim.x) out[e] = lh[e];
 }
 
+// Per expert (32 per block, one lane each in 8 groups of chunk rows): the exclusive
+// prefix of hist's column over the chunks, in place, and the column total into counts.
+// A group sums its run of rows, the runs' sums are scanned through LDS, then the group
+// rewrites its rows (the column is re-read from L2).
+__global__ __launch_bounds__(256) void perm_prefix_kernel(int32_t* __restrict__ hist, int nb,
+                                                          int E, int32_t* __restrict__ counts) {
+  __shared__ int part[8][32];
+  const int el = threadIdx.x & 31, grp = threadIdx.x >> 5;
+  const int e = blockIdx.x * 32 + el;
+  const int run = (nb + 7) / 8, q0 = grp * run, q1 = min(nb, q0 + run);
+  const int ec = min(e, E - 1);
+  int sum = 0;
+  for (int q = q0; q < q1; q += 8) {  // 8 loads in flight (clamped rows, unused dropped)
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = hist[(int64_t)min(q + u, q1 - 1) * E + ec];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sum += q + u < q1 ? v[u] : 0;
+  }
+  part[grp][el] = sum;
+  __syncthreads();
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    pre += g < grp ? part[g][el] : 0;
+    tot += part[g][el];
+  }
+  if (e >= E) return;
+  if (grp == 0) counts[e] = tot;
+  for (int q = q0; q < q1; ++q) {
+    int32_t* p = hist + (int64_t)q * E + e;
+    const int v = *p;
+    *p = pre;
+    pre += v;
+  }
+}
+
 // Expert offsets from the per-expert totals in base[E] (LDS): every thread owns a
 // contiguous range of experts; a wavefront scan (lane shuffles) plus one pass over the
 // wave totals gives each range its first row and first m-tile.  base[e] becomes e's
 // first row plus prev[e] (the rows of e in earlier chunks, or nullptr); with pub,
-// counts / goff / toff and the tile descriptors are written; with pad, prev[e] becomes
-// the shift from e's compact positions to its tile-padded ones.  s_wave: 32 ints.
+// goff / toff and the tile descriptors are written; with pad, prev[e] becomes the shift
+// from e's compact positions to its tile-padded ones.  s_wave: 32 ints.
 DEV void expert_offsets(int* base, int* prev, int E, int tile_m, bool pub, bool pad,
                         int32_t* __restrict__ counts, int32_t* __restrict__ goff,
                         int32_t* __restrict__ toff, int4* __restrict__ tiles, int* s_wave) {
@@ -681,7 +719,6 @@ DEV void expert_offsets(int* base, int* prev, int E, int tile_m, bool pub, bool 
   for (int e = e0; e < e1; ++e) {
     const int tot = base[e];
     if (pub) {
-      counts[e] = tot;
       goff[e] = rr;
       toff[e] = tt;
       if (tiles)  // one descriptor per m-tile: expert, first row, end of the expert's rows
@@ -700,8 +737,8 @@ DEV void expert_offsets(int* base, int* prev, int E, int tile_m, bool pub, bool 
 }
 
 // One block of PERM_THREADS per chunk: the chunk's experts and gates are loaded first
-// (their latency overlaps the histogram reads), then the totals and the rows of each
-// expert in earlier chunks, the offsets, and the scatter from registers.  pad: slot ids
+// (their latency overlaps the other reads), then the totals and the rows of each expert
+// in earlier chunks, the offsets, and the scatter from registers.  pad: slot ids
 // and gates go to tile-padded positions (m-tile t of the expert-major order owns
 // positions t * tile_m ..), the layout the expert FFN reads per tile.
 constexpr int PERM_THREADS = 512, PERM_PER = PERM_CHUNK / PERM_THREADS;
@@ -725,34 +762,10 @@ __global__ __launch_bounds__(PERM_THREADS) void perm_scatter_kernel(
     ex[j] = s < nslots ? min(max(idx[s], 0), E - 1) : -1;
     gv[j] = (pgate && s < nslots) ? gate[s] : 0.f;
   }
-  // column sums of hist over 4 experts per thread, 8 chunk rows at a time: 32 loads in
-  // flight (clamped addresses, unused values dropped)
-  for (int eb = 0; eb < E; eb += 4 * PERM_THREADS) {
-    int tot[4] = {0, 0, 0, 0}, pre[4] = {0, 0, 0, 0};
-    for (int q0 = 0; q0 < nb; q0 += 8) {
-      int v[4][8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          v[j][u] = hist[(int64_t)min(q0 + u, nb - 1) * E + min(eb + j * PERM_THREADS + tid, E - 1)];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int vv = q0 + u < nb ? v[j][u] : 0;
-          tot[j] += vv;
-          pre[j] += q0 + u < b ? vv : 0;
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = eb + j * PERM_THREADS + tid;
-      if (e < E) {
-        base[e] = tot[j];
-        prev[e] = pre[j];
-      }
-    }
+  // the totals and this chunk's row of earlier-chunk counts (hist after kernel 2)
+  for (int e = tid; e < E; e += PERM_THREADS) {
+    base[e] = counts[e];
+    prev[e] = hist[(int64_t)b * E + e];
   }
   __syncthreads();
   expert_offsets(base, prev, E, tile_m, b == 0, pad != 0, counts, goff, toff, tiles, s_wave);
@@ -791,6 +804,7 @@ int launch_permute(const int32_t* idx, int64_t nslots, int E, int tile_m, int32_
   const size_t lds = (size_t)E * sizeof(int);
   const int nb = perm_blocks(nslots);
   if (!hist_ready) dlaunch(perm_hist_kernel, nb, 512, lds, st, idx, nslots, E, hist);
+  dlaunch(perm_prefix_kernel, (E + 31) / 32, 256, 0, st, hist, nb, E, counts);
   dlaunch(perm_scatter_kernel, nb, PERM_THREADS, 2 * lds, st, idx, nslots, E, nb, tile_m, hist,
           counts, goff, toff, perm, gate, pgate, tiles, pad, zero_next);
   return 0;
