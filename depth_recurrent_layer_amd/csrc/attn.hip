@@ -72,7 +72,7 @@ DEV void rope_chunk(float* x, int c, int d, int pos_fwd, int pos_rev, const floa
     const int p = lo ? dim : dim - half;       // rotary pair index
     const int pos = p < quarter ? pos_fwd : pos_rev;
     const float cv = cs[pos * half + p], sv = sn[pos * half + p];
-    x[i] = lo ? x[i] * cv - other[i] * sv : x[i] * cv + other[i] * sv;
+    x[i] = lo ? rot_first(x[i], other[i], cv, sv) : rot_second(x[i], other[i], cv, sv);
   }
 }
 
@@ -1030,8 +1030,8 @@ __global__ __launch_bounds__(256) void sa_prep_kernel(int B, int S, int H, const
         const int pair = c * 8 + e;
         const float cv = cs[pos * 32 + pair], sv = sn[pos * 32 + pair];
         const float x = lo[e], y = hi[e];
-        lo[e] = x * cv - y * sv;
-        hi[e] = y * cv + x * sv;
+        lo[e] = rot_first(x, y, cv, sv);
+        hi[e] = rot_second(y, x, cv, sv);
       }
     }
     store16(dsts[s] + head * 64 + c * 8, lo);

@@ -159,6 +159,21 @@ DEV float block_sum(float v, float* red) {
 DEV float fast_exp(float x) { return __expf(x); }
 
 
+// Rotary pair (x, y) turned by (c, s): x' = x c - y s and y' = y c + x s, each computed
+// as one fused multiply-add whose addend is the other product rounded on its own.  Every
+// kernel that rotates uses these, so that the bits never depend on which product the
+// compiler would otherwise fuse.
+DEV float rot_first(float x, float y, float c, float s) {
+#pragma clang fp contract(off)
+  const float ys = y * s;
+  return __builtin_fmaf(x, c, -ys);
+}
+DEV float rot_second(float y, float x, float c, float s) {
+#pragma clang fp contract(off)
+  const float xs = x * s;
+  return __builtin_fmaf(y, c, xs);
+}
+
 DEV float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
 
 DEV float silu_(float x) { return x / (1.0f + expf(-x)); }
@@ -556,8 +571,13 @@ DEV void lds_read_b128_2x4(bf16x8 (&x)[8], uint32_t b0, uint32_t b1) {
 // LDS writes of this wave complete and ordered before its following LDS reads (for
 // exchanges between the lanes of one wave; lgkmcnt(0), then a scheduling barrier).
 DEV void wave_lds_sync() {
+  // the empty asm statements keep the compiler from moving memory accesses across: a
+  // lane's LDS read after the sync need not touch the addresses that lane wrote before
+  // it, so without them the compiler may read before the other lanes' writes
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
   __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // MFMA 16x16x32 bf16 -> f32 (gfx950).  Lane l holds A[row l%16][k 8(l/16)..+8],

@@ -267,8 +267,8 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_bf16_kernel(GemmArgs a
                 cv = j == 0 ? td0.x : td1.y;
                 sv = j == 0 ? td0.z : td1.w;
               }
-              const float xr = x * cv - y * sv;
-              y = y * cv + x * sv;
+              const float xr = rot_first(x, y, cv, sv);
+              y = rot_second(y, x, cv, sv);
               x = xr;
             }
             sw[rt * S::LDB + pair] = (bf16)x;

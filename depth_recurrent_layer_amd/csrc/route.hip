@@ -87,7 +87,7 @@ DEV void router_u_parts(int64_t Ttok, int64_t t0, int h, int r, int l, int L,
     const float* pt = part + (e / r) * rp;
     const float a = ((pt[i] + pt[16 * rp + i]) + pt[32 * rp + i]) + pt[48 * rp + i];
     const float b = ((pt[ip] + pt[16 * rp + ip]) + pt[32 * rp + ip]) + pt[48 * rp + ip];
-    ur[(e / r) * rp + i] = i < half ? a * cv - b * sv : a * cv + b * sv;
+    ur[(e / r) * rp + i] = i < half ? rot_first(a, b, cv, sv) : rot_second(a, b, cv, sv);
   }
   __syncthreads();
 #pragma unroll
@@ -323,7 +323,7 @@ __global__ void router_scores_f32_kernel(int64_t Ttok, int r, int E, int l, int 
     const int pos = p < quarter ? l : L - 1 - l;
     const float cv = cs[pos * half + p], sv = sn[pos * half + p];
     const float a = ut[i], b = ut[i < half ? i + half : i - half];
-    acc = fmaf(i < half ? a * cv - b * sv : a * cv + b * sv, ke[i], acc);
+    acc = fmaf(i < half ? rot_first(a, b, cv, sv) : rot_second(a, b, cv, sv), ke[i], acc);
   }
   z[gid] = rho * acc;
 }
