@@ -322,6 +322,28 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_bf16_kernel(GemmArgs a
   bf16* C2 = (bf16*)a.C2;
 #pragma unroll
   for (int p = 0; p < EP; ++p) {
+    // The pass's row scales and residuals are loaded first, every load issued before the
+    // first use (item by item, each would wait for its own); a row past the tile or a
+    // chunk past N reads row 0 / the last chunk and is not stored.
+    float scl[PNIT], rr[S::PRE_RES ? 1 : PNIT][8];
+#pragma unroll
+    for (int mm = 0; mm < PNIT; ++mm) {
+      const int it = lane + 64 * (p * PNIT + mm);
+      scl[mm] = 1.0f;
+      if (a.row_scale) scl[mm] = a.row_scale[max(rows_s[rw0 + it / CPR], 0)];
+    }
+    if constexpr (!QKV && !S::PRE_RES) {
+      if (a.resid) {
+#pragma unroll
+        for (int mm = 0; mm < PNIT; ++mm) {
+          const int it = lane + 64 * (p * PNIT + mm);
+          const int orow = max(rows_s[rw0 + it / CPR], 0);
+          const int n = max(0, min(cw0 + (it % CPR) * 8, a.N - 8));
+          load16(a.resid + (int64_t)orow * a.ldr + n, rr[mm]);
+          load16(a.resid + (int64_t)orow * a.ldr + n + 4, rr[mm] + 4);
+        }
+      }
+    }
     if (p) wave_lds_sync();  // the previous pass's rows are read before they are replaced
 #pragma unroll
     for (int i = 0; i < PTM; ++i)
@@ -331,45 +353,48 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_bf16_kernel(GemmArgs a
         for (int v = 0; v < 4; ++v)
           sf[(i * 16 + lg * 4 + v) * S::LDF + j * 16 + lr] = acc[p * PTM + i][j][v];
     wave_lds_sync();
+    // all of the pass's values first, then all of its stores: with the values of one item
+    // at a time the next item waits for the previous item's stores to read their registers
+    float val[PNIT][8];
 #pragma unroll
     for (int mm = 0; mm < PNIT; ++mm) {
       const int m = p * PNIT + mm;
       const int it = lane + 64 * m, rt = it / CPR, cc = it % CPR;
       const int rs = rt - p * PTM * 16;  // row in the staged pass
-      const int orow = rows_s[rw0 + rt];
-      const int n = cw0 + cc * 8;
-      if (orow < 0 || n >= a.N) continue;
-      const float sc = a.row_scale ? a.row_scale[orow] : 1.0f;
+      const float sc = scl[mm];
       const floatx4 c0 = *reinterpret_cast<const floatx4*>(sf + rs * S::LDF + cc * 8);
       const floatx4 c1 = *reinterpret_cast<const floatx4*>(sf + rs * S::LDF + cc * 8 + 4);
-      float val[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        val[e] = c0[e] * sc;
-        val[4 + e] = c1[e] * sc;
+        val[mm][e] = c0[e] * sc;
+        val[mm][4 + e] = c1[e] * sc;
       }
       if constexpr (!QKV) {
         if (a.resid) {
           if constexpr (S::PRE_RES) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) val[e] += rres[m][e];
+            for (int e = 0; e < 8; ++e) val[mm][e] += rres[m][e];
           } else {
-            float r[8];
-            load16(a.resid + (int64_t)orow * a.ldr + n, r);
-            load16(a.resid + (int64_t)orow * a.ldr + n + 4, r + 4);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) val[e] += r[e];
+            for (int e = 0; e < 8; ++e) val[mm][e] += rr[mm][e];
           }
         }
       }
+    }
+#pragma unroll
+    for (int mm = 0; mm < PNIT; ++mm) {
+      const int it = lane + 64 * (p * PNIT + mm), rt = it / CPR, cc = it % CPR;
+      const int orow = rows_s[rw0 + rt];
+      const int n = cw0 + cc * 8;
+      if (orow < 0 || n >= a.N) continue;
       OutT* cp = C + (int64_t)orow * a.ldc + n;
       if constexpr (sizeof(OutT) == 2) {
-        store16(cp, val);
+        store16(cp, val[mm]);
       } else {
-        store16(cp, val);
-        store16(cp + 4, val + 4);
+        store16(cp, val[mm]);
+        store16(cp + 4, val[mm] + 4);
       }
-      if (C2) store16(C2 + (int64_t)orow * a.ldc2 + n, val);
+      if (C2) store16(C2 + (int64_t)orow * a.ldc2 + n, val[mm]);
     }
   }
 }
