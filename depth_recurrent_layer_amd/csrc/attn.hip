@@ -380,10 +380,13 @@ __global__ __launch_bounds__(256) void sa_rope_store_kernel(
 }
 
 // ------------------------------------------------------- SA: row-streaming (any shape)
-// One block per (query row, key split).  Threads = chunks of the row (h / VEC of them).
-// Query (b, i) sits at position pos0 + i and sees keys 0..pos0+i of kbuf/vbuf
-// ([B, cap, H, d], already rotated).  Split s covers keys [s*span, (s+1)*span).
-// nsplit == 1: writes the normalised output; else (m, lsum, acc) partials.
+// One wave per (query row, key split, group of 64 chunks of the row): thread = chunk of the
+// row (h / VEC of them; a head's LPH chunks lie in one wave).  One-wave blocks spread the
+// work evenly over the CUs (a block per row and split left some CUs one block more than
+// others, all streaming at the per-CU load rate).  Query (b, i) sits at position pos0 + i
+// and sees keys 0..pos0+i of kbuf/vbuf ([B, cap, H, d], already rotated).  Split s covers
+// keys [s*span, (s+1)*span).  nsplit == 1: writes the normalised output; else (m, lsum,
+// acc) partials.
 template <typename T, int LPH>
 __global__ void sa_rows_kernel(int B, int n, int H, int d, int64_t pos0, const T* __restrict__ q,
                                int64_t ldq, const T* __restrict__ kb, const T* __restrict__ vb,
@@ -395,7 +398,7 @@ __global__ void sa_rows_kernel(int B, int n, int H, int d, int64_t pos0, const T
   const int h = H * d;
   const int split = blockIdx.x;
   const int64_t row = blockIdx.y;  // b * n + i
-  const int chunk = threadIdx.x, c = chunk % LPH, col = chunk * VEC;
+  const int chunk = blockIdx.z * blockDim.x + threadIdx.x, c = chunk % LPH, col = chunk * VEC;
   const int head = chunk / LPH;
   const int64_t b = row / n, i = row % n, qpos = pos0 + i;
   const int64_t k0 = (int64_t)split * span;
@@ -1096,11 +1099,11 @@ static int sa_rows(int lph, int B, int n, int H, int d, int64_t pos0, const void
                    int nsplit, int span, float* pa, float* pm, hipStream_t st) {
   constexpr int VEC = Vec16<T>::N;
   const int threads = H * d / VEC;
-  const int blk = ((threads + 63) / 64) * 64;
-  if (blk > 1024) return -1;
-  dim3 grid(nsplit, (unsigned)((int64_t)B * n));
+  constexpr int SRT = 64;  // threads per block
+  if (64 % lph) return -1;  // a head's chunks in one wave
+  dim3 grid(nsplit, (unsigned)((int64_t)B * n), (unsigned)((threads + SRT - 1) / SRT));
 #define SR_CASE(LP)                                                                    \
-  dlaunch(sa_rows_kernel<T, LP>, grid, blk, 0, st, B, n, H, d, pos0, (const T*)q, ldq,      \
+  dlaunch(sa_rows_kernel<T, LP>, grid, SRT, 0, st, B, n, H, d, pos0, (const T*)q, ldq,      \
                                               (const T*)kb, (const T*)vb, cap, (T*)out, \
                                               ldo, cs, sn, rope, scale, nsplit, span, pa, pm)
   switch (lph) {
