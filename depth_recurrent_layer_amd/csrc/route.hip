@@ -422,25 +422,33 @@ DEV void topk_row_insert(float& lv, float& lz, int& li, bool none, float cv, flo
   li = keep ? li : (pk ? ce : pi);
 }
 
+// One token per block: group G of wave w (the block's 16 groups of 16 lanes) scans range
+// 4 w + G of 16 equal expert ranges; each wave's group 0 merges its wave's groups, then
+// wave 0 takes in the other waves' lists from LDS (a token's scan spread over four
+// waves: few tokens, as in decode, still occupy as many CUs as they have tokens).
 __global__ __launch_bounds__(256) void router_topk16_kernel(
     int64_t Ttok, int E, int k, const float* __restrict__ z, const float* __restrict__ bias,
     int normalize, const int32_t* __restrict__ idx_in, int32_t* __restrict__ idx,
     float* __restrict__ gate) {
-  const int lane = threadIdx.x & 63, G = lane >> 4, g = lane & 15;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= Ttok) return;  // the whole wave
+  __shared__ float s_v[4][16], s_z[4][16];
+  __shared__ int s_i[4][16];
+  const int lane = threadIdx.x & 63, G = lane >> 4, g = lane & 15, w = threadIdx.x >> 6;
+  const int64_t t = blockIdx.x;
+  if (t >= Ttok) return;  // the whole block
   const float* zt = z + t * E;
   int my = 0;
   float myz = 0.f;
   if (idx_in) {
+    if (w != 0) return;
     if (lane < k) {
       my = min(max(idx_in[t * k + lane], 0), E - 1);
       myz = zt[my];
     }
   } else {
     constexpr int NQ = RCH / 16;
-    const int eq = (E + 63) / 64 * 16;  // quarter length (a multiple of 16)
-    const int e1 = min(E, (G + 1) * eq);
+    const int eq = (E + 255) / 256 * 16;  // range length (a multiple of 16)
+    const int GG = w * 4 + G;             // this group's range
+    const int e1 = min(E, (GG + 1) * eq);
     float lv = -INFINITY, lz = 0.f;
     int li = 0x7fffffff;
     float zn[NQ], bn[NQ];  // the next chunk's scores and biases (clamped reads)
@@ -452,8 +460,8 @@ __global__ __launch_bounds__(256) void router_topk16_kernel(
         bn[q] = bias[e];
       }
     };
-    load(G * eq);
-    for (int c0 = G * eq; c0 < (G + 1) * eq; c0 += RCH) {  // same trip count in every group
+    load(GG * eq);
+    for (int c0 = GG * eq; c0 < (GG + 1) * eq; c0 += RCH) {  // same trip count in every group
       float vr[NQ], zr[NQ];
       float lmax = -INFINITY;
       unsigned m = 0;
@@ -520,6 +528,21 @@ __global__ __launch_bounds__(256) void router_topk16_kernel(
       const int ce = __builtin_amdgcn_readlane(li, sl);
       topk_row_insert(lv, lz, li, G != 0, cv, cz, ce);
     }
+    // wave 0's group 0 takes in the other waves' lists that are not below its k-th best
+    if (lane < k) {
+      s_v[w][lane] = lv;
+      s_z[w][lane] = lz;
+      s_i[w][lane] = li;
+    }
+    __syncthreads();
+    if (w != 0) return;
+    const float tau1 = __shfl(lv, k - 1, 64);
+    for (int wo = 1; wo < 4; ++wo)
+      for (int j = 0; j < k; ++j) {  // the same in every lane
+        const float cv = s_v[wo][j];
+        if (!(cv >= tau1)) continue;
+        topk_row_insert(lv, lz, li, G != 0, cv, s_z[wo][j], s_i[wo][j]);
+      }
     my = min(max(li, 0), E - 1);  // lanes 0..k-1 (group 0) hold the selection in order
     myz = lz;
   }
@@ -568,7 +591,8 @@ int router_topk(int64_t T, int E, int k, const float* z, const float* bias, int 
 #define TK_CASE(KM)                                                                       \
   dlaunch(router_topk_kernel<KM>, grid, 256, 0, st, T, E, k, z, bias, normalize, idx_in, idx, gate)
   if (k <= 16)
-    dlaunch(router_topk16_kernel, grid, 256, 0, st, T, E, k, z, bias, normalize, idx_in, idx, gate);
+    dlaunch(router_topk16_kernel, (unsigned)T, 256, 0, st, T, E, k, z, bias, normalize, idx_in,
+            idx, gate);
   else
     TK_CASE(32);
 #undef TK_CASE
