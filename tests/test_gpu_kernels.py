@@ -177,6 +177,7 @@ def test_seq_attn_decode(gpu_lib, dt, B, P, H, d):
     ("bf16", 64, 256, 32, 32, 32, True, 0.2),      # k == E: every expert selected
     ("bf16", 120, 512, 64, 112, 16, True, 0.2),    # k = 16, a partial last expert quarter
     ("f32", 50, 64, 16, 100, 13, True, 0.1),       # E not a multiple of 16, odd k
+    ("bf16", 100, 512, 64, 8192, 8, True, 0.2),    # few tokens: two chunks per expert range
     # >= 1024 tokens: scores and selection in one kernel (ragged last block of 16 tokens)
     ("bf16", 1037, 512, 64, 256, 4, True, 0.2),
     ("bf16", 1030, 1024, 128, 1024, 8, True, 0.2),  # four chunks of 256 experts
@@ -227,7 +228,8 @@ def test_expert_route(gpu_lib, dt, T, h, r, E, k, norm, bias):
 
 
 @pytest.mark.parametrize("T,E,tied", [(40, 16, (3, 7, 9)), (1040, 16, (3, 7, 9)),
-                                       (40, 256, (5, 70, 200)), (1040, 512, (5, 300, 260))])
+                                       (40, 256, (5, 70, 200)), (1040, 512, (5, 300, 260)),
+                                       (40, 1024, (700, 5, 300))])
 def test_expert_route_ties_go_to_lower_index(gpu_lib, T, E, tied):
     """Identical experts (same key, same bias) in one or in different expert chunks or
     quarters of the selection: they win in index order."""
