@@ -473,7 +473,7 @@ __global__ __launch_bounds__(256) void router_topk16_kernel(
         lmax = fmaxf(lmax, vr[q]);
         m |= (in ? 1u : 0u) << q;
       }
-      if (c0 + RCH < (G + 1) * eq) load(c0 + RCH);
+      if (c0 + RCH < (GG + 1) * eq) load(c0 + RCH);
       float tau = __shfl(lv, k - 1, 16), cut = -INFINITY;
       for (int j = 0; j < k; ++j) {
         cut = group_max16(lmax);
