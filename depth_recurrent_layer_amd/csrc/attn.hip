@@ -134,8 +134,8 @@ DEV void depth_attn_block(
     m = group_sum<LPH>(s) * scale;
   }
   // NB_ slots per batch (two batches in flight).  Two (eight 16-byte loads in flight) was
-  // measured faster than four at the deep workload in DA's own launch, most at the first
-  // depths, where a batch of four mostly re-reads clamped slots.
+  // measured faster than four in DA's own launch (8192 rows of 32 heads, 64 depths), most
+  // at the first depths, where a batch of four mostly re-reads clamped slots.
   constexpr int NB = NB_;
   // One batch of NB slots from raw 16-byte chunks: scores, one max and rescale for the
   // batch, then the weighted values (slots j >= l, or outside the key set, are skipped).
@@ -951,21 +951,25 @@ __global__ __launch_bounds__(256, 3) void attn_pair_kernel(SaFlashArgs sa, DaArg
 }
 
 // SA (the two-set flash grid) and DA of one depth in one launch, the two kinds of block
-// interleaved in proportion: block i is flash block k = floor(i nsa / n) when
-// floor((i + 1) nsa / n) > k, else DA block i - k.  The dispatcher hands each freed slot
-// to the next block, so every CU keeps running both kinds (matrix-core and VALU work
-// beside HBM streaming) and the two finish together; in separate launches on two streams
-// SA's blocks hold all registers of the CUs they occupy and the two split the CUs.  Flash
-// block k is item (k % 8, k / 8): a fixed XCD per (batch, head) pair whenever the flash
-// blocks' spacing is constant (n / nsa an odd integer), as at the deep workload.  The DA
-// blocks batch their slots as DA's own launch does (the same bits).
+// interleaved over the first m blocks: block i < m is flash block k = floor(i nsa / m)
+// when floor((i + 1) nsa / m) > k, else DA block i - k; the blocks from m on are DA's.
+// The dispatcher hands each freed slot to the next block, so every CU keeps running both
+// kinds (matrix-core and VALU work beside HBM streaming); in separate launches on two
+// streams SA's blocks hold all registers of the CUs they occupy and the two split the
+// CUs.  The launcher takes m = nsa + 3/5 of the DA blocks: the flash blocks, much longer
+// than DA's, then all start early, so that the launch ends on DA blocks (measured with
+// b = 2, s = 4096, 32 heads of 64, over 64 depths: 507 us per launch, against 536 with the
+// flash blocks spread over the whole grid and 563 with all of them first).  Flash block k
+// is item (k % 8, k / 8); spacings m / nsa that are not integers spread a (batch, head)
+// pair's blocks over the XCDs, which was faster there than keeping them on one.  The DA blocks batch their slots as DA's own
+// launch does (the same bits).
 template <bool NT>
 __global__ __launch_bounds__(256, 3) void attn_pair2_kernel(SaFlashArgs sa, DaArgs da, int B,
-                                                            int64_t nsa, int64_t n) {
+                                                            int64_t nsa, int64_t m) {
   __shared__ __attribute__((aligned(1024))) char stg[fa::NSTG][2 * fa::TILE];
   const int64_t i = blockIdx.x;
-  const int64_t k = i * nsa / n;
-  if ((i + 1) * nsa / n > k) {
+  const int64_t k = i < m ? i * nsa / m : nsa;
+  if (i < m && (i + 1) * nsa / m > k) {
     sa_flash2_block((int)(k & 7), (int)(k >> 3), B, sa.S, sa.H, sa.q, sa.ldq, sa.kk, sa.ldk,
                     sa.vt, sa.out, sa.ldo, sa.scale, stg);
   } else {
@@ -1243,10 +1247,11 @@ int launch_attn_pair2(int B, int S, int H, int l, int L, const void* q, const vo
             ldqkv, (bf16*)dkc, (bf16*)dvc, (bf16*)out_da, ldo, scale, window, dilation};
   // nontemporal cache reads once the K and V caches exceed 256 MiB (as depth_attn)
   const bool nt = 2 * rows * (int64_t)L * H * 64 * 2 > ((int64_t)256 << 20);
+  const int64_t m = nsa + nda * 3 / 5;  // the flash blocks lie among the first m
   if (nt)
-    dlaunch(attn_pair2_kernel<true>, (unsigned)(nsa + nda), 256, 0, st, sa, da, B, nsa, nsa + nda);
+    dlaunch(attn_pair2_kernel<true>, (unsigned)(nsa + nda), 256, 0, st, sa, da, B, nsa, m);
   else
-    dlaunch(attn_pair2_kernel<false>, (unsigned)(nsa + nda), 256, 0, st, sa, da, B, nsa, nsa + nda);
+    dlaunch(attn_pair2_kernel<false>, (unsigned)(nsa + nda), 256, 0, st, sa, da, B, nsa, m);
   return 0;
 }
 

@@ -22,9 +22,8 @@
 namespace dreamer {
 
 // Blocks per CU and the ring's LDS budget per block: narrow experts (f <= 64, 128-byte K
-// slices, 24 KiB stages) run three blocks per CU on a two-stage ring (measured faster at
-// the small workload's ~400 tiles than two blocks on three stages, and than 64-byte
-// slices on four stages); wider ones two blocks on 80 KiB, two stages of 128-byte slices
+// slices, 24 KiB stages) run three blocks per CU on a two-stage ring (measured faster over
+// ~400 tiles than two blocks on three stages, and than 64-byte slices on four stages); wider ones two blocks on 80 KiB, two stages of 128-byte slices
 // (whole cache lines: half the L2 requests of 64-byte slices for the same bytes).
 #ifndef DREAMER_FFN_NARROW_F
 #define DREAMER_FFN_NARROW_F 64

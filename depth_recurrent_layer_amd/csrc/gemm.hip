@@ -455,8 +455,8 @@ __global__ void splitk_reduce_kernel(int M, int N, int ksplit, const float* __re
 
 // Split count for a few-row dense launch with the generic epilogue: the number of
 // 64-element K slices per part stays whole, and the grid of 64 x 64 tiles reaches about
-// two blocks per CU.  (The QKV projection of the decode workload, 96 tiles of 64 x 128,
-// was measured no faster split.)
+// two blocks per CU.  (A 64-row QKV projection, 96 tiles of 64 x 128, was measured no
+// faster split.)
 static int choose_split(const GemmArgs& a) {
   if (a.qkv_h || a.toff || a.rows || a.row_div != 1 || !a.split_ws || a.M > 64 || a.K % 64)
     return 1;
