@@ -213,6 +213,10 @@ DEV void wait_vmcnt_upto(int n) { wait_vmcnt_range<0, 63>(n < 0 ? 0 : n > 63 ? 6
 DEV void store_b64_counted(void* p, bf16x4 v) {
   asm volatile("global_store_dwordx2 %0, %1, off" : : "v"(p), "v"(v) : "memory");
 }
+// The 16-byte form (global_store_dwordx4), same conventions.
+DEV void store_b128_counted(void* p, bf16x8 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off" : : "v"(p), "v"(v) : "memory");
+}
 
 // 8-byte LDS write that the compiler does not see as an LDS access: a plain store into
 // a ring that direct global->LDS loads still fill would first wait for all of them

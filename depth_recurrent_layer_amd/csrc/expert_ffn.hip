@@ -12,7 +12,9 @@
 // LDS once (64 x F bf16, in the ring stage GEMM1 has just finished with) and every wave
 // keeps all of it in registers as GEMM2's B operand.  In GEMM2, O^T = W2 H^T, wave w owns
 // a quarter of each stage's output columns for all token rows; every lane holds 4
-// consecutive gate-scaled outputs of one slot and stores them as 8 bytes.
+// consecutive gate-scaled outputs of one slot per column tile, and with two column tiles
+// per wave, neighbouring lanes trade one tile each so that every lane stores 8
+// consecutive outputs as 16 bytes.
 //
 // Slices are XOR-swizzled by row in 16-byte chunks so that the 16 rows one fragment
 // read touches fall into distinct banks.
@@ -164,9 +166,10 @@ __global__ __launch_bounds__(256, (FfnCfg<F, KIND>::OCC)) void expert_ffn_kernel
 
   // Stage s has landed once at most the operations issued after its loads are
   // outstanding: the loads of stages s+1 .. s+NS-2 and the output stores of the GEMM2
-  // iterations from the one that issued stage s on (CT store instructions per token
-  // tile that holds a slot row, per iteration; the same count in every wave).
-  const int nst_w = S::CT * ((nrows + 15) / 16);
+  // iterations from the one that issued stage s on (per iteration one store instruction
+  // per token tile that holds a slot row, or CT of them with one column tile per wave;
+  // the same count in every wave).
+  const int nst_w = (S::CT == 2 ? 1 : S::CT) * ((nrows + 15) / 16);
   auto wait_stage = [&](int s) {
     int later = 0;
     for (int t = s + 1; t < s + S::NS - 1 && t < ntot; ++t) later += t < n1 ? S::LPW1 : S::LPW2;
@@ -289,7 +292,30 @@ __global__ __launch_bounds__(256, (FfnCfg<F, KIND>::OCC)) void expert_ffn_kernel
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
       if (tt * 16 < nrows) {  // uniform; row 16 tt is a slot row, so some lanes store
-        if (sl[tt] >= 0) {
+        if constexpr (S::CT == 2) {
+          // Lane (lr, lg) holds columns 4 lg .. 4 lg + 3 of both column tiles (c = 0: the
+          // wave's columns 0..15, c = 1: 16..31).  Lanes lg and lg ^ 1 swap one tile each,
+          // so that an even lg holds columns 4 lg .. 4 lg + 7 and an odd lg columns
+          // 16 + 4 (lg - 1) .. + 7: every lane stores 16 bytes and the four lanes of a row
+          // write its 64 bytes with one instruction (8-byte stores split them in two).
+          bf16x4 v0, v1;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v0[i] = (bf16)(acc[0][tt][i] * gate[tt]);
+            v1[i] = (bf16)(acc[1][tt][i] * gate[tt]);
+          }
+          const bool even = (lg & 1) == 0;
+          const uint2 snd = __builtin_bit_cast(uint2, even ? v1 : v0);
+          uint2 rcv;
+          rcv.x = (uint32_t)__shfl_xor((int)snd.x, 16, 64);
+          rcv.y = (uint32_t)__shfl_xor((int)snd.y, 16, 64);
+          const bf16x4 vr = __builtin_bit_cast(bf16x4, rcv);
+          const bf16x4 lo = even ? v0 : vr, hi = even ? vr : v1;
+          const bf16x8 v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          if (sl[tt] >= 0)
+            store_b128_counted(slots + (int64_t)sl[tt] * h_out + nc + w * 32 +
+                                   (even ? lg * 4 : 16 + (lg - 1) * 4), v8);
+        } else if (sl[tt] >= 0) {
           bf16* orow = slots + (int64_t)sl[tt] * h_out + nc + w * S::CT * 16 + lg * 4;
 #pragma unroll
           for (int c = 0; c < S::CT; ++c) {
