@@ -94,11 +94,15 @@ def kernel_stats_md(csv_path: str, title: str, command: str, top: int = 16) -> s
     return "\n".join(out) + "\n"
 
 
-def launch_stats_md(trace_csv: str, title: str, command: str, top: int = 24) -> str:
+def launch_stats_md(trace_csv: str, title: str, command: str, top: int = 24,
+                    only: str | None = None) -> str:
     """Per (kernel, grid) durations from a kernel trace: one kernel launched with several
-    shapes (the projections of the different wirings, say) gets one row per shape."""
+    shapes (the projections of the different wirings, say) gets one row per shape.
+    only: keep the kernels whose name contains it (shares are then of their total)."""
     groups = {}
     for r in csv.DictReader(open(trace_csv)):
+        if only and only not in r["Kernel_Name"]:
+            continue
         grid = (f"{int(r['Grid_Size_X']) // max(1, int(r['Workgroup_Size_X']))}x"
                 f"{int(r['Grid_Size_Y']) // max(1, int(r['Workgroup_Size_Y']))}"
                 f"x{int(r['Workgroup_Size_X'])}")
@@ -107,7 +111,8 @@ def launch_stats_md(trace_csv: str, title: str, command: str, top: int = 24) -> 
     total = sum(sum(v) for v in groups.values())
     rows = sorted(groups.items(), key=lambda kv: -sum(kv[1]))[:top]
     out = [f"# {title}", "", "Command (repository root, one MI355X):", "", "```", command, "```",
-           "", "Durations per kernel and launch shape (blocks x, blocks y, threads per block).",
+           "", "Durations per kernel and launch shape (blocks x, blocks y, threads per block)" +
+           (f"; only kernels named `{only}`, shares of their total." if only else "."),
            "", "| kernel | shape | calls | total us | avg us | min us | max us | % |",
            "|---|---|---|---|---|---|---|---|"]
     for (name, grid), d in rows:
@@ -208,6 +213,9 @@ if __name__ == "__main__":
         sys.stdout.write(kernel_stats_md(sys.argv[2], sys.argv[3], sys.argv[4]))
     elif mode == "launches":
         sys.stdout.write(launch_stats_md(sys.argv[2], sys.argv[3], sys.argv[4]))
+    elif mode == "lib-launches":  # the library's own kernels only (names in dreamer::)
+        sys.stdout.write(launch_stats_md(sys.argv[2], sys.argv[3], sys.argv[4], top=64,
+                                         only="dreamer"))
     elif mode == "traffic":
         s = traffic_summary(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6],
                             sys.argv[7], float(sys.argv[8]), " ".join(sys.argv[9:]))
