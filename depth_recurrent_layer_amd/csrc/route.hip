@@ -805,6 +805,51 @@ __global__ __launch_bounds__(PERM_THREADS) void perm_scatter_kernel(
       zero_next[i] = 0;
 }
 
+// The whole permutation in one block when the slots fit one chunk (nslots <= PERM_CHUNK,
+// e.g. a decode step's few tokens): the chunk's histogram in LDS, the offsets, the
+// scatter, and (zero_next) the clearing of the router's other histogram buffer.  The
+// same outputs as the three-kernel path (rows of one expert in some order; every row's
+// result is independent of its place in the group).
+__global__ __launch_bounds__(PERM_THREADS) void perm_single_kernel(
+    const int32_t* __restrict__ idx, int64_t nslots, int E, int tile_m,
+    int32_t* __restrict__ counts, int32_t* __restrict__ goff, int32_t* __restrict__ toff,
+    int32_t* __restrict__ perm, const float* __restrict__ gate, float* __restrict__ pgate,
+    int4* __restrict__ tiles, int pad, int32_t* __restrict__ zero_next) {
+  extern __shared__ int sh[];  // base [E] (totals, then cursors), prev [E]
+  int* base = sh;
+  int* prev = sh + E;
+  __shared__ int s_wave[32];
+  const int tid = threadIdx.x;
+  int ex[PERM_PER];
+  float gv[PERM_PER];
+#pragma unroll
+  for (int j = 0; j < PERM_PER; ++j) {
+    const int64_t s = j * PERM_THREADS + tid;
+    ex[j] = s < nslots ? min(max(idx[s], 0), E - 1) : -1;
+    gv[j] = (pgate && s < nslots) ? gate[s] : 0.f;
+  }
+  for (int e = tid; e < E; e += PERM_THREADS) {
+    base[e] = 0;
+    prev[e] = 0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < PERM_PER; ++j)
+    if (ex[j] >= 0) atomicAdd(&base[ex[j]], 1);
+  __syncthreads();
+  for (int e = tid; e < E; e += PERM_THREADS) counts[e] = base[e];
+  expert_offsets(base, prev, E, tile_m, true, pad != 0, counts, goff, toff, tiles, s_wave);
+#pragma unroll
+  for (int j = 0; j < PERM_PER; ++j)
+    if (ex[j] >= 0) {
+      const int pos = atomicAdd(&base[ex[j]], 1) + (pad ? prev[ex[j]] : 0);
+      perm[pos] = (int32_t)(j * PERM_THREADS + tid);
+      if (pgate) pgate[pos] = gv[j];
+    }
+  if (zero_next)
+    for (int e = tid; e < E; e += PERM_THREADS) zero_next[e] = 0;
+}
+
 __global__ void hist_colsum_kernel(const int32_t* __restrict__ hist, int nb, int E,
                                    int32_t* __restrict__ counts) {
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
@@ -827,6 +872,11 @@ int launch_permute(const int32_t* idx, int64_t nslots, int E, int tile_m, int32_
   if (E <= 0 || E > PERM_MAX_E) return -1;
   const size_t lds = (size_t)E * sizeof(int);
   const int nb = perm_blocks(nslots);
+  if (nb == 1) {  // one chunk: one launch (a counted histogram, if any, is not needed)
+    dlaunch(perm_single_kernel, 1, PERM_THREADS, 2 * lds, st, idx, nslots, E, tile_m, counts,
+            goff, toff, perm, gate, pgate, tiles, pad, zero_next);
+    return 0;
+  }
   if (!hist_ready) dlaunch(perm_hist_kernel, nb, 512, lds, st, idx, nslots, E, hist);
   dlaunch(perm_prefix_kernel, (E + 31) / 32, 256, 0, st, hist, nb, E, counts);
   dlaunch(perm_scatter_kernel, nb, PERM_THREADS, 2 * lds, st, idx, nslots, E, nb, tile_m, hist,
