@@ -847,15 +847,20 @@ DEV void sa_flash2_block(int xcd, int j, int B, int S, int H, const bf16* __rest
 #pragma unroll
         for (int i = 0; i < 4; ++i) lmax[s] = fmaxf(lmax[s], sacc[s][t][i]);
     }
+    bool need = false;
 #pragma unroll
-    for (int s = 0; s < QS; ++s) {
-      if (__any(lmax[s] > m[s] + lazy_thr)) {
-        const float mn = fmaxf(m[s], max_xor32(max_xor16(lmax[s])));
-        const float corr = __builtin_amdgcn_exp2f((m[s] - mn) * sl2);
-        m[s] = mn;
-        osum[s] *= corr;
+    for (int s = 0; s < QS; ++s) need = need || lmax[s] > m[s] + lazy_thr;
+    if (__any(need)) {  // rare: one branch for both sets keeps the common path straight
 #pragma unroll
-        for (int t = 0; t < 4; ++t) o[s][t] *= corr;
+      for (int s = 0; s < QS; ++s) {
+        if (__any(lmax[s] > m[s] + lazy_thr)) {
+          const float mn = fmaxf(m[s], max_xor32(max_xor16(lmax[s])));
+          const float corr = __builtin_amdgcn_exp2f((m[s] - mn) * sl2);
+          m[s] = mn;
+          osum[s] *= corr;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) o[s][t] *= corr;
+        }
       }
     }
 #pragma unroll
