@@ -815,6 +815,8 @@ static int layer_run(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* 
         gq.rope_s4 = lw.rope_s4;
         gq.rope_d4 = lw.rope_d4;
         gq.vt = lw.vt;
+        // the paired attention launches read SA v transposed only
+        gq.vt_only = pair_attn || pair2_attn;
       }
       TB(DREAMER_KC_GEMM);
       int r2 = launch_gemm(gq, dt, 0, st);

@@ -277,8 +277,9 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_bf16_kernel(GemmArgs a
         }
       }
       wave_lds_sync();
-      // rows of 64 bf16 = 8 chunks of 16 bytes
-      for (int it = lane; it < WM * 8; it += 64) {
+      // rows of 64 bf16 = 8 chunks of 16 bytes (SA v with vt_only: the transposed copy only)
+      const bool plain = !(sect == 2 && a.vt && a.vt_only);
+      for (int it = plain ? lane : WM * 8; it < WM * 8; it += 64) {
         const int rt = it >> 3, ch = it & 7;
         const int orow = rows_s[rw0 + rt];
         if (orow < 0) continue;

@@ -50,6 +50,7 @@ struct GemmArgs {
   const float4* rope_s4 = nullptr;  // interleaved rotary tables (RopeJobs t4): sequence positions,
   const float4* rope_d4 = nullptr;  // and depths 0..depth_L-1
   void* vt = nullptr;
+  int vt_only = 0;                   // with vt: SA v only transposed (its plain rows unread)
   // Split-K for few rows (dense, no row gather, generic epilogue): float32 scratch of
   // split_elems elements for partial products; launch_gemm splits K when the grid would
   // leave CUs idle and the partials fit, and then sums them in a fixed order in a second
