@@ -758,6 +758,11 @@ static int layer_run(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* 
       if (rc) return fail(DREAMER_E_UNSUPPORTED, "layer: projection permutation");
     }
     const bool last = l == L - 1;
+    // bf16: DA's k / v of this depth are written by the QKV projection straight into the
+    // cache's slot l (rows L h apart), where DA reads them with the older slots
+    const bool kv_bf = dt == DREAMER_BF16 && c.use_da;
+    void* dak_l = kv_bf ? (char*)DAk + (size_t)l * h * es : nullptr;
+    void* dav_l = kv_bf ? (char*)DAv + (size_t)l * h * es : nullptr;
     // the storage copy of y feeds the router (PARTIAL, SERIAL); the fully parallel wiring's
     // router reads xh, so no copy of y is stored there
     void* y_out = y_steps ? (char*)y_steps + (size_t)l * T * h * es : nullptr;
@@ -817,6 +822,10 @@ static int layer_run(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* 
         gq.vt = lw.vt;
         // the paired attention launches read SA v transposed only
         gq.vt_only = pair_attn || pair2_attn;
+        // DA k / v go straight into the cache's slot l, where DA reads them
+        gq.da_k = dak_l;
+        gq.da_v = dav_l;
+        gq.da_ld = (int64_t)L * h;
       }
       TB(DREAMER_KC_GEMM);
       int r2 = launch_gemm(gq, dt, 0, st);
@@ -843,7 +852,9 @@ static int layer_run(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* 
     auto run_da = [&](hipStream_t s_) -> int {
       timing_begin(DREAMER_KC_DEPTH_ATTN, s_);
       int r2 = launch_depth_attn(dt, T, c.H, c.d, l, L, qkv + 3 * h * es, 6 * h,
-                                 qkv + 4 * h * es, 6 * h, qkv + 5 * h * es, 6 * h, DAk, DAv,
+                                 kv_bf ? dak_l : qkv + 4 * h * es, kv_bf ? (int64_t)L * h : 6 * h,
+                                 kv_bf ? dav_l : qkv + 5 * h * es, kv_bf ? (int64_t)L * h : 6 * h,
+                                 DAk, DAv,
                                  att + h * es, 2 * h, lw.cos_d, lw.sin_d, scale, 0, s_,
                                  c.da_window, c.da_dilation);
       timing_end(DREAMER_KC_DEPTH_ATTN, s_);  // s_: the stream DA runs on
@@ -905,7 +916,7 @@ static int layer_run(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* 
       if (pair_attn) {
         TB(DREAMER_KC_ATTN);
         int r2 = launch_attn_pair(c.b, c.s, c.H, l, L, qkv, qkv + h * es, lw.vt,
-                                  qkv + 3 * h * es, qkv + 4 * h * es, qkv + 5 * h * es, 6 * h,
+                                  qkv + 3 * h * es, dak_l, dav_l, 6 * h, (int64_t)L * h,
                                   DAk, DAv, att, att + h * es, 2 * h, scale, c.da_window,
                                   c.da_dilation, st);
         TE(DREAMER_KC_ATTN);
@@ -913,7 +924,7 @@ static int layer_run(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* 
       } else if (pair2_attn) {
         TB(DREAMER_KC_ATTN);
         int r2 = launch_attn_pair2(c.b, c.s, c.H, l, L, qkv, qkv + h * es, lw.vt,
-                                   qkv + 3 * h * es, qkv + 4 * h * es, qkv + 5 * h * es, 6 * h,
+                                   qkv + 3 * h * es, dak_l, dav_l, 6 * h, (int64_t)L * h,
                                    DAk, DAv, att, att + h * es, 2 * h, scale, c.da_window,
                                    c.da_dilation, st);
         TE(DREAMER_KC_ATTN);

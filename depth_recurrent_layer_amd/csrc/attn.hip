@@ -117,8 +117,10 @@ DEV void depth_attn_block(
   }
   T* krow = kc + row * (int64_t)L * h + col;
   T* vrow = vc + row * (int64_t)L * h + col;
-  store16(krow + (int64_t)l * h, kv);
-  store16(vrow + (int64_t)l * h, vv);
+  // k_new / v_new may already be the cache's slot l (the layer's projection writes them
+  // there); then they are not stored again
+  if (ROPE || kn + row * ldk + col != krow + (int64_t)l * h) store16(krow + (int64_t)l * h, kv);
+  if (vn + row * ldv + col != vrow + (int64_t)l * h) store16(vrow + (int64_t)l * h, vv);
 
   // The current slot first (from registers), so the running max starts finite; then the
   // older slots in batches of NB whose loads are issued together (the key test is the
@@ -1220,7 +1222,7 @@ bool attn_pair_ok(int dtype, int B, int q_len, int H, int d, int64_t pos0, const
 
 int launch_attn_pair(int B, int S, int H, int l, int L, const void* q, const void* k,
                      const void* vt, const void* dq, const void* dk, const void* dv,
-                     int64_t ldqkv, void* dkc, void* dvc, void* out_sa, void* out_da,
+                     int64_t ldqkv, int64_t ldkv, void* dkc, void* dvc, void* out_sa, void* out_da,
                      int64_t ldo, float scale, int window, int dilation, hipStream_t st) {
   if (!attn_pair_ok(DT_BF16, B, S, H, 64, 0, vt)) return -1;
   const int nqb = (S + fa::BQ - 1) / fa::BQ;
@@ -1230,15 +1232,15 @@ int launch_attn_pair(int B, int S, int H, int l, int L, const void* q, const voi
   if (nsa + nda > 0x7fffffff) return -1;
   SaFlashArgs sa{S, H, (const bf16*)q, ldqkv, (const bf16*)k, ldqkv, (const bf16*)vt,
                  (bf16*)out_sa, ldo, scale};
-  DaArgs da{rows, H, l, L, (const bf16*)dq, (const bf16*)dk, (const bf16*)dv, ldqkv, ldqkv,
-            ldqkv, (bf16*)dkc, (bf16*)dvc, (bf16*)out_da, ldo, scale, window, dilation};
+  DaArgs da{rows, H, l, L, (const bf16*)dq, (const bf16*)dk, (const bf16*)dv, ldqkv, ldkv,
+            ldkv, (bf16*)dkc, (bf16*)dvc, (bf16*)out_da, ldo, scale, window, dilation};
   dlaunch(attn_pair_kernel, (unsigned)(nsa + nda), 256, 0, st, sa, da, (int)nsa);
   return 0;
 }
 
 int launch_attn_pair2(int B, int S, int H, int l, int L, const void* q, const void* k,
                       const void* vt, const void* dq, const void* dk, const void* dv,
-                      int64_t ldqkv, void* dkc, void* dvc, void* out_sa, void* out_da,
+                      int64_t ldqkv, int64_t ldkv, void* dkc, void* dvc, void* out_sa, void* out_da,
                       int64_t ldo, float scale, int window, int dilation, hipStream_t st) {
   if (!attn_pair_ok(DT_BF16, B, S, H, 64, 0, vt) || S <= fa::BQ) return -1;
   const int64_t nqb = (S + fa2::BQ - 1) / fa2::BQ;
@@ -1248,8 +1250,8 @@ int launch_attn_pair2(int B, int S, int H, int l, int L, const void* q, const vo
   if (nsa + nda > 0x7fffffff) return -1;
   SaFlashArgs sa{S, H, (const bf16*)q, ldqkv, (const bf16*)k, ldqkv, (const bf16*)vt,
                  (bf16*)out_sa, ldo, scale};
-  DaArgs da{rows, H, l, L, (const bf16*)dq, (const bf16*)dk, (const bf16*)dv, ldqkv, ldqkv,
-            ldqkv, (bf16*)dkc, (bf16*)dvc, (bf16*)out_da, ldo, scale, window, dilation};
+  DaArgs da{rows, H, l, L, (const bf16*)dq, (const bf16*)dk, (const bf16*)dv, ldqkv, ldkv,
+            ldkv, (bf16*)dkc, (bf16*)dvc, (bf16*)out_da, ldo, scale, window, dilation};
   // nontemporal cache reads once the K and V caches exceed 256 MiB (as depth_attn)
   const bool nt = 2 * rows * (int64_t)L * H * 64 * 2 > ((int64_t)256 << 20);
   const int64_t m = nsa + nda * 3 / 5;  // the flash blocks lie among the first m

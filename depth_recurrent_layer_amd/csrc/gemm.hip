@@ -279,11 +279,18 @@ __global__ __launch_bounds__(CFG::NT, CFG::OCC) void gemm_bf16_kernel(GemmArgs a
       wave_lds_sync();
       // rows of 64 bf16 = 8 chunks of 16 bytes (SA v with vt_only: the transposed copy only)
       const bool plain = !(sect == 2 && a.vt && a.vt_only);
+      // DA k / v straight into the depth-attention cache's slot when given
+      bf16* dst = C + cw0;
+      int64_t ldd = a.ldc;
+      if ((sect == 4 || sect == 5) && a.da_k) {
+        dst = (bf16*)(sect == 4 ? a.da_k : a.da_v) + hcol0;
+        ldd = a.da_ld;
+      }
       for (int it = plain ? lane : WM * 8; it < WM * 8; it += 64) {
         const int rt = it >> 3, ch = it & 7;
         const int orow = rows_s[rw0 + rt];
         if (orow < 0) continue;
-        *reinterpret_cast<bf16x8*>(C + (int64_t)orow * a.ldc + cw0 + ch * 8) =
+        *reinterpret_cast<bf16x8*>(dst + (int64_t)orow * ldd + ch * 8) =
             *reinterpret_cast<const bf16x8*>(sw + rt * S::LDB + ch * 8);
       }
       if (sect == 2 && a.vt) {  // SA v, transposed: item = (dim, 8 consecutive rows)

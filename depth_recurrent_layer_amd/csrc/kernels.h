@@ -51,6 +51,11 @@ struct GemmArgs {
   const float4* rope_d4 = nullptr;  // and depths 0..depth_L-1
   void* vt = nullptr;
   int vt_only = 0;                   // with vt: SA v only transposed (its plain rows unread)
+  // optional: DA k and v (sections 4 and 5) written to these rows instead (row stride
+  // da_ld; the depth-attention cache's current slot) and not into C
+  void* da_k = nullptr;
+  void* da_v = nullptr;
+  int64_t da_ld = 0;
   // Split-K for few rows (dense, no row gather, generic epilogue): float32 scratch of
   // split_elems elements for partial products; launch_gemm splits K when the grid would
   // leave CUs idle and the partials fit, and then sums them in a fixed order in a second
@@ -113,13 +118,13 @@ int launch_seq_attn(int dtype, int B, int q_len, int H, int d, int64_t pos0, con
 bool attn_pair_ok(int dtype, int B, int q_len, int H, int d, int64_t pos0, const void* vt);
 int launch_attn_pair(int B, int S, int H, int l, int L, const void* q, const void* k,
                      const void* vt, const void* dq, const void* dk, const void* dv,
-                     int64_t ldqkv, void* dkc, void* dvc, void* out_sa, void* out_da,
+                     int64_t ldqkv, int64_t ldkv, void* dkc, void* dvc, void* out_sa, void* out_da,
                      int64_t ldo, float scale, int window, int dilation, hipStream_t st);
 // The same for query blocks of more than 64 rows (the two-set flash grid), the two kinds
 // of block interleaved in proportion in one launch; -1 when S <= 64 or unsupported.
 int launch_attn_pair2(int B, int S, int H, int l, int L, const void* q, const void* k,
                       const void* vt, const void* dq, const void* dk, const void* dv,
-                      int64_t ldqkv, void* dkc, void* dvc, void* out_sa, void* out_da,
+                      int64_t ldqkv, int64_t ldkv, void* dkc, void* dvc, void* out_sa, void* out_da,
                       int64_t ldo, float scale, int window, int dilation, hipStream_t st);
 
 // Router scores z [T, E] f32 = rho * RoPE_depth(x W_r^T) . keys.  bf16: u computed inside
