@@ -738,6 +738,11 @@ static int layer_run(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* 
     launch_fill_i32(lw.ffn.hist, (int64_t)std::max(1, perm_blocks(T * k)) * c.E, 0, st);
   char* qkv = (char*)lw.qkv;
   char* att = (char*)lw.att;
+  // The DA cache: the caller's [T, L, H, d] when given; the layer's own is slot-major
+  // [L, T, h], so that a depth's slot is one contiguous block (the projection writes it
+  // whole) -- the same values and the same DA reads either way.
+  const int64_t da_srow = da_k ? (int64_t)L * h : (int64_t)h;
+  const int64_t da_sslot = da_k ? (int64_t)h : (int64_t)T * h;
 
   for (int l = 0; l < L; ++l) {
     int32_t* pidx = nullptr;
@@ -759,10 +764,10 @@ static int layer_run(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* 
     }
     const bool last = l == L - 1;
     // bf16: DA's k / v of this depth are written by the QKV projection straight into the
-    // cache's slot l (rows L h apart), where DA reads them with the older slots
+    // cache's slot l, where DA reads them with the older slots
     const bool kv_bf = dt == DREAMER_BF16 && c.use_da;
-    void* dak_l = kv_bf ? (char*)DAk + (size_t)l * h * es : nullptr;
-    void* dav_l = kv_bf ? (char*)DAv + (size_t)l * h * es : nullptr;
+    void* dak_l = kv_bf ? (char*)DAk + (size_t)l * da_sslot * es : nullptr;
+    void* dav_l = kv_bf ? (char*)DAv + (size_t)l * da_sslot * es : nullptr;
     // the storage copy of y feeds the router (PARTIAL, SERIAL); the fully parallel wiring's
     // router reads xh, so no copy of y is stored there
     void* y_out = y_steps ? (char*)y_steps + (size_t)l * T * h * es : nullptr;
@@ -825,7 +830,7 @@ static int layer_run(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* 
         // DA k / v go straight into the cache's slot l, where DA reads them
         gq.da_k = dak_l;
         gq.da_v = dav_l;
-        gq.da_ld = (int64_t)L * h;
+        gq.da_ld = da_srow;
       }
       TB(DREAMER_KC_GEMM);
       int r2 = launch_gemm(gq, dt, 0, st);
@@ -852,11 +857,11 @@ static int layer_run(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* 
     auto run_da = [&](hipStream_t s_) -> int {
       timing_begin(DREAMER_KC_DEPTH_ATTN, s_);
       int r2 = launch_depth_attn(dt, T, c.H, c.d, l, L, qkv + 3 * h * es, 6 * h,
-                                 kv_bf ? dak_l : qkv + 4 * h * es, kv_bf ? (int64_t)L * h : 6 * h,
-                                 kv_bf ? dav_l : qkv + 5 * h * es, kv_bf ? (int64_t)L * h : 6 * h,
+                                 kv_bf ? dak_l : qkv + 4 * h * es, kv_bf ? da_srow : 6 * h,
+                                 kv_bf ? dav_l : qkv + 5 * h * es, kv_bf ? da_srow : 6 * h,
                                  DAk, DAv,
                                  att + h * es, 2 * h, lw.cos_d, lw.sin_d, scale, 0, s_,
-                                 c.da_window, c.da_dilation);
+                                 c.da_window, c.da_dilation, da_srow, da_sslot);
       timing_end(DREAMER_KC_DEPTH_ATTN, s_);  // s_: the stream DA runs on
       return r2 ? fail(DREAMER_E_UNSUPPORTED, "layer: depth attention shape") : ok();
     };
@@ -916,7 +921,8 @@ static int layer_run(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* 
       if (pair_attn) {
         TB(DREAMER_KC_ATTN);
         int r2 = launch_attn_pair(c.b, c.s, c.H, l, L, qkv, qkv + h * es, lw.vt,
-                                  qkv + 3 * h * es, dak_l, dav_l, 6 * h, (int64_t)L * h,
+                                  qkv + 3 * h * es, dak_l, dav_l, 6 * h, da_srow, da_srow,
+                                  da_sslot,
                                   DAk, DAv, att, att + h * es, 2 * h, scale, c.da_window,
                                   c.da_dilation, st);
         TE(DREAMER_KC_ATTN);
@@ -924,7 +930,8 @@ static int layer_run(const dreamer_layer_cfg* cfg, const dreamer_layer_weights* 
       } else if (pair2_attn) {
         TB(DREAMER_KC_ATTN);
         int r2 = launch_attn_pair2(c.b, c.s, c.H, l, L, qkv, qkv + h * es, lw.vt,
-                                   qkv + 3 * h * es, dak_l, dav_l, 6 * h, (int64_t)L * h,
+                                   qkv + 3 * h * es, dak_l, dav_l, 6 * h, da_srow, da_srow,
+                                   da_sslot,
                                    DAk, DAv, att, att + h * es, 2 * h, scale, c.da_window,
                                    c.da_dilation, st);
         TE(DREAMER_KC_ATTN);

@@ -91,7 +91,7 @@ DEV void depth_attn_block(
     int64_t ldq, const T* __restrict__ kn, int64_t ldk, const T* __restrict__ vn, int64_t ldv,
     T* __restrict__ kc, T* __restrict__ vc, T* __restrict__ out, int64_t ldo,
     const float* __restrict__ cosd, const float* __restrict__ sind, float scale, int window,
-    int dilation) {
+    int dilation, int64_t srow, int64_t sslot) {
   constexpr int VEC = Vec16<T>::N;
   const int h = H * d;
   const int cpr = h / VEC;  // chunks per row
@@ -115,12 +115,14 @@ DEV void depth_attn_block(
       kv[i] = round_to<T>(kv[i]);
     }
   }
-  T* krow = kc + row * (int64_t)L * h + col;
-  T* vrow = vc + row * (int64_t)L * h + col;
+  // the cache: row `row`'s slot j at kc + row srow + j sslot ([rows, L, h]: srow = L h,
+  // sslot = h; slot-major [L, rows, h]: srow = h, sslot = rows h)
+  T* krow = kc + row * srow + col;
+  T* vrow = vc + row * srow + col;
   // k_new / v_new may already be the cache's slot l (the layer's projection writes them
   // there); then they are not stored again
-  if (ROPE || kn + row * ldk + col != krow + (int64_t)l * h) store16(krow + (int64_t)l * h, kv);
-  if (vn + row * ldv + col != vrow + (int64_t)l * h) store16(vrow + (int64_t)l * h, vv);
+  if (ROPE || kn + row * ldk + col != krow + (int64_t)l * sslot) store16(krow + (int64_t)l * sslot, kv);
+  if (vn + row * ldv + col != vrow + (int64_t)l * sslot) store16(vrow + (int64_t)l * sslot, vv);
 
   // The current slot first (from registers), so the running max starts finite; then the
   // older slots in batches of NB whose loads are issued together (the key test is the
@@ -192,8 +194,8 @@ DEV void depth_attn_block(
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const int64_t jc = min(j0 + b, l - 1);
-        const raw16* kp = reinterpret_cast<const raw16*>(krow + jc * h);
-        const raw16* vp = reinterpret_cast<const raw16*>(vrow + jc * h);
+        const raw16* kp = reinterpret_cast<const raw16*>(krow + jc * sslot);
+        const raw16* vp = reinterpret_cast<const raw16*>(vrow + jc * sslot);
         if constexpr (NT) {  // a cache far larger than the caches: stream it past them
           kr[b] = __builtin_nontemporal_load(kp);
           vr[b] = __builtin_nontemporal_load(vp);
@@ -220,8 +222,8 @@ DEV void depth_attn_block(
       for (int b = 0; b < NB; ++b) {
         const int j = j0 + b;
         if (j < l && !(l - j >= window && (dilation <= 0 || (l - j) % dilation))) {
-          kr[b] = *reinterpret_cast<const raw16*>(krow + (int64_t)j * h);
-          vr[b] = *reinterpret_cast<const raw16*>(vrow + (int64_t)j * h);
+          kr[b] = *reinterpret_cast<const raw16*>(krow + (int64_t)j * sslot);
+          vr[b] = *reinterpret_cast<const raw16*>(vrow + (int64_t)j * sslot);
         }
       }
       batch(j0, kr, vr);
@@ -239,17 +241,21 @@ __global__ __launch_bounds__(256) void depth_attn_kernel(
     const T* __restrict__ kn, int64_t ldk, const T* __restrict__ vn, int64_t ldv,
     T* __restrict__ kc, T* __restrict__ vc, T* __restrict__ out, int64_t ldo,
     const float* __restrict__ cosd, const float* __restrict__ sind, float scale, int window,
-    int dilation) {
+    int dilation, int64_t srow, int64_t sslot) {
   depth_attn_block<T, LPH, ROPE, NT>(blockIdx.x, rows, H, d, l, L, q, ldq, kn, ldk, vn, ldv, kc, vc,
-                                 out, ldo, cosd, sind, scale, window, dilation);
+                                 out, ldo, cosd, sind, scale, window, dilation, srow, sslot);
 }
 
 int launch_depth_attn(int dtype, int64_t rows, int H, int d, int l, int L, const void* q,
                       int64_t ldq, const void* kn, int64_t ldk, const void* vn, int64_t ldv,
                       void* kc, void* vc, void* out, int64_t ldo, const float* cosd,
                       const float* sind, float scale, int rope, hipStream_t st, int window,
-                      int dilation) {
+                      int dilation, int64_t srow, int64_t sslot) {
   const int vec = dtype == DT_BF16 ? 8 : 4;
+  if (srow <= 0) {  // [rows, L, h]
+    srow = (int64_t)L * H * d;
+    sslot = (int64_t)H * d;
+  }
   const int lph = d / vec;
   const int64_t threads = rows * (int64_t)(H * d / vec);
   if (threads <= 0) return 0;
@@ -260,10 +266,10 @@ int launch_depth_attn(int dtype, int64_t rows, int H, int d, int l, int L, const
 #define DA_LAUNCH(T, LP, R)                                                              \
   if (nt) dlaunch(depth_attn_kernel<T, LP, R, true>, grid, 256, 0, st,                        \
       rows, H, d, l, L, (const T*)q, ldq, (const T*)kn, ldk, (const T*)vn, ldv, (T*)kc, \
-      (T*)vc, (T*)out, ldo, cosd, sind, scale, window, dilation);                         \
+      (T*)vc, (T*)out, ldo, cosd, sind, scale, window, dilation, srow, sslot);             \
   else dlaunch(depth_attn_kernel<T, LP, R, false>, grid, 256, 0, st,                          \
       rows, H, d, l, L, (const T*)q, ldq, (const T*)kn, ldk, (const T*)vn, ldv, (T*)kc, \
-      (T*)vc, (T*)out, ldo, cosd, sind, scale, window, dilation)
+      (T*)vc, (T*)out, ldo, cosd, sind, scale, window, dilation, srow, sslot)
 #define DA_CASE(T, LP)                 \
   if (rope) DA_LAUNCH(T, LP, true);    \
   else DA_LAUNCH(T, LP, false);        \
@@ -941,6 +947,7 @@ struct DaArgs {
   int64_t ldo;
   float scale;
   int window, dilation;
+  int64_t srow, sslot;  // cache strides (see depth_attn_block)
 };
 
 __global__ __launch_bounds__(256, 3) void attn_pair_kernel(SaFlashArgs sa, DaArgs da, int nsa) {
@@ -953,7 +960,7 @@ __global__ __launch_bounds__(256, 3) void attn_pair_kernel(SaFlashArgs sa, DaArg
   } else {
     depth_attn_block<bf16, 8, false>(bi - nsa, da.rows, da.H, 64, da.l, da.L, da.q, da.ldq, da.kn,
                                      da.ldk, da.vn, da.ldv, da.kc, da.vc, da.out, da.ldo, nullptr,
-                                     nullptr, da.scale, da.window, da.dilation);
+                                     nullptr, da.scale, da.window, da.dilation, da.srow, da.sslot);
   }
 }
 
@@ -983,7 +990,7 @@ __global__ __launch_bounds__(256, 3) void attn_pair2_kernel(SaFlashArgs sa, DaAr
     depth_attn_block<bf16, 8, false, NT>(i - k, da.rows, da.H, 64, da.l, da.L, da.q, da.ldq,
                                             da.kn, da.ldk, da.vn, da.ldv, da.kc, da.vc, da.out,
                                             da.ldo, nullptr, nullptr, da.scale, da.window,
-                                            da.dilation);
+                                            da.dilation, da.srow, da.sslot);
   }
 }
 
@@ -1222,7 +1229,7 @@ bool attn_pair_ok(int dtype, int B, int q_len, int H, int d, int64_t pos0, const
 
 int launch_attn_pair(int B, int S, int H, int l, int L, const void* q, const void* k,
                      const void* vt, const void* dq, const void* dk, const void* dv,
-                     int64_t ldqkv, int64_t ldkv, void* dkc, void* dvc, void* out_sa, void* out_da,
+                     int64_t ldqkv, int64_t ldkv, int64_t srow, int64_t sslot, void* dkc, void* dvc, void* out_sa, void* out_da,
                      int64_t ldo, float scale, int window, int dilation, hipStream_t st) {
   if (!attn_pair_ok(DT_BF16, B, S, H, 64, 0, vt)) return -1;
   const int nqb = (S + fa::BQ - 1) / fa::BQ;
@@ -1233,14 +1240,15 @@ int launch_attn_pair(int B, int S, int H, int l, int L, const void* q, const voi
   SaFlashArgs sa{S, H, (const bf16*)q, ldqkv, (const bf16*)k, ldqkv, (const bf16*)vt,
                  (bf16*)out_sa, ldo, scale};
   DaArgs da{rows, H, l, L, (const bf16*)dq, (const bf16*)dk, (const bf16*)dv, ldqkv, ldkv,
-            ldkv, (bf16*)dkc, (bf16*)dvc, (bf16*)out_da, ldo, scale, window, dilation};
+            ldkv, (bf16*)dkc, (bf16*)dvc, (bf16*)out_da, ldo, scale, window, dilation,
+            srow, sslot};
   dlaunch(attn_pair_kernel, (unsigned)(nsa + nda), 256, 0, st, sa, da, (int)nsa);
   return 0;
 }
 
 int launch_attn_pair2(int B, int S, int H, int l, int L, const void* q, const void* k,
                       const void* vt, const void* dq, const void* dk, const void* dv,
-                      int64_t ldqkv, int64_t ldkv, void* dkc, void* dvc, void* out_sa, void* out_da,
+                      int64_t ldqkv, int64_t ldkv, int64_t srow, int64_t sslot, void* dkc, void* dvc, void* out_sa, void* out_da,
                       int64_t ldo, float scale, int window, int dilation, hipStream_t st) {
   if (!attn_pair_ok(DT_BF16, B, S, H, 64, 0, vt) || S <= fa::BQ) return -1;
   const int64_t nqb = (S + fa2::BQ - 1) / fa2::BQ;
@@ -1251,7 +1259,8 @@ int launch_attn_pair2(int B, int S, int H, int l, int L, const void* q, const vo
   SaFlashArgs sa{S, H, (const bf16*)q, ldqkv, (const bf16*)k, ldqkv, (const bf16*)vt,
                  (bf16*)out_sa, ldo, scale};
   DaArgs da{rows, H, l, L, (const bf16*)dq, (const bf16*)dk, (const bf16*)dv, ldqkv, ldkv,
-            ldkv, (bf16*)dkc, (bf16*)dvc, (bf16*)out_da, ldo, scale, window, dilation};
+            ldkv, (bf16*)dkc, (bf16*)dvc, (bf16*)out_da, ldo, scale, window, dilation,
+            srow, sslot};
   // nontemporal cache reads once the K and V caches exceed 256 MiB (as depth_attn)
   const bool nt = 2 * rows * (int64_t)L * H * 64 * 2 > ((int64_t)256 << 20);
   const int64_t m = nsa + nda * 3 / 5;  // the flash blocks lie among the first m

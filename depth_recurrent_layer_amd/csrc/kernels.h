@@ -89,13 +89,14 @@ struct RopeJobs {
 };
 void launch_rope_jobs(const RopeJobs& jobs, hipStream_t st);
 
-// Depth attention (row strides in elements for q/k/v/out; cache contiguous [rows,L,H,d]).
+// Depth attention (row strides in elements for q/k/v/out).  Cache: row r's slot j at
+// r srow + j sslot elements; srow = 0 selects [rows, L, H, d] (srow = L h, sslot = h).
 // rope: rotate q and k_new by depth here (else they arrive rotated and rounded).
 int launch_depth_attn(int dtype, int64_t rows, int H, int d, int l, int L, const void* q,
                       int64_t ldq, const void* kn, int64_t ldk, const void* vn, int64_t ldv,
                       void* kc, void* vc, void* out, int64_t ldo, const float* cosd,
                       const float* sind, float scale, int rope, hipStream_t st,
-                      int window = 0, int dilation = 0);
+                      int window = 0, int dilation = 0, int64_t srow = 0, int64_t sslot = 0);
 
 // In-place RoPE of a [rows, 6h] QKV buffer (SA q/k by sequence position, DA q/k by depth).
 int launch_qkv_rope(int dtype, int64_t rows, int H, int d, int seq, int pos_fixed,
@@ -118,13 +119,13 @@ int launch_seq_attn(int dtype, int B, int q_len, int H, int d, int64_t pos0, con
 bool attn_pair_ok(int dtype, int B, int q_len, int H, int d, int64_t pos0, const void* vt);
 int launch_attn_pair(int B, int S, int H, int l, int L, const void* q, const void* k,
                      const void* vt, const void* dq, const void* dk, const void* dv,
-                     int64_t ldqkv, int64_t ldkv, void* dkc, void* dvc, void* out_sa, void* out_da,
+                     int64_t ldqkv, int64_t ldkv, int64_t srow, int64_t sslot, void* dkc, void* dvc, void* out_sa, void* out_da,
                      int64_t ldo, float scale, int window, int dilation, hipStream_t st);
 // The same for query blocks of more than 64 rows (the two-set flash grid), the two kinds
 // of block interleaved in proportion in one launch; -1 when S <= 64 or unsupported.
 int launch_attn_pair2(int B, int S, int H, int l, int L, const void* q, const void* k,
                       const void* vt, const void* dq, const void* dk, const void* dv,
-                      int64_t ldqkv, int64_t ldkv, void* dkc, void* dvc, void* out_sa, void* out_da,
+                      int64_t ldqkv, int64_t ldkv, int64_t srow, int64_t sslot, void* dkc, void* dvc, void* out_sa, void* out_da,
                       int64_t ldo, float scale, int window, int dilation, hipStream_t st);
 
 // Router scores z [T, E] f32 = rho * RoPE_depth(x W_r^T) . keys.  bf16: u computed inside
