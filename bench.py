@@ -107,9 +107,15 @@ def algorithmic_work(cfg, counts_per_depth, reps=1):
     else:
         w["seq_attn"] = dict(bound="mfma", flops=L * 4 * cfg.b * h * (cfg.s * (cfg.s + 1) // 2),
                              launches=L)
-    # q, k, v in, key and value stored, output out: 6 rows; 2 per older slot read
-    da_bytes = sum(T * h * es * (6 + 2 * (n_depth_keys(l, cfg.da_window, cfg.da_dilation) - 1))
-                   for l in range(L))
+    # bf16: q in and the output out (2 rows), the key and value of every slot read, the
+    # current one included (the projection writes it into the cache); float32: q, k, v in,
+    # key and value stored, output out (6 rows), 2 per older slot read
+    if cfg.dtype == "bf16":
+        da_bytes = sum(T * h * es * (2 + 2 * n_depth_keys(l, cfg.da_window, cfg.da_dilation))
+                       for l in range(L))
+    else:
+        da_bytes = sum(T * h * es * (6 + 2 * (n_depth_keys(l, cfg.da_window, cfg.da_dilation) - 1))
+                       for l in range(L))
     w["depth_attn"] = dict(bound="hbm", bytes=da_bytes, launches=L)
     # SA and DA in one launch: priced by its SA flops against the MFMA peak, and (reported
     # beside it) by its DA bytes against the HBM peak; each is a lower bound of the

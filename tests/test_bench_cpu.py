@@ -27,7 +27,12 @@ def test_depth_attn_bytes_full_and_windowed():
     b = _bench()
     cfg = CONFIGS["small"]
     T, h, L = cfg.T, cfg.h, cfg.L
+    # bf16: q and the output (2 rows) plus the key and value of each of the l + 1 slots
     full = b.algorithmic_work(cfg, [])["depth_attn"]["bytes"]
-    assert full == sum(T * h * 2 * (6 + 2 * l) for l in range(L))
+    assert full == sum(T * h * 2 * (2 + 2 * (l + 1)) for l in range(L))
     one = b.algorithmic_work(cfg.replace(da_window=1), [])["depth_attn"]["bytes"]
-    assert one == L * T * h * 2 * 6
+    assert one == L * T * h * 2 * 4
+    # float32: q, k, v in, the key and value stored, the output (6 rows), 2 per older slot
+    tiny = CONFIGS["tiny"]
+    f32 = b.algorithmic_work(tiny, [])["depth_attn"]["bytes"]
+    assert f32 == sum(tiny.T * tiny.h * 4 * (6 + 2 * l) for l in range(tiny.L))
