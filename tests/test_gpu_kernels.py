@@ -333,18 +333,19 @@ def test_expert_ffn(gpu_lib, dt, kind, T, h, f, E, k, skew):
     assert torch.equal(out0, res)
 
 
-def test_expert_ffn_grouping_paths_same_bits(gpu_lib):
-    # 4500 tokens x top-8 are grouped by the chunked kernels, the first 4000 tokens (32000
-    # slots) by the one-block kernel: every token's output is the same bits either way
+@pytest.mark.parametrize("T,n", [(4500, 4000), (129, 128)])
+def test_expert_ffn_grouping_paths_same_bits(gpu_lib, T, n):
+    # T tokens x top-8 and their first n tokens are grouped with different chunk counts
+    # (36 vs 32 chunks of 1024 slots; 1032 slots in two chunks vs 1024 in the one-block
+    # launch): every token's output is the same bits either way
     D = gpu_lib
-    T, h, f, E, k = 4500, 256, 64, 64, 8
+    h, f, E, k = 256, 64, 64, 8
     x = _t((T, h), 33, 0, 1.0, torch.bfloat16)
     idx, gate = _routing(T, E, k, 33, True)
     res = _t((T, h), 33, 1, 1.0, torch.float32)
     w1, w3 = _t((E, f, h), 33, 2, 0.05, torch.bfloat16), _t((E, f, h), 33, 3, 0.05, torch.bfloat16)
     w2 = _t((E, h, f), 33, 4, 0.05, torch.bfloat16)
     full = D.dreamer_expert_ffn("swiglu", x, idx, gate, w1, w3, w2, res)
-    n = 4000
     part = D.dreamer_expert_ffn("swiglu", x[:n].contiguous(), idx[:n].contiguous(),
                                 gate[:n].contiguous(), w1, w3, w2, res[:n].contiguous())
     torch.cuda.synchronize()

@@ -25,11 +25,12 @@ pytestmark = pytest.mark.gpu
 
 
 def run_gpu(D, cfg, W, x0, sa_cache=None, sa_cap=0, replay=None, streams=False,
-            fuse_attn=True, steps=False):
+            fuse_attn=True, steps=False, da_cache=None):
     """replay: an oracle result whose expert choices the GPU adopts (route_in);
     streams: independent branches on the library's side streams; fuse_attn: SA and DA
     of a depth may share one launch; steps: also return x_steps (x_{l+1}, float32) and
-    y_steps (the EA router input of every depth)."""
+    y_steps (the EA router input of every depth); da_cache: the caller's DA caches
+    (k, v) [T, L, H, d] to fill."""
     G = gpu_weights(D, cfg, W)
     lc = lib_cfg(D, cfg, sa_cap=sa_cap, streams=streams, fuse_attn=fuse_attn)
     T = cfg.T
@@ -52,7 +53,8 @@ def run_gpu(D, cfg, W, x0, sa_cache=None, sa_cap=0, replay=None, streams=False,
         if cfg.proj_experts:
             pin = torch.from_numpy(np.ascontiguousarray(replay["pidx"]).astype(np.int32)).cuda()
     out = D.dreamer_layer_forward(lc, G, x, route=route, proj_route=proj, sa_cache=sa_cache,
-                                  route_in=rin, proj_route_in=pin, x_steps=xs, y_steps=ys)
+                                  route_in=rin, proj_route_in=pin, x_steps=xs, y_steps=ys,
+                                  da_cache=da_cache)
     torch.cuda.synchronize()
     res = {"x_out": out.cpu().numpy().astype(np.float64)}
     if route is not None:
@@ -402,6 +404,28 @@ def test_layer_paired_attention_same_bits(gpu_lib, mixture, window, dilation, sh
         D.timing_disable()
         assert np.array_equal(a["x_out"], b["x_out"]) and np.array_equal(a["idx"], b["idx"])
     assert counts == {"attention": cfg.L, "seq_attn": 0, "depth_attn": 0}, counts
+
+
+@pytest.mark.parametrize("name", ["tiny", "small"])
+def test_layer_da_cache_output(gpu_lib, name):
+    """The caller's DA caches [T, L, H, d] (NaN-poisoned first) are written at every depth
+    and leave the output's bits as with the layer's own (slot-major) cache; in float32
+    they equal the oracle's caches."""
+    D = gpu_lib
+    cfg = CONFIGS["tiny"] if name == "tiny" else CONFIGS["small"].replace(b=2, s=128, L=3)
+    print(f"layer DA cache output {name}", flush=True)
+    W, x0 = make_weights(cfg), make_x0(cfg)
+    a = run_gpu(D, cfg, W, x0)
+    shape = (cfg.T, cfg.L, cfg.H, cfg.d)
+    dk = torch.full(shape, float("nan"), dtype=cfg.torch_dtype, device="cuda")
+    dv = torch.full_like(dk, float("nan"))
+    b = run_gpu(D, cfg, W, x0, da_cache=(dk, dv))
+    assert np.array_equal(a["x_out"], b["x_out"])
+    assert not torch.isnan(dk).any() and not torch.isnan(dv).any()
+    if cfg.dtype == "f32":
+        ref = run_ref(cfg, W, x0)
+        assert rel_err(dk.cpu().numpy(), ref["da_k"]) <= 1e-5
+        assert rel_err(dv.cpu().numpy(), ref["da_v"]) <= 1e-5
 
 
 # ------------------------------------------------------------------ multi-token decode
