@@ -3,7 +3,9 @@
 Tolerances: float32 storage -> max|err| / max|ref| <= 1e-5.  bf16 storage -> the oracle
 rounds at the same storage points, so outputs must agree to 1-2 bf16 ulps, plus a term
 for the one internal rounding the oracle does not model (bf16 softmax weights inside the
-MFMA attention kernel: |dP| <= 2^-9 P, hence |dO| <= 2^-9 max|v|).  Routing: the selected
+MFMA attention kernel: |dP| <= 2^-8 P, hence a per-element |dO| <= 2^-8 (sum p|v| / sum p
++ |o|) / (1 - 2^-8)), and, in depth attention, a term of 2^-8 max|v| for one-ulp
+differences of the independently rounded rotated q and k.  Routing: the selected
 sets must be identical except where the oracle's k-th and (k+1)-th biased scores are within
 1e-6; gates to 1e-5 relative."""
 import math
@@ -13,7 +15,7 @@ import pytest
 import torch
 
 import oracle
-from helpers import assert_close_ulps, rel_err, routing_mismatch
+from helpers import assert_close_ulps, bf16_ulp, rel_err, routing_mismatch
 from synth import CONFIGS, make_bias, rng
 
 pytestmark = pytest.mark.gpu
@@ -115,10 +117,19 @@ def test_seq_attn_prefill(gpu_lib, dt, B, S, H, d, rope):
     torch.cuda.synchronize()
     g = _np(out)
     if bf:
-        vmax = np.abs(_np(v)).max()
-        # P enters the P V product rounded to bf16 (relative error <= 2^-9 per weight), so
-        # an output moves by at most 2^-9 max|v| beyond its own final rounding
-        assert_close_ulps(g, ref, ulps=2, atol=2.0 ** -8 * vmax, what="SA prefill")
+        # Every softmax weight enters P.V rounded to bf16 (relative error <= u = 2^-8), and
+        # the denominator is summed from the same rounded weights, so out = sum p~ v / sum p~
+        # lies within u / (1 - u) * (sum p |v| / sum p + |o|) of the exact o, per element;
+        # sum p |v| / sum p is the oracle's attention over |v|.  With RoPE, q and k are
+        # rounded after the rotation on each side, and a rare one-ulp difference moves a
+        # score by up to about as much again.
+        vabs, _, _ = oracle.seq_attn(_np(q), _np(k), np.abs(_np(v)), 0, None, None, rope, 1e4,
+                                     bf)
+        u = 2.0 ** -8
+        bound = (2.0 if rope else 1.0) * u / (1 - u) * (vabs + np.abs(ref))
+        assert_close_ulps(g, ref, ulps=2, atol=bound, what="SA prefill")
+        lim = 2 * bf16_ulp(ref) + bound
+        print(f"  worst err / bound {(np.abs(g - ref) / lim).max():.3f}", flush=True)
         assert_close_ulps(_np(kc[:, :S]), krot, ulps=1, atol=2.0 ** -20, what="SA cache keys")
     else:
         assert rel_err(g, ref) <= 1e-5
